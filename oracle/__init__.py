@@ -1,0 +1,215 @@
+"""CPU oracle for the W4A16 mixed-precision GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import this package.  The product path (``weight_only_quantized_mpgemm_amd``) never
+imports it, and this package never imports the product path: the two share no code.
+
+The arithmetic lives in ``mpgemm_oracle.c`` (plain scalar C, fp64); this module builds it
+with gcc, loads it with ctypes and exposes numpy-level wrappers.  What each function
+computes, with its citation of "LMDeploy Accelerates Mixed-Precision LLM Inference with
+TurboMind" (arXiv 2508.15601), is stated in the C source.
+
+Parity status: every function is pinned by CPU tests against values fixed independently
+of this code (see tests/test_oracle.py); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mpgemm_oracle.c")
+_LIB_PATH = os.environ.get("MPGEMM_ORACLE_LIB") or os.path.join(_HERE, "libmpgemm_oracle.so")
+
+F16 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str | None = None) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP over output rows)."""
+    out = out or _LIB_PATH
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    i = ctypes.c_int
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_dequant.argtypes = [u8p, u16p, u8p, i, i, i, i, u16p]
+    lib.oracle_dequant.restype = None
+    lib.oracle_gemm.argtypes = [u16p, u16p, i, i, i, i, u16p, i]
+    lib.oracle_gemm.restype = None
+    lib.oracle_packed_code_bytes.argtypes = [i, i]
+    lib.oracle_packed_code_bytes.restype = ctypes.c_size_t
+    lib.oracle_packed_meta_bytes.argtypes = [i, i, i, i]
+    lib.oracle_packed_meta_bytes.restype = ctypes.c_size_t
+    lib.oracle_pack.argtypes = [u8p, u16p, u8p, i, i, i, u8p, u8p]
+    lib.oracle_pack.restype = None
+    lib.oracle_unpack.argtypes = [u8p, u8p, i, i, i, i, u8p, u16p, u8p]
+    lib.oracle_unpack.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _dtype_code(dtype: str) -> int:
+    if dtype in ("f16", "fp16", "float16"):
+        return F16
+    if dtype in ("bf16", "bfloat16"):
+        return BF16
+    raise ValueError(f"unknown activation dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------- number formats ----
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.oracle_f16_to_f64(int(b)) for b in flat]).reshape(np.shape(bits))
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.oracle_bf16_to_f64(int(b)) for b in flat]).reshape(np.shape(bits))
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    return np.array([lib.oracle_f64_to_f16(float(v)) for v in flat],
+                    dtype=np.uint16).reshape(np.shape(x))
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    return np.array([lib.oracle_f64_to_bf16(float(v)) for v in flat],
+                    dtype=np.uint16).reshape(np.shape(x))
+
+
+# ---------------------------------------------------------------- the method --------
+
+def dequant(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None,
+            group: int, dtype: str = "f16") -> np.ndarray:
+    """w[k][n] = round_act((q - z) * s); returns activation-format bits [K, N]."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert K % group == 0 and scales_bits.shape == (K // group, N)
+    zp = None
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        assert zeros.shape == (K // group, N)
+        zp = _ptr(zeros, ctypes.c_uint8)
+    w = np.empty((K, N), dtype=np.uint16)
+    lib.oracle_dequant(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16), zp,
+                       K, N, group, _dtype_code(dtype), _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def gemm(x_bits: np.ndarray, w_bits: np.ndarray, dtype: str = "f16",
+         threads: int = 1) -> np.ndarray:
+    """Y = round_act(X @ w) with the sum in fp64; inputs and output are format bits."""
+    lib = _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    K2, N = w_bits.shape
+    assert K == K2
+    y = np.empty((M, N), dtype=np.uint16)
+    lib.oracle_gemm(_ptr(x_bits, ctypes.c_uint16), _ptr(w_bits, ctypes.c_uint16),
+                    M, N, K, _dtype_code(dtype), _ptr(y, ctypes.c_uint16), int(threads))
+    return y
+
+
+def w4a16(x_bits, codes, scales_bits, zeros, group, dtype="f16", threads=1):
+    """The whole path: dequantize, then the GEMM."""
+    return gemm(x_bits, dequant(codes, scales_bits, zeros, group, dtype), dtype, threads)
+
+
+def packed_code_bytes(K: int, N: int) -> int:
+    return int(_load().oracle_packed_code_bytes(K, N))
+
+
+def packed_meta_bytes(K: int, N: int, group: int, symmetric: bool) -> int:
+    return int(_load().oracle_packed_meta_bytes(K, N, group, int(bool(symmetric))))
+
+
+def pack(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None, group: int):
+    """Layout-v1 packing; returns (packed_codes uint8, packed_meta uint8)."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    assert K % 128 == 0 and K % group == 0 and N % 16 == 0
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    zp = None
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        zp = _ptr(zeros, ctypes.c_uint8)
+    pc = np.empty(packed_code_bytes(K, N), dtype=np.uint8)
+    pm = np.empty(packed_meta_bytes(K, N, group, zeros is None), dtype=np.uint8)
+    lib.oracle_pack(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16), zp,
+                    K, N, group, _ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8))
+    return pc, pm
+
+
+def unpack(packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int, group: int,
+           symmetric: bool):
+    """Inverse of pack; returns (codes, scales_bits, zeros or None)."""
+    lib = _load()
+    pc = np.ascontiguousarray(packed_codes, dtype=np.uint8)
+    pm = np.ascontiguousarray(packed_meta, dtype=np.uint8)
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty((K // group, N), dtype=np.uint16)
+    zeros = None if symmetric else np.empty((K // group, N), dtype=np.uint8)
+    lib.oracle_unpack(_ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8), K, N, group,
+                      int(bool(symmetric)), _ptr(codes, ctypes.c_uint8),
+                      _ptr(scales, ctypes.c_uint16),
+                      None if zeros is None else _ptr(zeros, ctypes.c_uint8))
+    return codes, scales, zeros
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def timed_w4a16(x_bits, codes, scales_bits, zeros, group, dtype="f16", threads=1):
+    """Runs the whole oracle path and returns (Y, seconds)."""
+    t0 = time.perf_counter()
+    y = w4a16(x_bits, codes, scales_bits, zeros, group, dtype, threads)
+    return y, time.perf_counter() - t0

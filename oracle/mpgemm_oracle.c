@@ -1,0 +1,259 @@
+/*
+ * CPU oracle for the W4A16 mixed-precision GEMM -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may load this
+ * library.  It shares no code with the HIP path (weight_only_quantized_mpgemm_amd/csrc):
+ * no headers, no helpers, no tables.  It is plain, scalar and slow on purpose so that a
+ * reader can check it against the definitions by eye.
+ *
+ * Source cited throughout: "LMDeploy Accelerates Mixed-Precision LLM Inference with
+ * TurboMind" (arXiv 2508.15601), abbreviated [TurboMind].
+ *
+ *   - [TurboMind, Fig. 4 caption and Fig. 6 caption]: low-bit integers are turned into
+ *     FP16 by "I2F" conversion and scaling before the tensor-core multiply.  The formula is
+ *     not printed on the pages; the reading used here is the asymmetric group form
+ *     w = (q - z) * s with one scale s and one integer zero z per (group of g consecutive
+ *     k, column n), rounded once to the activation format (fp16; bf16 for bf16
+ *     activations).  zero = 8 for symmetric codes.
+ *   - The GEMM is Y[m][n] = sum_k X[m][k] * w[k][n].  The oracle forms the sum in fp64 in
+ *     ascending k and rounds it once (round-to-nearest-even) to the activation format.
+ *   - [TurboMind, Fig. 6 and Fig. 7 captions; the interleave diagram beside Fig. 24]:
+ *     packing is an offline, lossless permutation.  The word-internal nibble order is the
+ *     one that diagram shows (most to least significant: e7 e5 e3 e1 e6 e4 e2 e0).  The
+ *     tile and lane placement is this library's own gfx950 layout, restated below from
+ *     its specification (see include/mpgemm.h), not derived from the GPU code.
+ *
+ * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+
+/* ---------------------------------------------------------------- number formats --- */
+
+/* IEEE 754 binary16: 1 sign, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-24 */
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);     /* (1.f) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_bf16_to_f64(uint16_t b) {
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int f = b & 0x7f;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -133);                /* subnormal: f * 2^-133 */
+    } else if (e == 255) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + f), e - 134);     /* (1.f) * 2^(e-127) */
+    }
+    return sign ? -v : v;
+}
+
+/*
+ * Round a double to a binary format with `frac_bits` fraction bits, exponent bias `bias`
+ * and all-ones exponent `emax_field`, ties to even.  The value is split into an integer
+ * count of the format's spacing (ulp) at its exponent; rint() rounds that count in the
+ * default ties-to-even mode.  Below the smallest normal the spacing stays fixed
+ * (subnormals).  A count that carries into the next binade is encoded by the same sum.
+ */
+static uint16_t round_to_binary16_like(double x, int frac_bits, int bias, int emax_field) {
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    uint16_t inf_bits = (uint16_t)(emax_field << frac_bits);
+    if (isnan(x)) return (uint16_t)(inf_bits | (1u << (frac_bits - 1)));  /* quiet NaN */
+    double a = fabs(x);
+    if (isinf(a)) return (uint16_t)(sign | inf_bits);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);              /* a in [2^(e2-1), 2^e2) */
+    int exp_unbiased = e2 - 1;
+    int min_normal_exp = 1 - bias;
+    if (exp_unbiased < min_normal_exp) exp_unbiased = min_normal_exp;
+    if (exp_unbiased > emax_field - 1 - bias) {
+        return (uint16_t)(sign | inf_bits);  /* at or above 2^(emax+1): beyond every finite */
+    }
+    double spacing = ldexp(1.0, exp_unbiased - frac_bits);
+    double count = rint(a / spacing);       /* exact scaling, then ties-to-even */
+    /* count lies in [2^frac_bits, 2^(frac_bits+1)] for normals, [0, 2^frac_bits] below. */
+    /* Biased exponent field plus fraction; for the lowest binade the field is 1 and the
+       sum reduces to the count itself, which is the subnormal encoding. */
+    long bits = ((long)(exp_unbiased + bias) << frac_bits) + (long)count - (1L << frac_bits);
+    if (bits >= (long)inf_bits) return (uint16_t)(sign | inf_bits);   /* overflow */
+    return (uint16_t)(sign | (uint16_t)bits);
+}
+
+uint16_t oracle_f64_to_f16(double x) { return round_to_binary16_like(x, 10, 15, 31); }
+uint16_t oracle_f64_to_bf16(double x) { return round_to_binary16_like(x, 7, 127, 255); }
+
+static double act_to_f64(uint16_t v, int dtype) {
+    return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(v) : oracle_f16_to_f64(v);
+}
+static uint16_t f64_to_act(double v, int dtype) {
+    return dtype == ORACLE_BF16 ? oracle_f64_to_bf16(v) : oracle_f64_to_f16(v);
+}
+
+/* ---------------------------------------------------------------- dequantization --- */
+
+/*
+ * w[k][n] = round_act((q[k][n] - z[k/g][n]) * s[k/g][n])          [TurboMind, Fig. 6]
+ *   codes  uint8 [K][N], low 4 bits used (the code is an unsigned 4-bit integer)
+ *   scales fp16  [K/g][N]
+ *   zeros  uint8 [K/g][N], low 4 bits used; NULL means symmetric codes with zero 8
+ *   w      out, activation format bits, [K][N]
+ */
+void oracle_dequant(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                    int K, int N, int g, int dtype, uint16_t *w) {
+    for (int k = 0; k < K; ++k) {
+        int grp = k / g;
+        for (int n = 0; n < N; ++n) {
+            int q = codes[(size_t)k * N + n] & 0xf;
+            int z = zeros ? (zeros[(size_t)grp * N + n] & 0xf) : 8;
+            double s = oracle_f16_to_f64(scales[(size_t)grp * N + n]);
+            double exact = (double)(q - z) * s;      /* exact: 5-bit integer x 11-bit scale */
+            w[(size_t)k * N + n] = f64_to_act(exact, dtype);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- the GEMM --- */
+
+/*
+ * Y[m][n] = round_act( sum_{k ascending} X[m][k] * w[k][n] ), sum in fp64.
+ *   X [M][K], w [K][N], Y [M][N], all activation-format bits, row-major.
+ *   threads: OpenMP threads over independent output rows (1 = serial).
+ */
+void oracle_gemm(const uint16_t *X, const uint16_t *w, int M, int N, int K, int dtype,
+                 uint16_t *Y, int threads) {
+#ifdef _OPENMP
+    if (threads < 1) threads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads)
+#endif
+    for (int m = 0; m < M; ++m) {
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                acc += act_to_f64(X[(size_t)m * K + k], dtype) *
+                       act_to_f64(w[(size_t)k * N + n], dtype);
+            }
+            Y[(size_t)m * N + n] = f64_to_act(acc, dtype);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ packed layout --- */
+
+/*
+ * Layout version 1 (restated from its specification in include/mpgemm.h):
+ *
+ * Codes plane, K*N/2 bytes.  The [K][N] code matrix is cut into tiles of 16 columns by
+ * 128 rows of k.  Tile index T = (n/16)*(K/128) + k/128, tile base T*1024 bytes.  Within a
+ * tile, with kk = k%128 and nn = n%16: lane L = nn + 16*((kk%32)/8), word t = kk/32, and
+ * the 32-bit little-endian word sits at byte L*16 + t*4.  Element i = kk%8 of the word
+ * occupies nibble p(i) = i/2 for even i and 4 + i/2 for odd i (bits 4p..4p+3), which
+ * reads e7 e5 e3 e1 e6 e4 e2 e0 from the most significant nibble down
+ * [TurboMind, interleave diagram beside Fig. 24].
+ *
+ * Meta plane.  Scales first: fp16 at element index (n/16)*(K/g)*16 + (k/g)*16 + n%16,
+ * (K/g)*N*2 bytes.  Then, for asymmetric codes only, zeros: 4-bit values at the same
+ * element index e, byte e/2, low nibble for even e, high nibble for odd e,
+ * (K/g)*N/2 bytes.
+ */
+static int nibble_of_element(int i) { return (i % 2 == 0) ? i / 2 : 4 + i / 2; }
+
+static size_t code_byte_offset(int k, int n, int K) {
+    size_t T = (size_t)(n / 16) * (size_t)(K / 128) + (size_t)(k / 128);
+    int kk = k % 128, nn = n % 16;
+    int lane = nn + 16 * ((kk % 32) / 8);
+    int word = kk / 32;
+    return T * 1024 + (size_t)lane * 16 + (size_t)word * 4;
+}
+
+static size_t meta_index(int k, int n, int K, int g) {
+    return (size_t)(n / 16) * (size_t)(K / g) * 16 + (size_t)(k / g) * 16 + (size_t)(n % 16);
+}
+
+size_t oracle_packed_code_bytes(int K, int N) { return (size_t)K * N / 2; }
+size_t oracle_packed_meta_bytes(int K, int N, int g, int symmetric) {
+    size_t groups = (size_t)(K / g) * N;
+    return groups * 2 + (symmetric ? 0 : groups / 2);
+}
+
+/* Requires K % 128 == 0, K % g == 0, N % 16 == 0. */
+void oracle_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                 int K, int N, int g, uint8_t *packed_codes, uint8_t *packed_meta) {
+    memset(packed_codes, 0, oracle_packed_code_bytes(K, N));
+    memset(packed_meta, 0, oracle_packed_meta_bytes(K, N, g, zeros == NULL));
+    for (int k = 0; k < K; ++k) {
+        for (int n = 0; n < N; ++n) {
+            uint32_t q = codes[(size_t)k * N + n] & 0xf;
+            size_t off = code_byte_offset(k, n, K);
+            uint32_t word;
+            memcpy(&word, packed_codes + off, 4);
+            word |= q << (4 * nibble_of_element(k % 8));
+            memcpy(packed_codes + off, &word, 4);
+        }
+    }
+    uint16_t *meta_scales = (uint16_t *)packed_meta;
+    uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
+    for (int r = 0; r < K / g; ++r) {
+        for (int n = 0; n < N; ++n) {
+            size_t e = meta_index(r * g, n, K, g);
+            meta_scales[e] = scales[(size_t)r * N + n];
+            if (zeros) {
+                uint8_t z = zeros[(size_t)r * N + n] & 0xf;
+                meta_zeros[e / 2] |= (uint8_t)((e % 2) ? (z << 4) : z);
+            }
+        }
+    }
+}
+
+/* Inverse of oracle_pack.  zeros is written only for asymmetric packing. */
+void oracle_unpack(const uint8_t *packed_codes, const uint8_t *packed_meta, int K, int N,
+                   int g, int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    for (int k = 0; k < K; ++k) {
+        for (int n = 0; n < N; ++n) {
+            uint32_t word;
+            memcpy(&word, packed_codes + code_byte_offset(k, n, K), 4);
+            codes[(size_t)k * N + n] = (uint8_t)((word >> (4 * nibble_of_element(k % 8))) & 0xf);
+        }
+    }
+    const uint16_t *meta_scales = (const uint16_t *)packed_meta;
+    const uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
+    for (int r = 0; r < K / g; ++r) {
+        for (int n = 0; n < N; ++n) {
+            size_t e = meta_index(r * g, n, K, g);
+            scales[(size_t)r * N + n] = meta_scales[e];
+            if (!symmetric && zeros) {
+                uint8_t b = meta_zeros[e / 2];
+                zeros[(size_t)r * N + n] = (uint8_t)((e % 2) ? (b >> 4) : (b & 0xf));
+            }
+        }
+    }
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

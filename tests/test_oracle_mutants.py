@@ -1,0 +1,49 @@
+"""The oracle's pins must fail when a plausible mistake is planted in the oracle.
+
+Each mutant is a copy of oracle/mpgemm_oracle.c with one edit (a flipped sign, a wrong
+index, a dropped term, a transposed operand, a different rounding rule, a wrong layout
+formula).  It is compiled into a temporary directory and the pin suite
+(tests/test_oracle.py) runs against it in a subprocess; the suite must report failures.
+Everything happens on the CPU; the real oracle library is never touched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mpgemm_oracle.c")
+
+MUTANTS = {
+    "sign_of_q_minus_z": ("(double)(q - z) * s", "(double)(z - q) * s"),
+    "group_index_mod": ("int grp = k / g;", "int grp = k % g;"),
+    "zero_index": ("zeros[(size_t)grp * N + n] & 0xf", "zeros[(size_t)(n % (K / g)) * N + n] & 0xf"),
+    "nibble_order_plain": ("(i % 2 == 0) ? i / 2 : 4 + i / 2", "i"),
+    "lane_formula": ("int lane = nn + 16 * ((kk % 32) / 8);", "int lane = nn * 4 + ((kk % 32) / 8);"),
+    "transposed_w": ("act_to_f64(w[(size_t)k * N + n], dtype)",
+                     "act_to_f64(w[(size_t)(k % N) * N + (n % K)], dtype)"),
+    "dropped_last_k": ("for (int k = 0; k < K; ++k) {\n                acc",
+                       "for (int k = 0; k < K - 1; ++k) {\n                acc"),
+    "round_half_up": ("double count = rint(a / spacing);",
+                      "double count = floor(a / spacing + 0.5);"),
+    "meta_reversed_in_strip": ("(size_t)(k / g) * 16 + (size_t)(n % 16);",
+                               "(size_t)(k / g) * 16 + (size_t)(15 - n % 16);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(before) == 1, f"mutation anchor for {name} not found once"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(before, after))
+    lib = oracle.build(src=str(src), out=str(tmp_path / "libmutant.so"))
+    env = dict(os.environ, MPGEMM_ORACLE_LIB=lib)
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"

@@ -1,0 +1,96 @@
+"""Seeded synthetic inputs for the W4A16 GEMM, and the workload shape tables.
+
+This module is the only thing the HIP path's tests and the oracle share.  It draws random
+numbers and casts them to storage formats; it holds none of the method's arithmetic (no
+dequantization, no packing, no products).
+
+Recipe (every array is drawn from numpy's PCG64 with a per-case seed):
+  codes  uint8 [K, N]        uniform integers in [0, 15]
+  zeros  uint8 [K/g, N]      uniform integers in [0, 15]; None for symmetric codes (zero 8)
+  scales fp16  [K/g, N]      uniform in [lo, hi] drawn as float64, rounded to fp16 (RNE)
+  X      fp16|bf16 [M, K]    standard normal drawn as float32, rounded to the activation
+                             format (RNE; bf16 through torch's float32 -> bfloat16 cast)
+Shapes are those of the layers the workloads are named after (Llama-3-8B, Llama-3-70B,
+Qwen3-32B projection matrices).  No dataset or checkpoint is read.
+"""
+from __future__ import annotations
+
+import dataclasses
+import zlib
+
+import numpy as np
+
+BASE_SEED = 20250821
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    group: int
+    symmetric: bool
+    scale_lo: float
+    scale_hi: float
+    dtype: str                      # activation / output format: "f16" or "bf16"
+    ms: tuple
+    shapes: tuple                   # ((K, N, label), ...)
+
+
+TINY = Workload("tiny", 128, False, 0.005, 0.02, "f16", (4,), ((256, 256, "tiny"),))
+
+LLAMA3_8B_SHAPES = ((4096, 6144, "qkv"), (4096, 4096, "o_proj"),
+                    (4096, 28672, "gate_up"), (14336, 4096, "down"))
+LLAMA3_8B_DECODE = Workload("llama3_8b_decode", 128, False, 0.005, 0.02, "f16",
+                            (1, 8, 16), LLAMA3_8B_SHAPES)
+LLAMA3_8B_PREFILL = Workload("llama3_8b_prefill", 128, False, 0.005, 0.02, "f16",
+                             (512, 2048, 8192), LLAMA3_8B_SHAPES)
+LLAMA3_70B = Workload("llama3_70b", 128, False, 0.005, 0.02, "bf16", (1, 64, 4096),
+                      ((8192, 10240, "qkv"), (8192, 8192, "o_proj"),
+                       (8192, 57344, "gate_up"), (28672, 8192, "down")))
+QWEN3_32B = Workload("qwen3_32b", 64, True, 0.002, 0.01, "f16",
+                     (1, 2, 4, 16, 128, 1024, 8192),
+                     ((5120, 10240, "qkv"), (8192, 5120, "o_proj"),
+                      (5120, 51200, "gate_up"), (25600, 5120, "down")))
+
+ALL_WORKLOADS = (TINY, LLAMA3_8B_DECODE, LLAMA3_8B_PREFILL, LLAMA3_70B, QWEN3_32B)
+
+
+def seed_for(tag: str, M: int, K: int, N: int) -> int:
+    return BASE_SEED + zlib.crc32(f"{tag}:{M}:{K}:{N}".encode()) % 1_000_003
+
+
+def _to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def activations(M: int, K: int, dtype: str, seed: int) -> np.ndarray:
+    """X bits [M, K] in the activation format."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        return _to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def weights(K: int, N: int, group: int, symmetric: bool, scale_lo: float, scale_hi: float,
+            seed: int):
+    """(codes uint8 [K,N], scales fp16 bits [K/g,N], zeros uint8 [K/g,N] or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    scales = rng.uniform(scale_lo, scale_hi, size=(K // group, N)).astype(np.float16)
+    zeros = None if symmetric else rng.integers(0, 16, size=(K // group, N), dtype=np.uint8)
+    return codes, scales.view(np.uint16), zeros
+
+
+def make_case(wl: Workload, M: int, K: int, N: int, seed: int | None = None):
+    """All inputs of one GEMM of workload `wl` at (M, K, N)."""
+    if seed is None:
+        seed = seed_for(wl.name, M, K, N)
+    codes, scales, zeros = weights(K, N, wl.group, wl.symmetric, wl.scale_lo, wl.scale_hi,
+                                   seed)
+    x = activations(M, K, wl.dtype, seed + 1)
+    return dict(x=x, codes=codes, scales=scales, zeros=zeros, group=wl.group,
+                symmetric=wl.symmetric, dtype=wl.dtype, M=M, K=K, N=N, seed=seed)
