@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""W4A16 GEMM throughput on one MI355X: Llama-3-8B layer shapes at M = 1, 16 and 2048.
+
+One step = the four projection GEMMs of a Llama-3-8B layer (QKV 4096x6144, O 4096x4096,
+gate_up 4096x28672, down 14336x4096; g = 128, asymmetric uint4 codes, fp16 scales, fp16
+activations and output) at each of M = 1, 16 and 2048: twelve mpgemm_w4a16 calls.  Weights
+are pre-packed and resident in HBM; each call reads a different copy from a rotating pool
+larger than the 256 MB Infinity Cache, so weight bytes come from HBM, not from a cache that
+the previous call warmed.
+
+Prints one JSON line: value = whole-step TFLOP/s (2*M*N*K summed over the twelve GEMMs,
+divided by the step time), plus HBM GB/s of algorithmic bytes, a per-GEMM breakdown, the
+roofline of the dominant kernel (hipEvents around each of its launches, on the stream the
+library launches on), and the CPU oracle timed on a bounded sample (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+MS = (1, 16, 2048)
+
+
+def gemm_bytes(M, K, N, g, symmetric=False):
+    """Algorithmic HBM bytes of one W4A16 GEMM: packed codes, scales, zeros, X and Y."""
+    cells = (K // g) * N
+    return K * N // 2 + cells * 2 + (0 if symmetric else cells // 2) + M * K * 2 + M * N * 2
+
+
+def gemm_flops(M, K, N):
+    return 2 * M * N * K
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(shapes, group, m_rows=16):
+    """The oracle, as it stands, on M = m_rows rows of every shape (full N)."""
+    import oracle
+    import workloads
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = max(1, min(threads, os.cpu_count() or 1))
+    total_s, flops = 0.0, 0
+    for K, N, label in shapes:
+        case = workloads.make_case(workloads.LLAMA3_8B_DECODE, m_rows, K, N)
+        _, secs = oracle.timed_w4a16(case["x"], case["codes"], case["scales"], case["zeros"],
+                                     group, "f16", threads)
+        total_s += secs
+        flops += gemm_flops(m_rows, K, N)
+        log(f"cpu oracle {label} M={m_rows}: {secs:.2f} s")
+    return {"value": flops / total_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"M={m_rows} rows x all four Llama-3-8B shapes (full K, N), "
+                      f"dequantize + fp64 GEMM, {total_s:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--pool-gb", type=float, default=1.5,
+                    help="size of the rotating pool of packed weight copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would "
+              "run its own shard of N or K independently); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import weight_only_quantized_mpgemm_amd as mp
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.LLAMA3_8B_DECODE
+    shapes = wl.shapes
+    g = wl.group
+
+    # ---- packed weights: one seeded layer, replicated into a rotating pool ----
+    layer = []
+    for K, N, label in shapes:
+        codes, scales, zeros = workloads.weights(K, N, g, False, wl.scale_lo, wl.scale_hi,
+                                                 workloads.seed_for("bench", 0, K, N))
+        packed = mp.pack_weights(torch.from_numpy(codes).to(dev),
+                                 torch.from_numpy(scales.view(np.int16)).to(dev).view(torch.float16),
+                                 torch.from_numpy(zeros).to(dev), g)
+        layer.append(packed)
+    torch.cuda.synchronize()
+    layer_bytes = sum(p.nbytes for p in layer)
+    copies = max(3 * len(MS), int(np.ceil(args.pool_gb * 1e9 / layer_bytes)))
+    pool = [layer] + [[mp.PackedWeights(p.codes.clone(), p.meta.clone(), p.K, p.N, p.group,
+                                        p.symmetric) for p in layer] for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    log(f"weight pool: {copies} copies x {layer_bytes / 1e6:.1f} MB")
+
+    xs, ys = {}, {}
+    for M in MS:
+        for K in sorted({k for k, _, _ in shapes}):
+            bits = workloads.activations(M, K, "f16", workloads.seed_for("bench-x", M, K, 0))
+            xs[(M, K)] = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+        for N in sorted({n for _, n, _ in shapes}):
+            ys[(M, N)] = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+    calls = [(M, K, N, label) for M in MS for K, N, label in shapes]
+    cfg_of = {c: mp.select_config(c[0], c[2], c[1], g, torch.float16) for c in calls}
+    events = {c: [] for c in calls}
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s, record):
+        for mi, M in enumerate(MS):
+            pk = pool[(s * len(MS) + mi) % copies]
+            for j, (K, N, label) in enumerate(shapes):
+                c = (M, K, N, label)
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                mp.w4a16(xs[(M, K)], pk[j], out=ys[(M, N)])
+                if record:
+                    e1.record(stream)
+                    events[c].append((e0, e1))
+
+    for s in range(args.warmup):
+        step(s, record=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_s = elapsed / args.steps
+    step_flops = sum(gemm_flops(M, K, N) for M, K, N, _ in calls)
+    step_bytes = sum(gemm_bytes(M, K, N, g) for M, K, N, _ in calls)
+
+    per_call, per_cfg = [], {}
+    for c in calls:
+        M, K, N, label = c
+        durs = [a.elapsed_time(b) * 1e-3 for a, b in events[c]]
+        t = float(np.mean(durs))
+        fl, by = gemm_flops(M, K, N), gemm_bytes(M, K, N, g)
+        bound = "hbm" if M <= 64 else "mfma"
+        frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
+            (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
+        cfg = mp.config_name(cfg_of[c])
+        per_call.append({"M": M, "K": K, "N": N, "layer": label, "kernel": cfg,
+                         "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                         "gbps": round(by / t / 1e9, 1), "bound": bound, "frac": round(frac, 4)})
+        agg = per_cfg.setdefault(cfg, {"t": 0.0, "flops": 0, "bytes": 0, "n": 0, "bound": bound})
+        agg["t"] += t
+        agg["flops"] += fl
+        agg["bytes"] += by
+        agg["n"] += 1
+
+    def roofline(cfg):
+        a = per_cfg[cfg]
+        if a["bound"] == "mfma":
+            ach = a["flops"] / a["t"] / 1e12
+            return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": None, "kernel": cfg, "launches_per_step": a["n"]}
+        ach = a["bytes"] / a["t"] / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": cfg, "launches_per_step": a["n"]}
+
+    dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
+    out = {
+        "metric": "W4A16 GEMM TFLOP/s and HBM GB/s (% roofline), Llama-3-8B shapes M=1/16/2048",
+        "value": round(step_flops / step_s / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b W4A16 g128 asym fp16: qkv 4096x6144, o_proj "
+                               "4096x4096, gate_up 4096x28672, down 14336x4096 at "
+                               "M=1,16,2048 (12 GEMMs per step)",
+                   "weight_pool_copies": copies, "group": g},
+        "hbm_gbps": round(step_bytes / step_s / 1e9, 1),
+        "roofline": roofline(dominant),
+        "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
+        "per_gemm": per_call,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shapes, g)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

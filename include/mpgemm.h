@@ -1,0 +1,157 @@
+/*
+ * mpgemm -- W4A16 mixed-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmpgemm.so.  Every call takes plain pointers and sizes; no framework types.
+ *
+ * Source: "LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind"
+ * (arXiv 2508.15601), abbreviated [TurboMind] below.  Its GEMM pipeline has two halves:
+ * offline weight packing (technique (i), "hardware-aware weight packing"; Fig. 6 and Fig. 7
+ * captions) and an online mixed-precision GEMM that turns the low-bit codes into 16-bit
+ * values in registers ("I2F" conversion and scaling; Fig. 4 and Fig. 6 captions) and
+ * overlaps that work with the matrix multiply (technique (iii); Fig. 9 caption).  This
+ * header exposes exactly that: mpgemm_pack_weights (offline), mpgemm_w4a16 (online) and
+ * mpgemm_unpack (the inverse of packing, for round-trip checks).
+ *
+ * ---------------------------------------------------------------------------------
+ * Quantized weights (the caller's unpacked form)
+ *   codes  uint8  [K][N] row-major, each an unsigned 4-bit integer q in 0..15
+ *   scales fp16   [K/g][N] row-major (IEEE binary16 bits), one per (group, column)
+ *   zeros  uint8  [K/g][N] row-major, each a 4-bit integer z in 0..15; or NULL for
+ *                 symmetric codes, whose zero is 8
+ *   A group is g consecutive rows of k: rows [r*g, (r+1)*g) share scale and zero row r.
+ *   Only the low 4 bits of codes and zeros are read (higher bits are ignored).
+ *   Dequantized weight: w[k][n] = (q[k][n] - z[k/g][n]) * s[k/g][n], rounded once
+ *   (round to nearest even) to the activation format.
+ *
+ * Packed layout, version 1 (MPGEMM_LAYOUT_VERSION)
+ *   Codes plane, K*N/2 bytes.  The code matrix is cut into tiles of 16 columns x 128 rows
+ *   of k.  Tile T = (n/16)*(K/128) + k/128 starts at byte T*1024, so the tiles of one
+ *   16-column strip follow each other along k.  Inside a tile, with kk = k%128 and
+ *   nn = n%16, the element belongs to lane L = nn + 16*((kk%32)/8) and word t = kk/32;
+ *   that little-endian 32-bit word is at byte L*16 + t*4.  Element i = kk%8 of the word
+ *   sits in nibble p(i) = i/2 (even i) or 4 + i/2 (odd i), i.e. the nibbles read
+ *   e7 e5 e3 e1 e6 e4 e2 e0 from most to least significant -- the interleave shown in
+ *   [TurboMind]'s diagram beside Fig. 24.
+ *   Why: lane L of a 64-lane wave fetches its 16 bytes of a tile with one 128-bit load; word
+ *   t is the A operand of the t-th 16x16x32 MFMA step for that lane (row nn, k = 8*(L/16)
+ *   .. 8*(L/16)+7); and (word >> 4j) & 0x000F000F puts elements (2j, 2j+1) in the low and
+ *   high halves of a 32-bit register, the order the MFMA operand register needs, so one
+ *   bitwise OR with the fp16 pattern of 1024 turns them into 1024+q without any shuffle
+ *   ([TurboMind], Fig. 6 caption: after I2F the data already match the MMA lane layout).
+ *   Meta plane.  Scales first: fp16 at element index e = (n/16)*(K/g)*16 + (k/g)*16 + n%16
+ *   ((K/g)*N*2 bytes; the scales of one strip are contiguous).  Then, for asymmetric codes
+ *   only, zeros: 4-bit values at the same index e, byte e/2, low nibble for even e and high
+ *   nibble for odd e ((K/g)*N/2 bytes).
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers (hipMalloc'd or equivalent) owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; argument validation happens synchronously, before anything is
+ *     enqueued, and on error nothing is enqueued.
+ *   - Return value: MPGEMM_OK or a negative mpgemm_status.  MPGEMM_ERR_HIP means the HIP
+ *     runtime rejected the launch (e.g. no gfx950 device); mpgemm_status_string() names it.
+ *   - Calls are reentrant; concurrent calls must not write overlapping outputs.
+ *   - Shape limits: K % 128 == 0, K % g == 0, g in {64, 128}, N % 16 == 0, M >= 0,
+ *     each of M*K, K*N and M*N below 2^31.  M == 0 or N == 0 is a valid no-op.
+ *   - Alignment: every device pointer 16-byte aligned (MPGEMM_ERR_ALIGNMENT otherwise).
+ */
+#ifndef MPGEMM_H
+#define MPGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MPGEMM_LAYOUT_VERSION 1
+
+typedef enum {
+    MPGEMM_OK = 0,
+    MPGEMM_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum value */
+    MPGEMM_ERR_UNSUPPORTED = -2,   /* shape or group size outside the limits above */
+    MPGEMM_ERR_ALIGNMENT = -3,     /* a device pointer is not 16-byte aligned */
+    MPGEMM_ERR_WORKSPACE = -4,     /* workspace smaller than mpgemm_workspace_bytes() */
+    MPGEMM_ERR_HIP = -5            /* the HIP runtime reported an error for the launch */
+} mpgemm_status;
+
+typedef enum {
+    MPGEMM_F16 = 0,                /* fp16 activations, fp16 output */
+    MPGEMM_BF16 = 1                /* bf16 activations, bf16 output (scales stay fp16) */
+} mpgemm_dtype;
+
+/* Layout version of the packed planes this library reads and writes. */
+int mpgemm_layout_version(void);
+
+/* Size of the packed codes plane: K*N/2 bytes.  0 if the shape is unsupported. */
+size_t mpgemm_packed_code_bytes(int K, int N);
+
+/* Size of the packed meta plane: (K/g)*N*2 + (symmetric ? 0 : (K/g)*N/2) bytes.
+ * 0 if the shape or group size is unsupported. */
+size_t mpgemm_packed_meta_bytes(int K, int N, int group, int symmetric);
+
+/*
+ * Offline packing [TurboMind, technique (i); Fig. 6 and Fig. 7 captions]: rewrites codes,
+ * scales and zeros (layouts above) into the version-1 packed planes.  zeros == NULL packs
+ * symmetric weights (zero 8) and writes no zero plane.  A pure bit permutation: lossless.
+ *   codes        in  [K][N] uint8
+ *   scales       in  [K/g][N] fp16 bits
+ *   zeros        in  [K/g][N] uint8, or NULL
+ *   packed_codes out mpgemm_packed_code_bytes(K, N) bytes
+ *   packed_meta  out mpgemm_packed_meta_bytes(K, N, group, zeros == NULL) bytes
+ */
+int mpgemm_pack_weights(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                        int K, int N, int group, void *packed_codes, void *packed_meta,
+                        void *stream);
+
+/*
+ * Exact inverse of mpgemm_pack_weights (codes come back in 0..15).  With symmetric != 0
+ * the meta plane has no zero plane and `zeros` is not written (may be NULL).
+ */
+int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int N, int group,
+                  int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                  void *stream);
+
+/* Device workspace mpgemm_w4a16 needs for this problem (currently always 0: the split-K
+ * reduction of the small-M kernels stays inside one workgroup). */
+size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype);
+
+/*
+ * Online mixed-precision GEMM [TurboMind, GEMM pipeline; Fig. 6 and Fig. 9 captions]:
+ *   Y[m][n] = sum_k X[m][k] * w[k][n],  w dequantized from the packed planes in registers,
+ *   products accumulated in fp32, Y rounded to the activation format (nearest even).
+ *   X            in  [M][K] row-major, fp16 or bf16 bits per `dtype`
+ *   packed_*     in  planes written by mpgemm_pack_weights for (K, N, group, symmetric)
+ *   Y            out [M][N] row-major, same format as X
+ *   workspace    in  mpgemm_workspace_bytes() bytes (may be NULL when that is 0)
+ * K == 0 writes zeros to Y.  The kernel is chosen by shape (see mpgemm_select_config).
+ */
+int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
+                 int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
+ * Kernel selection.  mpgemm_select_config returns the configuration mpgemm_w4a16 uses for
+ * a shape (a positive id); mpgemm_config_name describes an id ("" for unknown ids);
+ * mpgemm_w4a16_config runs one configuration explicitly (same contract as mpgemm_w4a16;
+ * config_id 0 means "select"; an id that cannot run the shape returns
+ * MPGEMM_ERR_UNSUPPORTED).  Ids: 1..4 small-M kernel with 1..4 row blocks of 16
+ * (M <= 16*id); 10 tiled large-M kernel.
+ */
+int mpgemm_select_config(int M, int N, int K, int group, int dtype);
+const char *mpgemm_config_name(int config_id);
+int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
+                        const void *packed_meta, int M, int N, int K, int group, int symmetric,
+                        void *Y, void *workspace, size_t workspace_bytes, int config_id,
+                        void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *mpgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPGEMM_H */

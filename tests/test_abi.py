@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/mpgemm.h declares, answers size queries, and rejects bad arguments before
+enqueueing anything (every case here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_quantized_mpgemm_amd as mp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpgemm.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN = 0, -1, -2, -3
+A = 0x10000          # a 16-byte-aligned fake device address; never dereferenced here
+MIS = 0x10008        # a misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpgemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("mpgemm_pack_weights", "mpgemm_w4a16", "mpgemm_unpack"):
+        assert must in names
+
+
+def test_library_exports_every_declared_function():
+    lib = mp.lib()
+    names = declared_functions()
+    assert set(names) == set(mp.SIGNATURES), "binding and header disagree"
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_layout_version_and_sizes():
+    lib = mp.lib()
+    assert lib.mpgemm_layout_version() == mp.LAYOUT_VERSION == 1
+    assert mp.packed_code_bytes(4096, 6144) == 4096 * 6144 // 2
+    assert mp.packed_meta_bytes(4096, 6144, 128, False) == 32 * 6144 * 2 + 32 * 6144 // 2
+    assert mp.packed_meta_bytes(5120, 10240, 64, True) == 80 * 10240 * 2
+    assert mp.packed_code_bytes(100, 16) == 0          # K % 128 != 0
+    assert mp.packed_meta_bytes(256, 24, 128, False) == 0   # N % 16 != 0
+    assert mp.packed_meta_bytes(256, 32, 32, False) == 0    # unsupported group
+    assert lib.mpgemm_workspace_bytes(16, 4096, 4096, 128, 0) == 0
+
+
+def test_status_strings():
+    lib = mp.lib()
+    for code, name in mp.STATUS.items():
+        assert lib.mpgemm_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.mpgemm_status_string(42)
+
+
+def test_selector_and_config_names():
+    assert mp.lib().mpgemm_select_config(1, 4096, 4096, 128, 0) == 1
+    assert mp.lib().mpgemm_select_config(16, 4096, 4096, 128, 0) == 1
+    assert mp.lib().mpgemm_select_config(17, 4096, 4096, 128, 0) == 2
+    assert mp.lib().mpgemm_select_config(64, 4096, 4096, 128, 1) == 4
+    assert mp.lib().mpgemm_select_config(65, 4096, 4096, 128, 0) == 10
+    assert mp.lib().mpgemm_select_config(2048, 4096, 4096, 128, 0) == 10
+    for cid in (1, 2, 3, 4, 10):
+        assert mp.config_name(cid)
+    assert mp.config_name(7) == ""
+
+
+def _gemm(X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, sym=0, Y=A, cfg=None):
+    lib = mp.lib()
+    args = [ctypes.c_void_p(X), dtype, ctypes.c_void_p(pc), ctypes.c_void_p(pm), M, N, K, g,
+            sym, ctypes.c_void_p(Y), None, 0]
+    if cfg is None:
+        return lib.mpgemm_w4a16(*args, None)
+    return lib.mpgemm_w4a16_config(*args, cfg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), INVALID),
+    (dict(sym=2), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(K=100), UNSUPPORTED),
+    (dict(K=384, g=256), UNSUPPORTED),
+    (dict(g=32), UNSUPPORTED),
+    (dict(N=24), UNSUPPORTED),
+    (dict(M=70000, K=65536), UNSUPPORTED),          # M*K beyond 2^31
+    (dict(X=0), INVALID),
+    (dict(pc=0), INVALID),
+    (dict(pm=0), INVALID),
+    (dict(Y=0), INVALID),
+    (dict(X=MIS), ALIGN),
+    (dict(Y=MIS), ALIGN),
+    (dict(pc=MIS), ALIGN),
+    (dict(pm=MIS), ALIGN),
+    (dict(cfg=7), INVALID),
+    (dict(cfg=1, M=17), UNSUPPORTED),
+    (dict(cfg=4, M=65), UNSUPPORTED),
+    (dict(M=0), OK),                                  # empty: a valid no-op, nothing enqueued
+    (dict(N=0), OK),
+    (dict(M=0, X=0, pc=0, pm=0, Y=0), OK),
+])
+def test_gemm_validation(kw, status):
+    assert _gemm(**kw) == status
+
+
+def test_pack_and_unpack_validation():
+    lib = mp.lib()
+    vp = ctypes.c_void_p
+    assert lib.mpgemm_pack_weights(None, vp(A), None, 256, 32, 128, vp(A), vp(A), None) == INVALID
+    assert lib.mpgemm_pack_weights(vp(A), vp(A), None, 200, 32, 128, vp(A), vp(A), None) == UNSUPPORTED
+    assert lib.mpgemm_pack_weights(vp(A), vp(A), None, 256, 32, 96, vp(A), vp(A), None) == UNSUPPORTED
+    assert lib.mpgemm_pack_weights(vp(A), vp(MIS), None, 256, 32, 128, vp(A), vp(A), None) == ALIGN
+    assert lib.mpgemm_pack_weights(vp(A), vp(A), vp(MIS), 256, 32, 128, vp(A), vp(A), None) == ALIGN
+    assert lib.mpgemm_pack_weights(None, None, None, 0, 32, 128, None, None, None) == OK
+    # asymmetric unpack needs somewhere to put the zeros
+    assert lib.mpgemm_unpack(vp(A), vp(A), 256, 32, 128, 0, vp(A), vp(A), None, None) == INVALID
+    assert lib.mpgemm_unpack(vp(A), vp(A), 256, 32, 128, 3, vp(A), vp(A), vp(A), None) == INVALID
+    assert lib.mpgemm_unpack(vp(A), vp(A), 256, 32, 128, 1, vp(MIS), vp(A), None, None) == ALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    codes = torch.zeros((256, 32), dtype=torch.uint8)
+    scales = torch.zeros((2, 32), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        mp.pack_weights(codes, scales, None, 128)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "weight_only_quantized_mpgemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "mpgemm_oracle" not in text, f

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, on seeded inputs.
+
+Bars (fixed before any kernel ran):
+  * packing, unpacking and dequantized weights: bit-exact;
+  * cases whose every partial sum is exact (identity / one-hot activations, small-integer
+    activations with power-of-two scales): bit-exact;
+  * random fp16/bf16 inputs: max|Y - Y_ref| / max|Y_ref| <= 5e-3 (relative to the largest
+    reference output), with Y_ref from the oracle on the same inputs.
+Full-size shapes compare sampled rows x columns (rows and columns of Y are independent, so
+the oracle computes just those); every kernel configuration is forced on every case it can
+run, not only the one the selector picks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_quantized_mpgemm_amd as mp
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 5e-3
+DECODE_CONFIGS = (1, 2, 3, 4)
+PREFILL = 10
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def configs_for(M):
+    return [c for c in DECODE_CONFIGS if M <= 16 * c] + [PREFILL]
+
+
+# ------------------------------------------------------------------------ transfer --
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_half(bits, dtype="f16"):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_f64(bits, dtype):
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def pack_case(case):
+    z = None if case["zeros"] is None else dev_u8(case["zeros"])
+    return mp.pack_weights(dev_u8(case["codes"]), dev_half(case["scales"]), z, case["group"])
+
+
+def rel_err(y_bits, ref_bits, dtype):
+    y = to_f64(y_bits, dtype)
+    r = to_f64(ref_bits, dtype)
+    assert np.isfinite(y).all()
+    return float(np.max(np.abs(y - r)) / max(np.max(np.abs(r)), 1e-30))
+
+
+def oracle_sample(case, rows, cols):
+    zeros = None if case["zeros"] is None else case["zeros"][:, cols]
+    return oracle.w4a16(case["x"][rows], case["codes"][:, cols], case["scales"][:, cols],
+                        zeros, case["group"], case["dtype"], threads=8)
+
+
+def run(case, packed, config=0, rows=None, cols=None):
+    """Y bits (or just Y[rows][:, cols], gathered on the GPU)."""
+    x = dev_half(case["x"], case["dtype"])
+    y = mp.w4a16(x, packed, config=config)
+    if rows is not None:
+        y = y[torch.as_tensor(rows, device="cuda")][:, torch.as_tensor(cols, device="cuda")]
+    torch.cuda.synchronize()
+    return host_bits(y.contiguous())
+
+
+# ------------------------------------------------------------------------- packing --
+
+@pytest.mark.parametrize("wl,K,N", [(workloads.TINY, 256, 256),
+                                    (workloads.LLAMA3_8B_DECODE, 4096, 6144),
+                                    (workloads.QWEN3_32B, 5120, 10240),
+                                    (workloads.LLAMA3_70B, 28672, 8192)])
+def test_pack_bytes_match_oracle_and_unpack_round_trips(wl, K, N):
+    say(f"pack {wl.name} K={K} N={N}")
+    case = workloads.make_case(wl, 1, K, N)
+    packed = pack_case(case)
+    torch.cuda.synchronize()
+    pc, pm = oracle.pack(case["codes"], case["scales"], case["zeros"], case["group"])
+    assert np.array_equal(packed.codes.cpu().numpy(), pc)
+    assert np.array_equal(packed.meta.cpu().numpy(), pm)
+    codes, scales, zeros = mp.unpack(packed)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), case["codes"])
+    assert np.array_equal(host_bits(scales), case["scales"])
+    if case["zeros"] is not None:
+        assert np.array_equal(zeros.cpu().numpy(), case["zeros"])
+    else:
+        assert zeros is None
+
+
+def test_unpack_of_oracle_packed_planes():
+    case = workloads.make_case(workloads.QWEN3_32B, 1, 512, 96)
+    pc, pm = oracle.pack(case["codes"], case["scales"], None, 64)
+    packed = mp.PackedWeights(dev_u8(pc), dev_u8(pm), 512, 96, 64, True)
+    codes, scales, _ = mp.unpack(packed)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), case["codes"])
+    assert np.array_equal(host_bits(scales), case["scales"])
+
+
+def test_pack_ignores_high_bits_of_codes_and_zeros():
+    case = workloads.make_case(workloads.TINY, 1, 256, 64)
+    noisy = dict(case, codes=case["codes"] | 0xA0, zeros=case["zeros"] | 0x50)
+    a = pack_case(case)
+    b = pack_case(noisy)
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.meta, b.meta)
+
+
+# -------------------------------------------------------------- bit-exact GEMM cases --
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("g,sym", [(128, False), (64, True)])
+def test_identity_activations_give_dequantized_weights_bit_exact(dtype, g, sym):
+    K, N = 256, 272                       # N = 256 + 16: a ragged last prefill block
+    say(f"identity dtype={dtype} g={g} sym={sym}")
+    codes, scales, zeros = workloads.weights(K, N, g, sym, 0.005, 0.02, 31)
+    one = 0x3C00 if dtype == "f16" else 0x3F80
+    eye = (np.eye(K, dtype=np.uint16) * one).astype(np.uint16)
+    case = dict(x=eye, codes=codes, scales=scales, zeros=zeros, group=g, dtype=dtype)
+    packed = pack_case(case)
+    w = oracle.dequant(codes, scales, zeros, g, dtype)
+    y = run(case, packed, PREFILL)
+    assert np.array_equal(y, w)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("config", DECODE_CONFIGS)
+def test_one_hot_rows_give_weight_rows_bit_exact(dtype, config):
+    K, N, g = 1024, 64, 128
+    M = 16 * config - 3                   # a ragged row block
+    say(f"one-hot dtype={dtype} config={config} M={M}")
+    codes, scales, zeros = workloads.weights(K, N, g, False, 0.005, 0.02, 32)
+    rng = np.random.default_rng(33)
+    picks = rng.choice(K, M, replace=False)
+    one = 0x3C00 if dtype == "f16" else 0x3F80
+    x = np.zeros((M, K), dtype=np.uint16)
+    x[np.arange(M), picks] = one
+    case = dict(x=x, codes=codes, scales=scales, zeros=zeros, group=g, dtype=dtype)
+    packed = pack_case(case)
+    w = oracle.dequant(codes, scales, zeros, g, dtype)
+    assert np.array_equal(run(case, packed, config), w[picks])
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 200])
+def test_integer_activations_power_of_two_scales_bit_exact(M):
+    """X in {-1,0,1}, s = 2^-6: every partial sum is exact in fp32, so Y is unique."""
+    K, N, g = 1024, 96, 128
+    rng = np.random.default_rng(34 + M)
+    x = rng.integers(-1, 2, (M, K)).astype(np.float16).view(np.uint16)
+    codes = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 16, (K // g, N), dtype=np.uint8)
+    scales = np.full((K // g, N), 2.0 ** -6, dtype=np.float16).view(np.uint16)
+    case = dict(x=x, codes=codes, scales=scales, zeros=zeros, group=g, dtype="f16")
+    packed = pack_case(case)
+    ref = oracle.w4a16(x, codes, scales, zeros, g)
+    for cfg in configs_for(M):
+        say(f"integer M={M} config={cfg}")
+        assert np.array_equal(run(case, packed, cfg), ref), cfg
+
+
+def test_doubling_scales_doubles_output_bit_exact():
+    case = workloads.make_case(workloads.LLAMA3_8B_DECODE, 16, 1024, 128)
+    doubled = dict(case, scales=(case["scales"].view(np.float16) * 2).view(np.uint16))
+    pa, pb = pack_case(case), pack_case(doubled)
+    for cfg in configs_for(16):
+        ya = run(case, pa, cfg).view(np.float16).astype(np.float64)
+        yb = run(doubled, pb, cfg).view(np.float16).astype(np.float64)
+        assert np.array_equal(yb, 2 * ya), cfg
+
+
+# ---------------------------------------------------------------- random parity -----
+
+@pytest.mark.parametrize("M", [1, 4, 16, 37, 64, 128, 300])
+def test_tiny_config_all_kernels(M):
+    """The tiny workload's weights (K=256, N=256) at several M, every kernel that fits."""
+    case = workloads.make_case(workloads.TINY, M, 256, 256)
+    packed = pack_case(case)
+    ref = oracle.w4a16(case["x"], case["codes"], case["scales"], case["zeros"], 128)
+    for cfg in configs_for(M):
+        say(f"tiny M={M} config={cfg}")
+        assert rel_err(run(case, packed, cfg), ref, "f16") <= REL_TOL, cfg
+
+
+def test_tiny_config_exact_shape_through_selector():
+    case = workloads.make_case(workloads.TINY, 4, 256, 256)
+    packed = pack_case(case)
+    ref = oracle.w4a16(case["x"], case["codes"], case["scales"], case["zeros"], 128)
+    err = rel_err(run(case, packed), ref, "f16")
+    say(f"tiny selector rel_err={err:.3e}")
+    assert err <= REL_TOL
+
+
+def _full_shape(wl, M, K, N, nrows=12, ncols=192, configs=None):
+    case = workloads.make_case(wl, M, K, N)
+    packed = pack_case(case)
+    rng = np.random.default_rng(case["seed"])
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, nrows), replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, ncols), replace=False)]))
+    ref = oracle_sample(case, rows, cols)
+    for cfg in (configs or [0]):
+        say(f"{wl.name} M={M} K={K} N={N} config={cfg or 'select'}")
+        y = run(case, packed, cfg, rows, cols)
+        err = rel_err(y, ref, case["dtype"])
+        assert err <= REL_TOL, (cfg, err)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+@pytest.mark.parametrize("K,N,label", workloads.LLAMA3_8B_SHAPES)
+def test_llama3_8b_decode_full_shapes(M, K, N, label):
+    _full_shape(workloads.LLAMA3_8B_DECODE, M, K, N)
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+@pytest.mark.parametrize("K,N,label", workloads.LLAMA3_8B_SHAPES)
+def test_llama3_8b_prefill_full_shapes(M, K, N, label):
+    _full_shape(workloads.LLAMA3_8B_PREFILL, M, K, N)
+
+
+@pytest.mark.parametrize("K,N,label", [(4096, 28672, "gate_up"), (14336, 4096, "down")])
+def test_llama3_8b_prefill_m8192(K, N, label):
+    _full_shape(workloads.LLAMA3_8B_PREFILL, 8192, K, N, nrows=8, ncols=96)
+
+
+@pytest.mark.parametrize("M", [1, 64])
+@pytest.mark.parametrize("K,N,label", workloads.LLAMA3_70B.shapes)
+def test_llama3_70b_bf16_small_m(M, K, N, label):
+    _full_shape(workloads.LLAMA3_70B, M, K, N, ncols=128)
+
+
+@pytest.mark.parametrize("K,N,label", [(8192, 57344, "gate_up"), (28672, 8192, "down")])
+def test_llama3_70b_bf16_m4096(K, N, label):
+    _full_shape(workloads.LLAMA3_70B, 4096, K, N, nrows=6, ncols=64)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 128, 1024])
+@pytest.mark.parametrize("K,N,label", workloads.QWEN3_32B.shapes)
+def test_qwen3_32b_sym_g64(M, K, N, label):
+    _full_shape(workloads.QWEN3_32B, M, K, N, ncols=128)
+
+
+def test_qwen3_32b_m8192_gate_up():
+    _full_shape(workloads.QWEN3_32B, 8192, 5120, 51200, nrows=6, ncols=64)
+
+
+# --------------------------------------------------------------------- edge cases ---
+
+def test_empty_m_is_a_no_op():
+    case = workloads.make_case(workloads.TINY, 1, 256, 256)
+    packed = pack_case(case)
+    x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    y = mp.w4a16(x, packed)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 256)
+
+
+def test_k_zero_writes_zeros():
+    packed = mp.PackedWeights(torch.empty(0, dtype=torch.uint8, device="cuda"),
+                              torch.empty(0, dtype=torch.uint8, device="cuda"), 0, 64, 128, True)
+    x = torch.empty((5, 0), dtype=torch.float16, device="cuda")
+    y = torch.full((5, 64), 7.0, dtype=torch.float16, device="cuda")
+    mp.w4a16(x, packed, out=y)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("M,N", [(5, 16), (17, 48), (129, 272), (250, 528)])
+def test_ragged_m_and_n(M, N):
+    case = workloads.make_case(workloads.TINY, M, 512, N)
+    packed = pack_case(case)
+    ref = oracle.w4a16(case["x"], case["codes"], case["scales"], case["zeros"], 128)
+    for cfg in configs_for(M):
+        say(f"ragged M={M} N={N} config={cfg}")
+        assert rel_err(run(case, packed, cfg), ref, "f16") <= REL_TOL, cfg
+
+
+def test_outputs_outside_y_are_untouched():
+    """Guard bands around Y stay intact (no stray stores past M or N)."""
+    M, K, N = 130, 256, 272
+    case = workloads.make_case(workloads.TINY, M, K, N)
+    packed = pack_case(case)
+    x = dev_half(case["x"])
+    for cfg in configs_for(M) + configs_for(5):
+        m = M if cfg == PREFILL else min(M, 16 * cfg)
+        buf = torch.full((m + 2, N), -3.0, dtype=torch.float16, device="cuda")
+        mp.w4a16(x[:m], packed, out=buf[1:m + 1], config=cfg)
+        torch.cuda.synchronize()
+        assert bool((buf[0] == -3).all()) and bool((buf[m + 1] == -3).all()), cfg
+
+
+def test_repeated_runs_are_bitwise_identical():
+    for M in (16, 256):
+        case = workloads.make_case(workloads.LLAMA3_8B_DECODE, M, 4096, 4096)
+        packed = pack_case(case)
+        a = run(case, packed)
+        b = run(case, packed)
+        assert np.array_equal(a, b)
+
+
+def test_nonfinite_inputs_propagate():
+    case = workloads.make_case(workloads.TINY, 16, 256, 64)
+    x = case["x"].copy()
+    x[3, 10] = 0x7C00          # +inf in row 3
+    case = dict(case, x=x)
+    packed = pack_case(case)
+    for cfg in configs_for(16):
+        y = run(case, packed, cfg).view(np.float16)
+        assert not np.isfinite(y[3]).any()
+        assert np.isfinite(np.delete(y, 3, axis=0)).all()

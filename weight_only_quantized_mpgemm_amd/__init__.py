@@ -1,0 +1,220 @@
+"""W4A16 mixed-precision GEMM for AMD MI355X (gfx950): thin Python binding of libmpgemm.
+
+Every step of the computation runs in the library's HIP kernels; this module only checks
+tensor properties, passes ``data_ptr()`` values and torch's current HIP stream through the
+C ABI declared in ``include/mpgemm.h``, and allocates outputs with torch.  There is no
+fallback: if ``libmpgemm.so`` is missing or the call fails, an exception is raised.
+
+Method: "LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind"
+(arXiv 2508.15601) -- offline packing of group-quantized 4-bit weights (technique (i)) and
+an online GEMM that dequantizes them in registers (I2F; Fig. 6 and Fig. 9 captions).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmpgemm.so")
+
+F16 = 0
+BF16 = 1
+LAYOUT_VERSION = 1
+
+STATUS = {
+    0: "MPGEMM_OK",
+    -1: "MPGEMM_ERR_INVALID_ARG",
+    -2: "MPGEMM_ERR_UNSUPPORTED",
+    -3: "MPGEMM_ERR_ALIGNMENT",
+    -4: "MPGEMM_ERR_WORKSPACE",
+    -5: "MPGEMM_ERR_HIP",
+}
+
+# Every function declared in include/mpgemm.h: name -> (restype, argtypes).
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "mpgemm_layout_version": (_i, []),
+    "mpgemm_packed_code_bytes": (_sz, [_i, _i]),
+    "mpgemm_packed_meta_bytes": (_sz, [_i, _i, _i, _i]),
+    "mpgemm_pack_weights": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "mpgemm_unpack": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "mpgemm_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "mpgemm_w4a16": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "mpgemm_select_config": (_i, [_i, _i, _i, _i, _i]),
+    "mpgemm_config_name": (ctypes.c_char_p, [_i]),
+    "mpgemm_w4a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
+                                 _vp]),
+    "mpgemm_status_string": (ctypes.c_char_p, [_i]),
+}
+
+
+class MpgemmError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = lib().mpgemm_status_string(status).decode()
+        super().__init__(f"{call} failed: {msg}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmpgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m weight_only_quantized_mpgemm_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise MpgemmError(status, call)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------- packed weights --
+
+@dataclasses.dataclass
+class PackedWeights:
+    """Layout-v1 planes of one [K, N] weight matrix (see include/mpgemm.h)."""
+    codes: torch.Tensor          # uint8 [K*N/2]
+    meta: torch.Tensor           # uint8 [(K/g)*N*2 (+ (K/g)*N/2 zeros)]
+    K: int
+    N: int
+    group: int
+    symmetric: bool
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.meta.numel()
+
+
+def packed_code_bytes(K: int, N: int) -> int:
+    return int(lib().mpgemm_packed_code_bytes(K, N))
+
+
+def packed_meta_bytes(K: int, N: int, group: int, symmetric: bool) -> int:
+    return int(lib().mpgemm_packed_meta_bytes(K, N, group, int(bool(symmetric))))
+
+
+def empty_packed(K: int, N: int, group: int, symmetric: bool,
+                 device="cuda") -> PackedWeights:
+    cb = packed_code_bytes(K, N)
+    mb = packed_meta_bytes(K, N, group, symmetric)
+    if K * N and (cb == 0 or mb == 0):
+        raise MpgemmError(-2, "empty_packed")
+    return PackedWeights(torch.empty(cb, dtype=torch.uint8, device=device),
+                         torch.empty(mb, dtype=torch.uint8, device=device),
+                         K, N, group, bool(symmetric))
+
+
+def pack_weights(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | None,
+                 group: int, out: PackedWeights | None = None) -> PackedWeights:
+    """Offline packing (mpgemm_pack_weights).
+
+    codes  uint8 [K, N] (values 0..15); scales float16 [K/g, N]; zeros uint8 [K/g, N]
+    (values 0..15) or None for symmetric codes with zero 8.
+    """
+    K, N = codes.shape
+    _need(codes, torch.uint8, (K, N), "codes")
+    if group <= 0 or K % group:
+        raise ValueError(f"K={K} is not a multiple of group={group}")
+    _need(scales, torch.float16, (K // group, N), "scales")
+    if zeros is not None:
+        _need(zeros, torch.uint8, (K // group, N), "zeros")
+    if out is None:
+        out = empty_packed(K, N, group, zeros is None, codes.device)
+    st = lib().mpgemm_pack_weights(_ptr(codes), _ptr(scales), _ptr(zeros), K, N, group,
+                                   _ptr(out.codes), _ptr(out.meta), _stream(codes.device))
+    _check(st, "mpgemm_pack_weights")
+    return out
+
+
+def unpack(packed: PackedWeights):
+    """Inverse of pack_weights (mpgemm_unpack): (codes, scales, zeros or None)."""
+    K, N, g = packed.K, packed.N, packed.group
+    dev = packed.codes.device
+    codes = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    scales = torch.empty((K // g, N), dtype=torch.float16, device=dev)
+    zeros = None if packed.symmetric else torch.empty((K // g, N), dtype=torch.uint8,
+                                                      device=dev)
+    st = lib().mpgemm_unpack(_ptr(packed.codes), _ptr(packed.meta), K, N, g,
+                             int(packed.symmetric), _ptr(codes), _ptr(scales), _ptr(zeros),
+                             _stream(dev))
+    _check(st, "mpgemm_unpack")
+    return codes, scales, zeros
+
+
+# ------------------------------------------------------------------------- the GEMM --
+
+def _act_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float16:
+        return F16
+    if dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"activations must be float16 or bfloat16, got {dtype}")
+
+
+def select_config(M: int, N: int, K: int, group: int, dtype: torch.dtype) -> int:
+    return int(lib().mpgemm_select_config(M, N, K, group, _act_code(dtype)))
+
+
+def config_name(config_id: int) -> str:
+    return lib().mpgemm_config_name(config_id).decode()
+
+
+def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
+          config: int = 0) -> torch.Tensor:
+    """Y = X @ dequant(W) (mpgemm_w4a16; mpgemm_w4a16_config when config != 0).
+
+    x float16 or bfloat16 [M, K]; returns (or fills `out`) [M, N] in the same format.
+    """
+    M, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"x has K={K}, weights have K={packed.K}")
+    act = _act_code(x.dtype)
+    _need(x, x.dtype, (M, K), "x")
+    N = packed.N
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _need(out, x.dtype, (M, N), "out")
+    ws = int(lib().mpgemm_workspace_bytes(M, N, K, packed.group, act))
+    workspace = torch.empty(ws, dtype=torch.uint8, device=x.device) if ws else None
+    args = (_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K, packed.group,
+            int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
+    if config:
+        st = lib().mpgemm_w4a16_config(*args, int(config), _stream(x.device))
+        _check(st, "mpgemm_w4a16_config")
+    else:
+        st = lib().mpgemm_w4a16(*args, _stream(x.device))
+        _check(st, "mpgemm_w4a16")
+    return out

@@ -1,0 +1,204 @@
+// C ABI of libmpgemm (declared and specified in include/mpgemm.h): argument validation,
+// kernel selection by shape, and dispatch to the gfx950 kernels.
+//
+// Source of the method: "LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind"
+// (arXiv 2508.15601): an offline packing step and an online mixed-precision GEMM.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/mpgemm.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kIndexLimit = (int64_t)1 << 31;
+
+enum ConfigId {
+    kConfigSelect = 0,
+    kConfigDecode1 = 1,
+    kConfigDecode2 = 2,
+    kConfigDecode3 = 3,
+    kConfigDecode4 = 4,
+    kConfigPrefill = 10,
+};
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int M, int N, int K, int group) {
+    if (M < 0 || N < 0 || K < 0) return MPGEMM_ERR_INVALID_ARG;
+    if (group != 64 && group != 128) return MPGEMM_ERR_UNSUPPORTED;
+    if (K % 128 != 0 || K % group != 0 || N % 16 != 0) return MPGEMM_ERR_UNSUPPORTED;
+    if ((int64_t)M * K >= kIndexLimit || (int64_t)K * N >= kIndexLimit ||
+        (int64_t)M * N >= kIndexLimit)
+        return MPGEMM_ERR_UNSUPPORTED;
+    return MPGEMM_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MPGEMM_OK;
+    if (getenv("MPGEMM_LOG")) fprintf(stderr, "mpgemm: HIP error %s\n", hipGetErrorString(e));
+    return MPGEMM_ERR_HIP;
+}
+
+// Small M streams the weights once (HBM-bound): the split-K strip kernel with one to four
+// row blocks of 16.  Larger M is bound by the matrix cores: the 128 x 256 tiled kernel.
+int select_config(int M) {
+    if (M <= 16) return kConfigDecode1;
+    if (M <= 32) return kConfigDecode2;
+    if (M <= 48) return kConfigDecode3;
+    if (M <= 64) return kConfigDecode4;
+    return kConfigPrefill;
+}
+
+int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
+              int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
+              size_t workspace_bytes, int config_id, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;   // no configuration uses a workspace (mpgemm_workspace_bytes is 0)
+    if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
+    if (symmetric != 0 && symmetric != 1) return MPGEMM_ERR_INVALID_ARG;
+    const int st = check_shape(M, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if (config_id != kConfigSelect &&
+        !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) ||
+          config_id == kConfigPrefill))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return MPGEMM_OK;
+    if (Y == nullptr) return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(Y)) return MPGEMM_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) return hip_status(mpgemm::launch_fill_zero((uint16_t *)Y, (size_t)M * N, s));
+    if (X == nullptr || packed_codes == nullptr || packed_meta == nullptr)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(packed_codes) || !aligned16(packed_meta))
+        return MPGEMM_ERR_ALIGNMENT;
+
+    const int cfg = config_id == kConfigSelect ? select_config(M) : config_id;
+    if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
+        return MPGEMM_ERR_UNSUPPORTED;
+
+    mpgemm::GemmArgs a;
+    a.X = (const uint16_t *)X;
+    a.codes = (const uint32_t *)packed_codes;
+    a.scales = (const uint16_t *)packed_meta;
+    a.zeros = symmetric ? nullptr : (const uint8_t *)packed_meta + (size_t)(K / group) * N * 2;
+    a.Y = (uint16_t *)Y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.group = group;
+    a.act = dtype == MPGEMM_BF16 ? mpgemm::kBF16 : mpgemm::kF16;
+    if (getenv("MPGEMM_LOG"))
+        fprintf(stderr, "mpgemm: M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", M, N, K, group,
+                dtype, symmetric, mpgemm_config_name(cfg));
+    if (cfg == kConfigPrefill) return hip_status(mpgemm::launch_prefill(a, s));
+    return hip_status(mpgemm::launch_decode(a, cfg, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpgemm_layout_version(void) { return MPGEMM_LAYOUT_VERSION; }
+
+size_t mpgemm_packed_code_bytes(int K, int N) {
+    if (check_shape(0, N, K, 128) != MPGEMM_OK && check_shape(0, N, K, 64) != MPGEMM_OK) return 0;
+    return (size_t)K * (size_t)N / 2;
+}
+
+size_t mpgemm_packed_meta_bytes(int K, int N, int group, int symmetric) {
+    if (check_shape(0, N, K, group) != MPGEMM_OK) return 0;
+    const size_t cells = (size_t)(K / group) * (size_t)N;
+    return cells * 2 + (symmetric ? 0 : cells / 2);
+}
+
+int mpgemm_pack_weights(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                        int K, int N, int group, void *packed_codes, void *packed_meta,
+                        void *stream) {
+    const int st = check_shape(0, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if ((size_t)K * N == 0) return MPGEMM_OK;
+    if (codes == nullptr || scales == nullptr || packed_codes == nullptr ||
+        packed_meta == nullptr)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)) ||
+        !aligned16(packed_codes) || !aligned16(packed_meta))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_pack(codes, scales, zeros, K, N, group, packed_codes,
+                                          packed_meta, (hipStream_t)stream));
+}
+
+int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int N, int group,
+                  int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                  void *stream) {
+    if (symmetric != 0 && symmetric != 1) return MPGEMM_ERR_INVALID_ARG;
+    const int st = check_shape(0, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if ((size_t)K * N == 0) return MPGEMM_OK;
+    if (packed_codes == nullptr || packed_meta == nullptr || codes == nullptr ||
+        scales == nullptr || (!symmetric && zeros == nullptr))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(packed_codes) || !aligned16(packed_meta) || !aligned16(codes) ||
+        !aligned16(scales) || (!symmetric && !aligned16(zeros)))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_unpack(packed_codes, packed_meta, K, N, group, symmetric,
+                                            codes, scales, zeros, (hipStream_t)stream));
+}
+
+size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
+    (void)M;
+    (void)N;
+    (void)K;
+    (void)group;
+    (void)dtype;
+    return 0;
+}
+
+int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
+                 int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    return gemm_impl(X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+                     workspace, workspace_bytes, kConfigSelect, stream);
+}
+
+int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
+                        const void *packed_meta, int M, int N, int K, int group, int symmetric,
+                        void *Y, void *workspace, size_t workspace_bytes, int config_id,
+                        void *stream) {
+    return gemm_impl(X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+                     workspace, workspace_bytes, config_id, stream);
+}
+
+int mpgemm_select_config(int M, int N, int K, int group, int dtype) {
+    (void)N;
+    (void)K;
+    (void)group;
+    (void)dtype;
+    return select_config(M < 0 ? 0 : M);
+}
+
+const char *mpgemm_config_name(int config_id) {
+    switch (config_id) {
+        case kConfigDecode1: return "decode_splitk_m16";
+        case kConfigDecode2: return "decode_splitk_m32";
+        case kConfigDecode3: return "decode_splitk_m48";
+        case kConfigDecode4: return "decode_splitk_m64";
+        case kConfigPrefill: return "prefill_tiled_128x256";
+        default: return "";
+    }
+}
+
+const char *mpgemm_status_string(int status) {
+    switch (status) {
+        case MPGEMM_OK: return "MPGEMM_OK";
+        case MPGEMM_ERR_INVALID_ARG: return "MPGEMM_ERR_INVALID_ARG: null pointer, negative size or bad enum";
+        case MPGEMM_ERR_UNSUPPORTED: return "MPGEMM_ERR_UNSUPPORTED: shape or group size outside the supported limits";
+        case MPGEMM_ERR_ALIGNMENT: return "MPGEMM_ERR_ALIGNMENT: a device pointer is not 16-byte aligned";
+        case MPGEMM_ERR_WORKSPACE: return "MPGEMM_ERR_WORKSPACE: workspace too small";
+        case MPGEMM_ERR_HIP: return "MPGEMM_ERR_HIP: the HIP runtime reported an error";
+        default: return "unknown mpgemm status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,197 @@
+// Device-side building blocks shared by the gfx950 kernels of libmpgemm.
+//
+// Source: "LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind"
+// (arXiv 2508.15601), abbreviated [TurboMind].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpgemm {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+enum Act { kF16 = 0, kBF16 = 1 };
+
+// Packed layout v1 (include/mpgemm.h): 16 columns x 128 k per 1 KiB tile, 16 bytes per lane.
+constexpr int kTileK = 128;
+constexpr int kTileN = 16;
+constexpr int kTileWords = 256;  // 32-bit words per tile
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From &v) {
+    static_assert(sizeof(To) == sizeof(From), "bitcast size");
+    return __builtin_bit_cast(To, v);
+}
+
+// ---------------------------------------------------------------- I2F dequantization --
+//
+// [TurboMind, Fig. 6 caption and the interleave diagram beside Fig. 24]: a packed word
+// holds elements e0..e7 of one column at nibbles (LSB first) e0 e2 e4 e6 e1 e3 e5 e7, so
+// "isolate" with the mask 0x000F000F leaves e0 in the low and e1 in the high half of a
+// 32-bit register -- the (k, k+1) register order of the MFMA operand.  OR-ing the fp16
+// pattern 0x6400 (1024.0, spacing 1) into each half turns a 4-bit q into 1024 + q exactly.
+// The next nibble pair (e2, e3) sits 4 bits higher; OR-ing 0x5400 (64.0, spacing 1/16)
+// reads it as 64 + q exactly, so it needs no shift.  One 8-bit shift exposes (e4, e5) and
+// (e6, e7) the same way: four isolate-and-combine operations and one shift per 8 weights.
+
+// v_and_or_b32 with the mask in a scalar and the OR pattern in a vector register: VOP3 on
+// gfx9 takes no literal and reads at most one scalar register, and the compiler otherwise
+// splits this into two literal-carrying VOP2 operations.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(bits));
+    return r;
+}
+
+// fp16 path: w = fp16_rne((q - z) * s).  (B + q) + (-(B + z)) is exact (an integer of
+// magnitude <= 15, B = 1024 or 64), then one packed multiply by s rounds once, to nearest
+// even.  nz_hi2 / nz_lo2: half2 bits of -(1024 + z) / -(64 + z); s2: half2 bits of s.
+__device__ __forceinline__ u32x4_t dequant_word_f16(uint32_t w, uint32_t nz_hi2,
+                                                    uint32_t nz_lo2, uint32_t s2) {
+    const uint32_t w8 = w >> 8;
+    u32x4_t h;
+    h[0] = and_or(w, 0x000F000Fu, 0x64006400u);    // e0, e1 -> 1024 + q
+    h[1] = and_or(w, 0x00F000F0u, 0x54005400u);    // e2, e3 ->   64 + q
+    h[2] = and_or(w8, 0x000F000Fu, 0x64006400u);   // e4, e5 -> 1024 + q
+    h[3] = and_or(w8, 0x00F000F0u, 0x54005400u);   // e6, e7 ->   64 + q
+    const half2_t s = bitcast<half2_t>(s2);
+    u32x4_t r;
+    r[0] = bitcast<uint32_t>((bitcast<half2_t>(h[0]) + bitcast<half2_t>(nz_hi2)) * s);
+    r[1] = bitcast<uint32_t>((bitcast<half2_t>(h[1]) + bitcast<half2_t>(nz_lo2)) * s);
+    r[2] = bitcast<uint32_t>((bitcast<half2_t>(h[2]) + bitcast<half2_t>(nz_hi2)) * s);
+    r[3] = bitcast<uint32_t>((bitcast<half2_t>(h[3]) + bitcast<half2_t>(nz_lo2)) * s);
+    return r;
+}
+
+// bf16 path: w = bf16_rne((q - z) * s) with s in fp16.  The nibbles are spread to bytes
+// and converted to fp32 (v_cvt_f32_ubyteN); q*s + (-z*s) is exact in fp32 (every term is
+// an integer below 16 times an 11-bit significand), and the final conversion to bf16 is
+// the single rounding.  Byte order after the spread: lo = e0 e4 e1 e5, hi = e2 e6 e3 e7.
+//   s: the scale in fp32; nzs: -z * s in fp32 (exact).
+__device__ __forceinline__ float ubyte(uint32_t v, int b) {
+    return (float)((v >> (8 * b)) & 0xFFu);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo;
+    const __bf16 b = (__bf16)hi;
+    return (uint32_t)bitcast<uint16_t>(a) | ((uint32_t)bitcast<uint16_t>(b) << 16);
+}
+__device__ __forceinline__ u32x4_t dequant_word_bf16(uint32_t w, float s, float nzs) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+    const float e0 = __builtin_fmaf(ubyte(lo, 0), s, nzs);
+    const float e4 = __builtin_fmaf(ubyte(lo, 1), s, nzs);
+    const float e1 = __builtin_fmaf(ubyte(lo, 2), s, nzs);
+    const float e5 = __builtin_fmaf(ubyte(lo, 3), s, nzs);
+    const float e2 = __builtin_fmaf(ubyte(hi, 0), s, nzs);
+    const float e6 = __builtin_fmaf(ubyte(hi, 1), s, nzs);
+    const float e3 = __builtin_fmaf(ubyte(hi, 2), s, nzs);
+    const float e7 = __builtin_fmaf(ubyte(hi, 3), s, nzs);
+    u32x4_t r;
+    r[0] = pack_bf16x2(e0, e1);
+    r[1] = pack_bf16x2(e2, e3);
+    r[2] = pack_bf16x2(e4, e5);
+    r[3] = pack_bf16x2(e6, e7);
+    return r;
+}
+
+// Per-(group, column) dequantization constants in the form each path wants.
+struct DqF16 {
+    uint32_t nz_hi2, nz_lo2, s2;
+};
+struct DqBF16 {
+    float s, nzs;
+};
+
+__device__ __forceinline__ DqF16 make_dq_f16(uint16_t s_bits, uint32_t z) {
+    // -(1024 + z): sign, exponent of 1024 (0x6400), fraction z (spacing 1).
+    // -(64 + z):   sign, exponent of 64 (0x5400), fraction 16 z (spacing 1/16).
+    const uint32_t nh = 0xE400u | z;
+    const uint32_t nl = 0xD400u | (z << 4);
+    DqF16 d;
+    d.nz_hi2 = nh | (nh << 16);
+    d.nz_lo2 = nl | (nl << 16);
+    d.s2 = (uint32_t)s_bits | ((uint32_t)s_bits << 16);
+    return d;
+}
+__device__ __forceinline__ DqBF16 make_dq_bf16(uint16_t s_bits, uint32_t z) {
+    DqBF16 d;
+    d.s = (float)bitcast<_Float16>(s_bits);
+    d.nzs = -(float)z * d.s;     // exact: 4-bit integer times 11-bit significand
+    return d;
+}
+
+template <int ACT>
+struct Dq;
+template <>
+struct Dq<kF16> {
+    typedef DqF16 type;
+    static __device__ __forceinline__ DqF16 make(uint16_t s, uint32_t z) { return make_dq_f16(s, z); }
+    static __device__ __forceinline__ u32x4_t word(uint32_t w, const DqF16 &d) {
+        return dequant_word_f16(w, d.nz_hi2, d.nz_lo2, d.s2);
+    }
+};
+template <>
+struct Dq<kBF16> {
+    typedef DqBF16 type;
+    static __device__ __forceinline__ DqBF16 make(uint16_t s, uint32_t z) { return make_dq_bf16(s, z); }
+    static __device__ __forceinline__ u32x4_t word(uint32_t w, const DqBF16 &d) {
+        return dequant_word_bf16(w, d.s, d.nzs);
+    }
+};
+
+// ------------------------------------------------------------------------------ MFMA --
+//
+// v_mfma_f32_16x16x32_{f16,bf16}: D[i][j] += sum_k A[i][k] * B[k][j] over a 16x16x32
+// block.  Operand lane l holds A row (l % 16) / B column (l % 16) at k = 8*(l/16) .. +7 as
+// four 32-bit registers of (k, k+1) pairs; the fp32 result lane l holds D[4*(l/16) + r]
+// [l % 16] in register r.  The kernels put dequantized weights in A (rows = n) and
+// activations in B (columns = m), so lane l ends with four consecutive n of one row m.
+template <int ACT>
+__device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t &a, const u32x4_t &b, f32x4_t c);
+template <>
+__device__ __forceinline__ f32x4_t mfma16x16x32<kF16>(const u32x4_t &a, const u32x4_t &b,
+                                                      f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(a), bitcast<half8_t>(b), c,
+                                                  0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4_t mfma16x16x32<kBF16>(const u32x4_t &a, const u32x4_t &b,
+                                                       f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b),
+                                                   c, 0, 0, 0);
+}
+
+// fp32 -> activation format, round to nearest even; four values packed into 8 bytes.
+template <int ACT>
+__device__ __forceinline__ u32x2_t round4(const f32x4_t &v);
+template <>
+__device__ __forceinline__ u32x2_t round4<kF16>(const f32x4_t &v) {
+    u32x2_t r;
+    r[0] = (uint32_t)bitcast<uint16_t>((_Float16)v[0]) |
+           ((uint32_t)bitcast<uint16_t>((_Float16)v[1]) << 16);
+    r[1] = (uint32_t)bitcast<uint16_t>((_Float16)v[2]) |
+           ((uint32_t)bitcast<uint16_t>((_Float16)v[3]) << 16);
+    return r;
+}
+template <>
+__device__ __forceinline__ u32x2_t round4<kBF16>(const f32x4_t &v) {
+    u32x2_t r;
+    r[0] = pack_bf16x2(v[0], v[1]);
+    r[1] = pack_bf16x2(v[2], v[3]);
+    return r;
+}
+
+// Meta plane readers (layout v1): strip-major scales, then 4-bit zeros at the same index.
+__device__ __forceinline__ uint32_t read_zero(const uint8_t *zeros, size_t e) {
+    const uint32_t b = zeros[e >> 1];
+    return (e & 1) ? (b >> 4) : (b & 0xFu);
+}
+
+}  // namespace mpgemm

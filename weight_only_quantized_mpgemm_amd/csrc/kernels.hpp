@@ -1,0 +1,42 @@
+// Host-side launchers of the gfx950 kernels; the C ABI (api.hip) validates arguments and
+// calls these.  Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace mpgemm {
+
+hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                       int K, int N, int group, void *packed_codes, void *packed_meta,
+                       hipStream_t stream);
+
+hipError_t launch_unpack(const void *packed_codes, const void *packed_meta, int K, int N,
+                         int group, int symmetric, uint8_t *codes, uint16_t *scales,
+                         uint8_t *zeros, hipStream_t stream);
+
+// Arguments of one GEMM; planes as written by launch_pack.
+struct GemmArgs {
+    const uint16_t *X;          // [M][K] activation bits
+    const uint32_t *codes;      // packed codes plane
+    const uint16_t *scales;     // meta plane: scales
+    const uint8_t *zeros;       // meta plane: zeros (nullptr when symmetric)
+    uint16_t *Y;                // [M][N] output bits
+    int M, N, K, group;
+    int act;                    // Act
+};
+
+// Small-M kernel: one 16-column strip per workgroup, the K range split over the waves of the
+// workgroup, `mblocks` row blocks of 16 (M <= 16 * mblocks, mblocks in 1..4).
+hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
+
+// Tiled large-M kernel (128 rows x 256 columns per workgroup).
+hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
+
+// Writes zeros to Y (the K == 0 case).
+hipError_t launch_fill_zero(uint16_t *Y, size_t count, hipStream_t stream);
+
+}  // namespace mpgemm
