@@ -72,6 +72,9 @@ def main():
     ap.add_argument("--pool-gb", type=float, default=1.5,
                     help="size of the rotating pool of packed weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy, whose HBM "
+                         "counter readings scale the counter-based traffic figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would "
@@ -87,6 +90,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)       # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
     wl = workloads.LLAMA3_8B_DECODE
     shapes = wl.shapes
     g = wl.group

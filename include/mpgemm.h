@@ -53,7 +53,7 @@
  *     runtime rejected the launch (e.g. no gfx950 device); mpgemm_status_string() names it.
  *   - Calls are reentrant; concurrent calls must not write overlapping outputs.
  *   - Shape limits: K % 128 == 0, K % g == 0, g in {64, 128}, N % 16 == 0, M >= 0,
- *     each of M*K, K*N and M*N below 2^31.  M == 0 or N == 0 is a valid no-op.
+ *     (M+128)*K, K*N and M*N each below 2^31.  M == 0 or N == 0 is a valid no-op.
  *   - Alignment: every device pointer 16-byte aligned (MPGEMM_ERR_ALIGNMENT otherwise).
  */
 #ifndef MPGEMM_H

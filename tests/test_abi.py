@@ -86,6 +86,7 @@ def _gemm(X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, sym=0, Y=A, cfg=N
     (dict(g=32), UNSUPPORTED),
     (dict(N=24), UNSUPPORTED),
     (dict(M=70000, K=65536), UNSUPPORTED),          # M*K beyond 2^31
+    (dict(M=16384 - 128, K=131072), UNSUPPORTED),    # (M+128)*K at 2^31
     (dict(X=0), INVALID),
     (dict(pc=0), INVALID),
     (dict(pm=0), INVALID),

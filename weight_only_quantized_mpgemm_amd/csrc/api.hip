@@ -29,7 +29,8 @@ int check_shape(int M, int N, int K, int group) {
     if (M < 0 || N < 0 || K < 0) return MPGEMM_ERR_INVALID_ARG;
     if (group != 64 && group != 128) return MPGEMM_ERR_UNSUPPORTED;
     if (K % 128 != 0 || K % group != 0 || N % 16 != 0) return MPGEMM_ERR_UNSUPPORTED;
-    if ((int64_t)M * K >= kIndexLimit || (int64_t)K * N >= kIndexLimit ||
+    // Kernels address planes with 32-bit byte offsets, including one-past-the-end rows.
+    if ((int64_t)(M + 128) * K >= kIndexLimit || (int64_t)K * N >= kIndexLimit ||
         (int64_t)M * N >= kIndexLimit)
         return MPGEMM_ERR_UNSUPPORTED;
     return MPGEMM_OK;

@@ -194,4 +194,29 @@ __device__ __forceinline__ uint32_t read_zero(const uint8_t *zeros, size_t e) {
     return (e & 1) ? (b >> 4) : (b & 0xFu);
 }
 
+// ------------------------------------------------------------------- buffer loads --
+//
+// The GEMM kernels read through buffer resources: one 128-bit scalar descriptor per plane,
+// a 32-bit per-lane byte offset that stays fixed across the K loop, and a wave-uniform
+// scalar offset that advances it.  This keeps address arithmetic out of the vector ALU and
+// out of vector registers.  A lane whose own offset lies past the descriptor's byte count
+// reads zeros without touching memory (gfx9 raw-buffer range check), which the kernels use
+// for rows past M.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    // Third descriptor dword of gfx9-family raw buffers (32-bit data format, no swizzle).
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2_t buf_load_b64(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 }  // namespace mpgemm

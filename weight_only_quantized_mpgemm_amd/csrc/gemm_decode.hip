@@ -2,119 +2,241 @@
 //
 // [TurboMind, GEMM pipeline; Fig. 6 and Fig. 9 captions]: the packed 4-bit weights are
 // loaded straight into registers, turned into 16-bit values by I2F conversion and scaling,
-// and fed to the matrix cores while the next tiles' loads are in flight.  Source: "LMDeploy
+// and fed to the matrix cores while later tiles' loads are in flight.  Source: "LMDeploy
 // Accelerates Mixed-Precision LLM Inference with TurboMind" (arXiv 2508.15601).
 //
 // At M <= 64 the GEMM is bound by HBM bandwidth: every weight byte is read once and used
 // for at most M multiply-adds.  Design for MI355X:
-//   - one workgroup per 16-column strip; its NW waves split the strip's K range into
-//     contiguous slices (split-K inside the workgroup), so even N = 4096 gives 256
-//     workgroups x 8 waves and every CU has several KiB of weight loads in flight;
-//   - each lane fetches its 16 bytes of a 1 KiB tile with one 128-bit load (a wave reads
-//     1 KiB contiguously); U tiles are requested before any is used;
-//   - weights are the MFMA A operand (rows = n), activations the B operand (columns = m),
-//     read as one 16-byte row chunk per lane from L2 (they are small and shared by all
-//     workgroups);
-//   - the NW partial sums meet in LDS and are added in a fixed wave order, so results are
-//     deterministic; no global workspace and no atomics.
+//   - a workgroup owns S adjacent 16-column strips; its NW waves split the K range into
+//     contiguous slices (split-K inside the workgroup).  The host picks S and NW by shape
+//     (pick_split below);
+//   - each wave runs a D-slot register pipeline over its K slice: slot s holds, for one
+//     128-deep tile step, the S weight tiles (one 128-bit load per lane and strip; a wave
+//     reads 1 KiB contiguously per strip), the activation fragments of that step (shared by
+//     the S strips) and the raw scales/zeros; computing slot s is followed by refilling it
+//     with the step D positions later, so D steps are always in flight.  The loop body has
+//     no branches; refills past the slice are clamped onto its last step (cache hits) and a
+//     short tail computes the remaining slots;
+//   - all loads are buffer loads: fixed per-lane offsets, a wave-uniform scalar offset per
+//     step.  Activation rows past M fall outside the activation descriptor and read as
+//     zero without any memory traffic, so M = 1 moves 1/16 of a full row block;
+//   - weights are the MFMA A operand (rows = n), activations the B operand (columns = m);
+//   - the NW partial sums meet in LDS and are added in a fixed wave order: results are
+//     deterministic, with no global workspace and no atomics.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "kernels.hpp"
 
 namespace mpgemm {
 
 namespace {
 
-constexpr int kDecodeWaves = 8;
+constexpr int kMaxWaves = 8;
 
-template <int ACT, int MB, bool SYM, int G, int NW, int U>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(
+template <int MB, int S, int GPT>
+struct Slot {
+    u32x4_t w[S];              // per strip: 16 bytes of the packed tile = 4 MFMA k-steps
+    u32x4_t x[4][MB];          // activation B operands per k-step and row block
+    uint32_t s[S][GPT];        // dword holding the lane's fp16 scale, per strip and group
+    uint32_t z[S][GPT];        // dword holding the lane's 4-bit zero, per strip and group
+};
+
+template <int ACT, int MB, int S, bool SYM, int G, int D>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     uint16_t *__restrict__ Y) {
     constexpr int GPT = kTileK / G;              // groups per 128-k tile (1 or 2)
-    typedef typename Dq<ACT>::type DqT;
+    typedef Slot<MB, S, GPT> SlotT;
+    extern __shared__ f32x4_t red[];             // [NW][S][MB][64]
 
-    const int strip = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
+    const int NW = blockDim.x >> 6;
+    // The wave index is uniform across the wave; saying so keeps the K-slice bounds, the
+    // loop counter and every per-step scalar offset in scalar registers (otherwise each
+    // buffer load would be wrapped in a loop over distinct offsets).
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int KT = K >> 7;
     const int t_begin = (KT * wave) / NW;
-    const int t_end = (KT * (wave + 1)) / NW;
+    const int n = (KT * (wave + 1)) / NW - t_begin;
     const int groups = K / G;
+    const int strips = N >> 4;
+    const int strip0 = blockIdx.x * S;
 
-    const u32x4_t *tiles =
-        reinterpret_cast<const u32x4_t *>(codes) + (size_t)strip * KT * 64 + lane;
-    const size_t meta_lane = (size_t)strip * groups * 16 + (lane & 15);
-    const int mrow = lane & 15;
-    const int ksub = (lane >> 4) * 8;
+    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024));
+    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
+    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / 2));
 
-    f32x4_t acc[MB];
+    // Per-lane byte offsets, fixed for the whole K slice.  Strips past N read the last real
+    // strip (their outputs are never stored).  The meta element of a lane's column is a
+    // multiple of 16 plus lane % 16, so its scale is half (lane & 1) of a dword and its zero
+    // is nibble (lane & 7) of a dword.
+    uint32_t woff[S], soff[S], zoff[S];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int si = 0; si < S; ++si) {
+        const uint32_t strip = (uint32_t)min(strip0 + si, strips - 1);
+        woff[si] = (strip * KT + t_begin) * 1024u + lane * 16u;
+        const uint32_t e = strip * groups * 16u + t_begin * GPT * 16u + (lane & 15);
+        soff[si] = (e >> 1) * 4u;
+        zoff[si] = (e >> 3) * 4u;
+    }
+    uint32_t xoff[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        xoff[mb] = ((uint32_t)(mb * 16 + (lane & 15)) * K + t_begin * kTileK + (lane >> 4) * 8) * 2u;
+    const uint32_t sshift = (lane & 1) * 16;
+    const uint32_t zshift = (lane & 7) * 4;
 
-    for (int t0 = t_begin; t0 < t_end; t0 += U) {
-        u32x4_t w[U];
-        DqT dq[U][GPT];
+    auto load = [&](SlotT &sl, int i) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = t0 + u;
-            if (t < t_end) {
-                w[u] = tiles[(size_t)t * 64];
+        for (int si = 0; si < S; ++si) sl.w[si] = buf_load_b128(wrs, woff[si], i * 1024);
 #pragma unroll
-                for (int h = 0; h < GPT; ++h) {
-                    const size_t e = meta_lane + (size_t)(t * GPT + h) * 16;
-                    const uint32_t z = SYM ? 8u : read_zero(zeros, e);
-                    dq[u][h] = Dq<ACT>::make(scales[e], z);
-                }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                sl.x[j][mb] = buf_load_b128(xrs, xoff[mb], (i * kTileK + 32 * j) * 2);
+#pragma unroll
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int h = 0; h < GPT; ++h) {
+                sl.s[si][h] = buf_load_b32(srs, soff[si], (i * GPT + h) * 32);
+                sl.z[si][h] = SYM ? 0u : buf_load_b32(zrs, zoff[si], (i * GPT + h) * 8);
+            }
+    };
+
+    f32x4_t acc[S][MB];
+#pragma unroll
+    for (int si = 0; si < S; ++si)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[si][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const SlotT &sl) {
+        typename Dq<ACT>::type dq[S][GPT];
+#pragma unroll
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int h = 0; h < GPT; ++h)
+                dq[si][h] = Dq<ACT>::make((uint16_t)(sl.s[si][h] >> sshift),
+                                          SYM ? 8u : ((sl.z[si][h] >> zshift) & 0xFu));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int si = 0; si < S; ++si) {
+                const u32x4_t a = Dq<ACT>::word(sl.w[si][j], dq[si][(j * 32) / G]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[si][mb] = mfma16x16x32<ACT>(a, sl.x[j][mb], acc[si][mb]);
+            }
+    };
+
+    if (n > 0) {
+        SlotT slot[D];
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            load(slot[s], min(s, n - 1));
+            __builtin_amdgcn_sched_barrier(0);   // same load order as the loop's refills
+        }
+        const int n_main = n - n % D;
+        for (int base = 0; base < n_main; base += D) {
+#pragma unroll
+            for (int s = 0; s < D; ++s) {
+                // The barriers pin the order compute(s), refill(s), compute(s+1), ...: the
+                // scheduler would otherwise sink every refill to the end of the batch and
+                // the next batch would wait for all of them at once.
+                compute(slot[s]);
+                __builtin_amdgcn_sched_barrier(0);
+                load(slot[s], min(base + D + s, n - 1));
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        const int rest = n - n_main;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = t0 + u;
-            if (t < t_end) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32x4_t a = Dq<ACT>::word(w[u][j], dq[u][(j * 32) / G]);
-                    const int k = t * kTileK + 32 * j + ksub;
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        // Rows past M read the last real row: their products land in
-                        // output columns that are never stored.
-                        const int m = min(mb * 16 + mrow, M - 1);
-                        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k);
-                        acc[mb] = mfma16x16x32<ACT>(a, b, acc[mb]);
-                    }
-                }
-            }
-        }
+        for (int s = 0; s < D - 1; ++s)
+            if (s < rest) compute(slot[s]);
     }
 
-    __shared__ f32x4_t red[NW * MB * 64];
+    const int col_lane = 4 * (lane >> 4);
+    if (NW == 1) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[(wave * MB + mb) * 64 + lane] = acc[mb];
+        for (int si = 0; si < S; ++si) {
+            if (strip0 + si >= strips) continue;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = mb * 16 + (lane & 15);
+                if (m < M)
+                    *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + (strip0 + si) * 16 + col_lane) =
+                        round4<ACT>(acc[si][mb]);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int si = 0; si < S; ++si)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[((wave * S + si) * MB + mb) * 64 + lane] = acc[si][mb];
     __syncthreads();
-    for (int mb = wave; mb < MB; mb += NW) {
-        f32x4_t s = red[mb * 64 + lane];
-        for (int w2 = 1; w2 < NW; ++w2) s += red[(w2 * MB + mb) * 64 + lane];
-        const int m = mb * 16 + mrow;
-        if (m < M) {
-            const int n = strip * 16 + 4 * (lane >> 4);
-            *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + n) = round4<ACT>(s);
+    for (int b = wave; b < S * MB; b += NW) {
+        const int si = b / MB, mb = b % MB;
+        f32x4_t sum = red[b * 64 + lane];
+        for (int w2 = 1; w2 < NW; ++w2) sum += red[(w2 * S * MB + b) * 64 + lane];
+        const int m = mb * 16 + (lane & 15);
+        if (m < M && strip0 + si < strips)
+            *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + (strip0 + si) * 16 + col_lane) =
+                round4<ACT>(sum);
+    }
+}
+
+// Strips per workgroup (S) and waves per workgroup (NW).  S > 1 lets one activation
+// fragment feed S strips (less L1/L2 traffic per weight byte); NW splits K inside the
+// workgroup.  Measured on MI355X at the Llama-3-8B projection shapes: each wave does best
+// with a K slice of about 8 tile steps or more (a deep enough register pipeline), and with
+// the largest S that still leaves >= 128 workgroups.  MPGEMM_DECODE_SPLIT="S,NW" overrides
+// the choice for tuning sweeps (S in {1,2,4} with one row block, {1,2} with two, 1 above;
+// NW in 1..8).
+struct Split {
+    int s, nw;
+};
+Split pick_split(int strips, int KT, int mblocks) {
+    Split sp{1, 1};
+    if (mblocks == 1) sp.s = strips >= 1024 ? 4 : (strips >= 256 && KT <= 64 ? 2 : 1);
+    else if (mblocks == 2) sp.s = strips >= 512 ? 2 : 1;
+    sp.nw = KT / 8;
+    if (sp.nw < 1) sp.nw = 1;
+    if (sp.nw > kMaxWaves) sp.nw = kMaxWaves;
+    if (const char *env = getenv("MPGEMM_DECODE_SPLIT")) {
+        int s = 0, nw = 0;
+        if (sscanf(env, "%d,%d", &s, &nw) == 2 && (s == 1 || s == 2 || s == 4) && nw >= 1 &&
+            nw <= kMaxWaves && nw <= KT && (s == 1 || mblocks <= 2) && (s < 4 || mblocks == 1)) {
+            sp.s = s;
+            sp.nw = nw;
         }
     }
+    return sp;
+}
+
+template <int ACT, int MB, int S, bool SYM, int G>
+void launch_s(const GemmArgs &a, int nw, hipStream_t stream) {
+    constexpr int slot_regs = S * 4 + 16 * MB + 2 * S;
+    constexpr int D = slot_regs <= 24 ? 4 : (slot_regs <= 40 ? 3 : 2);
+    const int strips = a.N >> 4;
+    const int wgs = (strips + S - 1) / S;
+    const size_t lds = nw > 1 ? (size_t)nw * S * MB * 64 * sizeof(f32x4_t) : 0;
+    decode_kernel<ACT, MB, S, SYM, G, D><<<dim3(wgs), dim3(nw * 64), lds, stream>>>(
+        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
 }
 
 template <int ACT, int MB, bool SYM, int G>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    constexpr int NW = kDecodeWaves;
-    const int KT = a.K >> 7;
-    const dim3 grid(a.N >> 4), block(NW * 64);
-    if (KT >= 8 * NW) {
-        decode_kernel<ACT, MB, SYM, G, NW, 8><<<grid, block, 0, stream>>>(
-            a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
-    } else {
-        decode_kernel<ACT, MB, SYM, G, NW, 4><<<grid, block, 0, stream>>>(
-            a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
+    const Split sp = pick_split(a.N >> 4, a.K >> 7, MB);
+    if constexpr (MB == 1) {
+        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G>(a, sp.nw, stream);
     }
+    if constexpr (MB <= 2) {
+        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G>(a, sp.nw, stream);
+    }
+    launch_s<ACT, MB, 1, SYM, G>(a, sp.nw, stream);
 }
 
 template <int ACT, int MB>

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     uint16_t *__restrict__ Y) {
     typedef typename Dq<ACT>::type DqT;
+    constexpr int GPT = kTileK / G;               // groups per 128-k tile (1 or 2)
     __shared__ u32x4_t xs[2][kXChunks];
 
     const int tid = threadIdx.x;
@@ -46,21 +47,41 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int lane = tid & 63;
     const int m_blk = blockIdx.y * kBM;
     const int KT = K >> 7;
-    const int steps = K / kBK;
     const int groups = K / G;
     const int strips = N >> 4;
     const int strip0 = blockIdx.x * (kBN / 16) + wave * 4;
 
-    // Loads never branch: rows past M and strips past N are clamped onto the last real
-    // ones.  The products they feed land only in accumulators that are never stored
-    // (row m of Y depends on row m of X alone, strip s on strip s of W alone).
+    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024));
+    const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
+    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / 2));
+
+    // Per-thread byte offsets, fixed for the whole K loop (a wave-uniform scalar offset
+    // advances them).  Activation rows past M point one row past the end of X and read as
+    // zero; strips past N read the last real strip.  Their products land only in
+    // accumulators that are never stored (row m of Y depends on row m of X alone, strip s
+    // on strip s of W alone).  A lane's meta element is a multiple of 16 plus lane % 16,
+    // so its scale is half (lane & 1) of a dword and its zero nibble (lane & 7) of a dword.
+    uint32_t xoff[kXLoads];
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+        const int c = tid + kThreads * i;
+        const uint32_t row = (uint32_t)min(m_blk + c / kChunksPerRow, M);
+        xoff[i] = (row * K + (c % kChunksPerRow) * 8) * 2u;
+    }
     bool valid[4];
-    size_t wstrip[4];
+    uint32_t woff[4], soff[4], zoff[4];
 #pragma unroll
     for (int si = 0; si < 4; ++si) {
         valid[si] = (strip0 + si) < strips;
-        wstrip[si] = (size_t)min(strip0 + si, strips - 1);
+        const uint32_t strip = (uint32_t)min(strip0 + si, strips - 1);
+        woff[si] = strip * KT * 1024u + lane * 16u;
+        const uint32_t e = strip * groups * 16u + (lane & 15);
+        soff[si] = (e >> 1) * 4u;
+        zoff[si] = (e >> 3) * 4u;
     }
+    const uint32_t sshift = (lane & 1) * 16;
+    const uint32_t zshift = (lane & 7) * 4;
 
     f32x4_t acc[4][8];
 #pragma unroll
@@ -68,16 +89,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) acc[si][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto load_x = [&](int step, u32x4_t(&xr)[kXLoads]) {
-        const int k0 = step * kBK;
+    // X stage: one 64-deep half of a 128-deep tile.
+    auto load_x = [&](int half_step, u32x4_t(&xr)[kXLoads]) {
 #pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / kChunksPerRow;
-            const int ch = c % kChunksPerRow;
-            const int m = min(m_blk + r, M - 1);
-            xr[i] = *reinterpret_cast<const u32x4_t *>(X + (size_t)m * K + k0 + ch * 8);
-        }
+        for (int i = 0; i < kXLoads; ++i) xr[i] = buf_load_b128(xrs, xoff[i], half_step * kBK * 2);
     };
     auto store_x = [&](int buf, const u32x4_t(&xr)[kXLoads]) {
 #pragma unroll
@@ -88,76 +103,87 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
             xs[buf][r * kChunksPerRow + (ch ^ (r & 7))] = xr[i];
         }
     };
-    // Raw scale bits and zero byte are kept as loaded; the dequantization constants are
-    // formed only when the step that needs them starts, so nothing waits on the loads early.
-    // The zero's nibble (element index e odd/even) is the lane's n parity: e%2 == lane%2.
-    const uint32_t zshift = (lane & 1) * 4;
-    auto load_w = [&](int step, u32x2_t(&wr)[4], uint32_t(&sr)[4], uint32_t(&zr)[4]) {
-        const int k0 = step * kBK;
-        const int tile = k0 >> 7;
-        const int word0 = (k0 & 127) >> 5;            // 0 or 2
-        const int grp = k0 / G;
+    // Weights and raw meta of one 128-deep tile: 16 bytes per lane per strip.
+    auto load_w = [&](int t, u32x4_t(&wr)[4], uint32_t(&sr)[4][GPT], uint32_t(&zr)[4][GPT]) {
 #pragma unroll
         for (int si = 0; si < 4; ++si) {
-            const size_t strip = wstrip[si];
-            wr[si] = *reinterpret_cast<const u32x2_t *>(
-                codes + (strip * KT + tile) * kTileWords + lane * 4 + word0);
-            const size_t e = strip * groups * 16 + (size_t)grp * 16 + (lane & 15);
-            sr[si] = scales[e];
-            zr[si] = SYM ? 0u : zeros[e >> 1];
+            wr[si] = buf_load_b128(wrs, woff[si], t * 1024);
+#pragma unroll
+            for (int h = 0; h < GPT; ++h) {
+                sr[si][h] = buf_load_b32(srs, soff[si], (t * GPT + h) * 32);
+                zr[si][h] = SYM ? 0u : buf_load_b32(zrs, zoff[si], (t * GPT + h) * 8);
+            }
         }
     };
-    auto make_dq = [&](const uint32_t(&sr)[4], const uint32_t(&zr)[4], DqT(&dq)[4]) {
-#pragma unroll
-        for (int si = 0; si < 4; ++si)
-            dq[si] = Dq<ACT>::make((uint16_t)sr[si], SYM ? 8u : ((zr[si] >> zshift) & 0xFu));
-    };
-
-    u32x4_t xr[kXLoads];
-    u32x2_t wcur[4], wnext[4];
-    uint32_t scur[4], snext[4], zcur[4], znext[4];
-
-    load_x(0, xr);
-    store_x(0, xr);
-    load_w(0, wcur, scur, zcur);
-    __syncthreads();
-
-    // The loop body is one basic block (no data-dependent branches), which keeps the
-    // accumulators in place across iterations.  The last step prefetches a redundant copy
-    // of itself into the idle buffer instead of branching.
-    for (int step = 0; step < steps; ++step) {
-        const int buf = step & 1;
-        const int next = min(step + 1, steps - 1);
-        load_x(next, xr);
-        load_w(next, wnext, snext, znext);
-        // Keep the next step's loads ahead of this step's MFMAs: they then have a whole
-        // step of matrix work to arrive in.
-        __builtin_amdgcn_sched_barrier(0);
-        DqT dcur[4];
-        make_dq(scur, zcur, dcur);
+    // 64-deep half `half` of the current tile from LDS buffer `buf`.
+    auto compute_half = [&](int buf, int half, const u32x4_t(&wr)[4], const DqT(&dq)[4][GPT]) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            u32x4_t a[4];
-#pragma unroll
-            for (int si = 0; si < 4; ++si) a[si] = Dq<ACT>::word(wcur[si][s], dcur[si]);
+            const int word = half * 2 + s;
+            // All eight activation operands of this 32-deep step are requested first; the
+            // dequantization below then covers their LDS latency.
+            u32x4_t b[8];
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
                 const int r = mb * 16 + (lane & 15);
                 const int c = s * 4 + (lane >> 4);
-                const u32x4_t b = xs[buf][r * kChunksPerRow + (c ^ (r & 7))];
-#pragma unroll
-                for (int si = 0; si < 4; ++si) acc[si][mb] = mfma16x16x32<ACT>(a[si], b, acc[si][mb]);
+                b[mb] = xs[buf][r * kChunksPerRow + (c ^ (r & 7))];
             }
-        }
-        store_x(buf ^ 1, xr);
+            u32x4_t a[4];
 #pragma unroll
-        for (int si = 0; si < 4; ++si) {
-            wcur[si] = wnext[si];
-            scur[si] = snext[si];
-            zcur[si] = znext[si];
+            for (int si = 0; si < 4; ++si) a[si] = Dq<ACT>::word(wr[si][word], dq[si][(word * 32) / G]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int si = 0; si < 4; ++si) acc[si][mb] = mfma16x16x32<ACT>(a[si], b[mb], acc[si][mb]);
         }
+    };
+
+    // Weight/meta registers ping-pong between two sets (tile t computes from one set while
+    // tile t+1 is loaded into the other), so nothing is copied between iterations.
+    struct WSet {
+        u32x4_t w[4];
+        uint32_t s[4][GPT], z[4][GPT];
+    };
+    u32x4_t xr[kXLoads];
+    WSet set0, set1;
+
+    // Tile t: compute from `cur` while `nxt` receives tile tn.  Its two 64-deep halves use
+    // the two LDS buffers; every iteration ends with the X stage of tile tn in buffer 0.
+    auto tile = [&](int t, int tn, const WSet &cur, WSet &nxt) {
+        load_x(2 * t + 1, xr);
+        load_w(tn, nxt.w, nxt.s, nxt.z);
+        __builtin_amdgcn_sched_barrier(0);       // next loads go out before this tile's MFMAs
+        DqT dq[4][GPT];
+#pragma unroll
+        for (int si = 0; si < 4; ++si)
+#pragma unroll
+            for (int h = 0; h < GPT; ++h)
+                dq[si][h] = Dq<ACT>::make((uint16_t)(cur.s[si][h] >> sshift),
+                                          SYM ? 8u : ((cur.z[si][h] >> zshift) & 0xFu));
+        compute_half(0, 0, cur.w, dq);
+        store_x(1, xr);
         __syncthreads();
+        load_x(2 * tn, xr);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(1, 1, cur.w, dq);
+        store_x(0, xr);
+        __syncthreads();
+    };
+
+    load_x(0, xr);
+    store_x(0, xr);
+    load_w(0, set0.w, set0.s, set0.z);
+    __syncthreads();
+
+    // The loop body is one basic block; past the last tile the prefetches clamp onto it.
+    int t = 0;
+    for (; t + 1 < KT; t += 2) {
+        tile(t, t + 1, set0, set1);
+        tile(t + 1, min(t + 2, KT - 1), set1, set0);
     }
+    if (t < KT) tile(t, t, set0, set1);
 
 #pragma unroll
     for (int si = 0; si < 4; ++si) {
