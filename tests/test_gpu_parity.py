@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 
 REL_TOL = 5e-3
 DECODE_CONFIGS = (1, 2, 3, 4)
-PREFILL = 10
+PREFILL = 10          # LDS-ring kernel (two-buffer kernel when K % 256 != 0)
+PREFILL_2BUF = 11
 
 
 def say(msg):
@@ -30,7 +31,7 @@ def say(msg):
 
 
 def configs_for(M):
-    return [c for c in DECODE_CONFIGS if M <= 16 * c] + [PREFILL]
+    return [c for c in DECODE_CONFIGS if M <= 16 * c] + [PREFILL, PREFILL_2BUF]
 
 
 # ------------------------------------------------------------------------ transfer --

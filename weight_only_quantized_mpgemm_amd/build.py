@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmpgemm.so")
-SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_ring.hip"]
 HEADERS = ["device.hpp", "kernels.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

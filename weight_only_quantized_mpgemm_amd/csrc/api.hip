@@ -20,7 +20,8 @@ enum ConfigId {
     kConfigDecode2 = 2,
     kConfigDecode3 = 3,
     kConfigDecode4 = 4,
-    kConfigPrefill = 10,
+    kConfigPrefill = 10,       // LDS-ring kernel when K % 256 == 0, else the two-buffer one
+    kConfigPrefill2Buf = 11,   // two-buffer kernel
 };
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -63,7 +64,7 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     if (st != MPGEMM_OK) return st;
     if (config_id != kConfigSelect &&
         !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) ||
-          config_id == kConfigPrefill))
+          config_id == kConfigPrefill || config_id == kConfigPrefill2Buf))
         return MPGEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MPGEMM_OK;
     if (Y == nullptr) return MPGEMM_ERR_INVALID_ARG;
@@ -93,7 +94,9 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     if (getenv("MPGEMM_LOG"))
         fprintf(stderr, "mpgemm: M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", M, N, K, group,
                 dtype, symmetric, mpgemm_config_name(cfg));
-    if (cfg == kConfigPrefill) return hip_status(mpgemm::launch_prefill(a, s));
+    if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
+    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf)
+        return hip_status(mpgemm::launch_prefill(a, s));
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
 
@@ -185,7 +188,8 @@ const char *mpgemm_config_name(int config_id) {
         case kConfigDecode2: return "decode_splitk_m32";
         case kConfigDecode3: return "decode_splitk_m48";
         case kConfigDecode4: return "decode_splitk_m64";
-        case kConfigPrefill: return "prefill_tiled_128x256";
+        case kConfigPrefill: return "prefill_ring_128x256";
+        case kConfigPrefill2Buf: return "prefill_2buf_128x256";
         default: return "";
     }
 }

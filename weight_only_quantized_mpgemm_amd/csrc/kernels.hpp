@@ -33,7 +33,9 @@ struct GemmArgs {
 // workgroup, `mblocks` row blocks of 16 (M <= 16 * mblocks, mblocks in 1..4).
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
 
-// Tiled large-M kernel (128 rows x 256 columns per workgroup).
+// Tiled large-M kernels (128 rows x 256 columns per workgroup): the LDS-ring kernel
+// (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
+hipError_t launch_prefill_ring(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
 // Writes zeros to Y (the K == 0 case).
