@@ -9,13 +9,23 @@ larger than the 256 MB Infinity Cache, so weight bytes come from HBM, not from a
 the previous call warmed.
 
 Prints one JSON line: value = whole-step TFLOP/s (2*M*N*K summed over the twelve GEMMs,
-divided by the step time), plus HBM GB/s of algorithmic bytes, a per-GEMM breakdown, the
-roofline of the dominant kernel (hipEvents around each of its launches, on the stream the
-library launches on), and the CPU oracle timed on a bounded sample (cpu_baseline).
+divided by the step time), plus HBM GB/s of algorithmic bytes, the roofline of the dominant
+kernel, a per-GEMM breakdown and the CPU oracle timed on a bounded sample (cpu_baseline).
+
+Kernel durations come from hipEvents recorded, inside the timed steps, on the stream the
+library launches on, around each run of consecutive launches of one kernel (the four GEMMs of
+one M), divided by the launches in it; so per-launch event overhead does not inflate short
+decode kernels.  The per-GEMM breakdown is a separate pass after the timed steps (ten
+back-to-back launches per GEMM between one pair of events).  `traffic` is the HBM bytes per
+launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters read for the dominant kernel,
+scaled by what the same counters read for a plain 1 GiB copy (--copy-calibration); it is
+taken from the summary file under profiles/ and reported only while the kernel sources
+still hash to the digest recorded there, else null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +38,39 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 MS = (1, 16, 2048)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_llama3_8b_m1_16_2048_hbm_traffic.txt")
+
+
+def kernel_source_digest():
+    """sha256 (16 hex digits) over the HIP sources and the build flags of the library."""
+    pkg = os.path.join(ROOT, "weight_only_quantized_mpgemm_amd")
+    csrc = os.path.join(pkg, "csrc")
+    h = hashlib.sha256()
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
+             if f.endswith((".hip", ".hpp"))] + [os.path.join(pkg, "build.py")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """{(kernel, M, K, N): scaled HBM bytes per launch} from the counter summary, or {} when
+    the file is absent or was taken from other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    table, digest = {}, None
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("# source_digest:"):
+                digest = line.split(":", 1)[1].strip()
+            elif line.strip() and not line.startswith("#"):
+                f = line.split()
+                if f[0] == "kernel":
+                    continue
+                table[(f[0], int(f[1]), int(f[2]), int(f[3]))] = float(f[6])
+    return table if digest == kernel_source_digest() else {}
 
 
 def gemm_bytes(M, K, N, g, symmetric=False):
@@ -44,7 +87,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(shapes, group, m_rows=16):
+def cpu_baseline(shapes, group, m_rows=32):
     """The oracle, as it stands, on M = m_rows rows of every shape (full N)."""
     import oracle
     import workloads
@@ -72,6 +115,8 @@ def main():
     ap.add_argument("--pool-gb", type=float, default=1.5,
                     help="size of the rotating pool of packed weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-gemm", action="store_true",
+                    help="skip the per-GEMM breakdown pass (counter runs use this)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose HBM "
                          "counter readings scale the counter-based traffic figures")
@@ -129,22 +174,31 @@ def main():
 
     calls = [(M, K, N, label) for M in MS for K, N, label in shapes]
     cfg_of = {c: mp.select_config(c[0], c[2], c[1], g, torch.float16) for c in calls}
-    events = {c: [] for c in calls}
     stream = torch.cuda.current_stream(dev)
+    # runs of consecutive launches of one kernel at one M within a step: (kernel, [calls])
+    runs, run_starts = [], set()
+    for i, c in enumerate(calls):
+        name = mp.config_name(cfg_of[c])
+        if runs and runs[-1][0] == name and runs[-1][1][-1][0] == c[0]:
+            runs[-1][1].append(c)
+        else:
+            runs.append((name, [c]))
+            run_starts.add(i)
+    run_events = []
+    shape_idx = {(K, N): j for j, (K, N, _) in enumerate(shapes)}
 
     def step(s, record):
-        for mi, M in enumerate(MS):
-            pk = pool[(s * len(MS) + mi) % copies]
-            for j, (K, N, label) in enumerate(shapes):
-                c = (M, K, N, label)
-                if record:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                mp.w4a16(xs[(M, K)], pk[j], out=ys[(M, N)])
-                if record:
-                    e1.record(stream)
-                    events[c].append((e0, e1))
+        evs = []
+        for i, (M, K, N, label) in enumerate(calls):
+            pk = pool[(s * len(MS) + MS.index(M)) % copies]
+            if record and i in run_starts:
+                evs.append(torch.cuda.Event(enable_timing=True))
+                evs[-1].record(stream)
+            mp.w4a16(xs[(M, K)], pk[shape_idx[(K, N)]], out=ys[(M, N)])
+        if record:
+            evs.append(torch.cuda.Event(enable_timing=True))
+            evs[-1].record(stream)
+            run_events.append(evs)
 
     for s in range(args.warmup):
         step(s, record=False)
@@ -159,36 +213,61 @@ def main():
     step_flops = sum(gemm_flops(M, K, N) for M, K, N, _ in calls)
     step_bytes = sum(gemm_bytes(M, K, N, g) for M, K, N, _ in calls)
 
-    per_call, per_cfg = [], {}
-    for c in calls:
-        M, K, N, label = c
-        durs = [a.elapsed_time(b) * 1e-3 for a, b in events[c]]
-        t = float(np.mean(durs))
-        fl, by = gemm_flops(M, K, N), gemm_bytes(M, K, N, g)
-        bound = "hbm" if M <= 64 else "mfma"
-        frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
-            (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
-        cfg = mp.config_name(cfg_of[c])
-        per_call.append({"M": M, "K": K, "N": N, "layer": label, "kernel": cfg,
-                         "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
-                         "gbps": round(by / t / 1e9, 1), "bound": bound, "frac": round(frac, 4)})
-        agg = per_cfg.setdefault(cfg, {"t": 0.0, "flops": 0, "bytes": 0, "n": 0, "bound": bound})
+    # per kernel: total event time over the timed steps, launches, flops and bytes
+    per_cfg = {}
+    for r, (name, rcalls) in enumerate(runs):
+        t = sum(evs[r].elapsed_time(evs[r + 1]) * 1e-3 for evs in run_events)
+        agg = per_cfg.setdefault(name, {"t": 0.0, "flops": 0, "bytes": 0, "n": 0, "calls": [],
+                                        "bound": "hbm" if rcalls[0][0] <= 64 else "mfma"})
         agg["t"] += t
-        agg["flops"] += fl
-        agg["bytes"] += by
-        agg["n"] += 1
+        agg["n"] += len(rcalls) * args.steps
+        agg["flops"] += sum(gemm_flops(M, K, N) for M, K, N, _ in rcalls) * args.steps
+        agg["bytes"] += sum(gemm_bytes(M, K, N, g) for M, K, N, _ in rcalls) * args.steps
+        agg["calls"] += rcalls
+
+    traffic = load_traffic()
 
     def roofline(cfg):
         a = per_cfg[cfg]
+        avg_launch_s = a["t"] / a["n"]
+        tr = [traffic.get((cfg, M, K, N)) for M, K, N, _ in a["calls"]]
+        tr = round(sum(tr) / len(tr)) if tr and None not in tr else None
+        common = {"kernel": cfg, "launches_per_step": a["n"] // args.steps,
+                  "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                  "algorithmic_bytes_per_launch": round(a["bytes"] / a["n"]),
+                  "algorithmic_flops_per_launch": round(a["flops"] / a["n"])}
         if a["bound"] == "mfma":
             ach = a["flops"] / a["t"] / 1e12
             return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                    "traffic": None, "kernel": cfg, "launches_per_step": a["n"]}
+                    "traffic": tr, **common}
         ach = a["bytes"] / a["t"] / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": cfg, "launches_per_step": a["n"]}
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": tr,
+                **common}
+
+    per_call = []
+    if not args.no_per_gemm:
+        reps = 10
+        for ci, c in enumerate(calls):
+            M, K, N, label = c
+            j = shape_idx[(K, N)]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for r in range(reps):
+                mp.w4a16(xs[(M, K)], pool[(ci * reps + r) % copies][j], out=ys[(M, N)])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            fl, by = gemm_flops(M, K, N), gemm_bytes(M, K, N, g)
+            bound = "hbm" if M <= 64 else "mfma"
+            frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
+                (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
+            per_call.append({"M": M, "K": K, "N": N, "layer": label,
+                             "kernel": mp.config_name(cfg_of[c]), "us": round(t * 1e6, 2),
+                             "tflops": round(fl / t / 1e12, 2), "gbps": round(by / t / 1e9, 1),
+                             "bound": bound, "frac": round(frac, 4)})
 
     dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
@@ -212,6 +291,7 @@ def main():
         "roofline": roofline(dominant),
         "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
         "per_gemm": per_call,
+        "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, g)

@@ -45,12 +45,12 @@ int hip_status(hipError_t e) {
 
 // Small M streams the weights once (HBM-bound): the split-K strip kernel with one to four
 // row blocks of 16.  Larger M is bound by the matrix cores: the 128 x 256 tiled kernel.
-int select_config(int M) {
+int select_config(int M, int K) {
     if (M <= 16) return kConfigDecode1;
     if (M <= 32) return kConfigDecode2;
     if (M <= 48) return kConfigDecode3;
     if (M <= 64) return kConfigDecode4;
-    return kConfigPrefill;
+    return K % 256 == 0 ? kConfigPrefill : kConfigPrefill2Buf;
 }
 
 int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
@@ -76,7 +76,7 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     if (!aligned16(X) || !aligned16(packed_codes) || !aligned16(packed_meta))
         return MPGEMM_ERR_ALIGNMENT;
 
-    const int cfg = config_id == kConfigSelect ? select_config(M) : config_id;
+    const int cfg = config_id == kConfigSelect ? select_config(M, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
 
@@ -176,10 +176,9 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {
     (void)N;
-    (void)K;
     (void)group;
     (void)dtype;
-    return select_config(M < 0 ? 0 : M);
+    return select_config(M < 0 ? 0 : M, K);
 }
 
 const char *mpgemm_config_name(int config_id) {
