@@ -138,9 +138,10 @@ int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void 
  * mpgemm_w4a16_config runs one configuration explicitly (same contract as mpgemm_w4a16;
  * config_id 0 means "select"; an id that cannot run the shape returns
  * MPGEMM_ERR_UNSUPPORTED).  Ids: 1..4 small-M kernel with 1..4 row blocks of 16
- * (M <= 16*id); 10 tiled large-M kernel with a four-stage LDS ring (K % 256 == 0; run
- * explicitly on another K, id 10 runs as id 11); 11 tiled large-M kernel with two LDS
- * buffers (any K).  The selector picks 1..4 for M <= 64, else 10 when K % 256 == 0, else 11.
+ * (M <= 16*id); 10 tiled large-M kernel on 16x16x32 MFMAs with a four-stage LDS ring;
+ * 11 tiled large-M kernel with two LDS buffers (any K); 12 tiled large-M kernel on 32x32x16
+ * MFMAs with a four-stage LDS ring.  Ids 10 and 12 need K % 256 == 0 and run as id 11 on
+ * other K.  The selector picks 1..4 for M <= 64, else 12 when K % 256 == 0, else 11.
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);

@@ -61,11 +61,11 @@ def test_selector_and_config_names():
     assert mp.lib().mpgemm_select_config(16, 4096, 4096, 128, 0) == 1
     assert mp.lib().mpgemm_select_config(17, 4096, 4096, 128, 0) == 2
     assert mp.lib().mpgemm_select_config(64, 4096, 4096, 128, 1) == 4
-    assert mp.lib().mpgemm_select_config(65, 4096, 4096, 128, 0) == 10
-    assert mp.lib().mpgemm_select_config(2048, 4096, 4096, 128, 0) == 10
+    assert mp.lib().mpgemm_select_config(65, 4096, 4096, 128, 0) == 12
+    assert mp.lib().mpgemm_select_config(2048, 4096, 4096, 128, 0) == 12
     assert mp.lib().mpgemm_select_config(2048, 4096, 4224, 128, 0) == 11   # K % 256 != 0
     assert mp.lib().mpgemm_select_config(64, 4096, 4224, 128, 0) == 4
-    for cid in (1, 2, 3, 4, 10, 11):
+    for cid in (1, 2, 3, 4, 10, 11, 12):
         assert mp.config_name(cid)
     assert mp.config_name(7) == ""
 

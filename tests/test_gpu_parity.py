@@ -22,8 +22,9 @@ pytestmark = pytest.mark.gpu
 
 REL_TOL = 5e-3
 DECODE_CONFIGS = (1, 2, 3, 4)
-PREFILL = 10          # LDS-ring kernel (two-buffer kernel when K % 256 != 0)
+PREFILL = 10          # 16x16x32 LDS-ring kernel (two-buffer kernel when K % 256 != 0)
 PREFILL_2BUF = 11
+PREFILL_X32 = 12      # 32x32x16 kernel (two-buffer kernel when K % 256 != 0)
 
 
 def say(msg):
@@ -31,7 +32,7 @@ def say(msg):
 
 
 def configs_for(M):
-    return [c for c in DECODE_CONFIGS if M <= 16 * c] + [PREFILL, PREFILL_2BUF]
+    return [c for c in DECODE_CONFIGS if M <= 16 * c] + [PREFILL, PREFILL_2BUF, PREFILL_X32]
 
 
 # ------------------------------------------------------------------------ transfer --
@@ -128,18 +129,19 @@ def test_pack_ignores_high_bits_of_codes_and_zeros():
 
 # -------------------------------------------------------------- bit-exact GEMM cases --
 
+@pytest.mark.parametrize("config", [PREFILL, PREFILL_2BUF, PREFILL_X32])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("g,sym", [(128, False), (64, True)])
-def test_identity_activations_give_dequantized_weights_bit_exact(dtype, g, sym):
+def test_identity_activations_give_dequantized_weights_bit_exact(dtype, g, sym, config):
     K, N = 256, 272                       # N = 256 + 16: a ragged last prefill block
-    say(f"identity dtype={dtype} g={g} sym={sym}")
+    say(f"identity dtype={dtype} g={g} sym={sym} config={config}")
     codes, scales, zeros = workloads.weights(K, N, g, sym, 0.005, 0.02, 31)
     one = 0x3C00 if dtype == "f16" else 0x3F80
     eye = (np.eye(K, dtype=np.uint16) * one).astype(np.uint16)
     case = dict(x=eye, codes=codes, scales=scales, zeros=zeros, group=g, dtype=dtype)
     packed = pack_case(case)
     w = oracle.dequant(codes, scales, zeros, g, dtype)
-    y = run(case, packed, PREFILL)
+    y = run(case, packed, config)
     assert np.array_equal(y, w)
 
 

@@ -18,12 +18,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmpgemm.so")
-SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_ring.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_ring.hip",
+           "gemm_prefill_x32.hip"]
 HEADERS = ["device.hpp", "kernels.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
+FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 

@@ -7,7 +7,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include "../../include/mpgemm.h"
+#include "mpgemm.h"
 #include "kernels.hpp"
 
 namespace {
@@ -20,8 +20,9 @@ enum ConfigId {
     kConfigDecode2 = 2,
     kConfigDecode3 = 3,
     kConfigDecode4 = 4,
-    kConfigPrefill = 10,       // LDS-ring kernel when K % 256 == 0, else the two-buffer one
+    kConfigPrefill = 10,       // 16x16x32 LDS-ring kernel when K % 256 == 0, else two-buffer
     kConfigPrefill2Buf = 11,   // two-buffer kernel
+    kConfigPrefillX32 = 12,    // 32x32x16 kernel when K % 256 == 0, else the two-buffer one
 };
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -50,7 +51,7 @@ int select_config(int M, int K) {
     if (M <= 32) return kConfigDecode2;
     if (M <= 48) return kConfigDecode3;
     if (M <= 64) return kConfigDecode4;
-    return K % 256 == 0 ? kConfigPrefill : kConfigPrefill2Buf;
+    return K % 256 == 0 ? kConfigPrefillX32 : kConfigPrefill2Buf;
 }
 
 int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
@@ -64,7 +65,8 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     if (st != MPGEMM_OK) return st;
     if (config_id != kConfigSelect &&
         !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) ||
-          config_id == kConfigPrefill || config_id == kConfigPrefill2Buf))
+          config_id == kConfigPrefill || config_id == kConfigPrefill2Buf ||
+          config_id == kConfigPrefillX32))
         return MPGEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MPGEMM_OK;
     if (Y == nullptr) return MPGEMM_ERR_INVALID_ARG;
@@ -95,7 +97,8 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
         fprintf(stderr, "mpgemm: M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", M, N, K, group,
                 dtype, symmetric, mpgemm_config_name(cfg));
     if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
-    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf)
+    if (cfg == kConfigPrefillX32 && K % 256 == 0) return hip_status(mpgemm::launch_prefill_x32(a, s));
+    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf || cfg == kConfigPrefillX32)
         return hip_status(mpgemm::launch_prefill(a, s));
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
@@ -187,8 +190,9 @@ const char *mpgemm_config_name(int config_id) {
         case kConfigDecode2: return "decode_splitk_m32";
         case kConfigDecode3: return "decode_splitk_m48";
         case kConfigDecode4: return "decode_splitk_m64";
-        case kConfigPrefill: return "prefill_ring_128x256";
+        case kConfigPrefill: return "prefill_ring16_128x256";
         case kConfigPrefill2Buf: return "prefill_2buf_128x256";
+        case kConfigPrefillX32: return "prefill_x32_128x256";
         default: return "";
     }
 }

@@ -10,16 +10,18 @@
 //   - workgroup tile 128 (m) x 256 (n), four waves side by side along n, each owning a
 //     128 x 64 block (8 x 4 MFMA 16x16x32 blocks, 128 fp32 accumulators per lane); every
 //     dequantized weight fragment feeds 8 MFMAs;
-//   - activations: a ring of four 128 x 64 fp16 LDS stages (64 KiB).  Each stage is filled
-//     by buffer_load_dwordx4 ... lds (HBM/L2 straight into LDS, no register staging),
-//     issued three stages ahead; each wave DMAs four 1 KiB blocks per stage.  Rows are
+//   - activations: a ring of eight 128 x 64 fp16 LDS stages (128 KiB of the CU's 160 KiB;
+//     the kernel runs one workgroup per CU).  Each stage is filled by buffer_load_dwordx4
+//     ... lds (HBM/L2 straight into LDS, no register staging), issued seven stages ahead, so
+//     about six stages of MFMA work cover the load latency; each wave DMAs four 1 KiB blocks
+//     per stage.  Rows are
 //     XOR-swizzled in 16-byte chunks (chunk ^ row % 8) by choosing each lane's source
 //     address, so the LDS block stays contiguous while the operand reads of eight
 //     consecutive lanes hit eight distinct bank groups.  One barrier per stage: a wave
 //     waits for its own DMA of the next stage, then the barrier makes every wave's DMA
 //     visible and frees the stage about to be refilled;
-//   - weights: one 128-bit buffer load per lane per strip per 128-deep tile, one tile ahead,
-//     in two register sets that alternate between tiles;
+//   - weights: one 128-bit buffer load per lane per strip per 128-deep tile, three tiles
+//     ahead, into four register sets used in rotation;
 //   - inner loop over 32-deep MFMA steps: while step s runs its 32 MFMAs, step s+1's
 //     weight fragments are dequantized (VALU) and its activation operands are read from
 //     LDS; the accumulators stay in place in AGPRs (inline-asm MFMA, see mfma_acc).
@@ -32,7 +34,8 @@ namespace {
 constexpr int kRBM = 128;
 constexpr int kRBN = 256;
 constexpr int kRThreads = 256;
-constexpr int kRStages = 4;                  // 64-deep LDS stages in the ring
+constexpr int kRStages = 8;                  // 64-deep LDS stages in the ring
+constexpr int kRWSets = kRStages / 2;        // weight register sets (tiles in flight)
 constexpr int kRChunks = kRBM * 8;           // 16-byte chunks per stage (8 per 64-deep row)
 
 template <int N>
@@ -118,7 +121,7 @@ __device__ __forceinline__ void step_fence() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int ACT, bool SYM, int G>
+template <int ACT, bool SYM, int G, int NST, int NWS>
 __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
@@ -127,7 +130,20 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     constexpr int GPT = kTileK / G;          // groups per 128-deep tile (1 or 2)
     // Loads each wave issues per weight tile: codes + scales (+ zeros), four strips.
     constexpr int kWLoads = 4 * (1 + GPT * (SYM ? 1 : 2));
-    __shared__ u32x4_t xs[kRStages][kRChunks];
+    // Stage j issues the DMA of stage j + NST - 1 and, when j is even, the weights of tile
+    // j/2 + NWS - 1 (the tiles 0 .. NWS-2 come from the prologue, so NWS = NST / 2).  Stage
+    // j needs the DMA of stage j + 1, issued at stage j + 2 - NST; the wave's loads issued
+    // after it are NST - 3 stage DMAs and (NST - 2) / 2 weight tiles.  Loads complete in
+    // issue order, so waiting until no more than that many are outstanding suffices; a
+    // count past the counter's range (63) waits for a few more, which is still correct.
+    static_assert(NWS * 2 == NST && (NST == 4 || NST == 8), "ring shape");
+    constexpr int kAfter = 4 * (NST - 3) + kWLoads * ((NST - 2) / 2);
+    constexpr int kWait = kAfter < 63 ? kAfter : 63;
+    // Before stage 0: stage 0's DMA and tile 0's weights, issued before the DMAs of stages
+    // 2 .. NST-2 and the weights of tiles 1 .. NWS-2.
+    constexpr int kPro = 4 * (NST - 3) + kWLoads * ((NST - 4) / 2);
+    constexpr int kProWait = kPro < 63 ? kPro : 63;
+    __shared__ u32x4_t xs[NST][kRChunks];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,7 +199,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
         u32x4_t w[4];
         uint32_t s[4][GPT], z[4][GPT];
     };
-    WSet ws[2];
+    WSet ws[NWS];
     DqT dq[2][4][GPT];
     u32x4_t A[2][4], B[2][8];
 
@@ -244,29 +260,37 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
         }
     };
 
-    // One 64-deep stage st (ring buffer BUF = st % 4, tile t = st / 2, half H = st % 2,
-    // weight set TS = t % 2).  Step 0 runs word 2H while step 1's operands are prepared;
-    // step 1 runs word 2H+1 while the next stage's first operands are prepared.
-    auto stage = [&](int st, auto BUF, auto H, auto TS) {
-        constexpr int buf = decltype(BUF)::value, h = decltype(H)::value, ts = decltype(TS)::value;
-        constexpr int nbuf = (buf + 1) % kRStages;
+    // One 64-deep stage st (ring buffer BUF = st % NST, tile t = st / 2, half H = st % 2,
+    // TW = t % NWS: the weight set of tile t; dequant constants alternate by t % 2).  Step 0
+    // runs word 2H while step 1's operands are prepared; step 1 runs word 2H+1 while the
+    // next stage's first operands are prepared.
+    auto stage = [&](int st, auto BUF, auto H, auto TW) {
+        constexpr int buf = decltype(BUF)::value, h = decltype(H)::value;
+        constexpr int tw = decltype(TW)::value, td = tw % 2;
+        constexpr int nbuf = (buf + 1) % NST, nw = (tw + 1) % NWS, nd = 1 - td;
         const int t = st >> 1;
-        // The wave's DMA of stage st+1 was followed by the DMA of stage st+2 and one
-        // weight tile; once those are the only loads left, stage st+1 is in LDS.
-        wait_vm_barrier<4 + kWLoads>();
-        dma(st + 3, IC<(buf + 3) % kRStages>());
-        if (h == 0) load_w(t + 1, ws[1 - ts]);
+        wait_vm_barrier<kWait>();
+        dma(st + NST - 1, IC<(buf + NST - 1) % NST>());
+        if (h == 0) load_w(t + NWS - 1, ws[(tw + NWS - 1) % NWS]);
         // step 0: word 2h of tile t; prepares word 2h+1 from this stage's buffer
         step_fence();
-        step(A[0], B[0], A[1], B[1], ws[ts], dq[ts], 2 * h + 1, BUF, 1);
+        step(A[0], B[0], A[1], B[1], ws[tw], dq[td], 2 * h + 1, BUF, 1);
         // step 1: word 2h+1; prepares stage st+1's first step (next tile when h == 1)
         step_fence();
         if (h == 1) {
-            make_dq(ws[1 - ts], dq[1 - ts]);
-            step(A[1], B[1], A[0], B[0], ws[1 - ts], dq[1 - ts], 0, IC<nbuf>(), 0);
+            make_dq(ws[nw], dq[nd]);
+            step(A[1], B[1], A[0], B[0], ws[nw], dq[nd], 0, IC<nbuf>(), 0);
         } else {
-            step(A[1], B[1], A[0], B[0], ws[ts], dq[ts], 2, IC<nbuf>(), 0);
+            step(A[1], B[1], A[0], B[0], ws[tw], dq[td], 2, IC<nbuf>(), 0);
         }
+    };
+    // Stages u .. u+3 of an NST-stage block (u = 0 or 4).
+    auto four = [&](int st, auto U) {
+        constexpr int u = decltype(U)::value;
+        stage(st + 0, IC<u + 0>(), IC<0>(), IC<(u / 2) % NWS>());
+        stage(st + 1, IC<u + 1>(), IC<1>(), IC<(u / 2) % NWS>());
+        stage(st + 2, IC<u + 2>(), IC<0>(), IC<(u / 2 + 1) % NWS>());
+        stage(st + 3, IC<u + 3>(), IC<1>(), IC<(u / 2 + 1) % NWS>());
     };
 
     // The zeroed accumulators are written by VALU; pad before the first MFMA reads them.
@@ -274,22 +298,33 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     asm volatile("s_nop 4" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-    // Prologue: stages 0..2 in flight, tile 0's weights, then stage 0's first operands.
+    // Prologue, in the loop's issue order: the DMAs of stages 0 .. NST-2, with the weights
+    // of tiles 0 .. NWS-2 after the DMAs of stages 1, 3, ...; then stage 0's first operands.
     dma(0, IC<0>());
-    load_w(0, ws[0]);
     dma(1, IC<1>());
+    load_w(0, ws[0]);
     dma(2, IC<2>());
-    wait_vm_barrier<4>();                    // everything but stage 2's DMA has landed
+    if constexpr (NST == 8) {
+        dma(3, IC<3>());
+        load_w(1, ws[1]);
+        dma(4, IC<4>());
+        dma(5, IC<5>());
+        load_w(2, ws[2]);
+        dma(6, IC<6>());
+    }
+    wait_vm_barrier<kProWait>();
     make_dq(ws[0], dq[0]);
     read_b(IC<0>(), 0, B[0]);
     dequant_a(ws[0], dq[0], 0, A[0]);
 
-    for (int st = 0; st < S; st += 4) {
-        stage(st + 0, IC<0>(), IC<0>(), IC<0>());
-        stage(st + 1, IC<1>(), IC<1>(), IC<0>());
-        stage(st + 2, IC<2>(), IC<0>(), IC<1>());
-        stage(st + 3, IC<3>(), IC<1>(), IC<1>());
+    // S is a multiple of 4; NST-stage blocks, then a four-stage tail when S % 8 == 4 (the
+    // tail's stages are a block's first four, so its buffers and weight sets line up).
+    int st = 0;
+    for (; st + NST <= S; st += NST) {
+        four(st, IC<0>());
+        if constexpr (NST == 8) four(st + 4, IC<4>());
     }
+    if (st < S) four(st, IC<0>());
     // The last stages prefetched (redundant) LDS data; let every DMA land before the wave
     // can retire, so no write reaches LDS after the workgroup has released it.  The nops
     // give the last MFMAs' results time to land before the epilogue reads them.
@@ -312,7 +347,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
 template <int ACT, bool SYM, int G>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     const dim3 grid((a.N + kRBN - 1) / kRBN, (a.M + kRBM - 1) / kRBM);
-    prefill_ring_kernel<ACT, SYM, G><<<grid, dim3(kRThreads), 0, stream>>>(
+    prefill_ring_kernel<ACT, SYM, G, kRStages, kRWSets><<<grid, dim3(kRThreads), 0, stream>>>(
         a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
 }
 

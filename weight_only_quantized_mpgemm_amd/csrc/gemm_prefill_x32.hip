@@ -1,0 +1,499 @@
+// Large-M (prefill) W4A16 GEMM for gfx950 on the 32x32x16 matrix instruction.
+//
+// [TurboMind, technique (iii), Fig. 9 caption]: a software-pipelined main loop keeps the
+// matrix cores busy on step k with already-dequantized fragments while the integer/float
+// ALUs dequantize step k+1 and the memory pipeline fetches later tiles.  Source: "LMDeploy
+// Accelerates Mixed-Precision LLM Inference with TurboMind" (arXiv 2508.15601).
+//
+// Why 32x32x16: one wave of a CDNA4 SIMD issues at most one instruction every four cycles,
+// and a matrix instruction takes two of those slots.  v_mfma_f32_32x32x16 keeps the matrix
+// core busy 32 cycles per issue (twice the 16x16x32 form for the same two slots), which
+// leaves about six slots per matrix instruction for the dequantization, LDS reads and
+// bookkeeping of the next step -- the 16x16x32 form leaves two, fewer than the fp16
+// dequantization alone needs (13 vector operations per 8 weights, each weight feeding
+// 128 rows).
+//
+// Design (K % 256 == 0):
+//   - workgroup tile 128 (m) x 256 (n), four waves side by side along n, each owning a
+//     128 x 64 block = 2 (n) x 4 (m) blocks of 32 x 32, 128 fp32 accumulators per lane in
+//     AGPRs, updated in place by inline-asm MFMA;
+//   - weights are the A operand (rows = n): lane l holds column n = l % 32 of a 32-column
+//     block (two 16-column strips of the packed layout) at k = 16u + 8 (l / 32) .. +7 of a
+//     32-deep step.  In the packed layout that is strip (l % 32) / 16, lane position
+//     l % 16 + 16 (2u + l / 32), word = step within the 128-deep tile -- each lane simply
+//     loads a different 16-byte slot of the same 1 KiB tiles, so the layout is shared with
+//     the 16x16x32 kernels;
+//   - weights: one 16-byte load per lane per (column block, k half) per 128-deep tile,
+//     issued three tiles (six stages) ahead into four register sets used in rotation (one
+//     tile ahead in two sets for g = 64) --
+//     HBM latency under full load exceeds the one to two stages a two-set scheme gives;
+//   - activations are the B operand (columns = m), read from a ring of four 128 x 64 LDS
+//     stages filled by buffer_load_dwordx4 ... lds three stages ahead (XOR-swizzled 16-byte
+//     chunks, chunk ^ row % 8, so eight consecutive rows hit eight bank groups);
+//   - each 32-deep step runs 16 MFMAs; after MFMA i come 1/16 of the next step's work: an
+//     LDS operand read on even i and about three of the 52 dequantization operations of
+//     the next step's four weight words, taken round-robin over the words so no operation
+//     directly follows the one it depends on.  The dequantization is inline asm too, so
+//     the compiler neither reorders it nor pads it with wait states meant for the MFMAs.
+#include <utility>
+
+#include "kernels.hpp"
+
+namespace mpgemm {
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kXBM = 128;
+constexpr int kXBN = 256;
+constexpr int kXThreads = 256;
+constexpr int kXStages = 4;                  // 64-deep LDS stages in the ring
+// Weight register sets (loads run NWS - 1 tiles ahead): four for g = 128; two for g = 64,
+// whose doubled scale/zero registers would not fit four sets without spilling.
+template <int G>
+constexpr int kXWSets = G == 128 ? 4 : 2;
+constexpr int kXChunks = kXBM * 8;           // 16-byte chunks per stage (8 per 64-deep row)
+
+template <int N>
+struct IC {
+    static constexpr int value = N;
+};
+
+// Wait until at most NV vector-memory operations of this wave are outstanding, then meet
+// the rest of the workgroup.  The memory clobber keeps LDS accesses on their side of it.
+template <int NV>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(NV >= 0 && NV < 64, "vmcnt range");
+    constexpr int imm = (NV & 15) | ((NV >> 4) << 14) | (7 << 4) | (15 << 8);
+    asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
+}
+
+// acc += a * b on one 32 x 32 block, accumulator pinned in place in AGPRs.  Inline asm is
+// invisible to the compiler's hazard tracking: the schedule keeps every VALU write of an
+// operand at least three instructions ahead of the MFMA that reads it, and the epilogue
+// pads before reading results.
+template <int ACT>
+__device__ __forceinline__ void mfma32(f32x16_t &c, const u32x4_t &a, const u32x4_t &b);
+template <>
+__device__ __forceinline__ void mfma32<kF16>(f32x16_t &c, const u32x4_t &a, const u32x4_t &b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <>
+__device__ __forceinline__ void mfma32<kBF16>(f32x16_t &c, const u32x4_t &a, const u32x4_t &b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Constants the dequantization keeps in registers for the whole kernel.  Produced by asm
+// so the compiler cannot rematerialize them (an s_mov / v_mov per use) inside the loop.
+struct DqConst {
+    uint32_t m_lo, m_hi;     // SGPR masks 0x000F000F, 0x00F000F0
+    uint32_t b_hi, b_lo;     // VGPR fp16x2 patterns 1024.0 (0x6400) and 64.0 (0x5400)
+    uint32_t m_byte;         // VGPR 0x0F0F0F0F (bf16 nibble spread)
+};
+__device__ __forceinline__ DqConst make_dq_const() {
+    DqConst c;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(c.m_lo));
+    asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(c.m_hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.b_hi));
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(c.b_lo));
+    asm volatile("v_mov_b32 %0, 0x0F0F0F0F" : "=v"(c.m_byte));
+    return c;
+}
+
+// Scratch values of one word's dequantization.
+struct DqTmp {
+    uint32_t sh, h[4];
+    float f[8];
+};
+
+// Operation OP of the dequantization of word w into out (8 weights, k order), in the
+// same arithmetic as Dq<ACT>::word.  fp16 (13 operations): one shift, four isolate-and-
+// combine (1024 + q / 64 + q), four exact packed adds of -(B + z), four packed multiplies
+// by s (the one rounding).  bf16 (14 operations): spread nibbles to bytes (two), eight
+// convert-and-fma q * s - z * s (exact in fp32), four conversions to bf16 pairs (the one
+// rounding).
+template <int ACT>
+struct DqOps;
+
+template <>
+struct DqOps<kF16> {
+    static constexpr int kCount = 13;
+    template <int OP>
+    static __device__ __forceinline__ void run(uint32_t w, const DqF16 &d, const DqConst &c,
+                                               DqTmp &t, u32x4_t &out) {
+        if constexpr (OP == 0) {
+            asm("v_lshrrev_b32 %0, 8, %1" : "=v"(t.sh) : "v"(w));
+        } else if constexpr (OP >= 1 && OP <= 4) {
+            constexpr int j = OP - 1;
+            const uint32_t src = (j < 2) ? w : t.sh;
+            if constexpr ((j & 1) == 0)
+                asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t.h[j]) : "v"(src), "s"(c.m_lo), "v"(c.b_hi));
+            else
+                asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t.h[j]) : "v"(src), "s"(c.m_hi), "v"(c.b_lo));
+        } else if constexpr (OP >= 5 && OP <= 8) {
+            constexpr int j = OP - 5;
+            const uint32_t nz = (j & 1) ? d.nz_lo2 : d.nz_hi2;
+            asm("v_pk_add_f16 %0, %1, %2" : "=v"(t.h[j]) : "v"(t.h[j]), "v"(nz));
+        } else {
+            constexpr int j = OP - 9;
+            uint32_t r;
+            asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(t.h[j]), "v"(d.s2));
+            out[j] = r;
+        }
+    }
+};
+
+template <>
+struct DqOps<kBF16> {
+    static constexpr int kCount = 14;
+    template <int OP>
+    static __device__ __forceinline__ void run(uint32_t w, const DqBF16 &d, const DqConst &c,
+                                               DqTmp &t, u32x4_t &out) {
+        // lo bytes: e0 e4 e1 e5; hi bytes: e2 e6 e3 e7
+        if constexpr (OP == 0) {
+            t.h[0] = w & c.m_byte;
+        } else if constexpr (OP == 1) {
+            t.h[1] = (w >> 4) & c.m_byte;
+        } else if constexpr (OP >= 2 && OP <= 9) {
+            constexpr int e = OP - 2;                       // element e0 .. e7
+            constexpr int src = (e >> 1) & 1;               // e0 e1 e4 e5 in lo
+            constexpr int byte = ((e & 1) << 1) | (e >> 2);
+            t.f[e] = __builtin_fmaf(ubyte(t.h[src], byte), d.s, d.nzs);
+        } else {
+            constexpr int j = OP - 10;
+            out[j] = pack_bf16x2(t.f[2 * j], t.f[2 * j + 1]);
+        }
+    }
+};
+
+// Tile of workgroup b.  Workgroups are dispatched round-robin over the eight XCDs
+// (b % 8), each with its own L2; XCD x gets a contiguous range of tile indices, walked in
+// groups of four M-tiles (all four rows of one N-tile, then the next N-tile), so the
+// workgroups that run together on one XCD share four activation row-blocks and a few weight
+// column-blocks instead of touching every row-block of X.
+__device__ __forceinline__ void tile_of(int b, int tm, int tn, int &mt, int &nt) {
+    constexpr int kXcds = 8, kGroupM = 4;
+    const int T = tm * tn, per = T / kXcds, extra = T % kXcds;
+    const int x = b % kXcds;
+    const int t = x * per + min(x, extra) + b / kXcds;
+    const int g = t / (kGroupM * tn);
+    const int gm = min(kGroupM, tm - g * kGroupM);
+    const int r = t - g * kGroupM * tn;
+    mt = g * kGroupM + r % gm;
+    nt = r / gm;
+}
+
+template <int ACT, bool SYM, int G, int NWS>
+__global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
+    const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    uint16_t *__restrict__ Y) {
+    typedef typename Dq<ACT>::type DqT;
+    typedef DqOps<ACT> Ops;
+    constexpr int GPT = kTileK / G;          // groups per 128-deep tile (1 or 2)
+    // Loads each wave issues per weight tile: four 16-byte code slots (2 column blocks x
+    // 2 k halves), plus scales (and zeros) per column block and group.
+    constexpr int kWLoads = 4 + 2 * GPT * (SYM ? 1 : 2);
+    __shared__ u32x4_t xs[kXStages][kXChunks];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    int mt, nt;
+    tile_of(blockIdx.x, (M + kXBM - 1) / kXBM, (N + kXBN - 1) / kXBN, mt, nt);
+    const int m_blk = mt * kXBM;
+    const int KT = K >> 7;                   // 128-deep weight tiles
+    const int S = K >> 6;                    // 64-deep stages (a multiple of 4)
+    const int groups = K / G;
+    const int strips = N >> 4;
+    const int strip0 = nt * (kXBN / 16) + wave * 4;
+
+    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024));
+    const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
+    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / 2));
+    const DqConst dc = make_dq_const();
+
+    // DMA source offsets: wave w fills blocks b = 4w + i of every stage; block b holds rows
+    // 8b .. 8b+7, lane l writes LDS chunk 64b + l = (row 8b + l/8, physical chunk l%8),
+    // which holds logical chunk (l%8) ^ (l/8).  Rows past M read zeros (one past the end).
+    uint32_t xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * (wave * 4 + i) + (lane >> 3);
+        const uint32_t row = (uint32_t)min(m_blk + r, M);
+        xoff[i] = (row * K + (((lane & 7) ^ (lane >> 3)) * 8)) * 2u;
+    }
+    // Weight slots: column block nb (strips strip0 + 2nb, +1), k half u.  Strips past N
+    // read the last real strip; their results are never stored.
+    const int my_strip_in_pair = (lane & 31) >> 4;
+    uint32_t woff[2][2], soff[2], zoff[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t strip = (uint32_t)min(strip0 + 2 * nb + my_strip_in_pair, strips - 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t pos = (lane & 15) + 16 * (2 * u + (lane >> 5));
+            woff[nb][u] = strip * KT * 1024u + pos * 16u;
+        }
+        const uint32_t e = strip * groups * 16u + (lane & 15);
+        soff[nb] = (e >> 1) * 4u;
+        zoff[nb] = (e >> 3) * 4u;
+    }
+    const uint32_t sshift = (lane & 1) * 16;
+    const uint32_t zshift = (lane & 7) * 4;
+    // B operand: row 32 mb + lane % 32, logical chunk 4s + 2u + lane / 32 of the stage;
+    // physical chunk = logical ^ (lane % 8) = (4s + 2u) ^ cb.
+    const int brow = (lane & 31) * 8;
+    const int cb = (lane >> 5) ^ (lane & 7);
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16_t{};
+
+    struct WSet {
+        u32x4_t w[2][2];                     // [nb][u], words = 32-deep steps of the tile
+        uint32_t s[2][GPT], z[2][GPT];
+    };
+    static_assert(NWS == 2 || NWS == 4, "the stage loop unrolls 2 * NWS stages");
+    WSet ws[NWS];
+    DqT dq[NWS][2][GPT];
+    u32x4_t A[2][2][2], B[2][2][4];          // [set][u][nb] / [set][u][mb]
+
+    // Block i (of four) of this wave's share of stage st's DMA.
+    auto dma_part = [&](int st, auto buf, int i) __attribute__((always_inline)) {
+        const uint32_t soff_k = (uint32_t)min(st, S - 1) * 128u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * 4 + i) * 64],
+            16, xoff[i], soff_k, 0, 0);
+    };
+    auto dma = [&](int st, auto buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_part(st, buf, i);
+    };
+    // Load j (of kWLoads) of weight tile t: the four code slots, then scales and zeros.
+    auto load_w_part = [&](int t, WSet &w, auto J) __attribute__((always_inline)) {
+        constexpr int j = decltype(J)::value;
+        t = min(t, KT - 1);
+        if constexpr (j < 4) {
+            w.w[j / 2][j % 2] = buf_load_b128(wrs, woff[j / 2][j % 2], t * 1024);
+        } else {
+            constexpr int m = j - 4, per = SYM ? 1 : 2;
+            constexpr int nb = m / (GPT * per), h = (m / per) % GPT, kind = m % per;
+            if constexpr (kind == 0)
+                w.s[nb][h] = buf_load_b32(srs, soff[nb], (t * GPT + h) * 32);
+            else
+                w.z[nb][h] = buf_load_b32(zrs, zoff[nb], (t * GPT + h) * 8);
+        }
+    };
+    auto load_w = [&](int t, WSet &w) __attribute__((always_inline)) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            (load_w_part(t, w, IC<J>()), ...);
+        }(std::make_integer_sequence<int, kWLoads>{});
+    };
+    auto make_dq = [&](const WSet &w, DqT(&d)[2][GPT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int h = 0; h < GPT; ++h)
+                d[nb][h] = Dq<ACT>::make((uint16_t)(w.s[nb][h] >> sshift),
+                                         SYM ? 8u : ((w.z[nb][h] >> zshift) & 0xFu));
+    };
+    auto read_b = [&](auto buf, int s, u32x4_t(&b)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+                b[u][mb] = xs[decltype(buf)::value][mb * 256 + brow + ((4 * s + 2 * u) ^ cb)];
+    };
+    auto dequant_a = [&](const WSet &w, const DqT(&d)[2][GPT], int word, u32x4_t(&a)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                a[u][nb] = Dq<ACT>::word(w.w[nb][u][word], d[nb][(word * 32) / G]);
+    };
+
+    // Dequantization operations of the next step, round-robin over its four words
+    // (word q = (u, nb) = (q / 2, q % 2)): operation o is step o / 4 of word o % 4.
+    auto run_ops = [&](auto LO, auto HI, const WSet &wn, const DqT(&dn)[2][GPT], int word_n,
+                       DqTmp(&tmp)[4], u32x4_t(&an)[2][2]) __attribute__((always_inline)) {
+        constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+        [&]<int... O>(std::integer_sequence<int, O...>) {
+            (([&] {
+                 constexpr int o = lo + O;
+                 if constexpr (o < hi) {
+                     constexpr int q = o % 4, u = q / 2, nb = q % 2;
+                     Ops::template run<o / 4>(wn.w[nb][u][word_n], dn[nb][(word_n * 32) / G], dc,
+                                              tmp[q], an[u][nb]);
+                 }
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, 8>{});
+    };
+
+    // One 32-deep step: MFMA i (u = i/8, nb = i/4 % 2, mb = i % 4) on the current
+    // operands, then slice i of the next step's preparation.
+    auto step = [&](const u32x4_t(&a)[2][2], const u32x4_t(&b)[2][4], u32x4_t(&an)[2][2],
+                    u32x4_t(&bn)[2][4], const WSet &wn, const DqT(&dn)[2][GPT], int word_n,
+                    auto bufn, int s_n, auto hook) __attribute__((always_inline)) {
+        DqTmp tmp[4];
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (([&] {
+                 constexpr int u = I / 8, nb = (I / 4) % 2, mb = I % 4;
+                 mfma32<ACT>(acc[nb][mb], a[u][nb], b[u][mb]);
+                 if constexpr (I % 2 == 0) {
+                     constexpr int r = I / 2, ru = r / 4, rmb = r % 4;
+                     bn[ru][rmb] = xs[decltype(bufn)::value][rmb * 256 + brow + ((4 * s_n + 2 * ru) ^ cb)];
+                 }
+                 constexpr int total = 4 * Ops::kCount;
+                 run_ops(IC<(total * I) / 16>(), IC<(total * (I + 1)) / 16>(), wn, dn, word_n, tmp, an);
+                 hook(IC<I>());
+                 __builtin_amdgcn_sched_barrier(0);
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, 16>{});
+        // Keep this step's operands allocated to the end of the step, so no register of an
+        // operand that an in-flight MFMA reads is handed to the next step's values.
+        asm volatile("" ::"v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]), "v"(b[0][0]),
+                     "v"(b[0][1]), "v"(b[0][2]), "v"(b[0][3]), "v"(b[1][0]), "v"(b[1][1]),
+                     "v"(b[1][2]), "v"(b[1][3]));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One 64-deep stage st (ring buffer BUF = st % 4, tile t = st / 2, half H = st % 2,
+    // weight set TW = t % NWS): step 0 runs word 2H and prepares word 2H+1 from this
+    // stage's buffer; step 1 runs word 2H+1 and prepares the next stage's first step (the
+    // next tile's word 0 when H == 1).  Stage 2t loads tile t + NWS - 1.
+    auto stage = [&](int st, auto BUF, auto H, auto TW) __attribute__((always_inline)) {
+        constexpr int buf = decltype(BUF)::value, h = decltype(H)::value, tw = decltype(TW)::value;
+        constexpr int nbuf = (buf + 1) % kXStages, nw = (tw + 1) % NWS;
+        const int t = st >> 1;
+        // The wave's DMA of stage st+1 was followed by the DMA of stage st+2 and one weight
+        // tile; once only those are outstanding, stage st+1 is in LDS.  (In the first two
+        // stages more loads follow it and the wait is longer than needed, never shorter.)
+        wait_vm_barrier<4 + kWLoads>();
+        // The next stage's DMA (four blocks) and, in the first half of a tile, the weight
+        // loads of tile t + NWS - 1 go out one at a time between MFMAs, in the same order
+        // as before, instead of as one burst per wave at the barrier.
+        auto dma_hook = [&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (i % 4 == 1) dma_part(st + 3, IC<(buf + 3) % kXStages>(), i / 4);
+        };
+        auto w_hook = [&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            if constexpr (h == 0) {
+                if constexpr (kWLoads <= 8) {
+                    if constexpr (i % 2 == 0 && i / 2 < kWLoads)
+                        load_w_part(t + NWS - 1, ws[(tw + NWS - 1) % NWS], IC<i / 2>());
+                } else {
+                    if constexpr (i < kWLoads)
+                        load_w_part(t + NWS - 1, ws[(tw + NWS - 1) % NWS], IC<i>());
+                }
+            }
+        };
+        step(A[0], B[0], A[1], B[1], ws[tw], dq[tw], 2 * h + 1, BUF, 1, dma_hook);
+        if (h == 1) {
+            make_dq(ws[nw], dq[nw]);
+            __builtin_amdgcn_sched_barrier(0);
+            step(A[1], B[1], A[0], B[0], ws[nw], dq[nw], 0, IC<nbuf>(), 0, w_hook);
+        } else {
+            step(A[1], B[1], A[0], B[0], ws[tw], dq[tw], 2, IC<nbuf>(), 0, w_hook);
+        }
+    };
+    // Stages st .. st+3 (tiles 2u, 2u+1 of a 2 * NWS-stage block, u = 0 or 1).
+    auto four = [&](int st, auto U) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;
+        stage(st + 0, IC<0>(), IC<0>(), IC<(2 * u) % NWS>());
+        stage(st + 1, IC<1>(), IC<1>(), IC<(2 * u) % NWS>());
+        stage(st + 2, IC<2>(), IC<0>(), IC<(2 * u + 1) % NWS>());
+        stage(st + 3, IC<3>(), IC<1>(), IC<(2 * u + 1) % NWS>());
+    };
+
+    // Prologue: stages 0..2 in flight, tiles 0 .. NWS-2, then stage 0's first operands.
+    dma(0, IC<0>());
+    load_w(0, ws[0]);
+    dma(1, IC<1>());
+    dma(2, IC<2>());
+#pragma unroll
+    for (int t = 1; t < NWS - 1; ++t) load_w(t, ws[t]);
+    wait_vm_barrier<4 + kWLoads * (NWS - 2)>();   // stage 0's DMA and tile 0 have landed
+    make_dq(ws[0], dq[0]);
+    read_b(IC<0>(), 0, B[0]);
+    dequant_a(ws[0], dq[0], 0, A[0]);
+    // The zeroed accumulators and the first operands were written by VALU / LDS reads
+    // that the compiler waits for; pad before the first (inline-asm) MFMA reads them.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 4" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // S is a multiple of 4: blocks of 2 * NWS stages, then a four-stage tail (a block's
+    // first four stages, so ring buffers and weight sets line up).
+    int st = 0;
+    for (; st + 2 * NWS <= S; st += 2 * NWS) {
+        four(st, IC<0>());
+        if constexpr (NWS == 4) four(st + 4, IC<1>());
+    }
+    if constexpr (NWS == 4) {
+        if (st < S) four(st, IC<0>());
+    }
+    // The last stages prefetched (redundant) LDS data; let every DMA land before the wave
+    // can retire.  The nops cover the latency of the last MFMAs before their results are
+    // read.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Result element j of block (nb, mb) in lane l: n = 32 nb + 8 (j / 4) + 4 (l / 32) + j % 4
+    // of the wave's 64 columns, m = 32 mb + l % 32.
+    const int n_wave = strip0 * 16;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = n_wave + nb * 32 + 8 * q + 4 * (lane >> 5);
+            if (n >= N) continue;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const int m = m_blk + mb * 32 + (lane & 31);
+                if (m < M) {
+                    const f32x4_t v = {acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
+                                       acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]};
+                    *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + n) = round4<ACT>(v);
+                }
+            }
+        }
+}
+
+template <int ACT, bool SYM, int G>
+void launch_one(const GemmArgs &a, hipStream_t stream) {
+    const dim3 grid(((a.N + kXBN - 1) / kXBN) * ((a.M + kXBM - 1) / kXBM));
+    prefill_x32_kernel<ACT, SYM, G, kXWSets<G>><<<grid, dim3(kXThreads), 0, stream>>>(
+        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
+}
+
+template <int ACT>
+void launch_act(const GemmArgs &a, hipStream_t stream) {
+    const bool sym = a.zeros == nullptr;
+    if (a.group == 128) {
+        sym ? launch_one<ACT, true, 128>(a, stream) : launch_one<ACT, false, 128>(a, stream);
+    } else {
+        sym ? launch_one<ACT, true, 64>(a, stream) : launch_one<ACT, false, 64>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) {
+    if (a.act == kBF16) {
+        launch_act<kBF16>(a, stream);
+    } else {
+        launch_act<kF16>(a, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mpgemm

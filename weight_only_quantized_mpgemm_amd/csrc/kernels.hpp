@@ -36,6 +36,7 @@ hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
 // Tiled large-M kernels (128 rows x 256 columns per workgroup): the LDS-ring kernel
 // (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
 hipError_t launch_prefill_ring(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
 // Writes zeros to Y (the K == 0 case).
