@@ -10,18 +10,17 @@
 //   - workgroup tile 128 (m) x 256 (n), four waves side by side along n, each owning a
 //     128 x 64 block (8 x 4 MFMA 16x16x32 blocks, 128 fp32 accumulators per lane); every
 //     dequantized weight fragment feeds 8 MFMAs;
-//   - activations: a ring of eight 128 x 64 fp16 LDS stages (128 KiB of the CU's 160 KiB;
-//     the kernel runs one workgroup per CU).  Each stage is filled by buffer_load_dwordx4
-//     ... lds (HBM/L2 straight into LDS, no register staging), issued seven stages ahead, so
-//     about six stages of MFMA work cover the load latency; each wave DMAs four 1 KiB blocks
-//     per stage.  Rows are
+//   - activations: a ring of four 128 x 64 fp16 LDS stages (64 KiB).  Each stage is filled
+//     by buffer_load_dwordx4 ... lds (HBM/L2 straight into LDS, no register staging),
+//     issued three stages ahead; each wave DMAs four 1 KiB blocks per stage.  (The kernel is
+//     written for an eight-stage ring as well; measured, the deeper ring bought nothing.)  Rows are
 //     XOR-swizzled in 16-byte chunks (chunk ^ row % 8) by choosing each lane's source
 //     address, so the LDS block stays contiguous while the operand reads of eight
 //     consecutive lanes hit eight distinct bank groups.  One barrier per stage: a wave
 //     waits for its own DMA of the next stage, then the barrier makes every wave's DMA
 //     visible and frees the stage about to be refilled;
-//   - weights: one 128-bit buffer load per lane per strip per 128-deep tile, three tiles
-//     ahead, into four register sets used in rotation;
+//   - weights: one 128-bit buffer load per lane per strip per 128-deep tile, one tile
+//     ahead, in two register sets that alternate between tiles;
 //   - inner loop over 32-deep MFMA steps: while step s runs its 32 MFMAs, step s+1's
 //     weight fragments are dequantized (VALU) and its activation operands are read from
 //     LDS; the accumulators stay in place in AGPRs (inline-asm MFMA, see mfma_acc).
@@ -34,7 +33,7 @@ namespace {
 constexpr int kRBM = 128;
 constexpr int kRBN = 256;
 constexpr int kRThreads = 256;
-constexpr int kRStages = 8;                  // 64-deep LDS stages in the ring
+constexpr int kRStages = 4;                  // 64-deep LDS stages in the ring
 constexpr int kRWSets = kRStages / 2;        // weight register sets (tiles in flight)
 constexpr int kRChunks = kRBM * 8;           // 16-byte chunks per stage (8 per 64-deep row)
 
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     DqT dq[2][4][GPT];
     u32x4_t A[2][4], B[2][8];
 
-    auto dma = [&](int st, auto buf) {
+    auto dma = [&](int st, auto buf) __attribute__((always_inline)) {
         const uint32_t soff_k = (uint32_t)min(st, S - 1) * 128u;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
                 xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * 4 + i) * 64],
                 16, xoff[i], soff_k, 0, 0);
     };
-    auto load_w = [&](int t, WSet &w) {
+    auto load_w = [&](int t, WSet &w) __attribute__((always_inline)) {
         t = min(t, KT - 1);
 #pragma unroll
         for (int si = 0; si < 4; ++si) {
@@ -223,7 +222,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
             }
         }
     };
-    auto make_dq = [&](const WSet &w, DqT(&d)[4][GPT]) {
+    auto make_dq = [&](const WSet &w, DqT(&d)[4][GPT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int si = 0; si < 4; ++si)
 #pragma unroll
@@ -231,12 +230,12 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
                 d[si][h] = Dq<ACT>::make((uint16_t)(w.s[si][h] >> sshift),
                                          SYM ? 8u : ((w.z[si][h] >> zshift) & 0xFu));
     };
-    auto read_b = [&](auto buf, int s, u32x4_t(&b)[8]) {
+    auto read_b = [&](auto buf, int s, u32x4_t(&b)[8]) __attribute__((always_inline)) {
         const int c = (s * 4 + (lane >> 4)) ^ bsw;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) b[mb] = xs[decltype(buf)::value][mb * 128 + brow + c];
     };
-    auto dequant_a = [&](const WSet &w, const DqT(&d)[4][GPT], int word, u32x4_t(&a)[4]) {
+    auto dequant_a = [&](const WSet &w, const DqT(&d)[4][GPT], int word, u32x4_t(&a)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int si = 0; si < 4; ++si) a[si] = Dq<ACT>::word(w.w[si][word], d[si][(word * 32) / G]);
     };
@@ -246,7 +245,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     // i/8 -- so the matrix, vector and LDS pipes stay busy together.
     auto step = [&](const u32x4_t(&a)[4], const u32x4_t(&b)[8], u32x4_t(&an)[4],
                     u32x4_t(&bn)[8], const WSet &wn, const DqT(&dn)[4][GPT], int word_n,
-                    auto bufn, int s_n) {
+                    auto bufn, int s_n) __attribute__((always_inline)) {
         const int c = (s_n * 4 + (lane >> 4)) ^ bsw;
         PieceTmp tmp;
 #pragma unroll
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     // TW = t % NWS: the weight set of tile t; dequant constants alternate by t % 2).  Step 0
     // runs word 2H while step 1's operands are prepared; step 1 runs word 2H+1 while the
     // next stage's first operands are prepared.
-    auto stage = [&](int st, auto BUF, auto H, auto TW) {
+    auto stage = [&](int st, auto BUF, auto H, auto TW) __attribute__((always_inline)) {
         constexpr int buf = decltype(BUF)::value, h = decltype(H)::value;
         constexpr int tw = decltype(TW)::value, td = tw % 2;
         constexpr int nbuf = (buf + 1) % NST, nw = (tw + 1) % NWS, nd = 1 - td;
@@ -285,7 +284,7 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
         }
     };
     // Stages u .. u+3 of an NST-stage block (u = 0 or 4).
-    auto four = [&](int st, auto U) {
+    auto four = [&](int st, auto U) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
         stage(st + 0, IC<u + 0>(), IC<0>(), IC<(u / 2) % NWS>());
         stage(st + 1, IC<u + 1>(), IC<1>(), IC<(u / 2) % NWS>());
@@ -324,7 +323,9 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
         four(st, IC<0>());
         if constexpr (NST == 8) four(st + 4, IC<4>());
     }
-    if (st < S) four(st, IC<0>());
+    if constexpr (NST == 8) {
+        if (st < S) four(st, IC<0>());
+    }
     // The last stages prefetched (redundant) LDS data; let every DMA land before the wave
     // can retire, so no write reaches LDS after the workgroup has released it.  The nops
     // give the last MFMAs' results time to land before the epilogue reads them.
