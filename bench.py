@@ -12,11 +12,15 @@ Prints one JSON line: value = whole-step TFLOP/s (2*M*N*K summed over the twelve
 divided by the step time), plus HBM GB/s of algorithmic bytes, the roofline of the dominant
 kernel, a per-GEMM breakdown and the CPU oracle timed on a bounded sample (cpu_baseline).
 
+The timed steps launch every GEMM from Python (--graph instead captures each M's four
+GEMMs per weight copy as a HIP graph and replays it; measured, that is no faster here,
+because a replay starts later after the preceding event than an eager launch does).
 Kernel durations come from hipEvents recorded, inside the timed steps, on the stream the
-library launches on, around each run of consecutive launches of one kernel (the four GEMMs of
-one M), divided by the launches in it; so per-launch event overhead does not inflate short
-decode kernels.  The per-GEMM breakdown is a separate pass after the timed steps (ten
-back-to-back launches per GEMM between one pair of events).  `traffic` is the HBM bytes per
+library launches on, around each run of consecutive launches of one kernel (the four GEMMs
+of one M), divided by the launches in it; host launch gaps of a few microseconds still
+inflate the 6-20 us decode kernels there.  The per-GEMM breakdown is a separate pass after
+the timed steps: ten back-to-back launches per GEMM replayed from one HIP graph between
+one pair of events, which keeps host gaps out.  `traffic` is the HBM bytes per
 launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters read for the dominant kernel,
 scaled by what the same counters read for a plain 1 GiB copy (--copy-calibration); it is
 taken from the summary file under profiles/ and reported only while the kernel sources
@@ -115,6 +119,8 @@ def main():
     ap.add_argument("--pool-gb", type=float, default=1.5,
                     help="size of the rotating pool of packed weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the timed steps from captured HIP graphs")
     ap.add_argument("--no-per-gemm", action="store_true",
                     help="skip the per-GEMM breakdown pass (counter runs use this)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -187,14 +193,39 @@ def main():
     run_events = []
     shape_idx = {(K, N): j for j, (K, N, _) in enumerate(shapes)}
 
+    def launch_m(M, c):
+        for K, N, _ in shapes:
+            mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
+
+    # One graph per (M, weight copy): the four launches of one M are one run of one kernel.
+    use_graphs = args.graph and all(
+        sum(1 for _, rc in runs if rc[0][0] == M) == 1 for M in MS)
+    graphs = {}
+    if use_graphs:
+        for M in MS:
+            launch_m(M, 0)                     # load the library and kernels before capture
+        torch.cuda.synchronize()
+        for c in range(copies):
+            for M in MS:
+                g_ = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g_):
+                    launch_m(M, c)
+                graphs[(M, c)] = g_
+        torch.cuda.synchronize()
+        log(f"captured {len(graphs)} graphs")
+
     def step(s, record):
         evs = []
         for i, (M, K, N, label) in enumerate(calls):
-            pk = pool[(s * len(MS) + MS.index(M)) % copies]
+            c = (s * len(MS) + MS.index(M)) % copies
             if record and i in run_starts:
                 evs.append(torch.cuda.Event(enable_timing=True))
                 evs[-1].record(stream)
-            mp.w4a16(xs[(M, K)], pk[shape_idx[(K, N)]], out=ys[(M, N)])
+            if use_graphs:
+                if shape_idx[(K, N)] == 0:
+                    graphs[(M, c)].replay()
+            else:
+                mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
         if record:
             evs.append(torch.cuda.Event(enable_timing=True))
             evs[-1].record(stream)
@@ -252,11 +283,18 @@ def main():
         for ci, c in enumerate(calls):
             M, K, N, label = c
             j = shape_idx[(K, N)]
+            def launch_reps():
+                for r in range(reps):
+                    mp.w4a16(xs[(M, K)], pool[(ci * reps + r) % copies][j], out=ys[(M, N)])
+            launch_reps()                     # warm, then capture the ten launches
+            torch.cuda.synchronize()
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_):
+                launch_reps()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for r in range(reps):
-                mp.w4a16(xs[(M, K)], pool[(ci * reps + r) % copies][j], out=ys[(M, N)])
+            g_.replay()
             e1.record(stream)
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) * 1e-3 / reps
@@ -286,7 +324,8 @@ def main():
         "config": {"workload": "llama3-8b W4A16 g128 asym fp16: qkv 4096x6144, o_proj "
                                "4096x4096, gate_up 4096x28672, down 14336x4096 at "
                                "M=1,16,2048 (12 GEMMs per step)",
-                   "weight_pool_copies": copies, "group": g},
+                   "weight_pool_copies": copies, "group": g,
+                   "launch": "hip_graph" if use_graphs else "eager"},
         "hbm_gbps": round(step_bytes / step_s / 1e9, 1),
         "roofline": roofline(dominant),
         "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
