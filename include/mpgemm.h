@@ -114,8 +114,17 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
                   int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                   void *stream);
 
-/* Device workspace mpgemm_w4a16 needs for this problem (currently always 0: the split-K
- * reduction of the small-M kernels stays inside one workgroup). */
+/*
+ * Device workspace (bytes) mpgemm_w4a16 and mpgemm_w4a16_config need for this problem:
+ * nonzero only when a small-M kernel splits K over several workgroups (the largest need of
+ * the configurations that can run M rows).  The workspace holds fp32 partial sums and one
+ * 32-bit counter per group of columns at its start.
+ *   - It must be all zero before its first use; every call leaves the counters zero again,
+ *     so one zeroed allocation serves any number of later calls.
+ *   - Calls that share a workspace must not run concurrently (use one per stream).
+ *   - Passing less than this size (or NULL when it is nonzero) returns
+ *     MPGEMM_ERR_WORKSPACE and enqueues nothing.
+ */
 size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype);
 
 /*
@@ -125,7 +134,8 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype);
  *   X            in  [M][K] row-major, fp16 or bf16 bits per `dtype`
  *   packed_*     in  planes written by mpgemm_pack_weights for (K, N, group, symmetric)
  *   Y            out [M][N] row-major, same format as X
- *   workspace    in  mpgemm_workspace_bytes() bytes (may be NULL when that is 0)
+ *   workspace    in/out  mpgemm_workspace_bytes() bytes, zeroed before its first use (may
+ *                be NULL when that is 0); see mpgemm_workspace_bytes
  * K == 0 writes zeros to Y.  The kernel is chosen by shape (see mpgemm_select_config).
  */
 int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,

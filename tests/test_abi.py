@@ -139,3 +139,24 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "mpgemm_oracle" not in text, f
+
+
+def test_split_k_workspace_is_sized_and_required(monkeypatch):
+    """A split of K over workgroups needs a workspace; without one (or with too small or a
+    misaligned one) the call fails validation and enqueues nothing.  Every call here must
+    fail validation: the pointers are fake."""
+    lib = mp.lib()
+    assert lib.mpgemm_workspace_bytes(16, 256, 256, 128, 0) == 0       # default: no split
+    monkeypatch.setenv("MPGEMM_DECODE_SPLIT", "1,1,2")
+    need = lib.mpgemm_workspace_bytes(16, 256, 256, 128, 0)
+    # the fixed 256 KiB counter region, then 16 strip groups x 2 splits x 1 KiB of
+    # partials per row block, sized for every configuration that can run M = 16 (up to 4)
+    assert need == 256 * 1024 + 16 * 2 * 4 * 1024
+    assert lib.mpgemm_workspace_bytes(2048, 256, 256, 128, 0) == 0     # large M: no split
+    assert _gemm() == -4                                                # workspace NULL
+    args = [ctypes.c_void_p(A), 0, ctypes.c_void_p(A), ctypes.c_void_p(A), 16, 256, 256, 128,
+            0, ctypes.c_void_p(A), ctypes.c_void_p(A), 100]
+    assert lib.mpgemm_w4a16(*args, None) == -4                         # far too small
+    args[-1] = need
+    args[-2] = ctypes.c_void_p(MIS)
+    assert lib.mpgemm_w4a16(*args, None) == -4                         # misaligned

@@ -192,11 +192,36 @@ def config_name(config_id: int) -> str:
     return lib().mpgemm_config_name(config_id).decode()
 
 
+# One zeroed workspace per device, grown on demand and never freed: the kernels leave its
+# counters zero after every call, and graphs captured with an older (smaller) one keep a
+# valid pointer.  Calls that run concurrently on different streams of one device must
+# each pass their own zeroed `workspace`.
+_WORKSPACES: dict[int, list[torch.Tensor]] = {}
+
+
+def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
+    """The cached zeroed workspace of `device` with at least `nbytes` (None for 0)."""
+    if nbytes == 0:
+        return None
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    cached = _WORKSPACES.setdefault(idx, [])
+    if cached and cached[-1].numel() >= nbytes:
+        return cached[-1]
+    if torch.cuda.is_current_stream_capturing():
+        raise MpgemmError(-4, f"allocating a {nbytes}-byte workspace during graph capture "
+                              "(make one eager call of this shape first)")
+    ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+    cached.append(ws)
+    return ws
+
+
 def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
-          config: int = 0) -> torch.Tensor:
+          config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X @ dequant(W) (mpgemm_w4a16; mpgemm_w4a16_config when config != 0).
 
     x float16 or bfloat16 [M, K]; returns (or fills `out`) [M, N] in the same format.
+    workspace: uint8 device tensor, zeroed before its first use (default: the device's
+    cached one).
     """
     M, K = x.shape
     if K != packed.K:
@@ -208,7 +233,11 @@ def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = Non
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _need(out, x.dtype, (M, N), "out")
     ws = int(lib().mpgemm_workspace_bytes(M, N, K, packed.group, act))
-    workspace = torch.empty(ws, dtype=torch.uint8, device=x.device) if ws else None
+    if workspace is None:
+        workspace = workspace_for(x.device, ws)
+    elif ws:
+        _need(workspace, torch.uint8, (workspace.numel(),), "workspace")
+        ws = workspace.numel()
     args = (_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K, packed.group,
             int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
     if config:

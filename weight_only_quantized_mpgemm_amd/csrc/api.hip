@@ -57,8 +57,6 @@ int select_config(int M, int K) {
 int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
               int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
               size_t workspace_bytes, int config_id, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;   // no configuration uses a workspace (mpgemm_workspace_bytes is 0)
     if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
     if (symmetric != 0 && symmetric != 1) return MPGEMM_ERR_INVALID_ARG;
     const int st = check_shape(M, N, K, group);
@@ -93,6 +91,12 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     a.K = K;
     a.group = group;
     a.act = dtype == MPGEMM_BF16 ? mpgemm::kBF16 : mpgemm::kF16;
+    a.workspace = workspace;
+    if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4) {
+        const size_t need = mpgemm::decode_workspace_bytes(N, K, cfg);
+        if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+            return MPGEMM_ERR_WORKSPACE;
+    }
     if (getenv("MPGEMM_LOG"))
         fprintf(stderr, "mpgemm: M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", M, N, K, group,
                 dtype, symmetric, mpgemm_config_name(cfg));
@@ -154,12 +158,14 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
 }
 
 size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
-    (void)M;
-    (void)N;
-    (void)K;
-    (void)group;
     (void)dtype;
-    return 0;
+    if (check_shape(M, N, K, group) != MPGEMM_OK || M == 0 || N == 0 || K == 0) return 0;
+    size_t need = 0;
+    for (int mblocks = (M + 15) / 16; mblocks <= 4; ++mblocks) {
+        const size_t b = mpgemm::decode_workspace_bytes(N, K, mblocks);
+        if (b > need) need = b;
+    }
+    return need;
 }
 
 int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,

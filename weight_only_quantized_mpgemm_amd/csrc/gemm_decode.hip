@@ -21,8 +21,15 @@
 //     step.  Activation rows past M fall outside the activation descriptor and read as
 //     zero without any memory traffic, so M = 1 moves 1/16 of a full row block;
 //   - weights are the MFMA A operand (rows = n), activations the B operand (columns = m);
-//   - the NW partial sums meet in LDS and are added in a fixed wave order: results are
-//     deterministic, with no global workspace and no atomics.
+//   - the NW partial sums meet in LDS and are added in a fixed wave order;
+//   - optionally the K range is also split over P workgroups (grid.y).  Every workgroup of
+//     a strip group writes its fp32 partial to the workspace, then bumps the group's
+//     counter; the workgroup that arrives last adds the P partials in split order, stores
+//     Y and sets the counter back to zero.  Nobody waits for anybody, the sum order is
+//     fixed (results are deterministic for a given split), and the counters are left as
+//     they were found, so the workspace needs zeroing only once.  P > 1 balances the work
+//     over the CUs and lets several strips share one activation fragment (S) without
+//     leaving CUs idle at small N.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -46,7 +53,7 @@ template <int ACT, int MB, int S, bool SYM, int G, int D>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    uint16_t *__restrict__ Y) {
+    uint16_t *__restrict__ Y, f32x4_t *__restrict__ part, uint32_t *__restrict__ cnt) {
     constexpr int GPT = kTileK / G;              // groups per 128-k tile (1 or 2)
     typedef Slot<MB, S, GPT> SlotT;
     extern __shared__ f32x4_t red[];             // [NW][S][MB][64]
@@ -58,8 +65,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int KT = K >> 7;
-    const int t_begin = (KT * wave) / NW;
-    const int n = (KT * (wave + 1)) / NW - t_begin;
+    // This workgroup's K range (split p of P), then this wave's share of it.
+    const int P = gridDim.y, p = blockIdx.y;
+    const int k_lo = (KT * p) / P, k_n = (KT * (p + 1)) / P - k_lo;
+    const int t_begin = k_lo + (k_n * wave) / NW;
+    const int n = k_lo + (k_n * (wave + 1)) / NW - t_begin;
     const int groups = K / G;
     const int strips = N >> 4;
     const int strip0 = blockIdx.x * S;
@@ -158,85 +168,135 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     }
 
     const int col_lane = 4 * (lane >> 4);
-    if (NW == 1) {
-#pragma unroll
-        for (int si = 0; si < S; ++si) {
-            if (strip0 + si >= strips) continue;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int m = mb * 16 + (lane & 15);
-                if (m < M)
-                    *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + (strip0 + si) * 16 + col_lane) =
-                        round4<ACT>(acc[si][mb]);
-            }
-        }
-        return;
-    }
-#pragma unroll
-    for (int si = 0; si < S; ++si)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) red[((wave * S + si) * MB + mb) * 64 + lane] = acc[si][mb];
-    __syncthreads();
-    for (int b = wave; b < S * MB; b += NW) {
-        const int si = b / MB, mb = b % MB;
-        f32x4_t sum = red[b * 64 + lane];
-        for (int w2 = 1; w2 < NW; ++w2) sum += red[(w2 * S * MB + b) * 64 + lane];
+    auto store_y = [&](int si, int mb, const f32x4_t &v) {
         const int m = mb * 16 + (lane & 15);
         if (m < M && strip0 + si < strips)
             *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + (strip0 + si) * 16 + col_lane) =
-                round4<ACT>(sum);
+                round4<ACT>(v);
+    };
+    // Partial of block b (strip si = b / MB, row block mb = b % MB) of split q.
+    auto part_at = [&](int q, int b) -> f32x4_t & {
+        return part[(((size_t)blockIdx.x * P + q) * (S * MB) + b) * 64 + lane];
+    };
+    if (NW == 1 && P == 1) {
+#pragma unroll
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) store_y(si, mb, acc[si][mb]);
+        return;
     }
+    if (NW == 1) {
+#pragma unroll
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) part_at(p, si * MB + mb) = acc[si][mb];
+    } else {
+#pragma unroll
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                red[((wave * S + si) * MB + mb) * 64 + lane] = acc[si][mb];
+        __syncthreads();
+        for (int b = wave; b < S * MB; b += NW) {
+            f32x4_t sum = red[b * 64 + lane];
+            for (int w2 = 1; w2 < NW; ++w2) sum += red[(w2 * S * MB + b) * 64 + lane];
+            if (P == 1)
+                store_y(b / MB, b % MB, sum);
+            else
+                part_at(p, b) = sum;
+        }
+        if (P == 1) return;
+    }
+    // Split-K fixup: publish this partial, count it, and let the last arriver finish.  Every
+    // wave fences its own partial stores (a fence only waits for the issuing wave's memory
+    // operations) before the barrier; then one thread counts the workgroup in.
+    __shared__ uint32_t is_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        is_last = atomicAdd(&cnt[blockIdx.x], 1u) == (uint32_t)(P - 1);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __threadfence();
+    for (int b = wave; b < S * MB; b += NW) {
+        f32x4_t sum = part_at(0, b);
+        for (int q = 1; q < P; ++q) sum += part_at(q, b);
+        store_y(b / MB, b % MB, sum);
+    }
+    if (threadIdx.x == 0) atomicExch(&cnt[blockIdx.x], 0u);
 }
 
-// Strips per workgroup (S) and waves per workgroup (NW).  S > 1 lets one activation
-// fragment feed S strips (less L1/L2 traffic per weight byte); NW splits K inside the
-// workgroup.  Measured on MI355X at the Llama-3-8B projection shapes: each wave does best
-// with a K slice of about 8 tile steps or more (a deep enough register pipeline), and with
-// the largest S that still leaves >= 128 workgroups.  MPGEMM_DECODE_SPLIT="S,NW" overrides
-// the choice for tuning sweeps (S in {1,2,4} with one row block, {1,2} with two, 1 above;
-// NW in 1..8).
+// Workspace of a split: a fixed region of counters (one per strip group) at the start, then
+// one 1 KiB fp32 block per (strip, row block, split).  The counter region has the same size
+// for every shape, so partials of one call never land on counters of another call that
+// shares the workspace (counters must read zero at every call's start).
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr int kMaxGroups = (int)(kCounterBytes / 4);
+
+// Strips per workgroup (S), waves per workgroup (NW) and workgroups per strip group along
+// K (P).  S > 1 lets one activation fragment feed S strips (less L2 traffic per weight
+// byte, which matters as M grows); NW and P split K inside and across workgroups.
+// MPGEMM_DECODE_SPLIT="S,NW" or "S,NW,P" overrides the choice for tuning sweeps (S in
+// {1,2,4} with one row block, {1,2} with two, 1 above; NW in 1..8; P in 1..16).
 struct Split {
-    int s, nw;
+    int s, nw, p;
 };
 Split pick_split(int strips, int KT, int mblocks) {
-    Split sp{1, 1};
+    Split sp{1, 1, 1};
     if (mblocks == 1) sp.s = strips >= 1024 ? 4 : (strips >= 256 && KT <= 64 ? 2 : 1);
     else if (mblocks == 2) sp.s = strips >= 512 ? 2 : 1;
     sp.nw = KT / 8;
     if (sp.nw < 1) sp.nw = 1;
     if (sp.nw > kMaxWaves) sp.nw = kMaxWaves;
     if (const char *env = getenv("MPGEMM_DECODE_SPLIT")) {
-        int s = 0, nw = 0;
-        if (sscanf(env, "%d,%d", &s, &nw) == 2 && (s == 1 || s == 2 || s == 4) && nw >= 1 &&
-            nw <= kMaxWaves && nw <= KT && (s == 1 || mblocks <= 2) && (s < 4 || mblocks == 1)) {
+        int s = 0, nw = 0, p = 1;
+        const int got = sscanf(env, "%d,%d,%d", &s, &nw, &p);
+        if (got >= 2 && (s == 1 || s == 2 || s == 4) && nw >= 1 && nw <= kMaxWaves &&
+            p >= 1 && p <= 16 && nw * p <= KT && (s == 1 || mblocks <= 2) &&
+            (s < 4 || mblocks == 1)) {
             sp.s = s;
             sp.nw = nw;
+            sp.p = got == 3 ? p : 1;
         }
     }
+    if ((strips + sp.s - 1) / sp.s > kMaxGroups) sp.p = 1;     // more groups than counters
     return sp;
 }
 
+size_t split_workspace(const Split &sp, int strips, int mblocks) {
+    if (sp.p == 1) return 0;
+    const size_t groups = (size_t)(strips + sp.s - 1) / sp.s;
+    return kCounterBytes + groups * sp.p * sp.s * mblocks * 64 * sizeof(f32x4_t);
+}
+
 template <int ACT, int MB, int S, bool SYM, int G>
-void launch_s(const GemmArgs &a, int nw, hipStream_t stream) {
+void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
     constexpr int slot_regs = S * 4 + 16 * MB + 2 * S;
     constexpr int D = slot_regs <= 24 ? 4 : (slot_regs <= 40 ? 3 : 2);
     const int strips = a.N >> 4;
     const int wgs = (strips + S - 1) / S;
-    const size_t lds = nw > 1 ? (size_t)nw * S * MB * 64 * sizeof(f32x4_t) : 0;
-    decode_kernel<ACT, MB, S, SYM, G, D><<<dim3(wgs), dim3(nw * 64), lds, stream>>>(
-        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
+    const size_t lds = sp.nw > 1 ? (size_t)sp.nw * S * MB * 64 * sizeof(f32x4_t) : 0;
+    uint32_t *cnt = nullptr;
+    f32x4_t *part = nullptr;
+    if (sp.p > 1) {
+        cnt = static_cast<uint32_t *>(a.workspace);
+        part = reinterpret_cast<f32x4_t *>(static_cast<char *>(a.workspace) + kCounterBytes);
+    }
+    decode_kernel<ACT, MB, S, SYM, G, D><<<dim3(wgs, sp.p), dim3(sp.nw * 64), lds, stream>>>(
+        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y, part, cnt);
 }
 
 template <int ACT, int MB, bool SYM, int G>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     const Split sp = pick_split(a.N >> 4, a.K >> 7, MB);
     if constexpr (MB == 1) {
-        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G>(a, sp.nw, stream);
+        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G>(a, sp, stream);
     }
     if constexpr (MB <= 2) {
-        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G>(a, sp.nw, stream);
+        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G>(a, sp, stream);
     }
-    launch_s<ACT, MB, 1, SYM, G>(a, sp.nw, stream);
+    launch_s<ACT, MB, 1, SYM, G>(a, sp, stream);
 }
 
 template <int ACT, int MB>
@@ -260,6 +320,10 @@ void launch_act(const GemmArgs &a, int mblocks, hipStream_t stream) {
 }
 
 }  // namespace
+
+size_t decode_workspace_bytes(int N, int K, int mblocks) {
+    return split_workspace(pick_split(N >> 4, K >> 7, mblocks), N >> 4, mblocks);
+}
 
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream) {
     if (a.act == kBF16) {

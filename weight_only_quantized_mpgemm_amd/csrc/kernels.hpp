@@ -27,11 +27,15 @@ struct GemmArgs {
     uint16_t *Y;                // [M][N] output bits
     int M, N, K, group;
     int act;                    // Act
+    void *workspace;            // decode split-K partials and counters (see decode kernel)
 };
 
 // Small-M kernel: one 16-column strip per workgroup, the K range split over the waves of the
 // workgroup, `mblocks` row blocks of 16 (M <= 16 * mblocks, mblocks in 1..4).
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
+// Workspace bytes launch_decode needs for this shape (0 when K is not split over
+// workgroups).  The counter region must be zero before the first call; calls leave it zero.
+size_t decode_workspace_bytes(int N, int K, int mblocks);
 
 // Tiled large-M kernels (128 rows x 256 columns per workgroup): the LDS-ring kernel
 // (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
