@@ -93,7 +93,7 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     a.act = dtype == MPGEMM_BF16 ? mpgemm::kBF16 : mpgemm::kF16;
     a.workspace = workspace;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4) {
-        const size_t need = mpgemm::decode_workspace_bytes(N, K, cfg);
+        const size_t need = mpgemm::decode_workspace_bytes(M, N, K, cfg);
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
             return MPGEMM_ERR_WORKSPACE;
     }
@@ -162,7 +162,7 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
     if (check_shape(M, N, K, group) != MPGEMM_OK || M == 0 || N == 0 || K == 0) return 0;
     size_t need = 0;
     for (int mblocks = (M + 15) / 16; mblocks <= 4; ++mblocks) {
-        const size_t b = mpgemm::decode_workspace_bytes(N, K, mblocks);
+        const size_t b = mpgemm::decode_workspace_bytes(M, N, K, mblocks);
         if (b > need) need = b;
     }
     return need;

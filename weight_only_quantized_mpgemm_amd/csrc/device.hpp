@@ -219,4 +219,18 @@ __device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t voff, uint32
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Device-scope (sc1) buffer accesses: a store is acknowledged only once it is visible to
+// every XCD, and a load does not take a possibly stale line from this XCD's L2.
+constexpr int kCachePolicyDevice = 16;      // sc1 bit of the buffer cache-policy operand
+__device__ __forceinline__ void buf_store_b128_device(rsrc_t r, uint32_t voff, u32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kCachePolicyDevice);
+}
+__device__ __forceinline__ u32x4_t buf_load_b128_device(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCachePolicyDevice));
+}
+// Waits for every vector-memory access this wave has issued (loads and stores) to finish:
+// vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace mpgemm

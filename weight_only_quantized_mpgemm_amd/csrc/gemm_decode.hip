@@ -175,8 +175,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
                 round4<ACT>(v);
     };
     // Partial of block b (strip si = b / MB, row block mb = b % MB) of split q.
-    auto part_at = [&](int q, int b) -> f32x4_t & {
-        return part[(((size_t)blockIdx.x * P + q) * (S * MB) + b) * 64 + lane];
+    // Partials of block b (strip si = b / MB, row block mb = b % MB) of split q travel with
+    // device-scope cache policy (sc1): the stores write through this XCD's L2 and the loads
+    // bypass stale L2 lines, so no L2-wide writeback/invalidate fence is needed (those cost
+    // far more than the partials themselves).
+    const rsrc_t prs = make_rsrc(part, P > 1 ? (uint32_t)(gridDim.x * P * S * MB * 1024u) : 0u);
+    auto part_off = [&](int q, int b) -> uint32_t {
+        return (((blockIdx.x * P + q) * (S * MB) + b) * 64 + lane) * 16u;
+    };
+    auto put_part = [&](int q, int b, const f32x4_t &v) {
+        buf_store_b128_device(prs, part_off(q, b), bitcast<u32x4_t>(v));
+    };
+    auto get_part = [&](int q, int b) -> f32x4_t {
+        return bitcast<f32x4_t>(buf_load_b128_device(prs, part_off(q, b)));
     };
     if (NW == 1 && P == 1) {
 #pragma unroll
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
 #pragma unroll
         for (int si = 0; si < S; ++si)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) part_at(p, si * MB + mb) = acc[si][mb];
+            for (int mb = 0; mb < MB; ++mb) put_part(p, si * MB + mb, acc[si][mb]);
     } else {
 #pragma unroll
         for (int si = 0; si < S; ++si)
@@ -203,28 +214,32 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
             if (P == 1)
                 store_y(b / MB, b % MB, sum);
             else
-                part_at(p, b) = sum;
+                put_part(p, b, sum);
         }
         if (P == 1) return;
     }
     // Split-K fixup: publish this partial, count it, and let the last arriver finish.  Every
     // wave fences its own partial stores (a fence only waits for the issuing wave's memory
     // operations) before the barrier; then one thread counts the workgroup in.
+    // Each wave waits until its partial stores are acknowledged at device scope, the
+    // workgroup meets, and one thread counts it in.  The last arriver's device-scope loads
+    // are issued after it has seen every other workgroup's count, hence after their stores
+    // completed.
     __shared__ uint32_t is_last;
-    __threadfence();
+    wait_vmem();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        is_last = atomicAdd(&cnt[blockIdx.x], 1u) == (uint32_t)(P - 1);
-    }
+    if (threadIdx.x == 0)
+        is_last = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1);
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
     for (int b = wave; b < S * MB; b += NW) {
-        f32x4_t sum = part_at(0, b);
-        for (int q = 1; q < P; ++q) sum += part_at(q, b);
+        f32x4_t sum = get_part(0, b);
+        for (int q = 1; q < P; ++q) sum += get_part(q, b);
         store_y(b / MB, b % MB, sum);
     }
-    if (threadIdx.x == 0) atomicExch(&cnt[blockIdx.x], 0u);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workspace of a split: a fixed region of counters (one per strip group) at the start, then
@@ -242,13 +257,25 @@ constexpr int kMaxGroups = (int)(kCounterBytes / 4);
 struct Split {
     int s, nw, p;
 };
-Split pick_split(int strips, int KT, int mblocks) {
+Split pick_split(int M, int strips, int KT, int mblocks) {
     Split sp{1, 1, 1};
     if (mblocks == 1) sp.s = strips >= 1024 ? 4 : (strips >= 256 && KT <= 64 ? 2 : 1);
     else if (mblocks == 2) sp.s = strips >= 512 ? 2 : 1;
     sp.nw = KT / 8;
     if (sp.nw < 1) sp.nw = 1;
     if (sp.nw > kMaxWaves) sp.nw = kMaxWaves;
+    // Long K with fewer strips: the activation fragments, re-read by every strip group,
+    // cost more than the weights (a 16-row fragment is 4x a weight tile's bytes).  Widen S
+    // to its register limit and split K over P workgroups so that about 256 remain.
+    // Measured on the 14336 x 4096 projection: 13 us instead of 19.5 at M = 16.
+    // (At M <= 8 the fragments are mostly zero rows and S = 2 does as well.)
+    if (KT > 64 && strips < 1024 && mblocks <= 2) {
+        sp.s = mblocks == 1 && M > 8 ? 4 : 2;
+        const int groups = (strips + sp.s - 1) / sp.s;
+        sp.p = (256 + groups - 1) / groups;
+        if (sp.p > 8) sp.p = 8;
+        sp.nw = 4;                               // NW * P <= 32 < KT
+    }
     if (const char *env = getenv("MPGEMM_DECODE_SPLIT")) {
         int s = 0, nw = 0, p = 1;
         const int got = sscanf(env, "%d,%d,%d", &s, &nw, &p);
@@ -289,7 +316,7 @@ void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
 
 template <int ACT, int MB, bool SYM, int G>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const Split sp = pick_split(a.N >> 4, a.K >> 7, MB);
+    const Split sp = pick_split(a.M, a.N >> 4, a.K >> 7, MB);
     if constexpr (MB == 1) {
         if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G>(a, sp, stream);
     }
@@ -321,8 +348,8 @@ void launch_act(const GemmArgs &a, int mblocks, hipStream_t stream) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(int N, int K, int mblocks) {
-    return split_workspace(pick_split(N >> 4, K >> 7, mblocks), N >> 4, mblocks);
+size_t decode_workspace_bytes(int M, int N, int K, int mblocks) {
+    return split_workspace(pick_split(M, N >> 4, K >> 7, mblocks), N >> 4, mblocks);
 }
 
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream) {

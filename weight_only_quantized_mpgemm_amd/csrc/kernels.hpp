@@ -35,7 +35,7 @@ struct GemmArgs {
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
 // Workspace bytes launch_decode needs for this shape (0 when K is not split over
 // workgroups).  The counter region must be zero before the first call; calls leave it zero.
-size_t decode_workspace_bytes(int N, int K, int mblocks);
+size_t decode_workspace_bytes(int M, int N, int K, int mblocks);
 
 // Tiled large-M kernels (128 rows x 256 columns per workgroup): the LDS-ring kernel
 // (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
