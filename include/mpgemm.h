@@ -150,8 +150,10 @@ int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void 
  * MPGEMM_ERR_UNSUPPORTED).  Ids: 1..4 small-M kernel with 1..4 row blocks of 16
  * (M <= 16*id); 10 tiled large-M kernel on 16x16x32 MFMAs with a four-stage LDS ring;
  * 11 tiled large-M kernel with two LDS buffers (any K); 12 tiled large-M kernel on 32x32x16
- * MFMAs with a four-stage LDS ring.  Ids 10 and 12 need K % 256 == 0 and run as id 11 on
- * other K.  The selector picks 1..4 for M <= 64, else 12 when K % 256 == 0, else 11.
+ * MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a 256 x 128
+ * tile.  Ids 10, 12 and 13 need K % 256 == 0 and run as id 11 on other K.  The selector
+ * picks 1..4 for M <= 64; else 11 when K % 256 != 0; else 13 when M >= 512 and
+ * (N >= 16384 or K >= 8192); else 12.
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);

@@ -65,7 +65,11 @@ def test_selector_and_config_names():
     assert mp.lib().mpgemm_select_config(2048, 4096, 4096, 128, 0) == 12
     assert mp.lib().mpgemm_select_config(2048, 4096, 4224, 128, 0) == 11   # K % 256 != 0
     assert mp.lib().mpgemm_select_config(64, 4096, 4224, 128, 0) == 4
-    for cid in (1, 2, 3, 4, 10, 11, 12):
+    assert mp.lib().mpgemm_select_config(2048, 6144, 4096, 128, 0) == 12
+    assert mp.lib().mpgemm_select_config(2048, 28672, 4096, 128, 0) == 13  # wide N
+    assert mp.lib().mpgemm_select_config(2048, 4096, 14336, 128, 0) == 13  # long K
+    assert mp.lib().mpgemm_select_config(256, 28672, 4096, 128, 0) == 12   # M < 512
+    for cid in (1, 2, 3, 4, 10, 11, 12, 13):
         assert mp.config_name(cid)
     assert mp.config_name(7) == ""
 

@@ -25,6 +25,8 @@ DECODE_CONFIGS = (1, 2, 3, 4)
 PREFILL = 10          # 16x16x32 LDS-ring kernel (two-buffer kernel when K % 256 != 0)
 PREFILL_2BUF = 11
 PREFILL_X32 = 12      # 32x32x16 kernel (two-buffer kernel when K % 256 != 0)
+PREFILL_X32_TALL = 13  # the same with a 256 x 128 workgroup tile
+PREFILL_CONFIGS = (PREFILL, PREFILL_2BUF, PREFILL_X32, PREFILL_X32_TALL)
 
 
 def say(msg):
@@ -32,7 +34,7 @@ def say(msg):
 
 
 def configs_for(M):
-    return [c for c in DECODE_CONFIGS if M <= 16 * c] + [PREFILL, PREFILL_2BUF, PREFILL_X32]
+    return [c for c in DECODE_CONFIGS if M <= 16 * c] + list(PREFILL_CONFIGS)
 
 
 # ------------------------------------------------------------------------ transfer --
@@ -129,7 +131,7 @@ def test_pack_ignores_high_bits_of_codes_and_zeros():
 
 # -------------------------------------------------------------- bit-exact GEMM cases --
 
-@pytest.mark.parametrize("config", [PREFILL, PREFILL_2BUF, PREFILL_X32])
+@pytest.mark.parametrize("config", PREFILL_CONFIGS)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("g,sym", [(128, False), (64, True)])
 def test_identity_activations_give_dequantized_weights_bit_exact(dtype, g, sym, config):
@@ -235,12 +237,13 @@ def test_llama3_8b_decode_full_shapes(M, K, N, label):
 @pytest.mark.parametrize("M", [512, 2048])
 @pytest.mark.parametrize("K,N,label", workloads.LLAMA3_8B_SHAPES)
 def test_llama3_8b_prefill_full_shapes(M, K, N, label):
-    _full_shape(workloads.LLAMA3_8B_PREFILL, M, K, N)
+    _full_shape(workloads.LLAMA3_8B_PREFILL, M, K, N, configs=[0, PREFILL_X32, PREFILL_X32_TALL])
 
 
 @pytest.mark.parametrize("K,N,label", [(4096, 28672, "gate_up"), (14336, 4096, "down")])
 def test_llama3_8b_prefill_m8192(K, N, label):
-    _full_shape(workloads.LLAMA3_8B_PREFILL, 8192, K, N, nrows=8, ncols=96)
+    _full_shape(workloads.LLAMA3_8B_PREFILL, 8192, K, N, nrows=8, ncols=96,
+                configs=[0, PREFILL_X32, PREFILL_X32_TALL])
 
 
 @pytest.mark.parametrize("M", [1, 64])
@@ -251,7 +254,8 @@ def test_llama3_70b_bf16_small_m(M, K, N, label):
 
 @pytest.mark.parametrize("K,N,label", [(8192, 57344, "gate_up"), (28672, 8192, "down")])
 def test_llama3_70b_bf16_m4096(K, N, label):
-    _full_shape(workloads.LLAMA3_70B, 4096, K, N, nrows=6, ncols=64)
+    _full_shape(workloads.LLAMA3_70B, 4096, K, N, nrows=6, ncols=64,
+                configs=[0, PREFILL_X32, PREFILL_X32_TALL])
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 16, 128, 1024])
@@ -261,7 +265,8 @@ def test_qwen3_32b_sym_g64(M, K, N, label):
 
 
 def test_qwen3_32b_m8192_gate_up():
-    _full_shape(workloads.QWEN3_32B, 8192, 5120, 51200, nrows=6, ncols=64)
+    _full_shape(workloads.QWEN3_32B, 8192, 5120, 51200, nrows=6, ncols=64,
+                configs=[0, PREFILL_X32, PREFILL_X32_TALL])
 
 
 # --------------------------------------------------------------------- edge cases ---

@@ -23,6 +23,7 @@ enum ConfigId {
     kConfigPrefill = 10,       // 16x16x32 LDS-ring kernel when K % 256 == 0, else two-buffer
     kConfigPrefill2Buf = 11,   // two-buffer kernel
     kConfigPrefillX32 = 12,    // 32x32x16 kernel when K % 256 == 0, else the two-buffer one
+    kConfigPrefillX32Tall = 13,  // same, 256 x 128 workgroup tile
 };
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -45,13 +46,17 @@ int hip_status(hipError_t e) {
 }
 
 // Small M streams the weights once (HBM-bound): the split-K strip kernel with one to four
-// row blocks of 16.  Larger M is bound by the matrix cores: the 128 x 256 tiled kernel.
-int select_config(int M, int K) {
+// row blocks of 16.  Larger M is bound by the matrix cores: the 32x32x16 tiled kernel, with
+// the 256 x 128 tile (each dequantized weight feeds 256 rows) for long K or wide N, where
+// it measured 6-15% faster on MI355X; the 128 x 256 tile for the rest (it was 2-4% faster
+// at K = 4096, N <= 6144).
+int select_config(int M, int N, int K) {
     if (M <= 16) return kConfigDecode1;
     if (M <= 32) return kConfigDecode2;
     if (M <= 48) return kConfigDecode3;
     if (M <= 64) return kConfigDecode4;
-    return K % 256 == 0 ? kConfigPrefillX32 : kConfigPrefill2Buf;
+    if (K % 256 != 0) return kConfigPrefill2Buf;
+    return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
 }
 
 int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
@@ -64,7 +69,7 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     if (config_id != kConfigSelect &&
         !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) ||
           config_id == kConfigPrefill || config_id == kConfigPrefill2Buf ||
-          config_id == kConfigPrefillX32))
+          config_id == kConfigPrefillX32 || config_id == kConfigPrefillX32Tall))
         return MPGEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MPGEMM_OK;
     if (Y == nullptr) return MPGEMM_ERR_INVALID_ARG;
@@ -76,7 +81,7 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     if (!aligned16(X) || !aligned16(packed_codes) || !aligned16(packed_meta))
         return MPGEMM_ERR_ALIGNMENT;
 
-    const int cfg = config_id == kConfigSelect ? select_config(M, K) : config_id;
+    const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
 
@@ -102,7 +107,10 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
                 dtype, symmetric, mpgemm_config_name(cfg));
     if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
     if (cfg == kConfigPrefillX32 && K % 256 == 0) return hip_status(mpgemm::launch_prefill_x32(a, s));
-    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf || cfg == kConfigPrefillX32)
+    if (cfg == kConfigPrefillX32Tall && K % 256 == 0)
+        return hip_status(mpgemm::launch_prefill_x32_tall(a, s));
+    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf || cfg == kConfigPrefillX32 ||
+        cfg == kConfigPrefillX32Tall)
         return hip_status(mpgemm::launch_prefill(a, s));
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
@@ -184,10 +192,9 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
 }
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {
-    (void)N;
     (void)group;
     (void)dtype;
-    return select_config(M < 0 ? 0 : M, K);
+    return select_config(M < 0 ? 0 : M, N, K);
 }
 
 const char *mpgemm_config_name(int config_id) {
@@ -199,6 +206,7 @@ const char *mpgemm_config_name(int config_id) {
         case kConfigPrefill: return "prefill_ring16_128x256";
         case kConfigPrefill2Buf: return "prefill_2buf_128x256";
         case kConfigPrefillX32: return "prefill_x32_128x256";
+        case kConfigPrefillX32Tall: return "prefill_x32_256x128";
         default: return "";
     }
 }

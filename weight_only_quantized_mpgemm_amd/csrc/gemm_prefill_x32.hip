@@ -13,10 +13,16 @@
 // dequantization alone needs (13 vector operations per 8 weights, each weight feeding
 // 128 rows).
 //
-// Design (K % 256 == 0):
-//   - workgroup tile 128 (m) x 256 (n), four waves side by side along n, each owning a
-//     128 x 64 block = 2 (n) x 4 (m) blocks of 32 x 32, 128 fp32 accumulators per lane in
-//     AGPRs, updated in place by inline-asm MFMA;
+// Design (K % 256 == 0), in two tile shapes of equal work per wave (NB column blocks x
+// MB = 8 / NB row blocks of 32 x 32):
+//   - NB = 2: workgroup tile 128 (m) x 256 (n), four waves side by side along n, each
+//     owning a 128 x 64 block = 2 (n) x 4 (m) blocks;
+//   - NB = 1: workgroup tile 256 (m) x 128 (n), each wave a 256 x 32 block = 1 (n) x 8 (m)
+//     blocks.  Every dequantized weight then feeds 256 rows instead of 128, halving the
+//     dequantization work (and the weight loads) per MFMA, for twice the LDS operand reads
+//     (one ds_read_b128 per MFMA; gfx950's LDS sustains that beside full-rate MFMAs);
+//   - either way 128 fp32 accumulators per lane in AGPRs, updated in place by inline-asm
+//     MFMA;
 //   - weights are the A operand (rows = n): lane l holds column n = l % 32 of a 32-column
 //     block (two 16-column strips of the packed layout) at k = 16u + 8 (l / 32) .. +7 of a
 //     32-deep step.  In the packed layout that is strip (l % 32) / 16, lane position
@@ -27,14 +33,16 @@
 //     issued three tiles (six stages) ahead into four register sets used in rotation (one
 //     tile ahead in two sets for g = 64) --
 //     HBM latency under full load exceeds the one to two stages a two-set scheme gives;
-//   - activations are the B operand (columns = m), read from a ring of four 128 x 64 LDS
+//   - activations are the B operand (columns = m), read from a ring of four BM x 64 LDS
 //     stages filled by buffer_load_dwordx4 ... lds three stages ahead (XOR-swizzled 16-byte
 //     chunks, chunk ^ row % 8, so eight consecutive rows hit eight bank groups);
-//   - each 32-deep step runs 16 MFMAs; after MFMA i come 1/16 of the next step's work: an
-//     LDS operand read on even i and about three of the 52 dequantization operations of
-//     the next step's four weight words, taken round-robin over the words so no operation
-//     directly follows the one it depends on.  The dequantization is inline asm too, so
-//     the compiler neither reorders it nor pads it with wait states meant for the MFMAs.
+//   - each 32-deep step runs 16 MFMAs; after MFMA i come 1/16 of the next step's work: its
+//     LDS operand reads (2 MB per step) and dequantization operations (13 or 14 for each of
+//     the next step's 2 NB weight words).  With four words the operations go round-robin
+//     over them, so no operation directly follows the one it depends on; with two, word 0
+//     is done first, since the next step's first MFMA needs it.  The dequantization is
+//     inline asm too, so the compiler neither reorders it nor pads it with wait states
+//     meant for the MFMAs.
 #include <utility>
 
 #include "kernels.hpp"
@@ -45,15 +53,14 @@ namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kXBM = 128;
-constexpr int kXBN = 256;
 constexpr int kXThreads = 256;
 constexpr int kXStages = 4;                  // 64-deep LDS stages in the ring
+constexpr int tile_m(int nb) { return 32 * (8 / nb); }   // workgroup tile rows (m)
+constexpr int tile_n(int nb) { return 128 * nb; }        // workgroup tile columns (n)
 // Weight register sets (loads run NWS - 1 tiles ahead): four for g = 128; two for g = 64,
 // whose doubled scale/zero registers would not fit four sets without spilling.
 template <int G>
 constexpr int kXWSets = G == 128 ? 4 : 2;
-constexpr int kXChunks = kXBM * 8;           // 16-byte chunks per stage (8 per 64-deep row)
 
 template <int N>
 struct IC {
@@ -82,6 +89,23 @@ __device__ __forceinline__ void mfma32<kF16>(f32x16_t &c, const u32x4_t &a, cons
 template <>
 __device__ __forceinline__ void mfma32<kBF16>(f32x16_t &c, const u32x4_t &a, const u32x4_t &b) {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// acc = acc + 0 * 0 on every block through the compiler-visible builtin (see the kernel's
+// epilogue).
+template <int ACT, int NB, int MB>
+__device__ __forceinline__ void finish_acc(f32x16_t (&acc)[NB][MB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (ACT == kF16)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(half8_t{}, half8_t{},
+                                                                     acc[nb][mb], 0, 0, 0);
+            else
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_t{}, bf16x8_t{},
+                                                                      acc[nb][mb], 0, 0, 0);
+        }
 }
 
 // Constants the dequantization keeps in registers for the whole kernel.  Produced by asm
@@ -184,7 +208,7 @@ __device__ __forceinline__ void tile_of(int b, int tm, int tn, int &mt, int &nt)
     nt = r / gm;
 }
 
-template <int ACT, bool SYM, int G, int NWS>
+template <int ACT, bool SYM, int G, int NWS, int NB>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
@@ -192,22 +216,26 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     typedef typename Dq<ACT>::type DqT;
     typedef DqOps<ACT> Ops;
     constexpr int GPT = kTileK / G;          // groups per 128-deep tile (1 or 2)
-    // Loads each wave issues per weight tile: four 16-byte code slots (2 column blocks x
-    // 2 k halves), plus scales (and zeros) per column block and group.
-    constexpr int kWLoads = 4 + 2 * GPT * (SYM ? 1 : 2);
-    __shared__ u32x4_t xs[kXStages][kXChunks];
+    constexpr int MB = 8 / NB;               // 32-row blocks per wave
+    constexpr int BM = tile_m(NB), BN = tile_n(NB);
+    constexpr int kChunks = BM * 8;          // 16-byte chunks per stage (8 per 64-deep row)
+    // Loads each wave issues per weight tile: 2 NB 16-byte code slots (column blocks x
+    // k halves), plus scales (and zeros) per column block and group.
+    constexpr int kWLoads = 2 * NB + NB * GPT * (SYM ? 1 : 2);
+    static_assert(kWLoads <= 16, "weight loads are spread over one step's 16 MFMAs");
+    __shared__ u32x4_t xs[kXStages][kChunks];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     int mt, nt;
-    tile_of(blockIdx.x, (M + kXBM - 1) / kXBM, (N + kXBN - 1) / kXBN, mt, nt);
-    const int m_blk = mt * kXBM;
+    tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
+    const int m_blk = mt * BM;
     const int KT = K >> 7;                   // 128-deep weight tiles
     const int S = K >> 6;                    // 64-deep stages (a multiple of 4)
     const int groups = K / G;
     const int strips = N >> 4;
-    const int strip0 = nt * (kXBN / 16) + wave * 4;
+    const int strip0 = nt * (BN / 16) + wave * 2 * NB;
 
     const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
     const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024));
@@ -215,13 +243,16 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / 2));
     const DqConst dc = make_dq_const();
 
-    // DMA source offsets: wave w fills blocks b = 4w + i of every stage; block b holds rows
-    // 8b .. 8b+7, lane l writes LDS chunk 64b + l = (row 8b + l/8, physical chunk l%8),
+    // DMA source offsets: wave w fills blocks b = MB w + i of every stage; block b holds
+    // rows 8b .. 8b+7, lane l writes LDS chunk 64b + l = (row 8b + l/8, physical chunk l%8),
     // which holds logical chunk (l%8) ^ (l/8).  Rows past M read zeros (one past the end).
-    uint32_t xoff[4];
+    // (Offset arrays have fixed bounds, of which MB / NB entries are used: with bounds
+    // that depend on a template parameter, the host pass of this compiler silently emits
+    // no launch stub for the kernel.)
+    uint32_t xoff[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (wave * 4 + i) + (lane >> 3);
+    for (int i = 0; i < MB; ++i) {
+        const int r = 8 * (wave * MB + i) + (lane >> 3);
         const uint32_t row = (uint32_t)min(m_blk + r, M);
         xoff[i] = (row * K + (((lane & 7) ^ (lane >> 3)) * 8)) * 2u;
     }
@@ -230,7 +261,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const int my_strip_in_pair = (lane & 31) >> 4;
     uint32_t woff[2][2], soff[2], zoff[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
         const uint32_t strip = (uint32_t)min(strip0 + 2 * nb + my_strip_in_pair, strips - 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -248,40 +279,40 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const int brow = (lane & 31) * 8;
     const int cb = (lane >> 5) ^ (lane & 7);
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[NB][MB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16_t{};
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16_t{};
 
     struct WSet {
-        u32x4_t w[2][2];                     // [nb][u], words = 32-deep steps of the tile
-        uint32_t s[2][GPT], z[2][GPT];
+        u32x4_t w[NB][2];                    // [nb][u], words = 32-deep steps of the tile
+        uint32_t s[NB][GPT], z[NB][GPT];
     };
     static_assert(NWS == 2 || NWS == 4, "the stage loop unrolls 2 * NWS stages");
     WSet ws[NWS];
-    DqT dq[NWS][2][GPT];
-    u32x4_t A[2][2][2], B[2][2][4];          // [set][u][nb] / [set][u][mb]
+    DqT dq[NWS][NB][GPT];
+    u32x4_t A[2][2][NB], B[2][2][MB];        // [set][u][nb] / [set][u][mb]
 
-    // Block i (of four) of this wave's share of stage st's DMA.
+    // Block i (of MB) of this wave's share of stage st's DMA.
     auto dma_part = [&](int st, auto buf, int i) __attribute__((always_inline)) {
         const uint32_t soff_k = (uint32_t)min(st, S - 1) * 128u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * 4 + i) * 64],
+            xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * MB + i) * 64],
             16, xoff[i], soff_k, 0, 0);
     };
     auto dma = [&](int st, auto buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma_part(st, buf, i);
+        for (int i = 0; i < MB; ++i) dma_part(st, buf, i);
     };
-    // Load j (of kWLoads) of weight tile t: the four code slots, then scales and zeros.
+    // Load j (of kWLoads) of weight tile t: the 2 NB code slots, then scales and zeros.
     auto load_w_part = [&](int t, WSet &w, auto J) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         t = min(t, KT - 1);
-        if constexpr (j < 4) {
+        if constexpr (j < 2 * NB) {
             w.w[j / 2][j % 2] = buf_load_b128(wrs, woff[j / 2][j % 2], t * 1024);
         } else {
-            constexpr int m = j - 4, per = SYM ? 1 : 2;
+            constexpr int m = j - 2 * NB, per = SYM ? 1 : 2;
             constexpr int nb = m / (GPT * per), h = (m / per) % GPT, kind = m % per;
             if constexpr (kind == 0)
                 w.s[nb][h] = buf_load_b32(srs, soff[nb], (t * GPT + h) * 32);
@@ -294,62 +325,66 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
             (load_w_part(t, w, IC<J>()), ...);
         }(std::make_integer_sequence<int, kWLoads>{});
     };
-    auto make_dq = [&](const WSet &w, DqT(&d)[2][GPT]) __attribute__((always_inline)) {
+    auto make_dq = [&](const WSet &w, DqT(&d)[NB][GPT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int h = 0; h < GPT; ++h)
                 d[nb][h] = Dq<ACT>::make((uint16_t)(w.s[nb][h] >> sshift),
                                          SYM ? 8u : ((w.z[nb][h] >> zshift) & 0xFu));
     };
-    auto read_b = [&](auto buf, int s, u32x4_t(&b)[2][4]) __attribute__((always_inline)) {
+    auto read_b = [&](auto buf, int s, u32x4_t(&b)[2][MB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
                 b[u][mb] = xs[decltype(buf)::value][mb * 256 + brow + ((4 * s + 2 * u) ^ cb)];
     };
-    auto dequant_a = [&](const WSet &w, const DqT(&d)[2][GPT], int word, u32x4_t(&a)[2][2]) __attribute__((always_inline)) {
+    auto dequant_a = [&](const WSet &w, const DqT(&d)[NB][GPT], int word, u32x4_t(&a)[2][NB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
                 a[u][nb] = Dq<ACT>::word(w.w[nb][u][word], d[nb][(word * 32) / G]);
     };
 
-    // Dequantization operations of the next step, round-robin over its four words
-    // (word q = (u, nb) = (q / 2, q % 2)): operation o is step o / 4 of word o % 4.
-    auto run_ops = [&](auto LO, auto HI, const WSet &wn, const DqT(&dn)[2][GPT], int word_n,
-                       DqTmp(&tmp)[4], u32x4_t(&an)[2][2]) __attribute__((always_inline)) {
+    // Dequantization operations of the next step.  Four words (word q = (u, nb) = (q / 2,
+    // q % 2)): operation o is step o / 4 of word o % 4.  Two words (q = u): word 0's
+    // operations first, then word 1's.
+    auto run_ops = [&](auto LO, auto HI, const WSet &wn, const DqT(&dn)[NB][GPT], int word_n,
+                       DqTmp(&tmp)[2 * NB], u32x4_t(&an)[2][NB]) __attribute__((always_inline)) {
         constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
         [&]<int... O>(std::integer_sequence<int, O...>) {
             (([&] {
                  constexpr int o = lo + O;
                  if constexpr (o < hi) {
-                     constexpr int q = o % 4, u = q / 2, nb = q % 2;
-                     Ops::template run<o / 4>(wn.w[nb][u][word_n], dn[nb][(word_n * 32) / G], dc,
-                                              tmp[q], an[u][nb]);
+                     constexpr int q = NB == 2 ? o % 4 : o / Ops::kCount;
+                     constexpr int op = NB == 2 ? o / 4 : o % Ops::kCount;
+                     constexpr int u = q / NB, nb = q % NB;
+                     Ops::template run<op>(wn.w[nb][u][word_n], dn[nb][(word_n * 32) / G], dc,
+                                           tmp[q], an[u][nb]);
                  }
              }()),
              ...);
         }(std::make_integer_sequence<int, 8>{});
     };
 
-    // One 32-deep step: MFMA i (u = i/8, nb = i/4 % 2, mb = i % 4) on the current
+    // One 32-deep step: MFMA i (u = i/8, nb = i/MB % NB, mb = i % MB) on the current
     // operands, then slice i of the next step's preparation.
-    auto step = [&](const u32x4_t(&a)[2][2], const u32x4_t(&b)[2][4], u32x4_t(&an)[2][2],
-                    u32x4_t(&bn)[2][4], const WSet &wn, const DqT(&dn)[2][GPT], int word_n,
+    auto step = [&](const u32x4_t(&a)[2][NB], const u32x4_t(&b)[2][MB], u32x4_t(&an)[2][NB],
+                    u32x4_t(&bn)[2][MB], const WSet &wn, const DqT(&dn)[NB][GPT], int word_n,
                     auto bufn, int s_n, auto hook) __attribute__((always_inline)) {
-        DqTmp tmp[4];
+        DqTmp tmp[2 * NB];
+        constexpr int kReadEvery = 8 / MB;   // 2 MB operand reads spread over 16 MFMAs
         [&]<int... I>(std::integer_sequence<int, I...>) {
             (([&] {
-                 constexpr int u = I / 8, nb = (I / 4) % 2, mb = I % 4;
+                 constexpr int u = I / 8, nb = (I / MB) % NB, mb = I % MB;
                  mfma32<ACT>(acc[nb][mb], a[u][nb], b[u][mb]);
-                 if constexpr (I % 2 == 0) {
-                     constexpr int r = I / 2, ru = r / 4, rmb = r % 4;
+                 if constexpr (I % kReadEvery == 0) {
+                     constexpr int r = I / kReadEvery, ru = r / MB, rmb = r % MB;
                      bn[ru][rmb] = xs[decltype(bufn)::value][rmb * 256 + brow + ((4 * s_n + 2 * ru) ^ cb)];
                  }
-                 constexpr int total = 4 * Ops::kCount;
+                 constexpr int total = 2 * NB * Ops::kCount;
                  run_ops(IC<(total * I) / 16>(), IC<(total * (I + 1)) / 16>(), wn, dn, word_n, tmp, an);
                  hook(IC<I>());
                  __builtin_amdgcn_sched_barrier(0);
@@ -358,9 +393,13 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         }(std::make_integer_sequence<int, 16>{});
         // Keep this step's operands allocated to the end of the step, so no register of an
         // operand that an in-flight MFMA reads is handed to the next step's values.
-        asm volatile("" ::"v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]), "v"(b[0][0]),
-                     "v"(b[0][1]), "v"(b[0][2]), "v"(b[0][3]), "v"(b[1][0]), "v"(b[1][1]),
-                     "v"(b[1][2]), "v"(b[1][3]));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) asm volatile("" ::"v"(a[u][nb]));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) asm volatile("" ::"v"(b[u][mb]));
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -375,13 +414,14 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         // The wave's DMA of stage st+1 was followed by the DMA of stage st+2 and one weight
         // tile; once only those are outstanding, stage st+1 is in LDS.  (In the first two
         // stages more loads follow it and the wait is longer than needed, never shorter.)
-        wait_vm_barrier<4 + kWLoads>();
-        // The next stage's DMA (four blocks) and, in the first half of a tile, the weight
+        wait_vm_barrier<MB + kWLoads>();
+        // The next stage's DMA (MB blocks) and, in the first half of a tile, the weight
         // loads of tile t + NWS - 1 go out one at a time between MFMAs, in the same order
         // as before, instead of as one burst per wave at the barrier.
         auto dma_hook = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
-            if constexpr (i % 4 == 1) dma_part(st + 3, IC<(buf + 3) % kXStages>(), i / 4);
+            constexpr int every = 16 / MB;
+            if constexpr (i % every == 1) dma_part(st + 3, IC<(buf + 3) % kXStages>(), i / every);
         };
         auto w_hook = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
@@ -420,7 +460,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     dma(2, IC<2>());
 #pragma unroll
     for (int t = 1; t < NWS - 1; ++t) load_w(t, ws[t]);
-    wait_vm_barrier<4 + kWLoads * (NWS - 2)>();   // stage 0's DMA and tile 0 have landed
+    wait_vm_barrier<MB + kWLoads * (NWS - 2)>();  // stage 0's DMA and tile 0 have landed
     make_dq(ws[0], dq[0]);
     read_b(IC<0>(), 0, B[0]);
     dequant_a(ws[0], dq[0], 0, A[0]);
@@ -441,23 +481,28 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         if (st < S) four(st, IC<0>());
     }
     // The last stages prefetched (redundant) LDS data; let every DMA land before the wave
-    // can retire.  The nops cover the latency of the last MFMAs before their results are
-    // read.
+    // can retire.
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    // The compiler cannot see when the inline-asm MFMAs finish writing the accumulators, and
+    // it may copy them out of the AGPRs anywhere after the loop.  One more MFMA per block,
+    // through the builtin, adds (+0) * (+0) -- an exact no-op, since no accumulator holds
+    // -0 (they start at +0, and x + (-0) = x) -- and makes the last write visible to the
+    // compiler, which then keeps every later read of the block far enough behind it.
+    finish_acc<ACT>(acc);
 
     // Result element j of block (nb, mb) in lane l: n = 32 nb + 8 (j / 4) + 4 (l / 32) + j % 4
-    // of the wave's 64 columns, m = 32 mb + l % 32.
+    // of the wave's 32 NB columns, m = 32 mb + l % 32.
     const int n_wave = strip0 * 16;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int n = n_wave + nb * 32 + 8 * q + 4 * (lane >> 5);
             if (n >= N) continue;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int mb = 0; mb < MB; ++mb) {
                 const int m = m_blk + mb * 32 + (lane & 31);
                 if (m < M) {
                     const f32x4_t v = {acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
@@ -468,32 +513,38 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         }
 }
 
-template <int ACT, bool SYM, int G>
+template <int ACT, bool SYM, int G, int NB>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const dim3 grid(((a.N + kXBN - 1) / kXBN) * ((a.M + kXBM - 1) / kXBM));
-    prefill_x32_kernel<ACT, SYM, G, kXWSets<G>><<<grid, dim3(kXThreads), 0, stream>>>(
+    const dim3 grid(((a.N + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB)));
+    prefill_x32_kernel<ACT, SYM, G, kXWSets<G>, NB><<<grid, dim3(kXThreads), 0, stream>>>(
         a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
 }
 
-template <int ACT>
+template <int ACT, int NB>
 void launch_act(const GemmArgs &a, hipStream_t stream) {
     const bool sym = a.zeros == nullptr;
     if (a.group == 128) {
-        sym ? launch_one<ACT, true, 128>(a, stream) : launch_one<ACT, false, 128>(a, stream);
+        sym ? launch_one<ACT, true, 128, NB>(a, stream) : launch_one<ACT, false, 128, NB>(a, stream);
     } else {
-        sym ? launch_one<ACT, true, 64>(a, stream) : launch_one<ACT, false, 64>(a, stream);
+        sym ? launch_one<ACT, true, 64, NB>(a, stream) : launch_one<ACT, false, 64, NB>(a, stream);
     }
+}
+
+template <int NB>
+hipError_t launch_nb(const GemmArgs &a, hipStream_t stream) {
+    if (a.act == kBF16) {
+        launch_act<kBF16, NB>(a, stream);
+    } else {
+        launch_act<kF16, NB>(a, stream);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) {
-    if (a.act == kBF16) {
-        launch_act<kBF16>(a, stream);
-    } else {
-        launch_act<kF16>(a, stream);
-    }
-    return hipGetLastError();
+hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) { return launch_nb<2>(a, stream); }
+hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream) {
+    return launch_nb<1>(a, stream);
 }
 
 }  // namespace mpgemm

@@ -41,6 +41,8 @@ size_t decode_workspace_bytes(int M, int N, int K, int mblocks);
 // (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
 hipError_t launch_prefill_ring(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
+// The 32x32x16 kernel with a 256 (m) x 128 (n) workgroup tile (needs K % 256 == 0).
+hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
 // Writes zeros to Y (the K == 0 case).
