@@ -18,3 +18,32 @@ def test_scratch_users_names_only_spilling_kernels():
 
 def test_scratch_users_empty_report():
     assert build.scratch_users("") == []
+
+
+ASM = """\
+    .text
+_Z6kernelPf:                            ; @_Z6kernelPf
+; %bb.0:
+	v_mfma_f32_32x32x16_f16 a[0:15], v[0:3], v[4:7], a[0:15]
+	v_mfma_f32_32x32x16_f16 a[16:31], v[0:3], v[4:7], a[16:31]
+	v_accvgpr_read_b32 v8, a3
+	s_endpgm
+.Lfunc_end0:
+_Z7kernel2Pf:                           ; @_Z7kernel2Pf
+; %bb.0:
+	v_mfma_f32_32x32x16_f16 a[0:15], v[0:3], v[4:7], a[0:15]
+	s_nop 7
+	s_nop 7
+	s_nop 7
+	s_nop 7
+	v_accvgpr_read_b32 v8, a3
+	v_accvgpr_read_b32 v9, a40
+	s_endpgm
+.Lfunc_end1:
+"""
+
+
+def test_acc_read_hazards_flags_early_reads_only():
+    # kernel 1 reads a3 one instruction after the MFMA that writes a[0:15]; kernel 2 waits
+    # 32 states (and its read of a40 belongs to no MFMA)
+    assert build.acc_read_hazards(ASM) == [("_Z6kernelPf", 1)]

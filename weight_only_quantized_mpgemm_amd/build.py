@@ -7,7 +7,9 @@ switched off (those forms are avoided on this hardware) and floating-point contr
 (the dequantization relies on an exact add followed by a single rounding multiply).  The
 compiler's per-kernel resource report is checked: a kernel that spills to scratch memory
 fails the build (a spill in these register-resident pipelines costs far more than it
-saves, and nothing else would show it).
+saves, and nothing else would show it).  The generated code of the kernels that issue
+MFMAs through inline asm is checked too: no accumulator may be read sooner than 32 wait
+states after the MFMA that writes it (the compiler cannot enforce that for asm).
 """
 from __future__ import annotations
 
@@ -46,6 +48,64 @@ def scratch_users(report: str) -> list[tuple[str, int]]:
     return out
 
 
+# Sources whose kernels issue MFMAs through inline asm: the compiler does not know those
+# instructions' result latency, so the build checks the generated code instead.
+ASM_MFMA_SOURCES = ["gemm_prefill_ring.hip", "gemm_prefill_x32.hip"]
+MIN_RESULT_WAIT = 32     # wait states between an MFMA and the first read of its result
+
+
+def acc_read_hazards(asm: str, min_wait: int = MIN_RESULT_WAIT) -> list[tuple[str, int]]:
+    """(kernel, distance) for every kernel in which some MFMA's accumulator result is read
+    (v_accvgpr_read / v_accvgpr_mov) fewer than `min_wait` wait states after the MFMA, in
+    straight-line order; distance = instructions in between plus s_nop wait states."""
+    out = []
+    for name in re.findall(r"\n([A-Za-z_][\w.$]*):[^\n]*\n", asm):
+        if "kernel" not in name:
+            continue
+        start = asm.index("\n" + name + ":")
+        end = asm.find(".Lfunc_end", start)
+        lines = [ln.strip() for ln in asm[start:end].split("\n")[1:]]
+        lines = [ln for ln in lines if ln and not ln.startswith((";", "."))]
+        worst = None
+        for k, ln in enumerate(lines):
+            if not ln.startswith("v_mfma"):
+                continue
+            dst = ln.split()[1].rstrip(",")
+            m = re.match(r"a\[(\d+):(\d+)\]", dst)
+            if not m:
+                continue
+            lo, hi = int(m.group(1)), int(m.group(2))
+            states = 0
+            for j in range(k + 1, min(k + 128, len(lines))):
+                ln2 = lines[j]
+                if ln2.startswith("s_nop"):
+                    states += int(ln2.split()[1]) + 1
+                    continue
+                if ln2.startswith(("v_accvgpr_read", "v_accvgpr_mov")):
+                    srcs = re.findall(r"a(\d+)", ln2.split(",", 1)[1])
+                    if any(lo <= int(a) <= hi for a in srcs):
+                        d = j - k - 1 + states
+                        worst = d if worst is None else min(worst, d)
+                        break
+                if ln2.startswith("v_mfma") and ln2.split()[1].rstrip(",") == dst:
+                    break
+        if worst is not None and worst < min_wait:
+            out.append((name, worst))
+    return out
+
+
+def _check_asm_mfma(src: str, extra: list[str]) -> None:
+    asm_path = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *FLAGS, *extra, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
+           asm_path]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{res.stderr}")
+    bad = acc_read_hazards(open(asm_path).read())
+    if bad:
+        raise RuntimeError(f"{src}: MFMA results read too early (wait states): {bad}")
+
+
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", *extra, "-c",
@@ -63,8 +123,11 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compiles every source (always; no staleness shortcuts) and links libmpgemm.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = list(extra or [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
+        checks = [ex.submit(_check_asm_mfma, s, extra) for s in ASM_MFMA_SOURCES]
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+        for c in checks:
+            c.result()
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -229,6 +229,15 @@ __device__ __forceinline__ u32x4_t buf_load_b128_device(rsrc_t r, uint32_t voff)
     return __builtin_bit_cast(u32x4_t,
                               __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCachePolicyDevice));
 }
+// 32 wait states: longer than any MFMA of these kernels takes to write its result.  Kernels
+// that issue MFMAs through inline asm (invisible to the compiler's hazard tracking) run it
+// after their last MFMA, before any code that may read the accumulators.
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Waits for every vector-memory access this wave has issued (loads and stores) to finish:
 // vmcnt = 0, expcnt and lgkmcnt left at their maxima.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -55,8 +55,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // In-place accumulation c += a * b with the accumulator pinned to AGPRs.  (The compiler's
 // builtin form renames accumulators between MFMAs and pays a copy per MFMA.)  Written as
 // inline asm, the MFMA is invisible to the compiler's hazard tracking, so every caller
-// separates it from VALU writes of its sources and from reads of its result with s_nop
-// padding (see step_fence and the epilogue).
+// separates it from VALU writes of its sources with s_nop padding (see step_fence), and
+// the main loop drains the matrix pipeline (mfma_drain) before any code after it.
 template <int ACT>
 __device__ __forceinline__ void mfma_acc(f32x4_t &c, const u32x4_t &a, const u32x4_t &b);
 template <>
@@ -318,19 +318,25 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
 
     // S is a multiple of 4; NST-stage blocks, then a four-stage tail when S % 8 == 4 (the
     // tail's stages are a block's first four, so its buffers and weight sets line up).
+    // Each pass ends with mfma_drain, so whatever the compiler places after the loop (it
+    // may copy accumulators between registers right at the loop exit) finds the inline-asm
+    // MFMAs' results written.
     int st = 0;
     for (; st + NST <= S; st += NST) {
         four(st, IC<0>());
         if constexpr (NST == 8) four(st + 4, IC<4>());
+        mfma_drain();
     }
     if constexpr (NST == 8) {
-        if (st < S) four(st, IC<0>());
+        if (st < S) {
+            four(st, IC<0>());
+            mfma_drain();
+        }
     }
     // The last stages prefetched (redundant) LDS data; let every DMA land before the wave
-    // can retire, so no write reaches LDS after the workgroup has released it.  The nops
-    // give the last MFMAs' results time to land before the epilogue reads them.
+    // can retire, so no write reaches LDS after the workgroup has released it.
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll

@@ -78,8 +78,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // acc += a * b on one 32 x 32 block, accumulator pinned in place in AGPRs.  Inline asm is
 // invisible to the compiler's hazard tracking: the schedule keeps every VALU write of an
-// operand at least three instructions ahead of the MFMA that reads it, and the epilogue
-// pads before reading results.
+// operand at least three instructions ahead of the MFMA that reads it, and the main loop
+// drains the matrix pipeline (mfma_drain) before any code the compiler places after it.
 template <int ACT>
 __device__ __forceinline__ void mfma32(f32x16_t &c, const u32x4_t &a, const u32x4_t &b);
 template <>
@@ -89,23 +89,6 @@ __device__ __forceinline__ void mfma32<kF16>(f32x16_t &c, const u32x4_t &a, cons
 template <>
 __device__ __forceinline__ void mfma32<kBF16>(f32x16_t &c, const u32x4_t &a, const u32x4_t &b) {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-
-// acc = acc + 0 * 0 on every block through the compiler-visible builtin (see the kernel's
-// epilogue).
-template <int ACT, int NB, int MB>
-__device__ __forceinline__ void finish_acc(f32x16_t (&acc)[NB][MB]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            if constexpr (ACT == kF16)
-                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(half8_t{}, half8_t{},
-                                                                     acc[nb][mb], 0, 0, 0);
-            else
-                acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_t{}, bf16x8_t{},
-                                                                      acc[nb][mb], 0, 0, 0);
-        }
 }
 
 // Constants the dequantization keeps in registers for the whole kernel.  Produced by asm
@@ -472,25 +455,26 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 
     // S is a multiple of 4: blocks of 2 * NWS stages, then a four-stage tail (a block's
     // first four stages, so ring buffers and weight sets line up).
+    // Each pass ends with mfma_drain, so whatever the compiler places after the loop (it
+    // may copy accumulators between registers right at the loop exit) finds the inline-asm
+    // MFMAs' results written.
     int st = 0;
     for (; st + 2 * NWS <= S; st += 2 * NWS) {
         four(st, IC<0>());
         if constexpr (NWS == 4) four(st + 4, IC<1>());
+        mfma_drain();
     }
     if constexpr (NWS == 4) {
-        if (st < S) four(st, IC<0>());
+        if (st < S) {
+            four(st, IC<0>());
+            mfma_drain();
+        }
     }
     // The last stages prefetched (redundant) LDS data; let every DMA land before the wave
     // can retire.
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // The compiler cannot see when the inline-asm MFMAs finish writing the accumulators, and
-    // it may copy them out of the AGPRs anywhere after the loop.  One more MFMA per block,
-    // through the builtin, adds (+0) * (+0) -- an exact no-op, since no accumulator holds
-    // -0 (they start at +0, and x + (-0) = x) -- and makes the last write visible to the
-    // compiler, which then keeps every later read of the block far enough behind it.
-    finish_acc<ACT>(acc);
 
     // Result element j of block (nb, mb) in lane l: n = 32 nb + 8 (j / 4) + 4 (l / 32) + j % 4
     // of the wave's 32 NB columns, m = 32 mb + l % 32.
