@@ -74,6 +74,16 @@ def _load():
     lib.oracle_pack.restype = None
     lib.oracle_unpack.argtypes = [u8p, u8p, i, i, i, i, u8p, u16p, u8p]
     lib.oracle_unpack.restype = None
+    lib.oracle_dequant_w8.argtypes = [u8p, u16p, u8p, i, i, i, i, u16p]
+    lib.oracle_dequant_w8.restype = None
+    lib.oracle_packed_code_bytes_w8.argtypes = [i, i]
+    lib.oracle_packed_code_bytes_w8.restype = ctypes.c_size_t
+    lib.oracle_packed_meta_bytes_w8.argtypes = [i, i, i, i]
+    lib.oracle_packed_meta_bytes_w8.restype = ctypes.c_size_t
+    lib.oracle_pack_w8.argtypes = [u8p, u16p, u8p, i, i, i, u8p, u8p]
+    lib.oracle_pack_w8.restype = None
+    lib.oracle_unpack_w8.argtypes = [u8p, u8p, i, i, i, i, u8p, u16p, u8p]
+    lib.oracle_unpack_w8.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -201,6 +211,74 @@ def unpack(packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int, gr
                       int(bool(symmetric)), _ptr(codes, ctypes.c_uint8),
                       _ptr(scales, ctypes.c_uint16),
                       None if zeros is None else _ptr(zeros, ctypes.c_uint8))
+    return codes, scales, zeros
+
+
+# ------------------------------------------------------------ 8-bit weights (W8A16) --
+
+def dequant_w8(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None,
+               group: int, dtype: str = "f16") -> np.ndarray:
+    """w[k][n] = round_act((q - z) * s), q and z 8-bit (z = 128 when zeros is None)."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert K % group == 0 and scales_bits.shape == (K // group, N)
+    zp = None
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        assert zeros.shape == (K // group, N)
+        zp = _ptr(zeros, ctypes.c_uint8)
+    w = np.empty((K, N), dtype=np.uint16)
+    lib.oracle_dequant_w8(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16), zp,
+                          K, N, group, _dtype_code(dtype), _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def w8a16(x_bits, codes, scales_bits, zeros, group, dtype="f16", threads=1):
+    """The whole 8-bit path: dequantize, then the GEMM."""
+    return gemm(x_bits, dequant_w8(codes, scales_bits, zeros, group, dtype), dtype, threads)
+
+
+def packed_code_bytes_w8(K: int, N: int) -> int:
+    return int(_load().oracle_packed_code_bytes_w8(K, N))
+
+
+def packed_meta_bytes_w8(K: int, N: int, group: int, symmetric: bool) -> int:
+    return int(_load().oracle_packed_meta_bytes_w8(K, N, group, int(bool(symmetric))))
+
+
+def pack_w8(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None, group: int):
+    """8-bit layout packing; returns (packed_codes uint8, packed_meta uint8)."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    assert K % 128 == 0 and K % group == 0 and N % 16 == 0
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    zp = None
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        zp = _ptr(zeros, ctypes.c_uint8)
+    pc = np.empty(packed_code_bytes_w8(K, N), dtype=np.uint8)
+    pm = np.zeros(packed_meta_bytes_w8(K, N, group, zeros is None), dtype=np.uint8)
+    lib.oracle_pack_w8(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16), zp,
+                       K, N, group, _ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8))
+    return pc, pm
+
+
+def unpack_w8(packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int, group: int,
+              symmetric: bool):
+    """Inverse of pack_w8; returns (codes, scales_bits, zeros or None)."""
+    lib = _load()
+    pc = np.ascontiguousarray(packed_codes, dtype=np.uint8)
+    pm = np.ascontiguousarray(packed_meta, dtype=np.uint8)
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty((K // group, N), dtype=np.uint16)
+    zeros = None if symmetric else np.empty((K // group, N), dtype=np.uint8)
+    lib.oracle_unpack_w8(_ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8), K, N, group,
+                         int(bool(symmetric)), _ptr(codes, ctypes.c_uint8),
+                         _ptr(scales, ctypes.c_uint16),
+                         None if zeros is None else _ptr(zeros, ctypes.c_uint8))
     return codes, scales, zeros
 
 

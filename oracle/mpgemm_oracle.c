@@ -23,7 +23,8 @@
  *     tile and lane placement is this library's own gfx950 layout, restated below from
  *     its specification (see include/mpgemm.h), not derived from the GPU code.
  *
- * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py).
+ * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py and,
+ * for the 8-bit functions, tests/test_oracle_w8.py).
  */
 #include <math.h>
 #include <stddef.h>
@@ -246,6 +247,90 @@ void oracle_unpack(const uint8_t *packed_codes, const uint8_t *packed_meta, int 
                 uint8_t b = meta_zeros[e / 2];
                 zeros[(size_t)r * N + n] = (uint8_t)((e % 2) ? (b >> 4) : (b & 0xf));
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------ 8-bit weights (W8A16) --- */
+
+/*
+ * [TurboMind, abstract (pg1): the GEMM pipeline generalizes across precision formats].
+ * The 8-bit reading of the same group form: w = round_act((q - z) * s) with q and z
+ * unsigned 8-bit integers (0..255) and z = 128 for symmetric codes.  (q - z) is an
+ * integer of at most 9 bits, so the product with an 11-bit fp16 scale is exact in fp64.
+ *   codes  uint8 [K][N]; scales fp16 [K/g][N]; zeros uint8 [K/g][N] or NULL (z = 128)
+ *   w      out, activation format bits, [K][N]
+ */
+void oracle_dequant_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                       int K, int N, int g, int dtype, uint16_t *w) {
+    for (int k = 0; k < K; ++k) {
+        int r = k / g;                             /* group row of k */
+        for (int n = 0; n < N; ++n) {
+            int q8 = codes[(size_t)k * N + n];
+            int z8 = zeros ? zeros[(size_t)r * N + n] : 128;
+            double scale = oracle_f16_to_f64(scales[(size_t)r * N + n]);
+            double d = (double)(q8 - z8);          /* exact integer in [-255, 255] */
+            w[(size_t)k * N + n] = f64_to_act(d * scale, dtype);
+        }
+    }
+}
+
+/*
+ * Packed layout for 8-bit codes (restated from its specification in include/mpgemm.h):
+ *
+ * Codes plane, K*N bytes, one byte per code.  Tiles of 16 columns by 64 rows of k, 1 KiB
+ * each; tile index T = (n/16)*(K/64) + k/64, so the tiles of one 16-column strip follow
+ * each other along k.  Within a tile, with kk = k%64 and nn = n%16: lane L = nn +
+ * 16*((kk%32)/8), step t = kk/32, and the code sits at byte L*16 + t*8 + kk%8 (k ascending
+ * inside each 8-byte run).
+ *
+ * Meta plane: scales exactly as for 4-bit codes (fp16 at element index
+ * (n/16)*(K/g)*16 + (k/g)*16 + n%16); then, for asymmetric codes only, the zeros as one
+ * byte per element at the same index, (K/g)*N bytes.
+ */
+static size_t code8_byte_offset(int k, int n, int K) {
+    size_t T = (size_t)(n / 16) * (size_t)(K / 64) + (size_t)(k / 64);
+    int kk = k % 64, col = n % 16;
+    int lane8 = col + 16 * ((kk % 32) / 8);
+    return T * 1024 + (size_t)lane8 * 16 + (size_t)(kk / 32) * 8 + (size_t)(kk % 8);
+}
+
+size_t oracle_packed_code_bytes_w8(int K, int N) { return (size_t)K * N; }
+size_t oracle_packed_meta_bytes_w8(int K, int N, int g, int symmetric) {
+    size_t groups = (size_t)(K / g) * N;
+    return groups * 2 + (symmetric ? 0 : groups);
+}
+
+/* Requires K % 128 == 0, K % g == 0, N % 16 == 0. */
+void oracle_pack_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                    int K, int N, int g, uint8_t *packed_codes, uint8_t *packed_meta) {
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            packed_codes[code8_byte_offset(k, n, K)] = codes[(size_t)k * N + n];
+    uint16_t *meta_scales = (uint16_t *)packed_meta;
+    uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
+    for (int r = 0; r < K / g; ++r) {
+        for (int n = 0; n < N; ++n) {
+            size_t e = meta_index(r * g, n, K, g);
+            meta_scales[e] = scales[(size_t)r * N + n];
+            if (zeros) meta_zeros[e] = zeros[(size_t)r * N + n];
+        }
+    }
+}
+
+/* Inverse of oracle_pack_w8.  zeros is written only for asymmetric packing. */
+void oracle_unpack_w8(const uint8_t *packed_codes, const uint8_t *packed_meta, int K, int N,
+                      int g, int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            codes[(size_t)k * N + n] = packed_codes[code8_byte_offset(k, n, K)];
+    const uint16_t *meta_scales = (const uint16_t *)packed_meta;
+    const uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
+    for (int r = 0; r < K / g; ++r) {
+        for (int n = 0; n < N; ++n) {
+            size_t e = meta_index(r * g, n, K, g);
+            scales[(size_t)r * N + n] = meta_scales[e];
+            if (!symmetric && zeros) zeros[(size_t)r * N + n] = meta_zeros[e];
         }
     }
 }

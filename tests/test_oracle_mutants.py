@@ -34,6 +34,38 @@ MUTANTS = {
 }
 
 
+# Mistakes in the 8-bit functions, caught by tests/test_oracle_w8.py.
+MUTANTS_W8 = {
+    "w8_sign": ("double d = (double)(q8 - z8);", "double d = (double)(z8 - q8);"),
+    "w8_sym_zero": ("zeros[(size_t)r * N + n] : 128;", "zeros[(size_t)r * N + n] : 127;"),
+    "w8_group_row": ("int r = k / g;                             /* group row of k */",
+                     "int r = (k + 1) / g;"),
+    "w8_step_bytes": ("(size_t)(kk / 32) * 8 + (size_t)(kk % 8);",
+                      "(size_t)(kk / 32) + (size_t)(kk % 8) * 2;"),
+    "w8_lane": ("int lane8 = col + 16 * ((kk % 32) / 8);", "int lane8 = col * 4 + ((kk % 32) / 8);"),
+    "w8_zero_nibble": ("if (zeros) meta_zeros[e] = zeros[(size_t)r * N + n];",
+                       "if (zeros) meta_zeros[e] = zeros[(size_t)r * N + n] & 0xf;"),
+}
+
+
+def _run_pins(text, before, after, pins, tmp_path):
+    assert text.count(before) == 1, f"mutation anchor not found once: {before}"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(before, after))
+    lib = oracle.build(src=str(src), out=str(tmp_path / "libmutant.so"))
+    env = dict(os.environ, MPGEMM_ORACLE_LIB=lib)
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                           os.path.join(ROOT, "tests", pins)],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_W8))
+def test_w8_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTANTS_W8[name]
+    res = _run_pins(open(SRC).read(), before, after, "test_oracle_w8.py", tmp_path)
+    assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     before, after = MUTANTS[name]
