@@ -162,6 +162,59 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,
                         void *stream);
 
+/*
+ * ---------------------------------------------------------------------------------
+ * 8-bit weights (W8A16).  [TurboMind, abstract (pg1)]: the GEMM pipeline generalizes
+ * across precision formats.  Same group form with 8-bit integers:
+ *   codes  uint8 [K][N], all 8 bits: q in 0..255
+ *   zeros  uint8 [K/g][N], all 8 bits: z in 0..255; or NULL for symmetric codes (z = 128)
+ *   scales fp16 [K/g][N] as above
+ *   w[k][n] = (q - z) * s rounded once to the activation format.
+ * Packed 8-bit layout (same layout version)
+ *   Codes plane, K*N bytes.  Tiles of 16 columns x 64 rows of k, 1 KiB each; tile
+ *   T = (n/16)*(K/64) + k/64 starts at byte T*1024 (a strip's tiles follow each other
+ *   along k).  Inside a tile, with kk = k%64 and nn = n%16: lane L = nn + 16*((kk%32)/8),
+ *   step t = kk/32, and the code sits at byte L*16 + t*8 + kk%8 (k ascending in each
+ *   8-byte run).  Why: lane L's 16 bytes, one 128-bit load, are the A operands of two
+ *   16x16x32 MFMA steps (row nn, k = 8*(L/16) .. +7), and a byte permute against the fp16
+ *   pattern of 1024 turns each pair of codes into the (k, k+1) register pair 1024 + q.
+ *   Meta plane.  Scales exactly as for 4-bit codes; then, for asymmetric codes only, one
+ *   zero byte per element at the same index e ((K/g)*N bytes).
+ * Shape limits and conventions as above; in addition M > 64 needs K % 256 == 0.  The
+ * workspace is sized by mpgemm_workspace_bytes (the same for both code widths).
+ */
+
+/* Size of the packed 8-bit codes plane: K*N bytes.  0 if the shape is unsupported. */
+size_t mpgemm_packed_code_bytes_w8(int K, int N);
+
+/* Size of the packed 8-bit meta plane: (K/g)*N*2 + (symmetric ? 0 : (K/g)*N) bytes. */
+size_t mpgemm_packed_meta_bytes_w8(int K, int N, int group, int symmetric);
+
+/* Offline packing of 8-bit codes into the 8-bit layout; contract as mpgemm_pack_weights
+ * (zeros == NULL packs symmetric weights, zero 128, and writes no zero plane). */
+int mpgemm_pack_weights_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                           int K, int N, int group, void *packed_codes, void *packed_meta,
+                           void *stream);
+
+/* Exact inverse of mpgemm_pack_weights_w8; contract as mpgemm_unpack. */
+int mpgemm_unpack_w8(const void *packed_codes, const void *packed_meta, int K, int N,
+                     int group, int symmetric, uint8_t *codes, uint16_t *scales,
+                     uint8_t *zeros, void *stream);
+
+/*
+ * Y[M][N] = X[M][K] * dequant(W8)[K][N] with fp32 accumulation; arguments as for
+ * mpgemm_w4a16, with planes written by mpgemm_pack_weights_w8.  mpgemm_w8a16_config runs
+ * one configuration (ids as for mpgemm_w4a16_config: 1..4 small-M, 12 and 13 tiled
+ * 32x32x16; 10 and 11 are not provided for 8-bit codes and return MPGEMM_ERR_UNSUPPORTED).
+ */
+int mpgemm_w8a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
+                 int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
+                 size_t workspace_bytes, void *stream);
+int mpgemm_w8a16_config(const void *X, int dtype, const void *packed_codes,
+                        const void *packed_meta, int M, int N, int K, int group, int symmetric,
+                        void *Y, void *workspace, size_t workspace_bytes, int config_id,
+                        void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *mpgemm_status_string(int status);
 

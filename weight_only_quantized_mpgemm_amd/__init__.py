@@ -48,6 +48,13 @@ SIGNATURES = {
     "mpgemm_w4a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
     "mpgemm_status_string": (ctypes.c_char_p, [_i]),
+    "mpgemm_packed_code_bytes_w8": (_sz, [_i, _i]),
+    "mpgemm_packed_meta_bytes_w8": (_sz, [_i, _i, _i, _i]),
+    "mpgemm_pack_weights_w8": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "mpgemm_unpack_w8": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "mpgemm_w8a16": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "mpgemm_w8a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
+                                 _vp]),
 }
 
 
@@ -105,13 +112,15 @@ def _need(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str) -> None:
 
 @dataclasses.dataclass
 class PackedWeights:
-    """Layout-v1 planes of one [K, N] weight matrix (see include/mpgemm.h)."""
-    codes: torch.Tensor          # uint8 [K*N/2]
-    meta: torch.Tensor           # uint8 [(K/g)*N*2 (+ (K/g)*N/2 zeros)]
+    """Packed planes of one [K, N] weight matrix (see include/mpgemm.h): layout v1 for
+    4-bit codes, the 8-bit layout for bits == 8."""
+    codes: torch.Tensor          # uint8 [K*N/2] (4-bit) or [K*N] (8-bit)
+    meta: torch.Tensor           # uint8 [(K/g)*N*2 (+ zeros: (K/g)*N/2 or (K/g)*N)]
     K: int
     N: int
     group: int
     symmetric: bool
+    bits: int = 4
 
     @property
     def nbytes(self) -> int:
@@ -159,18 +168,47 @@ def pack_weights(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor 
     return out
 
 
+def pack_weights_w8(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | None,
+                    group: int) -> PackedWeights:
+    """Offline packing of 8-bit codes (mpgemm_pack_weights_w8).
+
+    codes  uint8 [K, N] (0..255); scales float16 [K/g, N]; zeros uint8 [K/g, N] or None for
+    symmetric codes with zero 128.
+    """
+    K, N = codes.shape
+    _need(codes, torch.uint8, (K, N), "codes")
+    if group <= 0 or K % group:
+        raise ValueError(f"K={K} is not a multiple of group={group}")
+    _need(scales, torch.float16, (K // group, N), "scales")
+    if zeros is not None:
+        _need(zeros, torch.uint8, (K // group, N), "zeros")
+    cb = int(lib().mpgemm_packed_code_bytes_w8(K, N))
+    mb = int(lib().mpgemm_packed_meta_bytes_w8(K, N, group, int(zeros is None)))
+    if K * N and (cb == 0 or mb == 0):
+        raise MpgemmError(-2, "pack_weights_w8")
+    out = PackedWeights(torch.empty(cb, dtype=torch.uint8, device=codes.device),
+                        torch.empty(mb, dtype=torch.uint8, device=codes.device),
+                        K, N, group, zeros is None, 8)
+    st = lib().mpgemm_pack_weights_w8(_ptr(codes), _ptr(scales), _ptr(zeros), K, N, group,
+                                      _ptr(out.codes), _ptr(out.meta), _stream(codes.device))
+    _check(st, "mpgemm_pack_weights_w8")
+    return out
+
+
 def unpack(packed: PackedWeights):
-    """Inverse of pack_weights (mpgemm_unpack): (codes, scales, zeros or None)."""
+    """Inverse of packing (mpgemm_unpack / mpgemm_unpack_w8): (codes, scales, zeros or
+    None)."""
     K, N, g = packed.K, packed.N, packed.group
     dev = packed.codes.device
     codes = torch.empty((K, N), dtype=torch.uint8, device=dev)
     scales = torch.empty((K // g, N), dtype=torch.float16, device=dev)
     zeros = None if packed.symmetric else torch.empty((K // g, N), dtype=torch.uint8,
                                                       device=dev)
-    st = lib().mpgemm_unpack(_ptr(packed.codes), _ptr(packed.meta), K, N, g,
-                             int(packed.symmetric), _ptr(codes), _ptr(scales), _ptr(zeros),
-                             _stream(dev))
-    _check(st, "mpgemm_unpack")
+    name = "mpgemm_unpack_w8" if packed.bits == 8 else "mpgemm_unpack"
+    st = getattr(lib(), name)(_ptr(packed.codes), _ptr(packed.meta), K, N, g,
+                              int(packed.symmetric), _ptr(codes), _ptr(scales), _ptr(zeros),
+                              _stream(dev))
+    _check(st, name)
     return codes, scales, zeros
 
 
@@ -215,14 +253,9 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
     return ws
 
 
-def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
-          config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X @ dequant(W) (mpgemm_w4a16; mpgemm_w4a16_config when config != 0).
-
-    x float16 or bfloat16 [M, K]; returns (or fills `out`) [M, N] in the same format.
-    workspace: uint8 device tensor, zeroed before its first use (default: the device's
-    cached one).
-    """
+def _gemm(bits: int, x: torch.Tensor, packed: PackedWeights, out, config, workspace):
+    if packed.bits != bits:
+        raise ValueError(f"weights are packed with {packed.bits}-bit codes, not {bits}-bit")
     M, K = x.shape
     if K != packed.K:
         raise ValueError(f"x has K={K}, weights have K={packed.K}")
@@ -240,10 +273,26 @@ def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = Non
         ws = workspace.numel()
     args = (_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K, packed.group,
             int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
-    if config:
-        st = lib().mpgemm_w4a16_config(*args, int(config), _stream(x.device))
-        _check(st, "mpgemm_w4a16_config")
-    else:
-        st = lib().mpgemm_w4a16(*args, _stream(x.device))
-        _check(st, "mpgemm_w4a16")
+    name = f"mpgemm_w{bits}a16" + ("_config" if config else "")
+    fn = getattr(lib(), name)
+    st = fn(*args, int(config), _stream(x.device)) if config else fn(*args, _stream(x.device))
+    _check(st, name)
     return out
+
+
+def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
+          config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X @ dequant(W) (mpgemm_w4a16; mpgemm_w4a16_config when config != 0).
+
+    x float16 or bfloat16 [M, K]; returns (or fills `out`) [M, N] in the same format.
+    workspace: uint8 device tensor, zeroed before its first use (default: the device's
+    cached one).
+    """
+    return _gemm(4, x, packed, out, config, workspace)
+
+
+def w8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
+          config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X @ dequant(W8) for weights packed by pack_weights_w8 (mpgemm_w8a16; the
+    _config variant when config != 0).  Arguments as for w4a16."""
+    return _gemm(8, x, packed, out, config, workspace)

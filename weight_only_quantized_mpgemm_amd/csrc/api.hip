@@ -59,9 +59,9 @@ int select_config(int M, int N, int K) {
     return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
 }
 
-int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
-              int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
-              size_t workspace_bytes, int config_id, void *stream) {
+int gemm_impl(int bits, const void *X, int dtype, const void *packed_codes,
+              const void *packed_meta, int M, int N, int K, int group, int symmetric, void *Y,
+              void *workspace, size_t workspace_bytes, int config_id, void *stream) {
     if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
     if (symmetric != 0 && symmetric != 1) return MPGEMM_ERR_INVALID_ARG;
     const int st = check_shape(M, N, K, group);
@@ -84,12 +84,17 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
     const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
+    // 8-bit codes run the small-M kernel and the 32x32x16 tiled kernels (K % 256 == 0).
+    if (bits == 8 && (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf ||
+                      ((cfg == kConfigPrefillX32 || cfg == kConfigPrefillX32Tall) && K % 256 != 0)))
+        return MPGEMM_ERR_UNSUPPORTED;
 
     mpgemm::GemmArgs a;
     a.X = (const uint16_t *)X;
     a.codes = (const uint32_t *)packed_codes;
     a.scales = (const uint16_t *)packed_meta;
     a.zeros = symmetric ? nullptr : (const uint8_t *)packed_meta + (size_t)(K / group) * N * 2;
+    a.bits = bits;
     a.Y = (uint16_t *)Y;
     a.M = M;
     a.N = N;
@@ -103,8 +108,8 @@ int gemm_impl(const void *X, int dtype, const void *packed_codes, const void *pa
             return MPGEMM_ERR_WORKSPACE;
     }
     if (getenv("MPGEMM_LOG"))
-        fprintf(stderr, "mpgemm: M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", M, N, K, group,
-                dtype, symmetric, mpgemm_config_name(cfg));
+        fprintf(stderr, "mpgemm: W%dA16 M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", bits, M, N,
+                K, group, dtype, symmetric, mpgemm_config_name(cfg));
     if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
     if (cfg == kConfigPrefillX32 && K % 256 == 0) return hip_status(mpgemm::launch_prefill_x32(a, s));
     if (cfg == kConfigPrefillX32Tall && K % 256 == 0)
@@ -179,7 +184,7 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
 int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
                  int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
                  size_t workspace_bytes, void *stream) {
-    return gemm_impl(X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+    return gemm_impl(4, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
                      workspace, workspace_bytes, kConfigSelect, stream);
 }
 
@@ -187,7 +192,66 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
                         const void *packed_meta, int M, int N, int K, int group, int symmetric,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,
                         void *stream) {
-    return gemm_impl(X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+    return gemm_impl(4, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+                     workspace, workspace_bytes, config_id, stream);
+}
+
+size_t mpgemm_packed_code_bytes_w8(int K, int N) {
+    if (check_shape(0, N, K, 128) != MPGEMM_OK && check_shape(0, N, K, 64) != MPGEMM_OK) return 0;
+    return (size_t)K * (size_t)N;
+}
+
+size_t mpgemm_packed_meta_bytes_w8(int K, int N, int group, int symmetric) {
+    if (check_shape(0, N, K, group) != MPGEMM_OK) return 0;
+    const size_t cells = (size_t)(K / group) * (size_t)N;
+    return cells * 2 + (symmetric ? 0 : cells);
+}
+
+int mpgemm_pack_weights_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                           int K, int N, int group, void *packed_codes, void *packed_meta,
+                           void *stream) {
+    const int st = check_shape(0, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if ((size_t)K * N == 0) return MPGEMM_OK;
+    if (codes == nullptr || scales == nullptr || packed_codes == nullptr ||
+        packed_meta == nullptr)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)) ||
+        !aligned16(packed_codes) || !aligned16(packed_meta))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_pack_w8(codes, scales, zeros, K, N, group, packed_codes,
+                                             packed_meta, (hipStream_t)stream));
+}
+
+int mpgemm_unpack_w8(const void *packed_codes, const void *packed_meta, int K, int N, int group,
+                     int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                     void *stream) {
+    if (symmetric != 0 && symmetric != 1) return MPGEMM_ERR_INVALID_ARG;
+    const int st = check_shape(0, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if ((size_t)K * N == 0) return MPGEMM_OK;
+    if (packed_codes == nullptr || packed_meta == nullptr || codes == nullptr ||
+        scales == nullptr || (!symmetric && zeros == nullptr))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(packed_codes) || !aligned16(packed_meta) || !aligned16(codes) ||
+        !aligned16(scales) || (!symmetric && !aligned16(zeros)))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_unpack_w8(packed_codes, packed_meta, K, N, group, symmetric,
+                                               codes, scales, zeros, (hipStream_t)stream));
+}
+
+int mpgemm_w8a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
+                 int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    return gemm_impl(8, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+                     workspace, workspace_bytes, kConfigSelect, stream);
+}
+
+int mpgemm_w8a16_config(const void *X, int dtype, const void *packed_codes,
+                        const void *packed_meta, int M, int N, int K, int group, int symmetric,
+                        void *Y, void *workspace, size_t workspace_bytes, int config_id,
+                        void *stream) {
+    return gemm_impl(8, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
                      workspace, workspace_bytes, config_id, stream);
 }
 

@@ -146,6 +146,66 @@ struct Dq<kBF16> {
     }
 };
 
+// ------------------------------------------------------- 8-bit codes (W8A16) --------
+//
+// A pair of 32-bit words holds the codes of k0 .. k0+7 of one column, k0 in the low byte.
+// A byte permute against the fp16 pattern 0x64 builds each (k, k+1) register pair as
+// (1024 + q) halves in one operation (v_perm_b32: selector bytes 0..3 pick the word,
+// 4..7 the pattern); then, as for 4-bit codes, an exact packed add of -(1024 + z) (an
+// integer of magnitude <= 255) and one rounding packed multiply by s.
+__device__ __forceinline__ u32x4_t dequant_pair_w8_f16(uint32_t w0, uint32_t w1,
+                                                       uint32_t nz2, uint32_t s2) {
+    u32x4_t h;
+    h[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);   // k0, k1
+    h[1] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);   // k2, k3
+    h[2] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);   // k4, k5
+    h[3] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);   // k6, k7
+    const half2_t s = bitcast<half2_t>(s2);
+    const half2_t nz = bitcast<half2_t>(nz2);
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = bitcast<uint32_t>((bitcast<half2_t>(h[j]) + nz) * s);
+    return r;
+}
+// bf16: q * s + (-z * s) in fp32 (exact: 8-bit integer times 11-bit significand), one
+// rounding to bf16.
+__device__ __forceinline__ u32x4_t dequant_pair_w8_bf16(uint32_t w0, uint32_t w1, float s,
+                                                        float nzs) {
+    u32x4_t r;
+    r[0] = pack_bf16x2(__builtin_fmaf(ubyte(w0, 0), s, nzs), __builtin_fmaf(ubyte(w0, 1), s, nzs));
+    r[1] = pack_bf16x2(__builtin_fmaf(ubyte(w0, 2), s, nzs), __builtin_fmaf(ubyte(w0, 3), s, nzs));
+    r[2] = pack_bf16x2(__builtin_fmaf(ubyte(w1, 0), s, nzs), __builtin_fmaf(ubyte(w1, 1), s, nzs));
+    r[3] = pack_bf16x2(__builtin_fmaf(ubyte(w1, 2), s, nzs), __builtin_fmaf(ubyte(w1, 3), s, nzs));
+    return r;
+}
+
+template <int ACT>
+struct Dq8;
+template <>
+struct Dq8<kF16> {
+    typedef DqF16 type;
+    // -(1024 + z): sign, exponent of 1024 (0x6400), fraction z (spacing 1, z < 1024).
+    static __device__ __forceinline__ DqF16 make(uint16_t s, uint32_t z) {
+        const uint32_t nh = 0xE400u | z;
+        DqF16 d;
+        d.nz_hi2 = nh | (nh << 16);
+        d.nz_lo2 = 0u;
+        d.s2 = (uint32_t)s | ((uint32_t)s << 16);
+        return d;
+    }
+    static __device__ __forceinline__ u32x4_t pair(uint32_t w0, uint32_t w1, const DqF16 &d) {
+        return dequant_pair_w8_f16(w0, w1, d.nz_hi2, d.s2);
+    }
+};
+template <>
+struct Dq8<kBF16> {
+    typedef DqBF16 type;
+    static __device__ __forceinline__ DqBF16 make(uint16_t s, uint32_t z) { return make_dq_bf16(s, z); }
+    static __device__ __forceinline__ u32x4_t pair(uint32_t w0, uint32_t w1, const DqBF16 &d) {
+        return dequant_pair_w8_bf16(w0, w1, d.s, d.nzs);
+    }
+};
+
 // ------------------------------------------------------------------------------ MFMA --
 //
 // v_mfma_f32_16x16x32_{f16,bf16}: D[i][j] += sum_k A[i][k] * B[k][j] over a 16x16x32

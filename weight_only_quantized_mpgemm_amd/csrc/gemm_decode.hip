@@ -1,4 +1,4 @@
-// Small-M (decode) W4A16 GEMM for gfx950.
+// Small-M (decode) W4A16 / W8A16 GEMM for gfx950.
 //
 // [TurboMind, GEMM pipeline; Fig. 6 and Fig. 9 captions]: the packed 4-bit weights are
 // loaded straight into registers, turned into 16-bit values by I2F conversion and scaling,
@@ -33,6 +33,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace mpgemm {
@@ -41,21 +43,24 @@ namespace {
 
 constexpr int kMaxWaves = 8;
 
-template <int MB, int S, int GPT>
+template <int MB, int S, int GPT, int WV>
 struct Slot {
-    u32x4_t w[S];              // per strip: 16 bytes of the packed tile = 4 MFMA k-steps
+    u32x4_t w[S][WV];          // per strip: WV 16-byte pieces of packed tile = 4 MFMA k-steps
     u32x4_t x[4][MB];          // activation B operands per k-step and row block
     uint32_t s[S][GPT];        // dword holding the lane's fp16 scale, per strip and group
     uint32_t z[S][GPT];        // dword holding the lane's 4-bit zero, per strip and group
 };
 
-template <int ACT, int MB, int S, bool SYM, int G, int D>
+template <int ACT, int MB, int S, bool SYM, int G, int D, int BITS>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     uint16_t *__restrict__ Y, f32x4_t *__restrict__ part, uint32_t *__restrict__ cnt) {
     constexpr int GPT = kTileK / G;              // groups per 128-k tile (1 or 2)
-    typedef Slot<MB, S, GPT> SlotT;
+    // 128-bit pieces per lane and strip per 128-deep step: one 16 x 128 tile of 4-bit codes,
+    // two 16 x 64 tiles of 8-bit codes.
+    constexpr int WV = BITS / 4;
+    typedef Slot<MB, S, GPT, WV> SlotT;
     extern __shared__ f32x4_t red[];             // [NW][S][MB][64]
 
     const int NW = blockDim.x >> 6;
@@ -74,34 +79,40 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const int strips = N >> 4;
     const int strip0 = blockIdx.x * S;
 
-    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024));
+    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024 * WV));
     const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
     const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
-    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / 2));
+    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
 
     // Per-lane byte offsets, fixed for the whole K slice.  Strips past N read the last real
     // strip (their outputs are never stored).  The meta element of a lane's column is a
     // multiple of 16 plus lane % 16, so its scale is half (lane & 1) of a dword and its zero
-    // is nibble (lane & 7) of a dword.
+    // is nibble (lane & 7) of a dword (4-bit codes) or byte (lane & 3) (8-bit codes).
     uint32_t woff[S], soff[S], zoff[S];
 #pragma unroll
     for (int si = 0; si < S; ++si) {
         const uint32_t strip = (uint32_t)min(strip0 + si, strips - 1);
-        woff[si] = (strip * KT + t_begin) * 1024u + lane * 16u;
+        woff[si] = (strip * KT + t_begin) * 1024u * WV + lane * 16u;
         const uint32_t e = strip * groups * 16u + t_begin * GPT * 16u + (lane & 15);
         soff[si] = (e >> 1) * 4u;
-        zoff[si] = (e >> 3) * 4u;
+        zoff[si] = BITS == 4 ? (e >> 3) * 4u : (e >> 2) * 4u;
     }
     uint32_t xoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
         xoff[mb] = ((uint32_t)(mb * 16 + (lane & 15)) * K + t_begin * kTileK + (lane >> 4) * 8) * 2u;
     const uint32_t sshift = (lane & 1) * 16;
-    const uint32_t zshift = (lane & 7) * 4;
+    const uint32_t zshift = BITS == 4 ? (lane & 7) * 4 : (lane & 3) * 8;
+    constexpr uint32_t zmask = (1u << BITS) - 1;
+    constexpr uint32_t zsym = 1u << (BITS - 1);        // symmetric zero: 8 or 128
+    constexpr int zrow = 16 * BITS / 8;                // zero bytes per (strip, group)
 
     auto load = [&](SlotT &sl, int i) {
 #pragma unroll
-        for (int si = 0; si < S; ++si) sl.w[si] = buf_load_b128(wrs, woff[si], i * 1024);
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int v = 0; v < WV; ++v)
+                sl.w[si][v] = buf_load_b128(wrs, woff[si], (i * WV + v) * 1024);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
 #pragma unroll
             for (int h = 0; h < GPT; ++h) {
                 sl.s[si][h] = buf_load_b32(srs, soff[si], (i * GPT + h) * 32);
-                sl.z[si][h] = SYM ? 0u : buf_load_b32(zrs, zoff[si], (i * GPT + h) * 8);
+                sl.z[si][h] = SYM ? 0u : buf_load_b32(zrs, zoff[si], (i * GPT + h) * zrow);
             }
     };
 
@@ -123,18 +134,24 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
         for (int mb = 0; mb < MB; ++mb) acc[si][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const SlotT &sl) {
-        typename Dq<ACT>::type dq[S][GPT];
+        typedef typename std::conditional<BITS == 4, Dq<ACT>, Dq8<ACT>>::type DqB;
+        typename DqB::type dq[S][GPT];
 #pragma unroll
         for (int si = 0; si < S; ++si)
 #pragma unroll
             for (int h = 0; h < GPT; ++h)
-                dq[si][h] = Dq<ACT>::make((uint16_t)(sl.s[si][h] >> sshift),
-                                          SYM ? 8u : ((sl.z[si][h] >> zshift) & 0xFu));
+                dq[si][h] = DqB::make((uint16_t)(sl.s[si][h] >> sshift),
+                                      SYM ? zsym : ((sl.z[si][h] >> zshift) & zmask));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int si = 0; si < S; ++si) {
-                const u32x4_t a = Dq<ACT>::word(sl.w[si][j], dq[si][(j * 32) / G]);
+                u32x4_t a;
+                if constexpr (BITS == 4)
+                    a = Dq<ACT>::word(sl.w[si][0][j], dq[si][(j * 32) / G]);
+                else
+                    a = Dq8<ACT>::pair(sl.w[si][j / 2][2 * (j % 2)], sl.w[si][j / 2][2 * (j % 2) + 1],
+                                       dq[si][(j * 32) / G]);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[si][mb] = mfma16x16x32<ACT>(a, sl.x[j][mb], acc[si][mb]);
@@ -297,9 +314,9 @@ size_t split_workspace(const Split &sp, int strips, int mblocks) {
     return kCounterBytes + groups * sp.p * sp.s * mblocks * 64 * sizeof(f32x4_t);
 }
 
-template <int ACT, int MB, int S, bool SYM, int G>
+template <int ACT, int MB, int S, bool SYM, int G, int BITS>
 void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
-    constexpr int slot_regs = S * 4 + 16 * MB + 2 * S;
+    constexpr int slot_regs = S * BITS + 16 * MB + 2 * S;
     constexpr int D = slot_regs <= 24 ? 4 : (slot_regs <= 40 ? 3 : 2);
     const int strips = a.N >> 4;
     const int wgs = (strips + S - 1) / S;
@@ -310,39 +327,41 @@ void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
         cnt = static_cast<uint32_t *>(a.workspace);
         part = reinterpret_cast<f32x4_t *>(static_cast<char *>(a.workspace) + kCounterBytes);
     }
-    decode_kernel<ACT, MB, S, SYM, G, D><<<dim3(wgs, sp.p), dim3(sp.nw * 64), lds, stream>>>(
+    decode_kernel<ACT, MB, S, SYM, G, D, BITS><<<dim3(wgs, sp.p), dim3(sp.nw * 64), lds, stream>>>(
         a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y, part, cnt);
 }
 
-template <int ACT, int MB, bool SYM, int G>
+template <int ACT, int MB, bool SYM, int G, int BITS>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     const Split sp = pick_split(a.M, a.N >> 4, a.K >> 7, MB);
     if constexpr (MB == 1) {
-        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G>(a, sp, stream);
+        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G, BITS>(a, sp, stream);
     }
     if constexpr (MB <= 2) {
-        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G>(a, sp, stream);
+        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G, BITS>(a, sp, stream);
     }
-    launch_s<ACT, MB, 1, SYM, G>(a, sp, stream);
+    launch_s<ACT, MB, 1, SYM, G, BITS>(a, sp, stream);
 }
 
-template <int ACT, int MB>
+template <int ACT, int MB, int BITS>
 void launch_mb(const GemmArgs &a, hipStream_t stream) {
     const bool sym = a.zeros == nullptr;
     if (a.group == 128) {
-        sym ? launch_one<ACT, MB, true, 128>(a, stream) : launch_one<ACT, MB, false, 128>(a, stream);
+        sym ? launch_one<ACT, MB, true, 128, BITS>(a, stream)
+            : launch_one<ACT, MB, false, 128, BITS>(a, stream);
     } else {
-        sym ? launch_one<ACT, MB, true, 64>(a, stream) : launch_one<ACT, MB, false, 64>(a, stream);
+        sym ? launch_one<ACT, MB, true, 64, BITS>(a, stream)
+            : launch_one<ACT, MB, false, 64, BITS>(a, stream);
     }
 }
 
-template <int ACT>
+template <int ACT, int BITS>
 void launch_act(const GemmArgs &a, int mblocks, hipStream_t stream) {
     switch (mblocks) {
-        case 1: launch_mb<ACT, 1>(a, stream); break;
-        case 2: launch_mb<ACT, 2>(a, stream); break;
-        case 3: launch_mb<ACT, 3>(a, stream); break;
-        default: launch_mb<ACT, 4>(a, stream); break;
+        case 1: launch_mb<ACT, 1, BITS>(a, stream); break;
+        case 2: launch_mb<ACT, 2, BITS>(a, stream); break;
+        case 3: launch_mb<ACT, 3, BITS>(a, stream); break;
+        default: launch_mb<ACT, 4, BITS>(a, stream); break;
     }
 }
 
@@ -353,10 +372,12 @@ size_t decode_workspace_bytes(int M, int N, int K, int mblocks) {
 }
 
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream) {
-    if (a.act == kBF16) {
-        launch_act<kBF16>(a, mblocks, stream);
+    if (a.bits == 8) {
+        a.act == kBF16 ? launch_act<kBF16, 8>(a, mblocks, stream)
+                       : launch_act<kF16, 8>(a, mblocks, stream);
     } else {
-        launch_act<kF16>(a, mblocks, stream);
+        a.act == kBF16 ? launch_act<kBF16, 4>(a, mblocks, stream)
+                       : launch_act<kF16, 4>(a, mblocks, stream);
     }
     return hipGetLastError();
 }

@@ -43,6 +43,7 @@
 //     is done first, since the next step's first MFMA needs it.  The dequantization is
 //     inline asm too, so the compiler neither reorders it nor pads it with wait states
 //     meant for the MFMAs.
+#include <type_traits>
 #include <utility>
 
 #include "kernels.hpp"
@@ -57,10 +58,11 @@ constexpr int kXThreads = 256;
 constexpr int kXStages = 4;                  // 64-deep LDS stages in the ring
 constexpr int tile_m(int nb) { return 32 * (8 / nb); }   // workgroup tile rows (m)
 constexpr int tile_n(int nb) { return 128 * nb; }        // workgroup tile columns (n)
-// Weight register sets (loads run NWS - 1 tiles ahead): four for g = 128; two for g = 64,
-// whose doubled scale/zero registers would not fit four sets without spilling.
-template <int G>
-constexpr int kXWSets = G == 128 ? 4 : 2;
+// Weight register sets (loads run NWS - 1 tiles ahead): four for 4-bit codes with
+// g = 128; two for g = 64, whose doubled scale/zero registers would not fit four sets
+// without spilling, and two for 8-bit codes (twice the code registers per set).
+template <int G, int BITS>
+constexpr int kXWSets = (G == 128 && BITS == 4) ? 4 : 2;
 
 template <int N>
 struct IC {
@@ -97,14 +99,23 @@ struct DqConst {
     uint32_t m_lo, m_hi;     // SGPR masks 0x000F000F, 0x00F000F0
     uint32_t b_hi, b_lo;     // VGPR fp16x2 patterns 1024.0 (0x6400) and 64.0 (0x5400)
     uint32_t m_byte;         // VGPR 0x0F0F0F0F (bf16 nibble spread)
+    uint32_t p_hi;           // VGPR bytes 0x64 (8-bit codes: the byte-permute pattern)
+    uint32_t sel_lo, sel_hi; // SGPR permute selectors for codes (0, 1) and (2, 3) of a word
 };
+template <int BITS>
 __device__ __forceinline__ DqConst make_dq_const() {
     DqConst c;
-    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(c.m_lo));
-    asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(c.m_hi));
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.b_hi));
-    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(c.b_lo));
-    asm volatile("v_mov_b32 %0, 0x0F0F0F0F" : "=v"(c.m_byte));
+    if constexpr (BITS == 4) {
+        asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(c.m_lo));
+        asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(c.m_hi));
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.b_hi));
+        asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(c.b_lo));
+        asm volatile("v_mov_b32 %0, 0x0F0F0F0F" : "=v"(c.m_byte));
+    } else {
+        asm volatile("v_mov_b32 %0, 0x64646464" : "=v"(c.p_hi));
+        asm volatile("s_mov_b32 %0, 0x04010400" : "=s"(c.sel_lo));
+        asm volatile("s_mov_b32 %0, 0x04030402" : "=s"(c.sel_hi));
+    }
     return c;
 }
 
@@ -174,6 +185,54 @@ struct DqOps<kBF16> {
     }
 };
 
+// The same for 8-bit codes: the words w0, w1 hold codes k0..k7 (k0 in the low byte), in the
+// arithmetic of Dq8<ACT>::pair.  fp16 (12 operations): four byte permutes against 0x64
+// (1024 + q pairs), four exact packed adds of -(1024 + z), four packed multiplies by s.
+// bf16 (12 operations): eight convert-and-fma q * s - z * s, four conversions to bf16
+// pairs.
+template <int ACT>
+struct DqOps8;
+
+template <>
+struct DqOps8<kF16> {
+    static constexpr int kCount = 12;
+    template <int OP>
+    static __device__ __forceinline__ void run(uint32_t w0, uint32_t w1, const DqF16 &d,
+                                               const DqConst &c, DqTmp &t, u32x4_t &out) {
+        if constexpr (OP <= 3) {
+            const uint32_t w = OP < 2 ? w0 : w1;
+            if constexpr ((OP & 1) == 0)
+                asm("v_perm_b32 %0, %1, %2, %3" : "=v"(t.h[OP]) : "v"(c.p_hi), "v"(w), "s"(c.sel_lo));
+            else
+                asm("v_perm_b32 %0, %1, %2, %3" : "=v"(t.h[OP]) : "v"(c.p_hi), "v"(w), "s"(c.sel_hi));
+        } else if constexpr (OP <= 7) {
+            constexpr int j = OP - 4;
+            asm("v_pk_add_f16 %0, %1, %2" : "=v"(t.h[j]) : "v"(t.h[j]), "v"(d.nz_hi2));
+        } else {
+            constexpr int j = OP - 8;
+            uint32_t r;
+            asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(t.h[j]), "v"(d.s2));
+            out[j] = r;
+        }
+    }
+};
+
+template <>
+struct DqOps8<kBF16> {
+    static constexpr int kCount = 12;
+    template <int OP>
+    static __device__ __forceinline__ void run(uint32_t w0, uint32_t w1, const DqBF16 &d,
+                                               const DqConst &c, DqTmp &t, u32x4_t &out) {
+        (void)c;
+        if constexpr (OP <= 7) {
+            t.f[OP] = __builtin_fmaf(ubyte(OP < 4 ? w0 : w1, OP & 3), d.s, d.nzs);
+        } else {
+            constexpr int j = OP - 8;
+            out[j] = pack_bf16x2(t.f[2 * j], t.f[2 * j + 1]);
+        }
+    }
+};
+
 // Tile of workgroup b.  Workgroups are dispatched round-robin over the eight XCDs
 // (b % 8), each with its own L2; XCD x gets a contiguous range of tile indices, walked in
 // groups of four M-tiles (all four rows of one N-tile, then the next N-tile), so the
@@ -191,20 +250,24 @@ __device__ __forceinline__ void tile_of(int b, int tm, int tn, int &mt, int &nt)
     nt = r / gm;
 }
 
-template <int ACT, bool SYM, int G, int NWS, int NB>
+template <int ACT, bool SYM, int G, int NWS, int NB, int BITS>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     uint16_t *__restrict__ Y) {
-    typedef typename Dq<ACT>::type DqT;
-    typedef DqOps<ACT> Ops;
+    typedef typename Dq<ACT>::type DqT;       // the same constants type for 8-bit codes
+    typedef typename std::conditional<BITS == 4, DqOps<ACT>, DqOps8<ACT>>::type Ops;
+    typedef typename std::conditional<BITS == 4, Dq<ACT>, Dq8<ACT>>::type DqB;
+    // 128-bit pieces per lane, column block and k half per 128-deep step: one slot of a
+    // 16 x 128 tile of 4-bit codes, one slot of each of two 16 x 64 tiles of 8-bit codes.
+    constexpr int WV = BITS / 4;
     constexpr int GPT = kTileK / G;          // groups per 128-deep tile (1 or 2)
     constexpr int MB = 8 / NB;               // 32-row blocks per wave
     constexpr int BM = tile_m(NB), BN = tile_n(NB);
     constexpr int kChunks = BM * 8;          // 16-byte chunks per stage (8 per 64-deep row)
-    // Loads each wave issues per weight tile: 2 NB 16-byte code slots (column blocks x
-    // k halves), plus scales (and zeros) per column block and group.
-    constexpr int kWLoads = 2 * NB + NB * GPT * (SYM ? 1 : 2);
+    // Loads each wave issues per weight tile: 2 NB WV 16-byte code slots (column blocks x
+    // k halves x pieces), plus scales (and zeros) per column block and group.
+    constexpr int kWLoads = 2 * NB * WV + NB * GPT * (SYM ? 1 : 2);
     static_assert(kWLoads <= 16, "weight loads are spread over one step's 16 MFMAs");
     __shared__ u32x4_t xs[kXStages][kChunks];
 
@@ -221,10 +284,10 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const int strip0 = nt * (BN / 16) + wave * 2 * NB;
 
     const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
-    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024));
+    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024 * WV));
     const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
-    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / 2));
-    const DqConst dc = make_dq_const();
+    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
+    const DqConst dc = make_dq_const<BITS>();
 
     // DMA source offsets: wave w fills blocks b = MB w + i of every stage; block b holds
     // rows 8b .. 8b+7, lane l writes LDS chunk 64b + l = (row 8b + l/8, physical chunk l%8),
@@ -249,14 +312,18 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const uint32_t pos = (lane & 15) + 16 * (2 * u + (lane >> 5));
-            woff[nb][u] = strip * KT * 1024u + pos * 16u;
+            woff[nb][u] = strip * KT * 1024u * WV + pos * 16u;
         }
         const uint32_t e = strip * groups * 16u + (lane & 15);
         soff[nb] = (e >> 1) * 4u;
-        zoff[nb] = (e >> 3) * 4u;
+        zoff[nb] = BITS == 4 ? (e >> 3) * 4u : (e >> 2) * 4u;
     }
     const uint32_t sshift = (lane & 1) * 16;
-    const uint32_t zshift = (lane & 7) * 4;
+    // A lane's zero is nibble (lane & 7) of a dword (4-bit codes) or byte (lane & 3).
+    const uint32_t zshift = BITS == 4 ? (lane & 7) * 4 : (lane & 3) * 8;
+    constexpr uint32_t zmask = (1u << BITS) - 1;
+    constexpr uint32_t zsym = 1u << (BITS - 1);        // symmetric zero: 8 or 128
+    constexpr int zrow = 16 * BITS / 8;                // zero bytes per (strip, group)
     // B operand: row 32 mb + lane % 32, logical chunk 4s + 2u + lane / 32 of the stage;
     // physical chunk = logical ^ (lane % 8) = (4s + 2u) ^ cb.
     const int brow = (lane & 31) * 8;
@@ -269,7 +336,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16_t{};
 
     struct WSet {
-        u32x4_t w[NB][2];                    // [nb][u], words = 32-deep steps of the tile
+        u32x4_t w[NB][2][WV];                // [nb][u][piece]: the tile's four 32-deep steps
         uint32_t s[NB][GPT], z[NB][GPT];
     };
     static_assert(NWS == 2 || NWS == 4, "the stage loop unrolls 2 * NWS stages");
@@ -292,15 +359,16 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     auto load_w_part = [&](int t, WSet &w, auto J) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
         t = min(t, KT - 1);
-        if constexpr (j < 2 * NB) {
-            w.w[j / 2][j % 2] = buf_load_b128(wrs, woff[j / 2][j % 2], t * 1024);
+        if constexpr (j < 2 * NB * WV) {
+            constexpr int nb = j / (2 * WV), u = (j / WV) % 2, v = j % WV;
+            w.w[nb][u][v] = buf_load_b128(wrs, woff[nb][u], (t * WV + v) * 1024);
         } else {
-            constexpr int m = j - 2 * NB, per = SYM ? 1 : 2;
+            constexpr int m = j - 2 * NB * WV, per = SYM ? 1 : 2;
             constexpr int nb = m / (GPT * per), h = (m / per) % GPT, kind = m % per;
             if constexpr (kind == 0)
                 w.s[nb][h] = buf_load_b32(srs, soff[nb], (t * GPT + h) * 32);
             else
-                w.z[nb][h] = buf_load_b32(zrs, zoff[nb], (t * GPT + h) * 8);
+                w.z[nb][h] = buf_load_b32(zrs, zoff[nb], (t * GPT + h) * zrow);
         }
     };
     auto load_w = [&](int t, WSet &w) __attribute__((always_inline)) {
@@ -313,8 +381,8 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int h = 0; h < GPT; ++h)
-                d[nb][h] = Dq<ACT>::make((uint16_t)(w.s[nb][h] >> sshift),
-                                         SYM ? 8u : ((w.z[nb][h] >> zshift) & 0xFu));
+                d[nb][h] = DqB::make((uint16_t)(w.s[nb][h] >> sshift),
+                                     SYM ? zsym : ((w.z[nb][h] >> zshift) & zmask));
     };
     auto read_b = [&](auto buf, int s, u32x4_t(&b)[2][MB]) __attribute__((always_inline)) {
 #pragma unroll
@@ -323,12 +391,21 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
             for (int mb = 0; mb < MB; ++mb)
                 b[u][mb] = xs[decltype(buf)::value][mb * 256 + brow + ((4 * s + 2 * u) ^ cb)];
     };
+    // The A operand of 32-deep step `word` of column block nb, k half u (compiler-scheduled
+    // form, for the prologue).
+    auto dq_word = [&](const WSet &w, int nb, int u, int word, const DqT &d) __attribute__((always_inline)) {
+        if constexpr (BITS == 4)
+            return Dq<ACT>::word(w.w[nb][u][0][word], d);
+        else
+            return Dq8<ACT>::pair(w.w[nb][u][word / 2][2 * (word % 2)],
+                                  w.w[nb][u][word / 2][2 * (word % 2) + 1], d);
+    };
     auto dequant_a = [&](const WSet &w, const DqT(&d)[NB][GPT], int word, u32x4_t(&a)[2][NB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                a[u][nb] = Dq<ACT>::word(w.w[nb][u][word], d[nb][(word * 32) / G]);
+                a[u][nb] = dq_word(w, nb, u, word, d[nb][(word * 32) / G]);
     };
 
     // Dequantization operations of the next step.  Four words (word q = (u, nb) = (q / 2,
@@ -344,8 +421,13 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
                      constexpr int q = NB == 2 ? o % 4 : o / Ops::kCount;
                      constexpr int op = NB == 2 ? o / 4 : o % Ops::kCount;
                      constexpr int u = q / NB, nb = q % NB;
-                     Ops::template run<op>(wn.w[nb][u][word_n], dn[nb][(word_n * 32) / G], dc,
-                                           tmp[q], an[u][nb]);
+                     if constexpr (BITS == 4)
+                         Ops::template run<op>(wn.w[nb][u][0][word_n], dn[nb][(word_n * 32) / G],
+                                               dc, tmp[q], an[u][nb]);
+                     else
+                         Ops::template run<op>(wn.w[nb][u][word_n / 2][2 * (word_n % 2)],
+                                               wn.w[nb][u][word_n / 2][2 * (word_n % 2) + 1],
+                                               dn[nb][(word_n * 32) / G], dc, tmp[q], an[u][nb]);
                  }
              }()),
              ...);
@@ -497,29 +579,32 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         }
 }
 
-template <int ACT, bool SYM, int G, int NB>
+template <int ACT, bool SYM, int G, int NB, int BITS>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     const dim3 grid(((a.N + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB)));
-    prefill_x32_kernel<ACT, SYM, G, kXWSets<G>, NB><<<grid, dim3(kXThreads), 0, stream>>>(
-        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
+    prefill_x32_kernel<ACT, SYM, G, kXWSets<G, BITS>, NB, BITS>
+        <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K,
+                                               a.Y);
 }
 
-template <int ACT, int NB>
+template <int ACT, int NB, int BITS>
 void launch_act(const GemmArgs &a, hipStream_t stream) {
     const bool sym = a.zeros == nullptr;
     if (a.group == 128) {
-        sym ? launch_one<ACT, true, 128, NB>(a, stream) : launch_one<ACT, false, 128, NB>(a, stream);
+        sym ? launch_one<ACT, true, 128, NB, BITS>(a, stream)
+            : launch_one<ACT, false, 128, NB, BITS>(a, stream);
     } else {
-        sym ? launch_one<ACT, true, 64, NB>(a, stream) : launch_one<ACT, false, 64, NB>(a, stream);
+        sym ? launch_one<ACT, true, 64, NB, BITS>(a, stream)
+            : launch_one<ACT, false, 64, NB, BITS>(a, stream);
     }
 }
 
 template <int NB>
 hipError_t launch_nb(const GemmArgs &a, hipStream_t stream) {
-    if (a.act == kBF16) {
-        launch_act<kBF16, NB>(a, stream);
+    if (a.bits == 8) {
+        a.act == kBF16 ? launch_act<kBF16, NB, 8>(a, stream) : launch_act<kF16, NB, 8>(a, stream);
     } else {
-        launch_act<kF16, NB>(a, stream);
+        a.act == kBF16 ? launch_act<kBF16, NB, 4>(a, stream) : launch_act<kF16, NB, 4>(a, stream);
     }
     return hipGetLastError();
 }

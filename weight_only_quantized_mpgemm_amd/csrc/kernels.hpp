@@ -18,7 +18,16 @@ hipError_t launch_unpack(const void *packed_codes, const void *packed_meta, int 
                          int group, int symmetric, uint8_t *codes, uint16_t *scales,
                          uint8_t *zeros, hipStream_t stream);
 
-// Arguments of one GEMM; planes as written by launch_pack.
+// The same for 8-bit codes (16 x 64 one-byte tiles, byte zeros).
+hipError_t launch_pack_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                          int K, int N, int group, void *packed_codes, void *packed_meta,
+                          hipStream_t stream);
+hipError_t launch_unpack_w8(const void *packed_codes, const void *packed_meta, int K, int N,
+                            int group, int symmetric, uint8_t *codes, uint16_t *scales,
+                            uint8_t *zeros, hipStream_t stream);
+
+// Arguments of one GEMM; planes as written by launch_pack (bits == 4) or launch_pack_w8
+// (bits == 8).
 struct GemmArgs {
     const uint16_t *X;          // [M][K] activation bits
     const uint32_t *codes;      // packed codes plane
@@ -27,6 +36,7 @@ struct GemmArgs {
     uint16_t *Y;                // [M][N] output bits
     int M, N, K, group;
     int act;                    // Act
+    int bits;                   // code width: 4 or 8
     void *workspace;            // decode split-K partials and counters (see decode kernel)
 };
 

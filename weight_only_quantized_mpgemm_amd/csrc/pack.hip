@@ -1,4 +1,5 @@
-// Offline weight packing and its inverse (layout v1, specified in include/mpgemm.h).
+// Offline weight packing and its inverse (layout v1 for 4-bit codes and its 8-bit
+// counterpart, both specified in include/mpgemm.h).
 //
 // [TurboMind, technique (i); Fig. 6 and Fig. 7 captions]: packing is done once, offline, and
 // is a pure permutation of bits; it places every 4-bit code where the online kernel's
@@ -95,6 +96,68 @@ __global__ void unpack_meta_kernel(const uint16_t *__restrict__ in_scales,
     }
 }
 
+// ---- 8-bit codes: tiles of 16 columns x 64 k, one byte per code ----
+
+// Byte offset of the 8-byte run holding rows k0..k0+7 (k0 % 8 == 0) of column n.
+__device__ __forceinline__ size_t code8_run_offset(int k0, int n, int K) {
+    const size_t tile = (size_t)(n >> 4) * (size_t)(K >> 6) + (size_t)(k0 >> 6);
+    const int kk = k0 & 63;
+    const int lane = (n & 15) + 16 * ((kk & 31) >> 3);
+    return tile * 1024 + (size_t)lane * 16 + (size_t)(kk >> 5) * 8;
+}
+
+// One thread per (8-row block, column), as for 4-bit codes.
+__global__ void pack_codes8_kernel(const uint8_t *__restrict__ codes, int K, int N,
+                                   uint8_t *__restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)(K >> 3) * N;
+    if (i >= total) return;
+    const int n = (int)(i % N);
+    const int k0 = (int)(i / N) * 8;
+    u32x2_t run = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        run[e >> 2] |= (uint32_t)codes[(size_t)(k0 + e) * N + n] << (8 * (e & 3));
+    *reinterpret_cast<u32x2_t *>(out + code8_run_offset(k0, n, K)) = run;
+}
+
+__global__ void unpack_codes8_kernel(const uint8_t *__restrict__ in, int K, int N,
+                                     uint8_t *__restrict__ codes) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)(K >> 3) * N;
+    if (i >= total) return;
+    const int n = (int)(i % N);
+    const int k0 = (int)(i / N) * 8;
+    const u32x2_t run = *reinterpret_cast<const u32x2_t *>(in + code8_run_offset(k0, n, K));
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        codes[(size_t)(k0 + e) * N + n] = (uint8_t)(run[e >> 2] >> (8 * (e & 3)));
+}
+
+// Meta for 8-bit codes: scales as above, one zero byte per element.
+__global__ void pack_meta8_kernel(const uint16_t *__restrict__ scales,
+                                  const uint8_t *__restrict__ zeros, int groups, int N,
+                                  uint16_t *__restrict__ out_scales,
+                                  uint8_t *__restrict__ out_zeros) {
+    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (size_t)groups * N) return;
+    int r, n;
+    meta_coords(e, groups, &r, &n);
+    out_scales[e] = scales[(size_t)r * N + n];
+    if (zeros != nullptr) out_zeros[e] = zeros[(size_t)r * N + n];
+}
+
+__global__ void unpack_meta8_kernel(const uint16_t *__restrict__ in_scales,
+                                    const uint8_t *__restrict__ in_zeros, int groups, int N,
+                                    uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros) {
+    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (size_t)groups * N) return;
+    int r, n;
+    meta_coords(e, groups, &r, &n);
+    scales[(size_t)r * N + n] = in_scales[e];
+    if (in_zeros != nullptr) zeros[(size_t)r * N + n] = in_zeros[e];
+}
+
 unsigned blocks_for(size_t total, unsigned threads) {
     return (unsigned)((total + threads - 1) / threads);
 }
@@ -136,6 +199,46 @@ hipError_t launch_unpack(const void *packed_codes, const void *packed_meta, int 
     }
     if (metas) {
         unpack_meta_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(
+            ms, mz, groups, N, scales, symmetric ? nullptr : zeros);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                          int K, int N, int group, void *packed_codes, void *packed_meta,
+                          hipStream_t stream) {
+    const unsigned threads = 256;
+    const size_t runs = (size_t)(K >> 3) * N;
+    const int groups = K / group;
+    const size_t metas = (size_t)groups * N;
+    uint16_t *ms = (uint16_t *)packed_meta;
+    uint8_t *mz = zeros ? (uint8_t *)packed_meta + metas * 2 : nullptr;
+    if (runs) {
+        pack_codes8_kernel<<<blocks_for(runs, threads), threads, 0, stream>>>(
+            codes, K, N, (uint8_t *)packed_codes);
+    }
+    if (metas) {
+        pack_meta8_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(scales, zeros,
+                                                                              groups, N, ms, mz);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_w8(const void *packed_codes, const void *packed_meta, int K, int N,
+                            int group, int symmetric, uint8_t *codes, uint16_t *scales,
+                            uint8_t *zeros, hipStream_t stream) {
+    const unsigned threads = 256;
+    const size_t runs = (size_t)(K >> 3) * N;
+    const int groups = K / group;
+    const size_t metas = (size_t)groups * N;
+    const uint16_t *ms = (const uint16_t *)packed_meta;
+    const uint8_t *mz = symmetric ? nullptr : (const uint8_t *)packed_meta + metas * 2;
+    if (runs) {
+        unpack_codes8_kernel<<<blocks_for(runs, threads), threads, 0, stream>>>(
+            (const uint8_t *)packed_codes, K, N, codes);
+    }
+    if (metas) {
+        unpack_meta8_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(
             ms, mz, groups, N, scales, symmetric ? nullptr : zeros);
     }
     return hipGetLastError();

@@ -10,6 +10,9 @@ Recipe (every array is drawn from numpy's PCG64 with a per-case seed):
   scales fp16  [K/g, N]      uniform in [lo, hi] drawn as float64, rounded to fp16 (RNE)
   X      fp16|bf16 [M, K]    standard normal drawn as float32, rounded to the activation
                              format (RNE; bf16 through torch's float32 -> bfloat16 cast)
+8-bit codes (W8A16): codes and zeros uniform integers in [0, 255] (None: symmetric, zero
+128), scales as above with the range divided by 16, so dequantized weights keep the 4-bit
+workloads' magnitudes.
 Shapes are those of the layers the workloads are named after (Llama-3-8B, Llama-3-70B,
 Qwen3-32B projection matrices).  No dataset or checkpoint is read.
 """
@@ -83,6 +86,29 @@ def weights(K: int, N: int, group: int, symmetric: bool, scale_lo: float, scale_
     scales = rng.uniform(scale_lo, scale_hi, size=(K // group, N)).astype(np.float16)
     zeros = None if symmetric else rng.integers(0, 16, size=(K // group, N), dtype=np.uint8)
     return codes, scales.view(np.uint16), zeros
+
+
+def weights_w8(K: int, N: int, group: int, symmetric: bool, scale_lo: float, scale_hi: float,
+               seed: int):
+    """8-bit codes: (codes uint8 [K,N] in 0..255, scales fp16 bits [K/g,N] drawn in
+    [scale_lo/16, scale_hi/16], zeros uint8 [K/g,N] in 0..255 or None)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = rng.integers(0, 256, size=(K, N), dtype=np.uint8)
+    scales = rng.uniform(scale_lo / 16, scale_hi / 16, size=(K // group, N)).astype(np.float16)
+    zeros = None if symmetric else rng.integers(0, 256, size=(K // group, N), dtype=np.uint8)
+    return codes, scales.view(np.uint16), zeros
+
+
+def make_case_w8(wl: Workload, M: int, K: int, N: int, seed: int | None = None):
+    """All inputs of one W8A16 GEMM with workload `wl`'s group, symmetry, scale range
+    (divided by 16) and activation format."""
+    if seed is None:
+        seed = seed_for(wl.name + "-w8", M, K, N)
+    codes, scales, zeros = weights_w8(K, N, wl.group, wl.symmetric, wl.scale_lo, wl.scale_hi,
+                                      seed)
+    x = activations(M, K, wl.dtype, seed + 1)
+    return dict(x=x, codes=codes, scales=scales, zeros=zeros, group=wl.group,
+                symmetric=wl.symmetric, dtype=wl.dtype, M=M, K=K, N=N, seed=seed)
 
 
 def make_case(wl: Workload, M: int, K: int, N: int, seed: int | None = None):
