@@ -25,6 +25,10 @@ launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters read for the dominant
 scaled by what the same counters read for a plain 1 GiB copy (--copy-calibration); it is
 taken from the summary file under profiles/ and reported only while the kernel sources
 still hash to the digest recorded there, else null.
+
+`w8a16_per_gemm` repeats the per-GEMM pass with 8-bit weights (mpgemm_w8a16, same shapes,
+its own rotating pool), each GEMM against the HBM roofline (M <= 64; bytes count one byte
+per code and per zero) or the fp16 MFMA roofline.  It is not part of `value`.
 """
 from __future__ import annotations
 
@@ -83,6 +87,12 @@ def gemm_bytes(M, K, N, g, symmetric=False):
     return K * N // 2 + cells * 2 + (0 if symmetric else cells // 2) + M * K * 2 + M * N * 2
 
 
+def gemm_bytes_w8(M, K, N, g, symmetric=False):
+    """Algorithmic HBM bytes of one W8A16 GEMM: 8-bit codes, scales, byte zeros, X and Y."""
+    cells = (K // g) * N
+    return K * N + cells * 2 + (0 if symmetric else cells) + M * K * 2 + M * N * 2
+
+
 def gemm_flops(M, K, N):
     return 2 * M * N * K
 
@@ -123,6 +133,8 @@ def main():
                     help="replay the timed steps from captured HIP graphs")
     ap.add_argument("--no-per-gemm", action="store_true",
                     help="skip the per-GEMM breakdown pass (counter runs use this)")
+    ap.add_argument("--no-w8", action="store_true",
+                    help="skip the W8A16 per-GEMM pass (8-bit weights, same shapes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose HBM "
                          "counter readings scale the counter-based traffic figures")
@@ -307,6 +319,55 @@ def main():
                              "tflops": round(fl / t / 1e12, 2), "gbps": round(by / t / 1e9, 1),
                              "bound": bound, "frac": round(frac, 4)})
 
+    # W8A16 (8-bit weights) at the same shapes: a per-GEMM pass like the one above, on its
+    # own rotating pool; reported beside the W4A16 step, not part of `value`.
+    w8 = []
+    if not args.no_w8:
+        del pool
+        torch.cuda.empty_cache()
+        layer8 = []
+        for K, N, label in shapes:
+            codes, scales, zeros = workloads.weights_w8(K, N, g, False, wl.scale_lo, wl.scale_hi,
+                                                        workloads.seed_for("bench-w8", 0, K, N))
+            layer8.append(mp.pack_weights_w8(
+                torch.from_numpy(codes).to(dev),
+                torch.from_numpy(scales.view(np.int16)).to(dev).view(torch.float16),
+                torch.from_numpy(zeros).to(dev), g))
+        torch.cuda.synchronize()
+        bytes8 = sum(p.nbytes for p in layer8)
+        copies8 = max(3, int(np.ceil(args.pool_gb * 1e9 / bytes8)))
+        pool8 = [layer8] + [[mp.PackedWeights(p.codes.clone(), p.meta.clone(), p.K, p.N,
+                                              p.group, p.symmetric, 8) for p in layer8]
+                            for _ in range(copies8 - 1)]
+        torch.cuda.synchronize()
+        reps = 10
+        for ci, (M, K, N, label) in enumerate(calls):
+            j = shape_idx[(K, N)]
+            def launch_reps8():
+                for r in range(reps):
+                    mp.w8a16(xs[(M, K)], pool8[(ci * reps + r) % copies8][j], out=ys[(M, N)])
+            launch_reps8()
+            torch.cuda.synchronize()
+            g8 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g8):
+                launch_reps8()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g8.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            fl, by = gemm_flops(M, K, N), gemm_bytes_w8(M, K, N, g)
+            bound = "hbm" if M <= 64 else "mfma"
+            frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
+                (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
+            w8.append({"M": M, "K": K, "N": N, "layer": label,
+                       "kernel": mp.config_name(cfg_of[(M, K, N, label)]),
+                       "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                       "gbps": round(by / t / 1e9, 1), "bound": bound, "frac": round(frac, 4)})
+        del pool8, layer8
+
     dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
         "metric": "W4A16 GEMM TFLOP/s and HBM GB/s (% roofline), Llama-3-8B shapes M=1/16/2048",
@@ -330,6 +391,7 @@ def main():
         "roofline": roofline(dominant),
         "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
         "per_gemm": per_call,
+        "w8a16_per_gemm": w8,
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
