@@ -84,6 +84,12 @@ def _load():
     lib.oracle_pack_w8.restype = None
     lib.oracle_unpack_w8.argtypes = [u8p, u8p, i, i, i, i, u8p, u16p, u8p]
     lib.oracle_unpack_w8.restype = None
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e5m2_to_f64.restype = ctypes.c_double
+    lib.oracle_dequant_fp8.argtypes = [u8p, u16p, i, i, i, i, i, u16p]
+    lib.oracle_dequant_fp8.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -280,6 +286,39 @@ def unpack_w8(packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int,
                          _ptr(scales, ctypes.c_uint16),
                          None if zeros is None else _ptr(zeros, ctypes.c_uint8))
     return codes, scales, zeros
+
+
+# ------------------------------------------------------------ FP8 weights ----------
+
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def fp8_to_f64(codes: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
+    """Values of OCP FP8 codes (E4M3 or E5M2)."""
+    lib = _load()
+    fn = lib.oracle_e5m2_to_f64 if FP8_FORMATS[fmt] else lib.oracle_e4m3_to_f64
+    flat = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
+    return np.array([fn(int(b)) for b in flat]).reshape(np.shape(codes))
+
+
+def dequant_fp8(codes: np.ndarray, scales_bits: np.ndarray, group: int, fmt: str = "e4m3",
+                dtype: str = "f16") -> np.ndarray:
+    """w[k][n] = round_act(fp8(q) * s); returns activation-format bits [K, N]."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert K % group == 0 and scales_bits.shape == (K // group, N)
+    w = np.empty((K, N), dtype=np.uint16)
+    lib.oracle_dequant_fp8(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16),
+                           K, N, group, FP8_FORMATS[fmt], _dtype_code(dtype),
+                           _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def wfp8a16(x_bits, codes, scales_bits, group, fmt="e4m3", dtype="f16", threads=1):
+    """The whole FP8-weight path: dequantize, then the GEMM."""
+    return gemm(x_bits, dequant_fp8(codes, scales_bits, group, fmt, dtype), dtype, threads)
 
 
 def max_threads() -> int:

@@ -23,8 +23,8 @@
  *     tile and lane placement is this library's own gfx950 layout, restated below from
  *     its specification (see include/mpgemm.h), not derived from the GPU code.
  *
- * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py and,
- * for the 8-bit functions, tests/test_oracle_w8.py).
+ * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py; the
+ * 8-bit functions by tests/test_oracle_w8.py, the FP8 ones by tests/test_oracle_fp8.py).
  */
 #include <math.h>
 #include <stddef.h>
@@ -331,6 +331,63 @@ void oracle_unpack_w8(const uint8_t *packed_codes, const uint8_t *packed_meta, i
             size_t e = meta_index(r * g, n, K, g);
             scales[(size_t)r * N + n] = meta_scales[e];
             if (!symmetric && zeros) zeros[(size_t)r * N + n] = meta_zeros[e];
+        }
+    }
+}
+
+/* ------------------------------------------------------ FP8 weights (W-FP8 A16) --- */
+
+/*
+ * [TurboMind, Fig. 19 caption: an FP8 Qwen3 8B model served by the same engine].  The FP8
+ * reading of the group form: each code is an 8-bit floating-point number, scaled by the
+ * fp16 group scale with no zero point, and the product is rounded once:
+ *   w = round_act(fp8(q) * s).
+ * The product (at most a 4-bit significand times an 11-bit one) is exact in fp64.  The
+ * codes are stored in the 8-bit packed layout with no zero plane.  Two OCP FP8 encodings:
+ *   E4M3 (format 0): 1 sign, 4 exponent bits with bias 7, 3 fraction bits; exponent 0 is
+ *                    subnormal; 0x7F and 0xFF are NaN; no infinities (largest 448).
+ *   E5M2 (format 1): 1 sign, 5 exponent bits with bias 15, 2 fraction bits; exponent 0 is
+ *                    subnormal; exponent 31 is infinity (fraction 0) or NaN.
+ */
+double oracle_e4m3_to_f64(uint8_t b) {
+    int sign = b >> 7;
+    int e = (b >> 3) & 0xf;
+    int f = b & 0x7;
+    double v;
+    if (e == 15 && f == 7) {
+        v = NAN;
+    } else if (e == 0) {
+        v = ldexp((double)f, -9);                  /* subnormal: f/8 * 2^-6 */
+    } else {
+        v = ldexp((double)(8 + f), e - 10);        /* (1.f) * 2^(e-7) */
+    }
+    return sign ? -v : v;                          /* E4M3 sign bit */
+}
+
+double oracle_e5m2_to_f64(uint8_t b) {
+    int neg = (b & 0x80) != 0;
+    int ex = (b >> 2) & 0x1f;
+    int fr = b & 0x3;
+    double v;
+    if (ex == 31) {
+        v = fr ? NAN : INFINITY;
+    } else if (ex == 0) {
+        v = ldexp((double)fr, -16);                /* subnormal: fr/4 * 2^-14 */
+    } else {
+        v = ldexp((double)(4 + fr), ex - 17);      /* (1.fr) * 2^(ex-15) */
+    }
+    return neg ? -v : v;
+}
+
+void oracle_dequant_fp8(const uint8_t *codes, const uint16_t *scales, int K, int N, int g,
+                        int format, int dtype, uint16_t *w) {
+    for (int k = 0; k < K; ++k) {
+        int row = k / g;
+        for (int n = 0; n < N; ++n) {
+            uint8_t q = codes[(size_t)k * N + n];
+            double v = format == 1 ? oracle_e5m2_to_f64(q) : oracle_e4m3_to_f64(q);
+            double scale = oracle_f16_to_f64(scales[(size_t)row * N + n]);
+            w[(size_t)k * N + n] = f64_to_act(v * scale, dtype);
         }
     }
 }

@@ -48,6 +48,24 @@ MUTANTS_W8 = {
 }
 
 
+MUTANTS_FP8 = {
+    "fp8_bias": ("ldexp((double)(8 + f), e - 10);", "ldexp((double)(8 + f), e - 11);"),
+    "fp8_subnormal": ("ldexp((double)f, -9);", "ldexp((double)f, -10);"),
+    "fp8_subnormal_implicit": ("ldexp((double)f, -9);", "ldexp((double)(8 + f), -9);"),
+    "fp8_nan_all_exp15": ("if (e == 15 && f == 7) {", "if (e == 15 && f >= 6) {"),
+    "fp8_sign": ("return sign ? -v : v;                          /* E4M3 sign bit */",
+                 "return v;"),
+    "fp8_mantissa_bits": ("int f = b & 0x7;", "int f = b & 0x3;"),
+    "e5m2_bias": ("ldexp((double)(4 + fr), ex - 17);", "ldexp((double)(4 + fr), ex - 16);"),
+    "e5m2_subnormal": ("ldexp((double)fr, -16);", "ldexp((double)fr, -15);"),
+    "e5m2_inf_is_nan": ("v = fr ? NAN : INFINITY;", "v = NAN;"),
+    "e5m2_sign": ("return neg ? -v : v;", "return v;"),
+    "fp8_format_swap": ("format == 1 ? oracle_e5m2_to_f64(q)", "format == 0 ? oracle_e5m2_to_f64(q)"),
+    "fp8_group_row": ("int row = k / g;", "int row = (k + 1) / g;"),
+    "fp8_scale_col": ("scales[(size_t)row * N + n]", "scales[(size_t)row * N + (n ^ 1)]"),
+}
+
+
 def _run_pins(text, before, after, pins, tmp_path):
     assert text.count(before) == 1, f"mutation anchor not found once: {before}"
     src = tmp_path / "mutant.c"
@@ -78,4 +96,11 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                           os.path.join(ROOT, "tests", "test_oracle.py")],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_FP8))
+def test_fp8_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTANTS_FP8[name]
+    res = _run_pins(open(SRC).read(), before, after, "test_oracle_fp8.py", tmp_path)
     assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
