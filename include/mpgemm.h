@@ -215,6 +215,43 @@ int mpgemm_w8a16_config(const void *X, int dtype, const void *packed_codes,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,
                         void *stream);
 
+/*
+ * ---------------------------------------------------------------------------------
+ * FP8 weights (W-FP8 A16).  [TurboMind, Fig. 19 caption]: the same engine serves an FP8
+ * Qwen3 8B model.  Each code is an OCP 8-bit floating-point number with no zero point:
+ *   codes  uint8 [K][N], FP8 bit patterns in the format fp8_format:
+ *            MPGEMM_FP8_E4M3: 1 sign, 4 exponent bits (bias 7), 3 fraction bits, subnormals,
+ *                             no infinities, 0x7F / 0xFF are NaN (largest finite 448);
+ *            MPGEMM_FP8_E5M2: 1 sign, 5 exponent bits (bias 15), 2 fraction bits,
+ *                             subnormals, infinities and NaNs as in binary16 (it is the
+ *                             high byte of binary16);
+ *   scales fp16 [K/g][N] as above
+ *   w[k][n] = fp8(q) * s rounded once to the activation format (NaN and infinite codes
+ *   propagate as the product does).
+ * Packing: mpgemm_pack_weights_w8 with zeros == NULL (the codes are bytes, so the 8-bit
+ * layout holds them unchanged); mpgemm_unpack_w8 with symmetric = 1 inverts it.  Shape
+ * limits, workspace and configuration ids as for mpgemm_w8a16.
+ */
+typedef enum {
+    MPGEMM_FP8_E4M3 = 0,
+    MPGEMM_FP8_E5M2 = 1
+} mpgemm_fp8_format;
+
+/*
+ * Y[M][N] = X[M][K] * dequant(FP8 W)[K][N] with fp32 accumulation; X, Y, dtype, sizes,
+ * group, workspace and stream as for mpgemm_w4a16; packed planes from
+ * mpgemm_pack_weights_w8 with zeros == NULL.  A bad fp8_format returns
+ * MPGEMM_ERR_INVALID_ARG.  mpgemm_wfp8a16_config runs one configuration, as
+ * mpgemm_w8a16_config.
+ */
+int mpgemm_wfp8a16(const void *X, int dtype, int fp8_format, const void *packed_codes,
+                   const void *packed_meta, int M, int N, int K, int group, void *Y,
+                   void *workspace, size_t workspace_bytes, void *stream);
+int mpgemm_wfp8a16_config(const void *X, int dtype, int fp8_format, const void *packed_codes,
+                          const void *packed_meta, int M, int N, int K, int group, void *Y,
+                          void *workspace, size_t workspace_bytes, int config_id,
+                          void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *mpgemm_status_string(int status);
 

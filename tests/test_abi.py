@@ -164,3 +164,35 @@ def test_split_k_workspace_is_sized_and_required(monkeypatch):
     args[-1] = need
     args[-2] = ctypes.c_void_p(MIS)
     assert lib.mpgemm_w4a16(*args, None) == -4                         # misaligned
+
+
+def _fp8(fmt=0, X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, Y=A, cfg=None):
+    lib = mp.lib()
+    args = [ctypes.c_void_p(X), dtype, fmt, ctypes.c_void_p(pc), ctypes.c_void_p(pm), M, N, K,
+            g, ctypes.c_void_p(Y), None, 0]
+    if cfg is None:
+        return lib.mpgemm_wfp8a16(*args, None)
+    return lib.mpgemm_wfp8a16_config(*args, cfg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=2), INVALID),
+    (dict(fmt=-1), INVALID),
+    (dict(dtype=2), INVALID),
+    (dict(K=100), UNSUPPORTED),
+    (dict(X=0), INVALID),
+    (dict(Y=MIS), ALIGN),
+    (dict(cfg=10, M=128), UNSUPPORTED),              # the 16x16x32 tiled kernels take 4-bit only
+    (dict(cfg=11, M=128), UNSUPPORTED),
+    (dict(cfg=12, M=128, K=384), UNSUPPORTED),       # the 32x32x16 kernels need K % 256 == 0
+    (dict(M=65, K=384), UNSUPPORTED),
+    (dict(M=0), OK),
+])
+def test_fp8_gemm_validation(kw, status):
+    assert _fp8(**kw) == status
+
+
+def test_binding_fp8_format_names_match_header():
+    text = open(HEADER).read()
+    assert "MPGEMM_FP8_E4M3 = 0" in text and "MPGEMM_FP8_E5M2 = 1" in text
+    assert mp.FP8_FORMATS == {"e4m3": 0, "e5m2": 1}

@@ -55,7 +55,12 @@ SIGNATURES = {
     "mpgemm_w8a16": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "mpgemm_w8a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
+    "mpgemm_wfp8a16": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "mpgemm_wfp8a16_config": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _i,
+                                   _vp]),
 }
+
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}    # mpgemm_fp8_format
 
 
 class MpgemmError(RuntimeError):
@@ -113,7 +118,8 @@ def _need(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str) -> None:
 @dataclasses.dataclass
 class PackedWeights:
     """Packed planes of one [K, N] weight matrix (see include/mpgemm.h): layout v1 for
-    4-bit codes, the 8-bit layout for bits == 8."""
+    4-bit codes, the 8-bit layout for bits == 8 (integer codes, or FP8 codes when `fp8`
+    names their format)."""
     codes: torch.Tensor          # uint8 [K*N/2] (4-bit) or [K*N] (8-bit)
     meta: torch.Tensor           # uint8 [(K/g)*N*2 (+ zeros: (K/g)*N/2 or (K/g)*N)]
     K: int
@@ -121,6 +127,7 @@ class PackedWeights:
     group: int
     symmetric: bool
     bits: int = 4
+    fp8: str | None = None       # "e4m3" or "e5m2" for FP8 codes
 
     @property
     def nbytes(self) -> int:
@@ -195,6 +202,24 @@ def pack_weights_w8(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tens
     return out
 
 
+def pack_weights_fp8(codes: torch.Tensor, scales: torch.Tensor, group: int,
+                     fmt: str = "e4m3") -> PackedWeights:
+    """Offline packing of FP8 codes: the 8-bit layout with no zero plane
+    (mpgemm_pack_weights_w8 with zeros == NULL).
+
+    codes  uint8 [K, N] FP8 bit patterns (or a float8_e4m3fn / float8_e5m2 tensor, whose
+    format then decides `fmt`); scales float16 [K/g, N].
+    """
+    if codes.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        fmt = "e4m3" if codes.dtype == torch.float8_e4m3fn else "e5m2"
+        codes = codes.view(torch.uint8)
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"unknown FP8 format {fmt!r}")
+    out = pack_weights_w8(codes, scales, None, group)
+    out.fp8 = fmt
+    return out
+
+
 def unpack(packed: PackedWeights):
     """Inverse of packing (mpgemm_unpack / mpgemm_unpack_w8): (codes, scales, zeros or
     None)."""
@@ -253,9 +278,10 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
     return ws
 
 
-def _gemm(bits: int, x: torch.Tensor, packed: PackedWeights, out, config, workspace):
-    if packed.bits != bits:
-        raise ValueError(f"weights are packed with {packed.bits}-bit codes, not {bits}-bit")
+def _gemm(kind: str, x: torch.Tensor, packed: PackedWeights, out, config, workspace):
+    have = "fp8" if packed.fp8 else f"w{packed.bits}"
+    if have != kind:
+        raise ValueError(f"weights are packed as {have} codes, not {kind}")
     M, K = x.shape
     if K != packed.K:
         raise ValueError(f"x has K={K}, weights have K={packed.K}")
@@ -271,9 +297,14 @@ def _gemm(bits: int, x: torch.Tensor, packed: PackedWeights, out, config, worksp
     elif ws:
         _need(workspace, torch.uint8, (workspace.numel(),), "workspace")
         ws = workspace.numel()
-    args = (_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K, packed.group,
-            int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
-    name = f"mpgemm_w{bits}a16" + ("_config" if config else "")
+    if kind == "fp8":
+        args = (_ptr(x), act, FP8_FORMATS[packed.fp8], _ptr(packed.codes), _ptr(packed.meta),
+                M, N, K, packed.group, _ptr(out), _ptr(workspace), ws)
+    else:
+        args = (_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K, packed.group,
+                int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
+    name = ("mpgemm_wfp8a16" if kind == "fp8" else f"mpgemm_{kind}a16") + \
+        ("_config" if config else "")
     fn = getattr(lib(), name)
     st = fn(*args, int(config), _stream(x.device)) if config else fn(*args, _stream(x.device))
     _check(st, name)
@@ -288,11 +319,18 @@ def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = Non
     workspace: uint8 device tensor, zeroed before its first use (default: the device's
     cached one).
     """
-    return _gemm(4, x, packed, out, config, workspace)
+    return _gemm("w4", x, packed, out, config, workspace)
 
 
 def w8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
           config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X @ dequant(W8) for weights packed by pack_weights_w8 (mpgemm_w8a16; the
     _config variant when config != 0).  Arguments as for w4a16."""
-    return _gemm(8, x, packed, out, config, workspace)
+    return _gemm("w8", x, packed, out, config, workspace)
+
+
+def wfp8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
+            config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X @ (fp8(W) * s) for weights packed by pack_weights_fp8 (mpgemm_wfp8a16; the
+    _config variant when config != 0).  Arguments as for w4a16."""
+    return _gemm("fp8", x, packed, out, config, workspace)

@@ -59,7 +59,7 @@ int select_config(int M, int N, int K) {
     return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
 }
 
-int gemm_impl(int bits, const void *X, int dtype, const void *packed_codes,
+int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
               const void *packed_meta, int M, int N, int K, int group, int symmetric, void *Y,
               void *workspace, size_t workspace_bytes, int config_id, void *stream) {
     if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
@@ -84,8 +84,9 @@ int gemm_impl(int bits, const void *X, int dtype, const void *packed_codes,
     const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
-    // 8-bit codes run the small-M kernel and the 32x32x16 tiled kernels (K % 256 == 0).
-    if (bits == 8 && (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf ||
+    // 8-bit and FP8 codes run the small-M kernel and the 32x32x16 tiled kernels
+    // (K % 256 == 0).
+    if (code != mpgemm::kU4 && (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf ||
                       ((cfg == kConfigPrefillX32 || cfg == kConfigPrefillX32Tall) && K % 256 != 0)))
         return MPGEMM_ERR_UNSUPPORTED;
 
@@ -94,7 +95,7 @@ int gemm_impl(int bits, const void *X, int dtype, const void *packed_codes,
     a.codes = (const uint32_t *)packed_codes;
     a.scales = (const uint16_t *)packed_meta;
     a.zeros = symmetric ? nullptr : (const uint8_t *)packed_meta + (size_t)(K / group) * N * 2;
-    a.bits = bits;
+    a.code = code;
     a.Y = (uint16_t *)Y;
     a.M = M;
     a.N = N;
@@ -107,9 +108,11 @@ int gemm_impl(int bits, const void *X, int dtype, const void *packed_codes,
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
             return MPGEMM_ERR_WORKSPACE;
     }
-    if (getenv("MPGEMM_LOG"))
-        fprintf(stderr, "mpgemm: W%dA16 M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", bits, M, N,
-                K, group, dtype, symmetric, mpgemm_config_name(cfg));
+    if (getenv("MPGEMM_LOG")) {
+        static const char *const names[] = {"W4A16", "W8A16", "W(E4M3)A16", "W(E5M2)A16"};
+        fprintf(stderr, "mpgemm: %s M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", names[code],
+                M, N, K, group, dtype, symmetric, mpgemm_config_name(cfg));
+    }
     if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
     if (cfg == kConfigPrefillX32 && K % 256 == 0) return hip_status(mpgemm::launch_prefill_x32(a, s));
     if (cfg == kConfigPrefillX32Tall && K % 256 == 0)
@@ -184,16 +187,16 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
 int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
                  int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
                  size_t workspace_bytes, void *stream) {
-    return gemm_impl(4, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
-                     workspace, workspace_bytes, kConfigSelect, stream);
+    return gemm_impl(mpgemm::kU4, X, dtype, packed_codes, packed_meta, M, N, K, group,
+                     symmetric, Y, workspace, workspace_bytes, kConfigSelect, stream);
 }
 
 int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
                         const void *packed_meta, int M, int N, int K, int group, int symmetric,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,
                         void *stream) {
-    return gemm_impl(4, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
-                     workspace, workspace_bytes, config_id, stream);
+    return gemm_impl(mpgemm::kU4, X, dtype, packed_codes, packed_meta, M, N, K, group,
+                     symmetric, Y, workspace, workspace_bytes, config_id, stream);
 }
 
 size_t mpgemm_packed_code_bytes_w8(int K, int N) {
@@ -243,16 +246,34 @@ int mpgemm_unpack_w8(const void *packed_codes, const void *packed_meta, int K, i
 int mpgemm_w8a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
                  int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
                  size_t workspace_bytes, void *stream) {
-    return gemm_impl(8, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
-                     workspace, workspace_bytes, kConfigSelect, stream);
+    return gemm_impl(mpgemm::kU8, X, dtype, packed_codes, packed_meta, M, N, K, group,
+                     symmetric, Y, workspace, workspace_bytes, kConfigSelect, stream);
 }
 
 int mpgemm_w8a16_config(const void *X, int dtype, const void *packed_codes,
                         const void *packed_meta, int M, int N, int K, int group, int symmetric,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,
                         void *stream) {
-    return gemm_impl(8, X, dtype, packed_codes, packed_meta, M, N, K, group, symmetric, Y,
+    return gemm_impl(mpgemm::kU8, X, dtype, packed_codes, packed_meta, M, N, K, group,
+                     symmetric, Y, workspace, workspace_bytes, config_id, stream);
+}
+
+int mpgemm_wfp8a16_config(const void *X, int dtype, int fp8_format, const void *packed_codes,
+                          const void *packed_meta, int M, int N, int K, int group, void *Y,
+                          void *workspace, size_t workspace_bytes, int config_id,
+                          void *stream) {
+    if (fp8_format != MPGEMM_FP8_E4M3 && fp8_format != MPGEMM_FP8_E5M2)
+        return MPGEMM_ERR_INVALID_ARG;
+    const int code = fp8_format == MPGEMM_FP8_E4M3 ? mpgemm::kE4M3 : mpgemm::kE5M2;
+    return gemm_impl(code, X, dtype, packed_codes, packed_meta, M, N, K, group, 1, Y,
                      workspace, workspace_bytes, config_id, stream);
+}
+
+int mpgemm_wfp8a16(const void *X, int dtype, int fp8_format, const void *packed_codes,
+                   const void *packed_meta, int M, int N, int K, int group, void *Y,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return mpgemm_wfp8a16_config(X, dtype, fp8_format, packed_codes, packed_meta, M, N, K,
+                                 group, Y, workspace, workspace_bytes, kConfigSelect, stream);
 }
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {

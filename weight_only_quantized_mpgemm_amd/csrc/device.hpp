@@ -13,10 +13,19 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 enum Act { kF16 = 0, kBF16 = 1 };
+
+// Formats of the packed codes plane: 4-bit and 8-bit unsigned integers with a group zero
+// point, or 8-bit OCP floating point (E4M3, E5M2) with a group scale only.
+enum Code { kU4 = 0, kU8 = 1, kE4M3 = 2, kE5M2 = 3 };
+template <int CODE>
+constexpr int kCodeBits = CODE == kU4 ? 4 : 8;
+template <int CODE>
+constexpr bool kCodeFp8 = CODE == kE4M3 || CODE == kE5M2;
 
 // Packed layout v1 (include/mpgemm.h): 16 columns x 128 k per 1 KiB tile, 16 bytes per lane.
 constexpr int kTileK = 128;
@@ -205,6 +214,89 @@ struct Dq8<kBF16> {
         return dequant_pair_w8_bf16(w0, w1, d.s, d.nzs);
     }
 };
+
+// ------------------------------------------------------- FP8 codes (W-FP8 A16) -------
+//
+// w = fp8(q) * s, rounded once.  A pair of words holds codes k0 .. k7 of one column, k0 in
+// the low byte.  fp16: every E4M3 and E5M2 value is exactly an fp16 value, so each code
+// pair converts exactly to an fp16 pair (E4M3 by the scaled convert at scale 1.0; E5M2 is
+// the high byte of binary16, placed by a byte permute that zeroes the low bytes), and one
+// packed multiply by s rounds.  bf16: s is an fp16 value, not a bf16 one, so each code pair
+// converts exactly to fp32, multiplies by s exactly in fp32 (at most a 4-bit significand
+// times an 11-bit one) and rounds once to bf16.
+template <int CODE, bool HI>
+__device__ __forceinline__ uint32_t fp8_pair_f16(uint32_t w) {
+    if constexpr (CODE == kE4M3)
+        return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    else
+        return __builtin_amdgcn_perm(w, w, HI ? 0x030C020Cu : 0x010C000Cu);
+}
+template <int CODE, bool HI>
+__device__ __forceinline__ f32x2_t fp8_pair_f32(uint32_t w) {
+    if constexpr (CODE == kE4M3)
+        return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    else
+        return __builtin_amdgcn_cvt_pk_f32_bf8(w, HI);
+}
+
+template <int ACT, int CODE>
+struct DqF8;
+template <int CODE>
+struct DqF8<kF16, CODE> {
+    typedef DqF16 type;
+    static __device__ __forceinline__ DqF16 make(uint16_t s, uint32_t) {
+        DqF16 d;
+        d.nz_hi2 = d.nz_lo2 = 0u;
+        d.s2 = (uint32_t)s | ((uint32_t)s << 16);
+        return d;
+    }
+    static __device__ __forceinline__ u32x4_t pair(uint32_t w0, uint32_t w1, const DqF16 &d) {
+        const half2_t s = bitcast<half2_t>(d.s2);
+        u32x4_t r;
+        r[0] = bitcast<uint32_t>(bitcast<half2_t>(fp8_pair_f16<CODE, false>(w0)) * s);
+        r[1] = bitcast<uint32_t>(bitcast<half2_t>(fp8_pair_f16<CODE, true>(w0)) * s);
+        r[2] = bitcast<uint32_t>(bitcast<half2_t>(fp8_pair_f16<CODE, false>(w1)) * s);
+        r[3] = bitcast<uint32_t>(bitcast<half2_t>(fp8_pair_f16<CODE, true>(w1)) * s);
+        return r;
+    }
+};
+template <int CODE>
+struct DqF8<kBF16, CODE> {
+    typedef DqBF16 type;
+    static __device__ __forceinline__ DqBF16 make(uint16_t s, uint32_t) {
+        DqBF16 d;
+        d.s = (float)bitcast<_Float16>(s);
+        d.nzs = 0.f;
+        return d;
+    }
+    static __device__ __forceinline__ u32x4_t pair(uint32_t w0, uint32_t w1, const DqBF16 &d) {
+        const f32x2_t f0 = fp8_pair_f32<CODE, false>(w0), f1 = fp8_pair_f32<CODE, true>(w0);
+        const f32x2_t f2 = fp8_pair_f32<CODE, false>(w1), f3 = fp8_pair_f32<CODE, true>(w1);
+        u32x4_t r;
+        r[0] = pack_bf16x2(f0.x * d.s, f0.y * d.s);
+        r[1] = pack_bf16x2(f1.x * d.s, f1.y * d.s);
+        r[2] = pack_bf16x2(f2.x * d.s, f2.y * d.s);
+        r[3] = pack_bf16x2(f3.x * d.s, f3.y * d.s);
+        return r;
+    }
+};
+
+// The dequantization of code format CODE for activation format ACT: make(s, z) builds the
+// per-(group, column) constants; pair(w0, w1, d) (8-bit formats) dequantizes codes k0..k7.
+template <int ACT, int CODE>
+struct DqSel {
+    typedef DqF8<ACT, CODE> type;
+};
+template <int ACT>
+struct DqSel<ACT, kU4> {
+    typedef Dq<ACT> type;
+};
+template <int ACT>
+struct DqSel<ACT, kU8> {
+    typedef Dq8<ACT> type;
+};
+template <int ACT, int CODE>
+using DqFor = typename DqSel<ACT, CODE>::type;
 
 // ------------------------------------------------------------------------------ MFMA --
 //

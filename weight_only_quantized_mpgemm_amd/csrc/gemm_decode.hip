@@ -51,7 +51,7 @@ struct Slot {
     uint32_t z[S][GPT];        // dword holding the lane's 4-bit zero, per strip and group
 };
 
-template <int ACT, int MB, int S, bool SYM, int G, int D, int BITS>
+template <int ACT, int MB, int S, bool SYM, int G, int D, int CODE>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     constexpr int GPT = kTileK / G;              // groups per 128-k tile (1 or 2)
     // 128-bit pieces per lane and strip per 128-deep step: one 16 x 128 tile of 4-bit codes,
     // two 16 x 64 tiles of 8-bit codes.
+    constexpr int BITS = kCodeBits<CODE>;
     constexpr int WV = BITS / 4;
     typedef Slot<MB, S, GPT, WV> SlotT;
     extern __shared__ f32x4_t red[];             // [NW][S][MB][64]
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
         for (int mb = 0; mb < MB; ++mb) acc[si][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const SlotT &sl) {
-        typedef typename std::conditional<BITS == 4, Dq<ACT>, Dq8<ACT>>::type DqB;
+        typedef DqFor<ACT, CODE> DqB;
         typename DqB::type dq[S][GPT];
 #pragma unroll
         for (int si = 0; si < S; ++si)
@@ -148,9 +149,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
             for (int si = 0; si < S; ++si) {
                 u32x4_t a;
                 if constexpr (BITS == 4)
-                    a = Dq<ACT>::word(sl.w[si][0][j], dq[si][(j * 32) / G]);
+                    a = DqB::word(sl.w[si][0][j], dq[si][(j * 32) / G]);
                 else
-                    a = Dq8<ACT>::pair(sl.w[si][j / 2][2 * (j % 2)], sl.w[si][j / 2][2 * (j % 2) + 1],
+                    a = DqB::pair(sl.w[si][j / 2][2 * (j % 2)], sl.w[si][j / 2][2 * (j % 2) + 1],
                                        dq[si][(j * 32) / G]);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
@@ -314,9 +315,9 @@ size_t split_workspace(const Split &sp, int strips, int mblocks) {
     return kCounterBytes + groups * sp.p * sp.s * mblocks * 64 * sizeof(f32x4_t);
 }
 
-template <int ACT, int MB, int S, bool SYM, int G, int BITS>
+template <int ACT, int MB, int S, bool SYM, int G, int CODE>
 void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
-    constexpr int slot_regs = S * BITS + 16 * MB + 2 * S;
+    constexpr int slot_regs = S * kCodeBits<CODE> + 16 * MB + 2 * S;
     constexpr int D = slot_regs <= 24 ? 4 : (slot_regs <= 40 ? 3 : 2);
     const int strips = a.N >> 4;
     const int wgs = (strips + S - 1) / S;
@@ -327,42 +328,53 @@ void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
         cnt = static_cast<uint32_t *>(a.workspace);
         part = reinterpret_cast<f32x4_t *>(static_cast<char *>(a.workspace) + kCounterBytes);
     }
-    decode_kernel<ACT, MB, S, SYM, G, D, BITS><<<dim3(wgs, sp.p), dim3(sp.nw * 64), lds, stream>>>(
+    decode_kernel<ACT, MB, S, SYM, G, D, CODE><<<dim3(wgs, sp.p), dim3(sp.nw * 64), lds, stream>>>(
         a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y, part, cnt);
 }
 
-template <int ACT, int MB, bool SYM, int G, int BITS>
+template <int ACT, int MB, bool SYM, int G, int CODE>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     const Split sp = pick_split(a.M, a.N >> 4, a.K >> 7, MB);
     if constexpr (MB == 1) {
-        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G, BITS>(a, sp, stream);
+        if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G, CODE>(a, sp, stream);
     }
     if constexpr (MB <= 2) {
-        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G, BITS>(a, sp, stream);
+        if (sp.s == 2) return launch_s<ACT, MB, 2, SYM, G, CODE>(a, sp, stream);
     }
-    launch_s<ACT, MB, 1, SYM, G, BITS>(a, sp, stream);
+    launch_s<ACT, MB, 1, SYM, G, CODE>(a, sp, stream);
 }
 
-template <int ACT, int MB, int BITS>
+template <int ACT, int MB, int CODE>
 void launch_mb(const GemmArgs &a, hipStream_t stream) {
-    const bool sym = a.zeros == nullptr;
-    if (a.group == 128) {
-        sym ? launch_one<ACT, MB, true, 128, BITS>(a, stream)
-            : launch_one<ACT, MB, false, 128, BITS>(a, stream);
+    if constexpr (kCodeFp8<CODE>) {         // FP8 codes carry no zero point
+        a.group == 128 ? launch_one<ACT, MB, true, 128, CODE>(a, stream)
+                       : launch_one<ACT, MB, true, 64, CODE>(a, stream);
     } else {
-        sym ? launch_one<ACT, MB, true, 64, BITS>(a, stream)
-            : launch_one<ACT, MB, false, 64, BITS>(a, stream);
+        const bool sym = a.zeros == nullptr;
+        if (a.group == 128) {
+            sym ? launch_one<ACT, MB, true, 128, CODE>(a, stream)
+                : launch_one<ACT, MB, false, 128, CODE>(a, stream);
+        } else {
+            sym ? launch_one<ACT, MB, true, 64, CODE>(a, stream)
+                : launch_one<ACT, MB, false, 64, CODE>(a, stream);
+        }
     }
 }
 
-template <int ACT, int BITS>
+template <int ACT, int CODE>
 void launch_act(const GemmArgs &a, int mblocks, hipStream_t stream) {
     switch (mblocks) {
-        case 1: launch_mb<ACT, 1, BITS>(a, stream); break;
-        case 2: launch_mb<ACT, 2, BITS>(a, stream); break;
-        case 3: launch_mb<ACT, 3, BITS>(a, stream); break;
-        default: launch_mb<ACT, 4, BITS>(a, stream); break;
+        case 1: launch_mb<ACT, 1, CODE>(a, stream); break;
+        case 2: launch_mb<ACT, 2, CODE>(a, stream); break;
+        case 3: launch_mb<ACT, 3, CODE>(a, stream); break;
+        default: launch_mb<ACT, 4, CODE>(a, stream); break;
     }
+}
+
+template <int CODE>
+void launch_code(const GemmArgs &a, int mblocks, hipStream_t stream) {
+    a.act == kBF16 ? launch_act<kBF16, CODE>(a, mblocks, stream)
+                   : launch_act<kF16, CODE>(a, mblocks, stream);
 }
 
 }  // namespace
@@ -372,12 +384,11 @@ size_t decode_workspace_bytes(int M, int N, int K, int mblocks) {
 }
 
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream) {
-    if (a.bits == 8) {
-        a.act == kBF16 ? launch_act<kBF16, 8>(a, mblocks, stream)
-                       : launch_act<kF16, 8>(a, mblocks, stream);
-    } else {
-        a.act == kBF16 ? launch_act<kBF16, 4>(a, mblocks, stream)
-                       : launch_act<kF16, 4>(a, mblocks, stream);
+    switch (a.code) {
+        case kU8: launch_code<kU8>(a, mblocks, stream); break;
+        case kE4M3: launch_code<kE4M3>(a, mblocks, stream); break;
+        case kE5M2: launch_code<kE5M2>(a, mblocks, stream); break;
+        default: launch_code<kU4>(a, mblocks, stream); break;
     }
     return hipGetLastError();
 }

@@ -61,8 +61,8 @@ constexpr int tile_n(int nb) { return 128 * nb; }        // workgroup tile colum
 // Weight register sets (loads run NWS - 1 tiles ahead): four for 4-bit codes with
 // g = 128; two for g = 64, whose doubled scale/zero registers would not fit four sets
 // without spilling, and two for 8-bit codes (twice the code registers per set).
-template <int G, int BITS>
-constexpr int kXWSets = (G == 128 && BITS == 4) ? 4 : 2;
+template <int G, int CODE>
+constexpr int kXWSets = (G == 128 && CODE == kU4) ? 4 : 2;
 
 template <int N>
 struct IC {
@@ -102,19 +102,23 @@ struct DqConst {
     uint32_t p_hi;           // VGPR bytes 0x64 (8-bit codes: the byte-permute pattern)
     uint32_t sel_lo, sel_hi; // SGPR permute selectors for codes (0, 1) and (2, 3) of a word
 };
-template <int BITS>
+template <int CODE>
 __device__ __forceinline__ DqConst make_dq_const() {
     DqConst c;
-    if constexpr (BITS == 4) {
+    if constexpr (CODE == kU4) {
         asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(c.m_lo));
         asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(c.m_hi));
         asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.b_hi));
         asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(c.b_lo));
         asm volatile("v_mov_b32 %0, 0x0F0F0F0F" : "=v"(c.m_byte));
-    } else {
+    } else if constexpr (CODE == kU8) {
         asm volatile("v_mov_b32 %0, 0x64646464" : "=v"(c.p_hi));
         asm volatile("s_mov_b32 %0, 0x04010400" : "=s"(c.sel_lo));
         asm volatile("s_mov_b32 %0, 0x04030402" : "=s"(c.sel_hi));
+    } else if constexpr (CODE == kE5M2) {
+        // each code to the high byte of an fp16 half, low byte zero (selector 0x0C)
+        asm volatile("s_mov_b32 %0, 0x010C000C" : "=s"(c.sel_lo));
+        asm volatile("s_mov_b32 %0, 0x030C020C" : "=s"(c.sel_hi));
     }
     return c;
 }
@@ -233,6 +237,70 @@ struct DqOps8<kBF16> {
     }
 };
 
+// The same for FP8 codes, in the arithmetic of DqF8<ACT, CODE>::pair.  fp16 (8 operations):
+// four exact conversions of code pairs to fp16 pairs (E4M3: scaled convert at scale 1.0;
+// E5M2: byte permute to the high bytes), four packed multiplies by s.  bf16 (16
+// operations): four exact conversions of code pairs to fp32 pairs, eight exact fp32
+// multiplies by s, four conversions to bf16 pairs (the one rounding).
+template <int ACT, int CODE>
+struct DqOpsF8;
+
+template <int CODE>
+struct DqOpsF8<kF16, CODE> {
+    static constexpr int kCount = 8;
+    template <int OP>
+    static __device__ __forceinline__ void run(uint32_t w0, uint32_t w1, const DqF16 &d,
+                                               const DqConst &c, DqTmp &t, u32x4_t &out) {
+        if constexpr (OP <= 3) {
+            const uint32_t w = OP < 2 ? w0 : w1;
+            if constexpr (CODE == kE4M3) {
+                t.h[OP] = fp8_pair_f16<kE4M3, (OP & 1) != 0>(w);
+            } else {
+                const uint32_t sel = (OP & 1) ? c.sel_hi : c.sel_lo;
+                asm("v_perm_b32 %0, %1, %1, %2" : "=v"(t.h[OP]) : "v"(w), "s"(sel));
+            }
+        } else {
+            constexpr int j = OP - 4;
+            uint32_t r;
+            asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(t.h[j]), "v"(d.s2));
+            out[j] = r;
+        }
+    }
+};
+
+template <int CODE>
+struct DqOpsF8<kBF16, CODE> {
+    static constexpr int kCount = 16;
+    template <int OP>
+    static __device__ __forceinline__ void run(uint32_t w0, uint32_t w1, const DqBF16 &d,
+                                               const DqConst &c, DqTmp &t, u32x4_t &out) {
+        (void)c;
+        if constexpr (OP <= 3) {
+            const f32x2_t f = fp8_pair_f32<CODE, (OP & 1) != 0>(OP < 2 ? w0 : w1);
+            t.f[2 * OP] = f.x;
+            t.f[2 * OP + 1] = f.y;
+        } else if constexpr (OP <= 11) {
+            t.f[OP - 4] = t.f[OP - 4] * d.s;
+        } else {
+            constexpr int j = OP - 12;
+            out[j] = pack_bf16x2(t.f[2 * j], t.f[2 * j + 1]);
+        }
+    }
+};
+
+template <int ACT, int CODE>
+struct DqOpsSel {
+    typedef DqOpsF8<ACT, CODE> type;
+};
+template <int ACT>
+struct DqOpsSel<ACT, kU4> {
+    typedef DqOps<ACT> type;
+};
+template <int ACT>
+struct DqOpsSel<ACT, kU8> {
+    typedef DqOps8<ACT> type;
+};
+
 // Tile of workgroup b.  Workgroups are dispatched round-robin over the eight XCDs
 // (b % 8), each with its own L2; XCD x gets a contiguous range of tile indices, walked in
 // groups of four M-tiles (all four rows of one N-tile, then the next N-tile), so the
@@ -250,14 +318,15 @@ __device__ __forceinline__ void tile_of(int b, int tm, int tn, int &mt, int &nt)
     nt = r / gm;
 }
 
-template <int ACT, bool SYM, int G, int NWS, int NB, int BITS>
+template <int ACT, bool SYM, int G, int NWS, int NB, int CODE>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     uint16_t *__restrict__ Y) {
-    typedef typename Dq<ACT>::type DqT;       // the same constants type for 8-bit codes
-    typedef typename std::conditional<BITS == 4, DqOps<ACT>, DqOps8<ACT>>::type Ops;
-    typedef typename std::conditional<BITS == 4, Dq<ACT>, Dq8<ACT>>::type DqB;
+    typedef typename Dq<ACT>::type DqT;       // the same constants type for every code format
+    typedef typename DqOpsSel<ACT, CODE>::type Ops;
+    typedef DqFor<ACT, CODE> DqB;
+    constexpr int BITS = kCodeBits<CODE>;
     // 128-bit pieces per lane, column block and k half per 128-deep step: one slot of a
     // 16 x 128 tile of 4-bit codes, one slot of each of two 16 x 64 tiles of 8-bit codes.
     constexpr int WV = BITS / 4;
@@ -287,7 +356,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024 * WV));
     const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
     const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
-    const DqConst dc = make_dq_const<BITS>();
+    const DqConst dc = make_dq_const<CODE>();
 
     // DMA source offsets: wave w fills blocks b = MB w + i of every stage; block b holds
     // rows 8b .. 8b+7, lane l writes LDS chunk 64b + l = (row 8b + l/8, physical chunk l%8),
@@ -395,9 +464,9 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // form, for the prologue).
     auto dq_word = [&](const WSet &w, int nb, int u, int word, const DqT &d) __attribute__((always_inline)) {
         if constexpr (BITS == 4)
-            return Dq<ACT>::word(w.w[nb][u][0][word], d);
+            return DqB::word(w.w[nb][u][0][word], d);
         else
-            return Dq8<ACT>::pair(w.w[nb][u][word / 2][2 * (word % 2)],
+            return DqB::pair(w.w[nb][u][word / 2][2 * (word % 2)],
                                   w.w[nb][u][word / 2][2 * (word % 2) + 1], d);
     };
     auto dequant_a = [&](const WSet &w, const DqT(&d)[NB][GPT], int word, u32x4_t(&a)[2][NB]) __attribute__((always_inline)) {
@@ -579,32 +648,43 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         }
 }
 
-template <int ACT, bool SYM, int G, int NB, int BITS>
+template <int ACT, bool SYM, int G, int NB, int CODE>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     const dim3 grid(((a.N + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB)));
-    prefill_x32_kernel<ACT, SYM, G, kXWSets<G, BITS>, NB, BITS>
+    prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE>
         <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K,
                                                a.Y);
 }
 
-template <int ACT, int NB, int BITS>
+template <int ACT, int NB, int CODE>
 void launch_act(const GemmArgs &a, hipStream_t stream) {
-    const bool sym = a.zeros == nullptr;
-    if (a.group == 128) {
-        sym ? launch_one<ACT, true, 128, NB, BITS>(a, stream)
-            : launch_one<ACT, false, 128, NB, BITS>(a, stream);
+    if constexpr (kCodeFp8<CODE>) {         // FP8 codes carry no zero point
+        a.group == 128 ? launch_one<ACT, true, 128, NB, CODE>(a, stream)
+                       : launch_one<ACT, true, 64, NB, CODE>(a, stream);
     } else {
-        sym ? launch_one<ACT, true, 64, NB, BITS>(a, stream)
-            : launch_one<ACT, false, 64, NB, BITS>(a, stream);
+        const bool sym = a.zeros == nullptr;
+        if (a.group == 128) {
+            sym ? launch_one<ACT, true, 128, NB, CODE>(a, stream)
+                : launch_one<ACT, false, 128, NB, CODE>(a, stream);
+        } else {
+            sym ? launch_one<ACT, true, 64, NB, CODE>(a, stream)
+                : launch_one<ACT, false, 64, NB, CODE>(a, stream);
+        }
     }
+}
+
+template <int NB, int CODE>
+void launch_code(const GemmArgs &a, hipStream_t stream) {
+    a.act == kBF16 ? launch_act<kBF16, NB, CODE>(a, stream) : launch_act<kF16, NB, CODE>(a, stream);
 }
 
 template <int NB>
 hipError_t launch_nb(const GemmArgs &a, hipStream_t stream) {
-    if (a.bits == 8) {
-        a.act == kBF16 ? launch_act<kBF16, NB, 8>(a, stream) : launch_act<kF16, NB, 8>(a, stream);
-    } else {
-        a.act == kBF16 ? launch_act<kBF16, NB, 4>(a, stream) : launch_act<kF16, NB, 4>(a, stream);
+    switch (a.code) {
+        case kU8: launch_code<NB, kU8>(a, stream); break;
+        case kE4M3: launch_code<NB, kE4M3>(a, stream); break;
+        case kE5M2: launch_code<NB, kE5M2>(a, stream); break;
+        default: launch_code<NB, kU4>(a, stream); break;
     }
     return hipGetLastError();
 }

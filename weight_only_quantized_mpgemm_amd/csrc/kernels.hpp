@@ -26,8 +26,8 @@ hipError_t launch_unpack_w8(const void *packed_codes, const void *packed_meta, i
                             int group, int symmetric, uint8_t *codes, uint16_t *scales,
                             uint8_t *zeros, hipStream_t stream);
 
-// Arguments of one GEMM; planes as written by launch_pack (bits == 4) or launch_pack_w8
-// (bits == 8).
+// Arguments of one GEMM; planes as written by launch_pack (code kU4) or launch_pack_w8
+// (kU8, and the FP8 formats kE4M3 / kE5M2, which have no zero plane).
 struct GemmArgs {
     const uint16_t *X;          // [M][K] activation bits
     const uint32_t *codes;      // packed codes plane
@@ -36,7 +36,7 @@ struct GemmArgs {
     uint16_t *Y;                // [M][N] output bits
     int M, N, K, group;
     int act;                    // Act
-    int bits;                   // code width: 4 or 8
+    int code;                   // Code: format of the packed codes
     void *workspace;            // decode split-K partials and counters (see decode kernel)
 };
 

@@ -13,6 +13,10 @@ Recipe (every array is drawn from numpy's PCG64 with a per-case seed):
 8-bit codes (W8A16): codes and zeros uniform integers in [0, 255] (None: symmetric, zero
 128), scales as above with the range divided by 16, so dequantized weights keep the 4-bit
 workloads' magnitudes.
+FP8 codes: 64 * standard normal (float32), clipped to the format's largest finite value and
+cast to float8_e4m3fn / float8_e5m2 by torch (round to nearest even), taken as bytes; scales
+as above with the range divided by 64 (so weights are about normal with the scale's
+spread).  The FP8 workload has the shapes of the Qwen3-8B projections and bf16 activations.
 Shapes are those of the layers the workloads are named after (Llama-3-8B, Llama-3-70B,
 Qwen3-32B projection matrices).  No dataset or checkpoint is read.
 """
@@ -54,7 +58,13 @@ QWEN3_32B = Workload("qwen3_32b", 64, True, 0.002, 0.01, "f16",
                      ((5120, 10240, "qkv"), (8192, 5120, "o_proj"),
                       (5120, 51200, "gate_up"), (25600, 5120, "down")))
 
-ALL_WORKLOADS = (TINY, LLAMA3_8B_DECODE, LLAMA3_8B_PREFILL, LLAMA3_70B, QWEN3_32B)
+QWEN3_8B_SHAPES = ((4096, 6144, "qkv"), (4096, 4096, "o_proj"),
+                   (4096, 24576, "gate_up"), (12288, 4096, "down"))
+QWEN3_8B_FP8 = Workload("qwen3_8b_fp8", 128, True, 0.005, 0.02, "bf16", (1, 16, 2048),
+                        QWEN3_8B_SHAPES)
+
+ALL_WORKLOADS = (TINY, LLAMA3_8B_DECODE, LLAMA3_8B_PREFILL, LLAMA3_70B, QWEN3_32B,
+                 QWEN3_8B_FP8)
 
 
 def seed_for(tag: str, M: int, K: int, N: int) -> int:
@@ -109,6 +119,38 @@ def make_case_w8(wl: Workload, M: int, K: int, N: int, seed: int | None = None):
     x = activations(M, K, wl.dtype, seed + 1)
     return dict(x=x, codes=codes, scales=scales, zeros=zeros, group=wl.group,
                 symmetric=wl.symmetric, dtype=wl.dtype, M=M, K=K, N=N, seed=seed)
+
+
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def to_fp8_bits(v32: np.ndarray, fmt: str) -> np.ndarray:
+    """float32 values (within the format's finite range) cast to FP8 bytes by torch."""
+    import torch
+    dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    t = torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32))
+    return t.to(dt).view(torch.uint8).numpy()
+
+
+def weights_fp8(K: int, N: int, group: int, fmt: str, scale_lo: float, scale_hi: float,
+                seed: int):
+    """FP8 codes: (codes uint8 [K,N] FP8 bytes, scales fp16 bits [K/g,N])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    v = np.clip(rng.standard_normal((K, N), dtype=np.float32) * 64, -FP8_MAX[fmt], FP8_MAX[fmt])
+    scales = rng.uniform(scale_lo / 64, scale_hi / 64, size=(K // group, N)).astype(np.float16)
+    return to_fp8_bits(v, fmt), scales.view(np.uint16)
+
+
+def make_case_fp8(wl: Workload, M: int, K: int, N: int, fmt: str = "e4m3",
+                  seed: int | None = None):
+    """All inputs of one FP8-weight GEMM with workload `wl`'s group, scale range (divided
+    by 64) and activation format."""
+    if seed is None:
+        seed = seed_for(wl.name + "-" + fmt, M, K, N)
+    codes, scales = weights_fp8(K, N, wl.group, fmt, wl.scale_lo, wl.scale_hi, seed)
+    x = activations(M, K, wl.dtype, seed + 1)
+    return dict(x=x, codes=codes, scales=scales, zeros=None, group=wl.group, fmt=fmt,
+                symmetric=True, dtype=wl.dtype, M=M, K=K, N=N, seed=seed)
 
 
 def make_case(wl: Workload, M: int, K: int, N: int, seed: int | None = None):
