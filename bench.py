@@ -28,11 +28,15 @@ still hash to the digest recorded there, else null.
 
 `w8a16_per_gemm` repeats the per-GEMM pass with 8-bit weights (mpgemm_w8a16, same shapes,
 its own rotating pool), each GEMM against the HBM roofline (M <= 64; bytes count one byte
-per code and per zero) or the fp16 MFMA roofline.  It is not part of `value`.
+per code and per zero) or the fp16 MFMA roofline.  `wfp8a16_qwen3_8b_per_gemm` does the
+same with FP8 (E4M3) weights at the Qwen3-8B projection shapes (QKV 4096x6144, O 4096x4096,
+gate_up 4096x24576, down 12288x4096) and bf16 activations (mpgemm_wfp8a16; one byte per
+code, no zeros).  Neither is part of `value`.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -135,6 +139,8 @@ def main():
                     help="skip the per-GEMM breakdown pass (counter runs use this)")
     ap.add_argument("--no-w8", action="store_true",
                     help="skip the W8A16 per-GEMM pass (8-bit weights, same shapes)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8-weight per-GEMM pass (E4M3, Qwen3-8B shapes)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose HBM "
                          "counter readings scale the counter-based traffic figures")
@@ -319,54 +325,82 @@ def main():
                              "tflops": round(fl / t / 1e12, 2), "gbps": round(by / t / 1e9, 1),
                              "bound": bound, "frac": round(frac, 4)})
 
-    # W8A16 (8-bit weights) at the same shapes: a per-GEMM pass like the one above, on its
-    # own rotating pool; reported beside the W4A16 step, not part of `value`.
+    # Other code formats: a per-GEMM pass like the one above, each on its own rotating pool
+    # of packed copies; reported beside the W4A16 step, not part of `value`.
+    del pool
+    torch.cuda.empty_cache()
+
+    def variant_pass(layer, shape_list, gemm, bytes_fn, act_dtype):
+        torch.cuda.synchronize()
+        nbytes = sum(p.nbytes for p in layer)
+        ncopies = max(3, int(np.ceil(args.pool_gb * 1e9 / nbytes)))
+        vpool = [layer] + [[dataclasses.replace(p, codes=p.codes.clone(), meta=p.meta.clone())
+                            for p in layer] for _ in range(ncopies - 1)]
+        vx = {(M, K): torch.randn(M, K, device=dev).to(act_dtype)
+              for M in MS for K, _, _ in shape_list}
+        vy = {(M, N): torch.empty(M, N, device=dev, dtype=act_dtype)
+              for M in MS for _, N, _ in shape_list}
+        torch.cuda.synchronize()
+        rows, reps = [], 10
+        for ci, (M, (K, N, label)) in enumerate((M, sh) for M in MS for sh in shape_list):
+            j = [sh[:2] for sh in shape_list].index((K, N))
+            def launch_reps():
+                for r in range(reps):
+                    gemm(vx[(M, K)], vpool[(ci * reps + r) % ncopies][j], out=vy[(M, N)])
+            launch_reps()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                launch_reps()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            fl, by = gemm_flops(M, K, N), bytes_fn(M, K, N, g)
+            bound = "hbm" if M <= 64 else "mfma"
+            frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
+                (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
+            rows.append({"M": M, "K": K, "N": N, "layer": label,
+                         "kernel": mp.config_name(mp.select_config(M, N, K, g, act_dtype)),
+                         "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                         "gbps": round(by / t / 1e9, 1), "bound": bound,
+                         "frac": round(frac, 4)})
+        del vpool, vx, vy
+        torch.cuda.empty_cache()
+        return rows
+
+    def dev_f16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+
+    # W8A16 (8-bit weights, asymmetric) at the Llama-3-8B shapes, fp16 activations.
     w8 = []
     if not args.no_w8:
-        del pool
-        torch.cuda.empty_cache()
         layer8 = []
         for K, N, label in shapes:
             codes, scales, zeros = workloads.weights_w8(K, N, g, False, wl.scale_lo, wl.scale_hi,
                                                         workloads.seed_for("bench-w8", 0, K, N))
-            layer8.append(mp.pack_weights_w8(
-                torch.from_numpy(codes).to(dev),
-                torch.from_numpy(scales.view(np.int16)).to(dev).view(torch.float16),
-                torch.from_numpy(zeros).to(dev), g))
-        torch.cuda.synchronize()
-        bytes8 = sum(p.nbytes for p in layer8)
-        copies8 = max(3, int(np.ceil(args.pool_gb * 1e9 / bytes8)))
-        pool8 = [layer8] + [[mp.PackedWeights(p.codes.clone(), p.meta.clone(), p.K, p.N,
-                                              p.group, p.symmetric, 8) for p in layer8]
-                            for _ in range(copies8 - 1)]
-        torch.cuda.synchronize()
-        reps = 10
-        for ci, (M, K, N, label) in enumerate(calls):
-            j = shape_idx[(K, N)]
-            def launch_reps8():
-                for r in range(reps):
-                    mp.w8a16(xs[(M, K)], pool8[(ci * reps + r) % copies8][j], out=ys[(M, N)])
-            launch_reps8()
-            torch.cuda.synchronize()
-            g8 = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g8):
-                launch_reps8()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g8.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / reps
-            fl, by = gemm_flops(M, K, N), gemm_bytes_w8(M, K, N, g)
-            bound = "hbm" if M <= 64 else "mfma"
-            frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
-                (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
-            w8.append({"M": M, "K": K, "N": N, "layer": label,
-                       "kernel": mp.config_name(cfg_of[(M, K, N, label)]),
-                       "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
-                       "gbps": round(by / t / 1e9, 1), "bound": bound, "frac": round(frac, 4)})
-        del pool8, layer8
+            layer8.append(mp.pack_weights_w8(torch.from_numpy(codes).to(dev), dev_f16(scales),
+                                             torch.from_numpy(zeros).to(dev), g))
+        w8 = variant_pass(layer8, shapes, mp.w8a16, gemm_bytes_w8, torch.float16)
+        del layer8
+
+    # FP8 (E4M3) weights at the Qwen3-8B shapes, bf16 activations.
+    fp8 = []
+    if not args.no_fp8:
+        wl8 = workloads.QWEN3_8B_FP8
+        layerf = []
+        for K, N, label in wl8.shapes:
+            codes, scales = workloads.weights_fp8(K, N, g, "e4m3", wl8.scale_lo, wl8.scale_hi,
+                                                  workloads.seed_for("bench-fp8", 0, K, N))
+            layerf.append(mp.pack_weights_fp8(torch.from_numpy(codes).to(dev), dev_f16(scales),
+                                              g, "e4m3"))
+        fp8 = variant_pass(layerf, wl8.shapes, mp.wfp8a16,
+                           lambda M, K, N, g_: gemm_bytes_w8(M, K, N, g_, symmetric=True),
+                           torch.bfloat16)
+        del layerf
 
     dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
@@ -392,6 +426,7 @@ def main():
         "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
         "per_gemm": per_call,
         "w8a16_per_gemm": w8,
+        "wfp8a16_qwen3_8b_per_gemm": fp8,
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
