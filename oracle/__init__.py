@@ -90,6 +90,10 @@ def _load():
     lib.oracle_e5m2_to_f64.restype = ctypes.c_double
     lib.oracle_dequant_fp8.argtypes = [u8p, u16p, i, i, i, i, i, u16p]
     lib.oracle_dequant_fp8.restype = None
+    lib.oracle_padded_k.argtypes = [i]
+    lib.oracle_padded_k.restype = i
+    lib.oracle_padded_n.argtypes = [i]
+    lib.oracle_padded_n.restype = i
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -146,11 +150,11 @@ def dequant(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     K, N = codes.shape
     scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
-    assert K % group == 0 and scales_bits.shape == (K // group, N)
+    assert scales_bits.shape == (-(-K // group), N)
     zp = None
     if zeros is not None:
         zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
-        assert zeros.shape == (K // group, N)
+        assert zeros.shape == (-(-K // group), N)
         zp = _ptr(zeros, ctypes.c_uint8)
     w = np.empty((K, N), dtype=np.uint16)
     lib.oracle_dequant(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16), zp,
@@ -178,6 +182,12 @@ def w4a16(x_bits, codes, scales_bits, zeros, group, dtype="f16", threads=1):
     return gemm(x_bits, dequant(codes, scales_bits, zeros, group, dtype), dtype, threads)
 
 
+def padded_shape(K: int, N: int) -> tuple[int, int]:
+    """(Kp, Np): the packed planes' padded matrix for a user matrix of K x N."""
+    lib = _load()
+    return int(lib.oracle_padded_k(K)), int(lib.oracle_padded_n(N))
+
+
 def packed_code_bytes(K: int, N: int) -> int:
     return int(_load().oracle_packed_code_bytes(K, N))
 
@@ -191,11 +201,13 @@ def pack(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None, g
     lib = _load()
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     K, N = codes.shape
-    assert K % 128 == 0 and K % group == 0 and N % 16 == 0
+    rows = -(-K // group)
     scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert scales_bits.shape == (rows, N)
     zp = None
     if zeros is not None:
         zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        assert zeros.shape == (rows, N)
         zp = _ptr(zeros, ctypes.c_uint8)
     pc = np.empty(packed_code_bytes(K, N), dtype=np.uint8)
     pm = np.empty(packed_meta_bytes(K, N, group, zeros is None), dtype=np.uint8)
@@ -211,8 +223,9 @@ def unpack(packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int, gr
     pc = np.ascontiguousarray(packed_codes, dtype=np.uint8)
     pm = np.ascontiguousarray(packed_meta, dtype=np.uint8)
     codes = np.empty((K, N), dtype=np.uint8)
-    scales = np.empty((K // group, N), dtype=np.uint16)
-    zeros = None if symmetric else np.empty((K // group, N), dtype=np.uint8)
+    rows = -(-K // group)
+    scales = np.empty((rows, N), dtype=np.uint16)
+    zeros = None if symmetric else np.empty((rows, N), dtype=np.uint8)
     lib.oracle_unpack(_ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8), K, N, group,
                       int(bool(symmetric)), _ptr(codes, ctypes.c_uint8),
                       _ptr(scales, ctypes.c_uint16),
@@ -229,11 +242,11 @@ def dequant_w8(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | N
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     K, N = codes.shape
     scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
-    assert K % group == 0 and scales_bits.shape == (K // group, N)
+    assert scales_bits.shape == (-(-K // group), N)
     zp = None
     if zeros is not None:
         zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
-        assert zeros.shape == (K // group, N)
+        assert zeros.shape == (-(-K // group), N)
         zp = _ptr(zeros, ctypes.c_uint8)
     w = np.empty((K, N), dtype=np.uint16)
     lib.oracle_dequant_w8(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16), zp,
@@ -259,11 +272,13 @@ def pack_w8(codes: np.ndarray, scales_bits: np.ndarray, zeros: np.ndarray | None
     lib = _load()
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     K, N = codes.shape
-    assert K % 128 == 0 and K % group == 0 and N % 16 == 0
+    rows = -(-K // group)
     scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert scales_bits.shape == (rows, N)
     zp = None
     if zeros is not None:
         zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        assert zeros.shape == (rows, N)
         zp = _ptr(zeros, ctypes.c_uint8)
     pc = np.empty(packed_code_bytes_w8(K, N), dtype=np.uint8)
     pm = np.zeros(packed_meta_bytes_w8(K, N, group, zeros is None), dtype=np.uint8)
@@ -279,8 +294,9 @@ def unpack_w8(packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int,
     pc = np.ascontiguousarray(packed_codes, dtype=np.uint8)
     pm = np.ascontiguousarray(packed_meta, dtype=np.uint8)
     codes = np.empty((K, N), dtype=np.uint8)
-    scales = np.empty((K // group, N), dtype=np.uint16)
-    zeros = None if symmetric else np.empty((K // group, N), dtype=np.uint8)
+    rows = -(-K // group)
+    scales = np.empty((rows, N), dtype=np.uint16)
+    zeros = None if symmetric else np.empty((rows, N), dtype=np.uint8)
     lib.oracle_unpack_w8(_ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8), K, N, group,
                          int(bool(symmetric)), _ptr(codes, ctypes.c_uint8),
                          _ptr(scales, ctypes.c_uint16),
@@ -308,7 +324,7 @@ def dequant_fp8(codes: np.ndarray, scales_bits: np.ndarray, group: int, fmt: str
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     K, N = codes.shape
     scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
-    assert K % group == 0 and scales_bits.shape == (K // group, N)
+    assert scales_bits.shape == (-(-K // group), N)
     w = np.empty((K, N), dtype=np.uint16)
     lib.oracle_dequant_fp8(_ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16),
                            K, N, group, FP8_FORMATS[fmt], _dtype_code(dtype),

@@ -24,7 +24,8 @@
  *     its specification (see include/mpgemm.h), not derived from the GPU code.
  *
  * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py; the
- * 8-bit functions by tests/test_oracle_w8.py, the FP8 ones by tests/test_oracle_fp8.py).
+ * 8-bit functions by tests/test_oracle_w8.py, the FP8 ones by tests/test_oracle_fp8.py,
+ * packing of ragged shapes by tests/test_oracle_ragged.py).
  */
 #include <math.h>
 #include <stddef.h>
@@ -117,8 +118,8 @@ static uint16_t f64_to_act(double v, int dtype) {
 /*
  * w[k][n] = round_act((q[k][n] - z[k/g][n]) * s[k/g][n])          [TurboMind, Fig. 6]
  *   codes  uint8 [K][N], low 4 bits used (the code is an unsigned 4-bit integer)
- *   scales fp16  [K/g][N]
- *   zeros  uint8 [K/g][N], low 4 bits used; NULL means symmetric codes with zero 8
+ *   scales fp16  [ceil(K/g)][N]
+ *   zeros  uint8 [ceil(K/g)][N], low 4 bits used; NULL means symmetric codes with zero 8
  *   w      out, activation format bits, [K][N]
  */
 void oracle_dequant(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
@@ -180,6 +181,19 @@ void oracle_gemm(const uint16_t *X, const uint16_t *w, int M, int N, int K, int 
  */
 static int nibble_of_element(int i) { return (i % 2 == 0) ? i / 2 : 4 + i / 2; }
 
+/*
+ * Ragged shapes [TurboMind, Fig. 24: a data matrix padded up to the hardware tile]: the
+ * planes describe the matrix padded to Kp x Np, Np = N rounded up to a multiple of 16,
+ * Kp = K when K % 128 == 0, else K rounded up to a multiple of 256.  The user arrays stay
+ * [K][N] (codes) and [ceil(K/g)][N] (scales, zeros).  Padding: in columns n >= N, code 0,
+ * scale 0 and zero 0; in rows k >= K of columns n < N, the code equals the element's zero
+ * point (its group's zero, 0 in groups past ceil(K/g), 8 or 128 for symmetric codes), so
+ * every padded weight dequantizes to zero.  Groups past ceil(K/g) have scale 0, zero 0.
+ */
+int oracle_padded_k(int K) { return K % 128 == 0 ? K : (K + 255) / 256 * 256; }
+int oracle_padded_n(int N) { return (N + 15) / 16 * 16; }
+static int groups_of(int K, int g) { return (K + g - 1) / g; }
+
 static size_t code_byte_offset(int k, int n, int K) {
     size_t T = (size_t)(n / 16) * (size_t)(K / 128) + (size_t)(k / 128);
     int kk = k % 128, nn = n % 16;
@@ -192,21 +206,31 @@ static size_t meta_index(int k, int n, int K, int g) {
     return (size_t)(n / 16) * (size_t)(K / g) * 16 + (size_t)(k / g) * 16 + (size_t)(n % 16);
 }
 
-size_t oracle_packed_code_bytes(int K, int N) { return (size_t)K * N / 2; }
+size_t oracle_packed_code_bytes(int K, int N) {
+    return (size_t)oracle_padded_k(K) * oracle_padded_n(N) / 2;
+}
 size_t oracle_packed_meta_bytes(int K, int N, int g, int symmetric) {
-    size_t groups = (size_t)(K / g) * N;
-    return groups * 2 + (symmetric ? 0 : groups / 2);
+    size_t cells = (size_t)(oracle_padded_k(K) / g) * oracle_padded_n(N);
+    return cells * 2 + (symmetric ? 0 : cells / 2);
 }
 
-/* Requires K % 128 == 0, K % g == 0, N % 16 == 0. */
+/* Zero point of user element (k, n) as the padded matrix stores it. */
+static int zero_point(const uint8_t *zeros, int r, int n, int N, int rows, int sym_zero) {
+    if (!zeros) return sym_zero;
+    return r < rows ? zeros[(size_t)r * N + n] : 0;
+}
+
+/* K, N: the user matrix (any K, N >= 1; see the ragged-shape rule above). */
 void oracle_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                  int K, int N, int g, uint8_t *packed_codes, uint8_t *packed_meta) {
+    const int Kp = oracle_padded_k(K), Np = oracle_padded_n(N), rows = groups_of(K, g);
     memset(packed_codes, 0, oracle_packed_code_bytes(K, N));
     memset(packed_meta, 0, oracle_packed_meta_bytes(K, N, g, zeros == NULL));
-    for (int k = 0; k < K; ++k) {
-        for (int n = 0; n < N; ++n) {
-            uint32_t q = codes[(size_t)k * N + n] & 0xf;
-            size_t off = code_byte_offset(k, n, K);
+    for (int k = 0; k < Kp; ++k) {
+        for (int n = 0; n < N; ++n) {              /* columns n >= N keep code 0 */
+            uint32_t q = k < K ? (codes[(size_t)k * N + n] & 0xf)
+                               : (uint32_t)(zero_point(zeros, k / g, n, N, rows, 8) & 0xf);
+            size_t off = code_byte_offset(k, n, Kp);
             uint32_t word;
             memcpy(&word, packed_codes + off, 4);
             word |= q << (4 * nibble_of_element(k % 8));
@@ -214,10 +238,10 @@ void oracle_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *ze
         }
     }
     uint16_t *meta_scales = (uint16_t *)packed_meta;
-    uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
-    for (int r = 0; r < K / g; ++r) {
+    uint8_t *meta_zeros = packed_meta + (size_t)(Kp / g) * Np * 2;
+    for (int r = 0; r < rows; ++r) {
         for (int n = 0; n < N; ++n) {
-            size_t e = meta_index(r * g, n, K, g);
+            size_t e = meta_index(r * g, n, Kp, g);
             meta_scales[e] = scales[(size_t)r * N + n];
             if (zeros) {
                 uint8_t z = zeros[(size_t)r * N + n] & 0xf;
@@ -227,21 +251,23 @@ void oracle_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *ze
     }
 }
 
-/* Inverse of oracle_pack.  zeros is written only for asymmetric packing. */
+/* Inverse of oracle_pack (the user [K][N] part).  zeros is written only for asymmetric
+ * packing. */
 void oracle_unpack(const uint8_t *packed_codes, const uint8_t *packed_meta, int K, int N,
                    int g, int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    const int Kp = oracle_padded_k(K), Np = oracle_padded_n(N), rows = groups_of(K, g);
     for (int k = 0; k < K; ++k) {
         for (int n = 0; n < N; ++n) {
             uint32_t word;
-            memcpy(&word, packed_codes + code_byte_offset(k, n, K), 4);
+            memcpy(&word, packed_codes + code_byte_offset(k, n, Kp), 4);
             codes[(size_t)k * N + n] = (uint8_t)((word >> (4 * nibble_of_element(k % 8))) & 0xf);
         }
     }
     const uint16_t *meta_scales = (const uint16_t *)packed_meta;
-    const uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
-    for (int r = 0; r < K / g; ++r) {
+    const uint8_t *meta_zeros = packed_meta + (size_t)(Kp / g) * Np * 2;
+    for (int r = 0; r < rows; ++r) {
         for (int n = 0; n < N; ++n) {
-            size_t e = meta_index(r * g, n, K, g);
+            size_t e = meta_index(r * g, n, Kp, g);
             scales[(size_t)r * N + n] = meta_scales[e];
             if (!symmetric && zeros) {
                 uint8_t b = meta_zeros[e / 2];
@@ -258,7 +284,7 @@ void oracle_unpack(const uint8_t *packed_codes, const uint8_t *packed_meta, int 
  * The 8-bit reading of the same group form: w = round_act((q - z) * s) with q and z
  * unsigned 8-bit integers (0..255) and z = 128 for symmetric codes.  (q - z) is an
  * integer of at most 9 bits, so the product with an 11-bit fp16 scale is exact in fp64.
- *   codes  uint8 [K][N]; scales fp16 [K/g][N]; zeros uint8 [K/g][N] or NULL (z = 128)
+ *   codes  uint8 [K][N]; scales fp16 [ceil(K/g)][N]; zeros the same shape or NULL (z = 128)
  *   w      out, activation format bits, [K][N]
  */
 void oracle_dequant_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
@@ -295,40 +321,49 @@ static size_t code8_byte_offset(int k, int n, int K) {
     return T * 1024 + (size_t)lane8 * 16 + (size_t)(kk / 32) * 8 + (size_t)(kk % 8);
 }
 
-size_t oracle_packed_code_bytes_w8(int K, int N) { return (size_t)K * N; }
+size_t oracle_packed_code_bytes_w8(int K, int N) {
+    return (size_t)oracle_padded_k(K) * oracle_padded_n(N);
+}
 size_t oracle_packed_meta_bytes_w8(int K, int N, int g, int symmetric) {
-    size_t groups = (size_t)(K / g) * N;
-    return groups * 2 + (symmetric ? 0 : groups);
+    size_t cells = (size_t)(oracle_padded_k(K) / g) * oracle_padded_n(N);
+    return cells * 2 + (symmetric ? 0 : cells);
 }
 
-/* Requires K % 128 == 0, K % g == 0, N % 16 == 0. */
+/* K, N: the user matrix; padding as for 4-bit codes (symmetric zero point 128). */
 void oracle_pack_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                     int K, int N, int g, uint8_t *packed_codes, uint8_t *packed_meta) {
-    for (int k = 0; k < K; ++k)
+    const int Kp = oracle_padded_k(K), Np = oracle_padded_n(N), rows = groups_of(K, g);
+    memset(packed_codes, 0, oracle_packed_code_bytes_w8(K, N));
+    memset(packed_meta, 0, oracle_packed_meta_bytes_w8(K, N, g, zeros == NULL));
+    for (int k = 0; k < Kp; ++k)
         for (int n = 0; n < N; ++n)
-            packed_codes[code8_byte_offset(k, n, K)] = codes[(size_t)k * N + n];
+            packed_codes[code8_byte_offset(k, n, Kp)] =
+                k < K ? codes[(size_t)k * N + n]
+                      : (uint8_t)zero_point(zeros, k / g, n, N, rows, 128);
     uint16_t *meta_scales = (uint16_t *)packed_meta;
-    uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
-    for (int r = 0; r < K / g; ++r) {
+    uint8_t *meta_zeros = packed_meta + (size_t)(Kp / g) * Np * 2;
+    for (int r = 0; r < rows; ++r) {
         for (int n = 0; n < N; ++n) {
-            size_t e = meta_index(r * g, n, K, g);
+            size_t e = meta_index(r * g, n, Kp, g);
             meta_scales[e] = scales[(size_t)r * N + n];
             if (zeros) meta_zeros[e] = zeros[(size_t)r * N + n];
         }
     }
 }
 
-/* Inverse of oracle_pack_w8.  zeros is written only for asymmetric packing. */
+/* Inverse of oracle_pack_w8 (the user [K][N] part).  zeros is written only for asymmetric
+ * packing. */
 void oracle_unpack_w8(const uint8_t *packed_codes, const uint8_t *packed_meta, int K, int N,
                       int g, int symmetric, uint8_t *codes, uint16_t *scales, uint8_t *zeros) {
+    const int Kp = oracle_padded_k(K), Np = oracle_padded_n(N), rows = groups_of(K, g);
     for (int k = 0; k < K; ++k)
         for (int n = 0; n < N; ++n)
-            codes[(size_t)k * N + n] = packed_codes[code8_byte_offset(k, n, K)];
+            codes[(size_t)k * N + n] = packed_codes[code8_byte_offset(k, n, Kp)];
     const uint16_t *meta_scales = (const uint16_t *)packed_meta;
-    const uint8_t *meta_zeros = packed_meta + (size_t)(K / g) * N * 2;
-    for (int r = 0; r < K / g; ++r) {
+    const uint8_t *meta_zeros = packed_meta + (size_t)(Kp / g) * Np * 2;
+    for (int r = 0; r < rows; ++r) {
         for (int n = 0; n < N; ++n) {
-            size_t e = meta_index(r * g, n, K, g);
+            size_t e = meta_index(r * g, n, Kp, g);
             scales[(size_t)r * N + n] = meta_scales[e];
             if (!symmetric && zeros) zeros[(size_t)r * N + n] = meta_zeros[e];
         }

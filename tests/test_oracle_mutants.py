@@ -66,6 +66,19 @@ MUTANTS_FP8 = {
 }
 
 
+MUTANTS_RAGGED = {
+    "pad_k_to_128": ("(K + 255) / 256 * 256", "(K + 127) / 128 * 128"),
+    "pad_n_to_32": ("(N + 15) / 16 * 16", "(N + 31) / 32 * 32"),
+    "pad_code_zero_w4": ("(uint32_t)(zero_point(zeros, k / g, n, N, rows, 8) & 0xf)", "0u"),
+    "pad_sym_zero_w8": ("(uint8_t)zero_point(zeros, k / g, n, N, rows, 128)",
+                        "(uint8_t)zero_point(zeros, k / g, n, N, rows, 0)"),
+    "pad_group_past_end": ("return r < rows ? zeros[(size_t)r * N + n] : 0;",
+                           "return r < rows ? zeros[(size_t)r * N + n] : 8;"),
+    "unpack_w8_unpadded": ("codes[(size_t)k * N + n] = packed_codes[code8_byte_offset(k, n, Kp)];",
+                           "codes[(size_t)k * N + n] = packed_codes[code8_byte_offset(k, n, K)];"),
+}
+
+
 def _run_pins(text, before, after, pins, tmp_path):
     assert text.count(before) == 1, f"mutation anchor not found once: {before}"
     src = tmp_path / "mutant.c"
@@ -103,4 +116,11 @@ def test_pins_catch_planted_mistake(name, tmp_path):
 def test_fp8_pins_catch_planted_mistake(name, tmp_path):
     before, after = MUTANTS_FP8[name]
     res = _run_pins(open(SRC).read(), before, after, "test_oracle_fp8.py", tmp_path)
+    assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_RAGGED))
+def test_ragged_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTANTS_RAGGED[name]
+    res = _run_pins(open(SRC).read(), before, after, "test_oracle_ragged.py", tmp_path)
     assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
