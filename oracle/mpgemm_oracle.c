@@ -184,13 +184,13 @@ static int nibble_of_element(int i) { return (i % 2 == 0) ? i / 2 : 4 + i / 2; }
 /*
  * Ragged shapes [TurboMind, Fig. 24: a data matrix padded up to the hardware tile]: the
  * planes describe the matrix padded to Kp x Np, Np = N rounded up to a multiple of 16,
- * Kp = K when K % 128 == 0, else K rounded up to a multiple of 256.  The user arrays stay
+ * Kp = K rounded up to a multiple of 128 (one tile of the layout).  The user arrays stay
  * [K][N] (codes) and [ceil(K/g)][N] (scales, zeros).  Padding: in columns n >= N, code 0,
  * scale 0 and zero 0; in rows k >= K of columns n < N, the code equals the element's zero
  * point (its group's zero, 0 in groups past ceil(K/g), 8 or 128 for symmetric codes), so
  * every padded weight dequantizes to zero.  Groups past ceil(K/g) have scale 0, zero 0.
  */
-int oracle_padded_k(int K) { return K % 128 == 0 ? K : (K + 255) / 256 * 256; }
+int oracle_padded_k(int K) { return (K + 127) / 128 * 128; }
 int oracle_padded_n(int N) { return (N + 15) / 16 * 16; }
 static int groups_of(int K, int g) { return (K + g - 1) / g; }
 

@@ -67,7 +67,7 @@ MUTANTS_FP8 = {
 
 
 MUTANTS_RAGGED = {
-    "pad_k_to_128": ("(K + 255) / 256 * 256", "(K + 127) / 128 * 128"),
+    "pad_k_to_256": ("(K + 127) / 128 * 128", "(K + 255) / 256 * 256"),
     "pad_n_to_32": ("(N + 15) / 16 * 16", "(N + 31) / 32 * 32"),
     "pad_code_zero_w4": ("(uint32_t)(zero_point(zeros, k / g, n, N, rows, 8) & 0xf)", "0u"),
     "pad_sym_zero_w8": ("(uint8_t)zero_point(zeros, k / g, n, N, rows, 128)",

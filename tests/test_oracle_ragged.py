@@ -1,7 +1,7 @@
 """Pins for the oracle's ragged-shape packing (K % 128 != 0 or N % 16 != 0).
 
 Rule under test: the planes of a K x N matrix are those of the matrix padded to Kp x Np
-(Np = N rounded up to 16; Kp = K if K % 128 == 0, else K rounded up to 256), where every
+(Np = N rounded up to 16; Kp = K rounded up to 128), where every
 padded weight dequantizes to zero: in padded rows k >= K the code is the element's zero
 point (its group's zero, 0 in groups past ceil(K/g), 8 / 128 for symmetric codes); padded
 columns and padded groups hold code 0, scale 0 and zero 0.
@@ -18,12 +18,12 @@ import pytest
 
 import oracle
 
-SHAPES = [(200, 40, 64), (200, 40, 128), (72, 16, 64), (128, 33, 128), (384, 7, 64),
+SHAPES = [(200, 40, 64), (200, 40, 128), (72, 16, 64), (128, 33, 128), (384, 7, 64), (40, 20, 64),
           (136, 1, 128), (1000, 50, 128)]
 
 
 def pad_rule(K, N):
-    Kp = K if K % 128 == 0 else -(-K // 256) * 256
+    Kp = -(-K // 128) * 128
     return Kp, -(-N // 16) * 16
 
 
