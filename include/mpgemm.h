@@ -15,10 +15,12 @@
  * ---------------------------------------------------------------------------------
  * Quantized weights (the caller's unpacked form)
  *   codes  uint8  [K][N] row-major, each an unsigned 4-bit integer q in 0..15
- *   scales fp16   [K/g][N] row-major (IEEE binary16 bits), one per (group, column)
- *   zeros  uint8  [K/g][N] row-major, each a 4-bit integer z in 0..15; or NULL for
+ *   scales fp16   [G][N] row-major (IEEE binary16 bits), one per (group, column),
+ *                 G = ceil(K/g) group rows
+ *   zeros  uint8  [G][N] row-major, each a 4-bit integer z in 0..15; or NULL for
  *                 symmetric codes, whose zero is 8
- *   A group is g consecutive rows of k: rows [r*g, (r+1)*g) share scale and zero row r.
+ *   A group is g consecutive rows of k: rows [r*g, (r+1)*g) share scale and zero row r
+ *   (the last group is shorter when K % g != 0).
  *   Only the low 4 bits of codes and zeros are read (higher bits are ignored).
  *   Dequantized weight: w[k][n] = (q[k][n] - z[k/g][n]) * s[k/g][n], rounded once
  *   (round to nearest even) to the activation format.
@@ -42,6 +44,13 @@
  *   ((K/g)*N*2 bytes; the scales of one strip are contiguous).  Then, for asymmetric codes
  *   only, zeros: 4-bit values at the same index e, byte e/2, low nibble for even e and high
  *   nibble for odd e ((K/g)*N/2 bytes).
+ *   Ragged shapes [TurboMind, Fig. 24: a data matrix padded up to the hardware tile].  The
+ *   formulas above (and those of the 8-bit layout below) take K and N as the padded sizes
+ *   Kp x Np: Np = N rounded up to a multiple of 16; Kp = K rounded up to a multiple of
+ *   128.  Every padded weight dequantizes to zero: padded
+ *   columns (n >= N) hold code 0, scale 0 and zero 0; padded rows (k >= K) of real columns
+ *   hold the element's zero point as their code (its group's zero, 0 in groups past G,
+ *   8 -- or 128 for 8-bit codes -- when symmetric); groups past G hold scale 0 and zero 0.
  *
  * Conventions for every call
  *   - Pointers are device pointers (hipMalloc'd or equivalent) owned by the caller.  The
@@ -52,9 +61,11 @@
  *   - Return value: MPGEMM_OK or a negative mpgemm_status.  MPGEMM_ERR_HIP means the HIP
  *     runtime rejected the launch (e.g. no gfx950 device); mpgemm_status_string() names it.
  *   - Calls are reentrant; concurrent calls must not write overlapping outputs.
- *   - Shape limits: K % 128 == 0, K % g == 0, g in {64, 128}, N % 16 == 0, M >= 0,
- *     (M+128)*K, K*N and M*N each below 2^31.  M == 0 or N == 0 is a valid no-op.
+ *   - Shape limits: K % 8 == 0 (activation rows stay 16-byte aligned), any N >= 0,
+ *     g in {64, 128}, M >= 0; with the padded sizes Kp, Np: (M+128)*Kp, Kp*Np and M*Np each
+ *     below 2^31.  M == 0 or N == 0 is a valid no-op.
  *   - Alignment: every device pointer 16-byte aligned (MPGEMM_ERR_ALIGNMENT otherwise).
+ *     Rows of Y need not be: for N % 4 != 0 the kernels store 2-byte elements.
  */
 #ifndef MPGEMM_H
 #define MPGEMM_H
@@ -85,10 +96,10 @@ typedef enum {
 /* Layout version of the packed planes this library reads and writes. */
 int mpgemm_layout_version(void);
 
-/* Size of the packed codes plane: K*N/2 bytes.  0 if the shape is unsupported. */
+/* Size of the packed codes plane: Kp*Np/2 bytes.  0 if the shape is unsupported. */
 size_t mpgemm_packed_code_bytes(int K, int N);
 
-/* Size of the packed meta plane: (K/g)*N*2 + (symmetric ? 0 : (K/g)*N/2) bytes.
+/* Size of the packed meta plane: (Kp/g)*Np*2 + (symmetric ? 0 : (Kp/g)*Np/2) bytes.
  * 0 if the shape or group size is unsupported. */
 size_t mpgemm_packed_meta_bytes(int K, int N, int group, int symmetric);
 
@@ -97,8 +108,8 @@ size_t mpgemm_packed_meta_bytes(int K, int N, int group, int symmetric);
  * scales and zeros (layouts above) into the version-1 packed planes.  zeros == NULL packs
  * symmetric weights (zero 8) and writes no zero plane.  A pure bit permutation: lossless.
  *   codes        in  [K][N] uint8
- *   scales       in  [K/g][N] fp16 bits
- *   zeros        in  [K/g][N] uint8, or NULL
+ *   scales       in  [G][N] fp16 bits, G = ceil(K/g)
+ *   zeros        in  [G][N] uint8, or NULL
  *   packed_codes out mpgemm_packed_code_bytes(K, N) bytes
  *   packed_meta  out mpgemm_packed_meta_bytes(K, N, group, zeros == NULL) bytes
  */
@@ -151,9 +162,9 @@ int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void 
  * (M <= 16*id); 10 tiled large-M kernel on 16x16x32 MFMAs with a four-stage LDS ring;
  * 11 tiled large-M kernel with two LDS buffers (any K); 12 tiled large-M kernel on 32x32x16
  * MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a 256 x 128
- * tile.  Ids 10, 12 and 13 need K % 256 == 0 and run as id 11 on other K.  The selector
- * picks 1..4 for M <= 64; else 11 when K % 256 != 0; else 13 when M >= 512 and
- * (N >= 16384 or K >= 8192); else 12.
+ * tile.  Id 10 needs K % 256 == 0 and runs as id 11 on other K; ids 10 and 11 do not take
+ * ragged K (K % 128 != 0).  Ids 12 and 13 take every shape.  The selector picks 1..4 for
+ * M <= 64; else 13 when M >= 512 and (N >= 16384 or K >= 8192); else 12.
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);
@@ -167,8 +178,8 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
  * 8-bit weights (W8A16).  [TurboMind, abstract (pg1)]: the GEMM pipeline generalizes
  * across precision formats.  Same group form with 8-bit integers:
  *   codes  uint8 [K][N], all 8 bits: q in 0..255
- *   zeros  uint8 [K/g][N], all 8 bits: z in 0..255; or NULL for symmetric codes (z = 128)
- *   scales fp16 [K/g][N] as above
+ *   zeros  uint8 [G][N], all 8 bits: z in 0..255; or NULL for symmetric codes (z = 128)
+ *   scales fp16 [G][N] as above
  *   w[k][n] = (q - z) * s rounded once to the activation format.
  * Packed 8-bit layout (same layout version)
  *   Codes plane, K*N bytes.  Tiles of 16 columns x 64 rows of k, 1 KiB each; tile
@@ -180,14 +191,15 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
  *   pattern of 1024 turns each pair of codes into the (k, k+1) register pair 1024 + q.
  *   Meta plane.  Scales exactly as for 4-bit codes; then, for asymmetric codes only, one
  *   zero byte per element at the same index e ((K/g)*N bytes).
- * Shape limits and conventions as above; in addition M > 64 needs K % 256 == 0.  The
- * workspace is sized by mpgemm_workspace_bytes (the same for both code widths).
+ * Shape limits and conventions as above (ragged shapes padded the same way, symmetric
+ * padding code 128).  The workspace is sized by mpgemm_workspace_bytes (the same for both
+ * code widths).
  */
 
-/* Size of the packed 8-bit codes plane: K*N bytes.  0 if the shape is unsupported. */
+/* Size of the packed 8-bit codes plane: Kp*Np bytes.  0 if the shape is unsupported. */
 size_t mpgemm_packed_code_bytes_w8(int K, int N);
 
-/* Size of the packed 8-bit meta plane: (K/g)*N*2 + (symmetric ? 0 : (K/g)*N) bytes. */
+/* Size of the packed 8-bit meta plane: (Kp/g)*Np*2 + (symmetric ? 0 : (Kp/g)*Np) bytes. */
 size_t mpgemm_packed_meta_bytes_w8(int K, int N, int group, int symmetric);
 
 /* Offline packing of 8-bit codes into the 8-bit layout; contract as mpgemm_pack_weights
@@ -225,7 +237,7 @@ int mpgemm_w8a16_config(const void *X, int dtype, const void *packed_codes,
  *            MPGEMM_FP8_E5M2: 1 sign, 5 exponent bits (bias 15), 2 fraction bits,
  *                             subnormals, infinities and NaNs as in binary16 (it is the
  *                             high byte of binary16);
- *   scales fp16 [K/g][N] as above
+ *   scales fp16 [G][N] as above
  *   w[k][n] = fp8(q) * s rounded once to the activation format (NaN and infinite codes
  *   propagate as the product does).
  * Packing: mpgemm_pack_weights_w8 with zeros == NULL (the codes are bytes, so the 8-bit

@@ -43,9 +43,14 @@ def test_layout_version_and_sizes():
     assert mp.packed_code_bytes(4096, 6144) == 4096 * 6144 // 2
     assert mp.packed_meta_bytes(4096, 6144, 128, False) == 32 * 6144 * 2 + 32 * 6144 // 2
     assert mp.packed_meta_bytes(5120, 10240, 64, True) == 80 * 10240 * 2
-    assert mp.packed_code_bytes(100, 16) == 0          # K % 128 != 0
-    assert mp.packed_meta_bytes(256, 24, 128, False) == 0   # N % 16 != 0
+    assert mp.packed_code_bytes(100, 16) == 0          # K % 8 != 0
     assert mp.packed_meta_bytes(256, 32, 32, False) == 0    # unsupported group
+    # ragged shapes: planes of the matrix padded to Kp x Np (Np: 16s; Kp: 128s)
+    assert mp.packed_code_bytes(200, 24) == 256 * 32 // 2
+    assert mp.packed_meta_bytes(200, 24, 64, False) == 4 * 32 * 2 + 4 * 32 // 2
+    assert mp.packed_code_bytes(384, 1) == 384 * 16 // 2
+    assert mp.lib().mpgemm_packed_code_bytes_w8(136, 7) == 256 * 16
+    assert mp.lib().mpgemm_packed_meta_bytes_w8(136, 7, 128, 1) == 2 * 16 * 2
     assert lib.mpgemm_workspace_bytes(16, 4096, 4096, 128, 0) == 0
 
 
@@ -63,8 +68,9 @@ def test_selector_and_config_names():
     assert mp.lib().mpgemm_select_config(64, 4096, 4096, 128, 1) == 4
     assert mp.lib().mpgemm_select_config(65, 4096, 4096, 128, 0) == 12
     assert mp.lib().mpgemm_select_config(2048, 4096, 4096, 128, 0) == 12
-    assert mp.lib().mpgemm_select_config(2048, 4096, 4224, 128, 0) == 11   # K % 256 != 0
+    assert mp.lib().mpgemm_select_config(2048, 4096, 4224, 128, 0) == 12   # K % 256 == 128
     assert mp.lib().mpgemm_select_config(64, 4096, 4224, 128, 0) == 4
+    assert mp.lib().mpgemm_select_config(2048, 4096, 4104, 128, 0) == 12   # ragged K: Kp 4224
     assert mp.lib().mpgemm_select_config(2048, 6144, 4096, 128, 0) == 12
     assert mp.lib().mpgemm_select_config(2048, 28672, 4096, 128, 0) == 13  # wide N
     assert mp.lib().mpgemm_select_config(2048, 4096, 14336, 128, 0) == 13  # long K
@@ -90,7 +96,8 @@ def _gemm(X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, sym=0, Y=A, cfg=N
     (dict(K=100), UNSUPPORTED),
     (dict(K=384, g=256), UNSUPPORTED),
     (dict(g=32), UNSUPPORTED),
-    (dict(N=24), UNSUPPORTED),
+    (dict(K=260), UNSUPPORTED),                     # K % 8 != 0
+    (dict(N=-1), INVALID),
     (dict(M=70000, K=65536), UNSUPPORTED),          # M*K beyond 2^31
     (dict(M=16384 - 128, K=131072), UNSUPPORTED),    # (M+128)*K at 2^31
     (dict(X=0), INVALID),
@@ -116,7 +123,7 @@ def test_pack_and_unpack_validation():
     lib = mp.lib()
     vp = ctypes.c_void_p
     assert lib.mpgemm_pack_weights(None, vp(A), None, 256, 32, 128, vp(A), vp(A), None) == INVALID
-    assert lib.mpgemm_pack_weights(vp(A), vp(A), None, 200, 32, 128, vp(A), vp(A), None) == UNSUPPORTED
+    assert lib.mpgemm_pack_weights(vp(A), vp(A), None, 204, 32, 128, vp(A), vp(A), None) == UNSUPPORTED
     assert lib.mpgemm_pack_weights(vp(A), vp(A), None, 256, 32, 96, vp(A), vp(A), None) == UNSUPPORTED
     assert lib.mpgemm_pack_weights(vp(A), vp(MIS), None, 256, 32, 128, vp(A), vp(A), None) == ALIGN
     assert lib.mpgemm_pack_weights(vp(A), vp(A), vp(MIS), 256, 32, 128, vp(A), vp(A), None) == ALIGN
@@ -184,8 +191,8 @@ def _fp8(fmt=0, X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, Y=A, cfg=No
     (dict(Y=MIS), ALIGN),
     (dict(cfg=10, M=128), UNSUPPORTED),              # the 16x16x32 tiled kernels take 4-bit only
     (dict(cfg=11, M=128), UNSUPPORTED),
-    (dict(cfg=12, M=128, K=384), UNSUPPORTED),       # the 32x32x16 kernels need K % 256 == 0
-    (dict(M=65, K=384), UNSUPPORTED),
+    (dict(cfg=10, M=128, K=384), UNSUPPORTED),
+    (dict(cfg=12, M=128, K=4), UNSUPPORTED),
     (dict(M=0), OK),
 ])
 def test_fp8_gemm_validation(kw, status):
@@ -196,3 +203,9 @@ def test_binding_fp8_format_names_match_header():
     text = open(HEADER).read()
     assert "MPGEMM_FP8_E4M3 = 0" in text and "MPGEMM_FP8_E5M2 = 1" in text
     assert mp.FP8_FORMATS == {"e4m3": 0, "e5m2": 1}
+
+
+@pytest.mark.parametrize("cfg", [10, 11])
+def test_ragged_k_is_refused_by_the_16x16x32_tiled_kernels(cfg):
+    # K = 200 pads to 256: only the small-M and 32x32x16 kernels mask the activation tail
+    assert _gemm(M=128, K=200, cfg=cfg) == UNSUPPORTED

@@ -229,16 +229,15 @@ def host_bits_of(v):
     return np.asarray(v, dtype=np.float16).view(np.uint16)
 
 
-def test_fp8_large_m_needs_k_multiple_of_256():
-    K, N = 384, 64
-    codes, scales = workloads.weights_fp8(K, N, 128, "e4m3", 0.005, 0.02, 3)
-    packed = pack(dict(codes=codes, scales=scales, group=128, fmt="e4m3"))
-    x = torch.zeros((65, K), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(mp.MpgemmError):
-        mp.wfp8a16(x, packed)
-    y = mp.wfp8a16(x[:64], packed)          # the small-M kernel takes any K % 128 == 0
-    torch.cuda.synchronize()
-    assert not bool(y.isnan().any())
+@pytest.mark.parametrize("M", [65, 200])
+def test_fp8_k_a_multiple_of_128_not_256_runs_every_tiled_config(M):
+    K, N = 384, 64                         # three 128-deep tiles: the two-stage loop tail
+    case = workloads.make_case_fp8(workloads.QWEN3_8B_FP8, M, K, N, "e4m3")
+    packed = pack(case)
+    want = ref(case)
+    for cfg in (0, 12, 13):
+        say(f"fp8 K=384 M={M} config={cfg}")
+        assert rel_err(run(case, packed, cfg), want, "bf16") <= REL_TOL, cfg
 
 
 def test_fp8_repeated_runs_are_bitwise_identical():

@@ -24,7 +24,7 @@ REL_TOL = 5e-3
 DECODE_CONFIGS = (1, 2, 3, 4)
 PREFILL = 10          # 16x16x32 LDS-ring kernel (two-buffer kernel when K % 256 != 0)
 PREFILL_2BUF = 11
-PREFILL_X32 = 12      # 32x32x16 kernel (two-buffer kernel when K % 256 != 0)
+PREFILL_X32 = 12      # 32x32x16 kernel, 128 x 256 tile
 PREFILL_X32_TALL = 13  # the same with a 256 x 128 workgroup tile
 PREFILL_CONFIGS = (PREFILL, PREFILL_2BUF, PREFILL_X32, PREFILL_X32_TALL)
 

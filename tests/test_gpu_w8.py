@@ -158,16 +158,17 @@ def test_w8_llama3_8b_full_shapes(M, K, N, label):
 
 # --------------------------------------------------------------------- edge cases ------
 
-def test_w8_large_m_needs_k_multiple_of_256():
-    K, N = 384, 64
+@pytest.mark.parametrize("M", [65, 200])
+def test_w8_k_a_multiple_of_128_not_256_runs_every_tiled_config(M):
+    K, N = 384, 64                         # three 128-deep tiles: the two-stage loop tail
     codes, scales, zeros = workloads.weights_w8(K, N, 128, False, 0.005, 0.02, 3)
-    packed = pack8(dict(codes=codes, scales=scales, zeros=zeros, group=128))
-    x = torch.zeros((65, K), dtype=torch.float16, device="cuda")
-    with pytest.raises(mp.MpgemmError):
-        mp.w8a16(x, packed)
-    y = mp.w8a16(x[:64], packed)          # the small-M kernel takes any K % 128 == 0
-    torch.cuda.synchronize()
-    assert not bool(y.isnan().any())
+    case = dict(x=workloads.activations(M, K, "f16", 4), codes=codes, scales=scales,
+                zeros=zeros, group=128, dtype="f16")
+    packed = pack8(case)
+    want = ref8(case)
+    for cfg in (0, 12, 13):
+        say(f"w8 K=384 M={M} config={cfg}")
+        assert rel_err(run8(case, packed, cfg), want, "f16") <= REL_TOL, cfg
 
 
 def test_w8_repeated_runs_are_bitwise_identical():

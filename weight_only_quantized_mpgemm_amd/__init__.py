@@ -134,6 +134,13 @@ class PackedWeights:
         return self.codes.numel() + self.meta.numel()
 
 
+def _group_rows(K: int, group: int) -> int:
+    """Scale/zero rows of a K-deep weight: ceil(K / group) (the last group may be short)."""
+    if group not in (64, 128):
+        raise ValueError(f"group must be 64 or 128, got {group}")
+    return -(-K // group)
+
+
 def packed_code_bytes(K: int, N: int) -> int:
     return int(lib().mpgemm_packed_code_bytes(K, N))
 
@@ -157,16 +164,16 @@ def pack_weights(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor 
                  group: int, out: PackedWeights | None = None) -> PackedWeights:
     """Offline packing (mpgemm_pack_weights).
 
-    codes  uint8 [K, N] (values 0..15); scales float16 [K/g, N]; zeros uint8 [K/g, N]
-    (values 0..15) or None for symmetric codes with zero 8.
+    codes  uint8 [K, N] (values 0..15); scales float16 [G, N] with G = ceil(K/g); zeros
+    uint8 [G, N] (values 0..15) or None for symmetric codes with zero 8.  Any N and any
+    K % 8 == 0: ragged shapes are padded in the packed planes (include/mpgemm.h).
     """
     K, N = codes.shape
     _need(codes, torch.uint8, (K, N), "codes")
-    if group <= 0 or K % group:
-        raise ValueError(f"K={K} is not a multiple of group={group}")
-    _need(scales, torch.float16, (K // group, N), "scales")
+    rows = _group_rows(K, group)
+    _need(scales, torch.float16, (rows, N), "scales")
     if zeros is not None:
-        _need(zeros, torch.uint8, (K // group, N), "zeros")
+        _need(zeros, torch.uint8, (rows, N), "zeros")
     if out is None:
         out = empty_packed(K, N, group, zeros is None, codes.device)
     st = lib().mpgemm_pack_weights(_ptr(codes), _ptr(scales), _ptr(zeros), K, N, group,
@@ -179,16 +186,15 @@ def pack_weights_w8(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tens
                     group: int) -> PackedWeights:
     """Offline packing of 8-bit codes (mpgemm_pack_weights_w8).
 
-    codes  uint8 [K, N] (0..255); scales float16 [K/g, N]; zeros uint8 [K/g, N] or None for
-    symmetric codes with zero 128.
+    codes  uint8 [K, N] (0..255); scales float16 [ceil(K/g), N]; zeros uint8 of the same
+    shape or None for symmetric codes with zero 128.
     """
     K, N = codes.shape
     _need(codes, torch.uint8, (K, N), "codes")
-    if group <= 0 or K % group:
-        raise ValueError(f"K={K} is not a multiple of group={group}")
-    _need(scales, torch.float16, (K // group, N), "scales")
+    rows = _group_rows(K, group)
+    _need(scales, torch.float16, (rows, N), "scales")
     if zeros is not None:
-        _need(zeros, torch.uint8, (K // group, N), "zeros")
+        _need(zeros, torch.uint8, (rows, N), "zeros")
     cb = int(lib().mpgemm_packed_code_bytes_w8(K, N))
     mb = int(lib().mpgemm_packed_meta_bytes_w8(K, N, group, int(zeros is None)))
     if K * N and (cb == 0 or mb == 0):
@@ -208,7 +214,7 @@ def pack_weights_fp8(codes: torch.Tensor, scales: torch.Tensor, group: int,
     (mpgemm_pack_weights_w8 with zeros == NULL).
 
     codes  uint8 [K, N] FP8 bit patterns (or a float8_e4m3fn / float8_e5m2 tensor, whose
-    format then decides `fmt`); scales float16 [K/g, N].
+    format then decides `fmt`); scales float16 [ceil(K/g), N].
     """
     if codes.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         fmt = "e4m3" if codes.dtype == torch.float8_e4m3fn else "e5m2"
@@ -226,9 +232,9 @@ def unpack(packed: PackedWeights):
     K, N, g = packed.K, packed.N, packed.group
     dev = packed.codes.device
     codes = torch.empty((K, N), dtype=torch.uint8, device=dev)
-    scales = torch.empty((K // g, N), dtype=torch.float16, device=dev)
-    zeros = None if packed.symmetric else torch.empty((K // g, N), dtype=torch.uint8,
-                                                      device=dev)
+    scales = torch.empty((_group_rows(K, g), N), dtype=torch.float16, device=dev)
+    zeros = None if packed.symmetric else torch.empty((_group_rows(K, g), N),
+                                                      dtype=torch.uint8, device=dev)
     name = "mpgemm_unpack_w8" if packed.bits == 8 else "mpgemm_unpack"
     st = getattr(lib(), name)(_ptr(packed.codes), _ptr(packed.meta), K, N, g,
                               int(packed.symmetric), _ptr(codes), _ptr(scales), _ptr(zeros),

@@ -25,8 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmpgemm.so")
 SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_ring.hip",
-           "gemm_prefill_x32.hip"]
-HEADERS = ["device.hpp", "kernels.hpp"]
+           "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip", "gemm_prefill_x32_fp8.hip"]
+HEADERS = ["device.hpp", "kernels.hpp", "prefill_x32.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -50,7 +50,8 @@ def scratch_users(report: str) -> list[tuple[str, int]]:
 
 # Sources whose kernels issue MFMAs through inline asm: the compiler does not know those
 # instructions' result latency, so the build checks the generated code instead.
-ASM_MFMA_SOURCES = ["gemm_prefill_ring.hip", "gemm_prefill_x32.hip"]
+ASM_MFMA_SOURCES = ["gemm_prefill_ring.hip", "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip",
+                    "gemm_prefill_x32_fp8.hip"]
 MIN_RESULT_WAIT = 32     # wait states between an MFMA and the first read of its result
 
 

@@ -22,21 +22,28 @@ enum ConfigId {
     kConfigDecode4 = 4,
     kConfigPrefill = 10,       // 16x16x32 LDS-ring kernel when K % 256 == 0, else two-buffer
     kConfigPrefill2Buf = 11,   // two-buffer kernel
-    kConfigPrefillX32 = 12,    // 32x32x16 kernel when K % 256 == 0, else the two-buffer one
+    kConfigPrefillX32 = 12,    // 32x32x16 kernel, 128 x 256 workgroup tile
     kConfigPrefillX32Tall = 13,  // same, 256 x 128 workgroup tile
 };
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Any N >= 0 and any K >= 0 with K % 8 == 0 (activation rows stay 16-byte aligned); the
+// packed planes hold the matrix padded to padded_k(K) x padded_n(N).
 int check_shape(int M, int N, int K, int group) {
     if (M < 0 || N < 0 || K < 0) return MPGEMM_ERR_INVALID_ARG;
     if (group != 64 && group != 128) return MPGEMM_ERR_UNSUPPORTED;
-    if (K % 128 != 0 || K % group != 0 || N % 16 != 0) return MPGEMM_ERR_UNSUPPORTED;
+    if (K % 8 != 0 || K > (1 << 30) || N > (1 << 30)) return MPGEMM_ERR_UNSUPPORTED;
     // Kernels address planes with 32-bit byte offsets, including one-past-the-end rows.
-    if ((int64_t)(M + 128) * K >= kIndexLimit || (int64_t)K * N >= kIndexLimit ||
-        (int64_t)M * N >= kIndexLimit)
+    const int64_t Kp = mpgemm::padded_k(K), Np = mpgemm::padded_n(N);
+    if ((int64_t)(M + 128) * Kp >= kIndexLimit || Kp * Np >= kIndexLimit ||
+        (int64_t)M * Np >= kIndexLimit)
         return MPGEMM_ERR_UNSUPPORTED;
     return MPGEMM_OK;
+}
+
+int64_t packed_cells(int K, int N, int group) {
+    return (int64_t)(mpgemm::padded_k(K) / group) * mpgemm::padded_n(N);
 }
 
 int hip_status(hipError_t e) {
@@ -55,7 +62,6 @@ int select_config(int M, int N, int K) {
     if (M <= 32) return kConfigDecode2;
     if (M <= 48) return kConfigDecode3;
     if (M <= 64) return kConfigDecode4;
-    if (K % 256 != 0) return kConfigPrefill2Buf;
     return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
 }
 
@@ -84,18 +90,21 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
-    // 8-bit and FP8 codes run the small-M kernel and the 32x32x16 tiled kernels
-    // (K % 256 == 0).
-    if (code != mpgemm::kU4 && (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf ||
-                      ((cfg == kConfigPrefillX32 || cfg == kConfigPrefillX32Tall) && K % 256 != 0)))
+    // 8-bit and FP8 codes, and ragged K, run the small-M kernel and the 32x32x16 tiled
+    // kernels (which mask the activations past K); the 16x16x32 tiled kernels take aligned
+    // 4-bit problems only.
+    const int Kp = mpgemm::padded_k(K);
+    if ((code != mpgemm::kU4 || Kp != K) && (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf))
         return MPGEMM_ERR_UNSUPPORTED;
 
     mpgemm::GemmArgs a;
     a.X = (const uint16_t *)X;
     a.codes = (const uint32_t *)packed_codes;
     a.scales = (const uint16_t *)packed_meta;
-    a.zeros = symmetric ? nullptr : (const uint8_t *)packed_meta + (size_t)(K / group) * N * 2;
+    a.zeros = symmetric ? nullptr : (const uint8_t *)packed_meta + packed_cells(K, N, group) * 2;
     a.code = code;
+    a.Kp = Kp;
+    a.Np = mpgemm::padded_n(N);
     a.Y = (uint16_t *)Y;
     a.M = M;
     a.N = N;
@@ -114,11 +123,9 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
                 M, N, K, group, dtype, symmetric, mpgemm_config_name(cfg));
     }
     if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
-    if (cfg == kConfigPrefillX32 && K % 256 == 0) return hip_status(mpgemm::launch_prefill_x32(a, s));
-    if (cfg == kConfigPrefillX32Tall && K % 256 == 0)
-        return hip_status(mpgemm::launch_prefill_x32_tall(a, s));
-    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf || cfg == kConfigPrefillX32 ||
-        cfg == kConfigPrefillX32Tall)
+    if (cfg == kConfigPrefillX32) return hip_status(mpgemm::launch_prefill_x32(a, s));
+    if (cfg == kConfigPrefillX32Tall) return hip_status(mpgemm::launch_prefill_x32_tall(a, s));
+    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf)
         return hip_status(mpgemm::launch_prefill(a, s));
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
@@ -130,13 +137,13 @@ extern "C" {
 int mpgemm_layout_version(void) { return MPGEMM_LAYOUT_VERSION; }
 
 size_t mpgemm_packed_code_bytes(int K, int N) {
-    if (check_shape(0, N, K, 128) != MPGEMM_OK && check_shape(0, N, K, 64) != MPGEMM_OK) return 0;
-    return (size_t)K * (size_t)N / 2;
+    if (check_shape(0, N, K, 128) != MPGEMM_OK) return 0;
+    return (size_t)mpgemm::padded_k(K) * (size_t)mpgemm::padded_n(N) / 2;
 }
 
 size_t mpgemm_packed_meta_bytes(int K, int N, int group, int symmetric) {
     if (check_shape(0, N, K, group) != MPGEMM_OK) return 0;
-    const size_t cells = (size_t)(K / group) * (size_t)N;
+    const size_t cells = (size_t)packed_cells(K, N, group);
     return cells * 2 + (symmetric ? 0 : cells / 2);
 }
 
@@ -200,13 +207,13 @@ int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
 }
 
 size_t mpgemm_packed_code_bytes_w8(int K, int N) {
-    if (check_shape(0, N, K, 128) != MPGEMM_OK && check_shape(0, N, K, 64) != MPGEMM_OK) return 0;
-    return (size_t)K * (size_t)N;
+    if (check_shape(0, N, K, 128) != MPGEMM_OK) return 0;
+    return (size_t)mpgemm::padded_k(K) * (size_t)mpgemm::padded_n(N);
 }
 
 size_t mpgemm_packed_meta_bytes_w8(int K, int N, int group, int symmetric) {
     if (check_shape(0, N, K, group) != MPGEMM_OK) return 0;
-    const size_t cells = (size_t)(K / group) * (size_t)N;
+    const size_t cells = (size_t)packed_cells(K, N, group);
     return cells * 2 + (symmetric ? 0 : cells);
 }
 

@@ -340,6 +340,23 @@ __device__ __forceinline__ u32x2_t round4<kBF16>(const f32x4_t &v) {
     return r;
 }
 
+// Stores four consecutive outputs of one row at p, of which only the first `avail` exist
+// (a ragged last column block), rounded as round4: one 8-byte store when all four exist
+// and p is 8-byte aligned (rows of a width that is a multiple of 4), 2-byte stores
+// otherwise.
+template <int ACT>
+__device__ __forceinline__ void store4(uint16_t *p, int avail, const f32x4_t &v) {
+    const u32x2_t r = round4<ACT>(v);
+    if (avail >= 4 && ((uintptr_t)p & 7u) == 0) {
+        *reinterpret_cast<u32x2_t *>(p) = r;
+        return;
+    }
+    p[0] = (uint16_t)r[0];
+    if (avail > 1) p[1] = (uint16_t)(r[0] >> 16);
+    if (avail > 2) p[2] = (uint16_t)r[1];
+    if (avail > 3) p[3] = (uint16_t)(r[1] >> 16);
+}
+
 // Meta plane readers (layout v1): strip-major scales, then 4-bit zeros at the same index.
 __device__ __forceinline__ uint32_t read_zero(const uint8_t *zeros, size_t e) {
     const uint32_t b = zeros[e >> 1];

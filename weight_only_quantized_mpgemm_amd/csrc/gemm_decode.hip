@@ -55,7 +55,10 @@ template <int ACT, int MB, int S, bool SYM, int G, int D, int CODE>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    uint16_t *__restrict__ Y, f32x4_t *__restrict__ part, uint32_t *__restrict__ cnt) {
+    int Kx, int Ny, uint16_t *__restrict__ Y, f32x4_t *__restrict__ part,
+    uint32_t *__restrict__ cnt) {
+    // N, K: the padded matrix of the packed planes; Kx: activation row length (the user K,
+    // <= K); Ny: output row length (the user N, <= N).  Activations at k >= Kx read as zero.
     constexpr int GPT = kTileK / G;              // groups per 128-k tile (1 or 2)
     // 128-bit pieces per lane and strip per 128-deep step: one 16 x 128 tile of 4-bit codes,
     // two 16 x 64 tiles of 8-bit codes.
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const int strip0 = blockIdx.x * S;
 
     const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024 * WV));
-    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * Kx * 2));
     const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
     const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
 
@@ -101,7 +104,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     uint32_t xoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        xoff[mb] = ((uint32_t)(mb * 16 + (lane & 15)) * K + t_begin * kTileK + (lane >> 4) * 8) * 2u;
+        xoff[mb] = ((uint32_t)(mb * 16 + (lane & 15)) * Kx + t_begin * kTileK + (lane >> 4) * 8) * 2u;
+    // Ragged K: the lane's 8-element chunk of 32-deep step j of tile t_begin + i starts at
+    // k = k_lane + 128 i + 32 j; chunks at or past Kx take an offset outside the activation
+    // descriptor, which reads as zero.  Only tiles that reach past Kx take this path.
+    const int k_lane = t_begin * kTileK + (lane >> 4) * 8;
+    const bool ragged = Kx != K;
     const uint32_t sshift = (lane & 1) * 16;
     const uint32_t zshift = BITS == 4 ? (lane & 7) * 4 : (lane & 3) * 8;
     constexpr uint32_t zmask = (1u << BITS) - 1;
@@ -114,11 +122,22 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
 #pragma unroll
             for (int v = 0; v < WV; ++v)
                 sl.w[si][v] = buf_load_b128(wrs, woff[si], (i * WV + v) * 1024);
+        if (ragged && (t_begin + i + 1) * kTileK > Kx) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                const bool in = k_lane + i * kTileK + 32 * j < Kx;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                sl.x[j][mb] = buf_load_b128(xrs, xoff[mb], (i * kTileK + 32 * j) * 2);
+                for (int mb = 0; mb < MB; ++mb)
+                    sl.x[j][mb] = buf_load_b128(xrs, in ? xoff[mb] : 0x80000000u,
+                                                (i * kTileK + 32 * j) * 2);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    sl.x[j][mb] = buf_load_b128(xrs, xoff[mb], (i * kTileK + 32 * j) * 2);
+        }
 #pragma unroll
         for (int si = 0; si < S; ++si)
 #pragma unroll
@@ -188,9 +207,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const int col_lane = 4 * (lane >> 4);
     auto store_y = [&](int si, int mb, const f32x4_t &v) {
         const int m = mb * 16 + (lane & 15);
-        if (m < M && strip0 + si < strips)
-            *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + (strip0 + si) * 16 + col_lane) =
-                round4<ACT>(v);
+        const int n = (strip0 + si) * 16 + col_lane;
+        if (m < M && n < Ny) store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, v);
     };
     // Partial of block b (strip si = b / MB, row block mb = b % MB) of split q.
     // Partials of block b (strip si = b / MB, row block mb = b % MB) of split q travel with
@@ -319,7 +337,7 @@ template <int ACT, int MB, int S, bool SYM, int G, int CODE>
 void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
     constexpr int slot_regs = S * kCodeBits<CODE> + 16 * MB + 2 * S;
     constexpr int D = slot_regs <= 24 ? 4 : (slot_regs <= 40 ? 3 : 2);
-    const int strips = a.N >> 4;
+    const int strips = a.Np >> 4;
     const int wgs = (strips + S - 1) / S;
     const size_t lds = sp.nw > 1 ? (size_t)sp.nw * S * MB * 64 * sizeof(f32x4_t) : 0;
     uint32_t *cnt = nullptr;
@@ -329,12 +347,12 @@ void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
         part = reinterpret_cast<f32x4_t *>(static_cast<char *>(a.workspace) + kCounterBytes);
     }
     decode_kernel<ACT, MB, S, SYM, G, D, CODE><<<dim3(wgs, sp.p), dim3(sp.nw * 64), lds, stream>>>(
-        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y, part, cnt);
+        a.X, a.codes, a.scales, a.zeros, a.M, a.Np, a.Kp, a.K, a.N, a.Y, part, cnt);
 }
 
 template <int ACT, int MB, bool SYM, int G, int CODE>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const Split sp = pick_split(a.M, a.N >> 4, a.K >> 7, MB);
+    const Split sp = pick_split(a.M, a.Np >> 4, a.Kp >> 7, MB);
     if constexpr (MB == 1) {
         if (sp.s == 4) return launch_s<ACT, MB, 4, SYM, G, CODE>(a, sp, stream);
     }
@@ -380,7 +398,8 @@ void launch_code(const GemmArgs &a, int mblocks, hipStream_t stream) {
 }  // namespace
 
 size_t decode_workspace_bytes(int M, int N, int K, int mblocks) {
-    return split_workspace(pick_split(M, N >> 4, K >> 7, mblocks), N >> 4, mblocks);
+    const int strips = padded_n(N) >> 4;
+    return split_workspace(pick_split(M, strips, padded_k(K) >> 7, mblocks), strips, mblocks);
 }
 
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream) {

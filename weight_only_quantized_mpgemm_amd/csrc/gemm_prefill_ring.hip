@@ -124,7 +124,8 @@ template <int ACT, bool SYM, int G, int NST, int NWS>
 __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    uint16_t *__restrict__ Y) {
+    int Ny, uint16_t *__restrict__ Y) {
+    // N: the padded column count of the packed planes; Ny: output row length (the user N).
     typedef typename Dq<ACT>::type DqT;
     constexpr int GPT = kTileK / G;          // groups per 128-deep tile (1 or 2)
     // Loads each wave issues per weight tile: codes + scales (+ zeros), four strips.
@@ -343,19 +344,20 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     for (int si = 0; si < 4; ++si) {
         if (!valid[si]) continue;
         const int n = (strip0 + si) * 16 + 4 * (lane >> 4);
+        if (n >= Ny) continue;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const int m = m_blk + mb * 16 + (lane & 15);
-            if (m < M) *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + n) = round4<ACT>(acc[si][mb]);
+            if (m < M) store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, acc[si][mb]);
         }
     }
 }
 
 template <int ACT, bool SYM, int G>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const dim3 grid((a.N + kRBN - 1) / kRBN, (a.M + kRBM - 1) / kRBM);
+    const dim3 grid((a.Np + kRBN - 1) / kRBN, (a.M + kRBM - 1) / kRBM);
     prefill_ring_kernel<ACT, SYM, G, kRStages, kRWSets><<<grid, dim3(kRThreads), 0, stream>>>(
-        a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K, a.Y);
+        a.X, a.codes, a.scales, a.zeros, a.M, a.Np, a.K, a.N, a.Y);
 }
 
 template <int ACT>

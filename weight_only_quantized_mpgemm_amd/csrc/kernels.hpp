@@ -26,15 +26,21 @@ hipError_t launch_unpack_w8(const void *packed_codes, const void *packed_meta, i
                             int group, int symmetric, uint8_t *codes, uint16_t *scales,
                             uint8_t *zeros, hipStream_t stream);
 
+// Ragged shapes: the packed planes of a K x N weight matrix describe the matrix padded to
+// padded_k(K) x padded_n(N), whose padded weights dequantize to zero (include/mpgemm.h).
+__host__ __device__ inline int padded_k(int K) { return (K + 127) / 128 * 128; }
+__host__ __device__ inline int padded_n(int N) { return (N + 15) / 16 * 16; }
+
 // Arguments of one GEMM; planes as written by launch_pack (code kU4) or launch_pack_w8
 // (kU8, and the FP8 formats kE4M3 / kE5M2, which have no zero plane).
 struct GemmArgs {
-    const uint16_t *X;          // [M][K] activation bits
-    const uint32_t *codes;      // packed codes plane
+    const uint16_t *X;          // [M][K] activation bits (row stride K)
+    const uint32_t *codes;      // packed codes plane (Kp x Np matrix)
     const uint16_t *scales;     // meta plane: scales
     const uint8_t *zeros;       // meta plane: zeros (nullptr when symmetric)
-    uint16_t *Y;                // [M][N] output bits
-    int M, N, K, group;
+    uint16_t *Y;                // [M][N] output bits (row stride N)
+    int M, N, K, group;         // user shape (K % 8 == 0)
+    int Kp, Np;                 // padded shape of the packed planes
     int act;                    // Act
     int code;                   // Code: format of the packed codes
     void *workspace;            // decode split-K partials and counters (see decode kernel)
@@ -45,14 +51,20 @@ struct GemmArgs {
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
 // Workspace bytes launch_decode needs for this shape (0 when K is not split over
 // workgroups).  The counter region must be zero before the first call; calls leave it zero.
+// N, K: the user shape.
 size_t decode_workspace_bytes(int M, int N, int K, int mblocks);
 
 // Tiled large-M kernels (128 rows x 256 columns per workgroup): the LDS-ring kernel
 // (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
 hipError_t launch_prefill_ring(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
-// The 32x32x16 kernel with a 256 (m) x 128 (n) workgroup tile (needs K % 256 == 0).
+// The 32x32x16 kernel with a 256 (m) x 128 (n) workgroup tile.
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
+// Their instantiations per code format, one translation unit each (nb: column blocks per
+// wave, 2 for the 128 x 256 tile, 1 for 256 x 128).
+hipError_t launch_prefill_x32_u4(const GemmArgs &a, int nb, hipStream_t stream);
+hipError_t launch_prefill_x32_u8(const GemmArgs &a, int nb, hipStream_t stream);
+hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
 // Writes zeros to Y (the K == 0 case).

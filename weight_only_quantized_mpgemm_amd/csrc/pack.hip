@@ -23,76 +23,108 @@ __device__ __forceinline__ size_t code_word_index(int k0, int n, int K) {
     return tile * kTileWords + (size_t)lane * 4 + (kk >> 5);
 }
 
-// One thread per (8-row block, column): consecutive threads read consecutive columns.
-__global__ void pack_codes_kernel(const uint8_t *__restrict__ codes, int K, int N,
+// Ragged shapes ([TurboMind, Fig. 24]: a data matrix padded up to the hardware tile): the
+// planes hold the matrix padded to Kp x Np (Shape), in which every padded weight
+// dequantizes to zero.  Padded columns (n >= N) hold code 0, scale 0 and zero 0; padded
+// rows (k >= K) of real columns hold the element's zero point as their code (the group's
+// zero; 0 in groups past the user's ceil(K/g); 8 or 128 for symmetric codes).
+struct Shape {
+    int K, N;        // user matrix (K % 8 == 0)
+    int Kp, Np;      // padded matrix
+    int g, rows;     // group size, user group rows ceil(K/g)
+};
+
+// Code of padded-matrix element (k, n); `bits` = 4 or 8.
+__device__ __forceinline__ uint32_t padded_code(const uint8_t *codes, const uint8_t *zeros,
+                                                const Shape &sh, int k, int n, int bits) {
+    if (n >= sh.N) return 0u;
+    if (k < sh.K) return codes[(size_t)k * sh.N + n];
+    const int r = k / sh.g;
+    if (zeros == nullptr) return 1u << (bits - 1);
+    return r < sh.rows ? zeros[(size_t)r * sh.N + n] : 0u;
+}
+
+// One thread per (8-row block, column) of the padded matrix: consecutive threads read
+// consecutive columns.
+__global__ void pack_codes_kernel(const uint8_t *__restrict__ codes,
+                                  const uint8_t *__restrict__ zeros, Shape sh,
                                   uint32_t *__restrict__ out) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)(K >> 3) * N;
+    const size_t total = (size_t)(sh.Kp >> 3) * sh.Np;
     if (i >= total) return;
-    const int n = (int)(i % N);
-    const int k0 = (int)(i / N) * 8;
+    const int n = (int)(i % sh.Np);
+    const int k0 = (int)(i / sh.Np) * 8;
     uint32_t w = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t q = codes[(size_t)(k0 + e) * N + n] & 0xFu;
-        w |= q << (4 * nibble_pos(e));
-    }
-    out[code_word_index(k0, n, K)] = w;
+    for (int e = 0; e < 8; ++e)
+        w |= (padded_code(codes, zeros, sh, k0 + e, n, 4) & 0xFu) << (4 * nibble_pos(e));
+    out[code_word_index(k0, n, sh.Kp)] = w;
 }
 
-__global__ void unpack_codes_kernel(const uint32_t *__restrict__ in, int K, int N,
+// One thread per (8-row block, column) of the user matrix.
+__global__ void unpack_codes_kernel(const uint32_t *__restrict__ in, Shape sh,
                                     uint8_t *__restrict__ codes) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)(K >> 3) * N;
+    const size_t total = (size_t)(sh.K >> 3) * sh.N;
     if (i >= total) return;
-    const int n = (int)(i % N);
-    const int k0 = (int)(i / N) * 8;
-    const uint32_t w = in[code_word_index(k0, n, K)];
+    const int n = (int)(i % sh.N);
+    const int k0 = (int)(i / sh.N) * 8;
+    const uint32_t w = in[code_word_index(k0, n, sh.Kp)];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        codes[(size_t)(k0 + e) * N + n] = (uint8_t)((w >> (4 * nibble_pos(e))) & 0xFu);
+        codes[(size_t)(k0 + e) * sh.N + n] = (uint8_t)((w >> (4 * nibble_pos(e))) & 0xFu);
     }
 }
 
-// Meta element index e <-> (group r, column n): e = (n/16)*G*16 + r*16 + n%16, G = K/g.
+// Meta element index e <-> (group r, column n) of the padded matrix:
+// e = (n/16)*G*16 + r*16 + n%16, G = Kp/g.
 __device__ __forceinline__ void meta_coords(size_t e, int groups, int *r, int *n) {
     const size_t row = e >> 4;                   // (strip, group) pair
     *r = (int)(row % groups);
     *n = (int)(row / groups) * 16 + (int)(e & 15);
 }
 
-// One thread per output byte of the meta plane: scale bytes first, then zero bytes.
+__device__ __forceinline__ bool user_cell(const Shape &sh, int r, int n) {
+    return r < sh.rows && n < sh.N;
+}
+
+// One thread per element of the padded meta plane: scale, and (4-bit) the zero nibble
+// pair of even elements.
 __global__ void pack_meta_kernel(const uint16_t *__restrict__ scales,
-                                 const uint8_t *__restrict__ zeros, int groups, int N,
+                                 const uint8_t *__restrict__ zeros, Shape sh,
                                  uint16_t *__restrict__ out_scales,
                                  uint8_t *__restrict__ out_zeros) {
+    const int groups = sh.Kp / sh.g;
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t count = (size_t)groups * N;
+    const size_t count = (size_t)groups * sh.Np;
     if (e >= count) return;
     int r, n;
     meta_coords(e, groups, &r, &n);
-    out_scales[e] = scales[(size_t)r * N + n];
+    const bool in = user_cell(sh, r, n);
+    out_scales[e] = in ? scales[(size_t)r * sh.N + n] : (uint16_t)0;
     if (zeros != nullptr && (e & 1) == 0) {
         int r1, n1;
         meta_coords(e + 1, groups, &r1, &n1);
-        const uint32_t z0 = zeros[(size_t)r * N + n] & 0xFu;
-        const uint32_t z1 = zeros[(size_t)r1 * N + n1] & 0xFu;
+        const uint32_t z0 = in ? zeros[(size_t)r * sh.N + n] & 0xFu : 0u;
+        const uint32_t z1 = user_cell(sh, r1, n1) ? zeros[(size_t)r1 * sh.N + n1] & 0xFu : 0u;
         out_zeros[e >> 1] = (uint8_t)(z0 | (z1 << 4));
     }
 }
 
 __global__ void unpack_meta_kernel(const uint16_t *__restrict__ in_scales,
-                                   const uint8_t *__restrict__ in_zeros, int groups, int N,
+                                   const uint8_t *__restrict__ in_zeros, Shape sh,
                                    uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros) {
+    const int groups = sh.Kp / sh.g;
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t count = (size_t)groups * N;
+    const size_t count = (size_t)groups * sh.Np;
     if (e >= count) return;
     int r, n;
     meta_coords(e, groups, &r, &n);
-    scales[(size_t)r * N + n] = in_scales[e];
+    if (!user_cell(sh, r, n)) return;
+    scales[(size_t)r * sh.N + n] = in_scales[e];
     if (in_zeros != nullptr) {
         const uint32_t b = in_zeros[e >> 1];
-        zeros[(size_t)r * N + n] = (uint8_t)((e & 1) ? (b >> 4) : (b & 0xFu));
+        zeros[(size_t)r * sh.N + n] = (uint8_t)((e & 1) ? (b >> 4) : (b & 0xFu));
     }
 }
 
@@ -106,56 +138,62 @@ __device__ __forceinline__ size_t code8_run_offset(int k0, int n, int K) {
     return tile * 1024 + (size_t)lane * 16 + (size_t)(kk >> 5) * 8;
 }
 
-// One thread per (8-row block, column), as for 4-bit codes.
-__global__ void pack_codes8_kernel(const uint8_t *__restrict__ codes, int K, int N,
+// One thread per (8-row block, column) of the padded matrix, as for 4-bit codes.
+__global__ void pack_codes8_kernel(const uint8_t *__restrict__ codes,
+                                   const uint8_t *__restrict__ zeros, Shape sh,
                                    uint8_t *__restrict__ out) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)(K >> 3) * N;
+    const size_t total = (size_t)(sh.Kp >> 3) * sh.Np;
     if (i >= total) return;
-    const int n = (int)(i % N);
-    const int k0 = (int)(i / N) * 8;
+    const int n = (int)(i % sh.Np);
+    const int k0 = (int)(i / sh.Np) * 8;
     u32x2_t run = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        run[e >> 2] |= (uint32_t)codes[(size_t)(k0 + e) * N + n] << (8 * (e & 3));
-    *reinterpret_cast<u32x2_t *>(out + code8_run_offset(k0, n, K)) = run;
+        run[e >> 2] |= (padded_code(codes, zeros, sh, k0 + e, n, 8) & 0xFFu) << (8 * (e & 3));
+    *reinterpret_cast<u32x2_t *>(out + code8_run_offset(k0, n, sh.Kp)) = run;
 }
 
-__global__ void unpack_codes8_kernel(const uint8_t *__restrict__ in, int K, int N,
+__global__ void unpack_codes8_kernel(const uint8_t *__restrict__ in, Shape sh,
                                      uint8_t *__restrict__ codes) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)(K >> 3) * N;
+    const size_t total = (size_t)(sh.K >> 3) * sh.N;
     if (i >= total) return;
-    const int n = (int)(i % N);
-    const int k0 = (int)(i / N) * 8;
-    const u32x2_t run = *reinterpret_cast<const u32x2_t *>(in + code8_run_offset(k0, n, K));
+    const int n = (int)(i % sh.N);
+    const int k0 = (int)(i / sh.N) * 8;
+    const u32x2_t run =
+        *reinterpret_cast<const u32x2_t *>(in + code8_run_offset(k0, n, sh.Kp));
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        codes[(size_t)(k0 + e) * N + n] = (uint8_t)(run[e >> 2] >> (8 * (e & 3)));
+        codes[(size_t)(k0 + e) * sh.N + n] = (uint8_t)(run[e >> 2] >> (8 * (e & 3)));
 }
 
 // Meta for 8-bit codes: scales as above, one zero byte per element.
 __global__ void pack_meta8_kernel(const uint16_t *__restrict__ scales,
-                                  const uint8_t *__restrict__ zeros, int groups, int N,
+                                  const uint8_t *__restrict__ zeros, Shape sh,
                                   uint16_t *__restrict__ out_scales,
                                   uint8_t *__restrict__ out_zeros) {
+    const int groups = sh.Kp / sh.g;
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (size_t)groups * N) return;
+    if (e >= (size_t)groups * sh.Np) return;
     int r, n;
     meta_coords(e, groups, &r, &n);
-    out_scales[e] = scales[(size_t)r * N + n];
-    if (zeros != nullptr) out_zeros[e] = zeros[(size_t)r * N + n];
+    const bool in = user_cell(sh, r, n);
+    out_scales[e] = in ? scales[(size_t)r * sh.N + n] : (uint16_t)0;
+    if (zeros != nullptr) out_zeros[e] = in ? zeros[(size_t)r * sh.N + n] : (uint8_t)0;
 }
 
 __global__ void unpack_meta8_kernel(const uint16_t *__restrict__ in_scales,
-                                    const uint8_t *__restrict__ in_zeros, int groups, int N,
+                                    const uint8_t *__restrict__ in_zeros, Shape sh,
                                     uint16_t *__restrict__ scales, uint8_t *__restrict__ zeros) {
+    const int groups = sh.Kp / sh.g;
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= (size_t)groups * N) return;
+    if (e >= (size_t)groups * sh.Np) return;
     int r, n;
     meta_coords(e, groups, &r, &n);
-    scales[(size_t)r * N + n] = in_scales[e];
-    if (in_zeros != nullptr) zeros[(size_t)r * N + n] = in_zeros[e];
+    if (!user_cell(sh, r, n)) return;
+    scales[(size_t)r * sh.N + n] = in_scales[e];
+    if (in_zeros != nullptr) zeros[(size_t)r * sh.N + n] = in_zeros[e];
 }
 
 unsigned blocks_for(size_t total, unsigned threads) {
@@ -164,84 +202,98 @@ unsigned blocks_for(size_t total, unsigned threads) {
 
 }  // namespace
 
+namespace {
+
+Shape shape_of(int K, int N, int group) {
+    Shape sh;
+    sh.K = K;
+    sh.N = N;
+    sh.Kp = padded_k(K);
+    sh.Np = padded_n(N);
+    sh.g = group;
+    sh.rows = (K + group - 1) / group;
+    return sh;
+}
+
+// Launches the code and meta kernels of one direction over `code_items` / `meta_items`.
+template <typename CodeFn, typename MetaFn>
+hipError_t launch_two(size_t code_items, size_t meta_items, CodeFn code, MetaFn meta) {
+    const unsigned threads = 256;
+    if (code_items) code(blocks_for(code_items, threads), threads);
+    if (meta_items) meta(blocks_for(meta_items, threads), threads);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_pack(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                        int K, int N, int group, void *packed_codes, void *packed_meta,
                        hipStream_t stream) {
-    const unsigned threads = 256;
-    const size_t words = (size_t)(K >> 3) * N;
-    const int groups = K / group;
-    const size_t metas = (size_t)groups * N;
+    const Shape sh = shape_of(K, N, group);
+    const size_t metas = (size_t)(sh.Kp / group) * sh.Np;
     uint16_t *ms = (uint16_t *)packed_meta;
     uint8_t *mz = zeros ? (uint8_t *)packed_meta + metas * 2 : nullptr;
-    if (words) {
-        pack_codes_kernel<<<blocks_for(words, threads), threads, 0, stream>>>(
-            codes, K, N, (uint32_t *)packed_codes);
-    }
-    if (metas) {
-        pack_meta_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(scales, zeros,
-                                                                             groups, N, ms, mz);
-    }
-    return hipGetLastError();
+    return launch_two(
+        (size_t)(sh.Kp >> 3) * sh.Np, metas,
+        [&](unsigned b, unsigned t) {
+            pack_codes_kernel<<<b, t, 0, stream>>>(codes, zeros, sh, (uint32_t *)packed_codes);
+        },
+        [&](unsigned b, unsigned t) {
+            pack_meta_kernel<<<b, t, 0, stream>>>(scales, zeros, sh, ms, mz);
+        });
 }
 
 hipError_t launch_unpack(const void *packed_codes, const void *packed_meta, int K, int N,
                          int group, int symmetric, uint8_t *codes, uint16_t *scales,
                          uint8_t *zeros, hipStream_t stream) {
-    const unsigned threads = 256;
-    const size_t words = (size_t)(K >> 3) * N;
-    const int groups = K / group;
-    const size_t metas = (size_t)groups * N;
+    const Shape sh = shape_of(K, N, group);
+    const size_t metas = (size_t)(sh.Kp / group) * sh.Np;
     const uint16_t *ms = (const uint16_t *)packed_meta;
     const uint8_t *mz = symmetric ? nullptr : (const uint8_t *)packed_meta + metas * 2;
-    if (words) {
-        unpack_codes_kernel<<<blocks_for(words, threads), threads, 0, stream>>>(
-            (const uint32_t *)packed_codes, K, N, codes);
-    }
-    if (metas) {
-        unpack_meta_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(
-            ms, mz, groups, N, scales, symmetric ? nullptr : zeros);
-    }
-    return hipGetLastError();
+    return launch_two(
+        (size_t)(K >> 3) * N, metas,
+        [&](unsigned b, unsigned t) {
+            unpack_codes_kernel<<<b, t, 0, stream>>>((const uint32_t *)packed_codes, sh, codes);
+        },
+        [&](unsigned b, unsigned t) {
+            unpack_meta_kernel<<<b, t, 0, stream>>>(ms, mz, sh, scales,
+                                                    symmetric ? nullptr : zeros);
+        });
 }
 
 hipError_t launch_pack_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
                           int K, int N, int group, void *packed_codes, void *packed_meta,
                           hipStream_t stream) {
-    const unsigned threads = 256;
-    const size_t runs = (size_t)(K >> 3) * N;
-    const int groups = K / group;
-    const size_t metas = (size_t)groups * N;
+    const Shape sh = shape_of(K, N, group);
+    const size_t metas = (size_t)(sh.Kp / group) * sh.Np;
     uint16_t *ms = (uint16_t *)packed_meta;
     uint8_t *mz = zeros ? (uint8_t *)packed_meta + metas * 2 : nullptr;
-    if (runs) {
-        pack_codes8_kernel<<<blocks_for(runs, threads), threads, 0, stream>>>(
-            codes, K, N, (uint8_t *)packed_codes);
-    }
-    if (metas) {
-        pack_meta8_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(scales, zeros,
-                                                                              groups, N, ms, mz);
-    }
-    return hipGetLastError();
+    return launch_two(
+        (size_t)(sh.Kp >> 3) * sh.Np, metas,
+        [&](unsigned b, unsigned t) {
+            pack_codes8_kernel<<<b, t, 0, stream>>>(codes, zeros, sh, (uint8_t *)packed_codes);
+        },
+        [&](unsigned b, unsigned t) {
+            pack_meta8_kernel<<<b, t, 0, stream>>>(scales, zeros, sh, ms, mz);
+        });
 }
 
 hipError_t launch_unpack_w8(const void *packed_codes, const void *packed_meta, int K, int N,
                             int group, int symmetric, uint8_t *codes, uint16_t *scales,
                             uint8_t *zeros, hipStream_t stream) {
-    const unsigned threads = 256;
-    const size_t runs = (size_t)(K >> 3) * N;
-    const int groups = K / group;
-    const size_t metas = (size_t)groups * N;
+    const Shape sh = shape_of(K, N, group);
+    const size_t metas = (size_t)(sh.Kp / group) * sh.Np;
     const uint16_t *ms = (const uint16_t *)packed_meta;
     const uint8_t *mz = symmetric ? nullptr : (const uint8_t *)packed_meta + metas * 2;
-    if (runs) {
-        unpack_codes8_kernel<<<blocks_for(runs, threads), threads, 0, stream>>>(
-            (const uint8_t *)packed_codes, K, N, codes);
-    }
-    if (metas) {
-        unpack_meta8_kernel<<<blocks_for(metas, threads), threads, 0, stream>>>(
-            ms, mz, groups, N, scales, symmetric ? nullptr : zeros);
-    }
-    return hipGetLastError();
+    return launch_two(
+        (size_t)(K >> 3) * N, metas,
+        [&](unsigned b, unsigned t) {
+            unpack_codes8_kernel<<<b, t, 0, stream>>>((const uint8_t *)packed_codes, sh, codes);
+        },
+        [&](unsigned b, unsigned t) {
+            unpack_meta8_kernel<<<b, t, 0, stream>>>(ms, mz, sh, scales,
+                                                     symmetric ? nullptr : zeros);
+        });
 }
 
 }  // namespace mpgemm

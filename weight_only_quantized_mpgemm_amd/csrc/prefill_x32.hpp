@@ -13,7 +13,7 @@
 // dequantization alone needs (13 vector operations per 8 weights, each weight feeding
 // 128 rows).
 //
-// Design (K % 256 == 0), in two tile shapes of equal work per wave (NB column blocks x
+// Design (K % 128 == 0), in two tile shapes of equal work per wave (NB column blocks x
 // MB = 8 / NB row blocks of 32 x 32):
 //   - NB = 2: workgroup tile 128 (m) x 256 (n), four waves side by side along n, each
 //     owning a 128 x 64 block = 2 (n) x 4 (m) blocks;
@@ -43,6 +43,11 @@
 //     is done first, since the next step's first MFMA needs it.  The dequantization is
 //     inline asm too, so the compiler neither reorders it nor pads it with wait states
 //     meant for the MFMAs.
+//
+// This header holds the kernel template and its launch helpers; the gemm_prefill_x32*.hip
+// translation units instantiate it per code format (they compile in parallel).
+#pragma once
+
 #include <type_traits>
 #include <utility>
 
@@ -318,11 +323,17 @@ __device__ __forceinline__ void tile_of(int b, int tm, int tn, int &mt, int &nt)
     nt = r / gm;
 }
 
-template <int ACT, bool SYM, int G, int NWS, int NB, int CODE>
+// RAG: Kx < K; activation chunks at k >= Kx are loaded as zeros.
+template <int ACT, bool SYM, int G, int NWS, int NB, int CODE, bool RAG>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    uint16_t *__restrict__ Y) {
+    int Kw, int Kx, int Ny, uint16_t *__restrict__ Y) {
+    // N: the padded column count of the packed planes; Kw: their padded K (a multiple of
+    // 128); K: the loop length, Kw rounded up to a multiple of 256 (the stage loop runs
+    // blocks of four 64-deep stages; a 128-deep tile past Kw re-reads the last weight tile
+    // against activations that read as zero, adding exact zeros); Kx: activation row length
+    // (the user K); Ny: output row length (the user N).
     typedef typename Dq<ACT>::type DqT;       // the same constants type for every code format
     typedef typename DqOpsSel<ACT, CODE>::type Ops;
     typedef DqFor<ACT, CODE> DqB;
@@ -346,13 +357,13 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     int mt, nt;
     tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
     const int m_blk = mt * BM;
-    const int KT = K >> 7;                   // 128-deep weight tiles
+    const int KT = Kw >> 7;                  // 128-deep weight tiles in the packed planes
     const int S = K >> 6;                    // 64-deep stages (a multiple of 4)
-    const int groups = K / G;
+    const int groups = Kw / G;
     const int strips = N >> 4;
     const int strip0 = nt * (BN / 16) + wave * 2 * NB;
 
-    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * Kx * 2));
     const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024 * WV));
     const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
     const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
@@ -369,8 +380,10 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     for (int i = 0; i < MB; ++i) {
         const int r = 8 * (wave * MB + i) + (lane >> 3);
         const uint32_t row = (uint32_t)min(m_blk + r, M);
-        xoff[i] = (row * K + (((lane & 7) ^ (lane >> 3)) * 8)) * 2u;
+        xoff[i] = (row * Kx + (((lane & 7) ^ (lane >> 3)) * 8)) * 2u;
     }
+    // Ragged K: first k of the lane's chunk within a stage.
+    const int k_chunk = ((lane & 7) ^ (lane >> 3)) * 8;
     // Weight slots: column block nb (strips strip0 + 2nb, +1), k half u.  Strips past N
     // read the last real strip; their results are never stored.
     const int my_strip_in_pair = (lane & 31) >> 4;
@@ -415,10 +428,13 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 
     // Block i (of MB) of this wave's share of stage st's DMA.
     auto dma_part = [&](int st, auto buf, int i) __attribute__((always_inline)) {
-        const uint32_t soff_k = (uint32_t)min(st, S - 1) * 128u;
+        const int sc = min(st, S - 1);
+        const uint32_t soff_k = (uint32_t)sc * 128u;
+        uint32_t off = xoff[i];
+        if constexpr (RAG) off = sc * 64 + k_chunk < Kx ? off : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * MB + i) * 64],
-            16, xoff[i], soff_k, 0, 0);
+            16, off, soff_k, 0, 0);
     };
     auto dma = [&](int st, auto buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -635,65 +651,57 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int n = n_wave + nb * 32 + 8 * q + 4 * (lane >> 5);
-            if (n >= N) continue;
+            if (n >= Ny) continue;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int m = m_blk + mb * 32 + (lane & 31);
                 if (m < M) {
                     const f32x4_t v = {acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
                                        acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]};
-                    *reinterpret_cast<u32x2_t *>(Y + (size_t)m * N + n) = round4<ACT>(v);
+                    store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, v);
                 }
             }
         }
 }
 
-template <int ACT, bool SYM, int G, int NB, int CODE>
+// Stage-loop length of the kernel: the packed K rounded up to a multiple of 256.
+inline int x32_loop_k(int Kp) { return (Kp + 255) / 256 * 256; }
+
+template <int ACT, bool SYM, int G, int NB, int CODE, bool RAG>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const dim3 grid(((a.N + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB)));
-    prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE>
-        <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.N, a.K,
-                                               a.Y);
+    const dim3 grid(((a.Np + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB)));
+    prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG>
+        <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
+                                               x32_loop_k(a.Kp), a.Kp, a.K, a.N, a.Y);
 }
 
-template <int ACT, int NB, int CODE>
+template <int ACT, int NB, int CODE, bool RAG>
 void launch_act(const GemmArgs &a, hipStream_t stream) {
     if constexpr (kCodeFp8<CODE>) {         // FP8 codes carry no zero point
-        a.group == 128 ? launch_one<ACT, true, 128, NB, CODE>(a, stream)
-                       : launch_one<ACT, true, 64, NB, CODE>(a, stream);
+        a.group == 128 ? launch_one<ACT, true, 128, NB, CODE, RAG>(a, stream)
+                       : launch_one<ACT, true, 64, NB, CODE, RAG>(a, stream);
     } else {
         const bool sym = a.zeros == nullptr;
         if (a.group == 128) {
-            sym ? launch_one<ACT, true, 128, NB, CODE>(a, stream)
-                : launch_one<ACT, false, 128, NB, CODE>(a, stream);
+            sym ? launch_one<ACT, true, 128, NB, CODE, RAG>(a, stream)
+                : launch_one<ACT, false, 128, NB, CODE, RAG>(a, stream);
         } else {
-            sym ? launch_one<ACT, true, 64, NB, CODE>(a, stream)
-                : launch_one<ACT, false, 64, NB, CODE>(a, stream);
+            sym ? launch_one<ACT, true, 64, NB, CODE, RAG>(a, stream)
+                : launch_one<ACT, false, 64, NB, CODE, RAG>(a, stream);
         }
     }
 }
 
+// Every variant of code format CODE with NB column blocks per wave.
 template <int NB, int CODE>
-void launch_code(const GemmArgs &a, hipStream_t stream) {
-    a.act == kBF16 ? launch_act<kBF16, NB, CODE>(a, stream) : launch_act<kF16, NB, CODE>(a, stream);
-}
-
-template <int NB>
-hipError_t launch_nb(const GemmArgs &a, hipStream_t stream) {
-    switch (a.code) {
-        case kU8: launch_code<NB, kU8>(a, stream); break;
-        case kE4M3: launch_code<NB, kE4M3>(a, stream); break;
-        case kE5M2: launch_code<NB, kE5M2>(a, stream); break;
-        default: launch_code<NB, kU4>(a, stream); break;
-    }
-    return hipGetLastError();
+void launch_x32(const GemmArgs &a, hipStream_t stream) {
+    const bool rag = a.K != x32_loop_k(a.Kp);
+    if (a.act == kBF16)
+        rag ? launch_act<kBF16, NB, CODE, true>(a, stream) : launch_act<kBF16, NB, CODE, false>(a, stream);
+    else
+        rag ? launch_act<kF16, NB, CODE, true>(a, stream) : launch_act<kF16, NB, CODE, false>(a, stream);
 }
 
 }  // namespace
-
-hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) { return launch_nb<2>(a, stream); }
-hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream) {
-    return launch_nb<1>(a, stream);
-}
 
 }  // namespace mpgemm
