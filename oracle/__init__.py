@@ -94,6 +94,14 @@ def _load():
     lib.oracle_padded_k.restype = i
     lib.oracle_padded_n.argtypes = [i]
     lib.oracle_padded_n.restype = i
+    lib.oracle_dequant_lowbit.argtypes = [i, u8p, u16p, u8p, i, i, i, i, u16p]
+    lib.oracle_dequant_lowbit.restype = None
+    lib.oracle_packed_code_bytes_lowbit.argtypes = [i, i, i]
+    lib.oracle_packed_code_bytes_lowbit.restype = ctypes.c_size_t
+    lib.oracle_pack_lowbit.argtypes = [i, u8p, u16p, u8p, i, i, i, u8p, u8p]
+    lib.oracle_pack_lowbit.restype = None
+    lib.oracle_unpack_lowbit.argtypes = [i, u8p, u8p, i, i, i, i, u8p, u16p, u8p]
+    lib.oracle_unpack_lowbit.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -335,6 +343,76 @@ def dequant_fp8(codes: np.ndarray, scales_bits: np.ndarray, group: int, fmt: str
 def wfp8a16(x_bits, codes, scales_bits, group, fmt="e4m3", dtype="f16", threads=1):
     """The whole FP8-weight path: dequantize, then the GEMM."""
     return gemm(x_bits, dequant_fp8(codes, scales_bits, group, fmt, dtype), dtype, threads)
+
+
+# ---------------------------------------------------- 2-bit and 3-bit weights -------
+
+def dequant_lowbit(bits: int, codes: np.ndarray, scales_bits: np.ndarray,
+                   zeros: np.ndarray | None, group: int, dtype: str = "f16") -> np.ndarray:
+    """w[k][n] = round_act((q - z) * s) with b-bit q, z (z = 2^(b-1) when zeros is None)."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert bits in (2, 3) and scales_bits.shape == (-(-K // group), N)
+    zp = None
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        assert zeros.shape == scales_bits.shape
+        zp = _ptr(zeros, ctypes.c_uint8)
+    w = np.empty((K, N), dtype=np.uint16)
+    lib.oracle_dequant_lowbit(bits, _ptr(codes, ctypes.c_uint8),
+                              _ptr(scales_bits, ctypes.c_uint16), zp, K, N, group,
+                              _dtype_code(dtype), _ptr(w, ctypes.c_uint16))
+    return w
+
+
+def wlowbit_a16(bits, x_bits, codes, scales_bits, zeros, group, dtype="f16", threads=1):
+    """The whole b-bit path: dequantize, then the GEMM."""
+    return gemm(x_bits, dequant_lowbit(bits, codes, scales_bits, zeros, group, dtype), dtype,
+                threads)
+
+
+def packed_code_bytes_lowbit(bits: int, K: int, N: int) -> int:
+    return int(_load().oracle_packed_code_bytes_lowbit(bits, K, N))
+
+
+def pack_lowbit(bits: int, codes: np.ndarray, scales_bits: np.ndarray,
+                zeros: np.ndarray | None, group: int):
+    """Sub-4-bit layout packing; returns (packed_codes uint8, packed_meta uint8)."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    K, N = codes.shape
+    rows = -(-K // group)
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    assert bits in (2, 3) and scales_bits.shape == (rows, N)
+    zp = None
+    if zeros is not None:
+        zeros = np.ascontiguousarray(zeros, dtype=np.uint8)
+        assert zeros.shape == (rows, N)
+        zp = _ptr(zeros, ctypes.c_uint8)
+    pc = np.empty(packed_code_bytes_lowbit(bits, K, N), dtype=np.uint8)
+    pm = np.empty(packed_meta_bytes(K, N, group, zeros is None), dtype=np.uint8)
+    lib.oracle_pack_lowbit(bits, _ptr(codes, ctypes.c_uint8), _ptr(scales_bits, ctypes.c_uint16),
+                           zp, K, N, group, _ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8))
+    return pc, pm
+
+
+def unpack_lowbit(bits: int, packed_codes: np.ndarray, packed_meta: np.ndarray, K: int, N: int,
+                  group: int, symmetric: bool):
+    """Inverse of pack_lowbit; returns (codes, scales_bits, zeros or None)."""
+    lib = _load()
+    pc = np.ascontiguousarray(packed_codes, dtype=np.uint8)
+    pm = np.ascontiguousarray(packed_meta, dtype=np.uint8)
+    rows = -(-K // group)
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty((rows, N), dtype=np.uint16)
+    zeros = None if symmetric else np.empty((rows, N), dtype=np.uint8)
+    lib.oracle_unpack_lowbit(bits, _ptr(pc, ctypes.c_uint8), _ptr(pm, ctypes.c_uint8), K, N,
+                             group, int(bool(symmetric)), _ptr(codes, ctypes.c_uint8),
+                             _ptr(scales, ctypes.c_uint16),
+                             None if zeros is None else _ptr(zeros, ctypes.c_uint8))
+    return codes, scales, zeros
 
 
 def max_threads() -> int:

@@ -25,7 +25,8 @@
  *
  * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py; the
  * 8-bit functions by tests/test_oracle_w8.py, the FP8 ones by tests/test_oracle_fp8.py,
- * packing of ragged shapes by tests/test_oracle_ragged.py).
+ * packing of ragged shapes by tests/test_oracle_ragged.py, the 2-bit and 3-bit functions by
+ * tests/test_oracle_lowbit.py).
  */
 #include <math.h>
 #include <stddef.h>
@@ -425,6 +426,139 @@ void oracle_dequant_fp8(const uint8_t *codes, const uint16_t *scales, int K, int
             w[(size_t)k * N + n] = f64_to_act(v * scale, dtype);
         }
     }
+}
+
+/* ------------------------------------------ 2-bit and 3-bit weights (sub-4-bit) --- */
+
+/*
+ * "Progressive Mixed-Precision Decoding for Efficient LLM Inference" (arXiv 2410.13461),
+ * abstract: 2/3-bit weights relieve the memory-boundedness of decoding; here with the
+ * [TurboMind] pipeline.  The same group form with b-bit codes (b = 2 or 3):
+ *   w = round_act((q - z) * s),  q, z in 0..2^b - 1,  z = 2^(b-1) for symmetric codes.
+ *   codes uint8 [K][N] (low b bits used); scales fp16 [ceil(K/g)][N]; zeros uint8 of the
+ *   same shape (low b bits used) or NULL.
+ */
+void oracle_dequant_lowbit(int bits, const uint8_t *codes, const uint16_t *scales,
+                           const uint8_t *zeros, int K, int N, int g, int dtype, uint16_t *w) {
+    const int cmask = (1 << bits) - 1;
+    for (int k = 0; k < K; ++k) {
+        int gr = k / g;
+        for (int n = 0; n < N; ++n) {
+            int qb = codes[(size_t)k * N + n] & cmask;
+            int zb = zeros ? (zeros[(size_t)gr * N + n] & cmask) : (1 << (bits - 1));
+            double sb = oracle_f16_to_f64(scales[(size_t)gr * N + n]);
+            w[(size_t)k * N + n] = f64_to_act((double)(qb - zb) * sb, dtype);
+        }
+    }
+}
+
+/*
+ * Packed sub-4-bit layout (restated from its specification in include/mpgemm.h).  Tiles of
+ * 16 columns x 128 rows of k over the padded matrix (Kp x Np as for 4-bit codes), 4*b
+ * bytes per lane and 256*b bytes per tile; tile T = (n/16)*(Kp/128) + k/128.  With
+ * kk = k%128 and nn = n%16: lane L = nn + 16*((kk%32)/8), step t = kk/32, element
+ * i = kk%8; the lane's b little-endian 32-bit words start at byte T*256*b + L*4*b.  The
+ * element belongs to pair register r = 4t + i/2, in its low 16-bit half for even i and its
+ * high half for odd i (half offset h = 16*(i%2)).
+ *   b = 2: word r/8; field of 2 bits at bit h + 2*((r%8)%4) + 8*((r%8)/4).
+ *   b = 3: r < 15: word r/5, field of 3 bits at bit h + 3*(r%5).  r = 15: bit c (c = 0..2)
+ *          of the code sits in word c at bit h + 15.
+ * Meta plane exactly as for 4-bit codes (fp16 scales, then 4-bit zeros), padding as there
+ * (padded rows of real columns carry the zero point, 2 or 4 when symmetric).
+ */
+size_t oracle_packed_code_bytes_lowbit(int bits, int K, int N) {
+    return (size_t)oracle_padded_k(K) * oracle_padded_n(N) * bits / 8;
+}
+
+/* Sets code q of padded element (k, n) in the plane (which starts zeroed). */
+static void put_lowbit(uint8_t *plane, int bits, int k, int n, int Kp, uint32_t q) {
+    size_t T = (size_t)(n / 16) * (size_t)(Kp / 128) + (size_t)(k / 128);
+    int kk = k % 128, L = n % 16 + 16 * ((kk % 32) / 8), t = kk / 32, i = kk % 8;
+    int r = 4 * t + i / 2, h = 16 * (i % 2);
+    uint8_t *lane_words = plane + T * 256 * bits + (size_t)L * 4 * bits;
+    for (int c = 0; c < bits; ++c) {
+        int word, bit;
+        if (bits == 2) {
+            word = r / 8;
+            bit = h + 2 * ((r % 8) % 4) + 8 * ((r % 8) / 4) + c;
+        } else if (r < 15) {
+            word = r / 5;
+            bit = h + 3 * (r % 5) + c;
+        } else {
+            word = c;
+            bit = h + 15;
+        }
+        if ((q >> c) & 1u) lane_words[4 * word + bit / 8] |= (uint8_t)(1u << (bit % 8));
+    }
+}
+
+static uint32_t get_lowbit(const uint8_t *plane, int bits, int k, int n, int Kp) {
+    size_t T = (size_t)(n / 16) * (size_t)(Kp / 128) + (size_t)(k / 128);
+    int kk = k % 128, L = n % 16 + 16 * ((kk % 32) / 8), t = kk / 32, i = kk % 8;
+    int r = 4 * t + i / 2, h = 16 * (i % 2);
+    const uint8_t *lane_words = plane + T * 256 * bits + (size_t)L * 4 * bits;
+    uint32_t q = 0;
+    for (int c = 0; c < bits; ++c) {
+        int word, bit;
+        if (bits == 2) {
+            word = r / 8;
+            bit = h + 2 * ((r % 8) % 4) + 8 * ((r % 8) / 4) + c;
+        } else if (r < 15) {
+            word = r / 5;
+            bit = h + 3 * (r % 5) + c;
+        } else {
+            word = c;
+            bit = h + 15;
+        }
+        q |= (uint32_t)((lane_words[4 * word + bit / 8] >> (bit % 8)) & 1u) << c;
+    }
+    return q;
+}
+
+void oracle_pack_lowbit(int bits, const uint8_t *codes, const uint16_t *scales,
+                        const uint8_t *zeros, int K, int N, int g, uint8_t *packed_codes,
+                        uint8_t *packed_meta) {
+    const int Kp = oracle_padded_k(K), Np = oracle_padded_n(N), rows = groups_of(K, g);
+    const int cmask = (1 << bits) - 1;
+    memset(packed_codes, 0, oracle_packed_code_bytes_lowbit(bits, K, N));
+    memset(packed_meta, 0, oracle_packed_meta_bytes(K, N, g, zeros == NULL));
+    for (int k = 0; k < Kp; ++k)
+        for (int n = 0; n < N; ++n) {
+            uint32_t q = k < K ? codes[(size_t)k * N + n]
+                               : (uint32_t)zero_point(zeros, k / g, n, N, rows, 1 << (bits - 1));
+            put_lowbit(packed_codes, bits, k, n, Kp, q & (uint32_t)cmask);
+        }
+    uint16_t *meta_scales = (uint16_t *)packed_meta;
+    uint8_t *meta_zeros = packed_meta + (size_t)(Kp / g) * Np * 2;
+    for (int r = 0; r < rows; ++r)
+        for (int n = 0; n < N; ++n) {
+            size_t e = meta_index(r * g, n, Kp, g);
+            meta_scales[e] = scales[(size_t)r * N + n];
+            if (zeros) {
+                uint8_t z = zeros[(size_t)r * N + n] & (uint8_t)cmask;
+                meta_zeros[e / 2] |= (uint8_t)((e % 2) ? (z << 4) : z);
+            }
+        }
+}
+
+void oracle_unpack_lowbit(int bits, const uint8_t *packed_codes, const uint8_t *packed_meta,
+                          int K, int N, int g, int symmetric, uint8_t *codes, uint16_t *scales,
+                          uint8_t *zeros) {
+    const int Kp = oracle_padded_k(K), Np = oracle_padded_n(N), rows = groups_of(K, g);
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            codes[(size_t)k * N + n] = (uint8_t)get_lowbit(packed_codes, bits, k, n, Kp);
+    const uint16_t *meta_scales = (const uint16_t *)packed_meta;
+    const uint8_t *meta_zeros = packed_meta + (size_t)(Kp / g) * Np * 2;
+    for (int r = 0; r < rows; ++r)
+        for (int n = 0; n < N; ++n) {
+            size_t e = meta_index(r * g, n, Kp, g);
+            scales[(size_t)r * N + n] = meta_scales[e];
+            if (!symmetric && zeros) {
+                uint8_t b = meta_zeros[e / 2];
+                zeros[(size_t)r * N + n] = (uint8_t)((e % 2) ? (b >> 4) : (b & 0xf));
+            }
+        }
 }
 
 int oracle_max_threads(void) {

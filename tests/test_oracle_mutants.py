@@ -79,6 +79,24 @@ MUTANTS_RAGGED = {
 }
 
 
+MUTANTS_LOWBIT = {
+    "lowbit_sign": ("f64_to_act((double)(qb - zb) * sb, dtype);",
+                    "f64_to_act((double)(zb - qb) * sb, dtype);"),
+    "lowbit_sym_zero": ("(zeros[(size_t)gr * N + n] & cmask) : (1 << (bits - 1));",
+                        "(zeros[(size_t)gr * N + n] & cmask) : (1 << bits) / 4;"),
+    "lowbit_code_mask": ("int qb = codes[(size_t)k * N + n] & cmask;",
+                         "int qb = codes[(size_t)k * N + n] & 0xf;"),
+    "w2_field_order": ("bit = h + 2 * ((r % 8) % 4) + 8 * ((r % 8) / 4) + c;\n        } else if (r < 15) {\n            word = r / 5;\n            bit = h + 3 * (r % 5) + c;\n        } else {\n            word = c;\n            bit = h + 15;\n        }\n        if ((q >> c) & 1u)",
+                       "bit = h + 2 * ((r % 8) / 2) + 8 * ((r % 8) % 2) + c;\n        } else if (r < 15) {\n            word = r / 5;\n            bit = h + 3 * (r % 5) + c;\n        } else {\n            word = c;\n            bit = h + 15;\n        }\n        if ((q >> c) & 1u)"),
+    "w3_spare_pair": ("            word = c;\n            bit = h + 15;\n        }\n        if ((q >> c) & 1u)",
+                      "            word = 2 - c;\n            bit = h + 15;\n        }\n        if ((q >> c) & 1u)"),
+    "lowbit_tile_stride": ("uint8_t *lane_words = plane + T * 256 * bits + (size_t)L * 4 * bits;\n    for (int c = 0; c < bits; ++c) {\n        int word, bit;\n        if (bits == 2) {\n            word = r / 8;\n            bit = h + 2 * ((r % 8) % 4) + 8 * ((r % 8) / 4) + c;\n        } else if (r < 15) {\n            word = r / 5;\n            bit = h + 3 * (r % 5) + c;\n        } else {\n            word = c;\n            bit = h + 15;\n        }\n        if ((q >> c) & 1u)",
+                           "uint8_t *lane_words = plane + T * 256 * bits + (size_t)(L ^ 16) * 4 * bits;\n    for (int c = 0; c < bits; ++c) {\n        int word, bit;\n        if (bits == 2) {\n            word = r / 8;\n            bit = h + 2 * ((r % 8) % 4) + 8 * ((r % 8) / 4) + c;\n        } else if (r < 15) {\n            word = r / 5;\n            bit = h + 3 * (r % 5) + c;\n        } else {\n            word = c;\n            bit = h + 15;\n        }\n        if ((q >> c) & 1u)"),
+    "lowbit_pad_zero": ("(uint32_t)zero_point(zeros, k / g, n, N, rows, 1 << (bits - 1));",
+                        "(uint32_t)zero_point(zeros, k / g, n, N, rows, 0);"),
+}
+
+
 def _run_pins(text, before, after, pins, tmp_path):
     assert text.count(before) == 1, f"mutation anchor not found once: {before}"
     src = tmp_path / "mutant.c"
@@ -123,4 +141,11 @@ def test_fp8_pins_catch_planted_mistake(name, tmp_path):
 def test_ragged_pins_catch_planted_mistake(name, tmp_path):
     before, after = MUTANTS_RAGGED[name]
     res = _run_pins(open(SRC).read(), before, after, "test_oracle_ragged.py", tmp_path)
+    assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_LOWBIT))
+def test_lowbit_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTANTS_LOWBIT[name]
+    res = _run_pins(open(SRC).read(), before, after, "test_oracle_lowbit.py", tmp_path)
     assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
