@@ -128,7 +128,7 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
 /*
  * Device workspace (bytes) mpgemm_w4a16 and mpgemm_w4a16_config need for this problem:
  * nonzero only when a small-M kernel splits K over several workgroups (the largest need of
- * the configurations that can run M rows).  The workspace holds fp32 partial sums and one
+ * the configurations that can run M rows, and of 64-row chunks when M > 64).  The workspace holds fp32 partial sums and one
  * 32-bit counter per group of columns at its start.
  *   - It must be all zero before its first use; every call leaves the counters zero again,
  *     so one zeroed allocation serves any number of later calls.
@@ -263,6 +263,61 @@ int mpgemm_wfp8a16_config(const void *X, int dtype, int fp8_format, const void *
                           const void *packed_meta, int M, int N, int K, int group, void *Y,
                           void *workspace, size_t workspace_bytes, int config_id,
                           void *stream);
+
+/*
+ * ---------------------------------------------------------------------------------
+ * 2-bit and 3-bit weights.  "Progressive Mixed-Precision Decoding for Efficient LLM
+ * Inference" (arXiv 2410.13461), abstract: 2/3-bit weights ease the memory-boundedness of
+ * decoding.  The same group form with b-bit integers (bits = b = 2 or 3):
+ *   codes  uint8 [K][N], low b bits read: q in 0..2^b-1
+ *   zeros  uint8 [G][N], low b bits read; or NULL for symmetric codes (z = 2^(b-1))
+ *   scales fp16 [G][N] as above
+ *   w[k][n] = (q - z) * s rounded once to the activation format.
+ * Packed sub-4-bit layout (same layout version; ragged shapes padded to Kp x Np as above,
+ * symmetric padding code 2^(b-1))
+ *   Codes plane, Kp*Np*b/8 bytes.  Tiles of 16 columns x 128 rows of k, 256*b bytes each;
+ *   tile T = (n/16)*(Kp/128) + k/128 at byte T*256*b.  With kk = k%128 and nn = n%16:
+ *   lane L = nn + 16*((kk%32)/8), step t = kk/32, element i = kk%8; lane L's b
+ *   little-endian 32-bit words start at byte L*4*b of the tile.  The element belongs to
+ *   pair register r = 4t + i/2, in its low 16-bit half (h = 0) for even i and its high
+ *   half (h = 1) for odd i:
+ *     b = 2: word r/8, code at bits 16h + 2*(r%4) + 8*((r%8)/4) .. +1;
+ *     b = 3: r < 15: word r/5, code at bits 16h + 3*(r%5) .. +2;
+ *            r = 15: bit c (c = 0, 1, 2) of the code at bit 16h + 15 of word c.
+ *   Why: every code field sits inside the fp16 mantissa of its half (after at most one
+ *   shift: by 8 for 2-bit, by 9 for 3-bit fields at 9 and 12), so one v_and_or_b32 with the
+ *   fp16 pattern of the power of two whose mantissa step at that bit is 1 yields the pair
+ *   (B + q_lo, B + q_hi), ready for the exact subtraction of B + z and the scaling; the
+ *   register is the 16x16x32 MFMA A operand of step t (row nn, k = 8*(L/16) + 2*(i/2)).
+ *   Meta plane exactly as for 4-bit codes (zeros as 4-bit values).
+ * The GEMM runs the small-M kernel (configurations 1..4); with configuration 0 and M > 64
+ * it runs that kernel on 64-row chunks (the weights are read once per chunk).  Other ids
+ * return MPGEMM_ERR_UNSUPPORTED.  A bits value other than 2 or 3 returns
+ * MPGEMM_ERR_INVALID_ARG.  Workspace as for mpgemm_w4a16.
+ */
+
+/* Size of the packed sub-4-bit codes plane: Kp*Np*bits/8 bytes (0 if unsupported).  The
+ * meta plane is sized by mpgemm_packed_meta_bytes. */
+size_t mpgemm_packed_code_bytes_lowbit(int bits, int K, int N);
+
+/* Offline packing of b-bit codes; contract as mpgemm_pack_weights. */
+int mpgemm_pack_weights_lowbit(int bits, const uint8_t *codes, const uint16_t *scales,
+                               const uint8_t *zeros, int K, int N, int group,
+                               void *packed_codes, void *packed_meta, void *stream);
+
+/* Exact inverse of mpgemm_pack_weights_lowbit (codes come back in 0..2^b-1). */
+int mpgemm_unpack_lowbit(int bits, const void *packed_codes, const void *packed_meta, int K,
+                         int N, int group, int symmetric, uint8_t *codes, uint16_t *scales,
+                         uint8_t *zeros, void *stream);
+
+/* Y[M][N] = X[M][K] * dequant(Wb)[K][N]; arguments as for mpgemm_w4a16. */
+int mpgemm_wlowbit_a16(int bits, const void *X, int dtype, const void *packed_codes,
+                       const void *packed_meta, int M, int N, int K, int group, int symmetric,
+                       void *Y, void *workspace, size_t workspace_bytes, void *stream);
+int mpgemm_wlowbit_a16_config(int bits, const void *X, int dtype, const void *packed_codes,
+                              const void *packed_meta, int M, int N, int K, int group,
+                              int symmetric, void *Y, void *workspace, size_t workspace_bytes,
+                              int config_id, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *mpgemm_status_string(int status);

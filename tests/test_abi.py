@@ -163,7 +163,8 @@ def test_split_k_workspace_is_sized_and_required(monkeypatch):
     # the fixed 256 KiB counter region, then 16 strip groups x 2 splits x 1 KiB of
     # partials per row block, sized for every configuration that can run M = 16 (up to 4)
     assert need == 256 * 1024 + 16 * 2 * 4 * 1024
-    assert lib.mpgemm_workspace_bytes(2048, 256, 256, 128, 0) == 0     # large M: no split
+    # large M: only the 64-row chunks of 2- and 3-bit codes run the small-M kernel
+    assert lib.mpgemm_workspace_bytes(2048, 256, 256, 128, 0) == 256 * 1024 + 16 * 2 * 4 * 1024
     assert _gemm() == -4                                                # workspace NULL
     args = [ctypes.c_void_p(A), 0, ctypes.c_void_p(A), ctypes.c_void_p(A), 16, 256, 256, 128,
             0, ctypes.c_void_p(A), ctypes.c_void_p(A), 100]
@@ -209,3 +210,38 @@ def test_binding_fp8_format_names_match_header():
 def test_ragged_k_is_refused_by_the_16x16x32_tiled_kernels(cfg):
     # K = 200 pads to 256: only the small-M and 32x32x16 kernels mask the activation tail
     assert _gemm(M=128, K=200, cfg=cfg) == UNSUPPORTED
+
+
+def _low(bits=2, cfg=0, M=16, K=256):
+    lib = mp.lib()
+    vp = ctypes.c_void_p
+    return lib.mpgemm_wlowbit_a16_config(bits, vp(A), 0, vp(A), vp(A), M, 256, K, 128, 0,
+                                         vp(A), None, 0, cfg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=4), INVALID),
+    (dict(bits=1), INVALID),
+    (dict(cfg=12, M=128), UNSUPPORTED),      # no tiled kernel for sub-4-bit codes
+    (dict(cfg=13, M=128), UNSUPPORTED),
+    (dict(cfg=10, M=128), UNSUPPORTED),
+    (dict(cfg=1, M=17), UNSUPPORTED),
+    (dict(K=12), UNSUPPORTED),
+    (dict(M=0), OK),
+])
+def test_lowbit_gemm_validation(kw, status):
+    assert _low(**kw) == status
+
+
+def test_lowbit_sizes_and_pack_validation():
+    lib = mp.lib()
+    vp = ctypes.c_void_p
+    assert lib.mpgemm_packed_code_bytes_lowbit(2, 256, 64) == 256 * 64 * 2 // 8
+    assert lib.mpgemm_packed_code_bytes_lowbit(3, 200, 40) == 256 * 48 * 3 // 8
+    assert lib.mpgemm_packed_code_bytes_lowbit(4, 256, 64) == 0
+    assert lib.mpgemm_pack_weights_lowbit(5, vp(A), vp(A), None, 256, 32, 128, vp(A), vp(A),
+                                          None) == INVALID
+    assert lib.mpgemm_pack_weights_lowbit(2, None, vp(A), None, 256, 32, 128, vp(A), vp(A),
+                                          None) == INVALID
+    assert lib.mpgemm_unpack_lowbit(3, vp(A), vp(A), 256, 32, 128, 0, vp(A), vp(A), None,
+                                    None) == INVALID

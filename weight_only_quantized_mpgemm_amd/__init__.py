@@ -56,6 +56,12 @@ SIGNATURES = {
     "mpgemm_w8a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
     "mpgemm_wfp8a16": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "mpgemm_packed_code_bytes_lowbit": (_sz, [_i, _i, _i]),
+    "mpgemm_pack_weights_lowbit": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "mpgemm_unpack_lowbit": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "mpgemm_wlowbit_a16": (_i, [_i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "mpgemm_wlowbit_a16_config": (_i, [_i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz,
+                                       _i, _vp]),
     "mpgemm_wfp8a16_config": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                    _vp]),
 }
@@ -226,6 +232,35 @@ def pack_weights_fp8(codes: torch.Tensor, scales: torch.Tensor, group: int,
     return out
 
 
+def pack_weights_lowbit(bits: int, codes: torch.Tensor, scales: torch.Tensor,
+                        zeros: torch.Tensor | None, group: int) -> PackedWeights:
+    """Offline packing of 2-bit or 3-bit codes (mpgemm_pack_weights_lowbit).
+
+    codes uint8 [K, N] (0..2^bits-1); scales float16 [ceil(K/g), N]; zeros uint8 of the
+    same shape or None for symmetric codes with zero 2^(bits-1).
+    """
+    if bits not in (2, 3):
+        raise ValueError(f"bits must be 2 or 3, got {bits}")
+    K, N = codes.shape
+    _need(codes, torch.uint8, (K, N), "codes")
+    rows = _group_rows(K, group)
+    _need(scales, torch.float16, (rows, N), "scales")
+    if zeros is not None:
+        _need(zeros, torch.uint8, (rows, N), "zeros")
+    cb = int(lib().mpgemm_packed_code_bytes_lowbit(bits, K, N))
+    mb = packed_meta_bytes(K, N, group, zeros is None)
+    if K * N and (cb == 0 or mb == 0):
+        raise MpgemmError(-2, "pack_weights_lowbit")
+    out = PackedWeights(torch.empty(cb, dtype=torch.uint8, device=codes.device),
+                        torch.empty(mb, dtype=torch.uint8, device=codes.device),
+                        K, N, group, zeros is None, bits)
+    st = lib().mpgemm_pack_weights_lowbit(bits, _ptr(codes), _ptr(scales), _ptr(zeros), K, N,
+                                          group, _ptr(out.codes), _ptr(out.meta),
+                                          _stream(codes.device))
+    _check(st, "mpgemm_pack_weights_lowbit")
+    return out
+
+
 def unpack(packed: PackedWeights):
     """Inverse of packing (mpgemm_unpack / mpgemm_unpack_w8): (codes, scales, zeros or
     None)."""
@@ -235,10 +270,14 @@ def unpack(packed: PackedWeights):
     scales = torch.empty((_group_rows(K, g), N), dtype=torch.float16, device=dev)
     zeros = None if packed.symmetric else torch.empty((_group_rows(K, g), N),
                                                       dtype=torch.uint8, device=dev)
-    name = "mpgemm_unpack_w8" if packed.bits == 8 else "mpgemm_unpack"
-    st = getattr(lib(), name)(_ptr(packed.codes), _ptr(packed.meta), K, N, g,
-                              int(packed.symmetric), _ptr(codes), _ptr(scales), _ptr(zeros),
-                              _stream(dev))
+    args = (_ptr(packed.codes), _ptr(packed.meta), K, N, g, int(packed.symmetric), _ptr(codes),
+            _ptr(scales), _ptr(zeros), _stream(dev))
+    if packed.bits in (2, 3):
+        name = "mpgemm_unpack_lowbit"
+        st = lib().mpgemm_unpack_lowbit(packed.bits, *args)
+    else:
+        name = "mpgemm_unpack_w8" if packed.bits == 8 else "mpgemm_unpack"
+        st = getattr(lib(), name)(*args)
     _check(st, name)
     return codes, scales, zeros
 
@@ -306,11 +345,14 @@ def _gemm(kind: str, x: torch.Tensor, packed: PackedWeights, out, config, worksp
     if kind == "fp8":
         args = (_ptr(x), act, FP8_FORMATS[packed.fp8], _ptr(packed.codes), _ptr(packed.meta),
                 M, N, K, packed.group, _ptr(out), _ptr(workspace), ws)
+    elif kind in ("w2", "w3"):
+        args = (packed.bits, _ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K,
+                packed.group, int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
     else:
         args = (_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N, K, packed.group,
                 int(packed.symmetric), _ptr(out), _ptr(workspace), ws)
-    name = ("mpgemm_wfp8a16" if kind == "fp8" else f"mpgemm_{kind}a16") + \
-        ("_config" if config else "")
+    base = {"fp8": "mpgemm_wfp8a16", "w2": "mpgemm_wlowbit_a16", "w3": "mpgemm_wlowbit_a16"}
+    name = base.get(kind, f"mpgemm_{kind}a16") + ("_config" if config else "")
     fn = getattr(lib(), name)
     st = fn(*args, int(config), _stream(x.device)) if config else fn(*args, _stream(x.device))
     _check(st, name)
@@ -333,6 +375,15 @@ def w8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = Non
     """Y = X @ dequant(W8) for weights packed by pack_weights_w8 (mpgemm_w8a16; the
     _config variant when config != 0).  Arguments as for w4a16."""
     return _gemm("w8", x, packed, out, config, workspace)
+
+
+def wlowbit_a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,
+                config: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X @ dequant(W) for 2-bit or 3-bit weights packed by pack_weights_lowbit
+    (mpgemm_wlowbit_a16; the _config variant when config != 0).  Arguments as for w4a16."""
+    if packed.bits not in (2, 3):
+        raise ValueError(f"weights are packed with {packed.bits}-bit codes, not 2 or 3")
+    return _gemm(f"w{packed.bits}", x, packed, out, config, workspace)
 
 
 def wfp8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,

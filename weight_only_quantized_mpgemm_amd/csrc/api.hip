@@ -90,6 +90,11 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
+    // 2- and 3-bit codes run the small-M kernel only (the tiled kernels have no sub-4-bit
+    // dequantization): larger M goes through it in chunks of 64 rows.
+    const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
+    if (lowbit && config_id != kConfigSelect && !(cfg >= kConfigDecode1 && cfg <= kConfigDecode4))
+        return MPGEMM_ERR_UNSUPPORTED;
     // 8-bit and FP8 codes, and ragged K, run the small-M kernel and the 32x32x16 tiled
     // kernels (which mask the activations past K); the 16x16x32 tiled kernels take aligned
     // 4-bit problems only.
@@ -117,8 +122,27 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
             return MPGEMM_ERR_WORKSPACE;
     }
+    if (lowbit && M > 64) {
+        const size_t need = mpgemm::decode_workspace_bytes(64, N, K, kConfigDecode4);
+        if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+            return MPGEMM_ERR_WORKSPACE;
+        if (getenv("MPGEMM_LOG"))
+            fprintf(stderr, "mpgemm: W%dA16 M=%d N=%d K=%d g=%d -> %s in %d row chunks\n",
+                    code == mpgemm::kU2 ? 2 : 3, M, N, K, group,
+                    mpgemm_config_name(kConfigDecode4), (M + 63) / 64);
+        for (int m0 = 0; m0 < M; m0 += 64) {
+            mpgemm::GemmArgs c = a;
+            c.X = a.X + (size_t)m0 * K;
+            c.Y = a.Y + (size_t)m0 * N;
+            c.M = M - m0 < 64 ? M - m0 : 64;
+            const int st = hip_status(mpgemm::launch_decode(c, kConfigDecode4, s));
+            if (st != MPGEMM_OK) return st;
+        }
+        return MPGEMM_OK;
+    }
     if (getenv("MPGEMM_LOG")) {
-        static const char *const names[] = {"W4A16", "W8A16", "W(E4M3)A16", "W(E5M2)A16"};
+        static const char *const names[] = {"W4A16", "W8A16", "W(E4M3)A16", "W(E5M2)A16",
+                                            "W2A16", "W3A16"};
         fprintf(stderr, "mpgemm: %s M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", names[code],
                 M, N, K, group, dtype, symmetric, mpgemm_config_name(cfg));
     }
@@ -186,6 +210,10 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
     size_t need = 0;
     for (int mblocks = (M + 15) / 16; mblocks <= 4; ++mblocks) {
         const size_t b = mpgemm::decode_workspace_bytes(M, N, K, mblocks);
+        if (b > need) need = b;
+    }
+    if (M > 64) {                   // 2- and 3-bit codes: 64-row chunks of the small-M kernel
+        const size_t b = mpgemm::decode_workspace_bytes(64, N, K, 4);
         if (b > need) need = b;
     }
     return need;
@@ -281,6 +309,64 @@ int mpgemm_wfp8a16(const void *X, int dtype, int fp8_format, const void *packed_
                    void *workspace, size_t workspace_bytes, void *stream) {
     return mpgemm_wfp8a16_config(X, dtype, fp8_format, packed_codes, packed_meta, M, N, K,
                                  group, Y, workspace, workspace_bytes, kConfigSelect, stream);
+}
+
+size_t mpgemm_packed_code_bytes_lowbit(int bits, int K, int N) {
+    if ((bits != 2 && bits != 3) || check_shape(0, N, K, 128) != MPGEMM_OK) return 0;
+    return (size_t)mpgemm::padded_k(K) * (size_t)mpgemm::padded_n(N) * bits / 8;
+}
+
+int mpgemm_pack_weights_lowbit(int bits, const uint8_t *codes, const uint16_t *scales,
+                               const uint8_t *zeros, int K, int N, int group, void *packed_codes,
+                               void *packed_meta, void *stream) {
+    if (bits != 2 && bits != 3) return MPGEMM_ERR_INVALID_ARG;
+    const int st = check_shape(0, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if ((size_t)K * N == 0) return MPGEMM_OK;
+    if (codes == nullptr || scales == nullptr || packed_codes == nullptr ||
+        packed_meta == nullptr)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)) ||
+        !aligned16(packed_codes) || !aligned16(packed_meta))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_pack_lowbit(bits, codes, scales, zeros, K, N, group,
+                                                 packed_codes, packed_meta, (hipStream_t)stream));
+}
+
+int mpgemm_unpack_lowbit(int bits, const void *packed_codes, const void *packed_meta, int K,
+                         int N, int group, int symmetric, uint8_t *codes, uint16_t *scales,
+                         uint8_t *zeros, void *stream) {
+    if ((bits != 2 && bits != 3) || (symmetric != 0 && symmetric != 1))
+        return MPGEMM_ERR_INVALID_ARG;
+    const int st = check_shape(0, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if ((size_t)K * N == 0) return MPGEMM_OK;
+    if (packed_codes == nullptr || packed_meta == nullptr || codes == nullptr ||
+        scales == nullptr || (!symmetric && zeros == nullptr))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(packed_codes) || !aligned16(packed_meta) || !aligned16(codes) ||
+        !aligned16(scales) || (!symmetric && !aligned16(zeros)))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_unpack_lowbit(bits, packed_codes, packed_meta, K, N, group,
+                                                   symmetric, codes, scales, zeros,
+                                                   (hipStream_t)stream));
+}
+
+int mpgemm_wlowbit_a16_config(int bits, const void *X, int dtype, const void *packed_codes,
+                              const void *packed_meta, int M, int N, int K, int group,
+                              int symmetric, void *Y, void *workspace, size_t workspace_bytes,
+                              int config_id, void *stream) {
+    if (bits != 2 && bits != 3) return MPGEMM_ERR_INVALID_ARG;
+    return gemm_impl(bits == 2 ? mpgemm::kU2 : mpgemm::kU3, X, dtype, packed_codes, packed_meta,
+                     M, N, K, group, symmetric, Y, workspace, workspace_bytes, config_id, stream);
+}
+
+int mpgemm_wlowbit_a16(int bits, const void *X, int dtype, const void *packed_codes,
+                       const void *packed_meta, int M, int N, int K, int group, int symmetric,
+                       void *Y, void *workspace, size_t workspace_bytes, void *stream) {
+    return mpgemm_wlowbit_a16_config(bits, X, dtype, packed_codes, packed_meta, M, N, K, group,
+                                     symmetric, Y, workspace, workspace_bytes, kConfigSelect,
+                                     stream);
 }
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {

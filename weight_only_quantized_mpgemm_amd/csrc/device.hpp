@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mpgemm {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -19,11 +21,11 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 enum Act { kF16 = 0, kBF16 = 1 };
 
-// Formats of the packed codes plane: 4-bit and 8-bit unsigned integers with a group zero
-// point, or 8-bit OCP floating point (E4M3, E5M2) with a group scale only.
-enum Code { kU4 = 0, kU8 = 1, kE4M3 = 2, kE5M2 = 3 };
+// Formats of the packed codes plane: 2-, 3-, 4- and 8-bit unsigned integers with a group
+// zero point, or 8-bit OCP floating point (E4M3, E5M2) with a group scale only.
+enum Code { kU4 = 0, kU8 = 1, kE4M3 = 2, kE5M2 = 3, kU2 = 4, kU3 = 5 };
 template <int CODE>
-constexpr int kCodeBits = CODE == kU4 ? 4 : 8;
+constexpr int kCodeBits = CODE == kU4 ? 4 : (CODE == kU2 ? 2 : (CODE == kU3 ? 3 : 8));
 template <int CODE>
 constexpr bool kCodeFp8 = CODE == kE4M3 || CODE == kE5M2;
 
@@ -281,6 +283,98 @@ struct DqF8<kBF16, CODE> {
     }
 };
 
+// ------------------------------------------------ 2-bit and 3-bit codes (sub-4-bit) ----
+//
+// A lane's 32 codes of a 128-deep tile (4 MFMA steps x 8) sit in b words (include/mpgemm.h):
+// pair register r = 4t + j holds elements 2j, 2j+1 of step t in its low and high 16-bit
+// halves.  Each code field of b bits sits inside the fp16 mantissa at bit p of its half, so
+// one v_and_or_b32 with the fp16 pattern of B_p (the power of two whose mantissa step at
+// bit p is 1) makes the pair B_p + q; an exact packed add of -(B_p + z) leaves q - z, and
+// one packed multiply by s rounds (fp16).  bf16: (q - z) to fp32, exact products with s,
+// one rounding.
+//   2-bit: fields at p = 0, 2, 4, 6 (B = 1024, 256, 64, 16) of the word, or of the word
+//          shifted right by 8; word r / 8.
+//   3-bit: fields at p = 0, 3, 6 (B = 1024, 128, 16) of the word, or at 9, 12 read after a
+//          shift by 9; word r / 5 for r < 15.  Pair 15 is gathered from bits 15 and 31 of
+//          the three words (bit c of each code in word c), at p = 0.
+template <int BITS>
+struct LowBases;
+template <>
+struct LowBases<2> {
+    static constexpr int kCount = 4;
+    static constexpr uint32_t kPattern[4] = {0x64006400u, 0x5C005C00u, 0x54005400u, 0x4C004C00u};
+    static constexpr float kValue[4] = {1024.f, 256.f, 64.f, 16.f};
+};
+template <>
+struct LowBases<3> {
+    static constexpr int kCount = 3;
+    static constexpr uint32_t kPattern[3] = {0x64006400u, 0x58005800u, 0x4C004C00u};
+    static constexpr float kValue[3] = {1024.f, 128.f, 16.f};
+};
+
+// Per-(group, column) constants: -(B_p + z) as fp16 pairs, and the scale.
+template <int BITS>
+struct DqLowConst {
+    uint32_t nz[LowBases<BITS>::kCount];
+    uint32_t s2;                 // fp16 pair of s
+    float s;                     // s as fp32 (bf16 path)
+};
+
+// Biased pair register r (B_p + q in each half) from the lane's words, and its base index.
+template <int BITS, int R>
+__device__ __forceinline__ uint32_t low_pair(const u32x4_t &w, int &base) {
+    if constexpr (BITS == 2) {
+        constexpr int j = R % 4, sh = 8 * ((R % 8) / 4);
+        base = j;
+        const uint32_t src = sh ? (w[R / 8] >> sh) : w[R / 8];
+        return and_or(src, 0x00030003u << (2 * j), LowBases<2>::kPattern[j]);
+    } else if constexpr (R < 15) {
+        constexpr int s5 = R % 5, j = s5 % 3;
+        base = j;
+        const uint32_t src = s5 >= 3 ? (w[R / 5] >> 9) : w[R / 5];
+        return and_or(src, 0x00070007u << (3 * j), LowBases<3>::kPattern[j]);
+    } else {
+        base = 0;
+        uint32_t h = and_or(w[0] >> 15, 0x00010001u, LowBases<3>::kPattern[0]);
+        h = and_or(w[1] >> 14, 0x00020002u, h);
+        return and_or(w[2] >> 13, 0x00040004u, h);
+    }
+}
+
+template <int ACT, int BITS>
+struct DqLow {
+    typedef DqLowConst<BITS> type;
+    static __device__ __forceinline__ type make(uint16_t s, uint32_t z) {
+        type d;
+#pragma unroll
+        for (int b = 0; b < LowBases<BITS>::kCount; ++b) {
+            const uint32_t h = bitcast<uint16_t>((_Float16)(-(LowBases<BITS>::kValue[b] + (float)z)));
+            d.nz[b] = h | (h << 16);
+        }
+        d.s2 = (uint32_t)s | ((uint32_t)s << 16);
+        d.s = (float)bitcast<_Float16>(s);
+        return d;
+    }
+    // The four MFMA steps' A operands of one lane-tile; d[t] holds step t's constants.
+    static __device__ __forceinline__ void tile(const u32x4_t &w, const type *const (&d)[4],
+                                                u32x4_t (&a)[4]) {
+        [&]<int... R>(std::integer_sequence<int, R...>) {
+            (([&] {
+                 int b;
+                 const uint32_t h = low_pair<BITS, R>(w, b);
+                 const type &c = *d[R / 4];
+                 const half2_t q = bitcast<half2_t>(h) + bitcast<half2_t>(c.nz[b]);   // exact
+                 if constexpr (ACT == kF16) {
+                     a[R / 4][R % 4] = bitcast<uint32_t>(q * bitcast<half2_t>(c.s2));
+                 } else {
+                     a[R / 4][R % 4] = pack_bf16x2((float)q.x * c.s, (float)q.y * c.s);
+                 }
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, 16>{});
+    }
+};
+
 // The dequantization of code format CODE for activation format ACT: make(s, z) builds the
 // per-(group, column) constants; pair(w0, w1, d) (8-bit formats) dequantizes codes k0..k7.
 template <int ACT, int CODE>
@@ -294,6 +388,14 @@ struct DqSel<ACT, kU4> {
 template <int ACT>
 struct DqSel<ACT, kU8> {
     typedef Dq8<ACT> type;
+};
+template <int ACT>
+struct DqSel<ACT, kU2> {
+    typedef DqLow<ACT, 2> type;
+};
+template <int ACT>
+struct DqSel<ACT, kU3> {
+    typedef DqLow<ACT, 3> type;
 };
 template <int ACT, int CODE>
 using DqFor = typename DqSel<ACT, CODE>::type;
@@ -383,6 +485,11 @@ __device__ __forceinline__ u32x4_t buf_load_b128(rsrc_t r, uint32_t voff, uint32
 }
 __device__ __forceinline__ u32x2_t buf_load_b64(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x4_t buf_load_b96(rsrc_t r, uint32_t voff, uint32_t soff) {
+    typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+    const u32x3_t v = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
+    return u32x4_t{v.x, v.y, v.z, 0u};
 }
 __device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);

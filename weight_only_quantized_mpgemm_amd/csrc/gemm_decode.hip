@@ -61,9 +61,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     // <= K); Ny: output row length (the user N, <= N).  Activations at k >= Kx read as zero.
     constexpr int GPT = kTileK / G;              // groups per 128-k tile (1 or 2)
     // 128-bit pieces per lane and strip per 128-deep step: one 16 x 128 tile of 4-bit codes,
-    // two 16 x 64 tiles of 8-bit codes.
+    // two 16 x 64 tiles of 8-bit codes; 2- and 3-bit codes fill 8 or 12 bytes of one piece.
     constexpr int BITS = kCodeBits<CODE>;
-    constexpr int WV = BITS / 4;
+    constexpr int WV = BITS >= 4 ? BITS / 4 : 1;
+    constexpr uint32_t kTileBytes = 256u * BITS;       // one 16 x 128 tile of the strip
+    constexpr uint32_t kLaneBytes = BITS >= 4 ? 16u : 4u * BITS;
+    constexpr bool kNibbleZeros = BITS <= 4;           // zeros stored as 4-bit values
     typedef Slot<MB, S, GPT, WV> SlotT;
     extern __shared__ f32x4_t red[];             // [NW][S][MB][64]
 
@@ -83,10 +86,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const int strips = N >> 4;
     const int strip0 = blockIdx.x * S;
 
-    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * 1024 * WV));
+    const rsrc_t wrs = make_rsrc(codes, (uint32_t)((size_t)strips * KT * kTileBytes));
     const rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)M * Kx * 2));
     const rsrc_t srs = make_rsrc(scales, (uint32_t)((size_t)groups * N * 2));
-    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
+    const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N / (kNibbleZeros ? 2 : 1)));
 
     // Per-lane byte offsets, fixed for the whole K slice.  Strips past N read the last real
     // strip (their outputs are never stored).  The meta element of a lane's column is a
@@ -96,10 +99,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
 #pragma unroll
     for (int si = 0; si < S; ++si) {
         const uint32_t strip = (uint32_t)min(strip0 + si, strips - 1);
-        woff[si] = (strip * KT + t_begin) * 1024u * WV + lane * 16u;
+        woff[si] = (strip * KT + t_begin) * kTileBytes + lane * kLaneBytes;
         const uint32_t e = strip * groups * 16u + t_begin * GPT * 16u + (lane & 15);
         soff[si] = (e >> 1) * 4u;
-        zoff[si] = BITS == 4 ? (e >> 3) * 4u : (e >> 2) * 4u;
+        zoff[si] = kNibbleZeros ? (e >> 3) * 4u : (e >> 2) * 4u;
     }
     uint32_t xoff[MB];
 #pragma unroll
@@ -111,17 +114,25 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
     const int k_lane = t_begin * kTileK + (lane >> 4) * 8;
     const bool ragged = Kx != K;
     const uint32_t sshift = (lane & 1) * 16;
-    const uint32_t zshift = BITS == 4 ? (lane & 7) * 4 : (lane & 3) * 8;
+    const uint32_t zshift = kNibbleZeros ? (lane & 7) * 4 : (lane & 3) * 8;
     constexpr uint32_t zmask = (1u << BITS) - 1;
-    constexpr uint32_t zsym = 1u << (BITS - 1);        // symmetric zero: 8 or 128
-    constexpr int zrow = 16 * BITS / 8;                // zero bytes per (strip, group)
+    constexpr uint32_t zsym = 1u << (BITS - 1);        // symmetric zero: 2, 4, 8 or 128
+    constexpr int zrow = kNibbleZeros ? 8 : 16;        // zero bytes per (strip, group)
 
     auto load = [&](SlotT &sl, int i) {
 #pragma unroll
-        for (int si = 0; si < S; ++si)
+        for (int si = 0; si < S; ++si) {
+            if constexpr (BITS == 2) {
+                const u32x2_t v = buf_load_b64(wrs, woff[si], i * kTileBytes);
+                sl.w[si][0] = u32x4_t{v.x, v.y, 0u, 0u};
+            } else if constexpr (BITS == 3) {
+                sl.w[si][0] = buf_load_b96(wrs, woff[si], i * kTileBytes);
+            } else {
 #pragma unroll
-            for (int v = 0; v < WV; ++v)
-                sl.w[si][v] = buf_load_b128(wrs, woff[si], (i * WV + v) * 1024);
+                for (int v = 0; v < WV; ++v)
+                    sl.w[si][v] = buf_load_b128(wrs, woff[si], i * kTileBytes + v * 1024);
+            }
+        }
         if (ragged && (t_begin + i + 1) * kTileK > Kx) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -162,20 +173,38 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
             for (int h = 0; h < GPT; ++h)
                 dq[si][h] = DqB::make((uint16_t)(sl.s[si][h] >> sshift),
                                       SYM ? zsym : ((sl.z[si][h] >> zshift) & zmask));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        if constexpr (BITS < 4) {
+            // Sub-4-bit codes: the four steps' operands of each strip at once.
+            u32x4_t at[S][4];
 #pragma unroll
             for (int si = 0; si < S; ++si) {
-                u32x4_t a;
-                if constexpr (BITS == 4)
-                    a = DqB::word(sl.w[si][0][j], dq[si][(j * 32) / G]);
-                else
-                    a = DqB::pair(sl.w[si][j / 2][2 * (j % 2)], sl.w[si][j / 2][2 * (j % 2) + 1],
-                                       dq[si][(j * 32) / G]);
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[si][mb] = mfma16x16x32<ACT>(a, sl.x[j][mb], acc[si][mb]);
+                const typename DqB::type *d[4] = {&dq[si][0], &dq[si][32 / G], &dq[si][64 / G],
+                                                  &dq[si][96 / G]};
+                DqB::tile(sl.w[si][0], d, at[si]);
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int si = 0; si < S; ++si)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[si][mb] = mfma16x16x32<ACT>(at[si][j], sl.x[j][mb], acc[si][mb]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int si = 0; si < S; ++si) {
+                    u32x4_t a;
+                    if constexpr (BITS == 4)
+                        a = DqB::word(sl.w[si][0][j], dq[si][(j * 32) / G]);
+                    else
+                        a = DqB::pair(sl.w[si][j / 2][2 * (j % 2)],
+                                      sl.w[si][j / 2][2 * (j % 2) + 1], dq[si][(j * 32) / G]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[si][mb] = mfma16x16x32<ACT>(a, sl.x[j][mb], acc[si][mb]);
+                }
+        }
     };
 
     if (n > 0) {
@@ -404,6 +433,8 @@ size_t decode_workspace_bytes(int M, int N, int K, int mblocks) {
 
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream) {
     switch (a.code) {
+        case kU2: launch_code<kU2>(a, mblocks, stream); break;
+        case kU3: launch_code<kU3>(a, mblocks, stream); break;
         case kU8: launch_code<kU8>(a, mblocks, stream); break;
         case kE4M3: launch_code<kE4M3>(a, mblocks, stream); break;
         case kE5M2: launch_code<kE5M2>(a, mblocks, stream); break;

@@ -31,8 +31,18 @@ hipError_t launch_unpack_w8(const void *packed_codes, const void *packed_meta, i
 __host__ __device__ inline int padded_k(int K) { return (K + 127) / 128 * 128; }
 __host__ __device__ inline int padded_n(int N) { return (N + 15) / 16 * 16; }
 
-// Arguments of one GEMM; planes as written by launch_pack (code kU4) or launch_pack_w8
-// (kU8, and the FP8 formats kE4M3 / kE5M2, which have no zero plane).
+// The same for 2-bit and 3-bit codes (bits = 2 or 3; tiles of 16 columns x 128 k, 4-bit
+// meta plane).
+hipError_t launch_pack_lowbit(int bits, const uint8_t *codes, const uint16_t *scales,
+                              const uint8_t *zeros, int K, int N, int group, void *packed_codes,
+                              void *packed_meta, hipStream_t stream);
+hipError_t launch_unpack_lowbit(int bits, const void *packed_codes, const void *packed_meta,
+                                int K, int N, int group, int symmetric, uint8_t *codes,
+                                uint16_t *scales, uint8_t *zeros, hipStream_t stream);
+
+// Arguments of one GEMM; planes as written by launch_pack (code kU4), launch_pack_w8 (kU8,
+// and the FP8 formats kE4M3 / kE5M2, which have no zero plane) or launch_pack_lowbit (kU2,
+// kU3).
 struct GemmArgs {
     const uint16_t *X;          // [M][K] activation bits (row stride K)
     const uint32_t *codes;      // packed codes plane (Kp x Np matrix)

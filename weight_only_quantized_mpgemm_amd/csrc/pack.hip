@@ -32,6 +32,7 @@ struct Shape {
     int K, N;        // user matrix (K % 8 == 0)
     int Kp, Np;      // padded matrix
     int g, rows;     // group size, user group rows ceil(K/g)
+    uint32_t zmask;  // bits of a zero that are read (4-bit meta plane)
 };
 
 // Code of padded-matrix element (k, n); `bits` = 4 or 8.
@@ -105,8 +106,8 @@ __global__ void pack_meta_kernel(const uint16_t *__restrict__ scales,
     if (zeros != nullptr && (e & 1) == 0) {
         int r1, n1;
         meta_coords(e + 1, groups, &r1, &n1);
-        const uint32_t z0 = in ? zeros[(size_t)r * sh.N + n] & 0xFu : 0u;
-        const uint32_t z1 = user_cell(sh, r1, n1) ? zeros[(size_t)r1 * sh.N + n1] & 0xFu : 0u;
+        const uint32_t z0 = in ? zeros[(size_t)r * sh.N + n] & sh.zmask : 0u;
+        const uint32_t z1 = user_cell(sh, r1, n1) ? zeros[(size_t)r1 * sh.N + n1] & sh.zmask : 0u;
         out_zeros[e >> 1] = (uint8_t)(z0 | (z1 << 4));
     }
 }
@@ -125,6 +126,78 @@ __global__ void unpack_meta_kernel(const uint16_t *__restrict__ in_scales,
     if (in_zeros != nullptr) {
         const uint32_t b = in_zeros[e >> 1];
         zeros[(size_t)r * sh.N + n] = (uint8_t)((e & 1) ? (b >> 4) : (b & 0xFu));
+    }
+}
+
+// ---- 2-bit and 3-bit codes: tiles of 16 columns x 128 k, 4 * b bytes per lane ----
+//
+// Pair register r = 4t + j of lane L holds elements 2j (low half) and 2j + 1 (high half)
+// of MFMA step t: rows k = 32t + 8 (L / 16) + 2j (+1) of the tile, column L % 16.
+//   2-bit: word r / 8, field at bit 16 h + 2 (r % 4) + 8 ((r % 8) / 4);
+//   3-bit: r < 15: word r / 5, field at bit 16 h + 3 (r % 5); r = 15: bit c of the code in
+//          word c at bit 16 h + 15.
+
+// One thread per (tile, lane) of the padded matrix.
+__global__ void pack_codes_low_kernel(const uint8_t *__restrict__ codes,
+                                      const uint8_t *__restrict__ zeros, Shape sh, int bits,
+                                      uint32_t *__restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int tiles_k = sh.Kp >> 7;
+    if (i >= (size_t)(sh.Np >> 4) * tiles_k * 64) return;
+    const int L = (int)(i & 63);
+    const size_t T = i >> 6;
+    const int strip = (int)(T / tiles_k), kt = (int)(T % tiles_k);
+    const int n = strip * 16 + (L & 15);
+    const uint32_t mask = (1u << bits) - 1;
+    uint32_t w[3] = {0u, 0u, 0u};
+    for (int r = 0; r < 16; ++r) {
+        const int t = r >> 2, j = r & 3;
+        for (int h = 0; h < 2; ++h) {
+            const int k = kt * 128 + 32 * t + 8 * (L >> 4) + 2 * j + h;
+            const uint32_t q = padded_code(codes, zeros, sh, k, n, bits) & mask;
+            if (bits == 2) {
+                w[r >> 3] |= q << (16 * h + 2 * (r & 3) + 8 * ((r & 7) >> 2));
+            } else if (r < 15) {
+                w[r / 5] |= q << (16 * h + 3 * (r % 5));
+            } else {
+                for (int c = 0; c < 3; ++c) w[c] |= ((q >> c) & 1u) << (16 * h + 15);
+            }
+        }
+    }
+    uint32_t *dst = out + (T * 256 * bits + (size_t)L * 4 * bits) / 4;
+    for (int c = 0; c < bits; ++c) dst[c] = w[c];
+}
+
+// One thread per (tile, lane) of the padded matrix; writes the user part.
+__global__ void unpack_codes_low_kernel(const uint32_t *__restrict__ in, Shape sh, int bits,
+                                        uint8_t *__restrict__ codes) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int tiles_k = sh.Kp >> 7;
+    if (i >= (size_t)(sh.Np >> 4) * tiles_k * 64) return;
+    const int L = (int)(i & 63);
+    const size_t T = i >> 6;
+    const int strip = (int)(T / tiles_k), kt = (int)(T % tiles_k);
+    const int n = strip * 16 + (L & 15);
+    if (n >= sh.N) return;
+    const uint32_t *src = in + (T * 256 * bits + (size_t)L * 4 * bits) / 4;
+    uint32_t w[3] = {0u, 0u, 0u};
+    for (int c = 0; c < bits; ++c) w[c] = src[c];
+    for (int r = 0; r < 16; ++r) {
+        const int t = r >> 2, j = r & 3;
+        for (int h = 0; h < 2; ++h) {
+            const int k = kt * 128 + 32 * t + 8 * (L >> 4) + 2 * j + h;
+            if (k >= sh.K) continue;
+            uint32_t q;
+            if (bits == 2) {
+                q = (w[r >> 3] >> (16 * h + 2 * (r & 3) + 8 * ((r & 7) >> 2))) & 3u;
+            } else if (r < 15) {
+                q = (w[r / 5] >> (16 * h + 3 * (r % 5))) & 7u;
+            } else {
+                q = 0;
+                for (int c = 0; c < 3; ++c) q |= ((w[c] >> (16 * h + 15)) & 1u) << c;
+            }
+            codes[(size_t)k * sh.N + n] = (uint8_t)q;
+        }
     }
 }
 
@@ -204,7 +277,7 @@ unsigned blocks_for(size_t total, unsigned threads) {
 
 namespace {
 
-Shape shape_of(int K, int N, int group) {
+Shape shape_of(int K, int N, int group, int bits = 4) {
     Shape sh;
     sh.K = K;
     sh.N = N;
@@ -212,6 +285,7 @@ Shape shape_of(int K, int N, int group) {
     sh.Np = padded_n(N);
     sh.g = group;
     sh.rows = (K + group - 1) / group;
+    sh.zmask = bits < 4 ? (1u << bits) - 1 : 0xFu;
     return sh;
 }
 
@@ -254,6 +328,43 @@ hipError_t launch_unpack(const void *packed_codes, const void *packed_meta, int 
         (size_t)(K >> 3) * N, metas,
         [&](unsigned b, unsigned t) {
             unpack_codes_kernel<<<b, t, 0, stream>>>((const uint32_t *)packed_codes, sh, codes);
+        },
+        [&](unsigned b, unsigned t) {
+            unpack_meta_kernel<<<b, t, 0, stream>>>(ms, mz, sh, scales,
+                                                    symmetric ? nullptr : zeros);
+        });
+}
+
+hipError_t launch_pack_lowbit(int bits, const uint8_t *codes, const uint16_t *scales,
+                              const uint8_t *zeros, int K, int N, int group, void *packed_codes,
+                              void *packed_meta, hipStream_t stream) {
+    const Shape sh = shape_of(K, N, group, bits);
+    const size_t metas = (size_t)(sh.Kp / group) * sh.Np;
+    uint16_t *ms = (uint16_t *)packed_meta;
+    uint8_t *mz = zeros ? (uint8_t *)packed_meta + metas * 2 : nullptr;
+    return launch_two(
+        (size_t)(sh.Np >> 4) * (sh.Kp >> 7) * 64, metas,
+        [&](unsigned b, unsigned t) {
+            pack_codes_low_kernel<<<b, t, 0, stream>>>(codes, zeros, sh, bits,
+                                                       (uint32_t *)packed_codes);
+        },
+        [&](unsigned b, unsigned t) {
+            pack_meta_kernel<<<b, t, 0, stream>>>(scales, zeros, sh, ms, mz);
+        });
+}
+
+hipError_t launch_unpack_lowbit(int bits, const void *packed_codes, const void *packed_meta,
+                                int K, int N, int group, int symmetric, uint8_t *codes,
+                                uint16_t *scales, uint8_t *zeros, hipStream_t stream) {
+    const Shape sh = shape_of(K, N, group, bits);
+    const size_t metas = (size_t)(sh.Kp / group) * sh.Np;
+    const uint16_t *ms = (const uint16_t *)packed_meta;
+    const uint8_t *mz = symmetric ? nullptr : (const uint8_t *)packed_meta + metas * 2;
+    return launch_two(
+        (size_t)(sh.Np >> 4) * (sh.Kp >> 7) * 64, metas,
+        [&](unsigned b, unsigned t) {
+            unpack_codes_low_kernel<<<b, t, 0, stream>>>((const uint32_t *)packed_codes, sh, bits,
+                                                         codes);
         },
         [&](unsigned b, unsigned t) {
             unpack_meta_kernel<<<b, t, 0, stream>>>(ms, mz, sh, scales,
