@@ -31,7 +31,9 @@ its own rotating pool), each GEMM against the HBM roofline (M <= 64; bytes count
 per code and per zero) or the fp16 MFMA roofline.  `wfp8a16_qwen3_8b_per_gemm` does the
 same with FP8 (E4M3) weights at the Qwen3-8B projection shapes (QKV 4096x6144, O 4096x4096,
 gate_up 4096x24576, down 12288x4096) and bf16 activations (mpgemm_wfp8a16; one byte per
-code, no zeros).  Neither is part of `value`.
+code, no zeros).  `w2a16_per_gemm` and `w3a16_per_gemm` do it with 2-bit and 3-bit weights
+(mpgemm_wlowbit_a16) at the Llama-3-8B shapes for M = 1 and 16, against the HBM roofline.
+None of these is part of `value`.
 """
 from __future__ import annotations
 
@@ -97,6 +99,12 @@ def gemm_bytes_w8(M, K, N, g, symmetric=False):
     return K * N + cells * 2 + (0 if symmetric else cells) + M * K * 2 + M * N * 2
 
 
+def gemm_bytes_lowbit(bits, M, K, N, g, symmetric=False):
+    """Algorithmic HBM bytes of one 2- or 3-bit GEMM: b-bit codes, scales, 4-bit zeros, X, Y."""
+    cells = (K // g) * N
+    return K * N * bits // 8 + cells * 2 + (0 if symmetric else cells // 2) + M * K * 2 + M * N * 2
+
+
 def gemm_flops(M, K, N):
     return 2 * M * N * K
 
@@ -141,6 +149,8 @@ def main():
                     help="skip the W8A16 per-GEMM pass (8-bit weights, same shapes)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8-weight per-GEMM pass (E4M3, Qwen3-8B shapes)")
+    ap.add_argument("--no-lowbit", action="store_true",
+                    help="skip the 2-bit and 3-bit per-GEMM passes (Llama-3-8B shapes, M=1,16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose HBM "
                          "counter readings scale the counter-based traffic figures")
@@ -330,19 +340,19 @@ def main():
     del pool
     torch.cuda.empty_cache()
 
-    def variant_pass(layer, shape_list, gemm, bytes_fn, act_dtype):
+    def variant_pass(layer, shape_list, gemm, bytes_fn, act_dtype, ms=MS):
         torch.cuda.synchronize()
         nbytes = sum(p.nbytes for p in layer)
         ncopies = max(3, int(np.ceil(args.pool_gb * 1e9 / nbytes)))
         vpool = [layer] + [[dataclasses.replace(p, codes=p.codes.clone(), meta=p.meta.clone())
                             for p in layer] for _ in range(ncopies - 1)]
         vx = {(M, K): torch.randn(M, K, device=dev).to(act_dtype)
-              for M in MS for K, _, _ in shape_list}
+              for M in ms for K, _, _ in shape_list}
         vy = {(M, N): torch.empty(M, N, device=dev, dtype=act_dtype)
-              for M in MS for _, N, _ in shape_list}
+              for M in ms for _, N, _ in shape_list}
         torch.cuda.synchronize()
         rows, reps = [], 10
-        for ci, (M, (K, N, label)) in enumerate((M, sh) for M in MS for sh in shape_list):
+        for ci, (M, (K, N, label)) in enumerate((M, sh) for M in ms for sh in shape_list):
             j = [sh[:2] for sh in shape_list].index((K, N))
             def launch_reps():
                 for r in range(reps):
@@ -402,6 +412,25 @@ def main():
                            torch.bfloat16)
         del layerf
 
+    # 2-bit and 3-bit weights (asymmetric, g = 128) at the Llama-3-8B shapes, decode M only.
+    lowbit = {}
+    if not args.no_lowbit:
+        for bits in (2, 3):
+            layerb = []
+            for K, N, label in shapes:
+                rng = np.random.default_rng(workloads.seed_for(f"bench-w{bits}", 0, K, N))
+                codes = rng.integers(0, 1 << bits, (K, N), dtype=np.uint8)
+                zeros = rng.integers(0, 1 << bits, (K // g, N), dtype=np.uint8)
+                scales = rng.uniform(0.01, 0.05, (K // g, N)).astype(np.float16).view(np.uint16)
+                layerb.append(mp.pack_weights_lowbit(bits, torch.from_numpy(codes).to(dev),
+                                                     dev_f16(scales),
+                                                     torch.from_numpy(zeros).to(dev), g))
+            lowbit[f"w{bits}a16_per_gemm"] = variant_pass(
+                layerb, shapes, mp.wlowbit_a16,
+                lambda M, K, N, g_, b=bits: gemm_bytes_lowbit(b, M, K, N, g_), torch.float16,
+                ms=(1, 16))
+            del layerb
+
     dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
         "metric": "W4A16 GEMM TFLOP/s and HBM GB/s (% roofline), Llama-3-8B shapes M=1/16/2048",
@@ -427,6 +456,7 @@ def main():
         "per_gemm": per_call,
         "w8a16_per_gemm": w8,
         "wfp8a16_qwen3_8b_per_gemm": fp8,
+        **lowbit,
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
