@@ -102,6 +102,17 @@ def _load():
     lib.oracle_pack_lowbit.restype = None
     lib.oracle_unpack_lowbit.argtypes = [i, u8p, u8p, i, i, i, i, u8p, u16p, u8p]
     lib.oracle_unpack_lowbit.restype = None
+    lib.oracle_attention_decode_kv8.argtypes = [u16p, u8p, u16p, u8p, u8p, u16p, u8p,
+                                                ctypes.POINTER(ctypes.c_int), i, i, i, i, i,
+                                                ctypes.c_float, i, u16p]
+    lib.oracle_attention_decode_kv8.restype = None
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_kv_block_bytes.argtypes = [i, i]
+    lib.oracle_kv_block_bytes.restype = ctypes.c_size_t
+    lib.oracle_kv_pack.argtypes = [u8p, u16p, u8p, u8p, u16p, u8p, i, i, i, i, ip, u8p]
+    lib.oracle_kv_pack.restype = None
+    lib.oracle_kv_unpack.argtypes = [u8p, ip, i, i, i, u8p, u16p, u8p, u8p, u16p, u8p]
+    lib.oracle_kv_unpack.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -413,6 +424,82 @@ def unpack_lowbit(bits: int, packed_codes: np.ndarray, packed_meta: np.ndarray, 
                              _ptr(scales, ctypes.c_uint16),
                              None if zeros is None else _ptr(zeros, ctypes.c_uint8))
     return codes, scales, zeros
+
+
+# ------------------------------------------------ attention decode (8-bit KV) --------
+
+def attention_decode_kv8(q_bits, kc, ks_bits, kz, vc, vs_bits, vz, lens, scale: float,
+                         dtype: str = "f16") -> np.ndarray:
+    """Decode attention over an 8-bit KV cache (user form; see the C source).
+
+    q_bits [B, Hq, D]; kc, vc [B, Tmax, Hkv, D] uint8; ks_bits, vs_bits [B, Tmax, Hkv]
+    fp16 bits; kz, vz [B, Tmax, Hkv] uint8; lens [B]; returns o bits [B, Hq, D].
+    """
+    lib = _load()
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    B, Hq, D = q_bits.shape
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    _, Tmax, Hkv, D2 = kc.shape
+    assert D2 == D and Hq % Hkv == 0
+    arrs = [np.ascontiguousarray(a, dtype=t) for a, t in
+            ((ks_bits, np.uint16), (kz, np.uint8), (vc, np.uint8), (vs_bits, np.uint16),
+             (vz, np.uint8))]
+    for a in (arrs[0], arrs[1], arrs[3], arrs[4]):
+        assert a.shape == (B, Tmax, Hkv)
+    assert arrs[2].shape == kc.shape
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    assert lens.shape == (B,) and (lens >= 0).all() and (lens <= Tmax).all()
+    o = np.empty((B, Hq, D), dtype=np.uint16)
+    lib.oracle_attention_decode_kv8(
+        _ptr(q_bits, ctypes.c_uint16), _ptr(kc, ctypes.c_uint8), _ptr(arrs[0], ctypes.c_uint16),
+        _ptr(arrs[1], ctypes.c_uint8), _ptr(arrs[2], ctypes.c_uint8),
+        _ptr(arrs[3], ctypes.c_uint16), _ptr(arrs[4], ctypes.c_uint8),
+        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), B, Hq, Hkv, D, Tmax,
+        ctypes.c_float(scale), _dtype_code(dtype), _ptr(o, ctypes.c_uint16))
+    return o
+
+
+def kv_block_bytes(Hkv: int, D: int) -> int:
+    return int(_load().oracle_kv_block_bytes(Hkv, D))
+
+
+def kv_pack(cache: np.ndarray, table_row, t0: int, kc, ks_bits, kz, vc, vs_bits, vz):
+    """Writes tokens t0 .. t0+n-1 (user form [n, Hkv, D] codes, [n, Hkv] scales/zeros) of
+    one sequence into `cache` (uint8, modified in place) through its block-table row."""
+    lib = _load()
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    n, Hkv, D = kc.shape
+    arrs = [np.ascontiguousarray(a, dtype=t) for a, t in
+            ((ks_bits, np.uint16), (kz, np.uint8), (vc, np.uint8), (vs_bits, np.uint16),
+             (vz, np.uint8))]
+    table_row = np.ascontiguousarray(table_row, dtype=np.int32)
+    assert cache.flags["C_CONTIGUOUS"] and cache.dtype == np.uint8
+    assert table_row.size * 64 >= t0 + n
+    assert (table_row[(t0 // 64):(t0 + n + 63) // 64] + 1).max() * kv_block_bytes(Hkv, D) <= cache.size
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_kv_pack(_ptr(kc, ctypes.c_uint8), _ptr(arrs[0], ctypes.c_uint16),
+                       _ptr(arrs[1], ctypes.c_uint8), _ptr(arrs[2], ctypes.c_uint8),
+                       _ptr(arrs[3], ctypes.c_uint16), _ptr(arrs[4], ctypes.c_uint8), n, t0,
+                       Hkv, D, table_row.ctypes.data_as(ip), _ptr(cache, ctypes.c_uint8))
+
+
+def kv_unpack(cache: np.ndarray, table_row, T: int, Hkv: int, D: int):
+    """Tokens 0 .. T-1 of one sequence: (kc, ks_bits, kz, vc, vs_bits, vz) in user form."""
+    lib = _load()
+    table_row = np.ascontiguousarray(table_row, dtype=np.int32)
+    kc = np.empty((T, Hkv, D), np.uint8)
+    vc = np.empty((T, Hkv, D), np.uint8)
+    ks = np.empty((T, Hkv), np.uint16)
+    vs = np.empty((T, Hkv), np.uint16)
+    kz = np.empty((T, Hkv), np.uint8)
+    vz = np.empty((T, Hkv), np.uint8)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_kv_unpack(_ptr(np.ascontiguousarray(cache), ctypes.c_uint8),
+                         table_row.ctypes.data_as(ip), T, Hkv, D, _ptr(kc, ctypes.c_uint8),
+                         _ptr(ks, ctypes.c_uint16), _ptr(kz, ctypes.c_uint8),
+                         _ptr(vc, ctypes.c_uint8), _ptr(vs, ctypes.c_uint16),
+                         _ptr(vz, ctypes.c_uint8))
+    return kc, ks, kz, vc, vs, vz
 
 
 def max_threads() -> int:

@@ -26,11 +26,12 @@
  * Parity status: every function here is pinned by CPU tests (tests/test_oracle.py; the
  * 8-bit functions by tests/test_oracle_w8.py, the FP8 ones by tests/test_oracle_fp8.py,
  * packing of ragged shapes by tests/test_oracle_ragged.py, the 2-bit and 3-bit functions by
- * tests/test_oracle_lowbit.py).
+ * tests/test_oracle_lowbit.py, attention decode by tests/test_oracle_attention.py).
  */
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -559,6 +560,132 @@ void oracle_unpack_lowbit(int bits, const uint8_t *packed_codes, const uint8_t *
                 zeros[(size_t)r * N + n] = (uint8_t)((e % 2) ? (b >> 4) : (b & 0xf));
             }
         }
+}
+
+/* ------------------------------------------- attention decode over an 8-bit KV cache --- */
+
+/*
+ * [TurboMind, Fig. 4 caption: the attention pipeline dequantizes the low-bit KV cache to
+ * FP16 by I2F scaling; Fig. 10 caption: KV is processed in 64-token macro-tiles].  The
+ * reading taken: 8-bit codes with one asymmetric scale (fp16) and zero (uint8) per
+ * (token, KV head), dequantized and rounded once to the activation format,
+ *   k[t][d] = round_act((kc[t][d] - kz[t]) * ks[t]),  v likewise,
+ * then exact attention for one query token per sequence (decode), grouped-query heads
+ * (query head h reads KV head h / (Hq / Hkv)):
+ *   score[t] = (sum_d q[h][d] * k[t][d]) * scale,  p = softmax over t < len[b],
+ *   o[h][d] = round_act(sum_t p[t] * v[t][d]),  all in fp64.  len[b] == 0 gives zeros.
+ * Layouts (user form): q, o [B][Hq][D] activation bits; kc, vc [B][Tmax][Hkv][D] uint8;
+ * ks, vs [B][Tmax][Hkv] fp16 bits; kz, vz [B][Tmax][Hkv] uint8; lens [B].
+ */
+void oracle_attention_decode_kv8(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
+                                 const uint8_t *kz, const uint8_t *vc, const uint16_t *vs,
+                                 const uint8_t *vz, const int *lens, int B, int Hq, int Hkv,
+                                 int D, int Tmax, float scale, int dtype, uint16_t *o) {
+    const int group = Hq / Hkv;
+    double *score = (double *)malloc(sizeof(double) * (size_t)(Tmax > 0 ? Tmax : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int b = 0; b < B; ++b) {
+        const int len = lens[b];
+        for (int h = 0; h < Hq; ++h) {
+            const int hk = h / group;
+            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;
+            double mx = -INFINITY;
+            for (int t = 0; t < len; ++t) {
+                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;
+                const double s_k = oracle_f16_to_f64(ks[row]);
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    double kd = act_to_f64(
+                        f64_to_act((double)((int)kc[row * D + d] - (int)kz[row]) * s_k, dtype), dtype);
+                    dot += act_to_f64(qh[d], dtype) * kd;
+                }
+                score[t] = dot * (double)scale;
+                if (score[t] > mx) mx = score[t];
+            }
+            double denom = 0.0;
+            for (int t = 0; t < len; ++t) {
+                score[t] = exp(score[t] - mx);
+                denom += score[t];
+            }
+            for (int d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int t = 0; t < len; ++t) {
+                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;
+                const double s_v = oracle_f16_to_f64(vs[row]);
+                const double pt = score[t] / denom;
+                for (int d = 0; d < D; ++d) {
+                    double vd = act_to_f64(
+                        f64_to_act((double)((int)vc[row * D + d] - (int)vz[row]) * s_v, dtype), dtype);
+                    acc[d] += pt * vd;
+                }
+            }
+            uint16_t *oh = o + ((size_t)b * Hq + h) * D;
+            for (int d = 0; d < D; ++d) oh[d] = f64_to_act(acc[d], dtype);
+        }
+    }
+    free(score);
+    free(acc);
+}
+
+/*
+ * Packed KV cache (restated from its specification in include/mpgemm.h).  Blocks of 64
+ * tokens of one sequence, all KV heads; block j of sequence b is cache block
+ * table[b][j].  Within a block, KV head h occupies HB = 128*D + 384 bytes at h*HB:
+ *   bytes [0, 64*D):      K codes of the 64 tokens, in the 8-bit weight layout of the
+ *                         D x 64 matrix K^T (k = d, n = token);
+ *   bytes [64*D, 128*D):  V codes, in the 8-bit weight layout of the 64 x D matrix V
+ *                         (k = token, n = d) -- V stored transposed for the matrix cores;
+ *   then K scales [64] fp16, V scales [64] fp16, K zeros [64] uint8, V zeros [64] uint8.
+ * D is a multiple of 64.
+ */
+size_t oracle_kv_block_bytes(int Hkv, int D) { return (size_t)Hkv * (128 * (size_t)D + 384); }
+
+/* Writes tokens t0 .. t0 + n - 1 of one sequence (user form kc, vc [n][Hkv][D]; ks, vs,
+ * kz, vz [n][Hkv]) into the cache through that sequence's block-table row. */
+void oracle_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, const uint8_t *vc,
+                    const uint16_t *vs, const uint8_t *vz, int n, int t0, int Hkv, int D,
+                    const int *table_row, uint8_t *cache) {
+    const size_t HB = 128 * (size_t)D + 384;
+    for (int i = 0; i < n; ++i) {
+        const int t = t0 + i, slot = t % 64;
+        uint8_t *blk = cache + (size_t)table_row[t / 64] * oracle_kv_block_bytes(Hkv, D);
+        for (int h = 0; h < Hkv; ++h) {
+            uint8_t *hb = blk + h * HB;
+            const size_t row = (size_t)i * Hkv + h;
+            for (int d = 0; d < D; ++d) {
+                hb[code8_byte_offset(d, slot, D)] = kc[row * D + d];
+                hb[64 * (size_t)D + code8_byte_offset(slot, d, 64)] = vc[row * D + d];
+            }
+            uint16_t *sc = (uint16_t *)(hb + 128 * (size_t)D);
+            sc[slot] = ks[row];
+            sc[64 + slot] = vs[row];
+            hb[128 * (size_t)D + 256 + slot] = kz[row];
+            hb[128 * (size_t)D + 320 + slot] = vz[row];
+        }
+    }
+}
+
+/* Reads tokens 0 .. T - 1 of one sequence back into the user form. */
+void oracle_kv_unpack(const uint8_t *cache, const int *table_row, int T, int Hkv, int D,
+                      uint8_t *kc, uint16_t *ks, uint8_t *kz, uint8_t *vc, uint16_t *vs,
+                      uint8_t *vz) {
+    const size_t HB = 128 * (size_t)D + 384;
+    for (int t = 0; t < T; ++t) {
+        const int slot = t % 64;
+        const uint8_t *blk = cache + (size_t)table_row[t / 64] * oracle_kv_block_bytes(Hkv, D);
+        for (int h = 0; h < Hkv; ++h) {
+            const uint8_t *hb = blk + h * HB;
+            const size_t row = (size_t)t * Hkv + h;
+            for (int d = 0; d < D; ++d) {
+                kc[row * D + d] = hb[code8_byte_offset(d, slot, D)];
+                vc[row * D + d] = hb[64 * (size_t)D + code8_byte_offset(slot, d, 64)];
+            }
+            const uint16_t *sc = (const uint16_t *)(hb + 128 * (size_t)D);
+            ks[row] = sc[slot];
+            vs[row] = sc[64 + slot];
+            kz[row] = hb[128 * (size_t)D + 256 + slot];
+            vz[row] = hb[128 * (size_t)D + 320 + slot];
+        }
+    }
 }
 
 int oracle_max_threads(void) {

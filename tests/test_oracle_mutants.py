@@ -97,6 +97,24 @@ MUTANTS_LOWBIT = {
 }
 
 
+MUTANTS_ATTENTION = {
+    "gqa_head_modulo": ("const int hk = h / group;", "const int hk = h % Hkv;"),
+    "no_softmax_scale": ("score[t] = dot * (double)scale;", "score[t] = dot;"),
+    "k_zero_sign": ("f64_to_act((double)((int)kc[row * D + d] - (int)kz[row]) * s_k, dtype)",
+                    "f64_to_act((double)((int)kz[row] - (int)kc[row * D + d]) * s_k, dtype)"),
+    "v_takes_k_scale": ("const double s_v = oracle_f16_to_f64(vs[row]);",
+                        "const double s_v = oracle_f16_to_f64(ks[row]);"),
+    "v_not_rounded": ("double vd = act_to_f64(\n                        f64_to_act((double)((int)vc[row * D + d] - (int)vz[row]) * s_v, dtype), dtype);",
+                      "double vd = (double)((int)vc[row * D + d] - (int)vz[row]) * s_v;"),
+    "last_token_dropped": ("            for (int t = 0; t < len; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double s_v",
+                           "            for (int t = 0; t < len - 1; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double s_v"),
+    "kv_v_not_transposed": ("hb[64 * (size_t)D + code8_byte_offset(slot, d, 64)] = vc[row * D + d];",
+                            "hb[64 * (size_t)D + code8_byte_offset(d, slot, D)] = vc[row * D + d];"),
+    "kv_zeros_swapped": ("hb[128 * (size_t)D + 256 + slot] = kz[row];",
+                         "hb[128 * (size_t)D + 320 + slot] = kz[row];"),
+}
+
+
 def _run_pins(text, before, after, pins, tmp_path):
     assert text.count(before) == 1, f"mutation anchor not found once: {before}"
     src = tmp_path / "mutant.c"
@@ -148,4 +166,11 @@ def test_ragged_pins_catch_planted_mistake(name, tmp_path):
 def test_lowbit_pins_catch_planted_mistake(name, tmp_path):
     before, after = MUTANTS_LOWBIT[name]
     res = _run_pins(open(SRC).read(), before, after, "test_oracle_lowbit.py", tmp_path)
+    assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_ATTENTION))
+def test_attention_pins_catch_planted_mistake(name, tmp_path):
+    before, after = MUTANTS_ATTENTION[name]
+    res = _run_pins(open(SRC).read(), before, after, "test_oracle_attention.py", tmp_path)
     assert res.returncode == 1, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"

@@ -17,6 +17,10 @@ FP8 codes: 64 * standard normal (float32), clipped to the format's largest finit
 cast to float8_e4m3fn / float8_e5m2 by torch (round to nearest even), taken as bytes; scales
 as above with the range divided by 64 (so weights are about normal with the scale's
 spread).  The FP8 workload has the shapes of the Qwen3-8B projections and bf16 activations.
+KV cache (attention decode): K and V codes uniform in [0, 255], zeros uniform in
+[100, 155], scales uniform in [0.005, 0.02] (values about uniform in [-2.5, 2.5]); queries
+standard normal in the activation format; heads and head size of Llama-3-8B (32 query
+heads, 8 KV heads, 128) unless a case says otherwise.
 Shapes are those of the layers the workloads are named after (Llama-3-8B, Llama-3-70B,
 Qwen3-32B projection matrices).  No dataset or checkpoint is read.
 """
@@ -151,6 +155,24 @@ def make_case_fp8(wl: Workload, M: int, K: int, N: int, fmt: str = "e4m3",
     x = activations(M, K, wl.dtype, seed + 1)
     return dict(x=x, codes=codes, scales=scales, zeros=None, group=wl.group, fmt=fmt,
                 symmetric=True, dtype=wl.dtype, M=M, K=K, N=N, seed=seed)
+
+
+def kv_cache(B: int, T: int, Hkv: int, D: int, seed: int):
+    """(kc, ks, kz, vc, vs, vz): codes [B, T, Hkv, D], scales (fp16 bits) and zeros
+    [B, T, Hkv] of an 8-bit KV cache in user form."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kc = rng.integers(0, 256, (B, T, Hkv, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (B, T, Hkv, D), dtype=np.uint8)
+    ks = rng.uniform(0.005, 0.02, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    vs = rng.uniform(0.005, 0.02, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    kz = rng.integers(100, 156, (B, T, Hkv), dtype=np.uint8)
+    vz = rng.integers(100, 156, (B, T, Hkv), dtype=np.uint8)
+    return kc, ks, kz, vc, vs, vz
+
+
+def queries(B: int, Hq: int, D: int, dtype: str, seed: int) -> np.ndarray:
+    """Query bits [B, Hq, D] in the activation format."""
+    return activations(B * Hq, D, dtype, seed).reshape(B, Hq, D)
 
 
 def make_case(wl: Workload, M: int, K: int, N: int, seed: int | None = None):
