@@ -319,6 +319,65 @@ int mpgemm_wlowbit_a16_config(int bits, const void *X, int dtype, const void *pa
                               int symmetric, void *Y, void *workspace, size_t workspace_bytes,
                               int config_id, void *stream);
 
+/*
+ * ---------------------------------------------------------------------------------
+ * Attention decode over an 8-bit KV cache.  [TurboMind, attention pipeline; Fig. 4 and
+ * Fig. 10 captions]: the low-bit KV cache is dequantized to 16-bit values by I2F scaling,
+ * V sits in a transposed tile layout for the matrix cores, KV streams in 64-token tiles.
+ * Quantized KV (the caller's form, per token):
+ *   kc, vc  uint8 [n][Hkv][D] codes;  ks, vs  fp16 [n][Hkv] scales;  kz, vz  uint8 [n][Hkv]
+ *   zeros: k[t][d] = (kc - kz[t]) * ks[t] rounded once to the activation format, v alike.
+ * Packed KV cache: an array of blocks of 64 tokens of one sequence, all KV heads, of
+ * mpgemm_kv_block_bytes(Hkv, D) = Hkv * (128*D + 384) bytes each; block j of sequence b is
+ * block block_table[b*table_stride + j] (token t in block t/64, slot t%64).  KV head h of a
+ * block occupies HB = 128*D + 384 bytes at h*HB:
+ *   [0, 64*D)        K codes in the 8-bit weight layout (above) of the D x 64 matrix K^T
+ *                    (k = d, n = slot), i.e. 16-slot strips of 64-deep 1 KiB tiles;
+ *   [64*D, 128*D)    V codes in the 8-bit weight layout of the 64 x D matrix V (k = slot,
+ *                    n = d): V transposed, so 16 values of d x 8 consecutive tokens form
+ *                    one matrix-core operand;
+ *   then K scales [64] fp16, V scales [64] fp16, K zeros [64] uint8, V zeros [64] uint8.
+ * D is 64, 128 or 256; Hq is a multiple of Hkv with Hq/Hkv <= 16.
+ */
+
+/* Bytes of one cache block (0 if Hkv or D is unsupported). */
+size_t mpgemm_kv_block_bytes(int Hkv, int D);
+
+/*
+ * Writes tokens t0 .. t0 + n_tokens - 1 of one sequence (the caller's form above, device
+ * pointers; ks, vs, table_row 4-byte aligned, kc, vc, cache 16-byte aligned) into the cache
+ * through that sequence's block-table row (table_len entries; t0 + n_tokens <= 64 *
+ * table_len).  Entries outside [0, num_blocks) are skipped.  Prefill and every decode
+ * step's append are calls of this one function.
+ */
+int mpgemm_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, const uint8_t *vc,
+                   const uint16_t *vs, const uint8_t *vz, int n_tokens, int t0, int Hkv, int D,
+                   const int *table_row, int table_len, int num_blocks, void *cache,
+                   void *stream);
+
+/* Device workspace (bytes) mpgemm_attention_decode_kv8 needs: fp32 partials when the
+ * block range of a sequence is split over several waves; 0 otherwise. */
+size_t mpgemm_attention_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len);
+
+/*
+ * One decode step of attention for B sequences, one query token each:
+ *   o[b][h] = sum_t p[t] v[t],  p = softmax_t<lens[b] (scale * q[b][h] . k[t]),
+ *   with query head h reading KV head h / (Hq / Hkv); fp32 scores, softmax and
+ *   accumulation (the probabilities, times V's scale, enter the matrix cores as 16-bit
+ *   values), o rounded to the activation format.  lens[b] == 0 gives zeros.
+ *   Q, O         [B][Hq][D] fp16 or bf16 bits per dtype (16-byte aligned)
+ *   cache        num_blocks packed blocks; block_table [B][table_stride] int32; lens [B]
+ *                int32 (device), each <= max_len (a host bound that sizes the launch);
+ *                table entries outside [0, num_blocks) are skipped
+ *   workspace    mpgemm_attention_workspace_bytes(B, Hq, Hkv, D, max_len) bytes (may be
+ *                NULL when that is 0); its contents need no initialization
+ */
+int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int num_blocks,
+                                const int *block_table, int table_stride, const int *lens,
+                                int B, int Hq, int Hkv, int D, int max_len, float scale,
+                                void *O, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *mpgemm_status_string(int status);
 

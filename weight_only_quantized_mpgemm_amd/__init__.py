@@ -56,6 +56,12 @@ SIGNATURES = {
     "mpgemm_w8a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
     "mpgemm_wfp8a16": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "mpgemm_kv_block_bytes": (_sz, [_i, _i]),
+    "mpgemm_kv_pack": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _vp,
+                            _vp]),
+    "mpgemm_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "mpgemm_attention_decode_kv8": (_i, [_vp, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i,
+                                         ctypes.c_float, _vp, _vp, _sz, _vp]),
     "mpgemm_packed_code_bytes_lowbit": (_sz, [_i, _i, _i]),
     "mpgemm_pack_weights_lowbit": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "mpgemm_unpack_lowbit": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
@@ -391,3 +397,87 @@ def wfp8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = N
     """Y = X @ (fp8(W) * s) for weights packed by pack_weights_fp8 (mpgemm_wfp8a16; the
     _config variant when config != 0).  Arguments as for w4a16."""
     return _gemm("fp8", x, packed, out, config, workspace)
+
+
+# ------------------------------------------------- attention decode (8-bit KV cache) --
+
+# Attention partials need no initialization, but must not share the GEMM workspace (whose
+# split-K counters have to stay zero between calls): a cache of their own.
+_ATTN_WORKSPACES: dict[int, torch.Tensor] = {}
+
+
+def _attention_workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _ATTN_WORKSPACES.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise MpgemmError(-4, f"allocating a {nbytes}-byte attention workspace during "
+                                  "graph capture (make one eager call of this shape first)")
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ATTN_WORKSPACES[idx] = ws
+    return ws
+
+
+def kv_block_bytes(Hkv: int, D: int) -> int:
+    """Bytes of one 64-token cache block holding every KV head (mpgemm_kv_block_bytes)."""
+    return int(lib().mpgemm_kv_block_bytes(Hkv, D))
+
+
+def kv_pack(cache: torch.Tensor, table_row: torch.Tensor, t0: int, kc: torch.Tensor,
+            ks: torch.Tensor, kz: torch.Tensor, vc: torch.Tensor, vs: torch.Tensor,
+            vz: torch.Tensor) -> None:
+    """Writes tokens t0 .. t0+n-1 of one sequence into `cache` (mpgemm_kv_pack).
+
+    kc, vc uint8 [n, Hkv, D]; ks, vs float16 [n, Hkv]; kz, vz uint8 [n, Hkv]; table_row
+    int32 [table_len] (device); cache uint8 [num_blocks * kv_block_bytes(Hkv, D)].
+    """
+    n, Hkv, D = kc.shape
+    for t, dt, shape, name in ((kc, torch.uint8, (n, Hkv, D), "kc"), (vc, torch.uint8, (n, Hkv, D), "vc"),
+                               (ks, torch.float16, (n, Hkv), "ks"), (vs, torch.float16, (n, Hkv), "vs"),
+                               (kz, torch.uint8, (n, Hkv), "kz"), (vz, torch.uint8, (n, Hkv), "vz")):
+        _need(t, dt, shape, name)
+    _need(table_row, torch.int32, (table_row.numel(),), "table_row")
+    bb = kv_block_bytes(Hkv, D)
+    if bb == 0:
+        raise MpgemmError(-2, "kv_pack")
+    _need(cache, torch.uint8, (cache.numel(),), "cache")
+    st = lib().mpgemm_kv_pack(_ptr(kc), _ptr(ks), _ptr(kz), _ptr(vc), _ptr(vs), _ptr(vz), n, t0,
+                              Hkv, D, _ptr(table_row), table_row.numel(), cache.numel() // bb,
+                              _ptr(cache), _stream(cache.device))
+    _check(st, "mpgemm_kv_pack")
+
+
+def attention_decode_kv8(q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor,
+                         lens: torch.Tensor, Hkv: int, max_len: int, scale: float,
+                         out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step of attention over a packed 8-bit KV cache
+    (mpgemm_attention_decode_kv8).  q float16/bfloat16 [B, Hq, D]; block_table int32
+    [B, table_stride]; lens int32 [B] (each <= max_len); returns [B, Hq, D]."""
+    B, Hq, D = q.shape
+    act = _act_code(q.dtype)
+    _need(q, q.dtype, (B, Hq, D), "q")
+    _need(block_table, torch.int32, (B, block_table.shape[1] if block_table.dim() == 2 else -1),
+          "block_table")
+    _need(lens, torch.int32, (B,), "lens")
+    bb = kv_block_bytes(Hkv, D)
+    if bb == 0:
+        raise MpgemmError(-2, "attention_decode_kv8")
+    _need(cache, torch.uint8, (cache.numel(),), "cache")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
+    _need(out, q.dtype, (B, Hq, D), "out")
+    ws = int(lib().mpgemm_attention_workspace_bytes(B, Hq, Hkv, D, max_len))
+    if workspace is None:
+        workspace = _attention_workspace(q.device, ws)
+    elif ws:
+        _need(workspace, torch.uint8, (workspace.numel(),), "workspace")
+        ws = workspace.numel()
+    st = lib().mpgemm_attention_decode_kv8(_ptr(q), act, _ptr(cache), cache.numel() // bb,
+                                           _ptr(block_table), block_table.shape[1], _ptr(lens),
+                                           B, Hq, Hkv, D, max_len, ctypes.c_float(scale),
+                                           _ptr(out), _ptr(workspace), ws, _stream(q.device))
+    _check(st, "mpgemm_attention_decode_kv8")
+    return out

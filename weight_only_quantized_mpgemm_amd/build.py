@@ -25,7 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmpgemm.so")
 SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_ring.hip",
-           "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip", "gemm_prefill_x32_fp8.hip"]
+           "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip", "gemm_prefill_x32_fp8.hip",
+           "attention.hip"]
 HEADERS = ["device.hpp", "kernels.hpp", "prefill_x32.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -3,6 +3,7 @@
 //
 // Source of the method: "LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind"
 // (arXiv 2508.15601): an offline packing step and an online mixed-precision GEMM.
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -367,6 +368,106 @@ int mpgemm_wlowbit_a16(int bits, const void *X, int dtype, const void *packed_co
     return mpgemm_wlowbit_a16_config(bits, X, dtype, packed_codes, packed_meta, M, N, K, group,
                                      symmetric, Y, workspace, workspace_bytes, kConfigSelect,
                                      stream);
+}
+
+// ------------------------------------------------------------ attention decode ------
+
+}  // extern "C"
+
+namespace {
+
+bool kv_shape_ok(int Hkv, int D) { return Hkv >= 1 && Hkv <= 1024 && (D == 64 || D == 128 || D == 256); }
+
+// Blocks per split and splits per (sequence, KV head): enough waves to cover the CUs
+// (about 1024), as few splits as that allows.  MPGEMM_ATTN_BPS overrides the blocks per
+// split (tuning sweeps).
+void attn_plan(int B, int Hkv, int max_len, int *bps, int *splits) {
+    const int64_t nblk = (max_len + 63) / 64;
+    const int64_t total = (int64_t)B * Hkv * nblk;
+    int64_t per = (total + 1023) / 1024;
+    if (per < 1) per = 1;
+    if (const char *env = getenv("MPGEMM_ATTN_BPS")) {
+        const int v = atoi(env);
+        if (v >= 1) per = v;
+    }
+    *bps = (int)per;
+    *splits = nblk > 0 ? (int)((nblk + per - 1) / per) : 1;
+}
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t mpgemm_kv_block_bytes(int Hkv, int D) {
+    return kv_shape_ok(Hkv, D) ? (size_t)Hkv * (128 * (size_t)D + 384) : 0;
+}
+
+int mpgemm_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, const uint8_t *vc,
+                   const uint16_t *vs, const uint8_t *vz, int n_tokens, int t0, int Hkv, int D,
+                   const int *table_row, int table_len, int num_blocks, void *cache,
+                   void *stream) {
+    if (!kv_shape_ok(Hkv, D)) return MPGEMM_ERR_UNSUPPORTED;
+    if (n_tokens < 0 || t0 < 0 || table_len < 0 || num_blocks < 0) return MPGEMM_ERR_INVALID_ARG;
+    if ((int64_t)t0 + n_tokens > (int64_t)table_len * 64) return MPGEMM_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * Hkv >= kIndexLimit) return MPGEMM_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return MPGEMM_OK;
+    if (!kc || !ks || !kz || !vc || !vs || !vz || !table_row || !cache) return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(kc) || !aligned16(vc) || !aligned4(ks) || !aligned4(vs) || !aligned4(table_row) ||
+        !aligned16(cache))
+        return MPGEMM_ERR_ALIGNMENT;
+    return hip_status(mpgemm::launch_kv_pack(kc, ks, kz, vc, vs, vz, n_tokens, t0, Hkv, D,
+                                             table_row, table_len, num_blocks, cache,
+                                             (hipStream_t)stream));
+}
+
+size_t mpgemm_attention_workspace_bytes(int B, int Hq, int Hkv, int D, int max_len) {
+    if (B < 0 || max_len < 0 || !kv_shape_ok(Hkv, D) || Hq < Hkv || Hq % Hkv) return 0;
+    int bps, splits;
+    attn_plan(B, Hkv, max_len, &bps, &splits);
+    return mpgemm::attn_part_bytes(B, Hq, D, splits);
+}
+
+int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int num_blocks,
+                                const int *block_table, int table_stride, const int *lens, int B,
+                                int Hq, int Hkv, int D, int max_len, float scale, void *O,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
+    if (B < 0 || max_len < 0 || num_blocks < 0 || table_stride < 0 || Hkv < 1 || Hq < 1)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (!kv_shape_ok(Hkv, D) || Hq % Hkv != 0 || Hq / Hkv > 16) return MPGEMM_ERR_UNSUPPORTED;
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return MPGEMM_ERR_INVALID_ARG;
+    if ((int64_t)B * Hq * D >= kIndexLimit || (int64_t)B * table_stride >= kIndexLimit)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (B == 0) return MPGEMM_OK;
+    if (!Q || !O || !lens || (max_len > 0 && (!cache || !block_table))) return MPGEMM_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(O) || !aligned4(lens) || (cache && !aligned16(cache)) ||
+        (block_table && !aligned4(block_table)))
+        return MPGEMM_ERR_ALIGNMENT;
+    mpgemm::AttnArgs a;
+    attn_plan(B, Hkv, max_len, &a.bps, &a.splits);
+    const size_t need = mpgemm::attn_part_bytes(B, Hq, D, a.splits);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return MPGEMM_ERR_WORKSPACE;
+    a.Q = (const uint16_t *)Q;
+    a.cache = (const uint8_t *)cache;
+    a.num_blocks = cache ? num_blocks : 0;
+    a.table = block_table;
+    a.table_stride = block_table ? table_stride : 0;
+    a.lens = lens;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.act = dtype == MPGEMM_BF16 ? mpgemm::kBF16 : mpgemm::kF16;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.O = (uint16_t *)O;
+    a.part = (float *)workspace;
+    if (getenv("MPGEMM_LOG"))
+        fprintf(stderr, "mpgemm: attention B=%d Hq=%d Hkv=%d D=%d max_len=%d -> %d splits of %d blocks\n",
+                B, Hq, Hkv, D, max_len, a.splits, a.bps);
+    return hip_status(mpgemm::launch_attention_kv8(a, (hipStream_t)stream));
 }
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {

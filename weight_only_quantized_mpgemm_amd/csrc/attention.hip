@@ -1,0 +1,340 @@
+// Decode attention over an 8-bit KV cache for gfx950, and the KV-cache packer.
+//
+// [TurboMind, attention pipeline; Fig. 4 and Fig. 10 captions]: the low-bit KV cache is
+// dequantized to 16-bit values by I2F conversion and scaling, V is kept in a transposed
+// (column-major) tile layout for the matrix cores, and KV is streamed in 64-token
+// macro-tiles.  Source: "LMDeploy Accelerates Mixed-Precision LLM Inference with
+// TurboMind" (arXiv 2508.15601).
+//
+// Cache layout (include/mpgemm.h): 64-token blocks holding every KV head; head h of a block
+// is HB = 128 D + 384 bytes: K codes as the 8-bit weight packing of K^T (k = d, n = token),
+// V codes as that of V (k = token, n = d), then K and V scales (fp16) and zeros (uint8).
+//
+// Design for MI355X (one 64-lane wave per (sequence, KV head, split of the blocks)):
+//   - S = K Q^T on 16x16x32 MFMAs: A = dequantized K (rows = 16 tokens of a strip, k = d;
+//     each lane's 16-byte load of a K tile is exactly two MFMA A operands, as for weights),
+//     B = the G <= 16 query heads of the KV head (columns), loaded once;
+//   - online softmax in the exp2 domain.  Every score and every output a lane holds
+//     belongs to head lane % 16, so rescaling is lane-local; block maxima and sums need
+//     two cross-lane exchanges;
+//   - O += V^T P' on MFMAs: A = V codes (rows = 16 values of d, k = tokens -- the
+//     transposed layout), B = P' (columns = heads, k = tokens) through 2 KiB of LDS.  V's
+//     per-token scale is folded into P' = round(p * s_v), and its zero point into one
+//     correction per head, sum_t P'_t z_t, subtracted at the end -- so V's codes enter the
+//     MFMA as exact integers (a byte permute and one exact packed add);
+//   - splits of the block range write unnormalized partials (O, max, sum) to a workspace;
+//     a second kernel combines them.  One split writes the output directly;
+//   - a block-table entry outside the cache is skipped (no access); every load goes
+//     through a buffer descriptor bounded to its block.
+#include "kernels.hpp"
+
+namespace mpgemm {
+
+namespace {
+
+constexpr int kKvTokens = 64;                  // tokens per cache block
+constexpr int kPartPad = 4;                    // partial record: D values, max, sum, pad
+
+__device__ __forceinline__ float xor_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float xor_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+template <int ACT>
+__device__ __forceinline__ uint16_t round_act(float x) {
+    if constexpr (ACT == kF16) return bitcast<uint16_t>((_Float16)x);
+    else return (uint16_t)pack_bf16x2(x, 0.f);
+}
+template <int ACT>
+__device__ __forceinline__ float act_to_f32(uint16_t h) {
+    if constexpr (ACT == kF16) return (float)bitcast<_Float16>(h);
+    else return __uint_as_float((uint32_t)h << 16);
+}
+
+// Eight V codes (two words, k ascending) as exact 16-bit integers in MFMA operand order.
+template <int ACT>
+__device__ __forceinline__ u32x4_t v_codes_exact(uint32_t w0, uint32_t w1) {
+    u32x4_t r;
+    if constexpr (ACT == kF16) {
+        // (1024 + v) pairs by a byte permute against 0x64, then - 1024 exactly
+        const half2_t m1024 = bitcast<half2_t>(0xE400E400u);
+        r[0] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + m1024);
+        r[1] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)) + m1024);
+        r[2] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)) + m1024);
+        r[3] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u)) + m1024);
+    } else {
+        r[0] = pack_bf16x2(ubyte(w0, 0), ubyte(w0, 1));
+        r[1] = pack_bf16x2(ubyte(w0, 2), ubyte(w0, 3));
+        r[2] = pack_bf16x2(ubyte(w1, 0), ubyte(w1, 1));
+        r[3] = pack_bf16x2(ubyte(w1, 2), ubyte(w1, 3));
+    }
+    return r;
+}
+
+template <int ACT, int D>
+__global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
+    const uint16_t *__restrict__ Q, const uint8_t *__restrict__ cache, int num_blocks,
+    const int *__restrict__ table, int table_stride, const int *__restrict__ lens, int Hq,
+    int Hkv, int bps, int splits, float scale_log2, uint16_t *__restrict__ O,
+    float *__restrict__ part) {
+    constexpr int DS = D / 32;                 // 32-deep k steps of Q K^T
+    constexpr int KT = D / 64;                 // 64-deep K tiles per 16-token strip
+    constexpr int VS = D / 16;                 // 16-row strips of V^T
+    constexpr uint32_t HB = 128u * D + 384u;   // bytes of one KV head in a block
+    __shared__ u32x4_t pl4[16 * kKvTokens / 8];   // P'[head][token], 16-bit values
+    u32x2_t *const pl = reinterpret_cast<u32x2_t *>(pl4);
+
+    const int lane = threadIdx.x;
+    const int split = blockIdx.x % splits;
+    const int bh = blockIdx.x / splits;
+    const int hk = bh % Hkv, b = bh / Hkv;
+    const int G = Hq / Hkv;
+    const int g = lane & 15;                   // this lane's head column
+    const int q4 = lane >> 4;
+    const int len = min(lens[b], table_stride * kKvTokens);
+    const int nblk = (len + kKvTokens - 1) / kKvTokens;
+    const int j0 = split * bps, j1 = min(nblk, j0 + bps);
+
+    // B operand of Q K^T: head g, k = 32 s + 8 (lane / 16) .. +7 (heads past G: zeros).
+    u32x4_t qb[DS];
+    {
+        const uint16_t *qrow = Q + ((size_t)b * Hq + hk * G + min(g, G - 1)) * D;
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+            qb[s] = g < G ? *reinterpret_cast<const u32x4_t *>(qrow + 32 * s + 8 * q4)
+                          : u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    f32x4_t oacc[VS];
+#pragma unroll
+    for (int i = 0; i < VS; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f, c = 0.f;
+
+    for (int j = j0; j < j1; ++j) {
+        const int pb = table[(size_t)b * table_stride + j];
+        if (pb < 0 || pb >= num_blocks) continue;
+        const uint8_t *hbase = cache + (size_t)pb * HB * Hkv + (size_t)hk * HB;
+        const rsrc_t rs = make_rsrc(hbase, HB);
+        // K: strip s, tile kt at (s KT + kt) KiB; lane's token column 16 s + lane % 16.
+        u32x4_t kw[4][KT];
+        uint32_t ksw[4], kzw[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                kw[s][kt] = buf_load_b128(rs, lane * 16u, (s * KT + kt) * 1024u);
+            const uint32_t tok = 16 * s + g;
+            ksw[s] = buf_load_b32(rs, 128u * D + (tok & ~1u) * 2u, 0);
+            kzw[s] = buf_load_b32(rs, 128u * D + 256u + (tok & ~3u), 0);
+        }
+        // V: strip sd at 64 D + sd KiB.  V scales / zeros of this lane's score tokens
+        // 16 s + 4 (lane / 16) + r.
+        u32x4_t vw[VS];
+#pragma unroll
+        for (int sd = 0; sd < VS; ++sd) vw[sd] = buf_load_b128(rs, lane * 16u, 64u * D + sd * 1024u);
+        u32x2_t vsw[4];
+        uint32_t vzw[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t tok = 16 * s + 4 * q4;
+            vsw[s] = buf_load_b64(rs, 128u * D + 128u + tok * 2u, 0);
+            vzw[s] = buf_load_b32(rs, 128u * D + 320u + tok, 0);
+        }
+
+        // S = K Q^T, strip by strip; lane holds tokens 16 s + 4 (lane / 16) + r of head g.
+        f32x4_t sacc[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t tok = 16 * s + g;
+            const uint16_t ks = (uint16_t)(ksw[s] >> ((tok & 1) * 16));
+            const uint32_t kz = (kzw[s] >> ((tok & 3) * 8)) & 0xFFu;
+            const typename Dq8<ACT>::type dq = Dq8<ACT>::make(ks, kz);
+            sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    sacc[s] = mfma16x16x32<ACT>(Dq8<ACT>::pair(kw[s][kt][2 * h], kw[s][kt][2 * h + 1], dq),
+                                                qb[2 * kt + h], sacc[s]);
+        }
+        // Online softmax (log2 domain) with masking of tokens past len.
+        float sc[4][4];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = j * kKvTokens + 16 * s + 4 * q4 + r;
+                sc[s][r] = t < len ? sacc[s][r] * scale_log2 : -INFINITY;
+                bmax = fmaxf(bmax, sc[s][r]);
+            }
+        bmax = xor_max(bmax);
+        const float mn = fmaxf(m, bmax);
+        if (mn == -INFINITY) continue;         // nothing unmasked yet (uniform)
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        c *= alpha;
+        float psum = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint16_t pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2f(sc[s][r] - mn);
+                psum += p;
+                const float vscale = (float)bitcast<_Float16>((uint16_t)(vsw[s][r >> 1] >> ((r & 1) * 16)));
+                pr[r] = round_act<ACT>(p * vscale);
+                c += act_to_f32<ACT>(pr[r]) * (float)((vzw[s] >> (8 * r)) & 0xFFu);
+            }
+            pl[(g * kKvTokens + 16 * s + 4 * q4) / 4] =
+                u32x2_t{(uint32_t)pr[0] | ((uint32_t)pr[1] << 16), (uint32_t)pr[2] | ((uint32_t)pr[3] << 16)};
+        }
+        l = l * alpha + xor_sum(psum);
+#pragma unroll
+        for (int sd = 0; sd < VS; ++sd) oacc[sd] *= alpha;
+        __syncthreads();
+        // O += V^T P': k = tokens 32 u + 8 (lane / 16) .. +7 of head g.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const u32x4_t pbv = pl4[(g * kKvTokens + 32 * u + 8 * q4) / 8];
+#pragma unroll
+            for (int sd = 0; sd < VS; ++sd)
+                oacc[sd] = mfma16x16x32<ACT>(v_codes_exact<ACT>(vw[sd][2 * u], vw[sd][2 * u + 1]), pbv,
+                                             oacc[sd]);
+        }
+        __syncthreads();
+    }
+    c = xor_sum(c);
+
+    // Output rows d = 16 sd + 4 (lane / 16) + r of head g.
+    const int h = hk * G + g;
+    if (splits == 1) {
+        if (g >= G) return;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t *orow = O + ((size_t)b * Hq + h) * D;
+#pragma unroll
+        for (int sd = 0; sd < VS; ++sd) {
+            const f32x4_t v = (oacc[sd] - c) * inv;
+            *reinterpret_cast<u32x2_t *>(orow + 16 * sd + 4 * q4) = round4<ACT>(v);
+        }
+        return;
+    }
+    if (g >= G) return;
+    float *rec = part + (((size_t)b * Hq + h) * splits + split) * (D + kPartPad);
+#pragma unroll
+    for (int sd = 0; sd < VS; ++sd)
+        *reinterpret_cast<f32x4_t *>(rec + 16 * sd + 4 * q4) = oacc[sd] - c;
+    if (q4 == 0) {
+        rec[D] = m;
+        rec[D + 1] = l;
+    }
+}
+
+// out[b][h] = sum_i w_i O_i / sum_i w_i l_i, w_i = 2^(m_i - max m).
+template <int ACT, int D>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ part, int splits,
+                                                          uint16_t *__restrict__ O) {
+    const size_t bh = blockIdx.x;
+    const float *rec = part + bh * splits * (D + kPartPad);
+    float mx = -INFINITY;
+    for (int i = 0; i < splits; ++i) mx = fmaxf(mx, rec[i * (D + kPartPad) + D]);
+    float acc[D / 64];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+    float lsum = 0.f;
+    if (mx != -INFINITY) {
+        for (int i = 0; i < splits; ++i) {
+            const float *r = rec + i * (D + kPartPad);
+            const float w = exp2f(r[D] - mx);
+            lsum += w * r[D + 1];
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) acc[e] += w * r[threadIdx.x + 64 * e];
+        }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) O[bh * D + threadIdx.x + 64 * e] = round_act<ACT>(acc[e] * inv);
+}
+
+// One thread per (token, KV head): writes its K and V codes, scales and zeros.
+__global__ void kv_pack_kernel(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks,
+                               const uint8_t *__restrict__ kz, const uint8_t *__restrict__ vc,
+                               const uint16_t *__restrict__ vs, const uint8_t *__restrict__ vz,
+                               int n, int t0, int Hkv, int D, const int *__restrict__ table_row,
+                               int table_len, int num_blocks, uint8_t *__restrict__ cache) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n * Hkv) return;
+    const int tl = i / Hkv, h = i % Hkv;
+    const int t = t0 + tl, slot = t % kKvTokens, jb = t / kKvTokens;
+    if (jb >= table_len) return;
+    const int pb = table_row[jb];
+    if (pb < 0 || pb >= num_blocks) return;
+    const size_t HB = 128 * (size_t)D + 384;
+    uint8_t *hb = cache + (size_t)pb * HB * Hkv + (size_t)h * HB;
+    const size_t row = (size_t)tl * Hkv + h;
+    for (int d = 0; d < D; ++d) {
+        // K^T: k = d, n = slot (16 x 64 tiles, K = D rows); V: k = slot, n = d (K = 64).
+        const int kk = d % 64, vk = slot % 64;
+        const size_t koff = ((size_t)(slot / 16) * (D / 64) + d / 64) * 1024 +
+                            (size_t)(slot % 16 + 16 * ((kk % 32) / 8)) * 16 + (kk / 32) * 8 + kk % 8;
+        const size_t voff = (size_t)(d / 16) * 1024 + (size_t)(d % 16 + 16 * ((vk % 32) / 8)) * 16 +
+                            (vk / 32) * 8 + vk % 8;
+        hb[koff] = kc[row * D + d];
+        hb[64 * (size_t)D + voff] = vc[row * D + d];
+    }
+    uint16_t *sc = reinterpret_cast<uint16_t *>(hb + 128 * (size_t)D);
+    sc[slot] = ks[row];
+    sc[kKvTokens + slot] = vs[row];
+    hb[128 * (size_t)D + 256 + slot] = kz[row];
+    hb[128 * (size_t)D + 320 + slot] = vz[row];
+}
+
+template <int ACT, int D>
+void launch_attn(const AttnArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
+    attn_decode_kv8_kernel<ACT, D><<<grid, dim3(64), 0, stream>>>(
+        a.Q, a.cache, a.num_blocks, a.table, a.table_stride, a.lens, a.Hq, a.Hkv, a.bps,
+        a.splits, a.scale_log2, a.O, a.part);
+    if (a.splits > 1)
+        attn_combine_kernel<ACT, D><<<dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, stream>>>(
+            a.part, a.splits, a.O);
+}
+
+template <int ACT>
+void launch_attn_act(const AttnArgs &a, hipStream_t stream) {
+    switch (a.D) {
+        case 64: launch_attn<ACT, 64>(a, stream); break;
+        case 256: launch_attn<ACT, 256>(a, stream); break;
+        default: launch_attn<ACT, 128>(a, stream); break;
+    }
+}
+
+}  // namespace
+
+size_t attn_part_bytes(int B, int Hq, int D, int splits) {
+    return splits > 1 ? (size_t)B * Hq * splits * (D + kPartPad) * sizeof(float) : 0;
+}
+
+hipError_t launch_attention_kv8(const AttnArgs &a, hipStream_t stream) {
+    a.act == kBF16 ? launch_attn_act<kBF16>(a, stream) : launch_attn_act<kF16>(a, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz,
+                          const uint8_t *vc, const uint16_t *vs, const uint8_t *vz, int n, int t0,
+                          int Hkv, int D, const int *table_row, int table_len, int num_blocks,
+                          void *cache, hipStream_t stream) {
+    const int threads = 128;
+    const int items = n * Hkv;
+    if (items > 0)
+        kv_pack_kernel<<<(items + threads - 1) / threads, threads, 0, stream>>>(
+            kc, ks, kz, vc, vs, vz, n, t0, Hkv, D, table_row, table_len, num_blocks,
+            (uint8_t *)cache);
+    return hipGetLastError();
+}
+
+}  // namespace mpgemm

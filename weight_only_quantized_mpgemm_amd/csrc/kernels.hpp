@@ -77,6 +77,28 @@ hipError_t launch_prefill_x32_u8(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
+// Decode attention over an 8-bit KV cache (attention.hip).
+struct AttnArgs {
+    const uint16_t *Q;          // [B][Hq][D] activation bits
+    const uint8_t *cache;       // packed KV cache: num_blocks blocks
+    int num_blocks;
+    const int *table;           // [B][table_stride] block indices
+    int table_stride;
+    const int *lens;            // [B] context lengths
+    int B, Hq, Hkv, D;
+    int act;
+    int bps, splits;            // blocks per split, splits per (sequence, KV head)
+    float scale_log2;           // softmax scale * log2(e)
+    uint16_t *O;                // [B][Hq][D]
+    float *part;                // split partials (splits > 1)
+};
+size_t attn_part_bytes(int B, int Hq, int D, int splits);
+hipError_t launch_attention_kv8(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz,
+                          const uint8_t *vc, const uint16_t *vs, const uint8_t *vz, int n, int t0,
+                          int Hkv, int D, const int *table_row, int table_len, int num_blocks,
+                          void *cache, hipStream_t stream);
+
 // Writes zeros to Y (the K == 0 case).
 hipError_t launch_fill_zero(uint16_t *Y, size_t count, hipStream_t stream);
 
