@@ -33,7 +33,10 @@ same with FP8 (E4M3) weights at the Qwen3-8B projection shapes (QKV 4096x6144, O
 gate_up 4096x24576, down 12288x4096) and bf16 activations (mpgemm_wfp8a16; one byte per
 code, no zeros).  `w2a16_per_gemm` and `w3a16_per_gemm` do it with 2-bit and 3-bit weights
 (mpgemm_wlowbit_a16) at the Llama-3-8B shapes for M = 1 and 16, against the HBM roofline.
-None of these is part of `value`.
+`attention_kv8_decode` times mpgemm_attention_decode_kv8 (Llama-3-8B heads, one query token
+per sequence, batch x context 1 x 8192, 16 x 2048, 64 x 2048, 128 x 4096) against the HBM
+roofline (bytes: K and V codes, scales and zeros, Q, O, the block table).  None of these is
+part of `value`.
 """
 from __future__ import annotations
 
@@ -149,6 +152,8 @@ def main():
                     help="skip the W8A16 per-GEMM pass (8-bit weights, same shapes)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8-weight per-GEMM pass (E4M3, Qwen3-8B shapes)")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the attention-decode pass (8-bit KV cache)")
     ap.add_argument("--no-lowbit", action="store_true",
                     help="skip the 2-bit and 3-bit per-GEMM passes (Llama-3-8B shapes, M=1,16)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -431,6 +436,52 @@ def main():
                 ms=(1, 16))
             del layerb
 
+    # Decode attention over the packed 8-bit KV cache (Llama-3-8B heads: 32 query, 8 KV, 128
+    # wide), one query token per sequence.  Calls rotate through block tables that point
+    # into a pool of blocks larger than the Infinity Cache, so KV bytes come from HBM.
+    attn = []
+    if not args.no_attention:
+        Hq, Hkv, D = 32, 8, 128
+        bb = mp.kv_block_bytes(Hkv, D)
+        nblocks = int(args.pool_gb * 1e9 // bb)
+        cache = torch.randint(0, 256, (nblocks * bb,), dtype=torch.uint8, device=dev)
+        # valid fp16 scales (0.01) in every block's scale fields
+        blk = cache.view(nblocks, Hkv, bb // Hkv)
+        blk[:, :, 128 * D:128 * D + 256].view(torch.float16).fill_(0.01)
+        reps = 10
+        for B, T in ((1, 8192), (16, 2048), (64, 2048), (128, 4096)):
+            nb = (T + 63) // 64
+            ntab = min(reps, nblocks // (B * nb))
+            if ntab < 2:
+                continue
+            tabs = [torch.arange(r * B * nb, (r + 1) * B * nb, dtype=torch.int32, device=dev)
+                    .view(B, nb) for r in range(ntab)]
+            tables = [tabs[r % ntab] for r in range(reps)]
+            lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+            q = torch.randn(B, Hq, D, device=dev).to(torch.float16)
+            o = torch.empty_like(q)
+            scale = 1.0 / D ** 0.5
+            for r in range(reps):           # warm (and allocate the workspace)
+                mp.attention_decode_kv8(q, cache, tables[r], lens, Hkv, T, scale, out=o)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for r in range(reps):
+                    mp.attention_decode_kv8(q, cache, tables[r], lens, Hkv, T, scale, out=o)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            by = B * Hkv * T * (2 * D + 6) + 2 * B * Hq * D * 2 + B * nb * 4
+            attn.append({"B": B, "context": T, "heads": [Hq, Hkv, D], "us": round(t * 1e6, 2),
+                         "gbps": round(by / t / 1e9, 1), "bound": "hbm",
+                         "frac": round(by / t / 1e9 / HBM_PEAK_GBPS, 4)})
+            del gr
+        del cache, blk
+
     dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
         "metric": "W4A16 GEMM TFLOP/s and HBM GB/s (% roofline), Llama-3-8B shapes M=1/16/2048",
@@ -457,6 +508,7 @@ def main():
         "w8a16_per_gemm": w8,
         "wfp8a16_qwen3_8b_per_gemm": fp8,
         **lowbit,
+        "attention_kv8_decode": attn,
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:

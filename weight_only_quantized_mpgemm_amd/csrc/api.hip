@@ -378,18 +378,22 @@ namespace {
 
 bool kv_shape_ok(int Hkv, int D) { return Hkv >= 1 && Hkv <= 1024 && (D == 64 || D == 128 || D == 256); }
 
-// Blocks per split and splits per (sequence, KV head): enough waves to cover the CUs
-// (about 1024), as few splits as that allows.  MPGEMM_ATTN_BPS overrides the blocks per
-// split (tuning sweeps).
+// Blocks per split and splits per (sequence, KV head): about 1024 waves (one per SIMD at
+// this kernel's register use), and at most 64 splits (a wider combine costs more than it
+// saves).  Measured on MI355X, Llama-3-8B heads: this picks the best of 1..16 blocks per
+// split for batch x context 1 x 8192, 1 x 32768, 8 x 4096, 16 x 2048 and 64 x 2048.
+// MPGEMM_ATTN_BPS overrides the blocks per split (tuning sweeps).
 void attn_plan(int B, int Hkv, int max_len, int *bps, int *splits) {
     const int64_t nblk = (max_len + 63) / 64;
     const int64_t total = (int64_t)B * Hkv * nblk;
     int64_t per = (total + 1023) / 1024;
+    if (per < (nblk + 63) / 64) per = (nblk + 63) / 64;
     if (per < 1) per = 1;
     if (const char *env = getenv("MPGEMM_ATTN_BPS")) {
         const int v = atoi(env);
         if (v >= 1) per = v;
     }
+    if (per < (nblk + 1023) / 1024) per = (nblk + 1023) / 1024;   // combine takes <= 1024 splits
     *bps = (int)per;
     *splits = nblk > 0 ? (int)((nblk + per - 1) / per) : 1;
 }

@@ -22,8 +22,11 @@
 //     per-token scale is folded into P' = round(p * s_v), and its zero point into one
 //     correction per head, sum_t P'_t z_t, subtracted at the end -- so V's codes enter the
 //     MFMA as exact integers (a byte permute and one exact packed add);
-//   - splits of the block range write unnormalized partials (O, max, sum) to a workspace;
-//     a second kernel combines them.  One split writes the output directly;
+//   - block j + 1's loads are issued before block j is computed (two register sets; one for
+//     D = 256, whose two sets would not fit);
+//   - splits of the block range write unnormalized partials (O, max, sum) to a workspace,
+//     split-contiguous per output element; a second kernel combines them with independent
+//     16-byte loads.  One split writes the output directly;
 //   - a block-table entry outside the cache is skipped (no access); every load goes
 //     through a buffer descriptor bounded to its block.
 #include "kernels.hpp"
@@ -33,7 +36,6 @@ namespace mpgemm {
 namespace {
 
 constexpr int kKvTokens = 64;                  // tokens per cache block
-constexpr int kPartPad = 4;                    // partial record: D values, max, sum, pad
 
 __device__ __forceinline__ float xor_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 16, 64));
@@ -114,51 +116,57 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
     for (int i = 0; i < VS; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f, c = 0.f;
 
-    for (int j = j0; j < j1; ++j) {
-        const int pb = table[(size_t)b * table_stride + j];
-        if (pb < 0 || pb >= num_blocks) continue;
-        const uint8_t *hbase = cache + (size_t)pb * HB * Hkv + (size_t)hk * HB;
-        const rsrc_t rs = make_rsrc(hbase, HB);
-        // K: strip s, tile kt at (s KT + kt) KiB; lane's token column 16 s + lane % 16.
+    // One block's loads: K tiles and the lane's token scale/zero, V tiles and the V scales /
+    // zeros of the lane's score tokens.  Two sets alternate, so block j + 1 loads while
+    // block j computes.
+    struct Blk {
         u32x4_t kw[4][KT];
         uint32_t ksw[4], kzw[4];
+        u32x4_t vw[VS];
+        u32x2_t vsw[4];
+        uint32_t vzw[4];
+        bool ok;
+    };
+    auto load_blk = [&](int j, Blk &bl) __attribute__((always_inline)) {
+        const int pb = table[(size_t)b * table_stride + j];
+        bl.ok = pb >= 0 && pb < num_blocks;
+        if (!bl.ok) return;
+        const uint8_t *hbase = cache + (size_t)pb * HB * Hkv + (size_t)hk * HB;
+        const rsrc_t rs = make_rsrc(hbase, HB);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
-                kw[s][kt] = buf_load_b128(rs, lane * 16u, (s * KT + kt) * 1024u);
+                bl.kw[s][kt] = buf_load_b128(rs, lane * 16u, (s * KT + kt) * 1024u);
             const uint32_t tok = 16 * s + g;
-            ksw[s] = buf_load_b32(rs, 128u * D + (tok & ~1u) * 2u, 0);
-            kzw[s] = buf_load_b32(rs, 128u * D + 256u + (tok & ~3u), 0);
+            bl.ksw[s] = buf_load_b32(rs, 128u * D + (tok & ~1u) * 2u, 0);
+            bl.kzw[s] = buf_load_b32(rs, 128u * D + 256u + (tok & ~3u), 0);
         }
-        // V: strip sd at 64 D + sd KiB.  V scales / zeros of this lane's score tokens
-        // 16 s + 4 (lane / 16) + r.
-        u32x4_t vw[VS];
 #pragma unroll
-        for (int sd = 0; sd < VS; ++sd) vw[sd] = buf_load_b128(rs, lane * 16u, 64u * D + sd * 1024u);
-        u32x2_t vsw[4];
-        uint32_t vzw[4];
+        for (int sd = 0; sd < VS; ++sd) bl.vw[sd] = buf_load_b128(rs, lane * 16u, 64u * D + sd * 1024u);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t tok = 16 * s + 4 * q4;
-            vsw[s] = buf_load_b64(rs, 128u * D + 128u + tok * 2u, 0);
-            vzw[s] = buf_load_b32(rs, 128u * D + 320u + tok, 0);
+            bl.vsw[s] = buf_load_b64(rs, 128u * D + 128u + tok * 2u, 0);
+            bl.vzw[s] = buf_load_b32(rs, 128u * D + 320u + tok, 0);
         }
-
+    };
+    auto compute_blk = [&](int j, const Blk &bl) __attribute__((always_inline)) {
+        if (!bl.ok) return;
         // S = K Q^T, strip by strip; lane holds tokens 16 s + 4 (lane / 16) + r of head g.
         f32x4_t sacc[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t tok = 16 * s + g;
-            const uint16_t ks = (uint16_t)(ksw[s] >> ((tok & 1) * 16));
-            const uint32_t kz = (kzw[s] >> ((tok & 3) * 8)) & 0xFFu;
+            const uint16_t ks = (uint16_t)(bl.ksw[s] >> ((tok & 1) * 16));
+            const uint32_t kz = (bl.kzw[s] >> ((tok & 3) * 8)) & 0xFFu;
             const typename Dq8<ACT>::type dq = Dq8<ACT>::make(ks, kz);
             sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    sacc[s] = mfma16x16x32<ACT>(Dq8<ACT>::pair(kw[s][kt][2 * h], kw[s][kt][2 * h + 1], dq),
+                    sacc[s] = mfma16x16x32<ACT>(Dq8<ACT>::pair(bl.kw[s][kt][2 * h], bl.kw[s][kt][2 * h + 1], dq),
                                                 qb[2 * kt + h], sacc[s]);
         }
         // Online softmax (log2 domain) with masking of tokens past len.
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
             }
         bmax = xor_max(bmax);
         const float mn = fmaxf(m, bmax);
-        if (mn == -INFINITY) continue;         // nothing unmasked yet (uniform)
+        if (mn == -INFINITY) return;           // nothing unmasked yet (uniform)
         const float alpha = exp2f(m - mn);
         m = mn;
         c *= alpha;
@@ -186,9 +194,9 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
             for (int r = 0; r < 4; ++r) {
                 const float p = exp2f(sc[s][r] - mn);
                 psum += p;
-                const float vscale = (float)bitcast<_Float16>((uint16_t)(vsw[s][r >> 1] >> ((r & 1) * 16)));
+                const float vscale = (float)bitcast<_Float16>((uint16_t)(bl.vsw[s][r >> 1] >> ((r & 1) * 16)));
                 pr[r] = round_act<ACT>(p * vscale);
-                c += act_to_f32<ACT>(pr[r]) * (float)((vzw[s] >> (8 * r)) & 0xFFu);
+                c += act_to_f32<ACT>(pr[r]) * (float)((bl.vzw[s] >> (8 * r)) & 0xFFu);
             }
             pl[(g * kKvTokens + 16 * s + 4 * q4) / 4] =
                 u32x2_t{(uint32_t)pr[0] | ((uint32_t)pr[1] << 16), (uint32_t)pr[2] | ((uint32_t)pr[3] << 16)};
@@ -203,10 +211,28 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
             const u32x4_t pbv = pl4[(g * kKvTokens + 32 * u + 8 * q4) / 8];
 #pragma unroll
             for (int sd = 0; sd < VS; ++sd)
-                oacc[sd] = mfma16x16x32<ACT>(v_codes_exact<ACT>(vw[sd][2 * u], vw[sd][2 * u + 1]), pbv,
+                oacc[sd] = mfma16x16x32<ACT>(v_codes_exact<ACT>(bl.vw[sd][2 * u], bl.vw[sd][2 * u + 1]), pbv,
                                              oacc[sd]);
         }
         __syncthreads();
+    };
+
+    if constexpr (D <= 128) {
+        Blk ba, bb;
+        if (j0 < j1) load_blk(j0, ba);
+        for (int j = j0; j < j1; j += 2) {
+            if (j + 1 < j1) load_blk(j + 1, bb);
+            compute_blk(j, ba);
+            if (j + 1 >= j1) break;
+            if (j + 2 < j1) load_blk(j + 2, ba);
+            compute_blk(j + 1, bb);
+        }
+    } else {                                   // D = 256: one set (two would spill)
+        Blk ba;
+        for (int j = j0; j < j1; ++j) {
+            load_blk(j, ba);
+            compute_blk(j, ba);
+        }
     }
     c = xor_sum(c);
 
@@ -224,40 +250,73 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
         return;
     }
     if (g >= G) return;
-    float *rec = part + (((size_t)b * Hq + h) * splits + split) * (D + kPartPad);
+    // Partials, split-contiguous per output element: O at part[(bh D + d) SP + split],
+    // then (max, sum) pairs at part[B Hq D SP + 2 (bh SP + split)] (SP: splits padded to 4).
+    const int SP = (splits + 3) & ~3;
+    const size_t bhq = (size_t)b * Hq + h;
+    const size_t nbh = (size_t)(gridDim.x / splits) / Hkv * Hq;     // B * Hq
 #pragma unroll
     for (int sd = 0; sd < VS; ++sd)
-        *reinterpret_cast<f32x4_t *>(rec + 16 * sd + 4 * q4) = oacc[sd] - c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            part[(bhq * D + 16 * sd + 4 * q4 + r) * SP + split] = oacc[sd][r] - c;
     if (q4 == 0) {
-        rec[D] = m;
-        rec[D + 1] = l;
+        float *ml = part + nbh * D * SP + 2 * (bhq * SP + split);
+        ml[0] = m;
+        ml[1] = l;
     }
 }
 
-// out[b][h] = sum_i w_i O_i / sum_i w_i l_i, w_i = 2^(m_i - max m).
+// out[b][h][d] = sum_i w_i O_i[d] / sum_i w_i l_i, w_i = 2^(m_i - max m); one thread per d.
+// (splits <= kMaxSplits)
+constexpr int kMaxSplits = 1024;
 template <int ACT, int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ part, int splits,
-                                                          uint16_t *__restrict__ O) {
-    const size_t bh = blockIdx.x;
-    const float *rec = part + bh * splits * (D + kPartPad);
+__global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict__ part, int splits,
+                                                         int nbh, uint16_t *__restrict__ O) {
+    __shared__ float w[kMaxSplits];
+    __shared__ float red[D / 64][2];
+    const int bh = blockIdx.x, d = threadIdx.x;
+    const int SP = (splits + 3) & ~3;
+    const float *ml = part + (size_t)nbh * D * SP + 2 * (size_t)bh * SP;
     float mx = -INFINITY;
-    for (int i = 0; i < splits; ++i) mx = fmaxf(mx, rec[i * (D + kPartPad) + D]);
-    float acc[D / 64];
+    for (int i = d; i < splits; i += D) mx = fmaxf(mx, ml[2 * i]);
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((d & 63) == 0) red[d >> 6][0] = mx;
+    __syncthreads();
+    mx = red[0][0];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-    float lsum = 0.f;
-    if (mx != -INFINITY) {
-        for (int i = 0; i < splits; ++i) {
-            const float *r = rec + i * (D + kPartPad);
-            const float w = exp2f(r[D] - mx);
-            lsum += w * r[D + 1];
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) acc[e] += w * r[threadIdx.x + 64 * e];
-        }
+    for (int k = 1; k < D / 64; ++k) mx = fmaxf(mx, red[k][0]);
+    float ls = 0.f;
+    for (int i = d; i < splits; i += D) {
+        const float wi = mx == -INFINITY ? 0.f : exp2f(ml[2 * i] - mx);
+        w[i] = wi;
+        ls += wi * ml[2 * i + 1];
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o, 64);
+    if ((d & 63) == 0) red[d >> 6][1] = ls;
+    __syncthreads();
+    ls = 0.f;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) O[bh * D + threadIdx.x + 64 * e] = round_act<ACT>(acc[e] * inv);
+    for (int k = 0; k < D / 64; ++k) ls += red[k][1];
+    const f32x4_t *row = reinterpret_cast<const f32x4_t *>(part + ((size_t)bh * D + d) * SP);
+    float acc = 0.f;
+    // Eight independent 16-byte loads in flight per batch (the loop would otherwise wait
+    // out one memory latency per load).
+    constexpr int kBatch = 8;
+    for (int i0 = 0; i0 < SP / 4; i0 += kBatch) {
+        f32x4_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = i0 + u < SP / 4 ? row[i0 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * (i0 + u) + e;
+                if (i < splits && w[i] != 0.f) acc += w[i] * v[u][e];
+            }
+    }
+    O[(size_t)bh * D + d] = round_act<ACT>(ls > 0.f ? acc / ls : 0.f);
 }
 
 // One thread per (token, KV head): writes its K and V codes, scales and zeros.
@@ -300,8 +359,8 @@ void launch_attn(const AttnArgs &a, hipStream_t stream) {
         a.Q, a.cache, a.num_blocks, a.table, a.table_stride, a.lens, a.Hq, a.Hkv, a.bps,
         a.splits, a.scale_log2, a.O, a.part);
     if (a.splits > 1)
-        attn_combine_kernel<ACT, D><<<dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, stream>>>(
-            a.part, a.splits, a.O);
+        attn_combine_kernel<ACT, D><<<dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, stream>>>(
+            a.part, a.splits, a.B * a.Hq, a.O);
 }
 
 template <int ACT>
@@ -316,7 +375,8 @@ void launch_attn_act(const AttnArgs &a, hipStream_t stream) {
 }  // namespace
 
 size_t attn_part_bytes(int B, int Hq, int D, int splits) {
-    return splits > 1 ? (size_t)B * Hq * splits * (D + kPartPad) * sizeof(float) : 0;
+    const size_t sp = (size_t)((splits + 3) & ~3);
+    return splits > 1 ? (size_t)B * Hq * sp * (D + 2) * sizeof(float) : 0;
 }
 
 hipError_t launch_attention_kv8(const AttnArgs &a, hipStream_t stream) {
