@@ -106,6 +106,10 @@ def _load():
                                                 ctypes.POINTER(ctypes.c_int), i, i, i, i, i,
                                                 ctypes.c_float, i, u16p]
     lib.oracle_attention_decode_kv8.restype = None
+    lib.oracle_attention_decode_kvfp8.argtypes = [u16p, u8p, u16p, u8p, u16p,
+                                                  ctypes.POINTER(ctypes.c_int), i, i, i, i, i,
+                                                  ctypes.c_float, i, i, u16p]
+    lib.oracle_attention_decode_kvfp8.restype = None
     ip = ctypes.POINTER(ctypes.c_int)
     lib.oracle_kv_block_bytes.argtypes = [i, i]
     lib.oracle_kv_block_bytes.restype = ctypes.c_size_t
@@ -456,6 +460,31 @@ def attention_decode_kv8(q_bits, kc, ks_bits, kz, vc, vs_bits, vz, lens, scale: 
         _ptr(arrs[3], ctypes.c_uint16), _ptr(arrs[4], ctypes.c_uint8),
         lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), B, Hq, Hkv, D, Tmax,
         ctypes.c_float(scale), _dtype_code(dtype), _ptr(o, ctypes.c_uint16))
+    return o
+
+
+def attention_decode_kvfp8(q_bits, kc, ks_bits, vc, vs_bits, lens, scale: float,
+                           fmt: str = "e4m3", dtype: str = "f16") -> np.ndarray:
+    """Decode attention over an FP8 KV cache (user form as attention_decode_kv8, no
+    zeros); returns o bits [B, Hq, D]."""
+    lib = _load()
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    B, Hq, D = q_bits.shape
+    kc = np.ascontiguousarray(kc, dtype=np.uint8)
+    _, Tmax, Hkv, D2 = kc.shape
+    assert D2 == D and Hq % Hkv == 0
+    vc = np.ascontiguousarray(vc, dtype=np.uint8)
+    ks_bits = np.ascontiguousarray(ks_bits, dtype=np.uint16)
+    vs_bits = np.ascontiguousarray(vs_bits, dtype=np.uint16)
+    assert vc.shape == kc.shape and ks_bits.shape == vs_bits.shape == (B, Tmax, Hkv)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    assert lens.shape == (B,) and (lens >= 0).all() and (lens <= Tmax).all()
+    o = np.empty((B, Hq, D), dtype=np.uint16)
+    lib.oracle_attention_decode_kvfp8(
+        _ptr(q_bits, ctypes.c_uint16), _ptr(kc, ctypes.c_uint8), _ptr(ks_bits, ctypes.c_uint16),
+        _ptr(vc, ctypes.c_uint8), _ptr(vs_bits, ctypes.c_uint16),
+        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), B, Hq, Hkv, D, Tmax,
+        ctypes.c_float(scale), FP8_FORMATS[fmt], _dtype_code(dtype), _ptr(o, ctypes.c_uint16))
     return o
 
 

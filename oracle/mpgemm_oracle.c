@@ -627,6 +627,60 @@ void oracle_attention_decode_kv8(const uint16_t *q, const uint8_t *kc, const uin
 }
 
 /*
+ * The same attention over an FP8 KV cache: k[t][d] = round_act(fp8(kc[t][d]) * ks[t]),
+ * v alike, fp8 in the OCP format `format` (0 = E4M3, 1 = E5M2; see the FP8 weights above),
+ * no zero points.  The other arguments and the arithmetic as oracle_attention_decode_kv8.
+ */
+void oracle_attention_decode_kvfp8(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
+                                   const uint8_t *vc, const uint16_t *vs, const int *lens,
+                                   int B, int Hq, int Hkv, int D, int Tmax, float scale,
+                                   int format, int dtype, uint16_t *o) {
+    const int group = Hq / Hkv;
+    double *score = (double *)malloc(sizeof(double) * (size_t)(Tmax > 0 ? Tmax : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int b = 0; b < B; ++b) {
+        const int len = lens[b];
+        for (int h = 0; h < Hq; ++h) {
+            const int hk = h / group;
+            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;
+            double mx = -INFINITY;
+            for (int t = 0; t < len; ++t) {
+                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;
+                const double sk8 = oracle_f16_to_f64(ks[row]);
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    uint8_t c8 = kc[row * D + d];
+                    double e8 = format == 1 ? oracle_e5m2_to_f64(c8) : oracle_e4m3_to_f64(c8);
+                    dot += act_to_f64(qh[d], dtype) * act_to_f64(f64_to_act(e8 * sk8, dtype), dtype);
+                }
+                score[t] = dot * (double)scale;
+                if (score[t] > mx) mx = score[t];
+            }
+            double denom = 0.0;
+            for (int t = 0; t < len; ++t) {
+                score[t] = exp(score[t] - mx);
+                denom += score[t];
+            }
+            for (int d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int t = 0; t < len; ++t) {
+                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;
+                const double sv8 = oracle_f16_to_f64(vs[row]);
+                const double pt = score[t] / denom;
+                for (int d = 0; d < D; ++d) {
+                    uint8_t c8 = vc[row * D + d];
+                    double e8 = format == 1 ? oracle_e5m2_to_f64(c8) : oracle_e4m3_to_f64(c8);
+                    acc[d] += pt * act_to_f64(f64_to_act(e8 * sv8, dtype), dtype);
+                }
+            }
+            uint16_t *oh = o + ((size_t)b * Hq + h) * D;
+            for (int d = 0; d < D; ++d) oh[d] = f64_to_act(acc[d], dtype);
+        }
+    }
+    free(score);
+    free(acc);
+}
+
+/*
  * Packed KV cache (restated from its specification in include/mpgemm.h).  Blocks of 64
  * tokens of one sequence, all KV heads; block j of sequence b is cache block
  * table[b][j].  Within a block, KV head h occupies HB = 128*D + 384 bytes at h*HB:

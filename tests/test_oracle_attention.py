@@ -206,3 +206,65 @@ def test_kv_pack_in_pieces_through_a_block_table_round_trips():
     untouched = [i for i in range(8) if i not in table]
     bb = oracle.kv_block_bytes(Hkv, D)
     assert all((cache[i * bb:(i + 1) * bb] == 0).all() for i in untouched)
+
+
+# ------------------------------------------------------------- FP8 KV cache ---------
+
+import torch  # noqa: E402
+
+FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def fp8_value(code, fmt) -> Fraction:
+    t = torch.tensor([int(code)], dtype=torch.uint8).view(FP8[fmt])
+    return Fraction(float(t.to(torch.float64)[0]))
+
+
+def finite_fp8(shape, fmt, seed):
+    rng = np.random.default_rng(seed)
+    v = np.clip(rng.standard_normal(shape).astype(np.float32) * 2, -400, 400)
+    return torch.from_numpy(v).to(FP8[fmt]).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_single_token_gives_its_value_row(fmt):
+    B, T, Hkv, Hq, D = 1, 2, 2, 4, 64
+    kc, vc = finite_fp8((B, T, Hkv, D), fmt, 1), finite_fp8((B, T, Hkv, D), fmt, 2)
+    ks = np.full((B, T, Hkv), 0.5, np.float16).view(np.uint16)
+    vs = np.random.default_rng(3).uniform(0.01, 0.1, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    q = rand_q(B, Hq, D, 4)
+    o = oracle.attention_decode_kvfp8(q, kc, ks, vc, vs, [1], 0.1, fmt)
+    for h in range(Hq):
+        j = h // 2
+        want = [f16(float(fp8_value(vc[0, 0, j, d], fmt) * f16_val(vs[0, 0, j]))) for d in range(D)]
+        assert o[0, h].tolist() == want
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_zero_query_averages_the_value_rows(fmt):
+    L, D = 8, 64
+    kc, vc = finite_fp8((1, L, 1, D), fmt, 5), finite_fp8((1, L, 1, D), fmt, 6)
+    ks = np.full((1, L, 1), 1.0, np.float16).view(np.uint16)
+    vs = np.full((1, L, 1), 0.25, np.float16).view(np.uint16)
+    o = oracle.attention_decode_kvfp8(np.zeros((1, 1, D), np.uint16), kc, ks, vc, vs, [L], 0.1, fmt)
+    for d in range(D):
+        vals = [f16_val(f16(float(fp8_value(vc[0, t, 0, d], fmt) / 4))) for t in range(L)]
+        assert o[0, 0, d] == f16(float(sum(vals) / L))
+
+
+def test_fp8_formats_differ_and_match_the_integer_cache_on_shared_values():
+    """Codes whose E4M3 value is an integer v: the FP8 cache with scale s equals the 8-bit
+    cache with codes v + 128, zero 128 and the same scale."""
+    B, T, Hkv, Hq, D = 1, 20, 1, 2, 64
+    rng = np.random.default_rng(7)
+    ints = rng.integers(-16, 17, (B, T, Hkv, D))
+    codes = torch.from_numpy(ints.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ks = rng.uniform(0.01, 0.05, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    vs = rng.uniform(0.01, 0.05, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    q = rand_q(B, Hq, D, 8)
+    a = oracle.attention_decode_kvfp8(q, codes, ks, codes, vs, [T], 0.1, "e4m3")
+    u8 = (ints + 128).astype(np.uint8)
+    z = np.full((B, T, Hkv), 128, np.uint8)
+    b = oracle.attention_decode_kv8(q, u8, ks, z, u8, vs, z, [T], 0.1)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, oracle.attention_decode_kvfp8(q, codes, ks, codes, vs, [T], 0.1, "e5m2"))

@@ -98,8 +98,12 @@ MUTANTS_LOWBIT = {
 
 
 MUTANTS_ATTENTION = {
-    "gqa_head_modulo": ("const int hk = h / group;", "const int hk = h % Hkv;"),
-    "no_softmax_scale": ("score[t] = dot * (double)scale;", "score[t] = dot;"),
+    "gqa_head_modulo": ("const int hk = h / group;\n            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;\n            double mx = -INFINITY;\n            for (int t = 0; t < len; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double s_k",
+                        "const int hk = h % Hkv;\n            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;\n            double mx = -INFINITY;\n            for (int t = 0; t < len; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double s_k"),
+    "no_softmax_scale": ("dot += act_to_f64(qh[d], dtype) * kd;\n                }\n                score[t] = dot * (double)scale;",
+                         "dot += act_to_f64(qh[d], dtype) * kd;\n                }\n                score[t] = dot;"),
+    "kvfp8_gqa_head_modulo": ("const int hk = h / group;\n            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;\n            double mx = -INFINITY;\n            for (int t = 0; t < len; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double sk8",
+                              "const int hk = h % Hkv;\n            const uint16_t *qh = q + ((size_t)b * Hq + h) * D;\n            double mx = -INFINITY;\n            for (int t = 0; t < len; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double sk8"),
     "k_zero_sign": ("f64_to_act((double)((int)kc[row * D + d] - (int)kz[row]) * s_k, dtype)",
                     "f64_to_act((double)((int)kz[row] - (int)kc[row * D + d]) * s_k, dtype)"),
     "v_takes_k_scale": ("const double s_v = oracle_f16_to_f64(vs[row]);",
@@ -112,6 +116,12 @@ MUTANTS_ATTENTION = {
                             "hb[64 * (size_t)D + code8_byte_offset(d, slot, D)] = vc[row * D + d];"),
     "kv_zeros_swapped": ("hb[128 * (size_t)D + 256 + slot] = kz[row];",
                          "hb[128 * (size_t)D + 320 + slot] = kz[row];"),
+    "kvfp8_format_swap": ("double e8 = format == 1 ? oracle_e5m2_to_f64(c8) : oracle_e4m3_to_f64(c8);\n                    acc[d]",
+                          "double e8 = format == 0 ? oracle_e5m2_to_f64(c8) : oracle_e4m3_to_f64(c8);\n                    acc[d]"),
+    "kvfp8_v_scale": ("const double sv8 = oracle_f16_to_f64(vs[row]);",
+                      "const double sv8 = oracle_f16_to_f64(ks[row]);"),
+    "kvfp8_k_unrounded": ("dot += act_to_f64(qh[d], dtype) * act_to_f64(f64_to_act(e8 * sk8, dtype), dtype);",
+                          "dot += act_to_f64(qh[d], dtype) * e8 * sk8;"),
 }
 
 
