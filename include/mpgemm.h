@@ -348,7 +348,8 @@ size_t mpgemm_kv_block_bytes(int Hkv, int D);
  * pointers; ks, vs, table_row 4-byte aligned, kc, vc, cache 16-byte aligned) into the cache
  * through that sequence's block-table row (table_len entries; t0 + n_tokens <= 64 *
  * table_len).  Entries outside [0, num_blocks) are skipped.  Prefill and every decode
- * step's append are calls of this one function.
+ * step's append are calls of this one function.  kz and vz are NULL together for FP8 codes
+ * (no zero points).
  */
 int mpgemm_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, const uint8_t *vc,
                    const uint16_t *vs, const uint8_t *vz, int n_tokens, int t0, int Hkv, int D,
@@ -377,6 +378,19 @@ int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int
                                 int B, int Hq, int Hkv, int D, int max_len, float scale,
                                 void *O, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * The same over an FP8 KV cache: codes are OCP FP8 numbers in fp8_format
+ * (MPGEMM_FP8_E4M3 / MPGEMM_FP8_E5M2), k = fp8(kc) * ks and v = fp8(vc) * vs rounded once
+ * to the activation format, no zero points (pack with kz = vz = NULL; the zero fields of
+ * the blocks are then written as 0 and not read).  Arguments otherwise as
+ * mpgemm_attention_decode_kv8; a bad fp8_format returns MPGEMM_ERR_INVALID_ARG.
+ */
+int mpgemm_attention_decode_kvfp8(const void *Q, int dtype, int fp8_format, const void *cache,
+                                  int num_blocks, const int *block_table, int table_stride,
+                                  const int *lens, int B, int Hq, int Hkv, int D, int max_len,
+                                  float scale, void *O, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *mpgemm_status_string(int status);

@@ -1,5 +1,5 @@
-"""GPU parity of decode attention over the packed 8-bit KV cache, through the C ABI,
-against the CPU oracle.
+"""GPU parity of decode attention over the packed 8-bit and FP8 (E4M3 / E5M2) KV caches,
+through the C ABI, against the CPU oracle.
 
   * the GPU packer writes the same cache bytes as the oracle's (pieces, scattered blocks);
   * outputs over random caches, for head groups of 1 to 16 query heads, head sizes 64 /
@@ -15,7 +15,10 @@ against the CPU oracle.
   * one-token contexts give the dequantized value row bit-exact (fp16: p = 1 and the
     value scale enter the matrix cores exactly);
   * tokens past each length never matter (bit-identical output with other contents);
-  * table entries outside the cache are skipped without touching other sequences.
+  * table entries outside the cache are skipped without touching other sequences;
+  * FP8 caches (no zero points) to the same bars: the same value bar (the kernel rounds
+    p_t s_t, the oracle fp8(v) s_t, each once), bit-exact one-token rows, and bytes of the
+    packed cache equal to the oracle's with zero bytes in the zero fields.
 """
 import os
 
@@ -56,22 +59,27 @@ class Cache:
         for b, L in enumerate(lens):
             if L == 0:
                 continue
-            parts = [a[b, :L] for a in kv]
+            # FP8 caches have no zero points: the oracle packs zero bytes, the GPU NULL
+            parts = [a[b, :L] if a is not None else np.zeros((L, Hkv), np.uint8) for a in kv]
             oracle.kv_pack(self.host, self.table[b], 0, *parts)
             row = dev(self.table[b])
             for t0, t1 in ((0, min(L, 37)), (min(L, 37), L)):      # a prefill, then an append
                 if t1 > t0:
-                    p = [a[b, t0:t1] for a in kv]
+                    p = [a[b, t0:t1] if a is not None else None for a in kv]
+                    z = (None, None) if p[2] is None else (dev(p[2]), dev(p[5]))
                     mp.kv_pack(self.gpu, row, t0, dev(p[0]), dev(p[1].view(np.int16), torch.float16),
-                               dev(p[2]), dev(p[3]), dev(p[4].view(np.int16), torch.float16),
-                               dev(p[5]))
+                               z[0], dev(p[3]), dev(p[4].view(np.int16), torch.float16), z[1])
 
 
-def run(q_bits, cache, lens, Hkv, scale, dtype, max_len=None):
+def run(q_bits, cache, lens, Hkv, scale, dtype, max_len=None, fp8=None):
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
     q = dev(q_bits.view(np.int16), tdt)
-    o = mp.attention_decode_kv8(q, cache.gpu, dev(cache.table), dev(np.asarray(lens, np.int32)),
-                                Hkv, max(lens) if max_len is None else max_len, scale)
+    args = (q, cache.gpu, dev(cache.table), dev(np.asarray(lens, np.int32)), Hkv,
+            max(lens) if max_len is None else max_len, scale)
+    if fp8 is None:
+        o = mp.attention_decode_kv8(*args)
+    else:
+        o = mp.attention_decode_kvfp8(*args, fp8_format=fp8)
     torch.cuda.synchronize()
     return host_bits(o)
 
@@ -86,15 +94,16 @@ def rel(y, ref, dtype):
     return float(np.abs(a - r).max() / max(np.abs(r).max(), 1e-30))
 
 
-def within_value_bar(y, ref, kv, lens, dtype):
+def within_value_bar(y, ref, kv, lens, dtype, fp8=None):
     """max|O - O_ref| <= 4 * 2^-(f+1) * max|x| over the sequences' live values."""
     conv = oracle.f16_bits_to_f64 if dtype == "f16" else oracle.bf16_bits_to_f64
     _, _, _, vc, vs, vz = kv
+    table = None if fp8 is None else oracle.fp8_to_f64(np.arange(256, dtype=np.uint8), fp8)
     xmax = 0.0
     for b, L in enumerate(lens):
         if L:
-            x = (vc[b, :L].astype(np.float64) - vz[b, :L, :, None]) * \
-                vs[b, :L].view(np.float16).astype(np.float64)[..., None]
+            v = vc[b, :L].astype(np.float64) - vz[b, :L, :, None] if fp8 is None else table[vc[b, :L]]
+            x = v * vs[b, :L].view(np.float16).astype(np.float64)[..., None]
             xmax = max(xmax, float(np.abs(x).max()))
     err = float(np.abs(conv(y) - conv(ref)).max())
     assert np.isfinite(conv(y)).all()
@@ -194,3 +203,79 @@ def test_attention_leaves_the_gemm_workspace_zero():
     ws = mp.workspace_for(torch.device("cuda"), 1 << 20)
     run(q, c, lens, 8, 0.1, "f16")
     assert int(ws.count_nonzero()) == 0
+
+
+# ------------------------------------------------------------------ FP8 KV cache ----------
+
+def case_fp8(B, Hq, Hkv, D, lens, dtype, fmt, seed):
+    kv = workloads.kv_cache_fp8(B, max(max(lens), 1), Hkv, D, fmt, seed)
+    return kv, workloads.queries(B, Hq, D, dtype, seed + 1)
+
+
+def fp8_ref(q, kv, lens, scale, fmt, dtype):
+    kc, ks, _, vc, vs, _ = kv
+    return oracle.attention_decode_kvfp8(q, kc, ks, vc, vs, lens, scale, fmt, dtype)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_kvfp8_pack_matches_oracle_bytes(fmt):
+    lens, Hkv, D = [150, 64, 1], 2, 128
+    kv, _ = case_fp8(3, 4, Hkv, D, lens, "f16", fmt, 3)
+    c = Cache(kv, lens, Hkv, D, 5)
+    assert np.array_equal(c.gpu.cpu().numpy(), c.host)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 1, 64), (8, 2, 256)])
+@pytest.mark.parametrize("bps", [None, "1"])
+def test_kvfp8_attention_matches_oracle(fmt, dtype, Hq, Hkv, D, bps, monkeypatch):
+    if bps:
+        monkeypatch.setenv("MPGEMM_ATTN_BPS", bps)
+    lens = [1, 63, 64, 65, 300, 1000, 0, 129]
+    kv, q = case_fp8(len(lens), Hq, Hkv, D, lens, dtype, fmt, Hq + D + len(fmt))
+    c = Cache(kv, lens, Hkv, D, 7)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    say(f"attention fp8 {fmt} {dtype} Hq={Hq} Hkv={Hkv} D={D} bps={bps}")
+    y = run(q, c, lens, Hkv, scale, dtype, fp8=fmt)
+    want = fp8_ref(q, kv, lens, scale, fmt, dtype)
+    assert (y[6] == 0).all() and (want[6] == 0).all()        # empty context
+    ok, detail = within_value_bar(y, want, kv, lens, dtype, fp8=fmt)
+    assert ok, detail
+    if dtype == "f16":
+        assert rel(y, want, dtype) <= REL_TOL
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_kvfp8_one_token_context_gives_the_value_row_bit_exact(fmt):
+    lens, Hq, Hkv, D = [1, 1, 1], 8, 2, 128
+    kv, q = case_fp8(3, Hq, Hkv, D, lens, "f16", fmt, 71)
+    c = Cache(kv, lens, Hkv, D, 72)
+    y = run(q, c, lens, Hkv, 0.1, "f16", fp8=fmt)
+    assert np.array_equal(y, fp8_ref(q, kv, lens, 0.1, fmt, "f16"))
+
+
+def test_kvfp8_long_context_llama3_8b_heads():
+    lens = [2000, 1777, 64, 3]
+    kv, q = case_fp8(4, 32, 8, 128, lens, "f16", "e4m3", 81)
+    c = Cache(kv, lens, 8, 128, 82)
+    say("attention fp8 long")
+    y = run(q, c, lens, 8, 0.0883883461356163, "f16", fp8="e4m3")
+    want = fp8_ref(q, kv, lens, 0.0883883461356163, "e4m3", "f16")
+    assert within_value_bar(y, want, kv, lens, "f16", fp8="e4m3")[0]
+    assert rel(y, want, "f16") <= REL_TOL
+
+
+def test_kvfp8_rejects_an_unknown_format():
+    lens = [5]
+    kv, q = case_fp8(1, 8, 2, 128, lens, "f16", "e4m3", 91)
+    c = Cache(kv, lens, 2, 128, 92)
+    q_t = dev(q.view(np.int16), torch.float16)
+    with pytest.raises(ValueError):
+        mp.attention_decode_kvfp8(q_t, c.gpu, dev(c.table), dev(np.asarray(lens, np.int32)), 2, 5,
+                                  0.1, fp8_format="e3m4")
+    st = mp.lib().mpgemm_attention_decode_kvfp8(
+        q_t.data_ptr(), 0, 7, c.gpu.data_ptr(), c.gpu.numel() // mp.kv_block_bytes(2, 128),
+        dev(c.table).data_ptr(), c.table.shape[1], dev(np.asarray(lens, np.int32)).data_ptr(), 1, 8,
+        2, 128, 5, 0.1, q_t.data_ptr(), None, 0, None)
+    assert st != 0

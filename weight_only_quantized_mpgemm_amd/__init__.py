@@ -62,6 +62,8 @@ SIGNATURES = {
     "mpgemm_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "mpgemm_attention_decode_kv8": (_i, [_vp, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i, _i,
                                          ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "mpgemm_attention_decode_kvfp8": (_i, [_vp, _i, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
+                                           _i, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "mpgemm_packed_code_bytes_lowbit": (_sz, [_i, _i, _i]),
     "mpgemm_pack_weights_lowbit": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "mpgemm_unpack_lowbit": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
@@ -399,7 +401,7 @@ def wfp8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = N
     return _gemm("fp8", x, packed, out, config, workspace)
 
 
-# ------------------------------------------------- attention decode (8-bit KV cache) --
+# ------------------------------------------- attention decode (8-bit / FP8 KV cache) --
 
 # Attention partials need no initialization, but must not share the GEMM workspace (whose
 # split-K counters have to stay zero between calls): a cache of their own.
@@ -426,17 +428,22 @@ def kv_block_bytes(Hkv: int, D: int) -> int:
 
 
 def kv_pack(cache: torch.Tensor, table_row: torch.Tensor, t0: int, kc: torch.Tensor,
-            ks: torch.Tensor, kz: torch.Tensor, vc: torch.Tensor, vs: torch.Tensor,
-            vz: torch.Tensor) -> None:
+            ks: torch.Tensor, kz: torch.Tensor | None, vc: torch.Tensor, vs: torch.Tensor,
+            vz: torch.Tensor | None) -> None:
     """Writes tokens t0 .. t0+n-1 of one sequence into `cache` (mpgemm_kv_pack).
 
-    kc, vc uint8 [n, Hkv, D]; ks, vs float16 [n, Hkv]; kz, vz uint8 [n, Hkv]; table_row
-    int32 [table_len] (device); cache uint8 [num_blocks * kv_block_bytes(Hkv, D)].
+    kc, vc uint8 [n, Hkv, D]; ks, vs float16 [n, Hkv]; kz, vz uint8 [n, Hkv], or both None
+    for FP8 codes (no zero points); table_row int32 [table_len] (device); cache uint8
+    [num_blocks * kv_block_bytes(Hkv, D)].
     """
     n, Hkv, D = kc.shape
-    for t, dt, shape, name in ((kc, torch.uint8, (n, Hkv, D), "kc"), (vc, torch.uint8, (n, Hkv, D), "vc"),
-                               (ks, torch.float16, (n, Hkv), "ks"), (vs, torch.float16, (n, Hkv), "vs"),
-                               (kz, torch.uint8, (n, Hkv), "kz"), (vz, torch.uint8, (n, Hkv), "vz")):
+    if (kz is None) != (vz is None):
+        raise ValueError("kz and vz are given together or not at all")
+    need = [(kc, torch.uint8, (n, Hkv, D), "kc"), (vc, torch.uint8, (n, Hkv, D), "vc"),
+            (ks, torch.float16, (n, Hkv), "ks"), (vs, torch.float16, (n, Hkv), "vs")]
+    if kz is not None:
+        need += [(kz, torch.uint8, (n, Hkv), "kz"), (vz, torch.uint8, (n, Hkv), "vz")]
+    for t, dt, shape, name in need:
         _need(t, dt, shape, name)
     _need(table_row, torch.int32, (table_row.numel(),), "table_row")
     bb = kv_block_bytes(Hkv, D)
@@ -456,6 +463,23 @@ def attention_decode_kv8(q: torch.Tensor, cache: torch.Tensor, block_table: torc
     """One decode step of attention over a packed 8-bit KV cache
     (mpgemm_attention_decode_kv8).  q float16/bfloat16 [B, Hq, D]; block_table int32
     [B, table_stride]; lens int32 [B] (each <= max_len); returns [B, Hq, D]."""
+    return _attention(None, q, cache, block_table, lens, Hkv, max_len, scale, out, workspace)
+
+
+def attention_decode_kvfp8(q: torch.Tensor, cache: torch.Tensor, block_table: torch.Tensor,
+                           lens: torch.Tensor, Hkv: int, max_len: int, scale: float,
+                           fp8_format: str = "e4m3", out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The same over a cache of FP8 codes ("e4m3" or "e5m2") packed without zero points
+    (mpgemm_attention_decode_kvfp8)."""
+    if fp8_format not in FP8_FORMATS:
+        raise ValueError(f"unknown FP8 format {fp8_format!r}")
+    return _attention(fp8_format, q, cache, block_table, lens, Hkv, max_len, scale, out,
+                      workspace)
+
+
+def _attention(fp8_format, q, cache, block_table, lens, Hkv, max_len, scale, out, workspace):
+    call = "mpgemm_attention_decode_kv8" if fp8_format is None else "mpgemm_attention_decode_kvfp8"
     B, Hq, D = q.shape
     act = _act_code(q.dtype)
     _need(q, q.dtype, (B, Hq, D), "q")
@@ -464,7 +488,7 @@ def attention_decode_kv8(q: torch.Tensor, cache: torch.Tensor, block_table: torc
     _need(lens, torch.int32, (B,), "lens")
     bb = kv_block_bytes(Hkv, D)
     if bb == 0:
-        raise MpgemmError(-2, "attention_decode_kv8")
+        raise MpgemmError(-2, call)
     _need(cache, torch.uint8, (cache.numel(),), "cache")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
@@ -475,9 +499,12 @@ def attention_decode_kv8(q: torch.Tensor, cache: torch.Tensor, block_table: torc
     elif ws:
         _need(workspace, torch.uint8, (workspace.numel(),), "workspace")
         ws = workspace.numel()
-    st = lib().mpgemm_attention_decode_kv8(_ptr(q), act, _ptr(cache), cache.numel() // bb,
-                                           _ptr(block_table), block_table.shape[1], _ptr(lens),
-                                           B, Hq, Hkv, D, max_len, ctypes.c_float(scale),
-                                           _ptr(out), _ptr(workspace), ws, _stream(q.device))
-    _check(st, "mpgemm_attention_decode_kv8")
+    rest = (_ptr(cache), cache.numel() // bb, _ptr(block_table), block_table.shape[1],
+            _ptr(lens), B, Hq, Hkv, D, max_len, ctypes.c_float(scale), _ptr(out),
+            _ptr(workspace), ws, _stream(q.device))
+    if fp8_format is None:
+        st = lib().mpgemm_attention_decode_kv8(_ptr(q), act, *rest)
+    else:
+        st = lib().mpgemm_attention_decode_kvfp8(_ptr(q), act, FP8_FORMATS[fp8_format], *rest)
+    _check(st, call)
     return out

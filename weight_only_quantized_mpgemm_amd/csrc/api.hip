@@ -417,7 +417,8 @@ int mpgemm_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, con
     if ((int64_t)t0 + n_tokens > (int64_t)table_len * 64) return MPGEMM_ERR_INVALID_ARG;
     if ((int64_t)n_tokens * Hkv >= kIndexLimit) return MPGEMM_ERR_UNSUPPORTED;
     if (n_tokens == 0) return MPGEMM_OK;
-    if (!kc || !ks || !kz || !vc || !vs || !vz || !table_row || !cache) return MPGEMM_ERR_INVALID_ARG;
+    if (!kc || !ks || !vc || !vs || !table_row || !cache || (!kz) != (!vz))
+        return MPGEMM_ERR_INVALID_ARG;
     if (!aligned16(kc) || !aligned16(vc) || !aligned4(ks) || !aligned4(vs) || !aligned4(table_row) ||
         !aligned16(cache))
         return MPGEMM_ERR_ALIGNMENT;
@@ -433,10 +434,14 @@ size_t mpgemm_attention_workspace_bytes(int B, int Hq, int Hkv, int D, int max_l
     return mpgemm::attn_part_bytes(B, Hq, D, splits);
 }
 
-int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int num_blocks,
-                                const int *block_table, int table_stride, const int *lens, int B,
-                                int Hq, int Hkv, int D, int max_len, float scale, void *O,
-                                void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int attention_impl(int kv_code, const void *Q, int dtype, const void *cache, int num_blocks,
+                   const int *block_table, int table_stride, const int *lens, int B, int Hq,
+                   int Hkv, int D, int max_len, float scale, void *O, void *workspace,
+                   size_t workspace_bytes, void *stream) {
     if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
     if (B < 0 || max_len < 0 || num_blocks < 0 || table_stride < 0 || Hkv < 1 || Hq < 1)
         return MPGEMM_ERR_INVALID_ARG;
@@ -465,6 +470,7 @@ int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int
     a.Hkv = Hkv;
     a.D = D;
     a.act = dtype == MPGEMM_BF16 ? mpgemm::kBF16 : mpgemm::kF16;
+    a.kv_code = kv_code;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.O = (uint16_t *)O;
     a.part = (float *)workspace;
@@ -472,6 +478,30 @@ int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int
         fprintf(stderr, "mpgemm: attention B=%d Hq=%d Hkv=%d D=%d max_len=%d -> %d splits of %d blocks\n",
                 B, Hq, Hkv, D, max_len, a.splits, a.bps);
     return hip_status(mpgemm::launch_attention_kv8(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpgemm_attention_decode_kv8(const void *Q, int dtype, const void *cache, int num_blocks,
+                                const int *block_table, int table_stride, const int *lens, int B,
+                                int Hq, int Hkv, int D, int max_len, float scale, void *O,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    return attention_impl(mpgemm::kU8, Q, dtype, cache, num_blocks, block_table, table_stride,
+                          lens, B, Hq, Hkv, D, max_len, scale, O, workspace, workspace_bytes,
+                          stream);
+}
+
+int mpgemm_attention_decode_kvfp8(const void *Q, int dtype, int fp8_format, const void *cache,
+                                  int num_blocks, const int *block_table, int table_stride,
+                                  const int *lens, int B, int Hq, int Hkv, int D, int max_len,
+                                  float scale, void *O, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    if (fp8_format != MPGEMM_FP8_E4M3 && fp8_format != MPGEMM_FP8_E5M2) return MPGEMM_ERR_INVALID_ARG;
+    return attention_impl(fp8_format == MPGEMM_FP8_E4M3 ? mpgemm::kE4M3 : mpgemm::kE5M2, Q, dtype,
+                          cache, num_blocks, block_table, table_stride, lens, B, Hq, Hkv, D,
+                          max_len, scale, O, workspace, workspace_bytes, stream);
 }
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {

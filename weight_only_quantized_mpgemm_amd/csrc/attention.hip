@@ -1,4 +1,4 @@
-// Decode attention over an 8-bit KV cache for gfx950, and the KV-cache packer.
+// Decode attention over an 8-bit or FP8 KV cache for gfx950, and the KV-cache packer.
 //
 // [TurboMind, attention pipeline; Fig. 4 and Fig. 10 captions]: the low-bit KV cache is
 // dequantized to 16-bit values by I2F conversion and scaling, V is kept in a transposed
@@ -17,6 +17,8 @@
 //   - online softmax in the exp2 domain.  Every score and every output a lane holds
 //     belongs to head lane % 16, so rescaling is lane-local; block maxima and sums need
 //     two cross-lane exchanges;
+//   - FP8 codes (E4M3 / E5M2, no zero points): K by the FP8 weight dequantizer, V's codes
+//     converted exactly to the activation format, no zero correction;
 //   - O += V^T P' on MFMAs: A = V codes (rows = 16 values of d, k = tokens -- the
 //     transposed layout), B = P' (columns = heads, k = tokens) through 2 KiB of LDS.  V's
 //     per-token scale is folded into P' = round(p * s_v), and its zero point into one
@@ -57,11 +59,24 @@ __device__ __forceinline__ float act_to_f32(uint16_t h) {
     else return __uint_as_float((uint32_t)h << 16);
 }
 
-// Eight V codes (two words, k ascending) as exact 16-bit integers in MFMA operand order.
-template <int ACT>
+// Eight V codes (two words, k ascending) as exact 16-bit values in MFMA operand order:
+// 8-bit integers, or FP8 values (every E4M3 / E5M2 value is an fp16 and a bf16 value).
+template <int ACT, int KVC>
 __device__ __forceinline__ u32x4_t v_codes_exact(uint32_t w0, uint32_t w1) {
     u32x4_t r;
-    if constexpr (ACT == kF16) {
+    if constexpr (kCodeFp8<KVC> && ACT == kF16) {
+        r[0] = fp8_pair_f16<KVC, false>(w0);
+        r[1] = fp8_pair_f16<KVC, true>(w0);
+        r[2] = fp8_pair_f16<KVC, false>(w1);
+        r[3] = fp8_pair_f16<KVC, true>(w1);
+    } else if constexpr (kCodeFp8<KVC>) {
+        const f32x2_t a = fp8_pair_f32<KVC, false>(w0), b = fp8_pair_f32<KVC, true>(w0);
+        const f32x2_t c = fp8_pair_f32<KVC, false>(w1), d = fp8_pair_f32<KVC, true>(w1);
+        r[0] = pack_bf16x2(a.x, a.y);
+        r[1] = pack_bf16x2(b.x, b.y);
+        r[2] = pack_bf16x2(c.x, c.y);
+        r[3] = pack_bf16x2(d.x, d.y);
+    } else if constexpr (ACT == kF16) {
         // (1024 + v) pairs by a byte permute against 0x64, then - 1024 exactly
         const half2_t m1024 = bitcast<half2_t>(0xE400E400u);
         r[0] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)) + m1024);
@@ -77,7 +92,8 @@ __device__ __forceinline__ u32x4_t v_codes_exact(uint32_t w0, uint32_t w1) {
     return r;
 }
 
-template <int ACT, int D>
+// KVC: format of the KV codes (kU8 with zero points, or kE4M3 / kE5M2 without).
+template <int ACT, int D, int KVC>
 __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ cache, int num_blocks,
     const int *__restrict__ table, int table_stride, const int *__restrict__ lens, int Hq,
@@ -160,13 +176,14 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
             const uint32_t tok = 16 * s + g;
             const uint16_t ks = (uint16_t)(bl.ksw[s] >> ((tok & 1) * 16));
             const uint32_t kz = (bl.kzw[s] >> ((tok & 3) * 8)) & 0xFFu;
-            const typename Dq8<ACT>::type dq = Dq8<ACT>::make(ks, kz);
+            typedef DqFor<ACT, KVC> DqK;
+            const typename DqK::type dq = DqK::make(ks, kz);
             sacc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    sacc[s] = mfma16x16x32<ACT>(Dq8<ACT>::pair(bl.kw[s][kt][2 * h], bl.kw[s][kt][2 * h + 1], dq),
+                    sacc[s] = mfma16x16x32<ACT>(DqK::pair(bl.kw[s][kt][2 * h], bl.kw[s][kt][2 * h + 1], dq),
                                                 qb[2 * kt + h], sacc[s]);
         }
         // Online softmax (log2 domain) with masking of tokens past len.
@@ -196,7 +213,8 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
                 psum += p;
                 const float vscale = (float)bitcast<_Float16>((uint16_t)(bl.vsw[s][r >> 1] >> ((r & 1) * 16)));
                 pr[r] = round_act<ACT>(p * vscale);
-                c += act_to_f32<ACT>(pr[r]) * (float)((bl.vzw[s] >> (8 * r)) & 0xFFu);
+                if constexpr (!kCodeFp8<KVC>)
+                    c += act_to_f32<ACT>(pr[r]) * (float)((bl.vzw[s] >> (8 * r)) & 0xFFu);
             }
             pl[(g * kKvTokens + 16 * s + 4 * q4) / 4] =
                 u32x2_t{(uint32_t)pr[0] | ((uint32_t)pr[1] << 16), (uint32_t)pr[2] | ((uint32_t)pr[3] << 16)};
@@ -211,8 +229,8 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
             const u32x4_t pbv = pl4[(g * kKvTokens + 32 * u + 8 * q4) / 8];
 #pragma unroll
             for (int sd = 0; sd < VS; ++sd)
-                oacc[sd] = mfma16x16x32<ACT>(v_codes_exact<ACT>(bl.vw[sd][2 * u], bl.vw[sd][2 * u + 1]), pbv,
-                                             oacc[sd]);
+                oacc[sd] = mfma16x16x32<ACT>(v_codes_exact<ACT, KVC>(bl.vw[sd][2 * u], bl.vw[sd][2 * u + 1]),
+                                             pbv, oacc[sd]);
         }
         __syncthreads();
     };
@@ -348,14 +366,14 @@ __global__ void kv_pack_kernel(const uint8_t *__restrict__ kc, const uint16_t *_
     uint16_t *sc = reinterpret_cast<uint16_t *>(hb + 128 * (size_t)D);
     sc[slot] = ks[row];
     sc[kKvTokens + slot] = vs[row];
-    hb[128 * (size_t)D + 256 + slot] = kz[row];
-    hb[128 * (size_t)D + 320 + slot] = vz[row];
+    hb[128 * (size_t)D + 256 + slot] = kz ? kz[row] : (uint8_t)0;
+    hb[128 * (size_t)D + 320 + slot] = vz ? vz[row] : (uint8_t)0;
 }
 
-template <int ACT, int D>
+template <int ACT, int D, int KVC>
 void launch_attn(const AttnArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
-    attn_decode_kv8_kernel<ACT, D><<<grid, dim3(64), 0, stream>>>(
+    attn_decode_kv8_kernel<ACT, D, KVC><<<grid, dim3(64), 0, stream>>>(
         a.Q, a.cache, a.num_blocks, a.table, a.table_stride, a.lens, a.Hq, a.Hkv, a.bps,
         a.splits, a.scale_log2, a.O, a.part);
     if (a.splits > 1)
@@ -363,12 +381,21 @@ void launch_attn(const AttnArgs &a, hipStream_t stream) {
             a.part, a.splits, a.B * a.Hq, a.O);
 }
 
+template <int ACT, int KVC>
+void launch_attn_kvc(const AttnArgs &a, hipStream_t stream) {
+    switch (a.D) {
+        case 64: launch_attn<ACT, 64, KVC>(a, stream); break;
+        case 256: launch_attn<ACT, 256, KVC>(a, stream); break;
+        default: launch_attn<ACT, 128, KVC>(a, stream); break;
+    }
+}
+
 template <int ACT>
 void launch_attn_act(const AttnArgs &a, hipStream_t stream) {
-    switch (a.D) {
-        case 64: launch_attn<ACT, 64>(a, stream); break;
-        case 256: launch_attn<ACT, 256>(a, stream); break;
-        default: launch_attn<ACT, 128>(a, stream); break;
+    switch (a.kv_code) {
+        case kE4M3: launch_attn_kvc<ACT, kE4M3>(a, stream); break;
+        case kE5M2: launch_attn_kvc<ACT, kE5M2>(a, stream); break;
+        default: launch_attn_kvc<ACT, kU8>(a, stream); break;
     }
 }
 

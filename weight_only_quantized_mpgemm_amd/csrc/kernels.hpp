@@ -87,6 +87,7 @@ struct AttnArgs {
     const int *lens;            // [B] context lengths
     int B, Hq, Hkv, D;
     int act;
+    int kv_code;                // Code of the KV codes: kU8, kE4M3 or kE5M2
     int bps, splits;            // blocks per split, splits per (sequence, KV head)
     float scale_log2;           // softmax scale * log2(e)
     uint16_t *O;                // [B][Hq][D]

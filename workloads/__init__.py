@@ -18,7 +18,9 @@ cast to float8_e4m3fn / float8_e5m2 by torch (round to nearest even), taken as b
 as above with the range divided by 64 (so weights are about normal with the scale's
 spread).  The FP8 workload has the shapes of the Qwen3-8B projections and bf16 activations.
 KV cache (attention decode): K and V codes uniform in [0, 255], zeros uniform in
-[100, 155], scales uniform in [0.005, 0.02] (values about uniform in [-2.5, 2.5]); queries
+[100, 155], scales uniform in [0.005, 0.02] (values about uniform in [-2.5, 2.5]); FP8 KV
+codes cast as FP8 weights are, with scales uniform in [1/128, 1/32] (values about normal,
+standard deviation 0.5 to 2); queries
 standard normal in the activation format; heads and head size of Llama-3-8B (32 query
 heads, 8 KV heads, 128) unless a case says otherwise.
 Shapes are those of the layers the workloads are named after (Llama-3-8B, Llama-3-70B,
@@ -168,6 +170,18 @@ def kv_cache(B: int, T: int, Hkv: int, D: int, seed: int):
     kz = rng.integers(100, 156, (B, T, Hkv), dtype=np.uint8)
     vz = rng.integers(100, 156, (B, T, Hkv), dtype=np.uint8)
     return kc, ks, kz, vc, vs, vz
+
+
+def kv_cache_fp8(B: int, T: int, Hkv: int, D: int, fmt: str, seed: int):
+    """(kc, ks, None, vc, vs, None): FP8 codes [B, T, Hkv, D] and scales (fp16 bits)
+    [B, T, Hkv] of an FP8 KV cache in user form (no zero points)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lim = FP8_MAX[fmt]
+    kc = to_fp8_bits(np.clip(64 * rng.standard_normal((B, T, Hkv, D), dtype=np.float32), -lim, lim), fmt)
+    vc = to_fp8_bits(np.clip(64 * rng.standard_normal((B, T, Hkv, D), dtype=np.float32), -lim, lim), fmt)
+    ks = rng.uniform(1 / 128, 1 / 32, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    vs = rng.uniform(1 / 128, 1 / 32, (B, T, Hkv)).astype(np.float16).view(np.uint16)
+    return kc, ks, None, vc, vs, None
 
 
 def queries(B: int, Hq: int, D: int, dtype: str, seed: int) -> np.ndarray:
