@@ -35,8 +35,9 @@ code, no zeros).  `w2a16_per_gemm` and `w3a16_per_gemm` do it with 2-bit and 3-b
 (mpgemm_wlowbit_a16) at the Llama-3-8B shapes for M = 1 and 16, against the HBM roofline.
 `attention_kv8_decode` times mpgemm_attention_decode_kv8 (Llama-3-8B heads, one query token
 per sequence, batch x context 1 x 8192, 16 x 2048, 64 x 2048, 128 x 4096) against the HBM
-roofline (bytes: K and V codes, scales and zeros, Q, O, the block table).  None of these is
-part of `value`.
+roofline (bytes: K and V codes, scales and zeros, Q, O, the block table);
+`attention_kvfp8_decode` does the same over an E4M3 cache (mpgemm_attention_decode_kvfp8;
+no zeros).  None of these is part of `value`.
 """
 from __future__ import annotations
 
@@ -136,6 +137,65 @@ def cpu_baseline(shapes, group, m_rows=32):
                       f"dequantize + fp64 GEMM, {total_s:.1f} s"}
 
 
+def attention_pass(args, dev, stream, fp8):
+    """Times decode attention (mpgemm_attention_decode_kv8, or _kvfp8 for an FP8 format) at
+    batch x context 1 x 8192, 16 x 2048, 64 x 2048 and 128 x 4096 under a HIP graph."""
+    import torch
+    import weight_only_quantized_mpgemm_amd as mp
+    Hq, Hkv, D = 32, 8, 128
+    bb = mp.kv_block_bytes(Hkv, D)
+    nblocks = int(args.pool_gb * 1e9 // bb)
+    cache = torch.randint(0, 256, (nblocks * bb,), dtype=torch.uint8, device=dev)
+    if fp8:
+        cache &= 0xF7          # finite E4M3 and E5M2 codes (no all-ones exponent / NaN)
+    # valid fp16 scales (0.01) in every block's scale fields
+    blk = cache.view(nblocks, Hkv, bb // Hkv)
+    blk[:, :, 128 * D:128 * D + 256].view(torch.float16).fill_(0.01)
+
+    def call(q, table, lens, T, scale, o):
+        if fp8:
+            mp.attention_decode_kvfp8(q, cache, table, lens, Hkv, T, scale, fp8, out=o)
+        else:
+            mp.attention_decode_kv8(q, cache, table, lens, Hkv, T, scale, out=o)
+
+    res, reps = [], 10
+    for B, T in ((1, 8192), (16, 2048), (64, 2048), (128, 4096)):
+        nb = (T + 63) // 64
+        ntab = min(reps, nblocks // (B * nb))
+        if ntab < 2:
+            continue
+        tabs = [torch.arange(r * B * nb, (r + 1) * B * nb, dtype=torch.int32, device=dev)
+                .view(B, nb) for r in range(ntab)]
+        tables = [tabs[r % ntab] for r in range(reps)]
+        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        q = torch.randn(B, Hq, D, device=dev).to(torch.float16)
+        o = torch.empty_like(q)
+        scale = 1.0 / D ** 0.5
+        for r in range(reps):               # warm (and allocate the workspace)
+            call(q, tables[r], lens, T, scale, o)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for r in range(reps):
+                call(q, tables[r], lens, T, scale, o)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        # codes, fp16 scales (and 8-bit zeros: none for FP8), Q and O, the block table
+        per_tok = 2 * D + 4 + (0 if fp8 else 2)
+        by = B * Hkv * T * per_tok + 2 * B * Hq * D * 2 + B * nb * 4
+        res.append({"B": B, "context": T, "heads": [Hq, Hkv, D], "us": round(t * 1e6, 2),
+                    "gbps": round(by / t / 1e9, 1), "bound": "hbm",
+                    "frac": round(by / t / 1e9 / HBM_PEAK_GBPS, 4)})
+        del gr
+    del cache, blk
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,7 +213,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8-weight per-GEMM pass (E4M3, Qwen3-8B shapes)")
     ap.add_argument("--no-attention", action="store_true",
-                    help="skip the attention-decode pass (8-bit KV cache)")
+                    help="skip the attention-decode passes (8-bit and FP8 KV caches)")
     ap.add_argument("--no-lowbit", action="store_true",
                     help="skip the 2-bit and 3-bit per-GEMM passes (Llama-3-8B shapes, M=1,16)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -436,51 +496,14 @@ def main():
                 ms=(1, 16))
             del layerb
 
-    # Decode attention over the packed 8-bit KV cache (Llama-3-8B heads: 32 query, 8 KV, 128
-    # wide), one query token per sequence.  Calls rotate through block tables that point
-    # into a pool of blocks larger than the Infinity Cache, so KV bytes come from HBM.
-    attn = []
+    # Decode attention over the packed 8-bit and FP8 (E4M3) KV caches (Llama-3-8B heads: 32
+    # query, 8 KV, 128 wide), one query token per sequence.  Calls rotate through block
+    # tables that point into a pool of blocks larger than the Infinity Cache, so KV bytes
+    # come from HBM.
+    attn, attn_fp8 = [], []
     if not args.no_attention:
-        Hq, Hkv, D = 32, 8, 128
-        bb = mp.kv_block_bytes(Hkv, D)
-        nblocks = int(args.pool_gb * 1e9 // bb)
-        cache = torch.randint(0, 256, (nblocks * bb,), dtype=torch.uint8, device=dev)
-        # valid fp16 scales (0.01) in every block's scale fields
-        blk = cache.view(nblocks, Hkv, bb // Hkv)
-        blk[:, :, 128 * D:128 * D + 256].view(torch.float16).fill_(0.01)
-        reps = 10
-        for B, T in ((1, 8192), (16, 2048), (64, 2048), (128, 4096)):
-            nb = (T + 63) // 64
-            ntab = min(reps, nblocks // (B * nb))
-            if ntab < 2:
-                continue
-            tabs = [torch.arange(r * B * nb, (r + 1) * B * nb, dtype=torch.int32, device=dev)
-                    .view(B, nb) for r in range(ntab)]
-            tables = [tabs[r % ntab] for r in range(reps)]
-            lens = torch.full((B,), T, dtype=torch.int32, device=dev)
-            q = torch.randn(B, Hq, D, device=dev).to(torch.float16)
-            o = torch.empty_like(q)
-            scale = 1.0 / D ** 0.5
-            for r in range(reps):           # warm (and allocate the workspace)
-                mp.attention_decode_kv8(q, cache, tables[r], lens, Hkv, T, scale, out=o)
-            torch.cuda.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                for r in range(reps):
-                    mp.attention_decode_kv8(q, cache, tables[r], lens, Hkv, T, scale, out=o)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            gr.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / reps
-            by = B * Hkv * T * (2 * D + 6) + 2 * B * Hq * D * 2 + B * nb * 4
-            attn.append({"B": B, "context": T, "heads": [Hq, Hkv, D], "us": round(t * 1e6, 2),
-                         "gbps": round(by / t / 1e9, 1), "bound": "hbm",
-                         "frac": round(by / t / 1e9 / HBM_PEAK_GBPS, 4)})
-            del gr
-        del cache, blk
+        attn = attention_pass(args, dev, stream, None)
+        attn_fp8 = attention_pass(args, dev, stream, "e4m3")
 
     dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
@@ -509,6 +532,7 @@ def main():
         "wfp8a16_qwen3_8b_per_gemm": fp8,
         **lowbit,
         "attention_kv8_decode": attn,
+        "attention_kvfp8_decode": attn_fp8,
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:

@@ -643,25 +643,54 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-    // Result element j of block (nb, mb) in lane l: n = 32 nb + 8 (j / 4) + 4 (l / 32) + j % 4
-    // of the wave's 32 NB columns, m = 32 mb + l % 32.
-    const int n_wave = strip0 * 16;
+    // Epilogue through LDS.  Result element j of block (nb, mb) in lane l is
+    // n = 32 nb + 8 (j / 4) + 4 (l / 32) + j % 4 of the wave's 32 NB columns and
+    // m = 32 mb + l % 32: written out directly, every store would put 8 bytes into each of
+    // 32 rows, and the memory system then writes partly filled lines back.  Instead the
+    // workgroup's BM x BN result tile (64 KiB, rounded to the output format) goes into the
+    // activation ring, free once every wave has passed the barrier, and comes back as
+    // whole rows: each 16-byte store of a wave covers complete lines.  16-byte chunk c of
+    // tile row r sits at chunk c ^ (r % 16), so the 8-byte writes of 16 rows and the
+    // 16-byte reads of a row each spread over all 64 banks.
+    __syncthreads();
+    {
+        constexpr int CPR = BN / 8;              // 16-byte chunks per tile row
+        static_assert(BM * BN * 2 <= (int)sizeof(xs), "the result tile fits the ring");
+        u32x2_t *ot = reinterpret_cast<u32x2_t *>(&xs[0][0]);
+        const int half = lane >> 5;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n_wave + nb * 32 + 8 * q + 4 * (lane >> 5);
-            if (n >= Ny) continue;
+            for (int q = 0; q < 4; ++q) {
+                const int c = wave * 4 * NB + 4 * nb + q;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int m = m_blk + mb * 32 + (lane & 31);
-                if (m < M) {
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int r = mb * 32 + (lane & 31);
                     const f32x4_t v = {acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
                                        acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]};
-                    store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, v);
+                    ot[2 * (r * CPR + (c ^ (r & 15))) + half] = round4<ACT>(v);
                 }
             }
+        __syncthreads();
+        const u32x4_t *oc = &xs[0][0];
+        const int n_blk = nt * BN;
+        const bool aligned = (Ny & 7) == 0;
+#pragma unroll
+        for (int i = 0; i < BM * CPR / kXThreads; ++i) {
+            const int idx = i * kXThreads + tid;
+            const int r = idx / CPR, c = idx % CPR;
+            const int m = m_blk + r, n = n_blk + 8 * c;
+            if (m >= M || n >= Ny) continue;
+            const u32x4_t v = oc[r * CPR + (c ^ (r & 15))];
+            uint16_t *p = Y + (size_t)m * Ny + n;
+            if (aligned && n + 8 <= Ny) {
+                *reinterpret_cast<u32x4_t *>(p) = v;
+            } else {
+                const int avail = min(8, Ny - n);
+                for (int e = 0; e < avail; ++e) p[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
         }
+    }
 }
 
 // Stage-loop length of the kernel: the packed K rounded up to a multiple of 256.
