@@ -126,15 +126,20 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
                   void *stream);
 
 /*
- * Device workspace (bytes) mpgemm_w4a16 and mpgemm_w4a16_config need for this problem:
- * nonzero only when a small-M kernel splits K over several workgroups (the largest need of
- * the configurations that can run M rows, and of 64-row chunks when M > 64).  The workspace holds fp32 partial sums and one
- * 32-bit counter per group of columns at its start.
+ * Device workspace (bytes) mpgemm_w4a16 and mpgemm_w4a16_config use for this problem on the
+ * current device: nonzero when a small-M kernel splits K over several workgroups (the
+ * largest need of the configurations that can run M rows, and of 64-row chunks when
+ * M > 64), or when a tiled kernel (M > 64) splits the K range of the tiles of its last,
+ * partial round of workgroups.  The workspace holds arrival counters in its first 256 KiB
+ * and fp32 partial sums after them.
  *   - It must be all zero before its first use; every call leaves the counters zero again,
  *     so one zeroed allocation serves any number of later calls.
  *   - Calls that share a workspace must not run concurrently (use one per stream).
- *   - Passing less than this size (or NULL when it is nonzero) returns
- *     MPGEMM_ERR_WORKSPACE and enqueues nothing.
+ *   - For a small-M kernel, passing less than its need (or NULL when it is nonzero)
+ *     returns MPGEMM_ERR_WORKSPACE and enqueues nothing.  The tiled kernels' split is
+ *     optional: with less workspace they run every tile whole (the same result up to the
+ *     order in which fp32 partial sums are added).  Results are deterministic for a given
+ *     shape, device and workspace size.
  */
 size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype);
 

@@ -202,7 +202,7 @@ def test_attention_leaves_the_gemm_workspace_zero():
     c = Cache(kv, lens, 8, 128, 62)
     ws = mp.workspace_for(torch.device("cuda"), 1 << 20)
     run(q, c, lens, 8, 0.1, "f16")
-    assert int(ws.count_nonzero()) == 0
+    assert int(ws[:256 * 1024].count_nonzero()) == 0          # the arrival counters
 
 
 # ------------------------------------------------------------------ FP8 KV cache ----------

@@ -118,6 +118,7 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     a.group = group;
     a.act = dtype == MPGEMM_BF16 ? mpgemm::kBF16 : mpgemm::kF16;
     a.workspace = workspace;
+    a.workspace_bytes = workspace ? workspace_bytes : 0;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4) {
         const size_t need = mpgemm::decode_workspace_bytes(M, N, K, cfg);
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
@@ -216,6 +217,8 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
     if (M > 64) {                   // 2- and 3-bit codes: 64-row chunks of the small-M kernel
         const size_t b = mpgemm::decode_workspace_bytes(64, N, K, 4);
         if (b > need) need = b;
+        const size_t x = mpgemm::x32_workspace_bytes(M, N, K);   // tiled kernels' last round
+        if (x > need) need = x;
     }
     return need;
 }

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(
 // one 1 KiB fp32 block per (strip, row block, split).  The counter region has the same size
 // for every shape, so partials of one call never land on counters of another call that
 // shares the workspace (counters must read zero at every call's start).
-constexpr size_t kCounterBytes = 256 * 1024;
+constexpr size_t kCounterBytes = kSplitCounterBytes;
 constexpr int kMaxGroups = (int)(kCounterBytes / 4);
 
 // Strips per workgroup (S), waves per workgroup (NW) and workgroups per strip group along

@@ -23,6 +23,17 @@ hipError_t launch_prefill_x32_u4(const GemmArgs &a, int nb, hipStream_t stream) 
     return hipGetLastError();
 }
 
+size_t x32_workspace_bytes(int M, int N, int K) {
+    const int loop_k = x32_loop_k(padded_k(K)), Np = padded_n(N);
+    size_t need = 0;
+    for (int nb = 1; nb <= 2; ++nb) {
+        const int tiles = ((Np + tile_n(nb) - 1) / tile_n(nb)) * ((M + tile_m(nb) - 1) / tile_m(nb));
+        const size_t b = x32_split_bytes(x32_split(tiles, loop_k, K != loop_k, device_cus()), tiles, nb);
+        if (b > need) need = b;
+    }
+    return need;
+}
+
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) { return by_code(a, 2, stream); }
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream) {
     return by_code(a, 1, stream);

@@ -53,8 +53,14 @@ struct GemmArgs {
     int Kp, Np;                 // padded shape of the packed planes
     int act;                    // Act
     int code;                   // Code: format of the packed codes
-    void *workspace;            // decode split-K partials and counters (see decode kernel)
+    void *workspace;            // split-K partials and counters (decode and tiled kernels)
+    size_t workspace_bytes;     // its size (0 without a workspace)
 };
+
+// Both split-K schemes keep their arrival counters in the first kSplitCounterBytes of the
+// workspace and their partials after it.  The counters must be zero before the first call;
+// every call leaves them zero.
+constexpr size_t kSplitCounterBytes = 256 * 1024;
 
 // Small-M kernel: one 16-column strip per workgroup, the K range split over the waves of the
 // workgroup, `mblocks` row blocks of 16 (M <= 16 * mblocks, mblocks in 1..4).
@@ -75,6 +81,9 @@ hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill_x32_u4(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill_x32_u8(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream);
+// Workspace bytes with which the 32x32x16 kernels (either tile shape) split the K range of
+// their last, partial round of tiles; 0 when they never do for this shape.  N, K: user shape.
+size_t x32_workspace_bytes(int M, int N, int K);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
 // Decode attention over an 8-bit KV cache (attention.hip).

@@ -48,6 +48,7 @@
 // translation units instantiate it per code format (they compile in parallel).
 #pragma once
 
+#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
@@ -328,12 +329,15 @@ template <int ACT, bool SYM, int G, int NWS, int NB, int CODE, bool RAG>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    int Kw, int Kx, int Ny, uint16_t *__restrict__ Y) {
+    int Kw, int Kx, int Ny, uint16_t *__restrict__ Y, int full, int P, float *__restrict__ part) {
     // N: the padded column count of the packed planes; Kw: their padded K (a multiple of
     // 128); K: the loop length, Kw rounded up to a multiple of 256 (the stage loop runs
     // blocks of four 64-deep stages; a 128-deep tile past Kw re-reads the last weight tile
     // against activations that read as zero, adding exact zeros); Kx: activation row length
     // (the user K); Ny: output row length (the user N).
+    // full, P, part: workgroups past the first `full` take 1/P of the K range of one tile
+    // each (P consecutive workgroups per tile; P = 1: no split) and store fp32 partials in
+    // `part` instead of Y.
     typedef typename Dq<ACT>::type DqT;       // the same constants type for every code format
     typedef typename DqOpsSel<ACT, CODE>::type Ops;
     typedef DqFor<ACT, CODE> DqB;
@@ -354,11 +358,19 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    int mt, nt;
-    tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
+    int mt, nt, bid = blockIdx.x, sidx = 0, sp = 0;
+    const int parts = bid >= full ? P : 1;   // K-range parts of this workgroup's tile
+    if (parts > 1) {
+        sidx = (bid - full) / P;             // split tile index
+        sp = (bid - full) % P;               // which part of its K range
+        bid = full + sidx;
+    }
+    tile_of(bid, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
     const int m_blk = mt * BM;
     const int KT = Kw >> 7;                  // 128-deep weight tiles in the packed planes
-    const int S = K >> 6;                    // 64-deep stages (a multiple of 4)
+    const int S = (K >> 6) / parts;          // 64-deep stages of this part (a multiple of 4)
+    const int t0 = sp * (S >> 1);            // its first weight tile (S = 2 tiles' stages)
+    const int KTl = parts > 1 ? S >> 1 : KT; // weight tiles it may read (loads clamp to them)
     const int groups = Kw / G;
     const int strips = N >> 4;
     const int strip0 = nt * (BN / 16) + wave * 2 * NB;
@@ -380,13 +392,14 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     for (int i = 0; i < MB; ++i) {
         const int r = 8 * (wave * MB + i) + (lane >> 3);
         const uint32_t row = (uint32_t)min(m_blk + r, M);
-        xoff[i] = (row * Kx + (((lane & 7) ^ (lane >> 3)) * 8)) * 2u;
+        xoff[i] = (row * Kx + (((lane & 7) ^ (lane >> 3)) * 8) + t0 * 128) * 2u;
     }
     // Ragged K: first k of the lane's chunk within a stage.
     const int k_chunk = ((lane & 7) ^ (lane >> 3)) * 8;
     // Weight slots: column block nb (strips strip0 + 2nb, +1), k half u.  Strips past N
     // read the last real strip; their results are never stored.
     const int my_strip_in_pair = (lane & 31) >> 4;
+    constexpr int zrow = 16 * BITS / 8;                // zero bytes per (strip, group)
     uint32_t woff[2][2], soff[2], zoff[2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -394,18 +407,17 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const uint32_t pos = (lane & 15) + 16 * (2 * u + (lane >> 5));
-            woff[nb][u] = strip * KT * 1024u * WV + pos * 16u;
+            woff[nb][u] = (strip * KT + t0) * 1024u * WV + pos * 16u;
         }
         const uint32_t e = strip * groups * 16u + (lane & 15);
-        soff[nb] = (e >> 1) * 4u;
-        zoff[nb] = BITS == 4 ? (e >> 3) * 4u : (e >> 2) * 4u;
+        soff[nb] = (e >> 1) * 4u + t0 * GPT * 32u;
+        zoff[nb] = (BITS == 4 ? (e >> 3) * 4u : (e >> 2) * 4u) + t0 * GPT * zrow;
     }
     const uint32_t sshift = (lane & 1) * 16;
     // A lane's zero is nibble (lane & 7) of a dword (4-bit codes) or byte (lane & 3).
     const uint32_t zshift = BITS == 4 ? (lane & 7) * 4 : (lane & 3) * 8;
     constexpr uint32_t zmask = (1u << BITS) - 1;
     constexpr uint32_t zsym = 1u << (BITS - 1);        // symmetric zero: 8 or 128
-    constexpr int zrow = 16 * BITS / 8;                // zero bytes per (strip, group)
     // B operand: row 32 mb + lane % 32, logical chunk 4s + 2u + lane / 32 of the stage;
     // physical chunk = logical ^ (lane % 8) = (4s + 2u) ^ cb.
     const int brow = (lane & 31) * 8;
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // Load j (of kWLoads) of weight tile t: the 2 NB code slots, then scales and zeros.
     auto load_w_part = [&](int t, WSet &w, auto J) __attribute__((always_inline)) {
         constexpr int j = decltype(J)::value;
-        t = min(t, KT - 1);
+        t = min(t, KTl - 1);
         if constexpr (j < 2 * NB * WV) {
             constexpr int nb = j / (2 * WV), u = (j / WV) % 2, v = j % WV;
             w.w[nb][u][v] = buf_load_b128(wrs, woff[nb][u], (t * WV + v) * 1024);
@@ -643,6 +655,23 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
+    // Split tile: store this part's fp32 accumulators in register order (chunk i of the
+    // lane's 32 four-float chunks at i * 256 + thread, so every store instruction writes
+    // 1 KiB in one piece) and stop; x32_split_reduce_kernel adds the P parts afterwards.
+    if (parts > 1) {
+        constexpr int kChunksPerPart = BM * BN / 4;
+        f32x4_t *dst = reinterpret_cast<f32x4_t *>(part) + (size_t)(sidx * P + sp) * kChunksPerPart;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dst[((nb * MB + mb) * 4 + q) * kXThreads + tid] =
+                        f32x4_t{acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
+                                acc[nb][mb][4 * q + 3]};
+        return;
+    }
     // Epilogue through LDS.  Result element j of block (nb, mb) in lane l is
     // n = 32 nb + 8 (j / 4) + 4 (l / 32) + j % 4 of the wave's 32 NB columns and
     // m = 32 mb + l % 32: written out directly, every store would put 8 bytes into each of
@@ -693,15 +722,107 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     }
 }
 
+// Y of the split tiles: the sum of their P fp32 partials, in split order (so results do not
+// depend on which part ran first), rounded once to the output format.  One workgroup per
+// (tile, register-order chunk): thread `tid` reads the four floats that thread `tid` of the
+// main kernel wrote for that chunk -- all P loads issued before the first add -- and knows
+// their (m, n) the same way.
+template <int ACT, int NB>
+__global__ __launch_bounds__(kXThreads) void x32_split_reduce_kernel(
+    const f32x4_t *__restrict__ part, int full, int P, int M, int N, int Ny,
+    uint16_t *__restrict__ Y) {
+    constexpr int MB = 8 / NB, BM = tile_m(NB), BN = tile_n(NB);
+    constexpr int kChunksPerPart = BM * BN / 4;
+    constexpr int kMaxParts = 8;
+    const int sidx = blockIdx.x >> 5, i = blockIdx.x & 31;
+    int mt, nt;
+    tile_of(full + sidx, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const f32x4_t *src = part + (size_t)sidx * P * kChunksPerPart + i * kXThreads + tid;
+    f32x4_t v[kMaxParts];
+#pragma unroll
+    for (int o = 0; o < kMaxParts; ++o)
+        if (o < P) v[o] = src[(size_t)o * kChunksPerPart];
+    f32x4_t s = v[0];
+#pragma unroll
+    for (int o = 1; o < kMaxParts; ++o)
+        if (o < P) s += v[o];
+    const int nb = i / (4 * MB), mb = (i / 4) % MB, q = i % 4;
+    const int n = nt * BN + wave * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
+    const int m = mt * BM + mb * 32 + (lane & 31);
+    if (m < M && n < Ny) store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, s);
+}
+
 // Stage-loop length of the kernel: the packed K rounded up to a multiple of 256.
 inline int x32_loop_k(int Kp) { return (Kp + 255) / 256 * 256; }
 
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Fewer tiles than compute units.  One workgroup fills a compute unit (its registers take
+// the whole SIMD), so T < CUs tiles leave CUs - T units idle.  Splitting each tile's K
+// range P ways (T P <= CUs) runs the tiles in about 1/P of the time, for one fp32 partial
+// of the tile per part, written to the workspace (past its counter region, which the
+// small-M kernels use) and added up by a second, small kernel.  Parts keep at least 1024
+// of K (the pipeline's prologue and epilogue stay small against the loop) and whole
+// 256-deep blocks of the stage loop.  A partial last round of a larger grid is left alone:
+// under the chip's power limit the busy units of such a round run at a higher clock, and
+// splitting it (measured at 2048 x 4096 x 6144: 384 tiles) saved less than the partials
+// cost.  MPGEMM_X32_SPLIT=0 turns the split off.
+struct X32Split {
+    int full, p;                             // tiles run whole; parts per remaining tile
+};
+inline X32Split x32_split(int tiles, int loop_k, bool rag, int cus) {
+    X32Split sp{tiles, 1};
+    if (rag || cus <= 0) return sp;
+    if (const char *env = getenv("MPGEMM_X32_SPLIT"))
+        if (env[0] == '0') return sp;
+    if (tiles >= cus) return sp;
+    const int r = tiles;
+    for (int p = 8; p >= 2; p /= 2)
+        if (r * p <= cus && loop_k % (256 * p) == 0 && loop_k / p >= 1024) {
+            sp.full = tiles - r;
+            sp.p = p;
+            break;
+        }
+    return sp;
+}
+inline size_t x32_split_bytes(const X32Split &sp, int tiles, int nb) {
+    if (sp.p == 1) return 0;
+    return kSplitCounterBytes + (size_t)(tiles - sp.full) * sp.p * tile_m(nb) * tile_n(nb) * 4;
+}
+
 template <int ACT, bool SYM, int G, int NB, int CODE, bool RAG>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const dim3 grid(((a.Np + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB)));
+    const int tiles = ((a.Np + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB));
+    const int loop_k = x32_loop_k(a.Kp);
+    X32Split sp = x32_split(tiles, loop_k, RAG, device_cus());
+    const size_t need = x32_split_bytes(sp, tiles, NB);
+    if (need > a.workspace_bytes || a.workspace == nullptr ||
+        ((uintptr_t)a.workspace & 15u) != 0)
+        sp = X32Split{tiles, 1};
+    float *part = sp.p > 1 ? reinterpret_cast<float *>(static_cast<char *>(a.workspace) +
+                                                       kSplitCounterBytes)
+                           : nullptr;
+    const dim3 grid((unsigned)(sp.full + (tiles - sp.full) * sp.p));
     prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG>
         <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
-                                               x32_loop_k(a.Kp), a.Kp, a.K, a.N, a.Y);
+                                               loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p, part);
+    if (sp.p > 1)
+        x32_split_reduce_kernel<ACT, NB><<<dim3((unsigned)(tiles - sp.full) * 32), dim3(kXThreads),
+                                           0, stream>>>(reinterpret_cast<const f32x4_t *>(part),
+                                                        sp.full, sp.p, a.M, a.Np, a.N, a.Y);
 }
 
 template <int ACT, int NB, int CODE, bool RAG>
