@@ -144,7 +144,8 @@ def attention_pass(args, dev, stream, fp8):
     import weight_only_quantized_mpgemm_amd as mp
     Hq, Hkv, D = 32, 8, 128
     bb = mp.kv_block_bytes(Hkv, D)
-    nblocks = int(args.pool_gb * 1e9 // bb)
+    # at least two block tables of the largest case (128 x 4096: 1.1 GB each)
+    nblocks = int(max(args.pool_gb, 2.5) * 1e9 // bb)
     cache = torch.randint(0, 256, (nblocks * bb,), dtype=torch.uint8, device=dev)
     if fp8:
         cache &= 0xF7          # finite E4M3 and E5M2 codes (no all-ones exponent / NaN)
