@@ -104,6 +104,20 @@ def weights(K: int, N: int, group: int, symmetric: bool, scale_lo: float, scale_
     return codes, scales.view(np.uint16), zeros
 
 
+def device_case(M: int, K: int, N: int, group: int, seed: int, device):
+    """Inputs too large to draw on the host quickly, drawn on `device` by torch's seeded
+    generator with the recipe of `weights` / `activations` (codes and zeros uniform in
+    0..15, scales uniform in [0.005, 0.02] rounded to fp16, X standard normal rounded to
+    fp16): (x fp16 [M,K], codes uint8 [K,N], scales fp16 [K/g,N], zeros uint8 [K/g,N])."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    codes = torch.randint(0, 16, (K, N), dtype=torch.uint8, device=device, generator=gen)
+    scales = (torch.rand((K // group, N), device=device, generator=gen) * 0.015 + 0.005).half()
+    zeros = torch.randint(0, 16, (K // group, N), dtype=torch.uint8, device=device, generator=gen)
+    x = torch.randn((M, K), device=device, generator=gen, dtype=torch.float16)
+    return x, codes, scales, zeros
+
+
 def weights_w8(K: int, N: int, group: int, symmetric: bool, scale_lo: float, scale_hi: float,
                seed: int):
     """8-bit codes: (codes uint8 [K,N] in 0..255, scales fp16 bits [K/g,N] drawn in
