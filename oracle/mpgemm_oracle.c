@@ -683,37 +683,41 @@ void oracle_attention_decode_kvfp8(const uint16_t *q, const uint8_t *kc, const u
 /*
  * Packed KV cache (restated from its specification in include/mpgemm.h).  Blocks of 64
  * tokens of one sequence, all KV heads; block j of sequence b is cache block
- * table[b][j].  Within a block, KV head h occupies HB = 128*D + 384 bytes at h*HB:
- *   bytes [0, 64*D):      K codes of the 64 tokens, in the 8-bit weight layout of the
- *                         D x 64 matrix K^T (k = d, n = token);
- *   bytes [64*D, 128*D):  V codes, in the 8-bit weight layout of the 64 x D matrix V
- *                         (k = token, n = d) -- V stored transposed for the matrix cores;
+ * table[b][j].  A head of D values (D a multiple of 16) is stored padded to
+ * Dp = D rounded up to a multiple of 64, the k depth of one 8-bit tile, with codes 0 at
+ * d >= D.  Within a block, KV head h occupies HB = 128*Dp + 384 bytes at h*HB:
+ *   bytes [0, 64*Dp):       K codes of the 64 tokens, in the 8-bit weight layout of the
+ *                           Dp x 64 matrix K^T (k = d, n = token);
+ *   bytes [64*Dp, 128*Dp):  V codes, in the 8-bit weight layout of the 64 x Dp matrix V
+ *                           (k = token, n = d) -- V stored transposed for the matrix cores;
  *   then K scales [64] fp16, V scales [64] fp16, K zeros [64] uint8, V zeros [64] uint8.
- * D is a multiple of 64.
  */
-size_t oracle_kv_block_bytes(int Hkv, int D) { return (size_t)Hkv * (128 * (size_t)D + 384); }
+static size_t kv_padded_d(int D) { return (size_t)(D + 63) / 64 * 64; }
+
+size_t oracle_kv_block_bytes(int Hkv, int D) { return (size_t)Hkv * (128 * kv_padded_d(D) + 384); }
 
 /* Writes tokens t0 .. t0 + n - 1 of one sequence (user form kc, vc [n][Hkv][D]; ks, vs,
- * kz, vz [n][Hkv]) into the cache through that sequence's block-table row. */
+ * kz, vz [n][Hkv]) into the cache through that sequence's block-table row, codes 0 in the
+ * padding d = D .. Dp-1. */
 void oracle_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, const uint8_t *vc,
                     const uint16_t *vs, const uint8_t *vz, int n, int t0, int Hkv, int D,
                     const int *table_row, uint8_t *cache) {
-    const size_t HB = 128 * (size_t)D + 384;
+    const size_t Dp = kv_padded_d(D), HB = 128 * Dp + 384;
     for (int i = 0; i < n; ++i) {
         const int t = t0 + i, slot = t % 64;
         uint8_t *blk = cache + (size_t)table_row[t / 64] * oracle_kv_block_bytes(Hkv, D);
         for (int h = 0; h < Hkv; ++h) {
             uint8_t *hb = blk + h * HB;
             const size_t row = (size_t)i * Hkv + h;
-            for (int d = 0; d < D; ++d) {
-                hb[code8_byte_offset(d, slot, D)] = kc[row * D + d];
-                hb[64 * (size_t)D + code8_byte_offset(slot, d, 64)] = vc[row * D + d];
+            for (int d = 0; d < (int)Dp; ++d) {
+                hb[code8_byte_offset(d, slot, (int)Dp)] = d < D ? kc[row * D + d] : 0;
+                hb[64 * Dp + code8_byte_offset(slot, d, 64)] = d < D ? vc[row * D + d] : 0;
             }
-            uint16_t *sc = (uint16_t *)(hb + 128 * (size_t)D);
+            uint16_t *sc = (uint16_t *)(hb + 128 * Dp);
             sc[slot] = ks[row];
             sc[64 + slot] = vs[row];
-            hb[128 * (size_t)D + 256 + slot] = kz[row];
-            hb[128 * (size_t)D + 320 + slot] = vz[row];
+            hb[128 * Dp + 256 + slot] = kz[row];
+            hb[128 * Dp + 320 + slot] = vz[row];
         }
     }
 }
@@ -722,7 +726,7 @@ void oracle_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, co
 void oracle_kv_unpack(const uint8_t *cache, const int *table_row, int T, int Hkv, int D,
                       uint8_t *kc, uint16_t *ks, uint8_t *kz, uint8_t *vc, uint16_t *vs,
                       uint8_t *vz) {
-    const size_t HB = 128 * (size_t)D + 384;
+    const size_t Dp = kv_padded_d(D), HB = 128 * Dp + 384;
     for (int t = 0; t < T; ++t) {
         const int slot = t % 64;
         const uint8_t *blk = cache + (size_t)table_row[t / 64] * oracle_kv_block_bytes(Hkv, D);
@@ -730,14 +734,14 @@ void oracle_kv_unpack(const uint8_t *cache, const int *table_row, int T, int Hkv
             const uint8_t *hb = blk + h * HB;
             const size_t row = (size_t)t * Hkv + h;
             for (int d = 0; d < D; ++d) {
-                kc[row * D + d] = hb[code8_byte_offset(d, slot, D)];
-                vc[row * D + d] = hb[64 * (size_t)D + code8_byte_offset(slot, d, 64)];
+                kc[row * D + d] = hb[code8_byte_offset(d, slot, (int)Dp)];
+                vc[row * D + d] = hb[64 * Dp + code8_byte_offset(slot, d, 64)];
             }
-            const uint16_t *sc = (const uint16_t *)(hb + 128 * (size_t)D);
+            const uint16_t *sc = (const uint16_t *)(hb + 128 * Dp);
             ks[row] = sc[slot];
             vs[row] = sc[64 + slot];
-            kz[row] = hb[128 * (size_t)D + 256 + slot];
-            vz[row] = hb[128 * (size_t)D + 320 + slot];
+            kz[row] = hb[128 * Dp + 256 + slot];
+            vz[row] = hb[128 * Dp + 320 + slot];
         }
     }
 }

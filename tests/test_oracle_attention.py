@@ -208,6 +208,41 @@ def test_kv_pack_in_pieces_through_a_block_table_round_trips():
     assert all((cache[i * bb:(i + 1) * bb] == 0).all() for i in untouched)
 
 
+@pytest.mark.parametrize("D", [16, 48, 80, 96, 112, 160, 192, 208])
+def test_kv_head_of_any_multiple_of_16_is_stored_as_the_zero_padded_head(D):
+    """A head of D values is laid out exactly as the head zero-padded to the next multiple
+    of 64 (the k depth of one 8-bit tile), and unpacks back to the D values."""
+    Hkv, T = 2, 70
+    Dp = -(-D // 64) * 64
+    kv = [a[0] for a in rand_kv(1, T, Hkv, D, D + 3)]
+    assert oracle.kv_block_bytes(Hkv, D) == Hkv * (128 * Dp + 384)
+    table = np.array([1, 0], np.int32)
+    cache = np.full(2 * oracle.kv_block_bytes(Hkv, D), 0xAB, np.uint8)
+    oracle.kv_pack(cache, table, 0, *kv)
+    pad = [np.pad(a, ((0, 0), (0, 0), (0, Dp - D))) if a.ndim == 3 else a for a in kv]
+    want = np.full(2 * oracle.kv_block_bytes(Hkv, Dp), 0xAB, np.uint8)
+    oracle.kv_pack(want, table, 0, *pad)
+    assert np.array_equal(cache, want)
+    for x, y in zip(kv, oracle.kv_unpack(cache, table, T, Hkv, D)):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("D", [48, 96])
+def test_attention_of_a_head_equals_that_of_the_zero_padded_head(D):
+    """Zero query elements and any values past D change no score, and value columns past D
+    feed only outputs past D: the outputs are the padded head's first D, bit for bit."""
+    B, Hq, Hkv, T = 2, 8, 2, 90
+    Dp = -(-D // 64) * 64
+    kc, ks, kz, vc, vs, vz = rand_kv(B, T, Hkv, D, D + 5)
+    q = rand_q(B, Hq, D, D + 6)
+    lens = [90, 33]
+    o = oracle.attention_decode_kv8(q, kc, ks, kz, vc, vs, vz, lens, 0.125)
+    padc = lambda a: np.pad(a, ((0, 0), (0, 0), (0, 0), (0, Dp - D)))
+    qp = np.pad(q, ((0, 0), (0, 0), (0, Dp - D)))
+    op = oracle.attention_decode_kv8(qp, padc(kc), ks, kz, padc(vc), vs, vz, lens, 0.125)
+    assert np.array_equal(o, op[..., :D])
+
+
 # ------------------------------------------------------------- FP8 KV cache ---------
 
 import torch  # noqa: E402

@@ -112,10 +112,14 @@ MUTANTS_ATTENTION = {
                       "double vd = (double)((int)vc[row * D + d] - (int)vz[row]) * s_v;"),
     "last_token_dropped": ("            for (int t = 0; t < len; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double s_v",
                            "            for (int t = 0; t < len - 1; ++t) {\n                const size_t row = ((size_t)b * Tmax + t) * Hkv + hk;\n                const double s_v"),
-    "kv_v_not_transposed": ("hb[64 * (size_t)D + code8_byte_offset(slot, d, 64)] = vc[row * D + d];",
-                            "hb[64 * (size_t)D + code8_byte_offset(d, slot, D)] = vc[row * D + d];"),
-    "kv_zeros_swapped": ("hb[128 * (size_t)D + 256 + slot] = kz[row];",
-                         "hb[128 * (size_t)D + 320 + slot] = kz[row];"),
+    "kv_v_not_transposed": ("hb[64 * Dp + code8_byte_offset(slot, d, 64)] = d < D ? vc[row * D + d] : 0;",
+                            "hb[64 * Dp + code8_byte_offset(d, slot, (int)Dp)] = d < D ? vc[row * D + d] : 0;"),
+    "kv_zeros_swapped": ("hb[128 * Dp + 256 + slot] = kz[row];",
+                         "hb[128 * Dp + 320 + slot] = kz[row];"),
+    "kv_pad_not_zero": ("hb[code8_byte_offset(d, slot, (int)Dp)] = d < D ? kc[row * D + d] : 0;",
+                        "hb[code8_byte_offset(d, slot, (int)Dp)] = d < D ? kc[row * D + d] : 128;"),
+    "kv_unpadded_head": ("static size_t kv_padded_d(int D) { return (size_t)(D + 63) / 64 * 64; }",
+                         "static size_t kv_padded_d(int D) { return (size_t)(D + 15) / 16 * 16; }"),
     "kvfp8_format_swap": ("double e8 = format == 1 ? oracle_e5m2_to_f64(c8) : oracle_e4m3_to_f64(c8);\n                    acc[d]",
                           "double e8 = format == 0 ? oracle_e5m2_to_f64(c8) : oracle_e4m3_to_f64(c8);\n                    acc[d]"),
     "kvfp8_v_scale": ("const double sv8 = oracle_f16_to_f64(vs[row]);",
