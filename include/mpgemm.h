@@ -332,17 +332,21 @@ int mpgemm_wlowbit_a16_config(int bits, const void *X, int dtype, const void *pa
  * Quantized KV (the caller's form, per token):
  *   kc, vc  uint8 [n][Hkv][D] codes;  ks, vs  fp16 [n][Hkv] scales;  kz, vz  uint8 [n][Hkv]
  *   zeros: k[t][d] = (kc - kz[t]) * ks[t] rounded once to the activation format, v alike.
+ * Head sizes (adaptive head alignment [TurboMind abstract, technique (ii); Fig. 24 caption:
+ * padding for MMA data misalignment]): D is any multiple of 16 from 16 to 256; a head is
+ * stored padded to Dp = D rounded up to a multiple of 64 (the k depth of one 8-bit tile),
+ * with codes 0 at d >= D.  Q and O rows keep D values.
  * Packed KV cache: an array of blocks of 64 tokens of one sequence, all KV heads, of
- * mpgemm_kv_block_bytes(Hkv, D) = Hkv * (128*D + 384) bytes each; block j of sequence b is
+ * mpgemm_kv_block_bytes(Hkv, D) = Hkv * (128*Dp + 384) bytes each; block j of sequence b is
  * block block_table[b*table_stride + j] (token t in block t/64, slot t%64).  KV head h of a
- * block occupies HB = 128*D + 384 bytes at h*HB:
- *   [0, 64*D)        K codes in the 8-bit weight layout (above) of the D x 64 matrix K^T
+ * block occupies HB = 128*Dp + 384 bytes at h*HB:
+ *   [0, 64*Dp)       K codes in the 8-bit weight layout (above) of the Dp x 64 matrix K^T
  *                    (k = d, n = slot), i.e. 16-slot strips of 64-deep 1 KiB tiles;
- *   [64*D, 128*D)    V codes in the 8-bit weight layout of the 64 x D matrix V (k = slot,
+ *   [64*Dp, 128*Dp)  V codes in the 8-bit weight layout of the 64 x Dp matrix V (k = slot,
  *                    n = d): V transposed, so 16 values of d x 8 consecutive tokens form
  *                    one matrix-core operand;
  *   then K scales [64] fp16, V scales [64] fp16, K zeros [64] uint8, V zeros [64] uint8.
- * D is 64, 128 or 256; Hq is a multiple of Hkv with Hq/Hkv <= 16.
+ * Hq is a multiple of Hkv with Hq/Hkv <= 16.
  */
 
 /* Bytes of one cache block (0 if Hkv or D is unsupported). */

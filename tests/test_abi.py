@@ -245,3 +245,23 @@ def test_lowbit_sizes_and_pack_validation():
                                           None) == INVALID
     assert lib.mpgemm_unpack_lowbit(3, vp(A), vp(A), 256, 32, 128, 0, vp(A), vp(A), None,
                                     None) == INVALID
+
+
+def test_kv_block_bytes_pad_heads_to_a_multiple_of_64():
+    lib = mp.lib()
+    assert lib.mpgemm_kv_block_bytes(8, 128) == 8 * (128 * 128 + 384)
+    assert lib.mpgemm_kv_block_bytes(8, 96) == 8 * (128 * 128 + 384)
+    assert lib.mpgemm_kv_block_bytes(2, 16) == 2 * (128 * 64 + 384)
+    assert lib.mpgemm_kv_block_bytes(4, 192) == lib.mpgemm_kv_block_bytes(4, 176) == 4 * (128 * 192 + 384)
+    for D in (0, 8, 100, 264, 512):                       # not a multiple of 16 in 16..256
+        assert lib.mpgemm_kv_block_bytes(8, D) == 0
+    assert lib.mpgemm_kv_block_bytes(0, 128) == 0
+
+
+def test_attention_rejects_unsupported_head_sizes_before_launching():
+    lib = mp.lib()
+    for D in (8, 100, 272):
+        for fn, extra in ((lib.mpgemm_attention_decode_kv8, ()), (lib.mpgemm_attention_decode_kvfp8, (0,))):
+            args = (A, 0, *extra, A, 4, A, 1, A, 1, 8, 2, D, 64, ctypes.c_float(0.1), A, None, 0, None)
+            assert fn(*args) == UNSUPPORTED
+        assert lib.mpgemm_kv_pack(A, A, A, A, A, A, 1, 0, 2, D, A, 1, 4, A, None) == UNSUPPORTED

@@ -279,3 +279,45 @@ def test_kvfp8_rejects_an_unknown_format():
         dev(c.table).data_ptr(), c.table.shape[1], dev(np.asarray(lens, np.int32)).data_ptr(), 1, 8,
         2, 128, 5, 0.1, q_t.data_ptr(), None, 0, None)
     assert st != 0
+
+
+# ----------------------------------------------------- head sizes padded to 64 --------
+
+@pytest.mark.parametrize("D", [48, 96, 160])
+def test_kv_pack_of_padded_heads_matches_oracle_bytes(D):
+    lens, Hkv = [150, 7], 2
+    kv, _ = case(2, 4, Hkv, D, lens, "f16", D + 1)
+    c = Cache(kv, lens, Hkv, D, 9)
+    assert np.array_equal(c.gpu.cpu().numpy(), c.host)
+
+
+@pytest.mark.parametrize("D", [16, 80, 96, 112, 176, 192, 208])
+@pytest.mark.parametrize("kvfmt", [None, "e4m3"])
+@pytest.mark.parametrize("bps", [None, "1"])
+def test_attention_head_sizes_padded_to_64(D, kvfmt, bps, monkeypatch):
+    if bps:
+        monkeypatch.setenv("MPGEMM_ATTN_BPS", bps)
+    lens, Hq, Hkv = [1, 64, 65, 700, 0, 130], 16, 4
+    seed = 100 + D
+    if kvfmt is None:
+        kv, q = case(len(lens), Hq, Hkv, D, lens, "f16", seed)
+    else:
+        kv, q = case_fp8(len(lens), Hq, Hkv, D, lens, "f16", kvfmt, seed)
+    c = Cache(kv, lens, Hkv, D, seed + 1)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    say(f"attention D={D} kv={kvfmt or 'u8'} bps={bps}")
+    y = run(q, c, lens, Hkv, scale, "f16", fp8=kvfmt)
+    want = (oracle.attention_decode_kv8(q, *kv, lens, scale, "f16") if kvfmt is None
+            else fp8_ref(q, kv, lens, scale, kvfmt, "f16"))
+    assert (y[4] == 0).all()
+    ok, detail = within_value_bar(y, want, kv, lens, "f16", fp8=kvfmt)
+    assert ok, detail
+    assert rel(y, want, "f16") <= REL_TOL
+
+
+def test_one_token_context_is_bit_exact_for_a_padded_head():
+    lens, Hq, Hkv, D = [1, 1], 8, 2, 80
+    kv, q = case(2, Hq, Hkv, D, lens, "f16", 33)
+    c = Cache(kv, lens, Hkv, D, 34)
+    y = run(q, c, lens, Hkv, 0.1, "f16")
+    assert np.array_equal(y, oracle.attention_decode_kv8(q, *kv, lens, 0.1, "f16"))

@@ -144,6 +144,12 @@ def test_identity_activations_give_dequantized_weights_bit_exact(dtype, g, sym, 
     packed = pack_case(case)
     w = oracle.dequant(codes, scales, zeros, g, dtype)
     y = run(case, packed, config)
+    if not np.array_equal(y, w):
+        bad = np.argwhere(y != w)
+        print(f"[diag] identity config={config} {dtype}: {len(bad)} wrong of {y.size}; rows "
+              f"{sorted(set(bad[:, 0].tolist()))[:24]} cols {sorted(set(bad[:, 1].tolist()))[:24]}; "
+              f"first {[(int(r), int(c), int(y[r, c]), int(w[r, c])) for r, c in bad[:4]]}",
+              flush=True)
     assert np.array_equal(y, w)
 
 

@@ -379,7 +379,7 @@ int mpgemm_wlowbit_a16(int bits, const void *X, int dtype, const void *packed_co
 
 namespace {
 
-bool kv_shape_ok(int Hkv, int D) { return Hkv >= 1 && Hkv <= 1024 && (D == 64 || D == 128 || D == 256); }
+bool kv_shape_ok(int Hkv, int D) { return Hkv >= 1 && Hkv <= 1024 && D >= 16 && D <= 256 && D % 16 == 0; }
 
 // Blocks per split and splits per (sequence, KV head): about 1024 waves (one per SIMD at
 // this kernel's register use), and at most 64 splits (a wider combine costs more than it
@@ -408,7 +408,7 @@ bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 extern "C" {
 
 size_t mpgemm_kv_block_bytes(int Hkv, int D) {
-    return kv_shape_ok(Hkv, D) ? (size_t)Hkv * (128 * (size_t)D + 384) : 0;
+    return kv_shape_ok(Hkv, D) ? (size_t)Hkv * (128 * (size_t)mpgemm::kv_padded_d(D) + 384) : 0;
 }
 
 int mpgemm_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz, const uint8_t *vc,

@@ -98,7 +98,11 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ cache, int num_blocks,
     const int *__restrict__ table, int table_stride, const int *__restrict__ lens, int Hq,
     int Hkv, int bps, int splits, float scale_log2, uint16_t *__restrict__ O,
-    float *__restrict__ part) {
+    float *__restrict__ part, int Du) {
+    // D: the stored head size (a multiple of 64); Du <= D: the caller's head size (a
+    // multiple of 16), the row length of Q and O.  Query elements past Du load as zeros,
+    // so the zero codes stored past Du add nothing to a score, and outputs past Du are
+    // not stored.
     constexpr int DS = D / 32;                 // 32-deep k steps of Q K^T
     constexpr int KT = D / 64;                 // 64-deep K tiles per 16-token strip
     constexpr int VS = D / 16;                 // 16-row strips of V^T
@@ -120,11 +124,12 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
     // B operand of Q K^T: head g, k = 32 s + 8 (lane / 16) .. +7 (heads past G: zeros).
     u32x4_t qb[DS];
     {
-        const uint16_t *qrow = Q + ((size_t)b * Hq + hk * G + min(g, G - 1)) * D;
+        const uint16_t *qrow = Q + ((size_t)b * Hq + hk * G + min(g, G - 1)) * Du;
 #pragma unroll
         for (int s = 0; s < DS; ++s)
-            qb[s] = g < G ? *reinterpret_cast<const u32x4_t *>(qrow + 32 * s + 8 * q4)
-                          : u32x4_t{0u, 0u, 0u, 0u};
+            qb[s] = g < G && 32 * s + 8 * q4 < Du
+                        ? *reinterpret_cast<const u32x4_t *>(qrow + 32 * s + 8 * q4)
+                        : u32x4_t{0u, 0u, 0u, 0u};
     }
 
     f32x4_t oacc[VS];
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
             if (j + 2 < j1) load_blk(j + 2, ba);
             compute_blk(j + 1, bb);
         }
-    } else {                                   // D = 256: one set (two would spill)
+    } else {                                   // D = 192, 256: one set (two would spill)
         Blk ba;
         for (int j = j0; j < j1; ++j) {
             load_blk(j, ba);
@@ -259,11 +264,12 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
     if (splits == 1) {
         if (g >= G) return;
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t *orow = O + ((size_t)b * Hq + h) * D;
+        uint16_t *orow = O + ((size_t)b * Hq + h) * Du;
 #pragma unroll
         for (int sd = 0; sd < VS; ++sd) {
             const f32x4_t v = (oacc[sd] - c) * inv;
-            *reinterpret_cast<u32x2_t *>(orow + 16 * sd + 4 * q4) = round4<ACT>(v);
+            if (16 * sd + 4 * q4 < Du)
+                *reinterpret_cast<u32x2_t *>(orow + 16 * sd + 4 * q4) = round4<ACT>(v);
         }
         return;
     }
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(64) void attn_decode_kv8_kernel(
 constexpr int kMaxSplits = 1024;
 template <int ACT, int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict__ part, int splits,
-                                                         int nbh, uint16_t *__restrict__ O) {
+                                                         int nbh, uint16_t *__restrict__ O, int Du) {
     __shared__ float w[kMaxSplits];
     __shared__ float red[D / 64][2];
     const int bh = blockIdx.x, d = threadIdx.x;
@@ -334,14 +340,15 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
                 if (i < splits && w[i] != 0.f) acc += w[i] * v[u][e];
             }
     }
-    O[(size_t)bh * D + d] = round_act<ACT>(ls > 0.f ? acc / ls : 0.f);
+    if (d < Du) O[(size_t)bh * Du + d] = round_act<ACT>(ls > 0.f ? acc / ls : 0.f);
 }
 
-// One thread per (token, KV head): writes its K and V codes, scales and zeros.
+// One thread per (token, KV head): writes its K and V codes (zeros past the caller's head
+// size D, up to the stored size Dp), scales and zeros.
 __global__ void kv_pack_kernel(const uint8_t *__restrict__ kc, const uint16_t *__restrict__ ks,
                                const uint8_t *__restrict__ kz, const uint8_t *__restrict__ vc,
                                const uint16_t *__restrict__ vs, const uint8_t *__restrict__ vz,
-                               int n, int t0, int Hkv, int D, const int *__restrict__ table_row,
+                               int n, int t0, int Hkv, int D, int Dp, const int *__restrict__ table_row,
                                int table_len, int num_blocks, uint8_t *__restrict__ cache) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n * Hkv) return;
@@ -350,24 +357,24 @@ __global__ void kv_pack_kernel(const uint8_t *__restrict__ kc, const uint16_t *_
     if (jb >= table_len) return;
     const int pb = table_row[jb];
     if (pb < 0 || pb >= num_blocks) return;
-    const size_t HB = 128 * (size_t)D + 384;
+    const size_t HB = 128 * (size_t)Dp + 384;
     uint8_t *hb = cache + (size_t)pb * HB * Hkv + (size_t)h * HB;
     const size_t row = (size_t)tl * Hkv + h;
-    for (int d = 0; d < D; ++d) {
-        // K^T: k = d, n = slot (16 x 64 tiles, K = D rows); V: k = slot, n = d (K = 64).
+    for (int d = 0; d < Dp; ++d) {
+        // K^T: k = d, n = slot (16 x 64 tiles, K = Dp rows); V: k = slot, n = d (K = 64).
         const int kk = d % 64, vk = slot % 64;
-        const size_t koff = ((size_t)(slot / 16) * (D / 64) + d / 64) * 1024 +
+        const size_t koff = ((size_t)(slot / 16) * (Dp / 64) + d / 64) * 1024 +
                             (size_t)(slot % 16 + 16 * ((kk % 32) / 8)) * 16 + (kk / 32) * 8 + kk % 8;
         const size_t voff = (size_t)(d / 16) * 1024 + (size_t)(d % 16 + 16 * ((vk % 32) / 8)) * 16 +
                             (vk / 32) * 8 + vk % 8;
-        hb[koff] = kc[row * D + d];
-        hb[64 * (size_t)D + voff] = vc[row * D + d];
+        hb[koff] = d < D ? kc[row * D + d] : (uint8_t)0;
+        hb[64 * (size_t)Dp + voff] = d < D ? vc[row * D + d] : (uint8_t)0;
     }
-    uint16_t *sc = reinterpret_cast<uint16_t *>(hb + 128 * (size_t)D);
+    uint16_t *sc = reinterpret_cast<uint16_t *>(hb + 128 * (size_t)Dp);
     sc[slot] = ks[row];
     sc[kKvTokens + slot] = vs[row];
-    hb[128 * (size_t)D + 256 + slot] = kz ? kz[row] : (uint8_t)0;
-    hb[128 * (size_t)D + 320 + slot] = vz ? vz[row] : (uint8_t)0;
+    hb[128 * (size_t)Dp + 256 + slot] = kz ? kz[row] : (uint8_t)0;
+    hb[128 * (size_t)Dp + 320 + slot] = vz ? vz[row] : (uint8_t)0;
 }
 
 template <int ACT, int D, int KVC>
@@ -375,16 +382,17 @@ void launch_attn(const AttnArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.B * a.Hkv * a.splits));
     attn_decode_kv8_kernel<ACT, D, KVC><<<grid, dim3(64), 0, stream>>>(
         a.Q, a.cache, a.num_blocks, a.table, a.table_stride, a.lens, a.Hq, a.Hkv, a.bps,
-        a.splits, a.scale_log2, a.O, a.part);
+        a.splits, a.scale_log2, a.O, a.part, a.D);
     if (a.splits > 1)
         attn_combine_kernel<ACT, D><<<dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, stream>>>(
-            a.part, a.splits, a.B * a.Hq, a.O);
+            a.part, a.splits, a.B * a.Hq, a.O, a.D);
 }
 
 template <int ACT, int KVC>
 void launch_attn_kvc(const AttnArgs &a, hipStream_t stream) {
-    switch (a.D) {
+    switch (kv_padded_d(a.D)) {
         case 64: launch_attn<ACT, 64, KVC>(a, stream); break;
+        case 192: launch_attn<ACT, 192, KVC>(a, stream); break;
         case 256: launch_attn<ACT, 256, KVC>(a, stream); break;
         default: launch_attn<ACT, 128, KVC>(a, stream); break;
     }
@@ -403,7 +411,7 @@ void launch_attn_act(const AttnArgs &a, hipStream_t stream) {
 
 size_t attn_part_bytes(int B, int Hq, int D, int splits) {
     const size_t sp = (size_t)((splits + 3) & ~3);
-    return splits > 1 ? (size_t)B * Hq * sp * (D + 2) * sizeof(float) : 0;
+    return splits > 1 ? (size_t)B * Hq * sp * (kv_padded_d(D) + 2) * sizeof(float) : 0;
 }
 
 hipError_t launch_attention_kv8(const AttnArgs &a, hipStream_t stream) {
@@ -419,8 +427,8 @@ hipError_t launch_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *
     const int items = n * Hkv;
     if (items > 0)
         kv_pack_kernel<<<(items + threads - 1) / threads, threads, 0, stream>>>(
-            kc, ks, kz, vc, vs, vz, n, t0, Hkv, D, table_row, table_len, num_blocks,
-            (uint8_t *)cache);
+            kc, ks, kz, vc, vs, vz, n, t0, Hkv, D, kv_padded_d(D), table_row, table_len,
+            num_blocks, (uint8_t *)cache);
     return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ struct AttnArgs {
     const int *table;           // [B][table_stride] block indices
     int table_stride;
     const int *lens;            // [B] context lengths
-    int B, Hq, Hkv, D;
+    int B, Hq, Hkv, D;          // D: the caller's head size (stored as kv_padded_d(D))
     int act;
     int kv_code;                // Code of the KV codes: kU8, kE4M3 or kE5M2
     int bps, splits;            // blocks per split, splits per (sequence, KV head)
@@ -102,6 +102,10 @@ struct AttnArgs {
     uint16_t *O;                // [B][Hq][D]
     float *part;                // split partials (splits > 1)
 };
+// A head of D values (a multiple of 16) is stored padded to a multiple of 64, the k depth
+// of one 8-bit tile, with zero codes past D.
+constexpr int kv_padded_d(int D) { return (D + 63) / 64 * 64; }
+// Split partials for the caller's head size D.
 size_t attn_part_bytes(int B, int Hq, int D, int splits);
 hipError_t launch_attention_kv8(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_kv_pack(const uint8_t *kc, const uint16_t *ks, const uint8_t *kz,
