@@ -32,7 +32,9 @@ per code and per zero) or the fp16 MFMA roofline.  `wfp8a16_qwen3_8b_per_gemm` d
 same with FP8 (E4M3) weights at the Qwen3-8B projection shapes (QKV 4096x6144, O 4096x4096,
 gate_up 4096x24576, down 12288x4096) and bf16 activations (mpgemm_wfp8a16; one byte per
 code, no zeros).  `w2a16_per_gemm` and `w3a16_per_gemm` do it with 2-bit and 3-bit weights
-(mpgemm_wlowbit_a16) at the Llama-3-8B shapes for M = 1 and 16, against the HBM roofline.
+(mpgemm_wlowbit_a16) at the Llama-3-8B shapes for M = 1 and 16, against the HBM roofline,
+and M = 2048 (the codes rewritten in the 4-bit layout, then the tiled kernel) against the
+fp16 MFMA roofline.
 `attention_kv8_decode` times mpgemm_attention_decode_kv8 (Llama-3-8B heads, one query token
 per sequence, batch x context 1 x 8192, 16 x 2048, 64 x 2048, 128 x 4096) against the HBM
 roofline (bytes: K and V codes, scales and zeros, Q, O, the block table);
@@ -494,7 +496,7 @@ def main():
             lowbit[f"w{bits}a16_per_gemm"] = variant_pass(
                 layerb, shapes, mp.wlowbit_a16,
                 lambda M, K, N, g_, b=bits: gemm_bytes_lowbit(b, M, K, N, g_), torch.float16,
-                ms=(1, 16))
+                ms=(1, 16, 2048))
             del layerb
 
     # Decode attention over the packed 8-bit and FP8 (E4M3) KV caches (Llama-3-8B heads: 32

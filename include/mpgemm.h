@@ -295,11 +295,21 @@ int mpgemm_wfp8a16_config(const void *X, int dtype, int fp8_format, const void *
  *   (B + q_lo, B + q_hi), ready for the exact subtraction of B + z and the scaling; the
  *   register is the 16x16x32 MFMA A operand of step t (row nn, k = 8*(L/16) + 2*(i/2)).
  *   Meta plane exactly as for 4-bit codes (zeros as 4-bit values).
- * The GEMM runs the small-M kernel (configurations 1..4); with configuration 0 and M > 64
- * it runs that kernel on 64-row chunks (the weights are read once per chunk).  Other ids
+ * The GEMM runs the small-M kernel (configurations 1..4).  For M > 64 the codes are
+ * rewritten in the 4-bit layout in the workspace (bits: 2 and 3-bit codes are valid 4-bit
+ * codes; symmetric codes shift onto the 4-bit zero 8, so every weight dequantizes to the
+ * same value) and a 32x32x16 tiled kernel runs on them with the same meta plane
+ * (configurations 0, 12 and 13).  That needs mpgemm_workspace_bytes_lowbit() bytes;
+ * configuration 0 with less runs the small-M kernel on 64-row chunks instead (reading the
+ * weights once per chunk), configurations 12 and 13 return MPGEMM_ERR_WORKSPACE.  Other ids
  * return MPGEMM_ERR_UNSUPPORTED.  A bits value other than 2 or 3 returns
- * MPGEMM_ERR_INVALID_ARG.  Workspace as for mpgemm_w4a16.
+ * MPGEMM_ERR_INVALID_ARG.
  */
+
+/* Workspace for mpgemm_wlowbit_a16(_config): that of mpgemm_workspace_bytes, and for
+ * M > 64 room for the 4-bit rewrite of the codes (Kp*Np/2 bytes) past the tiled kernels'
+ * region; same zero-initialization and sharing rules.  0 for a bits value other than 2, 3. */
+size_t mpgemm_workspace_bytes_lowbit(int bits, int M, int N, int K, int group, int dtype);
 
 /* Size of the packed sub-4-bit codes plane: Kp*Np*bits/8 bytes (0 if unsupported).  The
  * meta plane is sized by mpgemm_packed_meta_bytes. */

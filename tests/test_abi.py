@@ -12,7 +12,7 @@ import weight_only_quantized_mpgemm_amd as mp
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mpgemm.h")
 
-OK, INVALID, UNSUPPORTED, ALIGN = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
 A = 0x10000          # a 16-byte-aligned fake device address; never dereferenced here
 MIS = 0x10008        # a misaligned one
 
@@ -222,9 +222,10 @@ def _low(bits=2, cfg=0, M=16, K=256):
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=4), INVALID),
     (dict(bits=1), INVALID),
-    (dict(cfg=12, M=128), UNSUPPORTED),      # no tiled kernel for sub-4-bit codes
-    (dict(cfg=13, M=128), UNSUPPORTED),
-    (dict(cfg=10, M=128), UNSUPPORTED),
+    (dict(cfg=12, M=128), WORKSPACE),        # tiled: the 4-bit rewrite needs the workspace
+    (dict(cfg=13, M=128), WORKSPACE),
+    (dict(cfg=10, M=128), UNSUPPORTED),      # no 16x16x32 tiled kernel for sub-4-bit codes
+    (dict(cfg=11, M=128), UNSUPPORTED),
     (dict(cfg=1, M=17), UNSUPPORTED),
     (dict(K=12), UNSUPPORTED),
     (dict(M=0), OK),
@@ -265,3 +266,14 @@ def test_attention_rejects_unsupported_head_sizes_before_launching():
             args = (A, 0, *extra, A, 4, A, 1, A, 1, 8, 2, D, 64, ctypes.c_float(0.1), A, None, 0, None)
             assert fn(*args) == UNSUPPORTED
         assert lib.mpgemm_kv_pack(A, A, A, A, A, A, 1, 0, 2, D, A, 1, 4, A, None) == UNSUPPORTED
+
+
+def test_lowbit_workspace_covers_the_4bit_rewrite_at_large_m():
+    lib = mp.lib()
+    for bits in (2, 3):
+        small = lib.mpgemm_workspace_bytes_lowbit(bits, 16, 4096, 4096, 128, 0)
+        assert small == lib.mpgemm_workspace_bytes(16, 4096, 4096, 128, 0)
+        big = lib.mpgemm_workspace_bytes_lowbit(bits, 2048, 4096, 4096, 128, 0)
+        assert big >= 256 * 1024 + 4096 * 4096 // 2
+        assert lib.mpgemm_workspace_bytes_lowbit(bits, 300, 40, 200, 128, 0) >= 256 * 1024 + 256 * 48 // 2
+    assert lib.mpgemm_workspace_bytes_lowbit(4, 2048, 4096, 4096, 128, 0) == 0

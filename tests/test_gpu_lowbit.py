@@ -24,7 +24,9 @@ ONE = {"f16": 0x3C00, "bf16": 0x3F80}
 
 
 def configs_for(M):
-    return [0] + [c for c in (1, 2, 3, 4) if M <= 16 * c]
+    """Every configuration that runs M rows: the small-M kernel ids, and for M > 64 the two
+    32x32x16 tiled ids (on the codes rewritten in the 4-bit layout)."""
+    return [0] + [c for c in (1, 2, 3, 4) if M <= 16 * c] + ([12, 13] if M > 64 else [])
 
 
 def make(bits, K, N, g, sym, seed, lo=0.005, hi=0.05):
@@ -73,7 +75,7 @@ def test_lowbit_weights_are_not_accepted_by_the_other_gemms():
         mp.w4a16(x, packed)
     with pytest.raises(mp.MpgemmError):
         mp.wlowbit_a16(torch.zeros((128, 256), dtype=torch.float16, device="cuda"), packed,
-                       config=12)
+                       config=10)
 
 
 @pytest.mark.parametrize("bits", BITS)
@@ -138,7 +140,7 @@ def test_lowbit_ragged_shapes(bits, K, N, M):
 
 
 @pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 16, 2048])
 @pytest.mark.parametrize("K,N,label", workloads.LLAMA3_8B_SHAPES)
 def test_lowbit_llama3_8b_full_shapes(bits, M, K, N, label):
     codes, scales, zeros = make(bits, K, N, 128, False, K + N + M + bits)
@@ -146,8 +148,29 @@ def test_lowbit_llama3_8b_full_shapes(bits, M, K, N, label):
     packed = pack(bits, codes, scales, zeros, 128)
     rng = np.random.default_rng(K + N)
     cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 192, replace=False)]))
-    want = oracle.wlowbit_a16(bits, x, codes[:, cols], scales[:, cols], zeros[:, cols], 128,
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 12), replace=False)]))
+    want = oracle.wlowbit_a16(bits, x[rows], codes[:, cols], scales[:, cols], zeros[:, cols], 128,
                               threads=8)
-    say(f"w{bits} 8B M={M} K={K} N={N}")
-    y = run(x, packed, "f16")
-    assert rel_err(y[:, cols], want, "f16") <= REL_TOL
+    for cfg in [0] + ([12, 13] if M > 64 else []):
+        say(f"w{bits} 8B M={M} K={K} N={N} config={cfg}")
+        y = run(x, packed, "f16", cfg)
+        assert rel_err(y[rows][:, cols], want, "f16") <= REL_TOL, cfg
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("sym", [False, True])
+def test_lowbit_large_m_equals_the_4bit_gemm_of_the_same_codes_bit_for_bit(bits, sym):
+    """b-bit codes are valid 4-bit codes (symmetric ones shifted onto the 4-bit zero 8): the
+    tiled path must give the 4-bit GEMM's bits on the same weights."""
+    M, K, N, g = 300, 1024, 272, 128
+    codes, scales, zeros = make(bits, K, N, g, sym, 7 + bits)
+    x = workloads.activations(M, K, "f16", 8)
+    packed = pack(bits, codes, scales, zeros, g)
+    shift = 8 - (1 << (bits - 1)) if sym else 0
+    p4 = mp.pack_weights(dev_u8(codes + shift), dev_half(scales),
+                         None if zeros is None else dev_u8(zeros), g)
+    for cfg in (0, 12, 13):
+        y = run(x, packed, "f16", cfg)
+        y4 = host_bits(mp.w4a16(dev_half(x), p4, config=cfg if cfg else 12 if M < 512 else 13))
+        say(f"w{bits} vs w4 sym={sym} config={cfg}")
+        assert np.array_equal(y, y4), cfg

@@ -67,7 +67,14 @@ def rel_err(y_bits, ref_bits, dtype):
     y = to_f64(y_bits, dtype)
     r = to_f64(ref_bits, dtype)
     assert np.isfinite(y).all()
-    return float(np.max(np.abs(y - r)) / max(np.max(np.abs(r)), 1e-30))
+    err = float(np.max(np.abs(y - r)) / max(np.max(np.abs(r)), 1e-30))
+    if err > REL_TOL and y.ndim == 2:           # say where, for a failure that comes and goes
+        bad = np.argwhere(np.abs(y - r) > REL_TOL * max(np.max(np.abs(r)), 1e-30))
+        print(f"[diag] {len(bad)} of {y.size} outside the bar; rows "
+              f"{sorted(set(bad[:, 0].tolist()))[:24]} cols {sorted(set(bad[:, 1].tolist()))[:32]}; "
+              f"first {[(int(i), int(j), float(y[i, j]), float(r[i, j])) for i, j in bad[:4]]}",
+              flush=True)
+    return err
 
 
 def oracle_sample(case, rows, cols):

@@ -65,6 +65,7 @@ SIGNATURES = {
     "mpgemm_attention_decode_kvfp8": (_i, [_vp, _i, _i, _vp, _i, _vp, _i, _vp, _i, _i, _i, _i,
                                            _i, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "mpgemm_packed_code_bytes_lowbit": (_sz, [_i, _i, _i]),
+    "mpgemm_workspace_bytes_lowbit": (_sz, [_i, _i, _i, _i, _i, _i]),
     "mpgemm_pack_weights_lowbit": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "mpgemm_unpack_lowbit": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "mpgemm_wlowbit_a16": (_i, [_i, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -344,7 +345,10 @@ def _gemm(kind: str, x: torch.Tensor, packed: PackedWeights, out, config, worksp
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _need(out, x.dtype, (M, N), "out")
-    ws = int(lib().mpgemm_workspace_bytes(M, N, K, packed.group, act))
+    if kind in ("w2", "w3"):
+        ws = int(lib().mpgemm_workspace_bytes_lowbit(packed.bits, M, N, K, packed.group, act))
+    else:
+        ws = int(lib().mpgemm_workspace_bytes(M, N, K, packed.group, act))
     if workspace is None:
         workspace = workspace_for(x.device, ws)
     elif ws:

@@ -66,6 +66,29 @@ int select_config(int M, int N, int K) {
     return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
 }
 
+// 2- and 3-bit codes at M > 64: the sub-4-bit codes are rewritten in the 4-bit layout in
+// the workspace (past the region the tiled kernels' K split may use) and the 32x32x16
+// kernel runs on them with the same meta plane.  Measured on the Llama-3-8B projections,
+// this beats the small-M kernel on 64-row chunks from M = 128 on (2.2-3.7x there, 9x at
+// M = 2048).  MPGEMM_LOWBIT_REPACK_M sets a higher threshold (tuning sweeps).
+size_t lowbit_repack_offset(int M, int N, int K) {
+    size_t r = mpgemm::kSplitCounterBytes;
+    const size_t x = mpgemm::x32_workspace_bytes(M, N, K);
+    if (x > r) r = x;
+    return (r + 255) / 256 * 256;
+}
+size_t lowbit_repack_bytes(int M, int N, int K) {
+    return lowbit_repack_offset(M, N, K) +
+           (size_t)mpgemm::padded_k(K) * (size_t)mpgemm::padded_n(N) / 2;
+}
+int lowbit_repack_min_m() {
+    if (const char *env = getenv("MPGEMM_LOWBIT_REPACK_M")) {
+        const int v = atoi(env);
+        if (v > 64) return v;
+    }
+    return 65;
+}
+
 int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
               const void *packed_meta, int M, int N, int K, int group, int symmetric, void *Y,
               void *workspace, size_t workspace_bytes, int config_id, void *stream) {
@@ -94,7 +117,8 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     // 2- and 3-bit codes run the small-M kernel only (the tiled kernels have no sub-4-bit
     // dequantization): larger M goes through it in chunks of 64 rows.
     const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
-    if (lowbit && config_id != kConfigSelect && !(cfg >= kConfigDecode1 && cfg <= kConfigDecode4))
+    if (lowbit && config_id != kConfigSelect && !(cfg >= kConfigDecode1 && cfg <= kConfigDecode4) &&
+        cfg != kConfigPrefillX32 && cfg != kConfigPrefillX32Tall)
         return MPGEMM_ERR_UNSUPPORTED;
     // 8-bit and FP8 codes, and ragged K, run the small-M kernel and the 32x32x16 tiled
     // kernels (which mask the activations past K); the 16x16x32 tiled kernels take aligned
@@ -125,6 +149,27 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
             return MPGEMM_ERR_WORKSPACE;
     }
     if (lowbit && M > 64) {
+        const bool tiled = config_id != kConfigSelect || M >= lowbit_repack_min_m();
+        if (tiled && workspace != nullptr && aligned16(workspace) &&
+            workspace_bytes >= lowbit_repack_bytes(M, N, K)) {
+            const size_t off = lowbit_repack_offset(M, N, K);
+            void *codes4 = static_cast<char *>(workspace) + off;
+            int st = hip_status(mpgemm::launch_repack_lowbit_u4(code == mpgemm::kU2 ? 2 : 3,
+                                                                symmetric != 0, packed_codes,
+                                                                a.Kp, a.Np, codes4, s));
+            if (st != MPGEMM_OK) return st;
+            mpgemm::GemmArgs c = a;
+            c.codes = (const uint32_t *)codes4;
+            c.code = mpgemm::kU4;
+            c.workspace_bytes = off;
+            const int xcfg = config_id != kConfigSelect ? cfg : select_config(M, N, K);
+            if (getenv("MPGEMM_LOG"))
+                fprintf(stderr, "mpgemm: W%dA16 M=%d N=%d K=%d g=%d -> 4-bit repack, %s\n",
+                        code == mpgemm::kU2 ? 2 : 3, M, N, K, group, mpgemm_config_name(xcfg));
+            return hip_status(xcfg == kConfigPrefillX32Tall ? mpgemm::launch_prefill_x32_tall(c, s)
+                                                            : mpgemm::launch_prefill_x32(c, s));
+        }
+        if (config_id != kConfigSelect) return MPGEMM_ERR_WORKSPACE;
         const size_t need = mpgemm::decode_workspace_bytes(64, N, K, kConfigDecode4);
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
             return MPGEMM_ERR_WORKSPACE;
@@ -204,6 +249,16 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
         return MPGEMM_ERR_ALIGNMENT;
     return hip_status(mpgemm::launch_unpack(packed_codes, packed_meta, K, N, group, symmetric,
                                             codes, scales, zeros, (hipStream_t)stream));
+}
+
+size_t mpgemm_workspace_bytes_lowbit(int bits, int M, int N, int K, int group, int dtype) {
+    if (bits != 2 && bits != 3) return 0;
+    size_t need = mpgemm_workspace_bytes(M, N, K, group, dtype);
+    if (M > 64 && N > 0 && K > 0 && check_shape(M, N, K, group) == MPGEMM_OK) {
+        const size_t r = lowbit_repack_bytes(M, N, K);
+        if (r > need) need = r;
+    }
+    return need;
 }
 
 size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {

@@ -81,6 +81,12 @@ hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_prefill_x32_u4(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill_x32_u8(const GemmArgs &a, int nb, hipStream_t stream);
 hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream);
+// Sub-4-bit packed codes (Kp x Np, padded sizes) rewritten in the 4-bit packed layout
+// (Kp*Np/2 bytes at `out`, 16-byte aligned), so that the 4-bit kernels with the same meta
+// plane dequantize every weight to the same value (symmetric codes are shifted by
+// 8 - 2^(bits-1) onto the 4-bit symmetric zero 8).
+hipError_t launch_repack_lowbit_u4(int bits, bool symmetric, const void *packed_codes, int Kp,
+                                   int Np, void *out, hipStream_t stream);
 // Workspace bytes with which the 32x32x16 kernels (either tile shape) split the K range of
 // their last, partial round of tiles; 0 when they never do for this shape.  N, K: user shape.
 size_t x32_workspace_bytes(int M, int N, int K);

@@ -269,6 +269,39 @@ __global__ void unpack_meta8_kernel(const uint16_t *__restrict__ in_scales,
     if (in_zeros != nullptr) zeros[(size_t)r * sh.N + n] = in_zeros[e];
 }
 
+// Sub-4-bit packed codes -> the 4-bit packed layout of the same matrix (both layouts cut
+// 16 x 128 tiles the same way and give lane L the same elements: element (t, i) of lane L
+// is pair register r = 4t + i/2, half i%2, of the b-bit words, and nibble i/2 or 4 + i/2
+// of 4-bit word t).  Every code gains `add`: 0 for asymmetric codes (their b-bit zeros are
+// valid 4-bit zeros), 8 - 2^(b-1) for symmetric ones, whose zero point 2^(b-1) then
+// becomes the 4-bit symmetric zero 8.  Each dequantized weight is unchanged bit for bit.
+// One thread per (tile, lane); padding cells hold the zero point either way.
+__global__ void repack_low_u4_kernel(const uint32_t *__restrict__ in, size_t lanes, int bits,
+                                     uint32_t add, u32x4_t *__restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= lanes) return;
+    const uint32_t *src = in + i * bits;      // tile T = i / 64 at word T*64*bits, lane at L*bits
+    uint32_t w[3] = {0u, 0u, 0u};
+    for (int c = 0; c < bits; ++c) w[c] = src[c];
+    u32x4_t o = {0u, 0u, 0u, 0u};
+    for (int r = 0; r < 16; ++r) {
+        const int t = r >> 2, j = r & 3;
+        for (int h = 0; h < 2; ++h) {
+            uint32_t q;
+            if (bits == 2) {
+                q = (w[r >> 3] >> (16 * h + 2 * (r & 3) + 8 * ((r & 7) >> 2))) & 3u;
+            } else if (r < 15) {
+                q = (w[r / 5] >> (16 * h + 3 * (r % 5))) & 7u;
+            } else {
+                q = 0;
+                for (int c = 0; c < 3; ++c) q |= ((w[c] >> (16 * h + 15)) & 1u) << c;
+            }
+            o[t] |= (q + add) << (4 * (j + 4 * h));
+        }
+    }
+    out[i] = o;                               // 4-bit tile T at 1 KiB, lane L at 16 bytes
+}
+
 unsigned blocks_for(size_t total, unsigned threads) {
     return (unsigned)((total + threads - 1) / threads);
 }
@@ -370,6 +403,16 @@ hipError_t launch_unpack_lowbit(int bits, const void *packed_codes, const void *
             unpack_meta_kernel<<<b, t, 0, stream>>>(ms, mz, sh, scales,
                                                     symmetric ? nullptr : zeros);
         });
+}
+
+hipError_t launch_repack_lowbit_u4(int bits, bool symmetric, const void *packed_codes, int Kp,
+                                   int Np, void *out, hipStream_t stream) {
+    const size_t lanes = (size_t)(Np >> 4) * (Kp >> 7) * 64;
+    const uint32_t add = symmetric ? 8u - (1u << (bits - 1)) : 0u;
+    if (lanes)
+        repack_low_u4_kernel<<<blocks_for(lanes, 256), 256, 0, stream>>>(
+            (const uint32_t *)packed_codes, lanes, bits, add, (u32x4_t *)out);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_w8(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
