@@ -47,3 +47,28 @@ def test_acc_read_hazards_flags_early_reads_only():
     # kernel 1 reads a3 one instruction after the MFMA that writes a[0:15]; kernel 2 waits
     # 32 states (and its read of a40 belongs to no MFMA)
     assert build.acc_read_hazards(ASM) == [("_Z6kernelPf", 1)]
+
+
+def _ring_path(wait_imm_stage0):
+    """Prologue: DMA stages 0, 1, 2 (two loads each), two weight loads, barrier; then a
+    stage barrier whose wait is given, needing stage 1."""
+    dma = "buffer_load_dwordx4 v1, s[0:3], s4 offen lds"
+    w = "buffer_load_dwordx4 v[2:5], v6, s[8:11], s4 offen"
+    return ([dma, dma, dma, dma, dma, dma, w, w, "s_waitcnt vmcnt(4)", "s_barrier",
+             f"s_waitcnt vmcnt({wait_imm_stage0})", "s_barrier"])
+
+
+def test_stage_wait_check_accepts_waits_that_leave_only_later_loads():
+    # after stage 1's last part: stage 2 (2 loads) and two weight loads are in flight
+    assert build.stage_wait_violations(_ring_path(2), 2) == []
+    assert build.stage_wait_violations(_ring_path(4), 2) == []
+
+
+def test_stage_wait_check_flags_a_wait_that_can_pass_early():
+    # vmcnt(5) would let stage 1's last DMA part still be in flight
+    assert build.stage_wait_violations(_ring_path(5), 2) == [(1, 4, 5)]
+
+
+def test_stage_wait_check_flags_a_stage_never_issued():
+    seq = ["buffer_load_dwordx4 v1, s[0:3], s4 offen lds", "s_waitcnt vmcnt(0)", "s_barrier"]
+    assert build.stage_wait_violations(seq, 2) == [(0, -1, 0)]

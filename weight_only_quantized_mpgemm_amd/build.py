@@ -96,6 +96,87 @@ def acc_read_hazards(asm: str, min_wait: int = MIN_RESULT_WAIT) -> list[tuple[st
     return out
 
 
+def _path_lines(asm: str, name: str) -> list[str]:
+    start = asm.index("\n" + name + ":")
+    end = asm.find(".Lfunc_end", start)
+    out = []
+    for ln in asm[start:end].split("\n")[1:]:
+        ln = ln.strip()
+        if re.match(r"\.LBB\w+:", ln):
+            out.append(ln.split()[0])
+        elif ln and not ln.startswith((".", ";")):
+            out.append(ln)
+    return out
+
+
+def stage_wait_violations(seq: list[str], mb: int) -> list[tuple]:
+    """Walks one execution path of a ring-buffered kernel: the k-th group of `mb` LDS-DMA
+    loads (buffer_load ... lds) carries stage k; the b-th s_barrier (b = 0: the prologue's)
+    must find stage b's group complete, i.e. the s_waitcnt right before it must leave in
+    flight no more loads than were issued after that group's last part (vmcnt counts a
+    wave's loads in issue order).  Returns (barrier, loads after, vmcnt) per violation."""
+    loads, nlds, bars, bad, prev = [], 0, 0, [], None
+    for ln in seq:
+        if ln.startswith("buffer_load"):
+            if " lds" in ln:
+                loads.append(nlds // mb)
+                nlds += 1
+            else:
+                loads.append(None)
+        elif ln.startswith("s_barrier"):
+            nv = 63                                   # no wait right before: anything in flight
+            m = re.match(r"s_waitcnt (0x[0-9a-fA-F]+|\d+)$", prev or "")
+            if m:
+                imm = int(m.group(1), 0)
+                nv = (imm & 15) | (((imm >> 14) & 3) << 4)
+            elif (prev or "").startswith("s_waitcnt"):
+                v = re.search(r"vmcnt\((\d+)\)", prev)
+                nv = int(v.group(1)) if v else 63
+            idx = [k for k, t in enumerate(loads) if t == bars]
+            if len(idx) < mb:
+                bad.append((bars, -1, nv))
+            elif len(loads) - 1 - idx[-1] < nv:
+                bad.append((bars, len(loads) - 1 - idx[-1], nv))
+            bars += 1
+        prev = ln
+    return bad
+
+
+def ring_wait_violations(asm: str) -> list[tuple[str, str, list]]:
+    """Checks every 32x32x16 tiled kernel's stage waits along the paths a launch takes:
+    prologue, then the stage loop once and twice, then (four-weight-set kernels) the
+    four-stage tail after one pass of the loop or in place of it."""
+    out = []
+    for name in re.findall(r"\n([A-Za-z_][\w.$]*):[^\n]*\n", asm):
+        if "prefill_x32_kernel" not in name:
+            continue
+        lines = _path_lines(asm, name)
+        lab = {ln[:-1]: i for i, ln in enumerate(lines) if re.match(r"\.LBB\w+:$", ln)}
+        b0 = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
+        mb = sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // 3
+        br = next(i for i in range(b0, len(lines)) if lines[i].startswith("s_cbranch"))
+        skip = lines[br].split()[1]
+        top = next(i for i in range(br + 1, len(lines)) if re.match(r"\.LBB\w+:$", lines[i]))
+        back = next(i for i in range(top, len(lines))
+                    if lines[i].startswith("s_cbranch") and lines[i].split()[1] == lines[top][:-1])
+        prologue, loop = lines[:br], lines[top + 1:back]
+        paths = {"loop once": prologue + loop, "loop twice": prologue + loop + loop}
+        j = next(i for i in range(back + 1, len(lines)) if lines[i].startswith("s_cbranch"))
+        tl = next(i for i in range(j + 1, len(lines)) if re.match(r"\.LBB\w+:$", lines[i]))
+        after = lines[tl + 1:lab.get(lines[j].split()[1], tl + 1)]
+        if any(ln.startswith("s_barrier") for ln in after):          # a four-stage tail
+            tail = lines[j + 1:tl] + after
+            sk = lines[lab[skip] + 1:]
+            k = next(i for i, ln in enumerate(sk) if ln.startswith(("s_branch", "s_cbranch")))
+            paths["loop and tail"] = prologue + loop + tail
+            paths["tail only"] = prologue + sk[:k] + tail
+        for path, seq in paths.items():
+            bad = stage_wait_violations(seq, mb)
+            if bad:
+                out.append((name, path, bad))
+    return out
+
+
 def _check_asm_mfma(src: str, extra: list[str]) -> None:
     asm_path = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
     cmd = [HIPCC, *FLAGS, *extra, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
@@ -103,9 +184,14 @@ def _check_asm_mfma(src: str, extra: list[str]) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{res.stderr}")
-    bad = acc_read_hazards(open(asm_path).read())
+    asm = open(asm_path).read()
+    bad = acc_read_hazards(asm)
     if bad:
         raise RuntimeError(f"{src}: MFMA results read too early (wait states): {bad}")
+    if "prefill_x32" in src:
+        bad = ring_wait_violations(asm)
+        if bad:
+            raise RuntimeError(f"{src}: a stage wait can pass before its DMA landed: {bad[:4]}")
 
 
 def _compile(src: str, extra: list[str]) -> str:

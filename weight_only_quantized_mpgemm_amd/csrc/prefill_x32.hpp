@@ -568,15 +568,20 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // One 64-deep stage st (ring buffer BUF = st % 4, tile t = st / 2, half H = st % 2,
     // weight set TW = t % NWS): step 0 runs word 2H and prepares word 2H+1 from this
     // stage's buffer; step 1 runs word 2H+1 and prepares the next stage's first step (the
-    // next tile's word 0 when H == 1).  Stage 2t loads tile t + NWS - 1.
-    auto stage = [&](int st, auto BUF, auto H, auto TW) __attribute__((always_inline)) {
+    // next tile's word 0 when H == 1).  Stage 2t loads tile t + NWS - 1, except in the
+    // final four stages (LAST), whose weight loads nothing would read.
+    // The wait: vmcnt counts a wave's loads in issue order, and after its DMA of stage
+    // st+1 the wave issued at least the MB loads of its DMA of stage st+2 (DMAs write LDS,
+    // so the compiler neither moves them across the barrier nor drops them); leaving at
+    // most MB loads in flight therefore finds stage st+1 in LDS.  The weight loads are not
+    // counted: the compiler may move them (their memory never changes) or drop them when
+    // dead, as in the final stages, which therefore issue none.
+    auto stage = [&](int st, auto BUF, auto H, auto TW, auto LOADW) __attribute__((always_inline)) {
         constexpr int buf = decltype(BUF)::value, h = decltype(H)::value, tw = decltype(TW)::value;
         constexpr int nbuf = (buf + 1) % kXStages, nw = (tw + 1) % NWS;
+        constexpr bool loadw = decltype(LOADW)::value != 0;
         const int t = st >> 1;
-        // The wave's DMA of stage st+1 was followed by the DMA of stage st+2 and one weight
-        // tile; once only those are outstanding, stage st+1 is in LDS.  (In the first two
-        // stages more loads follow it and the wait is longer than needed, never shorter.)
-        wait_vm_barrier<MB + kWLoads>();
+        wait_vm_barrier<MB>();
         // The next stage's DMA (MB blocks) and, in the first half of a tile, the weight
         // loads of tile t + NWS - 1 go out one at a time between MFMAs, in the same order
         // as before, instead of as one burst per wave at the barrier.
@@ -587,7 +592,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         };
         auto w_hook = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
-            if constexpr (h == 0) {
+            if constexpr (h == 0 && loadw) {
                 if constexpr (kWLoads <= 8) {
                     if constexpr (i % 2 == 0 && i / 2 < kWLoads)
                         load_w_part(t + NWS - 1, ws[(tw + NWS - 1) % NWS], IC<i / 2>());
@@ -606,23 +611,28 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
             step(A[1], B[1], A[0], B[0], ws[tw], dq[tw], 2, IC<nbuf>(), 0, w_hook);
         }
     };
-    // Stages st .. st+3 (tiles 2u, 2u+1 of a 2 * NWS-stage block, u = 0 or 1).
-    auto four = [&](int st, auto U) __attribute__((always_inline)) {
+    // Stages st .. st+3 (tiles 2u, 2u+1 of a 2 * NWS-stage block, u = 0 or 1); LAST: the
+    // kernel's final four stages.
+    auto four = [&](int st, auto U, auto LAST) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
-        stage(st + 0, IC<0>(), IC<0>(), IC<(2 * u) % NWS>());
-        stage(st + 1, IC<1>(), IC<1>(), IC<(2 * u) % NWS>());
-        stage(st + 2, IC<2>(), IC<0>(), IC<(2 * u + 1) % NWS>());
-        stage(st + 3, IC<3>(), IC<1>(), IC<(2 * u + 1) % NWS>());
+        constexpr bool last = decltype(LAST)::value != 0;
+        constexpr int lw = last ? 0 : 1;
+        stage(st + 0, IC<0>(), IC<0>(), IC<(2 * u) % NWS>(), IC<lw>());
+        stage(st + 1, IC<1>(), IC<1>(), IC<(2 * u) % NWS>(), IC<lw>());
+        stage(st + 2, IC<2>(), IC<0>(), IC<(2 * u + 1) % NWS>(), IC<lw>());
+        stage(st + 3, IC<3>(), IC<1>(), IC<(2 * u + 1) % NWS>(), IC<lw>());
     };
 
     // Prologue: stages 0..2 in flight, tiles 0 .. NWS-2, then stage 0's first operands.
+    // The DMAs go first; the prologue's wait leaves at most their last two stages in
+    // flight, so stage 0 has landed whatever the compiler does with the weight loads.
     dma(0, IC<0>());
-    load_w(0, ws[0]);
     dma(1, IC<1>());
     dma(2, IC<2>());
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 1; t < NWS - 1; ++t) load_w(t, ws[t]);
-    wait_vm_barrier<MB + kWLoads * (NWS - 2)>();  // stage 0's DMA and tile 0 have landed
+    for (int t = 0; t < NWS - 1; ++t) load_w(t, ws[t]);
+    wait_vm_barrier<2 * MB>();
     make_dq(ws[0], dq[0]);
     read_b(IC<0>(), 0, B[0]);
     dequant_a(ws[0], dq[0], 0, A[0]);
@@ -639,13 +649,13 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // MFMAs' results written.
     int st = 0;
     for (; st + 2 * NWS <= S; st += 2 * NWS) {
-        four(st, IC<0>());
-        if constexpr (NWS == 4) four(st + 4, IC<1>());
+        four(st, IC<0>(), IC<0>());
+        if constexpr (NWS == 4) four(st + 4, IC<1>(), IC<0>());
         mfma_drain();
     }
     if constexpr (NWS == 4) {
         if (st < S) {
-            four(st, IC<0>());
+            four(st, IC<0>(), IC<1>());
             mfma_drain();
         }
     }
