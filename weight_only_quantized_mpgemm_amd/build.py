@@ -148,12 +148,15 @@ def ring_wait_violations(asm: str) -> list[tuple[str, str, list]]:
     four-stage tail after one pass of the loop or in place of it."""
     out = []
     for name in re.findall(r"\n([A-Za-z_][\w.$]*):[^\n]*\n", asm):
-        if "prefill_x32_kernel" not in name:
+        if "prefill_x32_kernel" not in name and "prefill_ring_kernel" not in name:
             continue
         lines = _path_lines(asm, name)
         lab = {ln[:-1]: i for i, ln in enumerate(lines) if re.match(r"\.LBB\w+:$", ln)}
         b0 = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
-        mb = sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // 3
+        # DMA loads per stage and wave: the x32 prologue issues three stages, the ring
+        # kernel four loads per stage
+        mb = 4 if "prefill_ring_kernel" in name else \
+            sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // 3
         br = next(i for i in range(b0, len(lines)) if lines[i].startswith("s_cbranch"))
         skip = lines[br].split()[1]
         top = next(i for i in range(br + 1, len(lines)) if re.match(r"\.LBB\w+:$", lines[i]))
@@ -188,7 +191,7 @@ def _check_asm_mfma(src: str, extra: list[str]) -> None:
     bad = acc_read_hazards(asm)
     if bad:
         raise RuntimeError(f"{src}: MFMA results read too early (wait states): {bad}")
-    if "prefill_x32" in src:
+    if "prefill_x32" in src or "prefill_ring" in src:
         bad = ring_wait_violations(asm)
         if bad:
             raise RuntimeError(f"{src}: a stage wait can pass before its DMA landed: {bad[:4]}")

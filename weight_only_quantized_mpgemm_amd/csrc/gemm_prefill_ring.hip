@@ -132,17 +132,18 @@ __global__ __launch_bounds__(kRThreads) void prefill_ring_kernel(
     constexpr int kWLoads = 4 * (1 + GPT * (SYM ? 1 : 2));
     // Stage j issues the DMA of stage j + NST - 1 and, when j is even, the weights of tile
     // j/2 + NWS - 1 (the tiles 0 .. NWS-2 come from the prologue, so NWS = NST / 2).  Stage
-    // j needs the DMA of stage j + 1, issued at stage j + 2 - NST; the wave's loads issued
-    // after it are NST - 3 stage DMAs and (NST - 2) / 2 weight tiles.  Loads complete in
-    // issue order, so waiting until no more than that many are outstanding suffices; a
-    // count past the counter's range (63) waits for a few more, which is still correct.
+    // j needs the DMA of stage j + 1, issued at stage j + 2 - NST; the wave issued at least
+    // the DMAs of the NST - 3 stages after it since (4 loads each).  vmcnt counts a wave's
+    // loads in issue order, so leaving at most that many in flight finds stage j + 1 in
+    // LDS.  The weight loads are not counted: the compiler may move them (their memory
+    // never changes) or drop them when dead, as in the final stages; DMAs write LDS and
+    // stay where they are.  (This over-waits a little when weights follow the last DMA.)
     static_assert(NWS * 2 == NST && (NST == 4 || NST == 8), "ring shape");
-    constexpr int kAfter = 4 * (NST - 3) + kWLoads * ((NST - 2) / 2);
-    constexpr int kWait = kAfter < 63 ? kAfter : 63;
-    // Before stage 0: stage 0's DMA and tile 0's weights, issued before the DMAs of stages
-    // 2 .. NST-2 and the weights of tiles 1 .. NWS-2.
-    constexpr int kPro = 4 * (NST - 3) + kWLoads * ((NST - 4) / 2);
-    constexpr int kProWait = kPro < 63 ? kPro : 63;
+    constexpr int kWait = 4 * (NST - 3);
+    // Before stage 0: stage 0's DMA, followed by the DMAs of stages 1 .. NST-2 (tile 0's
+    // weights are waited for by the compiler where they are used).
+    constexpr int kProWait = 4 * (NST - 2);
+    (void)kWLoads;
     __shared__ u32x4_t xs[NST][kRChunks];
 
     const int tid = threadIdx.x;
