@@ -62,12 +62,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_llama3_8b_m1_16_2048_hbm_tr
 
 
 def kernel_source_digest():
-    """sha256 (16 hex digits) over the HIP sources and the build flags of the library."""
+    """sha256 (16 hex digits) over the HIP sources and the build flags of the library's GEMM
+    path (everything but the attention kernels, which the GEMM profiles do not cover)."""
     pkg = os.path.join(ROOT, "weight_only_quantized_mpgemm_amd")
     csrc = os.path.join(pkg, "csrc")
     h = hashlib.sha256()
     files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
-             if f.endswith((".hip", ".hpp"))] + [os.path.join(pkg, "build.py")]
+             if f.endswith((".hip", ".hpp")) and f != "attention.hip"] + \
+        [os.path.join(pkg, "build.py")]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:

@@ -302,8 +302,22 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
     const int bh = blockIdx.x, d = threadIdx.x;
     const int SP = (splits + 3) & ~3;
     const float *ml = part + (size_t)nbh * D * SP + 2 * (size_t)bh * SP;
-    float mx = -INFINITY;
-    for (int i = d; i < splits; i += D) mx = fmaxf(mx, ml[2 * i]);
+    const f32x4_t *row = reinterpret_cast<const f32x4_t *>(part + ((size_t)bh * D + d) * SP);
+    // The first 64 splits of this thread's row are requested first, so that their latency
+    // overlaps the max and weight phases (a batch at a time afterwards).
+    constexpr int kPre = 16, kBatch = 8;
+    f32x4_t pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) pre[u] = u < SP / 4 ? row[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // This thread's first (max, sum) pair stays in registers for the weight phase.
+    float mi = -INFINITY, li = 0.f;
+    if (d < splits) {
+        const f32x2_t p = *reinterpret_cast<const f32x2_t *>(ml + 2 * d);
+        mi = p.x;
+        li = p.y;
+    }
+    float mx = mi;
+    for (int i = d + D; i < splits; i += D) mx = fmaxf(mx, ml[2 * i]);
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     if ((d & 63) == 0) red[d >> 6][0] = mx;
     __syncthreads();
@@ -311,7 +325,12 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
 #pragma unroll
     for (int k = 1; k < D / 64; ++k) mx = fmaxf(mx, red[k][0]);
     float ls = 0.f;
-    for (int i = d; i < splits; i += D) {
+    if (d < splits) {
+        const float wi = mx == -INFINITY ? 0.f : exp2f(mi - mx);
+        w[d] = wi;
+        ls = wi * li;
+    }
+    for (int i = d + D; i < splits; i += D) {
         const float wi = mx == -INFINITY ? 0.f : exp2f(ml[2 * i] - mx);
         w[i] = wi;
         ls += wi * ml[2 * i + 1];
@@ -322,23 +341,25 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
     ls = 0.f;
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) ls += red[k][1];
-    const f32x4_t *row = reinterpret_cast<const f32x4_t *>(part + ((size_t)bh * D + d) * SP);
     float acc = 0.f;
+    auto add = [&](int c, const f32x4_t &v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * c + e;
+            if (i < splits && w[i] != 0.f) acc += w[i] * v[e];
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) add(u, pre[u]);
     // Eight independent 16-byte loads in flight per batch (the loop would otherwise wait
     // out one memory latency per load).
-    constexpr int kBatch = 8;
-    for (int i0 = 0; i0 < SP / 4; i0 += kBatch) {
+    for (int i0 = kPre; i0 < SP / 4; i0 += kBatch) {
         f32x4_t v[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
             v[u] = i0 + u < SP / 4 ? row[i0 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * (i0 + u) + e;
-                if (i < splits && w[i] != 0.f) acc += w[i] * v[u][e];
-            }
+        for (int u = 0; u < kBatch; ++u) add(i0 + u, v[u]);
     }
     if (d < Du) O[(size_t)bh * Du + d] = round_act<ACT>(ls > 0.f ? acc / ls : 0.f);
 }
