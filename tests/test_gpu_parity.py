@@ -346,3 +346,32 @@ def test_nonfinite_inputs_propagate():
         y = run(case, packed, cfg).view(np.float16)
         assert not np.isfinite(y[3]).any()
         assert np.isfinite(np.delete(y, 3, axis=0)).all()
+
+
+@pytest.mark.parametrize("config", [PREFILL, PREFILL_X32, PREFILL_X32_TALL])
+@pytest.mark.parametrize("K", [256, 768, 1280])
+def test_ring_stage_waits_regression_tiny_grids_bit_exact(config, K):
+    """Regression guard for the LDS-ring race (a stage could pass its barrier before its
+    activation DMA landed): K = 256 + 512 j runs the four-stage tail, and grids of a few
+    workgroups run uncontended, where the race showed.  Identity activations make every
+    output a dequantized weight, so any stale activation stage shows as a wrong bit; each
+    case is repeated 20 times."""
+    N, g = 272, 128
+    codes, scales, zeros = workloads.weights(K, N, g, False, 0.005, 0.02, K + config)
+    for dtype in ("f16", "bf16"):
+        one = 0x3C00 if dtype == "f16" else 0x3F80
+        M = min(K, 256)
+        eye = np.zeros((M, K), dtype=np.uint16)
+        eye[np.arange(M), np.arange(M)] = one
+        case = dict(x=eye, codes=codes, scales=scales, zeros=zeros, group=g, dtype=dtype)
+        packed = pack_case(case)
+        w = oracle.dequant(codes, scales, zeros, g, dtype)[:M]
+        x = dev_half(eye, dtype)
+        say(f"ring regression config={config} K={K} {dtype}")
+        for rep in range(20):
+            y = host_bits(mp.w4a16(x, packed, config=config))
+            if not np.array_equal(y, w):
+                bad = np.argwhere(y != w)
+                print(f"[diag] rep={rep}: {len(bad)} wrong; rows {sorted(set(bad[:, 0].tolist()))[:24]}",
+                      flush=True)
+            assert np.array_equal(y, w), rep
