@@ -733,34 +733,40 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 }
 
 // Y of the split tiles: the sum of their P fp32 partials, in split order (so results do not
-// depend on which part ran first), rounded once to the output format.  One workgroup per
-// (tile, register-order chunk): thread `tid` reads the four floats that thread `tid` of the
-// main kernel wrote for that chunk -- all P loads issued before the first add -- and knows
-// their (m, n) the same way.
+// depend on which part ran first), rounded once to the output format.  Eight workgroups per
+// tile, four of its 32 register-order chunks each: thread `tid` reads the four floats that
+// thread `tid` of the main kernel wrote for each of its chunks -- all 4 P loads issued
+// before the first add, so one memory round trip covers them -- and knows their (m, n)
+// the same way.
 template <int ACT, int NB>
 __global__ __launch_bounds__(kXThreads) void x32_split_reduce_kernel(
     const f32x4_t *__restrict__ part, int full, int P, int M, int N, int Ny,
     uint16_t *__restrict__ Y) {
     constexpr int MB = 8 / NB, BM = tile_m(NB), BN = tile_n(NB);
     constexpr int kChunksPerPart = BM * BN / 4;
-    constexpr int kMaxParts = 8;
-    const int sidx = blockIdx.x >> 5, i = blockIdx.x & 31;
+    constexpr int kMaxParts = 8, kCpt = 4;     // parts, chunks per thread
+    const int sidx = blockIdx.x >> 3, c0 = (blockIdx.x & 7) * kCpt;
     int mt, nt;
     tile_of(full + sidx, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const f32x4_t *src = part + (size_t)sidx * P * kChunksPerPart + i * kXThreads + tid;
-    f32x4_t v[kMaxParts];
+    const f32x4_t *src = part + (size_t)sidx * P * kChunksPerPart + c0 * kXThreads + tid;
+    f32x4_t v[kMaxParts][kCpt];
 #pragma unroll
     for (int o = 0; o < kMaxParts; ++o)
-        if (o < P) v[o] = src[(size_t)o * kChunksPerPart];
-    f32x4_t s = v[0];
 #pragma unroll
-    for (int o = 1; o < kMaxParts; ++o)
-        if (o < P) s += v[o];
-    const int nb = i / (4 * MB), mb = (i / 4) % MB, q = i % 4;
-    const int n = nt * BN + wave * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
-    const int m = mt * BM + mb * 32 + (lane & 31);
-    if (m < M && n < Ny) store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, s);
+        for (int j = 0; j < kCpt; ++j)
+            if (o < P) v[o][j] = src[(size_t)o * kChunksPerPart + j * kXThreads];
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+        f32x4_t s = v[0][j];
+#pragma unroll
+        for (int o = 1; o < kMaxParts; ++o)
+            if (o < P) s += v[o][j];
+        const int i = c0 + j, nb = i / (4 * MB), mb = (i / 4) % MB, q = i % 4;
+        const int n = nt * BN + wave * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
+        const int m = mt * BM + mb * 32 + (lane & 31);
+        if (m < M && n < Ny) store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, s);
+    }
 }
 
 // Stage-loop length of the kernel: the packed K rounded up to a multiple of 256.
@@ -830,7 +836,7 @@ void launch_one(const GemmArgs &a, hipStream_t stream) {
         <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
                                                loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p, part);
     if (sp.p > 1)
-        x32_split_reduce_kernel<ACT, NB><<<dim3((unsigned)(tiles - sp.full) * 32), dim3(kXThreads),
+        x32_split_reduce_kernel<ACT, NB><<<dim3((unsigned)(tiles - sp.full) * 8), dim3(kXThreads),
                                            0, stream>>>(reinterpret_cast<const f32x4_t *>(part),
                                                         sp.full, sp.p, a.M, a.Np, a.N, a.Y);
 }
