@@ -129,9 +129,9 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
  * Device workspace (bytes) mpgemm_w4a16 and mpgemm_w4a16_config use for this problem on the
  * current device: nonzero when a small-M kernel splits K over several workgroups (the
  * largest need of the configurations that can run M rows, and of 64-row chunks when
- * M > 64), or when a tiled kernel (M > 64) splits the K range of the tiles of its last,
- * partial round of workgroups.  The workspace holds arrival counters in its first 256 KiB
- * and fp32 partial sums after them.
+ * M > 64), or when a tiled kernel (M > 64) splits the K range of its tiles because the
+ * grid has fewer tiles than the device has compute units.  The workspace holds arrival
+ * counters in its first 256 KiB and fp32 partial sums after them.
  *   - It must be all zero before its first use; every call leaves the counters zero again,
  *     so one zeroed allocation serves any number of later calls.
  *   - Calls that share a workspace must not run concurrently (use one per stream).

@@ -88,7 +88,8 @@ hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream)
 hipError_t launch_repack_lowbit_u4(int bits, bool symmetric, const void *packed_codes, int Kp,
                                    int Np, void *out, hipStream_t stream);
 // Workspace bytes with which the 32x32x16 kernels (either tile shape) split the K range of
-// their last, partial round of tiles; 0 when they never do for this shape.  N, K: user shape.
+// their tiles (grids of fewer tiles than compute units); 0 when they never do for this
+// shape.  N, K: user shape.
 size_t x32_workspace_bytes(int M, int N, int K);
 hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
