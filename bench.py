@@ -26,6 +26,8 @@ scaled by what the same counters read for a plain 1 GiB copy (--copy-calibration
 taken from the summary file under profiles/ and reported only while the kernel sources
 still hash to the digest recorded there, else null.
 
+`w4a16_small_m_per_gemm` repeats the per-GEMM pass at M = 128, 256 and 512 (grids of fewer
+tiles than compute units, where the tiled kernels split K), against the MFMA roofline.
 `w8a16_per_gemm` repeats the per-GEMM pass with 8-bit weights (mpgemm_w8a16, same shapes,
 its own rotating pool), each GEMM against the HBM roofline (M <= 64; bytes count one byte
 per code and per zero) or the fp16 MFMA roofline.  `wfp8a16_qwen3_8b_per_gemm` does the
@@ -213,6 +215,8 @@ def main():
                     help="replay the timed steps from captured HIP graphs")
     ap.add_argument("--no-per-gemm", action="store_true",
                     help="skip the per-GEMM breakdown pass (counter runs use this)")
+    ap.add_argument("--no-small-m", action="store_true",
+                    help="skip the W4A16 pass at M = 128, 256, 512")
     ap.add_argument("--no-w8", action="store_true",
                     help="skip the W8A16 per-GEMM pass (8-bit weights, same shapes)")
     ap.add_argument("--no-fp8", action="store_true",
@@ -455,6 +459,13 @@ def main():
     def dev_f16(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
 
+    # W4A16 at small prefill batches (M = 128, 256, 512): grids of fewer tiles than CUs,
+    # where the tiled kernels split K.
+    small = []
+    if not args.no_small_m:
+        small = variant_pass(layer, shapes, mp.w4a16, gemm_bytes, torch.float16,
+                             ms=(128, 256, 512))
+
     # W8A16 (8-bit weights, asymmetric) at the Llama-3-8B shapes, fp16 activations.
     w8 = []
     if not args.no_w8:
@@ -533,6 +544,7 @@ def main():
         "roofline": roofline(dominant),
         "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
         "per_gemm": per_call,
+        "w4a16_small_m_per_gemm": small,
         "w8a16_per_gemm": w8,
         "wfp8a16_qwen3_8b_per_gemm": fp8,
         **lowbit,
