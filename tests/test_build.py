@@ -72,3 +72,30 @@ def test_stage_wait_check_flags_a_wait_that_can_pass_early():
 def test_stage_wait_check_flags_a_stage_never_issued():
     seq = ["buffer_load_dwordx4 v1, s[0:3], s4 offen lds", "s_waitcnt vmcnt(0)", "s_barrier"]
     assert build.stage_wait_violations(seq, 2) == [(0, -1, 0)]
+
+
+def _kernel_asm(tail_wait):
+    """A ring kernel's skeleton as the compiler lays it out: prologue (three 2-load DMA
+    stages, barrier), a branch over the loop, the loop body (four stages), the branch over
+    the four-stage tail, the tail, and the block that skips the loop."""
+    dma = "\tbuffer_load_dwordx4 v1, s[0:3], s4 offen lds"
+    w = "\tbuffer_load_dwordx4 v[2:5], v6, s[8:11], s4 offen"
+
+    def stage(wait):
+        return [f"\ts_waitcnt vmcnt({wait})", "\ts_barrier", dma, dma, w]
+    lines = ["_Z18prefill_x32_kernelv:", dma, dma, dma, dma, dma, dma, w,
+             "\ts_waitcnt vmcnt(4)", "\ts_barrier", "\ts_cbranch_scc1 .LBB0_9", ".LBB0_2:"]
+    for _ in range(4):
+        lines += stage(2)
+    lines += ["\ts_cbranch_scc1 .LBB0_2", "\ts_cbranch_scc1 .LBB0_7", ".LBB0_6:"]
+    for _ in range(4):
+        lines += stage(tail_wait)
+    lines += [".LBB0_7:", "\ts_endpgm", ".LBB0_9:", "\ts_mov_b32 s5, 0",
+              "\ts_cbranch_scc0 .LBB0_6", "\ts_branch .LBB0_7", ".Lfunc_end0:", ""]
+    return "\n" + "\n".join(lines)
+
+
+def test_ring_wait_check_walks_loop_and_tail_paths():
+    assert build.ring_wait_violations(_kernel_asm(2)) == []
+    bad = build.ring_wait_violations(_kernel_asm(5))     # tail waits leave too much in flight
+    assert {path for _, path, _ in bad} == {"loop and tail", "tail only"}
