@@ -163,13 +163,11 @@ int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void 
  * a shape (a positive id); mpgemm_config_name describes an id ("" for unknown ids);
  * mpgemm_w4a16_config runs one configuration explicitly (same contract as mpgemm_w4a16;
  * config_id 0 means "select"; an id that cannot run the shape returns
- * MPGEMM_ERR_UNSUPPORTED).  Ids: 1..4 small-M kernel with 1..4 row blocks of 16
- * (M <= 16*id); 10 tiled large-M kernel on 16x16x32 MFMAs with a four-stage LDS ring;
- * 11 tiled large-M kernel with two LDS buffers (any K); 12 tiled large-M kernel on 32x32x16
- * MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a 256 x 128
- * tile.  Id 10 needs K % 256 == 0 and runs as id 11 on other K; ids 10 and 11 do not take
- * ragged K (K % 128 != 0).  Ids 12 and 13 take every shape.  The selector picks 1..4 for
- * M <= 64; else 13 when M >= 512 and (N >= 16384 or K >= 8192); else 12.
+ * MPGEMM_ERR_UNSUPPORTED; an unknown id returns MPGEMM_ERR_INVALID_ARG).  Ids: 1..4
+ * small-M kernel with 1..4 row blocks of 16 (M <= 16*id); 12 tiled large-M kernel on
+ * 32x32x16 MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a
+ * 256 x 128 tile.  Ids 12 and 13 take every shape.  The selector picks 1..4 for M <= 64;
+ * else 13 when M >= 512 and (N >= 16384 or K >= 8192); else 12.
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);
@@ -222,7 +220,7 @@ int mpgemm_unpack_w8(const void *packed_codes, const void *packed_meta, int K, i
  * Y[M][N] = X[M][K] * dequant(W8)[K][N] with fp32 accumulation; arguments as for
  * mpgemm_w4a16, with planes written by mpgemm_pack_weights_w8.  mpgemm_w8a16_config runs
  * one configuration (ids as for mpgemm_w4a16_config: 1..4 small-M, 12 and 13 tiled
- * 32x32x16; 10 and 11 are not provided for 8-bit codes and return MPGEMM_ERR_UNSUPPORTED).
+ * 32x32x16).
  */
 int mpgemm_w8a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
                  int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
@@ -301,8 +299,7 @@ int mpgemm_wfp8a16_config(const void *X, int dtype, int fp8_format, const void *
  * same value) and a 32x32x16 tiled kernel runs on them with the same meta plane
  * (configurations 0, 12 and 13).  That needs mpgemm_workspace_bytes_lowbit() bytes;
  * configuration 0 with less runs the small-M kernel on 64-row chunks instead (reading the
- * weights once per chunk), configurations 12 and 13 return MPGEMM_ERR_WORKSPACE.  Other ids
- * return MPGEMM_ERR_UNSUPPORTED.  A bits value other than 2 or 3 returns
+ * weights once per chunk), configurations 12 and 13 return MPGEMM_ERR_WORKSPACE.  A bits value other than 2 or 3 returns
  * MPGEMM_ERR_INVALID_ARG.
  */
 

@@ -205,6 +205,55 @@ def w4a16(x_bits, codes, scales_bits, zeros, group, dtype="f16", threads=1):
     return gemm(x_bits, dequant(codes, scales_bits, zeros, group, dtype), dtype, threads)
 
 
+def act_bits_to_f64(bits: np.ndarray, dtype: str = "f16") -> np.ndarray:
+    """Exact values of activation-format bits, in bulk: binary16 through numpy's float16;
+    bf16 as the high half of a binary32 (its definition).  Pinned against the scalar
+    conversions above over every bit pattern (tests/test_oracle.py)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    if _dtype_code(dtype) == F16:
+        return b.view(np.float16).astype(np.float64)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def gemm_f64(x_bits: np.ndarray, w_bits: np.ndarray, dtype: str = "f16") -> np.ndarray:
+    """X @ w in float64, before the output rounding, with numpy's float64 matmul as a
+    library step.  Each product of two 16-bit values is exact in float64, and any
+    summation order stays within about K * 2^-53 of the sum of magnitudes of the exact
+    sum: far below one unit in the last place of a 16-bit output.  For shapes whose scalar
+    loop (gemm) would take minutes; pinned against gemm and an exact rational sum
+    (tests/test_oracle.py)."""
+    x = act_bits_to_f64(x_bits, dtype)
+    w = act_bits_to_f64(w_bits, dtype)
+    assert x.ndim == 2 and w.ndim == 2 and x.shape[1] == w.shape[0]
+    return x @ w
+
+
+def w4a16_f64(x_bits, codes, scales_bits, zeros, group, dtype="f16",
+              col_chunk: int = 4096, threads: int = 0) -> np.ndarray:
+    """The whole path before the output rounding: dequantize (one rounding to the
+    activation format, as dequant), then gemm_f64.  Columns go in chunks of `col_chunk`,
+    whose dequantizations run in up to `threads` host threads at once (0: one per core, at
+    most 16); chunks are independent, so this changes nothing in the result.  Returns
+    float64 [M, N]."""
+    import concurrent.futures
+    codes = np.asarray(codes)
+    K, N = codes.shape
+    x = act_bits_to_f64(x_bits, dtype)
+    out = np.empty((x.shape[0], N), dtype=np.float64)
+    spans = [(c0, min(N, c0 + col_chunk)) for c0 in range(0, N, col_chunk)]
+
+    def deq(span):
+        c0, c1 = span
+        z = None if zeros is None else zeros[:, c0:c1]
+        return dequant(codes[:, c0:c1], scales_bits[:, c0:c1], z, group, dtype)
+
+    workers = threads or min(16, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for (c0, c1), w in zip(spans, ex.map(deq, spans)):
+            out[:, c0:c1] = x @ act_bits_to_f64(w, dtype)
+    return out
+
+
 def padded_shape(K: int, N: int) -> tuple[int, int]:
     """(Kp, Np): the packed planes' padded matrix for a user matrix of K x N."""
     lib = _load()

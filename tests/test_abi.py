@@ -75,9 +75,10 @@ def test_selector_and_config_names():
     assert mp.lib().mpgemm_select_config(2048, 28672, 4096, 128, 0) == 13  # wide N
     assert mp.lib().mpgemm_select_config(2048, 4096, 14336, 128, 0) == 13  # long K
     assert mp.lib().mpgemm_select_config(256, 28672, 4096, 128, 0) == 12   # M < 512
-    for cid in (1, 2, 3, 4, 10, 11, 12, 13):
+    for cid in (1, 2, 3, 4, 12, 13):
         assert mp.config_name(cid)
-    assert mp.config_name(7) == ""
+    for cid in (7, 10, 11):
+        assert mp.config_name(cid) == ""
 
 
 def _gemm(X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, sym=0, Y=A, cfg=None):
@@ -190,9 +191,8 @@ def _fp8(fmt=0, X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, Y=A, cfg=No
     (dict(K=100), UNSUPPORTED),
     (dict(X=0), INVALID),
     (dict(Y=MIS), ALIGN),
-    (dict(cfg=10, M=128), UNSUPPORTED),              # the 16x16x32 tiled kernels take 4-bit only
-    (dict(cfg=11, M=128), UNSUPPORTED),
-    (dict(cfg=10, M=128, K=384), UNSUPPORTED),
+    (dict(cfg=10, M=128), INVALID),                  # no such configuration
+    (dict(cfg=11, M=128, K=384), INVALID),
     (dict(cfg=12, M=128, K=4), UNSUPPORTED),
     (dict(M=0), OK),
 ])
@@ -206,10 +206,11 @@ def test_binding_fp8_format_names_match_header():
     assert mp.FP8_FORMATS == {"e4m3": 0, "e5m2": 1}
 
 
-@pytest.mark.parametrize("cfg", [10, 11])
-def test_ragged_k_is_refused_by_the_16x16x32_tiled_kernels(cfg):
-    # K = 200 pads to 256: only the small-M and 32x32x16 kernels mask the activation tail
-    assert _gemm(M=128, K=200, cfg=cfg) == UNSUPPORTED
+@pytest.mark.parametrize("cfg", [5, 10, 11, 14, -1])
+def test_unknown_configuration_ids_are_rejected(cfg):
+    # 10 and 11 named 16x16x32 tiled kernels that the selector never chose; they are gone
+    assert _gemm(M=128, K=256, cfg=cfg) == INVALID
+    assert _gemm(M=128, K=200, cfg=cfg) == INVALID
 
 
 def _low(bits=2, cfg=0, M=16, K=256):
@@ -224,8 +225,7 @@ def _low(bits=2, cfg=0, M=16, K=256):
     (dict(bits=1), INVALID),
     (dict(cfg=12, M=128), WORKSPACE),        # tiled: the 4-bit rewrite needs the workspace
     (dict(cfg=13, M=128), WORKSPACE),
-    (dict(cfg=10, M=128), UNSUPPORTED),      # no 16x16x32 tiled kernel for sub-4-bit codes
-    (dict(cfg=11, M=128), UNSUPPORTED),
+    (dict(cfg=10, M=128), INVALID),          # no such configuration
     (dict(cfg=1, M=17), UNSUPPORTED),
     (dict(K=12), UNSUPPORTED),
     (dict(M=0), OK),
@@ -277,3 +277,63 @@ def test_lowbit_workspace_covers_the_4bit_rewrite_at_large_m():
         assert big >= 256 * 1024 + 4096 * 4096 // 2
         assert lib.mpgemm_workspace_bytes_lowbit(bits, 300, 40, 200, 128, 0) >= 256 * 1024 + 256 * 48 // 2
     assert lib.mpgemm_workspace_bytes_lowbit(4, 2048, 4096, 4096, 128, 0) == 0
+
+
+# ------------------------------------------------------------ probes and the binding --
+
+PROBE_HEADER = os.path.join(ROOT, "include", "mpgemm_probes.h")
+
+
+def test_probe_library_exports_every_declared_function_and_validates():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mpgemm_\w+)\s*\(", text)))
+    assert names == ["mpgemm_probe_hbm_read", "mpgemm_probe_mfma"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_quantized_mpgemm_amd",
+                                   "libmpgemm_probes.so"))
+    for name in names:
+        assert hasattr(lib, name), name
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    read, mfma = lib.mpgemm_probe_hbm_read, lib.mpgemm_probe_mfma
+    read.argtypes = [vp, sz, ctypes.c_int, ctypes.c_int, vp, vp]
+    mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    assert read(None, 1024, 64, 8, vp(A), None) == INVALID
+    assert read(vp(A), 1000, 64, 8, vp(A), None) == INVALID          # not a multiple of 16
+    assert read(vp(A), 1024, 0, 8, vp(A), None) == INVALID
+    assert read(vp(A), 1024, 64, 5, vp(A), None) == INVALID          # unroll not 4/8/16
+    assert read(vp(MIS), 1024, 64, 8, vp(A), None) == ALIGN
+    assert mfma(9, 10, 1, vp(A), None) == INVALID
+    assert mfma(0, 0, 1, vp(A), None) == INVALID
+    assert mfma(0, 10, 1, None, None) == INVALID
+
+
+def test_workspace_cache_gives_each_stream_its_own_buffer():
+    """Split-K calls racing on shared arrival counters is what this prevents: two streams
+    of one device never share a workspace; one stream reuses its own."""
+    import torch
+    made = []
+
+    def alloc(idx, n):
+        made.append((idx, n))
+        return torch.zeros(n, dtype=torch.uint8)
+
+    cache = mp.WorkspaceCache(alloc)
+    a = cache.get(0, 111, 4096)
+    b = cache.get(0, 222, 4096)
+    assert a is not b and a.data_ptr() != b.data_ptr()
+    assert cache.get(0, 111, 100) is a
+    assert cache.get(1, 111, 100) is not a                 # another device
+    big = cache.get(0, 111, 8 << 20)
+    assert big is not a and big.numel() >= 8 << 20
+    assert cache.get(0, 111, 10) is big
+    assert cache.get(0, 222, 10) is b
+    assert cache.get(0, 111, 0) is None
+    assert int(a.sum()) == 0 and int(big.sum()) == 0
+    # under capture nothing is allocated: a stream without a workspace takes another
+    # stream's of the same device, if one is large enough
+    assert cache.get(0, 333, 10, capturing=True).numel() >= 10
+    assert cache.get(1, 333, 100, capturing=True) is not None
+    with pytest.raises(mp.MpgemmError):
+        cache.get(0, 333, 64 << 20, capturing=True)
+    with pytest.raises(mp.MpgemmError):
+        cache.get(2, 333, 10, capturing=True)
+    assert [i for i, _ in made] == [0, 0, 1, 0]

@@ -75,7 +75,7 @@ def test_lowbit_weights_are_not_accepted_by_the_other_gemms():
         mp.w4a16(x, packed)
     with pytest.raises(mp.MpgemmError):
         mp.wlowbit_a16(torch.zeros((128, 256), dtype=torch.float16, device="cuda"), packed,
-                       config=10)
+                       config=7)                     # no such configuration
 
 
 @pytest.mark.parametrize("bits", BITS)

@@ -27,10 +27,7 @@ SHAPES = [(200, 48), (256, 40), (384, 7), (136, 1), (1000, 33), (4104, 100), (8,
 
 
 def configs(M, K, code):
-    cs = [c for c in (1, 2, 3, 4) if M <= 16 * c] + [12, 13]
-    if code == "w4" and K % 128 == 0:       # 16x16x32 tiled kernels: aligned 4-bit only
-        cs += [11] + ([10] if K % 256 == 0 else [])
-    return cs
+    return [c for c in (1, 2, 3, 4) if M <= 16 * c] + [12, 13]
 
 
 def make(code, K, N, g, sym, seed):

@@ -95,3 +95,38 @@ def test_split_k_counters_reset_across_calls_and_shapes(monkeypatch):
         assert np.array_equal(host_bits(yb), first_b)
     ref = oracle.w4a16(a["x"], a["codes"], a["scales"], a["zeros"], a["group"])
     assert rel_err(first_a, ref, "f16") <= REL_TOL
+
+
+def test_split_k_on_two_streams_at_once():
+    """Each stream gets its own cached workspace, so split-K calls that overlap on two
+    streams do not share arrival counters: every result equals the one-stream result."""
+    say("split-K two streams")
+    a = _case(16, 14336, 4096, 3)
+    b = _case(1, 14336, 2048, 4)
+    _forced(16, 14336, 4096)
+    _forced(1, 14336, 2048)
+    pa, pb = pack_case(a), pack_case(b)
+    xa, xb = dev_half(a["x"]), dev_half(b["x"])
+    want_a = host_bits(mp.w4a16(xa, pa))
+    want_b = host_bits(mp.w4a16(xb, pb))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for _ in range(8):
+        with torch.cuda.stream(s1):
+            ya = mp.w4a16(xa, pa)
+        with torch.cuda.stream(s2):
+            yb = mp.w4a16(xb, pb)
+        outs.append((ya, yb))
+    torch.cuda.synchronize()
+    wa = mp.workspace_for(torch.device("cuda"), 1)
+    with torch.cuda.stream(s1):
+        w1 = mp.workspace_for(torch.device("cuda"), 1)
+    with torch.cuda.stream(s2):
+        w2 = mp.workspace_for(torch.device("cuda"), 1)
+    assert len({wa.data_ptr(), w1.data_ptr(), w2.data_ptr()}) == 3
+    for ya, yb in outs:
+        assert np.array_equal(host_bits(ya), want_a)
+        assert np.array_equal(host_bits(yb), want_b)
+    ref = oracle.w4a16(b["x"], b["codes"], b["scales"], b["zeros"], b["group"], threads=8)
+    assert rel_err(want_b, ref, "f16") <= REL_TOL

@@ -291,6 +291,49 @@ def test_gemm_threads_do_not_change_result():
                           oracle.gemm(case["x"], w, threads=4))
 
 
+# -------------------------------------------------- large-shape route (float64 step) --
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bulk_activation_decode_matches_scalar_conversion_every_pattern(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bulk = oracle.act_bits_to_f64(bits, dtype)
+    scalar = (oracle.f16_bits_to_f64 if dtype == "f16" else oracle.bf16_bits_to_f64)(bits)
+    nan = np.isnan(scalar)
+    assert np.array_equal(np.isnan(bulk), nan)
+    assert np.array_equal(bulk[~nan], scalar[~nan])
+    assert np.array_equal(np.signbit(bulk[~nan]), np.signbit(scalar[~nan]))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,K,N", [(3, 256, 40), (7, 1024, 24), (1, 4096, 16)])
+def test_gemm_f64_rounded_equals_scalar_gemm(dtype, M, K, N):
+    """Rounded once to the activation format, the float64 route gives the scalar loop's
+    output bit for bit (the two sums differ by far less than half an output ulp), on both
+    operand orders that a transposed-operand mistake would confuse (M != N)."""
+    seed = 200 + M + K + N
+    codes, scales, zeros = workloads.weights(K, N, 128, False, 0.005, 0.02, seed)
+    x = workloads.activations(M, K, dtype, seed + 1)
+    w = oracle.dequant(codes, scales, zeros, 128, dtype)
+    ref = oracle.gemm(x, w, dtype, threads=4)
+    y64 = oracle.gemm_f64(x, w, dtype)
+    enc = oracle.f64_to_f16_bits if dtype == "f16" else oracle.f64_to_bf16_bits
+    assert np.array_equal(enc(y64), ref)
+    assert np.array_equal(enc(oracle.w4a16_f64(x, codes, scales, zeros, 128, dtype,
+                                               col_chunk=7)), ref)
+
+
+def test_gemm_f64_within_its_bound_of_the_exact_rational_sum():
+    case = workloads.make_case(workloads.TINY, 2, 256, 256, seed=16)
+    w = oracle.dequant(case["codes"], case["scales"], case["zeros"], 128)
+    y64 = oracle.gemm_f64(case["x"], w)
+    for m in range(2):
+        for n in (0, 17, 255):
+            terms = [exact_f16(case["x"][m, k]) * exact_f16(w[k, n]) for k in range(256)]
+            exact = sum(terms, Fraction(0))
+            bound = 256 * 2.0 ** -53 * float(sum(abs(t) for t in terms))
+            assert abs(Fraction(float(y64[m, n])) - exact) <= Fraction(bound)
+
+
 # ------------------------------------------------------------------------- packing --
 
 def _read_golden(name):

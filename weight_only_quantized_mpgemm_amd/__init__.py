@@ -309,27 +309,59 @@ def config_name(config_id: int) -> str:
     return lib().mpgemm_config_name(config_id).decode()
 
 
-# One zeroed workspace per device, grown on demand and never freed: the kernels leave its
-# counters zero after every call, and graphs captured with an older (smaller) one keep a
-# valid pointer.  Calls that run concurrently on different streams of one device must
-# each pass their own zeroed `workspace`.
-_WORKSPACES: dict[int, list[torch.Tensor]] = {}
+class WorkspaceCache:
+    """Device workspaces keyed by (device index, stream handle), grown on demand and never
+    freed: graphs captured with an older (smaller) one keep a valid pointer.
+
+    Split-K calls that share a workspace must not overlap in time (their arrival counters
+    would race), and calls on different streams may overlap, so every stream gets a
+    workspace of its own.  `alloc(device_index, nbytes)` returns a zero-filled uint8
+    tensor; the GEMM kernels leave the counters zero after every call, so a buffer is
+    zeroed only once."""
+
+    def __init__(self, alloc):
+        self._alloc = alloc
+        self._bufs: dict[tuple[int, int], list[torch.Tensor]] = {}
+
+    def get(self, device_index: int, stream: int, nbytes: int, capturing: bool = False):
+        """The workspace of (device_index, stream) with at least `nbytes`.  Under graph
+        capture nothing is allocated: a stream being captured (torch captures on a side
+        stream) without a large enough workspace of its own takes one of another stream of
+        the device (the eager warm-up call's).  Such a graph must then not replay while
+        split-K calls run on that other stream; graphs that need that pass their own
+        `workspace`."""
+        if nbytes == 0:
+            return None
+        cached = self._bufs.setdefault((device_index, stream), [])
+        if cached and cached[-1].numel() >= nbytes:
+            return cached[-1]
+        if capturing:
+            for (dev, _), bufs in self._bufs.items():
+                if dev == device_index and bufs and bufs[-1].numel() >= nbytes:
+                    return bufs[-1]
+            raise MpgemmError(-4, f"allocating a {nbytes}-byte workspace during graph "
+                                  "capture (make one eager call of this shape first)")
+        ws = self._alloc(device_index, max(nbytes, 1 << 20))
+        cached.append(ws)
+        return ws
+
+
+def _device_index(device: torch.device) -> int:
+    return device.index if device.index is not None else torch.cuda.current_device()
+
+
+_WORKSPACES = WorkspaceCache(
+    lambda idx, n: torch.zeros(n, dtype=torch.uint8, device=torch.device("cuda", idx)))
 
 
 def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor | None:
-    """The cached zeroed workspace of `device` with at least `nbytes` (None for 0)."""
+    """The cached zeroed workspace of `device` and its current stream with at least
+    `nbytes` (None for 0)."""
     if nbytes == 0:
         return None
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    cached = _WORKSPACES.setdefault(idx, [])
-    if cached and cached[-1].numel() >= nbytes:
-        return cached[-1]
-    if torch.cuda.is_current_stream_capturing():
-        raise MpgemmError(-4, f"allocating a {nbytes}-byte workspace during graph capture "
-                              "(make one eager call of this shape first)")
-    ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-    cached.append(ws)
-    return ws
+    idx = _device_index(device)
+    return _WORKSPACES.get(idx, torch.cuda.current_stream(idx).cuda_stream, nbytes,
+                           torch.cuda.is_current_stream_capturing())
 
 
 def _gemm(kind: str, x: torch.Tensor, packed: PackedWeights, out, config, workspace):
@@ -408,22 +440,18 @@ def wfp8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = N
 # ------------------------------------------- attention decode (8-bit / FP8 KV cache) --
 
 # Attention partials need no initialization, but must not share the GEMM workspace (whose
-# split-K counters have to stay zero between calls): a cache of their own.
-_ATTN_WORKSPACES: dict[int, torch.Tensor] = {}
+# split-K counters have to stay zero between calls), nor a buffer with an attention call
+# that may run at the same time on another stream: a cache of their own, per stream.
+_ATTN_WORKSPACES = WorkspaceCache(
+    lambda idx, n: torch.empty(n, dtype=torch.uint8, device=torch.device("cuda", idx)))
 
 
 def _attention_workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
     if nbytes == 0:
         return None
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _ATTN_WORKSPACES.get(idx)
-    if ws is None or ws.numel() < nbytes:
-        if torch.cuda.is_current_stream_capturing():
-            raise MpgemmError(-4, f"allocating a {nbytes}-byte attention workspace during "
-                                  "graph capture (make one eager call of this shape first)")
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _ATTN_WORKSPACES[idx] = ws
-    return ws
+    idx = _device_index(device)
+    return _ATTN_WORKSPACES.get(idx, torch.cuda.current_stream(idx).cuda_stream, nbytes,
+                                torch.cuda.is_current_stream_capturing())
 
 
 def kv_block_bytes(Hkv: int, D: int) -> int:

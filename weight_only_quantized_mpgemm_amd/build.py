@@ -24,10 +24,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmpgemm.so")
-SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill.hip", "gemm_prefill_ring.hip",
-           "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip", "gemm_prefill_x32_fp8.hip",
+SOURCES = ["api.hip", "pack.hip", "gemm_decode.hip", "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip", "gemm_prefill_x32_fp8.hip",
            "attention.hip"]
 HEADERS = ["device.hpp", "kernels.hpp", "prefill_x32.hpp"]
+# Peak microkernels (include/mpgemm_probes.h): a library of their own, apart from the GEMM
+# path, for the measured roofline denominators.
+PROBE_SOURCES = ["probes.hip"]
+PROBE_LIB = os.path.join(PKG, "libmpgemm_probes.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -51,7 +54,7 @@ def scratch_users(report: str) -> list[tuple[str, int]]:
 
 # Sources whose kernels issue MFMAs through inline asm: the compiler does not know those
 # instructions' result latency, so the build checks the generated code instead.
-ASM_MFMA_SOURCES = ["gemm_prefill_ring.hip", "gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip",
+ASM_MFMA_SOURCES = ["gemm_prefill_x32.hip", "gemm_prefill_x32_w8.hip",
                     "gemm_prefill_x32_fp8.hip"]
 MIN_RESULT_WAIT = 32     # wait states between an MFMA and the first read of its result
 
@@ -148,15 +151,13 @@ def ring_wait_violations(asm: str) -> list[tuple[str, str, list]]:
     four-stage tail after one pass of the loop or in place of it."""
     out = []
     for name in re.findall(r"\n([A-Za-z_][\w.$]*):[^\n]*\n", asm):
-        if "prefill_x32_kernel" not in name and "prefill_ring_kernel" not in name:
+        if "prefill_x32_kernel" not in name:
             continue
         lines = _path_lines(asm, name)
         lab = {ln[:-1]: i for i, ln in enumerate(lines) if re.match(r"\.LBB\w+:$", ln)}
         b0 = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
-        # DMA loads per stage and wave: the x32 prologue issues three stages, the ring
-        # kernel four loads per stage
-        mb = 4 if "prefill_ring_kernel" in name else \
-            sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // 3
+        # DMA loads per stage and wave: the prologue issues three stages
+        mb = sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // 3
         br = next(i for i in range(b0, len(lines)) if lines[i].startswith("s_cbranch"))
         skip = lines[br].split()[1]
         top = next(i for i in range(br + 1, len(lines)) if re.match(r"\.LBB\w+:$", lines[i]))
@@ -191,7 +192,7 @@ def _check_asm_mfma(src: str, extra: list[str]) -> None:
     bad = acc_read_hazards(asm)
     if bad:
         raise RuntimeError(f"{src}: MFMA results read too early (wait states): {bad}")
-    if "prefill_x32" in src or "prefill_ring" in src:
+    if "prefill_x32" in src:
         bad = ring_wait_violations(asm)
         if bad:
             raise RuntimeError(f"{src}: a stage wait can pass before its DMA landed: {bad[:4]}")
@@ -210,23 +211,30 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compiles every source (always; no staleness shortcuts) and links libmpgemm.so."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    extra = list(extra or [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
-        checks = [ex.submit(_check_asm_mfma, s, extra) for s in ASM_MFMA_SOURCES]
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-        for c in checks:
-            c.result()
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compiles every source (always; no staleness shortcuts) and links libmpgemm.so and
+    libmpgemm_probes.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    extra = list(extra or [])
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs) + 2) as ex:
+        checks = [ex.submit(_check_asm_mfma, s, extra) for s in ASM_MFMA_SOURCES]
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra), srcs)))
+        for c in checks:
+            c.result()
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

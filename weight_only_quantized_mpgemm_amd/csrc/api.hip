@@ -21,8 +21,6 @@ enum ConfigId {
     kConfigDecode2 = 2,
     kConfigDecode3 = 3,
     kConfigDecode4 = 4,
-    kConfigPrefill = 10,       // 16x16x32 LDS-ring kernel when K % 256 == 0, else two-buffer
-    kConfigPrefill2Buf = 11,   // two-buffer kernel
     kConfigPrefillX32 = 12,    // 32x32x16 kernel, 128 x 256 workgroup tile
     kConfigPrefillX32Tall = 13,  // same, 256 x 128 workgroup tile
 };
@@ -98,7 +96,6 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     if (st != MPGEMM_OK) return st;
     if (config_id != kConfigSelect &&
         !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) ||
-          config_id == kConfigPrefill || config_id == kConfigPrefill2Buf ||
           config_id == kConfigPrefillX32 || config_id == kConfigPrefillX32Tall))
         return MPGEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return MPGEMM_OK;
@@ -114,18 +111,10 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
-    // 2- and 3-bit codes run the small-M kernel only (the tiled kernels have no sub-4-bit
-    // dequantization): larger M goes through it in chunks of 64 rows.
+    // 2- and 3-bit codes: the small-M kernel, or (M > 64) a 4-bit rewrite of the codes and
+    // the tiled kernel (below).
     const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
-    if (lowbit && config_id != kConfigSelect && !(cfg >= kConfigDecode1 && cfg <= kConfigDecode4) &&
-        cfg != kConfigPrefillX32 && cfg != kConfigPrefillX32Tall)
-        return MPGEMM_ERR_UNSUPPORTED;
-    // 8-bit and FP8 codes, and ragged K, run the small-M kernel and the 32x32x16 tiled
-    // kernels (which mask the activations past K); the 16x16x32 tiled kernels take aligned
-    // 4-bit problems only.
     const int Kp = mpgemm::padded_k(K);
-    if ((code != mpgemm::kU4 || Kp != K) && (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf))
-        return MPGEMM_ERR_UNSUPPORTED;
 
     mpgemm::GemmArgs a;
     a.X = (const uint16_t *)X;
@@ -193,11 +182,8 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
         fprintf(stderr, "mpgemm: %s M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", names[code],
                 M, N, K, group, dtype, symmetric, mpgemm_config_name(cfg));
     }
-    if (cfg == kConfigPrefill && K % 256 == 0) return hip_status(mpgemm::launch_prefill_ring(a, s));
     if (cfg == kConfigPrefillX32) return hip_status(mpgemm::launch_prefill_x32(a, s));
     if (cfg == kConfigPrefillX32Tall) return hip_status(mpgemm::launch_prefill_x32_tall(a, s));
-    if (cfg == kConfigPrefill || cfg == kConfigPrefill2Buf)
-        return hip_status(mpgemm::launch_prefill(a, s));
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
 
@@ -574,8 +560,6 @@ const char *mpgemm_config_name(int config_id) {
         case kConfigDecode2: return "decode_splitk_m32";
         case kConfigDecode3: return "decode_splitk_m48";
         case kConfigDecode4: return "decode_splitk_m64";
-        case kConfigPrefill: return "prefill_ring16_128x256";
-        case kConfigPrefill2Buf: return "prefill_2buf_128x256";
         case kConfigPrefillX32: return "prefill_x32_128x256";
         case kConfigPrefillX32Tall: return "prefill_x32_256x128";
         default: return "";

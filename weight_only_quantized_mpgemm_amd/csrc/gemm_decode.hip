@@ -424,7 +424,20 @@ void launch_code(const GemmArgs &a, int mblocks, hipStream_t stream) {
                    : launch_act<kF16, CODE>(a, mblocks, stream);
 }
 
+__global__ void fill_zero_kernel(uint16_t *__restrict__ Y, size_t count) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) Y[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero(uint16_t *Y, size_t count, hipStream_t stream) {
+    if (count) {
+        const unsigned threads = 256;
+        fill_zero_kernel<<<(unsigned)((count + threads - 1) / threads), threads, 0, stream>>>(Y, count);
+    }
+    return hipGetLastError();
+}
 
 size_t decode_workspace_bytes(int M, int N, int K, int mblocks) {
     const int strips = padded_n(N) >> 4;

@@ -70,9 +70,7 @@ hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
 // N, K: the user shape.
 size_t decode_workspace_bytes(int M, int N, int K, int mblocks);
 
-// Tiled large-M kernels (128 rows x 256 columns per workgroup): the LDS-ring kernel
-// (needs K % 256 == 0) and the two-buffer kernel (any K % 128 == 0).
-hipError_t launch_prefill_ring(const GemmArgs &a, hipStream_t stream);
+// Tiled large-M kernel on 32x32x16 MFMAs with a 128 (m) x 256 (n) workgroup tile.
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
 // The 32x32x16 kernel with a 256 (m) x 128 (n) workgroup tile.
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
@@ -91,7 +89,6 @@ hipError_t launch_repack_lowbit_u4(int bits, bool symmetric, const void *packed_
 // their tiles (grids of fewer tiles than compute units); 0 when they never do for this
 // shape.  N, K: user shape.
 size_t x32_workspace_bytes(int M, int N, int K);
-hipError_t launch_prefill(const GemmArgs &a, hipStream_t stream);
 
 // Decode attention over an 8-bit KV cache (attention.hip).
 struct AttnArgs {
