@@ -159,6 +159,28 @@ int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void 
                  size_t workspace_bytes, void *stream);
 
 /*
+ * mpgemm_w4a16 for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, result
+ * and kernel selection as mpgemm_w4a16 without the workspace: the kernels that split K
+ * take their arrival counters and fp32 partials from a static device buffer of
+ * MPGEMM_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on until
+ * the process ends (given the same workspace size, mpgemm_w4a16 splits identically, so
+ * the two return the same bits).  Nothing is allocated by the call.
+ *   - The first call on a device looks the buffer up (and, outside graph capture, clears
+ *     its counters with a kernel on `stream`); make that first call outside capture.
+ *   - Every call on one device shares that device's buffer, which keeps the last call's
+ *     contents (the kernels leave its counters zero).  Calls that overlap in time on one
+ *     device (two streams, or a graph replay beside another call) race and must not be
+ *     made.
+ *   - A problem whose workspace (mpgemm_workspace_bytes) exceeds the buffer returns
+ *     MPGEMM_ERR_WORKSPACE and enqueues nothing.  On MI355X every W4A16 shape fits.
+ */
+#define MPGEMM_NOALLOC_SCRATCH_BYTES (((size_t)32 << 20) + ((size_t)256 << 10))
+int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
+                         const void *packed_meta, int M, int N, int K, int group,
+                         int symmetric, void *Y, void *stream);
+
+/*
  * Kernel selection.  mpgemm_select_config returns the configuration mpgemm_w4a16 uses for
  * a shape (a positive id); mpgemm_config_name describes an id ("" for unknown ids);
  * mpgemm_w4a16_config runs one configuration explicitly (same contract as mpgemm_w4a16;

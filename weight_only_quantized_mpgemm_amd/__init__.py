@@ -48,6 +48,7 @@ SIGNATURES = {
     "mpgemm_w4a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
     "mpgemm_status_string": (ctypes.c_char_p, [_i]),
+    "mpgemm_w4a16_noalloc": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "mpgemm_packed_code_bytes_w8": (_sz, [_i, _i]),
     "mpgemm_packed_meta_bytes_w8": (_sz, [_i, _i, _i, _i]),
     "mpgemm_pack_weights_w8": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
@@ -412,6 +413,29 @@ def w4a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = Non
     cached one).
     """
     return _gemm("w4", x, packed, out, config, workspace)
+
+
+def w4a16_noalloc(x: torch.Tensor, packed: PackedWeights,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X @ dequant(W) through mpgemm_w4a16_noalloc: no workspace, the library's static
+    per-device scratch instead (see include/mpgemm.h; calls overlapping on one GPU race).
+    `out` is allocated here only when it is not given."""
+    if packed.bits != 4 or packed.fp8:
+        raise ValueError("w4a16_noalloc takes 4-bit packed weights")
+    M, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"x has K={K}, weights have K={packed.K}")
+    act = _act_code(x.dtype)
+    _need(x, x.dtype, (M, K), "x")
+    N = packed.N
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _need(out, x.dtype, (M, N), "out")
+    st = lib().mpgemm_w4a16_noalloc(_ptr(x), act, _ptr(packed.codes), _ptr(packed.meta), M, N,
+                                    K, packed.group, int(packed.symmetric), _ptr(out),
+                                    _stream(x.device))
+    _check(st, "mpgemm_w4a16_noalloc")
+    return out
 
 
 def w8a16(x: torch.Tensor, packed: PackedWeights, out: torch.Tensor | None = None,

@@ -8,8 +8,13 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "mpgemm.h"
 #include "kernels.hpp"
+
+// Workspace of mpgemm_w4a16_noalloc (see scratch_of_current_device).
+static __device__ __align__(256) uint8_t scratch[MPGEMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -187,6 +192,42 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
 
+// ------------------------------------------------------------ allocation-free scratch --
+// The workspace of mpgemm_w4a16_noalloc: a file-scope device array, one copy per device,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: the device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that pointer is handed to kernels.
+constexpr size_t kScratchBytes = MPGEMM_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > mpgemm::kSplitCounterBytes, "scratch holds the counters");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up and, outside graph capture, its counter
+// region cleared by a kernel on `stream`, at the first call on that device).
+int scratch_of_current_device(void *stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MPGEMM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MPGEMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return MPGEMM_ERR_HIP;
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing((hipStream_t)stream, &cap) != hipSuccess) return MPGEMM_ERR_HIP;
+        if (cap == hipStreamCaptureStatusNone) {
+            const int st = hip_status(mpgemm::launch_fill_zero(
+                static_cast<uint16_t *>(p), mpgemm::kSplitCounterBytes / 2, (hipStream_t)stream));
+            if (st != MPGEMM_OK) return st;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MPGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,6 +310,21 @@ int mpgemm_w4a16(const void *X, int dtype, const void *packed_codes, const void 
                  size_t workspace_bytes, void *stream) {
     return gemm_impl(mpgemm::kU4, X, dtype, packed_codes, packed_meta, M, N, K, group,
                      symmetric, Y, workspace, workspace_bytes, kConfigSelect, stream);
+}
+
+int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
+                         const void *packed_meta, int M, int N, int K, int group,
+                         int symmetric, void *Y, void *stream) {
+    if (dtype != MPGEMM_F16 && dtype != MPGEMM_BF16) return MPGEMM_ERR_INVALID_ARG;
+    const int st = check_shape(M, N, K, group);
+    if (st != MPGEMM_OK) return st;
+    if (mpgemm_workspace_bytes(M, N, K, group, dtype) > kScratchBytes)
+        return MPGEMM_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const int sst = scratch_of_current_device(stream, &ws);
+    if (sst != MPGEMM_OK) return sst;
+    return gemm_impl(mpgemm::kU4, X, dtype, packed_codes, packed_meta, M, N, K, group,
+                     symmetric, Y, ws, kScratchBytes, kConfigSelect, stream);
 }
 
 int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
