@@ -188,8 +188,9 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * MPGEMM_ERR_UNSUPPORTED; an unknown id returns MPGEMM_ERR_INVALID_ARG).  Ids: 1..4
  * small-M kernel with 1..4 row blocks of 16 (M <= 16*id); 12 tiled large-M kernel on
  * 32x32x16 MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a
- * 256 x 128 tile.  Ids 12 and 13 take every shape.  The selector picks 1..4 for M <= 64;
- * else 13 when M >= 512 and (N >= 16384 or K >= 8192); else 12.
+ * 256 x 128 tile.  Ids 12 and 13 take every shape.  The selector picks 1..2 for M <= 32
+ * and 3..4 for M <= 64 with N < 16384; else 13 when M >= 512 and (N >= 16384 or
+ * K >= 8192); else 12.  (2- and 3-bit codes take 1..4 for every M <= 64.)
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);

@@ -51,7 +51,7 @@ def test_layout_version_and_sizes():
     assert mp.packed_code_bytes(384, 1) == 384 * 16 // 2
     assert mp.lib().mpgemm_packed_code_bytes_w8(136, 7) == 256 * 16
     assert mp.lib().mpgemm_packed_meta_bytes_w8(136, 7, 128, 1) == 2 * 16 * 2
-    assert lib.mpgemm_workspace_bytes(16, 4096, 4096, 128, 0) == 0
+    assert lib.mpgemm_workspace_bytes(1, 28672, 4096, 128, 0) == 0     # wide N: no K split
 
 
 def test_status_strings():
@@ -75,6 +75,11 @@ def test_selector_and_config_names():
     assert mp.lib().mpgemm_select_config(2048, 28672, 4096, 128, 0) == 13  # wide N
     assert mp.lib().mpgemm_select_config(2048, 4096, 14336, 128, 0) == 13  # long K
     assert mp.lib().mpgemm_select_config(256, 28672, 4096, 128, 0) == 12   # M < 512
+    assert mp.lib().mpgemm_select_config(64, 57344, 8192, 128, 1) == 12   # 17..64 rows, wide N
+    assert mp.lib().mpgemm_select_config(33, 16384, 4096, 128, 0) == 12
+    assert mp.lib().mpgemm_select_config(33, 16368, 4096, 128, 0) == 3
+    assert mp.lib().mpgemm_select_config(32, 57344, 4096, 128, 0) == 2
+    assert mp.lib().mpgemm_select_config(16, 57344, 8192, 128, 0) == 1
     for cid in (1, 2, 3, 4, 12, 13):
         assert mp.config_name(cid)
     for cid in (7, 10, 11):

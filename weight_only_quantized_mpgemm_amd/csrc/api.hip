@@ -57,15 +57,17 @@ int hip_status(hipError_t e) {
 }
 
 // Small M streams the weights once (HBM-bound): the split-K strip kernel with one to four
-// row blocks of 16.  Larger M is bound by the matrix cores: the 32x32x16 tiled kernel, with
-// the 256 x 128 tile (each dequantized weight feeds 256 rows) for long K or wide N, where
-// it measured 6-15% faster on MI355X; the 128 x 256 tile for the rest (it was 2-4% faster
-// at K = 4096, N <= 6144).
+// row blocks of 16.  Above 32 rows each strip group re-reads the activations, M / (4 S)
+// times the weight bytes; for wide N (>= 16384) the tiled kernel, which reads them once per
+// tile row, was faster there on MI355X (Llama-3-70B gate_up at M = 64: 132 us against 456),
+// for narrower N the strip kernel (QKV 98 us against 123, down 218 against 417); at 32 rows
+// the strip kernel still won on wide N (Llama-3-8B gate_up: 38 us against 53).  Larger M
+// is bound by the matrix cores: the 32x32x16 tiled kernel, with the 256 x 128 tile (each
+// dequantized weight feeds 256 rows) for long K or wide N, where it measured 6-15% faster;
+// the 128 x 256 tile for the rest (it was 2-4% faster at K = 4096, N <= 6144).
 int select_config(int M, int N, int K) {
     if (M <= 16) return kConfigDecode1;
-    if (M <= 32) return kConfigDecode2;
-    if (M <= 48) return kConfigDecode3;
-    if (M <= 64) return kConfigDecode4;
+    if (M <= 32 || (M <= 64 && N < 16384)) return (M + 15) / 16;
     return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
 }
 
@@ -113,12 +115,14 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     if (!aligned16(X) || !aligned16(packed_codes) || !aligned16(packed_meta))
         return MPGEMM_ERR_ALIGNMENT;
 
-    const int cfg = config_id == kConfigSelect ? select_config(M, N, K) : config_id;
+    // 2- and 3-bit codes reach the tiled kernels only through the 4-bit rewrite (M > 64):
+    // up to 64 rows they take the strip kernel at every N.
+    const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
+    const int cfg = config_id != kConfigSelect ? config_id
+                    : lowbit && M <= 64     ? (M + 15) / 16
+                                            : select_config(M, N, K);
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
-    // 2- and 3-bit codes: the small-M kernel, or (M > 64) a 4-bit rewrite of the codes and
-    // the tiled kernel (below).
-    const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
     const int Kp = mpgemm::padded_k(K);
 
     mpgemm::GemmArgs a;
@@ -138,7 +142,7 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     a.workspace = workspace;
     a.workspace_bytes = workspace ? workspace_bytes : 0;
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4) {
-        const size_t need = mpgemm::decode_workspace_bytes(M, N, K, cfg);
+        const size_t need = mpgemm::decode_workspace_bytes(M, N, K, group, cfg);
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
             return MPGEMM_ERR_WORKSPACE;
     }
@@ -164,7 +168,7 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
                                                             : mpgemm::launch_prefill_x32(c, s));
         }
         if (config_id != kConfigSelect) return MPGEMM_ERR_WORKSPACE;
-        const size_t need = mpgemm::decode_workspace_bytes(64, N, K, kConfigDecode4);
+        const size_t need = mpgemm::decode_workspace_bytes(64, N, K, group, kConfigDecode4);
         if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
             return MPGEMM_ERR_WORKSPACE;
         if (getenv("MPGEMM_LOG"))
@@ -293,11 +297,11 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
     if (check_shape(M, N, K, group) != MPGEMM_OK || M == 0 || N == 0 || K == 0) return 0;
     size_t need = 0;
     for (int mblocks = (M + 15) / 16; mblocks <= 4; ++mblocks) {
-        const size_t b = mpgemm::decode_workspace_bytes(M, N, K, mblocks);
+        const size_t b = mpgemm::decode_workspace_bytes(M, N, K, group, mblocks);
         if (b > need) need = b;
     }
     if (M > 64) {                   // 2- and 3-bit codes: 64-row chunks of the small-M kernel
-        const size_t b = mpgemm::decode_workspace_bytes(64, N, K, 4);
+        const size_t b = mpgemm::decode_workspace_bytes(64, N, K, group, 4);
         if (b > need) need = b;
         const size_t x = mpgemm::x32_workspace_bytes(M, N, K);   // tiled kernels' last round
         if (x > need) need = x;

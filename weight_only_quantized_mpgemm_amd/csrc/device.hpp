@@ -80,6 +80,26 @@ __device__ __forceinline__ u32x4_t dequant_word_f16(uint32_t w, uint32_t nz_hi2,
     return r;
 }
 
+// The same word's exact differences q - z as fp16 pairs, without the scale: the small-M
+// kernel multiplies whole group sums by s in fp32 instead (one multiply per output and
+// group rather than one per weight pair).  Every (q - z) is an integer of magnitude <= 15,
+// exact in fp16, and its products with fp16 activations are exact in fp32.
+__device__ __forceinline__ u32x4_t dequant_word_f16_int(uint32_t w, uint32_t nz_hi2,
+                                                        uint32_t nz_lo2) {
+    const uint32_t w8 = w >> 8;
+    u32x4_t h;
+    h[0] = and_or(w, 0x000F000Fu, 0x64006400u);
+    h[1] = and_or(w, 0x00F000F0u, 0x54005400u);
+    h[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
+    h[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
+    u32x4_t r;
+    r[0] = bitcast<uint32_t>(bitcast<half2_t>(h[0]) + bitcast<half2_t>(nz_hi2));
+    r[1] = bitcast<uint32_t>(bitcast<half2_t>(h[1]) + bitcast<half2_t>(nz_lo2));
+    r[2] = bitcast<uint32_t>(bitcast<half2_t>(h[2]) + bitcast<half2_t>(nz_hi2));
+    r[3] = bitcast<uint32_t>(bitcast<half2_t>(h[3]) + bitcast<half2_t>(nz_lo2));
+    return r;
+}
+
 // bf16 path: w = bf16_rne((q - z) * s) with s in fp16.  The nibbles are spread to bytes
 // and converted to fp32 (v_cvt_f32_ubyteN); q*s + (-z*s) is exact in fp32 (every term is
 // an integer below 16 times an 11-bit significand), and the final conversion to bf16 is
@@ -176,6 +196,21 @@ __device__ __forceinline__ u32x4_t dequant_pair_w8_f16(uint32_t w0, uint32_t w1,
     u32x4_t r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = bitcast<uint32_t>((bitcast<half2_t>(h[j]) + nz) * s);
+    return r;
+}
+// The exact differences q - z (|q - z| <= 255, exact in fp16) of a pair of 8-bit code words,
+// without the scale (see dequant_word_f16_int).
+__device__ __forceinline__ u32x4_t dequant_pair_w8_f16_int(uint32_t w0, uint32_t w1,
+                                                           uint32_t nz2) {
+    u32x4_t h;
+    h[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
+    h[1] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
+    h[2] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
+    h[3] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
+    const half2_t nz = bitcast<half2_t>(nz2);
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = bitcast<uint32_t>(bitcast<half2_t>(h[j]) + nz);
     return r;
 }
 // bf16: q * s + (-z * s) in fp32 (exact: 8-bit integer times 11-bit significand), one
@@ -420,6 +455,15 @@ __device__ __forceinline__ f32x4_t mfma16x16x32<kBF16>(const u32x4_t &a, const u
                                                        f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b),
                                                    c, 0, 0, 0);
+}
+
+// fp32 -> activation format, round to nearest even; one value.
+template <int ACT>
+__device__ __forceinline__ uint16_t round1(float v) {
+    if constexpr (ACT == kF16)
+        return bitcast<uint16_t>((_Float16)v);
+    else
+        return bitcast<uint16_t>((__bf16)v);
 }
 
 // fp32 -> activation format, round to nearest even; four values packed into 8 bytes.

@@ -62,13 +62,14 @@ struct GemmArgs {
 // every call leaves them zero.
 constexpr size_t kSplitCounterBytes = 256 * 1024;
 
-// Small-M kernel: one 16-column strip per workgroup, the K range split over the waves of the
-// workgroup, `mblocks` row blocks of 16 (M <= 16 * mblocks, mblocks in 1..4).
+// Small-M kernel: S 16-column strips per workgroup, the K range split over the waves of the
+// workgroup (and over workgroups), `mblocks` row blocks of 16 (M <= 16 * mblocks, mblocks in
+// 1..4).
 hipError_t launch_decode(const GemmArgs &a, int mblocks, hipStream_t stream);
-// Workspace bytes launch_decode needs for this shape (0 when K is not split over
-// workgroups).  The counter region must be zero before the first call; calls leave it zero.
-// N, K: the user shape.
-size_t decode_workspace_bytes(int M, int N, int K, int mblocks);
+// Workspace bytes launch_decode needs for this shape and group size, for any code format
+// (0 when K is not split over workgroups).  The counter region must be zero before the
+// first call; calls leave it zero.  N, K: the user shape.
+size_t decode_workspace_bytes(int M, int N, int K, int group, int mblocks);
 
 // Tiled large-M kernel on 32x32x16 MFMAs with a 128 (m) x 256 (n) workgroup tile.
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
