@@ -10,46 +10,55 @@ the previous call warmed.
 
 Prints one JSON line: value = whole-step TFLOP/s (2*M*N*K summed over the twelve GEMMs,
 divided by the step time), plus HBM GB/s of algorithmic bytes, the roofline of the dominant
-kernel, a per-GEMM breakdown and the CPU oracle timed on a bounded sample (cpu_baseline).
+kernel, per-config GEMM lines and the CPU oracle timed on bounded samples (cpu_baseline).
 
-The timed steps launch every GEMM from Python (--graph instead captures each M's four
-GEMMs per weight copy as a HIP graph and replays it; measured, that is no faster here,
-because a replay starts later after the preceding event than an eager launch does).
-Kernel durations come from hipEvents recorded, inside the timed steps, on the stream the
-library launches on, around each run of consecutive launches of one kernel (the four GEMMs
-of one M), divided by the launches in it; host launch gaps of a few microseconds still
-inflate the 6-20 us decode kernels there.  The per-GEMM breakdown is a separate pass after
-the timed steps: ten back-to-back launches per GEMM replayed from one HIP graph between
-one pair of events, which keeps host gaps out.  `traffic` is the HBM bytes per
-launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters read for the dominant kernel,
-scaled by what the same counters read for a plain 1 GiB copy (--copy-calibration); it is
-taken from the summary file under profiles/ and reported only while the kernel sources
-still hash to the digest recorded there, else null.
+Timing.
+  * The timed steps launch every GEMM from Python.  Kernel durations come from hipEvents
+    recorded, inside the timed steps, on the stream the library launches on, around each
+    run of consecutive launches of one kernel (the four GEMMs of one M), divided by the
+    launches in it.  `roofline` uses them for the dominant kernel; it also carries the
+    average launch duration of the same kernel in the committed rocprofv3 kernel trace
+    (profiles/w4a16_llama3_8b_m1_16_2048_kernel_trace.txt, written by --trace-summary from
+    a trace of this same command) while the kernel sources still hash to the digest it
+    records, and the fraction that figure gives.
+  * Every other GEMM time ("cold per launch") replays one HIP graph of launches that each
+    read a different copy of the weights, with at least 1.2 GB between two reads of the same
+    copy, so no launch is served by the Infinity Cache; the time per launch includes the
+    graph's launch-to-launch gap.
+  * `peaks` are measured in the run by the probes of libmpgemm_probes.so: the cold stream
+    read time of a buffer of each GEMM's byte count (the floor for any kernel that must
+    read those bytes) and the MFMA loop rate on non-zero data under the power limit.
+    Every GEMM line reports its fraction of the published peak (`frac`: 8 TB/s, 2.5 PF)
+    and of the measured one (`frac_measured`).
+  * `traffic` is the HBM bytes per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE
+    counters read for the dominant kernel, scaled by what the same counters read for a
+    plain 1 GiB copy (--copy-calibration); it is taken from the summary file under
+    profiles/ and reported only while the kernel sources still hash to the digest recorded
+    there, else null.
 
-`w4a16_small_m_per_gemm` repeats the per-GEMM pass at M = 128, 256 and 512 (grids of fewer
-tiles than compute units, where the tiled kernels split K), against the MFMA roofline.
-`w8a16_per_gemm` repeats the per-GEMM pass with 8-bit weights (mpgemm_w8a16, same shapes,
-its own rotating pool), each GEMM against the HBM roofline (M <= 64; bytes count one byte
-per code and per zero) or the fp16 MFMA roofline.  `wfp8a16_qwen3_8b_per_gemm` does the
-same with FP8 (E4M3) weights at the Qwen3-8B projection shapes (QKV 4096x6144, O 4096x4096,
-gate_up 4096x24576, down 12288x4096) and bf16 activations (mpgemm_wfp8a16; one byte per
-code, no zeros).  `w2a16_per_gemm` and `w3a16_per_gemm` do it with 2-bit and 3-bit weights
-(mpgemm_wlowbit_a16) at the Llama-3-8B shapes for M = 1 and 16, against the HBM roofline,
-and M = 2048 (the codes rewritten in the 4-bit layout, then the tiled kernel) against the
-fp16 MFMA roofline.
-`attention_kv8_decode` times mpgemm_attention_decode_kv8 (Llama-3-8B heads, one query token
-per sequence, batch x context 1 x 8192, 16 x 2048, 64 x 2048, 128 x 4096) against the HBM
-roofline (bytes: K and V codes, scales and zeros, Q, O, the block table);
-`attention_kvfp8_decode` does the same over an E4M3 cache (mpgemm_attention_decode_kvfp8;
-no zeros).  None of these is part of `value`.
+Per-config lines (`configs`): every GEMM of the workloads the metric is quoted on, timed
+cold per launch: Llama-3-8B decode (M = 1, 8, 16) and prefill (M = 512, 2048, 8192),
+Llama-3-70B with bf16 activations (M = 1, 64, 4096) and Qwen3-32B with 64-deep groups and
+symmetric codes (M = 1, 2, 4, 16, 128, 1024, 8192).  Other code formats at the Llama-3-8B
+(or, for FP8, Qwen3-8B) shapes, the small-prefill pass at M = 128..512 and decode attention
+over 8-bit and FP8 KV caches follow.  None of these is part of `value`.
+
+cpu_baseline: the CPU oracle as it stands (scalar dequantization, then an fp64 GEMM
+parallel over rows), per Llama-3-8B shape: M = 1 in full on one thread (its rows give
+nothing to parallelize), and M = 2048 on a 32-row sample over all host threads, scaled by
+2048 / 32 (rows are independent; labelled as extrapolated).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
 import dataclasses
 import hashlib
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -58,19 +67,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA
 MS = (1, 16, 2048)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_llama3_8b_m1_16_2048_hbm_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "w4a16_llama3_8b_m1_16_2048_hbm_traffic.txt")
+TRACE_FILE = os.path.join(PROFILES, "w4a16_llama3_8b_m1_16_2048_kernel_trace.txt")
+COLD_BYTES = 1.2e9              # distinct weight bytes between two reads of one copy
 
 
 def kernel_source_digest():
     """sha256 (16 hex digits) over the HIP sources and the build flags of the library's GEMM
-    path (everything but the attention kernels, which the GEMM profiles do not cover)."""
+    path (everything but the attention kernels and the probes, which the GEMM profiles do
+    not cover)."""
     pkg = os.path.join(ROOT, "weight_only_quantized_mpgemm_amd")
     csrc = os.path.join(pkg, "csrc")
     h = hashlib.sha256()
     files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
-             if f.endswith((".hip", ".hpp")) and f != "attention.hip"] + \
+             if f.endswith((".hip", ".hpp")) and f not in ("attention.hip", "probes.hip")] + \
         [os.path.join(pkg, "build.py")]
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -79,39 +92,62 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """{(kernel, M, K, N): scaled HBM bytes per launch} from the counter summary, or {} when
-    the file is absent or was taken from other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return {}
-    table, digest = {}, None
-    with open(TRAFFIC_FILE) as fh:
+def _summary_rows(path):
+    """(digest, rows) of a summary file under profiles/: rows are whitespace-split lines
+    outside comments and headers."""
+    if not os.path.exists(path):
+        return None, []
+    digest, rows = None, []
+    with open(path) as fh:
         for line in fh:
             if line.startswith("# source_digest:"):
                 digest = line.split(":", 1)[1].strip()
             elif line.strip() and not line.startswith("#"):
-                f = line.split()
-                if f[0] == "kernel":
-                    continue
-                table[(f[0], int(f[1]), int(f[2]), int(f[3]))] = float(f[6])
-    return table if digest == kernel_source_digest() else {}
+                rows.append(line.split())
+    return digest, rows
+
+
+def load_traffic():
+    """{(kernel, M, K, N): scaled HBM bytes per launch} from the counter summary, or {} when
+    the file is absent or was taken from other kernel sources."""
+    digest, rows = _summary_rows(TRAFFIC_FILE)
+    if digest != kernel_source_digest():
+        return {}
+    return {(f[0], int(f[1]), int(f[2]), int(f[3])): float(f[6]) for f in rows
+            if f[0] != "kernel" and len(f) >= 7}
+
+
+def load_trace():
+    """{kernel: average launch us over the timed steps} from the committed kernel trace
+    summary, or {} when absent or taken from other kernel sources."""
+    digest, rows = _summary_rows(TRACE_FILE)
+    if digest != kernel_source_digest():
+        return {}
+    out = {}
+    for f in rows:
+        if len(f) == 3 and f[0] != "kernel":
+            try:
+                out[f[0]] = float(f[2])
+            except ValueError:
+                pass
+    return out
 
 
 def gemm_bytes(M, K, N, g, symmetric=False):
     """Algorithmic HBM bytes of one W4A16 GEMM: packed codes, scales, zeros, X and Y."""
-    cells = (K // g) * N
+    cells = -(-K // g) * N
     return K * N // 2 + cells * 2 + (0 if symmetric else cells // 2) + M * K * 2 + M * N * 2
 
 
 def gemm_bytes_w8(M, K, N, g, symmetric=False):
     """Algorithmic HBM bytes of one W8A16 GEMM: 8-bit codes, scales, byte zeros, X and Y."""
-    cells = (K // g) * N
+    cells = -(-K // g) * N
     return K * N + cells * 2 + (0 if symmetric else cells) + M * K * 2 + M * N * 2
 
 
 def gemm_bytes_lowbit(bits, M, K, N, g, symmetric=False):
     """Algorithmic HBM bytes of one 2- or 3-bit GEMM: b-bit codes, scales, 4-bit zeros, X, Y."""
-    cells = (K // g) * N
+    cells = -(-K // g) * N
     return K * N * bits // 8 + cells * 2 + (0 if symmetric else cells // 2) + M * K * 2 + M * N * 2
 
 
@@ -123,84 +159,311 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(shapes, group, m_rows=32):
-    """The oracle, as it stands, on M = m_rows rows of every shape (full N)."""
+# ------------------------------------------------------------------ rocprofv3 summary --
+
+def trace_summary(csv_path, out_path, steps, warmup, cmd):
+    """Writes the kernel-trace summary bench.py's roofline reads: the GEMM kernels'
+    dispatches of the timed steps (12 per step, after `warmup` steps) of a rocprofv3
+    --kernel-trace run of `python3 bench.py --steps S --warmup W ...`."""
+    import weight_only_quantized_mpgemm_amd as mp
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    gemm = [r for r in rows if "decode_kernel" in r["Kernel_Name"] or
+            "prefill_x32_kernel" in r["Kernel_Name"]]
+    calls = [(M, K, N) for M in MS for K, N, _ in LLAMA_SHAPES]
+    first = warmup * len(calls)
+    timed = gemm[first:first + steps * len(calls)]
+    assert len(timed) == steps * len(calls), (len(gemm), first, steps)
+    per_kernel, per_gemm = {}, {}
+    for i, r in enumerate(timed):
+        M, K, N = calls[i % len(calls)]
+        name = mp.config_name(mp.select_config(M, N, K, 128, __import__("torch").float16))
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per_kernel.setdefault(name, []).append(d)
+        per_gemm.setdefault((name, M, K, N), []).append(d)
+    stats = {}
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        stats.setdefault(r["Kernel_Name"], []).append(d)
+    with open(out_path, "w") as fh:
+        fh.write("# rocprofv3 kernel trace of the Llama-3-8B W4A16 step (M=1,16,2048; 12 GEMMs)\n")
+        fh.write(f"# command: {cmd}\n")
+        fh.write(f"# source_digest: {kernel_source_digest()}\n")
+        fh.write(f"# timed steps only ({steps} steps after {warmup} warmup); durations = "
+                 "End-Start per dispatch\n\n")
+        fh.write("## per kernel (the figure bench.py's roofline uses: average launch duration)\n")
+        fh.write(f"{'kernel':24s} {'launches':>9s} {'avg_us':>10s}\n")
+        for k, v in sorted(per_kernel.items()):
+            fh.write(f"{k:24s} {len(v):9d} {sum(v) / len(v):10.3f}\n")
+        fh.write("\n## per GEMM (TB/s and TFLOP/s of algorithmic bytes and flops)\n")
+        fh.write("# kernel M K N n avg_us min_us TFLOP/s TB/s\n")
+        for (k, M, K, N), v in sorted(per_gemm.items(), key=lambda x: (x[0][1], x[0][2], x[0][3])):
+            a = sum(v) / len(v)
+            fh.write(f"# {k:22s} {M:5d} {K:6d} {N:6d} {len(v):4d} {a:9.2f} {min(v):8.2f} "
+                     f"{gemm_flops(M, K, N) / a / 1e6:8.1f} {gemm_bytes(M, K, N, 128) / a / 1e6:7.2f}\n")
+        fh.write("\n## rocprofv3 kernel statistics (every dispatch of the run)\n")
+        for k, v in sorted(stats.items(), key=lambda x: -sum(x[1]))[:24]:
+            fh.write(f"# {k[:70]:70s} calls={len(v):6d} avg_us={sum(v) / len(v):10.3f} "
+                     f"min_us={min(v):10.3f} max_us={max(v):10.3f}\n")
+    print(f"wrote {out_path}")
+
+
+def _pmc_dispatches(csv_path, counter):
+    """[(kernel name, value)] per dispatch, in dispatch order, of one counter in a rocprofv3
+    --pmc CSV (values summed over the rows of a dispatch)."""
+    rows = list(csv.DictReader(open(csv_path)))
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name", counter) != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        per[d] = (name, per[d][1] + val) if d in per else (name, val)
+    return [per[d] for d in sorted(per)]
+
+
+def traffic_summary(fetch_csv, write_csv, out_path, steps, warmup, cmds):
+    """Writes the HBM traffic summary bench.py's roofline reads, from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE) of `python3 bench.py --copy-calibration --steps S
+    --warmup W --no-peaks --no-configs --no-variants --no-cpu-baseline`: counter KiB per
+    dispatch of the timed steps' GEMM kernels, scaled by what the counters read for the
+    1 GiB calibration copy (the first copy-kernel dispatch)."""
+    import torch
+    import weight_only_quantized_mpgemm_amd as mp
+    calls = [(M, K, N) for M in MS for K, N, _ in LLAMA_SHAPES]
+    tables, factors = [], []
+    for path, counter, true_kib in ((fetch_csv, "FETCH_SIZE", 1 << 20),
+                                    (write_csv, "WRITE_SIZE", 1 << 20)):
+        disp = _pmc_dispatches(path, counter)
+        cal = next(v for n, v in disp if "copyBuffer" in n or "copy" in n.lower())
+        factors.append(true_kib / cal)
+        gemm = [v for n, v in disp if "decode_kernel" in n or "prefill_x32_kernel" in n]
+        first = warmup * len(calls)
+        timed = gemm[first:first + steps * len(calls)]
+        assert len(timed) == steps * len(calls), (counter, len(gemm))
+        t = {}
+        for i, v in enumerate(timed):
+            t.setdefault(calls[i % len(calls)], []).append(v)
+        tables.append({k: sum(v) / len(v) for k, v in t.items()})
+        tables[-1]["_cal"] = cal
+    with open(out_path, "w") as fh:
+        fh.write("# HBM traffic per launch of the W4A16 kernels, Llama-3-8B step (M=1,16,2048)\n")
+        fh.write(f"# command (fetch): {cmds[0]}\n# command (write): {cmds[1]}\n")
+        fh.write("# calibration: first copy-kernel dispatch = the 1 GiB device copy "
+                 "(--copy-calibration):\n")
+        fh.write(f"#   FETCH_SIZE {tables[0]['_cal']:.1f} KiB -> factor {factors[0]:.4f}; "
+                 f"WRITE_SIZE {tables[1]['_cal']:.1f} KiB -> factor {factors[1]:.4f}\n")
+        fh.write(f"# bytes = (FETCH_SIZE * fetch factor + WRITE_SIZE * write factor) * 1024, "
+                 f"averaged over the {steps} timed steps\n")
+        fh.write(f"# source_digest: {kernel_source_digest()}\n")
+        fh.write("# ratio = counted bytes / algorithmic bytes (codes + scales + zeros + X + Y)\n")
+        fh.write(f"{'kernel':24s} {'M':>6s} {'K':>6s} {'N':>6s} {'fetch_kib':>12s} "
+                 f"{'write_kib':>12s} {'bytes':>14s} {'algorithmic':>14s} {'ratio':>7s}\n")
+        for M, K, N in calls:
+            name = mp.config_name(mp.select_config(M, N, K, 128, torch.float16))
+            fk, wk = tables[0][(M, K, N)], tables[1][(M, K, N)]
+            by = (fk * factors[0] + wk * factors[1]) * 1024
+            alg = gemm_bytes(M, K, N, 128)
+            fh.write(f"{name:24s} {M:6d} {K:6d} {N:6d} {fk:12.1f} {wk:12.1f} {by:14.0f} "
+                     f"{alg:14d} {by / alg:7.3f}\n")
+    print(f"wrote {out_path}")
+
+
+# ------------------------------------------------------------------------ CPU baseline --
+
+def cpu_baseline_per_shape(gpu_us):
+    """The oracle on the Llama-3-8B shapes: M = 1 in full on one thread, M = 2048 on a
+    32-row sample over all host threads (scaled by 64, labelled extrapolated)."""
     import oracle
     import workloads
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = max(1, min(threads, os.cpu_count() or 1))
-    total_s, flops = 0.0, 0
-    for K, N, label in shapes:
-        case = workloads.make_case(workloads.LLAMA3_8B_DECODE, m_rows, K, N)
-        _, secs = oracle.timed_w4a16(case["x"], case["codes"], case["scales"], case["zeros"],
-                                     group, "f16", threads)
-        total_s += secs
-        flops += gemm_flops(m_rows, K, N)
-        log(f"cpu oracle {label} M={m_rows}: {secs:.2f} s")
-    return {"value": flops / total_s / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"M={m_rows} rows x all four Llama-3-8B shapes (full K, N), "
-                      f"dequantize + fp64 GEMM, {total_s:.1f} s"}
+    rows, total_s, total_flops = [], 0.0, 0
+    for K, N, label in LLAMA_SHAPES:
+        for M, rows_run, th in ((1, 1, 1), (2048, 32, threads)):
+            case = workloads.make_case(workloads.LLAMA3_8B_DECODE, rows_run, K, N)
+            _, secs = oracle.timed_w4a16(case["x"], case["codes"], case["scales"], case["zeros"],
+                                         128, "f16", th)
+            total_s += secs
+            total_flops += gemm_flops(rows_run, K, N)
+            t_full = secs * M / rows_run
+            g = gpu_us.get((M, K, N))
+            rows.append({"M": M, "K": K, "N": N, "layer": label, "threads": th,
+                         "rows_timed": rows_run, "seconds": round(secs, 3),
+                         "seconds_full_M": round(t_full, 3),
+                         "extrapolated": rows_run != M,
+                         "gflops": round(gemm_flops(M, K, N) / t_full / 1e9, 3),
+                         "gpu_us": g, "speedup_gpu": round(t_full / (g * 1e-6)) if g else None})
+            log(f"cpu oracle {label} M={M} ({rows_run} rows, {th} threads): {secs:.2f} s")
+    summary = {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": "Llama-3-8B qkv/o_proj/gate_up/down: M=1 in full (1 thread) and a "
+                         f"32-row sample of M=2048 ({threads} threads); dequantize + fp64 "
+                         f"GEMM; {total_s:.1f} s"}
+    return summary, rows
 
 
-def attention_pass(args, dev, stream, fp8):
-    """Times decode attention (mpgemm_attention_decode_kv8, or _kvfp8 for an FP8 format) at
-    batch x context 1 x 8192, 16 x 2048, 64 x 2048 and 128 x 4096 under a HIP graph."""
-    import torch
-    import weight_only_quantized_mpgemm_amd as mp
-    Hq, Hkv, D = 32, 8, 128
-    bb = mp.kv_block_bytes(Hkv, D)
-    # at least two block tables of the largest case (128 x 4096: 1.1 GB each)
-    nblocks = int(max(args.pool_gb, 2.5) * 1e9 // bb)
-    cache = torch.randint(0, 256, (nblocks * bb,), dtype=torch.uint8, device=dev)
-    if fp8:
-        cache &= 0xF7          # finite E4M3 and E5M2 codes (no all-ones exponent / NaN)
-    # valid fp16 scales (0.01) in every block's scale fields
-    blk = cache.view(nblocks, Hkv, bb // Hkv)
-    blk[:, :, 128 * D:128 * D + 256].view(torch.float16).fill_(0.01)
+# ------------------------------------------------------------------- cold-weight pools --
 
-    def call(q, table, lens, T, scale, o):
+LLAMA_SHAPES = ((4096, 6144, "qkv"), (4096, 4096, "o_proj"), (4096, 28672, "gate_up"),
+                (14336, 4096, "down"))
+
+
+@dataclasses.dataclass
+class Spec:
+    """One GEMM of a per-config line."""
+    M: int
+    K: int
+    N: int
+    label: str
+    g: int = 128
+    sym: bool = False
+    act: str = "f16"            # "f16" or "bf16"
+    code: str = "w4"            # "w4", "w8", "fp8", "w2", "w3"
+    scale_lo: float = 0.005
+    scale_hi: float = 0.02
+
+
+def make_pool(mp, torch, dev, spec, min_copies=3):
+    """Packed-weight copies of one shape, random codes and zeros with valid fp16 scales in
+    [scale_lo, scale_hi], enough of them that COLD_BYTES pass between two reads of a copy.
+    (Timing does not depend on the values; the codes are uniform like real ones.)"""
+    K, N, g = spec.K, spec.N, spec.g
+    lib = mp.lib()
+    if spec.code == "w4":
+        cb = lib.mpgemm_packed_code_bytes(K, N)
+        mb = lib.mpgemm_packed_meta_bytes(K, N, g, int(spec.sym))
+        bits, fp8 = 4, None
+    elif spec.code in ("w8", "fp8"):
+        cb = lib.mpgemm_packed_code_bytes_w8(K, N)
+        mb = lib.mpgemm_packed_meta_bytes_w8(K, N, g, int(spec.sym or spec.code == "fp8"))
+        bits, fp8 = 8, ("e4m3" if spec.code == "fp8" else None)
+    else:
+        b = int(spec.code[1])
+        cb = lib.mpgemm_packed_code_bytes_lowbit(b, K, N)
+        mb = lib.mpgemm_packed_meta_bytes(K, N, g, int(spec.sym))
+        bits, fp8 = b, None
+    Kp, Np = -(-K // 128) * 128, -(-N // 16) * 16     # the packed planes' padded shape
+    cells = (Kp // g) * Np
+    copies = max(min_copies, math.ceil(COLD_BYTES / (cb + mb)) + 1)
+    pool = []
+    for _ in range(copies):
+        codes = torch.randint(0, 256, (cb,), dtype=torch.uint8, device=dev)
         if fp8:
-            mp.attention_decode_kvfp8(q, cache, table, lens, Hkv, T, scale, fp8, out=o)
-        else:
-            mp.attention_decode_kv8(q, cache, table, lens, Hkv, T, scale, out=o)
+            codes &= 0xF7          # finite E4M3 codes (no all-ones exponent and mantissa)
+        meta = torch.randint(0, 256, (mb,), dtype=torch.uint8, device=dev)
+        sc = meta[:cells * 2].view(torch.float16)
+        sc.uniform_(spec.scale_lo, spec.scale_hi)
+        pool.append(mp.PackedWeights(codes, meta, K, N, g, spec.sym, bits, fp8))
+    return pool
 
-    res, reps = [], 10
-    for B, T in ((1, 8192), (16, 2048), (64, 2048), (128, 4096)):
-        nb = (T + 63) // 64
-        ntab = min(reps, nblocks // (B * nb))
-        if ntab < 2:
-            continue
-        tabs = [torch.arange(r * B * nb, (r + 1) * B * nb, dtype=torch.int32, device=dev)
-                .view(B, nb) for r in range(ntab)]
-        tables = [tabs[r % ntab] for r in range(reps)]
-        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
-        q = torch.randn(B, Hq, D, device=dev).to(torch.float16)
-        o = torch.empty_like(q)
-        scale = 1.0 / D ** 0.5
-        for r in range(reps):               # warm (and allocate the workspace)
-            call(q, tables[r], lens, T, scale, o)
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for r in range(reps):
-                call(q, tables[r], lens, T, scale, o)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        gr.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / reps
-        # codes, fp16 scales (and 8-bit zeros: none for FP8), Q and O, the block table
-        per_tok = 2 * D + 4 + (0 if fp8 else 2)
-        by = B * Hkv * T * per_tok + 2 * B * Hq * D * 2 + B * nb * 4
-        res.append({"B": B, "context": T, "heads": [Hq, Hkv, D], "us": round(t * 1e6, 2),
-                    "gbps": round(by / t / 1e9, 1), "bound": "hbm",
-                    "frac": round(by / t / 1e9 / HBM_PEAK_GBPS, 4)})
-        del gr
-    del cache, blk
-    return res
+
+def time_cold(torch, stream, launch, n):
+    """Average time (s) of one launch in a HIP graph of n launches (launch(i) for each),
+    replayed once after a warm replay."""
+    for i in range(min(n, 2)):
+        launch(i)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for i in range(n):
+            launch(i)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    gr.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del gr
+    return e0.elapsed_time(e1) * 1e-3 / n
+
+
+# -------------------------------------------------------------------------- peaks -------
+
+def measure_peaks(torch, dev, stream):
+    """Cold stream-read floors at byte counts from 4 MiB to 1 GiB, and the MFMA loop rates,
+    from libmpgemm_probes.so."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_quantized_mpgemm_amd", "libmpgemm_probes.so"))
+    lib.mpgemm_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mpgemm_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    pool_bytes = 3 << 30
+    pool = torch.randint(0, 255, (pool_bytes,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    def cur():
+        # read at call time: under graph capture torch runs on its capture stream
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    reads = []
+    for mib in (4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 512, 1024):
+        nbytes = mib << 20
+        slots = pool_bytes // nbytes
+        n = max(4, min(slots, 64))
+        best = None
+        for chunk, unroll in ((16, 4), (32, 8), (64, 8)):
+            def launch(i, nbytes=nbytes, chunk=chunk, unroll=unroll, slots=slots):
+                off = (i % slots) * nbytes
+                st = lib.mpgemm_probe_hbm_read(ctypes.c_void_p(pool.data_ptr() + off), nbytes,
+                                               chunk, unroll, ctypes.c_void_p(sink.data_ptr()),
+                                               cur())
+                assert st == 0, st
+            t = time_cold(torch, stream, launch, n)
+            if best is None or t < best[0]:
+                best = (t, chunk, unroll)
+        reads.append({"MiB": mib, "us": round(best[0] * 1e6, 2),
+                      "tbps": round(nbytes / best[0] / 1e12, 3), "chunk_kib": best[1],
+                      "unroll": best[2]})
+    del pool
+    msink = torch.zeros(512 * 256, dtype=torch.float32, device=dev)
+    names = {0: "32x32x16_f16", 1: "16x16x32_f16", 2: "32x32x16_bf16", 3: "16x16x32_bf16"}
+    mfma = {}
+    for kind in range(4):
+        iters, blocks = 4000, 512
+
+        def launch(i, kind=kind):
+            assert lib.mpgemm_probe_mfma(kind, iters, blocks, ctypes.c_void_p(msink.data_ptr()),
+                                         cur()) == 0
+        t = time_cold(torch, stream, launch, 4)
+        mfma[names[kind]] = round(blocks * 4 * iters * 4 * 32768 / t / 1e12, 1)
+    torch.cuda.empty_cache()
+    return {"hbm_read_floor": reads, "mfma_tflops": mfma,
+            "method": "cold stream reads (best of 3 probe shapes; every launch reads bytes not "
+                      "read within 1 GiB) and four independent in-place MFMA chains per wave "
+                      "on non-zero data, 2 waves per SIMD"}
+
+
+def floor_us(peaks, nbytes):
+    """Stream-read time of nbytes (linear between the measured sizes, proportional above)."""
+    pts = [(r["MiB"] * 2**20, r["us"]) for r in peaks["hbm_read_floor"]]
+    if nbytes <= pts[0][0]:
+        return pts[0][1]
+    for (a, ta), (b, tb) in zip(pts, pts[1:]):
+        if nbytes <= b:
+            return ta + (tb - ta) * (nbytes - a) / (b - a)
+    return pts[-1][1] * nbytes / pts[-1][0]
+
+
+def gemm_line(spec, t, peaks, kernel, bytes_fn=None):
+    """One GEMM's record: time, rates, and fractions of the published and measured peaks."""
+    M, K, N = spec.M, spec.K, spec.N
+    by = (bytes_fn or (lambda: gemm_bytes(M, K, N, spec.g, spec.sym)))()
+    fl = gemm_flops(M, K, N)
+    bound = "hbm" if fl / by < 315 else "mfma"
+    rec = {"M": M, "K": K, "N": N, "layer": spec.label, "kernel": kernel,
+           "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+           "gbps": round(by / t / 1e9, 1), "bound": bound}
+    if bound == "hbm":
+        rec["frac"] = round(by / t / 1e9 / HBM_PEAK_GBPS, 4)
+        if peaks:
+            rec["frac_measured"] = round(floor_us(peaks, by) * 1e-6 / t, 4)
+    else:
+        rec["frac"] = round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+        if peaks:
+            pk = max(v for k, v in peaks["mfma_tflops"].items() if k.endswith(spec.act))
+            rec["frac_measured"] = round(fl / t / 1e12 / pk, 4)
+    return rec
 
 
 def main():
@@ -209,31 +472,39 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--pool-gb", type=float, default=1.5,
-                    help="size of the rotating pool of packed weight copies")
+                    help="size of the rotating pool of packed weight copies (timed steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay the timed steps from captured HIP graphs")
-    ap.add_argument("--no-per-gemm", action="store_true",
-                    help="skip the per-GEMM breakdown pass (counter runs use this)")
-    ap.add_argument("--no-small-m", action="store_true",
-                    help="skip the W4A16 pass at M = 128, 256, 512")
-    ap.add_argument("--no-w8", action="store_true",
-                    help="skip the W8A16 per-GEMM pass (8-bit weights, same shapes)")
-    ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the FP8-weight per-GEMM pass (E4M3, Qwen3-8B shapes)")
-    ap.add_argument("--no-attention", action="store_true",
-                    help="skip the attention-decode passes (8-bit and FP8 KV caches)")
-    ap.add_argument("--no-lowbit", action="store_true",
-                    help="skip the 2-bit and 3-bit per-GEMM passes (Llama-3-8B shapes, M=1,16)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the probe measurements")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config lines (counter runs use this)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other code formats, small-M prefill and attention passes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, whose HBM "
                          "counter readings scale the counter-based traffic figures")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "OUT"),
+                    help="summarize a rocprofv3 kernel trace of this command's timed steps "
+                         "(with the same --steps/--warmup) into OUT, then exit")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "command with --copy-calibration into OUT, then exit")
+    ap.add_argument("--trace-command", default="",
+                    help="the profiled command(s), recorded in a summary ('|' between the "
+                         "fetch and write commands of --traffic-summary)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each GPU would "
               "run its own shard of N or K independently); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.trace_summary[1], args.steps, args.warmup,
+                      args.trace_command)
+        return
+    if args.traffic_summary:
+        cmds = (args.trace_command.split("|") + ["", ""])[:2]
+        traffic_summary(*args.traffic_summary, args.steps, args.warmup, [c.strip() for c in cmds])
+        return
 
     import numpy as np
     import torch
@@ -243,6 +514,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.int16, device=dev)       # 1 GiB
         dst = torch.empty_like(src)
@@ -255,7 +527,7 @@ def main():
     shapes = wl.shapes
     g = wl.group
 
-    # ---- packed weights: one seeded layer, replicated into a rotating pool ----
+    # ---- the timed step: one seeded layer, replicated into a rotating pool ----
     layer = []
     for K, N, label in shapes:
         codes, scales, zeros = workloads.weights(K, N, g, False, wl.scale_lo, wl.scale_hi,
@@ -282,7 +554,6 @@ def main():
 
     calls = [(M, K, N, label) for M in MS for K, N, label in shapes]
     cfg_of = {c: mp.select_config(c[0], c[2], c[1], g, torch.float16) for c in calls}
-    stream = torch.cuda.current_stream(dev)
     # runs of consecutive launches of one kernel at one M within a step: (kernel, [calls])
     runs, run_starts = [], set()
     for i, c in enumerate(calls):
@@ -295,27 +566,6 @@ def main():
     run_events = []
     shape_idx = {(K, N): j for j, (K, N, _) in enumerate(shapes)}
 
-    def launch_m(M, c):
-        for K, N, _ in shapes:
-            mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
-
-    # One graph per (M, weight copy): the four launches of one M are one run of one kernel.
-    use_graphs = args.graph and all(
-        sum(1 for _, rc in runs if rc[0][0] == M) == 1 for M in MS)
-    graphs = {}
-    if use_graphs:
-        for M in MS:
-            launch_m(M, 0)                     # load the library and kernels before capture
-        torch.cuda.synchronize()
-        for c in range(copies):
-            for M in MS:
-                g_ = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g_):
-                    launch_m(M, c)
-                graphs[(M, c)] = g_
-        torch.cuda.synchronize()
-        log(f"captured {len(graphs)} graphs")
-
     def step(s, record):
         evs = []
         for i, (M, K, N, label) in enumerate(calls):
@@ -323,11 +573,7 @@ def main():
             if record and i in run_starts:
                 evs.append(torch.cuda.Event(enable_timing=True))
                 evs[-1].record(stream)
-            if use_graphs:
-                if shape_idx[(K, N)] == 0:
-                    graphs[(M, c)].replay()
-            else:
-                mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
+            mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
         if record:
             evs.append(torch.cuda.Event(enable_timing=True))
             evs[-1].record(stream)
@@ -359,169 +605,119 @@ def main():
         agg["calls"] += rcalls
 
     traffic = load_traffic()
+    trace = load_trace()
 
     def roofline(cfg):
         a = per_cfg[cfg]
         avg_launch_s = a["t"] / a["n"]
         tr = [traffic.get((cfg, M, K, N)) for M, K, N, _ in a["calls"]]
         tr = round(sum(tr) / len(tr)) if tr and None not in tr else None
+        per_launch = (a["flops"] if a["bound"] == "mfma" else a["bytes"]) / a["n"]
         common = {"kernel": cfg, "launches_per_step": a["n"] // args.steps,
                   "avg_launch_us": round(avg_launch_s * 1e6, 3),
                   "algorithmic_bytes_per_launch": round(a["bytes"] / a["n"]),
                   "algorithmic_flops_per_launch": round(a["flops"] / a["n"])}
+        prof = trace.get(cfg)
         if a["bound"] == "mfma":
             ach = a["flops"] / a["t"] / 1e12
-            return {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
-                    "traffic": tr, **common}
+            out = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                   "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4),
+                   "traffic": tr, **common}
+            if prof:
+                out["avg_launch_us_profile"] = prof
+                out["frac_profile"] = round(per_launch / (prof * 1e-6) / 1e12 /
+                                            MFMA_F16_PEAK_TFLOPS, 4)
+            return out
         ach = a["bytes"] / a["t"] / 1e9
-        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": tr,
-                **common}
+        out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": tr, **common}
+        if prof:
+            out["avg_launch_us_profile"] = prof
+            out["frac_profile"] = round(per_launch / (prof * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        return out
 
-    per_call = []
-    if not args.no_per_gemm:
-        reps = 10
-        for ci, c in enumerate(calls):
-            M, K, N, label = c
-            j = shape_idx[(K, N)]
-            def launch_reps():
-                for r in range(reps):
-                    mp.w4a16(xs[(M, K)], pool[(ci * reps + r) % copies][j], out=ys[(M, N)])
-            launch_reps()                     # warm, then capture the ten launches
-            torch.cuda.synchronize()
-            g_ = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_):
-                launch_reps()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g_.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / reps
-            fl, by = gemm_flops(M, K, N), gemm_bytes(M, K, N, g)
-            bound = "hbm" if M <= 64 else "mfma"
-            frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
-                (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
-            per_call.append({"M": M, "K": K, "N": N, "layer": label,
-                             "kernel": mp.config_name(cfg_of[c]), "us": round(t * 1e6, 2),
-                             "tflops": round(fl / t / 1e12, 2), "gbps": round(by / t / 1e9, 1),
-                             "bound": bound, "frac": round(frac, 4)})
-
-    # Other code formats: a per-GEMM pass like the one above, each on its own rotating pool
-    # of packed copies; reported beside the W4A16 step, not part of `value`.
-    del pool
+    dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
+    rl = {"roofline": roofline(dominant), "roofline_by_kernel": {k: roofline(k) for k in per_cfg}}
+    log(f"step {step_s * 1e3:.3f} ms, {step_flops / step_s / 1e12:.1f} TFLOP/s")
+    del pool, layer
     torch.cuda.empty_cache()
 
-    def variant_pass(layer, shape_list, gemm, bytes_fn, act_dtype, ms=MS):
-        torch.cuda.synchronize()
-        nbytes = sum(p.nbytes for p in layer)
-        ncopies = max(3, int(np.ceil(args.pool_gb * 1e9 / nbytes)))
-        vpool = [layer] + [[dataclasses.replace(p, codes=p.codes.clone(), meta=p.meta.clone())
-                            for p in layer] for _ in range(ncopies - 1)]
-        vx = {(M, K): torch.randn(M, K, device=dev).to(act_dtype)
-              for M in ms for K, _, _ in shape_list}
-        vy = {(M, N): torch.empty(M, N, device=dev, dtype=act_dtype)
-              for M in ms for _, N, _ in shape_list}
-        torch.cuda.synchronize()
-        rows, reps = [], 10
-        for ci, (M, (K, N, label)) in enumerate((M, sh) for M in ms for sh in shape_list):
-            j = [sh[:2] for sh in shape_list].index((K, N))
-            def launch_reps():
-                for r in range(reps):
-                    gemm(vx[(M, K)], vpool[(ci * reps + r) % ncopies][j], out=vy[(M, N)])
-            launch_reps()
-            torch.cuda.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                launch_reps()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            gr.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / reps
-            fl, by = gemm_flops(M, K, N), bytes_fn(M, K, N, g)
-            bound = "hbm" if M <= 64 else "mfma"
-            frac = (by / t / 1e9 / HBM_PEAK_GBPS) if bound == "hbm" else \
-                (fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS)
-            rows.append({"M": M, "K": K, "N": N, "layer": label,
-                         "kernel": mp.config_name(mp.select_config(M, N, K, g, act_dtype)),
-                         "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
-                         "gbps": round(by / t / 1e9, 1), "bound": bound,
-                         "frac": round(frac, 4)})
-        del vpool, vx, vy
+    # ---- measured peaks ----
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(torch, dev, stream)
+        log(f"peaks: read {[(r['MiB'], r['tbps']) for r in peaks['hbm_read_floor']]} "
+            f"mfma {peaks['mfma_tflops']}")
+
+    def cold_pass(specs, gemm_fn, bytes_fn=None):
+        """Cold per-launch timing of each spec; one pool per distinct (K, N, code)."""
+        rows, cur = [], None
+        for sp in specs:
+            key = (sp.K, sp.N, sp.code, sp.g, sp.sym)
+            if cur is None or cur[0] != key:
+                cur = None
+                torch.cuda.empty_cache()
+                cur = (key, make_pool(mp, torch, dev, sp))
+            cpool = cur[1]
+            dt = torch.float16 if sp.act == "f16" else torch.bfloat16
+            x = torch.randn(sp.M, sp.K, device=dev).to(dt)
+            y = torch.empty(sp.M, sp.N, device=dev, dtype=dt)
+            n = len(cpool)
+
+            def launch(i):
+                gemm_fn(x, cpool[i % n], out=y)
+            t = time_cold(torch, stream, launch, n)
+            kern = mp.config_name(mp.select_config(sp.M, sp.N, sp.K, sp.g, dt))
+            bf = (lambda sp=sp: bytes_fn(sp)) if bytes_fn else None
+            rows.append(gemm_line(sp, t, peaks, kern, bf))
+            del x, y
+        del cur
         torch.cuda.empty_cache()
         return rows
 
-    def dev_f16(bits):
-        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.float16)
+    # ---- per-config lines: every GEMM of the workloads, cold per launch ----
+    configs = {}
+    if not args.no_configs:
+        L8 = LLAMA_SHAPES
+        L70 = workloads.LLAMA3_70B.shapes
+        Q32 = workloads.QWEN3_32B.shapes
+        sets = {
+            "llama3_8b_w4a16_g128_decode": [Spec(M, K, N, lab) for K, N, lab in L8
+                                            for M in (1, 8, 16)],
+            "llama3_8b_w4a16_g128_prefill": [Spec(M, K, N, lab) for K, N, lab in L8
+                                             for M in (512, 2048, 8192)],
+            "llama3_70b_w4a16_g128_bf16": [Spec(M, K, N, lab, act="bf16") for K, N, lab in L70
+                                           for M in (1, 64, 4096)],
+            "qwen3_32b_w4a16_g64_sym": [Spec(M, K, N, lab, g=64, sym=True, scale_lo=0.002,
+                                             scale_hi=0.01) for K, N, lab in Q32
+                                        for M in (1, 2, 4, 16, 128, 1024, 8192)],
+        }
+        for name, specs in sets.items():
+            configs[name] = cold_pass(specs, mp.w4a16)
+            log(f"{name}: " + ", ".join(f"{r['M']}x{r['K']}x{r['N']} {r['us']}us "
+                                        f"{r['frac']:.2f}" for r in configs[name]))
 
-    # W4A16 at small prefill batches (M = 128, 256, 512): grids of fewer tiles than CUs,
-    # where the tiled kernels split K.
-    small = []
-    if not args.no_small_m:
-        small = variant_pass(layer, shapes, mp.w4a16, gemm_bytes, torch.float16,
-                             ms=(128, 256, 512))
-
-    # W8A16 (8-bit weights, asymmetric) at the Llama-3-8B shapes, fp16 activations.
-    w8 = []
-    if not args.no_w8:
-        layer8 = []
-        for K, N, label in shapes:
-            codes, scales, zeros = workloads.weights_w8(K, N, g, False, wl.scale_lo, wl.scale_hi,
-                                                        workloads.seed_for("bench-w8", 0, K, N))
-            layer8.append(mp.pack_weights_w8(torch.from_numpy(codes).to(dev), dev_f16(scales),
-                                             torch.from_numpy(zeros).to(dev), g))
-        w8 = variant_pass(layer8, shapes, mp.w8a16, gemm_bytes_w8, torch.float16)
-        del layer8
-
-    # FP8 (E4M3) weights at the Qwen3-8B shapes, bf16 activations.
-    fp8 = []
-    if not args.no_fp8:
-        wl8 = workloads.QWEN3_8B_FP8
-        layerf = []
-        for K, N, label in wl8.shapes:
-            codes, scales = workloads.weights_fp8(K, N, g, "e4m3", wl8.scale_lo, wl8.scale_hi,
-                                                  workloads.seed_for("bench-fp8", 0, K, N))
-            layerf.append(mp.pack_weights_fp8(torch.from_numpy(codes).to(dev), dev_f16(scales),
-                                              g, "e4m3"))
-        fp8 = variant_pass(layerf, wl8.shapes, mp.wfp8a16,
-                           lambda M, K, N, g_: gemm_bytes_w8(M, K, N, g_, symmetric=True),
-                           torch.bfloat16)
-        del layerf
-
-    # 2-bit and 3-bit weights (asymmetric, g = 128) at the Llama-3-8B shapes, decode M only.
-    lowbit = {}
-    if not args.no_lowbit:
+    # ---- other code formats, small prefill, attention ----
+    variants = {}
+    if not args.no_variants:
+        variants["w4a16_small_m_per_gemm"] = cold_pass(
+            [Spec(M, K, N, lab) for M in (128, 256, 512) for K, N, lab in LLAMA_SHAPES], mp.w4a16)
+        variants["w8a16_per_gemm"] = cold_pass(
+            [Spec(M, K, N, lab, code="w8", scale_lo=0.005 / 16, scale_hi=0.02 / 16)
+             for K, N, lab in LLAMA_SHAPES for M in MS], mp.w8a16,
+            lambda sp: gemm_bytes_w8(sp.M, sp.K, sp.N, sp.g))
+        variants["wfp8a16_qwen3_8b_per_gemm"] = cold_pass(
+            [Spec(M, K, N, lab, sym=True, act="bf16", code="fp8", scale_lo=0.005 / 64,
+                  scale_hi=0.02 / 64) for K, N, lab in workloads.QWEN3_8B_SHAPES for M in MS],
+            mp.wfp8a16, lambda sp: gemm_bytes_w8(sp.M, sp.K, sp.N, sp.g, symmetric=True))
         for bits in (2, 3):
-            layerb = []
-            for K, N, label in shapes:
-                rng = np.random.default_rng(workloads.seed_for(f"bench-w{bits}", 0, K, N))
-                codes = rng.integers(0, 1 << bits, (K, N), dtype=np.uint8)
-                zeros = rng.integers(0, 1 << bits, (K // g, N), dtype=np.uint8)
-                scales = rng.uniform(0.01, 0.05, (K // g, N)).astype(np.float16).view(np.uint16)
-                layerb.append(mp.pack_weights_lowbit(bits, torch.from_numpy(codes).to(dev),
-                                                     dev_f16(scales),
-                                                     torch.from_numpy(zeros).to(dev), g))
-            lowbit[f"w{bits}a16_per_gemm"] = variant_pass(
-                layerb, shapes, mp.wlowbit_a16,
-                lambda M, K, N, g_, b=bits: gemm_bytes_lowbit(b, M, K, N, g_), torch.float16,
-                ms=(1, 16, 2048))
-            del layerb
+            variants[f"w{bits}a16_per_gemm"] = cold_pass(
+                [Spec(M, K, N, lab, code=f"w{bits}", scale_lo=0.01, scale_hi=0.05)
+                 for K, N, lab in LLAMA_SHAPES for M in MS], mp.wlowbit_a16,
+                lambda sp, b=bits: gemm_bytes_lowbit(b, sp.M, sp.K, sp.N, sp.g))
+        variants["attention_kv8_decode"] = attention_pass(args, dev, stream, None, torch, mp)
+        variants["attention_kvfp8_decode"] = attention_pass(args, dev, stream, "e4m3", torch, mp)
 
-    # Decode attention over the packed 8-bit and FP8 (E4M3) KV caches (Llama-3-8B heads: 32
-    # query, 8 KV, 128 wide), one query token per sequence.  Calls rotate through block
-    # tables that point into a pool of blocks larger than the Infinity Cache, so KV bytes
-    # come from HBM.
-    attn, attn_fp8 = [], []
-    if not args.no_attention:
-        attn = attention_pass(args, dev, stream, None)
-        attn_fp8 = attention_pass(args, dev, stream, "e4m3")
-
-    dominant = max(per_cfg, key=lambda k: per_cfg[k]["t"])
     out = {
         "metric": "W4A16 GEMM TFLOP/s and HBM GB/s (% roofline), Llama-3-8B shapes M=1/16/2048",
         "value": round(step_flops / step_s / 1e12, 3),
@@ -538,23 +734,65 @@ def main():
         "config": {"workload": "llama3-8b W4A16 g128 asym fp16: qkv 4096x6144, o_proj "
                                "4096x4096, gate_up 4096x28672, down 14336x4096 at "
                                "M=1,16,2048 (12 GEMMs per step)",
-                   "weight_pool_copies": copies, "group": g,
-                   "launch": "hip_graph" if use_graphs else "eager"},
+                   "weight_pool_copies": copies, "group": g, "launch": "eager"},
         "hbm_gbps": round(step_bytes / step_s / 1e9, 1),
-        "roofline": roofline(dominant),
-        "roofline_by_kernel": {k: roofline(k) for k in per_cfg},
-        "per_gemm": per_call,
-        "w4a16_small_m_per_gemm": small,
-        "w8a16_per_gemm": w8,
-        "wfp8a16_qwen3_8b_per_gemm": fp8,
-        **lowbit,
-        "attention_kv8_decode": attn,
-        "attention_kvfp8_decode": attn_fp8,
+        **rl,
+        "peaks": peaks,
+        "configs": configs,
+        **variants,
         "kernel_source_digest": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shapes, g)
+        gpu_us = {}
+        for r in configs.get("llama3_8b_w4a16_g128_decode", []) + \
+                configs.get("llama3_8b_w4a16_g128_prefill", []):
+            gpu_us[(r["M"], r["K"], r["N"])] = r["us"]
+        out["cpu_baseline"], out["cpu_baseline_per_shape"] = cpu_baseline_per_shape(gpu_us)
     print(json.dumps(out), flush=True)
+
+
+def attention_pass(args, dev, stream, fp8, torch, mp):
+    """Decode attention (mpgemm_attention_decode_kv8, or _kvfp8 for an FP8 format) at batch x
+    context 1 x 8192, 16 x 2048, 64 x 2048 and 128 x 4096, cold per launch: one HIP graph of
+    calls over block tables that each point at blocks no other call of the graph reads, at
+    least 1.2 GB of them."""
+    Hq, Hkv, D = 32, 8, 128
+    bb = mp.kv_block_bytes(Hkv, D)
+    nblocks = int(max(args.pool_gb, 2.5) * 1e9 // bb)
+    cache = torch.randint(0, 256, (nblocks * bb,), dtype=torch.uint8, device=dev)
+    if fp8:
+        cache &= 0xF7          # finite E4M3 and E5M2 codes (no all-ones exponent / NaN)
+    blk = cache.view(nblocks, Hkv, bb // Hkv)
+    blk[:, :, 128 * D:128 * D + 256].view(torch.float16).fill_(0.01)
+
+    def call(q, table, lens, T, scale, o):
+        if fp8:
+            mp.attention_decode_kvfp8(q, cache, table, lens, Hkv, T, scale, fp8, out=o)
+        else:
+            mp.attention_decode_kv8(q, cache, table, lens, Hkv, T, scale, out=o)
+
+    res = []
+    for B, T in ((1, 8192), (16, 2048), (64, 2048), (128, 4096)):
+        nb = (T + 63) // 64
+        ntab = nblocks // (B * nb)
+        if ntab < 2:
+            continue
+        reps = max(2, min(ntab, math.ceil(COLD_BYTES / (B * nb * bb)) + 1))
+        tables = [torch.arange(r * B * nb, (r + 1) * B * nb, dtype=torch.int32, device=dev)
+                  .view(B, nb) for r in range(reps)]
+        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        q = torch.randn(B, Hq, D, device=dev).to(torch.float16)
+        o = torch.empty_like(q)
+        scale = 1.0 / D ** 0.5
+        t = time_cold(torch, stream, lambda i: call(q, tables[i], lens, T, scale, o), reps)
+        per_tok = 2 * D + 4 + (0 if fp8 else 2)
+        by = B * Hkv * T * per_tok + 2 * B * Hq * D * 2 + B * nb * 4
+        res.append({"B": B, "context": T, "heads": [Hq, Hkv, D], "us": round(t * 1e6, 2),
+                    "gbps": round(by / t / 1e9, 1), "bound": "hbm",
+                    "frac": round(by / t / 1e9 / HBM_PEAK_GBPS, 4)})
+    del cache, blk
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
