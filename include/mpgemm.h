@@ -194,6 +194,27 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);
+
+/*
+ * Workgroup schedule of the tiled kernels (ids 12 and 13), computed on the host for
+ * inspection; makes no GPU call.  The pages fix no tile order: this is the library's own
+ * (tiles spread over the eight XCDs in contiguous ranges, walked four M-tiles at a time;
+ * a grid of fewer tiles than compute units splits every tile's K range into P parts,
+ * reduced by a second kernel).  It is the schedule mpgemm_w4a16_config runs when its
+ * workspace holds mpgemm_workspace_bytes() bytes on a device with `cus` compute units
+ * (0: no K split).
+ *   M, N, K, config_id  shape (K % 8 == 0) and id 12 or 13
+ *   cus       compute units (256 on MI355X)
+ *   info      out, int[8]: grid size, tile rows, tile columns, M tiles, N tiles (over the
+ *             padded N), workgroups that run a whole tile, parts per split tile (1: none),
+ *             stage-loop K
+ *   work      out, int[4 * grid] or NULL: for workgroup b in launch order, {M tile, N tile,
+ *             K part, split tile index or -1}; written only when capacity >= grid
+ * Returns the grid size (> 0), MPGEMM_ERR_INVALID_ARG for a null info, a non-positive
+ * size or another id, MPGEMM_ERR_UNSUPPORTED for shapes mpgemm_w4a16 rejects.
+ */
+int mpgemm_prefill_schedule(int M, int N, int K, int config_id, int cus, int *info, int *work,
+                            int capacity);
 int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
                         const void *packed_meta, int M, int N, int K, int group, int symmetric,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,

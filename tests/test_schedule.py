@@ -1,0 +1,99 @@
+"""Workgroup schedule of the tiled kernels (ids 12 and 13), checked on the host through
+mpgemm_prefill_schedule: every output tile is computed exactly once -- whole by one
+workgroup, or split over P workgroups that take each K part once -- for both tile shapes,
+with and without the K split of small grids.  The schedule is the same function the
+kernels call (x32_work_of), compiled for the host."""
+import random
+
+import pytest
+import torch
+
+import weight_only_quantized_mpgemm_amd as mp
+
+CONFIGS = (12, 13)
+
+
+def _padded_n(N):
+    return (N + 15) // 16 * 16
+
+
+def _check(M, N, K, cfg, cus):
+    info, work = mp.prefill_schedule(M, N, K, cfg, cus)
+    bm, bn = (128, 256) if cfg == 12 else (256, 128)
+    tm, tn = (M + bm - 1) // bm, (_padded_n(N) + bn - 1) // bn
+    assert (info["tile_m"], info["tile_n"], info["tiles_m"], info["tiles_n"]) == (bm, bn, tm, tn)
+    tiles, full, P, grid = tm * tn, info["full"], info["parts"], info["grid"]
+    loop_k = info["loop_k"]
+    assert loop_k % 256 == 0 and loop_k - 256 < (K + 127) // 128 * 128 <= loop_k
+    assert grid == full + (tiles - full) * P == work.shape[0]
+    # the split rule: only grids of fewer tiles than units, P parts of whole 256-deep
+    # blocks, at least 1024 deep each, never with a ragged K
+    if P > 1:
+        assert cus > 0 and tiles < cus and tiles * P <= cus and full == 0
+        assert loop_k % (256 * P) == 0 and loop_k // P >= 1024 and K == loop_k
+    else:
+        assert full == tiles
+    mt, nt, part, sidx = (work[:, i] for i in range(4))
+    assert bool(((mt >= 0) & (mt < tm) & (nt >= 0) & (nt < tn)).all())
+    cover = torch.zeros(tm, tn, P, dtype=torch.int64)
+    cover.index_put_((mt.long(), nt.long(), part.long()), torch.ones(grid, dtype=torch.int64),
+                     accumulate=True)
+    assert bool((cover == 1).all()), (M, N, K, cfg, cus)
+    # whole tiles: part 0, no split index; split tile s: workgroups full + s P + p, part p
+    assert bool((part[:full] == 0).all()) and bool((sidx[:full] == -1).all())
+    if P > 1:
+        b = torch.arange(full, grid)
+        assert torch.equal(sidx[full:], ((b - full) // P).int())
+        assert torch.equal(part[full:], ((b - full) % P).int())
+        # the reduction kernel finds split tile s at tile index full + s: the same tile as
+        # that of workgroup full + s of an unsplit launch
+        _, flat = mp.prefill_schedule(M, N, K, cfg, 0)
+        s = sidx[full::P].long()
+        assert torch.equal(mt[full::P], flat[full + s, 0]) and torch.equal(nt[full::P],
+                                                                          flat[full + s, 1])
+    return info
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_schedule_covers_every_tile_once_at_the_workload_shapes(cfg):
+    shapes = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096), (8192, 10240),
+              (8192, 8192), (8192, 57344), (28672, 8192), (5120, 10240), (8192, 5120),
+              (5120, 51200), (25600, 5120)]
+    for K, N in shapes:
+        for M in (65, 128, 512, 1024, 2048, 4096, 8192):
+            _check(M, N, K, cfg, 256)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_schedule_covers_every_tile_once_at_random_shapes(cfg):
+    rng = random.Random(20 + cfg)
+    splits = 0
+    for _ in range(1500):
+        M = rng.choice([rng.randint(1, 300), rng.randint(1, 5000), rng.randint(1, 20000)])
+        N = rng.choice([rng.randint(1, 4000) * 8, rng.randint(1, 700) * 16])
+        K = rng.choice([rng.randint(1, 4096) * 8, rng.randint(1, 64) * 256])
+        cus = rng.choice([256, 256, 304, 80, 0])
+        splits += _check(M, N, K, cfg, cus)["parts"] > 1
+    assert splits > 50          # the split path is exercised, not only whole tiles
+
+
+def test_split_takes_the_largest_part_count_that_fits():
+    # 8 x 8192 tiles of 128 x 256 at M = 128, N = 2048: 8 tiles on 256 units, K = 8192
+    info = _check(128, 2048, 8192, 12, 256)
+    assert (info["grid"], info["parts"]) == (64, 8)
+    # 1024-deep parts at least: K = 2048 allows 2
+    assert _check(128, 2048, 2048, 12, 256)["parts"] == 2
+    # ragged K (not a multiple of 256) never splits
+    assert _check(128, 2048, 2048 + 128, 12, 256)["parts"] == 1
+    # a grid with as many tiles as units runs whole
+    assert _check(2048, 4096 * 4, 4096, 12, 256)["parts"] == 1
+
+
+def test_schedule_rejects_bad_arguments():
+    lib = mp.lib()
+    info = torch.zeros(8, dtype=torch.int32)
+    for args in ((0, 64, 64, 12, 256), (64, 64, 64, 1, 256), (64, 64, 64, 12, -1),
+                 (64, -8, 64, 13, 256)):
+        assert lib.mpgemm_prefill_schedule(*args, info.data_ptr(), None, 0) == -1
+    assert lib.mpgemm_prefill_schedule(64, 64, 64, 12, 256, None, None, 0) == -1
+    assert lib.mpgemm_prefill_schedule(64, 64, 68, 12, 256, info.data_ptr(), None, 0) == -2

@@ -45,6 +45,7 @@ SIGNATURES = {
     "mpgemm_w4a16": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "mpgemm_select_config": (_i, [_i, _i, _i, _i, _i]),
     "mpgemm_config_name": (ctypes.c_char_p, [_i]),
+    "mpgemm_prefill_schedule": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i]),
     "mpgemm_w4a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
     "mpgemm_status_string": (ctypes.c_char_p, [_i]),
@@ -308,6 +309,20 @@ def select_config(M: int, N: int, K: int, group: int, dtype: torch.dtype) -> int
 
 def config_name(config_id: int) -> str:
     return lib().mpgemm_config_name(config_id).decode()
+
+
+def prefill_schedule(M: int, N: int, K: int, config_id: int, cus: int = 256):
+    """Host-side workgroup schedule of a tiled kernel: (info dict, work array [grid][4] of
+    M tile, N tile, K part, split tile index or -1)."""
+    info = torch.zeros(8, dtype=torch.int32)
+    grid = lib().mpgemm_prefill_schedule(M, N, K, config_id, cus, info.data_ptr(), None, 0)
+    _check(min(grid, 0), "mpgemm_prefill_schedule")
+    work = torch.zeros(grid, 4, dtype=torch.int32)
+    _check(min(0, lib().mpgemm_prefill_schedule(M, N, K, config_id, cus, info.data_ptr(),
+                                                work.data_ptr(), grid)),
+           "mpgemm_prefill_schedule")
+    keys = ("grid", "tile_m", "tile_n", "tiles_m", "tiles_n", "full", "parts", "loop_k")
+    return dict(zip(keys, info.tolist())), work
 
 
 class WorkspaceCache:

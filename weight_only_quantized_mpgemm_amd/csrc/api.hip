@@ -614,6 +614,17 @@ int mpgemm_select_config(int M, int N, int K, int group, int dtype) {
     return select_config(M < 0 ? 0 : M, N, K);
 }
 
+int mpgemm_prefill_schedule(int M, int N, int K, int config_id, int cus, int *info, int *work,
+                            int capacity) {
+    if (info == nullptr || M <= 0 || N <= 0 || K <= 0 || cus < 0 || capacity < 0)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (config_id != kConfigPrefillX32 && config_id != kConfigPrefillX32Tall)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (const int st = check_shape(M, N, K, 128)) return st;
+    return mpgemm::x32_schedule(M, N, K, config_id == kConfigPrefillX32Tall ? 1 : 2, cus, info,
+                                work, capacity);
+}
+
 const char *mpgemm_config_name(int config_id) {
     switch (config_id) {
         case kConfigDecode1: return "decode_splitk_m16";

@@ -34,6 +34,25 @@ size_t x32_workspace_bytes(int M, int N, int K) {
     return need;
 }
 
+int x32_schedule(int M, int N, int K, int nb, int cus, int *info, int *work, int capacity) {
+    const int Kp = padded_k(K), Np = padded_n(N), loop_k = x32_loop_k(Kp);
+    const int tm = (M + tile_m(nb) - 1) / tile_m(nb), tn = (Np + tile_n(nb) - 1) / tile_n(nb);
+    const int tiles = tm * tn;
+    const X32Split sp = x32_split(tiles, loop_k, K != loop_k, cus);
+    const int grid = sp.full + (tiles - sp.full) * sp.p;
+    const int head[8] = {grid, tile_m(nb), tile_n(nb), tm, tn, sp.full, sp.p, loop_k};
+    for (int i = 0; i < 8; ++i) info[i] = head[i];
+    if (work != nullptr && capacity >= grid)
+        for (int b = 0; b < grid; ++b) {
+            const X32Work w = x32_work_of(b, tm, tn, sp.full, sp.p);
+            work[4 * b] = w.mt;
+            work[4 * b + 1] = w.nt;
+            work[4 * b + 2] = w.part;
+            work[4 * b + 3] = w.split_index;
+        }
+    return grid;
+}
+
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) { return by_code(a, 2, stream); }
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream) {
     return by_code(a, 1, stream);

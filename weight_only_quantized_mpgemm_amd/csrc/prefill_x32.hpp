@@ -312,16 +312,37 @@ struct DqOpsSel<ACT, kU8> {
 // groups of four M-tiles (all four rows of one N-tile, then the next N-tile), so the
 // workgroups that run together on one XCD share four activation row-blocks and a few weight
 // column-blocks instead of touching every row-block of X.
-__device__ __forceinline__ void tile_of(int b, int tm, int tn, int &mt, int &nt) {
+__host__ __device__ inline void tile_of(int b, int tm, int tn, int &mt, int &nt) {
     constexpr int kXcds = 8, kGroupM = 4;
     const int T = tm * tn, per = T / kXcds, extra = T % kXcds;
     const int x = b % kXcds;
-    const int t = x * per + min(x, extra) + b / kXcds;
+    const int t = x * per + (x < extra ? x : extra) + b / kXcds;
     const int g = t / (kGroupM * tn);
-    const int gm = min(kGroupM, tm - g * kGroupM);
+    const int rest = tm - g * kGroupM;
+    const int gm = rest < kGroupM ? rest : kGroupM;
     const int r = t - g * kGroupM * tn;
     mt = g * kGroupM + r % gm;
     nt = r / gm;
+}
+
+// Work of workgroup b in a launch whose first `full` workgroups run whole tiles and whose
+// remaining tiles are each split into P consecutive workgroups over the K range: the tile
+// (mt, nt), the part of its K range (0 .. parts-1) and the part count.  Split tile s (in
+// launch order) is tile index full + s, the index the reduction kernel looks up.
+struct X32Work {
+    int mt, nt, part, parts, split_index;
+};
+__host__ __device__ inline X32Work x32_work_of(int b, int tm, int tn, int full, int P) {
+    X32Work w{0, 0, 0, 1, -1};
+    int t = b;
+    if (b >= full && P > 1) {
+        w.split_index = (b - full) / P;
+        w.part = (b - full) % P;
+        w.parts = P;
+        t = full + w.split_index;
+    }
+    tile_of(t, tm, tn, w.mt, w.nt);
+    return w;
 }
 
 // RAG: Kx < K; activation chunks at k >= Kx are loaded as zeros.
@@ -358,14 +379,9 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    int mt, nt, bid = blockIdx.x, sidx = 0, sp = 0;
-    const int parts = bid >= full ? P : 1;   // K-range parts of this workgroup's tile
-    if (parts > 1) {
-        sidx = (bid - full) / P;             // split tile index
-        sp = (bid - full) % P;               // which part of its K range
-        bid = full + sidx;
-    }
-    tile_of(bid, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
+    const X32Work work = x32_work_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, full, P);
+    const int mt = work.mt, nt = work.nt, sp = work.part, parts = work.parts;
+    const int sidx = work.split_index;       // split tile index (parts > 1)
     const int m_blk = mt * BM;
     const int KT = Kw >> 7;                  // 128-deep weight tiles in the packed planes
     const int S = (K >> 6) / parts;          // 64-deep stages of this part (a multiple of 4)
