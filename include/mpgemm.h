@@ -129,8 +129,9 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
  * Device workspace (bytes) mpgemm_w4a16 and mpgemm_w4a16_config use for this problem on the
  * current device: nonzero when a small-M kernel splits K over several workgroups (the
  * largest need of the configurations that can run M rows, and of 64-row chunks when
- * M > 64), or when a tiled kernel (M > 64) splits the K range of its tiles because the
- * grid has fewer tiles than the device has compute units.  The workspace holds arrival
+ * M > 64), or when a tiled kernel (M > 32) splits the K range of its tiles because the
+ * grid has fewer tiles than the device has compute units (a tiled configuration forced at
+ * M <= 32 runs unsplit).  The workspace holds arrival
  * counters in its first 256 KiB and fp32 partial sums after them.
  *   - It must be all zero before its first use; every call leaves the counters zero again,
  *     so one zeroed allocation serves any number of later calls.
@@ -188,9 +189,11 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * MPGEMM_ERR_UNSUPPORTED; an unknown id returns MPGEMM_ERR_INVALID_ARG).  Ids: 1..4
  * small-M kernel with 1..4 row blocks of 16 (M <= 16*id); 12 tiled large-M kernel on
  * 32x32x16 MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a
- * 256 x 128 tile.  Ids 12 and 13 take every shape.  The selector picks 1..2 for M <= 32
- * and 3..4 for M <= 64 with N < 16384; else 13 when M >= 512 and (N >= 16384 or
- * K >= 8192); else 12.  (2- and 3-bit codes take 1..4 for every M <= 64.)
+ * 256 x 128 tile.  Ids 12 and 13 take every shape.  The selector picks 1..2 for M <= 32,
+ * and 3..4 for M <= 48 with N K <= 4096 * 6144 or M <= 64 with N K <= 4096 * 4096; else
+ * 12 for M <= 128 (13 when K >= 5 N), for 256 < M <= 384 with K < 16384 and for
+ * M >= 2048 with N < 16384 and K < 8192; else 13.
+ * (2- and 3-bit codes take 1..4 for every M <= 64.)
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);

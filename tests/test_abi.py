@@ -62,24 +62,37 @@ def test_status_strings():
 
 
 def test_selector_and_config_names():
-    assert mp.lib().mpgemm_select_config(1, 4096, 4096, 128, 0) == 1
-    assert mp.lib().mpgemm_select_config(16, 4096, 4096, 128, 0) == 1
-    assert mp.lib().mpgemm_select_config(17, 4096, 4096, 128, 0) == 2
-    assert mp.lib().mpgemm_select_config(64, 4096, 4096, 128, 1) == 4
-    assert mp.lib().mpgemm_select_config(65, 4096, 4096, 128, 0) == 12
-    assert mp.lib().mpgemm_select_config(2048, 4096, 4096, 128, 0) == 12
-    assert mp.lib().mpgemm_select_config(2048, 4096, 4224, 128, 0) == 12   # K % 256 == 128
-    assert mp.lib().mpgemm_select_config(64, 4096, 4224, 128, 0) == 4
-    assert mp.lib().mpgemm_select_config(2048, 4096, 4104, 128, 0) == 12   # ragged K: Kp 4224
-    assert mp.lib().mpgemm_select_config(2048, 6144, 4096, 128, 0) == 12
-    assert mp.lib().mpgemm_select_config(2048, 28672, 4096, 128, 0) == 13  # wide N
-    assert mp.lib().mpgemm_select_config(2048, 4096, 14336, 128, 0) == 13  # long K
-    assert mp.lib().mpgemm_select_config(256, 28672, 4096, 128, 0) == 12   # M < 512
-    assert mp.lib().mpgemm_select_config(64, 57344, 8192, 128, 1) == 12   # 17..64 rows, wide N
-    assert mp.lib().mpgemm_select_config(33, 16384, 4096, 128, 0) == 12
-    assert mp.lib().mpgemm_select_config(33, 16368, 4096, 128, 0) == 3
-    assert mp.lib().mpgemm_select_config(32, 57344, 4096, 128, 0) == 2
-    assert mp.lib().mpgemm_select_config(16, 57344, 8192, 128, 0) == 1
+    sel = mp.lib().mpgemm_select_config
+    assert sel(1, 4096, 4096, 128, 0) == 1
+    assert sel(16, 4096, 4096, 128, 0) == 1
+    assert sel(16, 57344, 8192, 128, 0) == 1
+    assert sel(17, 4096, 4096, 128, 0) == 2
+    assert sel(32, 57344, 4096, 128, 0) == 2
+    # 33..64 rows: the strip kernel only for the smallest matrices
+    assert sel(33, 6144, 4096, 128, 0) == 3
+    assert sel(48, 6144, 4096, 128, 0) == 3
+    assert sel(49, 6144, 4096, 128, 0) == 12
+    assert sel(64, 4096, 4096, 128, 1) == 4
+    assert sel(64, 4096, 4224, 128, 0) == 12          # N K past 4096 * 4096
+    assert sel(33, 16384, 4096, 128, 0) == 12
+    assert sel(64, 57344, 8192, 128, 1) == 12
+    # 65..128 rows: one 128-row tile row, the 256-row tile when K >= 5 N
+    assert sel(65, 4096, 4096, 128, 0) == 12
+    assert sel(128, 10240, 8192, 128, 1) == 12
+    assert sel(128, 5120, 25600, 64, 0) == 13
+    assert sel(128, 4096, 14336, 128, 0) == 12
+    # larger M: the 256-row tile, except where the 128-row one pads less (257..384 rows)
+    assert sel(129, 4096, 4096, 128, 0) == 13
+    assert sel(256, 28672, 4096, 128, 0) == 13
+    assert sel(384, 6144, 4096, 128, 0) == 12
+    assert sel(384, 8192, 28672, 128, 1) == 13        # long K
+    assert sel(385, 6144, 4096, 128, 0) == 13
+    assert sel(1024, 6144, 4096, 128, 0) == 13
+    assert sel(2048, 4096, 4096, 128, 0) == 12        # M >= 2048, N < 16384, K < 8192
+    assert sel(2048, 6144, 4096, 128, 0) == 12
+    assert sel(2048, 4096, 4104, 128, 0) == 12        # ragged K
+    assert sel(2048, 4096, 14336, 128, 0) == 13       # long K
+    assert sel(8192, 28672, 4096, 128, 0) == 13       # wide N
     for cid in (1, 2, 3, 4, 12, 13):
         assert mp.config_name(cid)
     for cid in (7, 10, 11):

@@ -56,19 +56,28 @@ int hip_status(hipError_t e) {
     return MPGEMM_ERR_HIP;
 }
 
-// Small M streams the weights once (HBM-bound): the split-K strip kernel with one to four
-// row blocks of 16.  Above 32 rows each strip group re-reads the activations, M / (4 S)
-// times the weight bytes; for wide N (>= 16384) the tiled kernel, which reads them once per
-// tile row, was faster there on MI355X (Llama-3-70B gate_up at M = 64: 132 us against 456),
-// for narrower N the strip kernel (QKV 98 us against 123, down 218 against 417); at 32 rows
-// the strip kernel still won on wide N (Llama-3-8B gate_up: 38 us against 53).  Larger M
-// is bound by the matrix cores: the 32x32x16 tiled kernel, with the 256 x 128 tile (each
-// dequantized weight feeds 256 rows) for long K or wide N, where it measured 6-15% faster;
-// the 128 x 256 tile for the rest (it was 2-4% faster at K = 4096, N <= 6144).
+// Small M streams the weights once (HBM-bound): the split-K strip kernel with one or two
+// row blocks of 16.  Above 32 rows each of its strip groups re-reads an activation block
+// of M rows, M / (4 S) times the weight bytes, and the tiled kernel -- which stages
+// activations once per tile through LDS and splits the K range of small grids -- was 1.2
+// to 3.3x faster on MI355X (cold weights; Llama-3-70B bf16 QKV at M = 64: 43 us against 98,
+// gate_up 137 against 457; Qwen3-32B down 86 against 193), except on the smallest
+// matrices (Llama-3-8B O, 4096 x 4096: 19 us against 23 at M = 64; QKV at M = 33: 21 against
+// 25).  Among the tiled shapes the 128 x 256 tile wins up to 128 rows (one tile row; the
+// 256-row tile would be half padding) unless K >= 5 N, and where it pads M less than the
+// 256-row tile (257..384 rows, K < 16384); the 256 x 128 tile, whose dequantized weights
+// each feed 256 rows, everywhere else (by 0-15% from 160 to 8192 rows, on the Llama-3-8B,
+// Llama-3-70B and Qwen3-32B shapes) but for M >= 2048 at N < 16384 and K < 8192 (Llama-3-8B
+// QKV and O), where the two measured within a few percent either way from box to box.
 int select_config(int M, int N, int K) {
     if (M <= 16) return kConfigDecode1;
-    if (M <= 32 || (M <= 64 && N < 16384)) return (M + 15) / 16;
-    return M >= 512 && (N >= 16384 || K >= 8192) ? kConfigPrefillX32Tall : kConfigPrefillX32;
+    const int64_t nk = (int64_t)N * K;
+    if (M <= 32 || (M <= 48 && nk <= 4096 * 6144) || (M <= 64 && nk <= 4096 * 4096))
+        return (M + 15) / 16;
+    if (M <= 128) return K >= 5 * (int64_t)N ? kConfigPrefillX32Tall : kConfigPrefillX32;
+    if (M > 256 && M <= 384 && K < 16384) return kConfigPrefillX32;
+    if (M >= 2048 && N < 16384 && K < 8192) return kConfigPrefillX32;
+    return kConfigPrefillX32Tall;
 }
 
 // 2- and 3-bit codes at M > 64: the sub-4-bit codes are rewritten in the 4-bit layout in
@@ -303,7 +312,9 @@ size_t mpgemm_workspace_bytes(int M, int N, int K, int group, int dtype) {
     if (M > 64) {                   // 2- and 3-bit codes: 64-row chunks of the small-M kernel
         const size_t b = mpgemm::decode_workspace_bytes(64, N, K, group, 4);
         if (b > need) need = b;
-        const size_t x = mpgemm::x32_workspace_bytes(M, N, K);   // tiled kernels' last round
+    }
+    if (M > 32) {                   // the tiled kernels' K split (small grids)
+        const size_t x = mpgemm::x32_workspace_bytes(M, N, K);
         if (x > need) need = x;
     }
     return need;
