@@ -17,7 +17,7 @@ import torch
 import oracle
 import weight_only_quantized_mpgemm_amd as mp
 import workloads
-from test_gpu_parity import REL_TOL, dev_half, dev_u8, host_bits, rel_err, say
+from test_gpu_parity import REL_TOL, dev_half, dev_u8, host_bits, rel_err, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -105,7 +105,7 @@ def test_ragged_gemm_random_all_configs(code, M, K, N):
         y = gemm(code, dev_half(x, dtype), packed, cfg)
         torch.cuda.synchronize()
         assert y.shape == (M, N)
-        assert rel_err(host_bits(y), want, dtype) <= REL_TOL, cfg
+        assert rel_err(host_bits(y), want, dtype) <= tol(dtype), cfg
 
 
 @pytest.mark.parametrize("code", ["w4", "w8"])

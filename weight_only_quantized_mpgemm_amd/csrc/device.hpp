@@ -100,6 +100,20 @@ __device__ __forceinline__ u32x4_t dequant_word_f16_int(uint32_t w, uint32_t nz_
     return r;
 }
 
+// bf16 codes for the small-M kernel's scaled group sums: every nibble moved to the low
+// four bits of its 16-bit half and OR-ed into 0x4300 (bf16 128.0, whose last place is 1),
+// which gives 128 + q exactly.  Pairs in element order (e0 e1) (e2 e3) (e4 e5) (e6 e7).  The
+// caller subtracts (128 + z) times the group's activation sum from each group sum and
+// scales it by s in fp32; no per-weight subtraction or multiply remains.
+__device__ __forceinline__ u32x4_t dequant_word_bf16_biased(uint32_t w) {
+    u32x4_t h;
+    h[0] = and_or(w, 0x000F000Fu, 0x43004300u);
+    h[1] = and_or(w >> 4, 0x000F000Fu, 0x43004300u);
+    h[2] = and_or(w >> 8, 0x000F000Fu, 0x43004300u);
+    h[3] = and_or(w >> 12, 0x000F000Fu, 0x43004300u);
+    return h;
+}
+
 // bf16 path: w = bf16_rne((q - z) * s) with s in fp16.  The nibbles are spread to bytes
 // and converted to fp32 (v_cvt_f32_ubyteN); q*s + (-z*s) is exact in fp32 (every term is
 // an integer below 16 times an 11-bit significand), and the final conversion to bf16 is

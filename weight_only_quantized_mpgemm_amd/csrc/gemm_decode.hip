@@ -88,19 +88,27 @@ constexpr int decode_waves() {
 // Slots in flight per wave (128-deep steps): what the register budget of the occupancy
 // above holds beside the accumulators, the activation operands and the per-strip
 // dequantization constants (and, where group sums are scaled in fp32, the group
-// accumulators); 2 to 8 (at most 4 for four strips, 2 for four strips of 8-bit codes, 3 with
-// the activations in the slots, 2 there for 64-deep groups: more did not fit without
-// spilling).
-template <int MB, int S, bool SYM, int G, int CODE, bool XL>
+// accumulators); 2 to 8 (at most 4 for four strips, 3 for four strips with bf16 group sums,
+// 2 for four strips of 8-bit codes, 3 with the activations in the slots, 2 there for 64-deep
+// groups: more did not fit without spilling).
+// bf16 activations with 4-bit codes scale group sums in fp32 too (g = 128, one or two row
+// blocks: the per-group activation sums of more did not fit beside the pipeline).
+template <int ACT, int MB, int G, int CODE>
+constexpr bool fold_bf16() {
+    return ACT == kBF16 && CODE == kU4 && G == 128 && MB <= 2;
+}
+
+template <int ACT, int MB, int S, bool SYM, int G, int CODE, bool XL>
 constexpr int pipeline_depth() {
     constexpr int bits = kCodeBits<CODE>;
     constexpr int regs = 512 / decode_waves<MB, S, SYM, G, CODE, XL>();
     constexpr int slot = S * (bits > 4 ? 8 : 4) + (XL ? 0 : 16 * MB);
-    constexpr bool fold = CODE == kU4 || CODE == kU8;     // (with fp16 activations)
+    constexpr bool fold = CODE == kU4 || CODE == kU8;     // (8-bit: fp16 activations only)
     constexpr int fixed = 8 * S * MB + (XL ? 16 * MB : 0) + 3 * S * (kTileK / G) +
                           (bits < 4 ? 16 : 0) + (fold ? 8 * S * MB + 4 * S * (kTileK / G) : 0) +
                           64;
-    constexpr int cap = !XL ? (G == 64 ? 2 : 3) : (S == 4 ? (bits > 4 ? 2 : 4) : 8);
+    constexpr int cap = !XL ? (G == 64 ? 2 : 3)
+                            : (S == 4 ? (bits > 4 ? 2 : fold_bf16<ACT, MB, G, CODE>() ? 3 : 4) : 8);
     constexpr int d = (regs - fixed) / slot;
     return d > cap ? cap : (d < 2 ? 2 : d);
 }
@@ -126,8 +134,12 @@ __attribute__((amdgpu_waves_per_eu(decode_waves<MB, S, SYM, G, CODE, XL>()))) vo
     constexpr bool kNibbleZeros = BITS <= 4;           // zeros stored as 4-bit values
     constexpr int zrow = kNibbleZeros ? 8 : 16;        // zero bytes per (strip, group)
     // fp16 activations with 4- or 8-bit integer codes: the MFMAs take the exact q - z and
-    // each group's sum is scaled in fp32 (see dequant_word_f16_int).
-    constexpr bool kFold = ACT == kF16 && (CODE == kU4 || CODE == kU8);
+    // each group's sum is scaled in fp32 (see dequant_word_f16_int).  bf16 activations with
+    // 4-bit codes: the MFMAs take the exact 128 + q, and each group's sum less (128 + z)
+    // times the group's activation sum (one more MFMA per step against a block of ones,
+    // shared by the strips) is scaled in fp32 (see dequant_word_bf16_biased).
+    constexpr bool kFoldB = fold_bf16<ACT, MB, G, CODE>();
+    constexpr bool kFold = (ACT == kF16 && (CODE == kU4 || CODE == kU8)) || kFoldB;
     typedef Slot<MB, S, WV, XL> SlotT;
     extern __shared__ __align__(16) uint8_t lds[];
 
@@ -287,7 +299,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves<MB, S, SYM, G, CODE, XL>()))) vo
             }
         typedef DqFor<ACT, CODE> DqB;
         typename DqB::type dq[S][GPT];
-        float sf[S][GPT];
+        float sf[S][GPT], zf[S][GPT];
 #pragma unroll
         for (int si = 0; si < S; ++si)
 #pragma unroll
@@ -303,12 +315,28 @@ __attribute__((amdgpu_waves_per_eu(decode_waves<MB, S, SYM, G, CODE, XL>()))) vo
                     else
                         zv = lds[zb + (lane & 15)];
                 }
-                dq[si][h] = DqB::make(sv, zv);
+                if constexpr (!kFoldB) dq[si][h] = DqB::make(sv, zv);
                 sf[si][h] = (float)bitcast<_Float16>(sv);
+                zf[si][h] = -(128.0f + (float)zv);
             }
         if constexpr (kFold) {
-            // Per strip and group: the MFMAs sum x * (q - z) exactly-multiplied into a fresh
-            // accumulator, which is then added to the output scaled by the group's s.
+            // Per strip and group: the MFMAs sum x * (q - z) (bf16: x * (128 + q)), products
+            // exact, into a fresh accumulator, which is then added to the output scaled by
+            // the group's s (bf16: after adding -(128 + z) times the group's activation sums,
+            // which take the same output layout from MFMAs against ones).
+            f32x4_t xs[kFoldB ? GPT : 1][MB];
+            if constexpr (kFoldB) {
+                const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+                for (int h = 0; h < GPT; ++h)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        xs[h][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = h * (4 / GPT); j < (h + 1) * (4 / GPT); ++j)
+                            xs[h][mb] = mfma16x16x32<ACT>(xv[j][mb], ones, xs[h][mb]);
+                    }
+            }
 #pragma unroll
             for (int si = 0; si < S; ++si)
 #pragma unroll
@@ -319,7 +347,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves<MB, S, SYM, G, CODE, XL>()))) vo
 #pragma unroll
                     for (int j = h * (4 / GPT); j < (h + 1) * (4 / GPT); ++j) {
                         u32x4_t b;
-                        if constexpr (BITS == 4)
+                        if constexpr (kFoldB)
+                            b = dequant_word_bf16_biased(sl.w[si][0][j]);
+                        else if constexpr (BITS == 4)
                             b = dequant_word_f16_int(sl.w[si][0][j], dq[si][h].nz_hi2,
                                                      dq[si][h].nz_lo2);
                         else
@@ -333,8 +363,11 @@ __attribute__((amdgpu_waves_per_eu(decode_waves<MB, S, SYM, G, CODE, XL>()))) vo
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[si][mb][r] = __builtin_fmaf(sf[si][h], ag[mb][r], acc[si][mb][r]);
+                        for (int r = 0; r < 4; ++r) {
+                            float g = ag[mb][r];
+                            if constexpr (kFoldB) g = __builtin_fmaf(zf[si][h], xs[h][mb][r], g);
+                            acc[si][mb][r] = __builtin_fmaf(sf[si][h], g, acc[si][mb][r]);
+                        }
                 }
         } else if constexpr (BITS < 4) {
             // Sub-4-bit codes: the four steps' operands of one strip at a time.
@@ -607,7 +640,7 @@ size_t split_workspace(const Split &sp, int strips, int mblocks) {
 
 template <int ACT, int MB, int S, bool SYM, int G, int CODE, bool XL>
 void launch_s(const GemmArgs &a, const Split &sp, hipStream_t stream) {
-    constexpr int D = pipeline_depth<MB, S, SYM, G, CODE, XL>();
+    constexpr int D = pipeline_depth<ACT, MB, S, SYM, G, CODE, XL>();
     const int strips = a.Np >> 4;
     const int wgs = (strips + S - 1) / S;
     const int KT = a.Kp >> 7;
