@@ -393,13 +393,15 @@ __device__ __forceinline__ uint32_t low_pair(const u32x4_t &w, int &base) {
 template <int ACT, int BITS>
 struct DqLow {
     typedef DqLowConst<BITS> type;
+    // -(B_b + z) in fp16 is the sign bit, B_b's pattern and z in units of B_b's last place
+    // (2^(-BITS b) for base b): z < 2^BITS shifted by BITS b stays below 2^10, inside the
+    // mantissa, so the pattern is exact and built with integer operations.
     static __device__ __forceinline__ type make(uint16_t s, uint32_t z) {
         type d;
+        const uint32_t zz = z * 0x00010001u;
 #pragma unroll
-        for (int b = 0; b < LowBases<BITS>::kCount; ++b) {
-            const uint32_t h = bitcast<uint16_t>((_Float16)(-(LowBases<BITS>::kValue[b] + (float)z)));
-            d.nz[b] = h | (h << 16);
-        }
+        for (int b = 0; b < LowBases<BITS>::kCount; ++b)
+            d.nz[b] = (zz << (BITS * b)) + (LowBases<BITS>::kPattern[b] | 0x80008000u);
         d.s2 = (uint32_t)s | ((uint32_t)s << 16);
         d.s = (float)bitcast<_Float16>(s);
         return d;
@@ -418,6 +420,21 @@ struct DqLow {
                  } else {
                      a[R / 4][R % 4] = pack_bf16x2((float)q.x * c.s, (float)q.y * c.s);
                  }
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, 16>{});
+    }
+    // fp16 only: the exact differences q - z as fp16 pairs, without the scale (the small-M
+    // kernel scales whole group sums in fp32, as for 4-bit codes).
+    static __device__ __forceinline__ void tile_int(const u32x4_t &w,
+                                                    const type *const (&d)[4],
+                                                    u32x4_t (&a)[4]) {
+        [&]<int... R>(std::integer_sequence<int, R...>) {
+            (([&] {
+                 int b;
+                 const uint32_t h = low_pair<BITS, R>(w, b);
+                 a[R / 4][R % 4] = bitcast<uint32_t>(bitcast<half2_t>(h) +
+                                                     bitcast<half2_t>(d[R / 4]->nz[b]));
              }()),
              ...);
         }(std::make_integer_sequence<int, 16>{});

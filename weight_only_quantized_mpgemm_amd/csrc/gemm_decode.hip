@@ -88,9 +88,9 @@ constexpr int decode_waves() {
 // Slots in flight per wave (128-deep steps): what the register budget of the occupancy
 // above holds beside the accumulators, the activation operands and the per-strip
 // dequantization constants (and, where group sums are scaled in fp32, the group
-// accumulators); 2 to 8 (at most 4 for four strips, 3 for four strips with bf16 group sums,
-// 2 for four strips of 8-bit codes, 3 with the activations in the slots, 2 there for 64-deep
-// groups: more did not fit without spilling).
+// accumulators); 2 to 8 (at most 4 for four strips, 3 for four strips with bf16 group sums
+// or with sub-4-bit codes in 64-deep groups, 2 for four strips of 8-bit codes, 3 with the
+// activations in the slots, 2 there for 64-deep groups: more did not fit without spilling).
 // bf16 activations with 4-bit codes scale group sums in fp32 too (g = 128, one or two row
 // blocks: the per-group activation sums of more did not fit beside the pipeline).
 template <int ACT, int MB, int G, int CODE>
@@ -108,7 +108,11 @@ constexpr int pipeline_depth() {
                           (bits < 4 ? 16 : 0) + (fold ? 8 * S * MB + 4 * S * (kTileK / G) : 0) +
                           64;
     constexpr int cap = !XL ? (G == 64 ? 2 : 3)
-                            : (S == 4 ? (bits > 4 ? 2 : fold_bf16<ACT, MB, G, CODE>() ? 3 : 4) : 8);
+                            : (S == 4 ? (bits > 4 ? 2
+                                         : fold_bf16<ACT, MB, G, CODE>() || (bits < 4 && G == 64)
+                                             ? 3
+                                             : 4)
+                                      : 8);
     constexpr int d = (regs - fixed) / slot;
     return d > cap ? cap : (d < 2 ? 2 : d);
 }
@@ -370,18 +374,40 @@ __attribute__((amdgpu_waves_per_eu(decode_waves<MB, S, SYM, G, CODE, XL>()))) vo
                         }
                 }
         } else if constexpr (BITS < 4) {
-            // Sub-4-bit codes: the four steps' operands of one strip at a time.
+            // Sub-4-bit codes: the four steps' operands of one strip at a time.  fp16: the
+            // exact q - z, each group's sum scaled by its s in fp32 as above.
 #pragma unroll
             for (int si = 0; si < S; ++si) {
                 u32x4_t at[4];
                 const typename DqB::type *d[4] = {&dq[si][0], &dq[si][32 / G], &dq[si][64 / G],
                                                   &dq[si][96 / G]};
-                DqB::tile(sl.w[si][0], d, at);
+                if constexpr (ACT == kF16) {
+                    DqB::tile_int(sl.w[si][0], d, at);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                    for (int h = 0; h < GPT; ++h) {
+                        f32x4_t ag[MB];
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        acc[si][mb] = mfma16x16x32<ACT>(xv[j][mb], at[j], acc[si][mb]);
+                        for (int mb = 0; mb < MB; ++mb) ag[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = h * (4 / GPT); j < (h + 1) * (4 / GPT); ++j)
+#pragma unroll
+                            for (int mb = 0; mb < MB; ++mb)
+                                ag[mb] = mfma16x16x32<ACT>(xv[j][mb], at[j], ag[mb]);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[si][mb][r] =
+                                    __builtin_fmaf(sf[si][h], ag[mb][r], acc[si][mb][r]);
+                    }
+                } else {
+                    DqB::tile(sl.w[si][0], d, at);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[si][mb] = mfma16x16x32<ACT>(xv[j][mb], at[j], acc[si][mb]);
+                }
             }
         } else {
 #pragma unroll
