@@ -324,6 +324,104 @@ class Spec:
     scale_hi: float = 0.02
 
 
+# Counter runs: the Llama-3-8B decode GEMMs (M = 1 and 16) and prefill GEMMs (M = 2048), each
+# launched once as a warm-up (left out of the summary) and then COUNTER_REPS times over
+# rotating cold weight copies, one shape after another, so the dispatch order names the shape.
+COUNTER_SHAPES = [(M, K, N) for M in (1, 16, 2048) for K, N, _ in LLAMA_SHAPES]
+COUNTER_REPS = 4
+COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_WAIT_INST_ANY",
+            "SQ_VALU_MFMA_BUSY_CYCLES", "FETCH_SIZE", "GRBM_GUI_ACTIVE")
+
+
+def counters_workload(lib_path):
+    """The launches a counter run profiles (see COUNTER_SHAPES), after the 1 GiB calibration
+    copy.  lib_path: another build of libmpgemm.so (e.g. of an earlier commit) to profile
+    instead of the in-tree one; exports it lacks are left out of the binding."""
+    import torch
+    import weight_only_quantized_mpgemm_amd as mp
+    if lib_path:
+        mp.LIB_PATH = os.path.abspath(lib_path)
+        have = ctypes.CDLL(mp.LIB_PATH)
+        for name in [n for n in mp.SIGNATURES if not hasattr(have, n)]:
+            mp.SIGNATURES.pop(name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.ones(1 << 29, dtype=torch.int16, device=dev)       # 1 GiB calibration copy
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    pools = {}
+    for M, K, N in COUNTER_SHAPES:
+        if (K, N) not in pools:
+            pools[(K, N)] = make_pool(mp, torch, dev, Spec(M=1, K=K, N=N, label="counters"))
+        pool = pools[(K, N)]
+        x = torch.randn(M, K, device=dev).half()
+        y = torch.empty(M, N, device=dev, dtype=torch.float16)
+        for i in range(1 + COUNTER_REPS):
+            mp.w4a16(x, pool[i % len(pool)], out=y)
+            torch.cuda.synchronize()
+        log(f"counters: M={M} K={K} N={N} x {COUNTER_REPS}")
+
+
+def _pmc_table(csv_path):
+    """{dispatch id: (kernel name, start ns, end ns, {counter: value summed over rows})}."""
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = int(r["Dispatch_Id"])
+        name, cnt = r["Kernel_Name"], r["Counter_Name"]
+        if d not in out:
+            out[d] = (name, int(r["Start_Timestamp"]), int(r["End_Timestamp"]), {})
+        c = out[d][3]
+        c[cnt] = c.get(cnt, 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def counters_summary(runs, out_path):
+    """Per-shape counter table of one or more `--counters` runs: runs = [(label, csv, cmd)]."""
+    lines = ["# rocprofv3 counters of the W4A16 GEMM kernels, Llama-3-8B shapes (fp16, g = 128,",
+             "# asymmetric), cold weights; averages over the timed launches of each shape",
+             "# dur: End - Start of the dispatch under counter collection (short kernels run slower",
+             "# than in a graph replay); clock = GRBM_GUI_ACTIVE / 8 XCDs / dur, shown from 50 us on",
+             "# (the counter also runs outside the dispatch, which dominates short ones); MFMA busy =",
+             "# SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 * 1024 SIMDs); VALU = SQ_INSTS_VALU",
+             "# in millions; wait/wave = SQ_WAIT_INST_ANY * 4 cycles / SQ_WAVES;",
+             "# VALU/wave = SQ_INSTS_VALU / SQ_WAVES; fetch = FETCH_SIZE KiB scaled by the 1 GiB copy's",
+             "# reading, against the algorithmic bytes (codes + scales + zeros + X + Y)",
+             f"# source_digest (current sources): {kernel_source_digest()}"]
+    for label, path, cmd in runs:
+        table = _pmc_table(path)
+        ids = sorted(table)
+        cal = next(d for d in ids if "copy" in table[d][0].lower())
+        factor = (1 << 20) / table[cal][3]["FETCH_SIZE"]
+        gemm = [d for d in ids if "decode_kernel" in table[d][0] or "prefill_x32_kernel" in table[d][0]]
+        per = 1 + COUNTER_REPS
+        assert len(gemm) == per * len(COUNTER_SHAPES), (label, len(gemm))
+        lines += ["", f"## {label}", f"# command: {cmd}", f"# FETCH_SIZE calibration factor {factor:.4f}",
+                  "# kernel                  M      K      N   dur_us  clk_GHz  mfma_busy  waves"
+                  "   VALU/wave  VALU_M  wait_cyc/wave  fetch_MB  fetch/alg"]
+        for i, (M, K, N) in enumerate(COUNTER_SHAPES):
+            ds = gemm[i * per + 1:(i + 1) * per]
+            avg = {c: sum(table[d][3].get(c, 0.0) for d in ds) / len(ds) for c in COUNTERS}
+            dur = sum(table[d][2] - table[d][1] for d in ds) / len(ds)          # ns
+            gui = avg["GRBM_GUI_ACTIVE"] / 8
+            clk = gui / dur
+            mfma = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024) if gui else 0.0
+            waves = avg["SQ_WAVES"]
+            fetch = avg["FETCH_SIZE"] * factor * 1024
+            alg = gemm_bytes(M, K, N, 128)
+            kname = "prefill_x32" if "prefill" in table[ds[0]][0] else "decode"
+            clk_s = f"{clk:8.3f}" if dur >= 50e3 else f"{'-':>8s}"
+            lines.append(f"  {kname:20s} {M:5d} {K:6d} {N:6d} {dur / 1e3:8.2f} {clk_s} "
+                         f"{mfma:10.3f} {waves:6.0f} {avg['SQ_INSTS_VALU'] / waves:11.1f} "
+                         f"{avg['SQ_INSTS_VALU'] / 1e6:7.3f} "
+                         f"{avg['SQ_WAIT_INST_ANY'] * 4 / waves:14.0f} {fetch / 1e6:9.2f} "
+                         f"{fetch / alg:9.3f}")
+    open(out_path, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {out_path}")
+
+
 def make_pool(mp, torch, dev, spec, min_copies=3):
     """Packed-weight copies of one shape, random codes and zeros with valid fp16 scales in
     [scale_lo, scale_hi], enough of them that COLD_BYTES pass between two reads of a copy.
@@ -488,6 +586,15 @@ def main():
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "command with --copy-calibration into OUT, then exit")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the counter workload (the Llama-3-8B GEMMs at M = 1, 16 and "
+                         "2048, cold) for a rocprofv3 --pmc run, then exit")
+    ap.add_argument("--lib", default="",
+                    help="with --counters: profile this build of libmpgemm.so instead")
+    ap.add_argument("--counters-summary", nargs="+", metavar="LABEL=CSV",
+                    help="summarize --counters runs (LABEL=CSV, one per run; --trace-command "
+                         "gives their commands separated by '|') into the last argument, "
+                         "then exit")
     ap.add_argument("--trace-command", default="",
                     help="the profiled command(s), recorded in a summary ('|' between the "
                          "fetch and write commands of --traffic-summary)")
@@ -504,6 +611,15 @@ def main():
     if args.traffic_summary:
         cmds = (args.trace_command.split("|") + ["", ""])[:2]
         traffic_summary(*args.traffic_summary, args.steps, args.warmup, [c.strip() for c in cmds])
+        return
+    if args.counters_summary:
+        *pairs, out = args.counters_summary
+        cmds = [c.strip() for c in args.trace_command.split("|")] + [""] * len(pairs)
+        counters_summary([(p.split("=", 1)[0], p.split("=", 1)[1], cmds[i])
+                          for i, p in enumerate(pairs)], out)
+        return
+    if args.counters:
+        counters_workload(args.lib)
         return
 
     import numpy as np
