@@ -272,20 +272,23 @@ def traffic_summary(fetch_csv, write_csv, out_path, steps, warmup, cmds):
 # ------------------------------------------------------------------------ CPU baseline --
 
 def cpu_baseline_per_shape(gpu_us):
-    """The oracle on the Llama-3-8B shapes: M = 1 in full on one thread, M = 2048 on a
-    32-row sample over all host threads (scaled by 64, labelled extrapolated)."""
+    """The oracle on the Llama-3-8B shapes: M = 1 in full on one thread (the oracle runs
+    rows in parallel, so one row takes one thread whatever the host has), M = 2048 on a
+    32-row sample over all host threads and on a 2-row sample on one thread (each scaled to
+    2048 rows and labelled extrapolated)."""
     import oracle
     import workloads
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = max(1, min(threads, os.cpu_count() or 1))
     rows, total_s, total_flops = [], 0.0, 0
     for K, N, label in LLAMA_SHAPES:
-        for M, rows_run, th in ((1, 1, 1), (2048, 32, threads)):
+        for M, rows_run, th in ((1, 1, 1), (2048, 32, threads), (2048, 2, 1)):
             case = workloads.make_case(workloads.LLAMA3_8B_DECODE, rows_run, K, N)
             _, secs = oracle.timed_w4a16(case["x"], case["codes"], case["scales"], case["zeros"],
                                          128, "f16", th)
-            total_s += secs
-            total_flops += gemm_flops(rows_run, K, N)
+            if not (th == 1 and rows_run < M):      # the 1-thread sample: reported only
+                total_s += secs
+                total_flops += gemm_flops(rows_run, K, N)
             t_full = secs * M / rows_run
             g = gpu_us.get((M, K, N))
             rows.append({"M": M, "K": K, "N": N, "layer": label, "threads": th,
