@@ -69,18 +69,20 @@ def test_selector_and_config_names():
     assert sel(17, 4096, 4096, 128, 0) == 2
     assert sel(32, 57344, 4096, 128, 0) == 2
     # 33..64 rows: the strip kernel only for the smallest matrices
-    assert sel(33, 6144, 4096, 128, 0) == 3
-    assert sel(48, 6144, 4096, 128, 0) == 3
-    assert sel(49, 6144, 4096, 128, 0) == 12
+    assert sel(33, 4096, 4096, 128, 0) == 3
+    assert sel(48, 4096, 4096, 128, 0) == 3
+    assert sel(33, 6144, 4096, 128, 0) == 13          # 192 workgroups against 96
     assert sel(64, 4096, 4096, 128, 1) == 4
-    assert sel(64, 4096, 4224, 128, 0) == 12          # N K past 4096 * 4096
-    assert sel(33, 16384, 4096, 128, 0) == 12
-    assert sel(64, 57344, 8192, 128, 1) == 12
-    # 65..128 rows: one 128-row tile row, the 256-row tile when K >= 5 N
-    assert sel(65, 4096, 4096, 128, 0) == 12
-    assert sel(128, 10240, 8192, 128, 1) == 12
-    assert sel(128, 5120, 25600, 64, 0) == 13
-    assert sel(128, 4096, 14336, 128, 0) == 12
+    assert sel(64, 4096, 4224, 128, 0) == 13          # N K past 4096 * 4096; 32 tiles, 16
+    assert sel(33, 16384, 4096, 128, 0) == 13         # both fill all 256 units
+    assert sel(64, 57344, 8192, 128, 1) == 12         # 448 tiles of 256 x 128: two rounds
+    # 33..128 rows: the tile whose grid (K split on 256 units) fills more units
+    assert sel(65, 4096, 4096, 128, 0) == 13          # 128 workgroups against 64
+    assert sel(96, 28672, 4096, 128, 0) == 13         # 224 each, only 256 x 128 unsplit
+    assert sel(128, 10240, 8192, 128, 1) == 12        # 160 each
+    assert sel(128, 8192, 8192, 128, 1) == 13         # 256 each: every unit filled
+    assert sel(128, 5120, 25600, 64, 0) == 13         # 160 against 80
+    assert sel(128, 4096, 14336, 128, 0) == 13        # 256 against 128
     # larger M: the 256-row tile, except where the 128-row one pads less (257..384 rows)
     assert sel(129, 4096, 4096, 128, 0) == 13
     assert sel(256, 28672, 4096, 128, 0) == 13

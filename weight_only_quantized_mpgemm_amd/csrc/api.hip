@@ -58,23 +58,38 @@ int hip_status(hipError_t e) {
 
 // Small M streams the weights once (HBM-bound): the split-K strip kernel with one or two
 // row blocks of 16.  Above 32 rows each of its strip groups re-reads an activation block
-// of M rows, M / (4 S) times the weight bytes, and the tiled kernel -- which stages
-// activations once per tile through LDS and splits the K range of small grids -- was 1.2
+// of M rows, M / (4 S) times the weight bytes, and the tiled kernels -- which stage
+// activations once per tile through LDS and split the K range of small grids -- were 1.2
 // to 3.3x faster on MI355X (cold weights; Llama-3-70B bf16 QKV at M = 64: 43 us against 98,
 // gate_up 137 against 457; Qwen3-32B down 86 against 193), except on the smallest
-// matrices (Llama-3-8B O, 4096 x 4096: 19 us against 23 at M = 64; QKV at M = 33: 21 against
-// 25).  Among the tiled shapes the 128 x 256 tile wins up to 128 rows (one tile row; the
-// 256-row tile would be half padding) unless K >= 5 N, and where it pads M less than the
-// 256-row tile (257..384 rows, K < 16384); the 256 x 128 tile, whose dequantized weights
-// each feed 256 rows, everywhere else (by 0-15% from 160 to 8192 rows, on the Llama-3-8B,
-// Llama-3-70B and Qwen3-32B shapes) but for M >= 2048 at N < 16384 and K < 8192 (Llama-3-8B
-// QKV and O), where the two measured within a few percent either way from box to box.
+// matrices (Llama-3-8B O, 4096 x 4096: 19 us against 23 at M = 64).  Up to 128 rows both
+// tiles run one tile row (their MFMAs skip the row blocks past M), and the one whose grid,
+// with its K split, fills more compute units wins: Llama-3-8B shapes went to the
+// 256 x 128 tile (QKV M = 64: 192 workgroups against 96, 19.4 us against 20.5; gate_up,
+// unsplit against split in two, 31.4 against 36.4), and so did grids that both fill every
+// unit (Llama-3-70B O: 28.0 against 29.3); the Llama-3-70B and Qwen3-32B QKV and gate_up
+// went to the 128 x 256 one (equal partial fill, or a 256 x 128 grid of more than one round:
+// 70B gate_up 115 against 125 us).  Above 128 rows the 256 x 128 tile, whose
+// dequantized weights each feed 256 rows (0-15% faster from 160 to 8192 rows on all three
+// workloads), except for 257..384 rows with K < 16384 (the 128-row tile pads less) and
+// M >= 2048 at N < 16384, K < 8192 (Llama-3-8B QKV and O), where the two measured within a
+// few percent either way from box to box.
+int pick_tile(int M, int N, int K) {
+    int p12 = 1, p13 = 1, cus = 256;
+    const int g12 = mpgemm::x32_grid(M, N, K, 2, &p12, &cus);
+    const int g13 = mpgemm::x32_grid(M, N, K, 1, &p13, nullptr);
+    if (g13 > cus && g12 <= cus) return kConfigPrefillX32;
+    const int f12 = g12 < cus ? g12 : cus, f13 = g13 < cus ? g13 : cus;
+    if (f13 > f12) return kConfigPrefillX32Tall;
+    if (f13 == f12 && (f13 == cus || (p13 == 1 && p12 > 1))) return kConfigPrefillX32Tall;
+    return kConfigPrefillX32;
+}
+
 int select_config(int M, int N, int K) {
     if (M <= 16) return kConfigDecode1;
     const int64_t nk = (int64_t)N * K;
-    if (M <= 32 || (M <= 48 && nk <= 4096 * 6144) || (M <= 64 && nk <= 4096 * 4096))
-        return (M + 15) / 16;
-    if (M <= 128) return K >= 5 * (int64_t)N ? kConfigPrefillX32Tall : kConfigPrefillX32;
+    if (M <= 32 || (M <= 64 && nk <= 4096 * 4096)) return (M + 15) / 16;
+    if (M <= 128) return pick_tile(M, N, K);
     if (M > 256 && M <= 384 && K < 16384) return kConfigPrefillX32;
     if (M >= 2048 && N < 16384 && K < 8192) return kConfigPrefillX32;
     return kConfigPrefillX32Tall;

@@ -34,6 +34,17 @@ size_t x32_workspace_bytes(int M, int N, int K) {
     return need;
 }
 
+int x32_grid(int M, int N, int K, int nb, int *parts, int *cus) {
+    const int Kp = padded_k(K), Np = padded_n(N), loop_k = x32_loop_k(Kp);
+    const int tiles = ((M + tile_m(nb) - 1) / tile_m(nb)) * ((Np + tile_n(nb) - 1) / tile_n(nb));
+    const int dev_cus = device_cus();
+    const int c = dev_cus > 0 ? dev_cus : 256;
+    const X32Split sp = x32_split(tiles, loop_k, K != loop_k, c);
+    if (parts) *parts = sp.p;
+    if (cus) *cus = c;
+    return sp.full + (tiles - sp.full) * sp.p;
+}
+
 int x32_schedule(int M, int N, int K, int nb, int cus, int *info, int *work, int capacity) {
     const int Kp = padded_k(K), Np = padded_n(N), loop_k = x32_loop_k(Kp);
     const int tm = (M + tile_m(nb) - 1) / tile_m(nb), tn = (Np + tile_n(nb) - 1) / tile_n(nb);

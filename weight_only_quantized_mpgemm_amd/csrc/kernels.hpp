@@ -90,6 +90,10 @@ hipError_t launch_repack_lowbit_u4(int bits, bool symmetric, const void *packed_
 // their tiles (grids of fewer tiles than compute units); 0 when they never do for this
 // shape.  N, K: user shape.
 size_t x32_workspace_bytes(int M, int N, int K);
+// Workgroups of a 32x32x16 launch with nb column blocks per wave, with the K split it takes
+// on the current device (256 compute units when none is current); *parts: its part count,
+// *cus: the compute units assumed (either pointer may be NULL).
+int x32_grid(int M, int N, int K, int nb, int *parts, int *cus);
 // Workgroup schedule of a 32x32x16 launch with nb column blocks per wave (host only):
 // info[8] and work[4 grid] as mpgemm_prefill_schedule documents; returns the grid size.
 int x32_schedule(int M, int N, int K, int nb, int cus, int *info, int *work, int capacity);

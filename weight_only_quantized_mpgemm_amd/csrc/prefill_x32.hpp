@@ -345,8 +345,11 @@ __host__ __device__ inline X32Work x32_work_of(int b, int tm, int tn, int full, 
     return w;
 }
 
-// RAG: Kx < K; activation chunks at k >= Kx are loaded as zeros.
-template <int ACT, bool SYM, int G, int NWS, int NB, int CODE, bool RAG>
+// RAG: Kx < K; activation chunks at k >= Kx are loaded as zeros.  MA: row blocks of 32 that
+// hold rows below M (MA < 8 / NB when M <= 32 MA): the MFMAs and activation operand reads
+// of the others are skipped (their accumulators stay zero and are never stored); loads and
+// DMAs are unchanged (rows past M read as zeros).
+template <int ACT, bool SYM, int G, int NWS, int NB, int CODE, bool RAG, int MA>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MA; ++mb)
                 b[u][mb] = xs[decltype(buf)::value][mb * 256 + brow + ((4 * s + 2 * u) ^ cb)];
     };
     // The A operand of 32-deep step `word` of column block nb, k half u (compiler-scheduled
@@ -557,10 +560,11 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         [&]<int... I>(std::integer_sequence<int, I...>) {
             (([&] {
                  constexpr int u = I / 8, nb = (I / MB) % NB, mb = I % MB;
-                 mfma32<ACT>(acc[nb][mb], a[u][nb], b[u][mb]);
+                 if constexpr (mb < MA) mfma32<ACT>(acc[nb][mb], a[u][nb], b[u][mb]);
                  if constexpr (I % kReadEvery == 0) {
                      constexpr int r = I / kReadEvery, ru = r / MB, rmb = r % MB;
-                     bn[ru][rmb] = xs[decltype(bufn)::value][rmb * 256 + brow + ((4 * s_n + 2 * ru) ^ cb)];
+                     if constexpr (rmb < MA)
+                         bn[ru][rmb] = xs[decltype(bufn)::value][rmb * 256 + brow + ((4 * s_n + 2 * ru) ^ cb)];
                  }
                  constexpr int total = 2 * NB * Ops::kCount;
                  run_ops(IC<(total * I) / 16>(), IC<(total * (I + 1)) / 16>(), wn, dn, word_n, tmp, an);
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) asm volatile("" ::"v"(a[u][nb]));
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) asm volatile("" ::"v"(b[u][mb]));
+            for (int mb = 0; mb < MA; ++mb) asm volatile("" ::"v"(b[u][mb]));
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -690,7 +694,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MA; ++mb)          // rows past M: never read back
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     dst[((nb * MB + mb) * 4 + q) * kXThreads + tid] =
@@ -848,9 +852,22 @@ void launch_one(const GemmArgs &a, hipStream_t stream) {
                                                        kSplitCounterBytes)
                            : nullptr;
     const dim3 grid((unsigned)(sp.full + (tiles - sp.full) * sp.p));
-    prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG>
-        <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
-                                               loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p, part);
+    constexpr int MB = 8 / NB;
+    if (NB == 1 && a.M <= 8 * MB)            // one 256-row tile row, three quarters empty
+        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, MB / 4>
+            <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
+                                                   loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
+                                                   part);
+    else if (a.M <= 16 * MB)                 // one tile row, its lower half empty
+        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, MB / 2>
+            <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
+                                                   loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
+                                                   part);
+    else
+        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, MB>
+            <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
+                                                   loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
+                                                   part);
     if (sp.p > 1)
         x32_split_reduce_kernel<ACT, NB><<<dim3((unsigned)(tiles - sp.full) * 8), dim3(kXThreads),
                                            0, stream>>>(reinterpret_cast<const f32x4_t *>(part),
