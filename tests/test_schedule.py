@@ -85,6 +85,10 @@ def test_split_takes_the_largest_part_count_that_fits():
     assert _check(128, 2048, 2048, 12, 256)["parts"] == 2
     # ragged K (not a multiple of 256) never splits
     assert _check(128, 2048, 2048 + 128, 12, 256)["parts"] == 1
+    # any part count to 8 that cuts K into whole 256-deep blocks: K = 5120 (20 blocks) at
+    # 40 tiles takes five parts (200 workgroups), K = 25600 (100 blocks) at 40 tiles five
+    assert _check(128, 10240, 5120, 12, 256)["parts"] == 5
+    assert _check(128, 5120, 25600, 13, 256)["parts"] == 5
     # a grid with as many tiles as units runs whole
     assert _check(2048, 4096 * 4, 4096, 12, 256)["parts"] == 1
 

@@ -605,10 +605,12 @@ bool split_fits(const Split &sp, int M, int KT, int mblocks, int group) {
 // Measured on MI355X (kernel trace, cold weights, the Llama-3-8B, Llama-3-70B and Qwen3-32B
 // projection shapes): with activations in LDS one strip per workgroup and no K split over
 // workgroups was best or within 5% everywhere, with eight waves where the strips alone
-// give fewer than 2048 waves and four otherwise; with per-wave activation fragments two
-// strips and eight waves for narrow matrices, four strips and four waves for wide ones
-// (five waves, the K / 8 rule at K = 5120, was 1.5x slower), and long K split over about
-// 256 workgroups.
+// give fewer than 2048 waves and four otherwise; with per-wave activation fragments one
+// strip and eight waves up to 256 strips (Llama-3-8B O at M = 16: 7.6 us against 8.4 with
+// two strips, for 2-, 3- and 4-bit codes alike), two strips and eight waves for other
+// narrow matrices, four strips and four waves for wide ones (five waves, the K / 8 rule at
+// K = 5120, was 1.5x slower), and long K split over about 256 workgroups, with eight waves
+// up to 8 rows (Llama-3-8B down at M = 8: 12.0 us against 14.4 with four) and four above.
 Split pick_split(int M, int strips, int KT, int mblocks, int group) {
     Split sp{1, 1, 1};
     if (split_xl(M, mblocks)) {
@@ -622,7 +624,10 @@ Split pick_split(int M, int strips, int KT, int mblocks, int group) {
             const int groups = (strips + sp.s - 1) / sp.s;
             sp.p = (256 + groups - 1) / groups;
             if (sp.p > 8) sp.p = 8;
-            sp.nw = 4;
+            sp.nw = M > 8 ? 4 : 8;
+        } else if (strips <= 256) {
+            sp.s = 1;
+            sp.nw = 8;
         } else {
             sp.s = 2;
             sp.nw = 8;

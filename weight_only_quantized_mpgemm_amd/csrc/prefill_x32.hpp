@@ -808,11 +808,11 @@ inline int device_cus() {
 
 // Fewer tiles than compute units.  One workgroup fills a compute unit (its registers take
 // the whole SIMD), so T < CUs tiles leave CUs - T units idle.  Splitting each tile's K
-// range P ways (T P <= CUs) runs the tiles in about 1/P of the time, for one fp32 partial
-// of the tile per part, written to the workspace (past its counter region, which the
-// small-M kernels use) and added up by a second, small kernel.  Parts keep at least 1024
-// of K (the pipeline's prologue and epilogue stay small against the loop) and whole
-// 256-deep blocks of the stage loop.  A partial last round of a larger grid is left alone:
+// range P ways (T P <= CUs, P <= 8) runs the tiles in about 1/P of the time, for one fp32
+// partial of the tile per part, written to the workspace (past its counter region, which
+// the small-M kernels use) and added up by a second, small kernel.  Parts keep at least
+// 1024 of K (the pipeline's prologue and epilogue stay small against the loop) and whole
+// 256-deep blocks of the stage loop (so K = 5120, twenty blocks, splits five ways).  A partial last round of a larger grid is left alone:
 // under the chip's power limit the busy units of such a round run at a higher clock, and
 // splitting it (measured at 2048 x 4096 x 6144: 384 tiles) saved less than the partials
 // cost.  MPGEMM_X32_SPLIT=0 turns the split off.
@@ -826,7 +826,7 @@ inline X32Split x32_split(int tiles, int loop_k, bool rag, int cus) {
         if (env[0] == '0') return sp;
     if (tiles >= cus) return sp;
     const int r = tiles;
-    for (int p = 8; p >= 2; p /= 2)
+    for (int p = 8; p >= 2; --p)
         if (r * p <= cus && loop_k % (256 * p) == 0 && loop_k / p >= 1024) {
             sp.full = tiles - r;
             sp.p = p;
