@@ -602,19 +602,32 @@ bool split_fits(const Split &sp, int M, int KT, int mblocks, int group) {
            xchunks <= kFillLoads * lanes && mchunks <= kMetaLoads * lanes;
 }
 
-// Measured on MI355X (kernel trace, cold weights, the Llama-3-8B, Llama-3-70B and Qwen3-32B
-// projection shapes): with activations in LDS one strip per workgroup and no K split over
-// workgroups was best or within 5% everywhere, with eight waves where the strips alone
-// give fewer than 2048 waves and four otherwise; with per-wave activation fragments one
-// strip and eight waves up to 256 strips (Llama-3-8B O at M = 16: 7.6 us against 8.4 with
-// two strips, for 2-, 3- and 4-bit codes alike), two strips and eight waves for other
-// narrow matrices, four strips and four waves for wide ones (five waves, the K / 8 rule at
-// K = 5120, was 1.5x slower), and long K split over about 256 workgroups, with eight waves
-// up to 8 rows (Llama-3-8B down at M = 8: 12.0 us against 14.4 with four) and four above.
+// Measured on MI355X (cold weights, the Llama-3-8B, Llama-3-70B and Qwen3-32B projection
+// shapes; sweeps over S, NW and P):
+//   - activations in LDS, one row: one strip per workgroup and no K split over workgroups
+//     was best or within 5% everywhere, with eight waves where the strips alone give fewer
+//     than 2048 waves and four otherwise;
+//   - activations in LDS, three or four rows and at least 16384 strip tiles: two strips and
+//     four waves (at M = 4: Qwen3-32B gate_up 38.0 us against 45.3, down 24.3 against 29.2;
+//     Llama-3-70B gate_up 64.8 against 76.3); on smaller matrices and at two rows that
+//     halved the waves of too few workgroups (Llama-3-8B O at M = 4: 8.3 us against 6.1);
+//   - per-wave activation fragments: one strip and eight waves up to 256 strips
+//     (Llama-3-8B O at M = 16: 7.6 us against 8.4 with two strips, for 2-, 3- and 4-bit
+//     codes alike), two strips and eight waves up to 512, four strips and eight waves below
+//     1024 (Qwen3-32B and Llama-3-70B QKV, 640 strips, at M = 16: 13.2 and 18.0 us against
+//     16.1 and 23.8), four strips and four waves for wider matrices (five waves, the K / 8
+//     rule at K = 5120, was 1.5x slower); long K split over about 256 workgroups, with eight
+//     waves up to 8 rows (Llama-3-8B down at M = 8: 12.0 us against 14.4 with four) and four
+//     above.
 Split pick_split(int M, int strips, int KT, int mblocks, int group) {
     Split sp{1, 1, 1};
     if (split_xl(M, mblocks)) {
-        sp.nw = strips * 4 < 2048 ? 8 : 4;
+        if (M >= 3 && (int64_t)strips * KT >= 16384) {
+            sp.s = 2;
+            sp.nw = 4;
+        } else {
+            sp.nw = strips * 4 < 2048 ? 8 : 4;
+        }
     } else if (mblocks == 1) {
         if (strips >= 1024) {
             sp.s = 4;
@@ -627,6 +640,9 @@ Split pick_split(int M, int strips, int KT, int mblocks, int group) {
             sp.nw = M > 8 ? 4 : 8;
         } else if (strips <= 256) {
             sp.s = 1;
+            sp.nw = 8;
+        } else if (strips > 512) {
+            sp.s = 4;
             sp.nw = 8;
         } else {
             sp.s = 2;
