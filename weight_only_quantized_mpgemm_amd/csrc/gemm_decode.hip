@@ -617,7 +617,8 @@ bool split_fits(const Split &sp, int M, int KT, int mblocks, int group) {
 //     1024 (Qwen3-32B and Llama-3-70B QKV, 640 strips, at M = 16: 13.2 and 18.0 us against
 //     16.1 and 23.8), four strips and four waves for wider matrices (five waves, the K / 8
 //     rule at K = 5120, was 1.5x slower); long K split over about 256 workgroups, with eight
-//     waves up to 8 rows (Llama-3-8B down at M = 8: 12.0 us against 14.4 with four) and four
+//     waves up to 8 rows (Llama-3-8B down at M = 8: 12.0 us against 14.4 with four; four
+//     strips from 512 strips, Llama-3-70B down at M = 8: 28.6 against 32.8 with two) and four
 //     above.
 Split pick_split(int M, int strips, int KT, int mblocks, int group) {
     Split sp{1, 1, 1};
@@ -633,7 +634,7 @@ Split pick_split(int M, int strips, int KT, int mblocks, int group) {
             sp.s = 4;
             sp.nw = 4;
         } else if (KT > 64) {
-            sp.s = M > 8 ? 4 : 2;
+            sp.s = M > 8 || strips >= 512 ? 4 : 2;
             const int groups = (strips + sp.s - 1) / sp.s;
             sp.p = (256 + groups - 1) / groups;
             if (sp.p > 8) sp.p = 8;

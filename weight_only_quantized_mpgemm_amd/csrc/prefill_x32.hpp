@@ -852,22 +852,23 @@ void launch_one(const GemmArgs &a, hipStream_t stream) {
                                                        kSplitCounterBytes)
                            : nullptr;
     const dim3 grid((unsigned)(sp.full + (tiles - sp.full) * sp.p));
+    // Row blocks that can hold rows below M: one tile row of a 256-row tile needs a quarter
+    // of them up to 64 rows, half up to 128; one of a 128-row tile half up to 64.
     constexpr int MB = 8 / NB;
-    if (NB == 1 && a.M <= 8 * MB)            // one 256-row tile row, three quarters empty
-        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, MB / 4>
+    auto run = [&](auto MA) __attribute__((always_inline)) {
+        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, decltype(MA)::value>
             <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
                                                    loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
                                                    part);
-    else if (a.M <= 16 * MB)                 // one tile row, its lower half empty
-        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, MB / 2>
-            <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
-                                                   loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
-                                                   part);
-    else
-        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, MB>
-            <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
-                                                   loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
-                                                   part);
+    };
+    if constexpr (NB == 1) {
+        if (a.M <= 8 * MB) run(IC<MB / 4>());
+        else if (a.M <= 16 * MB) run(IC<MB / 2>());
+        else run(IC<MB>());
+    } else {
+        if (a.M <= 16 * MB) run(IC<MB / 2>());
+        else run(IC<MB>());
+    }
     if (sp.p > 1)
         x32_split_reduce_kernel<ACT, NB><<<dim3((unsigned)(tiles - sp.full) * 8), dim3(kXThreads),
                                            0, stream>>>(reinterpret_cast<const f32x4_t *>(part),
