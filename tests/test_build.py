@@ -99,3 +99,46 @@ def test_ring_wait_check_walks_loop_and_tail_paths():
     assert build.ring_wait_violations(_kernel_asm(2)) == []
     bad = build.ring_wait_violations(_kernel_asm(5))     # tail waits leave too much in flight
     assert {path for _, path, _ in bad} == {"loop and tail", "tail only"}
+
+
+VALU_ASM = """\
+    .text
+_Z7kernelAPf:                           ; @_Z7kernelAPf
+; %bb.0:
+	v_and_or_b32 v5, v1, s2, v3
+	s_nop 0
+	v_mfma_f32_16x16x32_bf16 v[10:13], v[4:7], v[0:3], 0
+	s_endpgm
+.Lfunc_end0:
+_Z7kernelBPf:                           ; @_Z7kernelBPf
+; %bb.0:
+	v_and_or_b32 v5, v1, s2, v3
+	s_nop 1
+	v_mfma_f32_16x16x32_bf16 v[10:13], v[4:7], v[0:3], 0
+	v_readfirstlane_b32 s0, v9
+	v_mfma_f32_16x16x32_bf16 v[10:13], v[4:7], v[8:11], 0
+	v_mov_b32 v20, v1
+	v_mov_b32 v20, v2
+	s_nop 1
+	v_mfma_f32_16x16x32_bf16 v[10:13], v[20:23], v[0:3], 0
+	s_endpgm
+.Lfunc_end1:
+_Z7kernelCPf:                           ; @_Z7kernelCPf
+; %bb.0:
+	v_accvgpr_write_b32 a2, v1
+	s_cbranch_scc1 .LBB2_2
+	s_nop 7
+.LBB2_2:
+	v_mfma_f32_16x16x32_bf16 a[0:3], v[0:3], v[4:7], a[0:3]
+	s_endpgm
+.Lfunc_end2:
+"""
+
+
+def test_valu_mfma_hazards_flags_reads_within_two_wait_states_on_any_path():
+    # A: one wait state between the write of v5 and the MFMA reading v[4:7]; B: two, an SGPR
+    # write, and a write overwritten before any MFMA reads it; C: the taken branch reaches
+    # the MFMA reading a2 after one wait state (the branch), the fall-through after nine
+    assert build.valu_mfma_hazards(VALU_ASM) == [
+        ("_Z7kernelAPf", "v_and_or_b32 v5, v1, s2, v3", 1),
+        ("_Z7kernelCPf", "v_accvgpr_write_b32 a2, v1", 1)]

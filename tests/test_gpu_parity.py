@@ -311,7 +311,7 @@ def test_llama3_8b_prefill_m8192(K, N, label):
     _full_shape(workloads.LLAMA3_8B_PREFILL, 8192, K, N, configs=TILED)
 
 
-@pytest.mark.parametrize("M", [1, 64])
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 24, 64])
 @pytest.mark.parametrize("K,N,label", workloads.LLAMA3_70B.shapes)
 def test_llama3_70b_bf16_small_m(M, K, N, label):
     _full_shape(workloads.LLAMA3_70B, M, K, N)

@@ -14,7 +14,8 @@ import torch
 import oracle
 import weight_only_quantized_mpgemm_amd as mp
 import workloads
-from test_gpu_parity import REL_TOL, dev_half, host_bits, pack_case, rel_err, run, say
+from test_gpu_parity import (REL_TOL, dev_half, dev_u8, host_bits, pack_case, rel_err, run, say,
+                             tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +131,48 @@ def test_split_k_on_two_streams_at_once():
         assert np.array_equal(host_bits(yb), want_b)
     ref = oracle.w4a16(b["x"], b["codes"], b["scales"], b["zeros"], b["group"], threads=8)
     assert rel_err(want_b, ref, "f16") <= REL_TOL
+
+
+# Every plan shape, K split over workgroups or not, in both activation formats: each (S, NW)
+# is a kernel of its own, with its own pipeline depth and instruction schedule, and bf16
+# activations take another operand path (128 + q, less (128 + z) times the group's
+# activation sums) than fp16.  Plans that do not fit the row blocks fall back to the
+# selector's own, which is then tested once more.  M = 1 and 3 take the activations through
+# LDS; 13 and 24 (one and two row blocks) per wave.
+PLANS = ["1,1,1", "1,4,1", "1,8,1", "2,1,1", "2,4,1", "2,8,1", "4,2,1", "4,4,1", "4,8,1",
+         "2,4,3", "4,4,2"]
+
+
+@pytest.mark.parametrize("plan", PLANS)
+@pytest.mark.parametrize("M", [1, 3, 13, 24])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_every_plan_matches_oracle(monkeypatch, plan, M, dtype):
+    monkeypatch.setenv("MPGEMM_DECODE_SPLIT", plan)
+    K, N = 2048, 1056
+    wl = workloads.LLAMA3_8B_DECODE if dtype == "f16" else workloads.LLAMA3_70B
+    say(f"plan {plan} {dtype} M={M} K={K} N={N}")
+    case = workloads.make_case(wl, M, K, N, seed=300 + M)
+    packed = pack_case(case)
+    ref = oracle.w4a16(case["x"], case["codes"], case["scales"], case["zeros"], case["group"],
+                       dtype)
+    assert rel_err(run(case, packed, (M + 15) // 16), ref, dtype) <= tol(dtype)
+
+
+@pytest.mark.parametrize("plan", ["1,4,1", "2,4,1", "2,1,1", "4,4,1", "4,2,2"])
+@pytest.mark.parametrize("M", [1, 3, 13])
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_every_plan_lowbit_matches_oracle(monkeypatch, plan, M, bits, dtype):
+    monkeypatch.setenv("MPGEMM_DECODE_SPLIT", plan)
+    K, N, g = 2048, 1056, 64
+    say(f"plan {plan} w{bits} {dtype} M={M} K={K} N={N}")
+    rng = np.random.default_rng(400 + 10 * M + bits)
+    codes = rng.integers(0, 1 << bits, (K, N), dtype=np.uint8)
+    zeros = rng.integers(0, 1 << bits, (K // g, N), dtype=np.uint8)
+    scales = rng.uniform(0.005, 0.05, (K // g, N)).astype(np.float16).view(np.uint16)
+    x = workloads.activations(M, K, dtype, 500 + M)
+    packed = mp.pack_weights_lowbit(bits, dev_u8(codes), dev_half(scales), dev_u8(zeros), g)
+    want = oracle.wlowbit_a16(bits, x, codes, scales, zeros, g, dtype, threads=8)
+    y = mp.wlowbit_a16(dev_half(x, dtype), packed, config=1)
+    torch.cuda.synchronize()
+    assert rel_err(host_bits(y), want, dtype) <= REL_TOL

@@ -181,6 +181,73 @@ def ring_wait_violations(asm: str) -> list[tuple[str, str, list]]:
     return out
 
 
+# A vector ALU write of a register that an MFMA then reads (as A, B or C) needs two wait
+# states in between.  The compiler inserts them for instructions it emits itself, but it does
+# not know what an inline asm statement writes; the build checks every kernel instead.
+MIN_VALU_TO_MFMA_WAIT = 2
+
+
+def _regs(tok: str) -> set[tuple[str, int]]:
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.fullmatch(r"([va])(\d+)", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def _operands(line: str) -> list[str]:
+    parts = line.split(None, 1)
+    return [t.strip() for t in parts[1].split(",")] if len(parts) > 1 else []
+
+
+def valu_mfma_hazards(asm: str, min_wait: int = MIN_VALU_TO_MFMA_WAIT) -> list[tuple]:
+    """(kernel, VALU instruction, distance) for every vector ALU write of a VGPR or AGPR
+    that some MFMA reads fewer than `min_wait` wait states later, along every branch path;
+    distance = instructions in between plus s_nop wait states."""
+    out = []
+    for name in re.findall(r"\n([A-Za-z_][\w.$]*):[^\n]*\n", asm):
+        if "kernel" not in name:
+            continue
+        lines = _path_lines(asm, name)
+        lab = {ln[:-1]: i for i, ln in enumerate(lines) if re.match(r"\.LBB\w+:$", ln)}
+        for k, ln in enumerate(lines):
+            if not ln.startswith("v_") or ln.startswith(("v_mfma", "v_smfmac")):
+                continue
+            ops = _operands(ln)
+            dst = _regs(ops[0]) if ops else set()
+            if not dst:
+                continue
+            stack = [(k + 1, 0)]
+            while stack:
+                j, states = stack.pop()
+                while j < len(lines) and states < min_wait:
+                    ln2 = lines[j]
+                    if ln2.endswith(":"):
+                        j += 1
+                        continue
+                    if ln2.startswith(("v_mfma", "v_smfmac")):
+                        if dst & set().union(*map(_regs, _operands(ln2)[1:])):
+                            out.append((name, ln, states))
+                            break
+                    if ln2.startswith("s_nop"):
+                        states += int(ln2.split()[1], 0) + 1
+                        j += 1
+                        continue
+                    if ln2.startswith("s_endpgm"):
+                        break
+                    if ln2.startswith("s_branch"):
+                        j, states = lab[ln2.split()[1]] + 1, states + 1
+                        continue
+                    if ln2.startswith("s_cbranch"):
+                        stack.append((lab[ln2.split()[1]] + 1, states + 1))
+                    if ops and ln2.startswith("v_") and dst & _regs(_operands(ln2)[0]) and \
+                            not ln2.startswith(("v_mfma", "v_smfmac")):
+                        break                                     # overwritten first
+                    states += 1
+                    j += 1
+    return out
+
+
 def _check_asm_mfma(src: str, extra: list[str]) -> None:
     asm_path = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".s")
     cmd = [HIPCC, *FLAGS, *extra, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
@@ -189,6 +256,12 @@ def _check_asm_mfma(src: str, extra: list[str]) -> None:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{res.stderr}")
     asm = open(asm_path).read()
+    bad = valu_mfma_hazards(asm)
+    if bad:
+        raise RuntimeError(f"{src}: MFMA operands read too soon after a vector ALU write "
+                           f"(wait states): {len(bad)} cases, first {bad[:3]}")
+    if src not in ASM_MFMA_SOURCES:
+        return
     bad = acc_read_hazards(asm)
     if bad:
         raise RuntimeError(f"{src}: MFMA results read too early (wait states): {bad}")
@@ -227,7 +300,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     extra = list(extra or [])
     srcs = SOURCES + PROBE_SOURCES
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs) + 2) as ex:
-        checks = [ex.submit(_check_asm_mfma, s, extra) for s in ASM_MFMA_SOURCES]
+        checks = [ex.submit(_check_asm_mfma, s, extra) for s in srcs]
         objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra), srcs)))
         for c in checks:
             c.result()

@@ -51,13 +51,23 @@ __device__ __forceinline__ To bitcast(const From &v) {
 // reads it as 64 + q exactly, so it needs no shift.  One 8-bit shift exposes (e4, e5) and
 // (e6, e7) the same way: four isolate-and-combine operations and one shift per 8 weights.
 
-// v_and_or_b32 with the mask in a scalar and the OR pattern in a vector register: VOP3 on
-// gfx9 takes no literal and reads at most one scalar register, and the compiler otherwise
-// splits this into two literal-carrying VOP2 operations.
+// (v & mask) | bits as one v_and_or_b32, with the mask in a scalar and the OR pattern in a
+// vector register: VOP3 on gfx9 takes no literal and reads at most one scalar register, and
+// given the constants themselves the compiler splits the operation into two
+// literal-carrying VOP2s.  The empty statements only pin each constant to a register class;
+// the operation stays the compiler's own, so its hazard checks see a vector ALU write (an
+// MFMA must not read the result in the next two wait states, which the compiler cannot
+// know of an instruction written as inline asm).
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t v) {
+    asm("" : "+s"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
 __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bits) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(bits));
-    return r;
+    return (v & in_sgpr(mask)) | in_vgpr(bits);
 }
 
 // fp16 path: w = fp16_rne((q - z) * s).  (B + q) + (-(B + z)) is exact (an integer of
