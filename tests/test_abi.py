@@ -91,11 +91,17 @@ def test_selector_and_config_names():
     assert sel(385, 6144, 4096, 128, 0) == 13
     assert sel(1024, 6144, 4096, 128, 0) == 13
     assert sel(2048, 4096, 4096, 128, 0) == 12        # M >= 2048, N < 16384, K < 8192
-    assert sel(2048, 6144, 4096, 128, 0) == 12
     assert sel(2048, 4096, 4104, 128, 0) == 12        # ragged K
     assert sel(2048, 4096, 14336, 128, 0) == 13       # long K
-    assert sel(8192, 28672, 4096, 128, 0) == 13       # wide N
-    for cid in (1, 2, 3, 4, 12, 13):
+    # the 256 x 256 tile where its grid covers three quarters of the 256 units or more
+    assert sel(2048, 6144, 4096, 128, 0) == 14        # 192 tiles
+    assert sel(2048, 28672, 4096, 128, 0) == 14
+    assert sel(8192, 28672, 4096, 128, 0) == 14
+    assert sel(8192, 4096, 14336, 128, 0) == 14       # 512 tiles
+    assert sel(256, 57344, 8192, 128, 1) == 14        # 224 tiles
+    assert sel(300, 57344, 8192, 128, 1) == 12        # 257..384 rows: the 128-row tile
+    assert sel(1024, 4096, 14336, 128, 0) == 13       # 64 tiles: the split 256 x 128 one
+    for cid in (1, 2, 3, 4, 12, 13, 14):
         assert mp.config_name(cid)
     for cid in (7, 10, 11):
         assert mp.config_name(cid) == ""
@@ -138,6 +144,17 @@ def _gemm(X=A, dtype=0, pc=A, pm=A, M=16, N=256, K=256, g=128, sym=0, Y=A, cfg=N
 ])
 def test_gemm_validation(kw, status):
     assert _gemm(**kw) == status
+
+
+def test_wide_tile_rejects_8bit_and_fp8_codes():
+    """The 256 x 256 tile (id 14) is built for 4-bit codes: the 8-bit and FP8 entry points
+    refuse it before touching any pointer."""
+    lib = mp.lib()
+    common = [ctypes.c_void_p(A), 0, ctypes.c_void_p(A), ctypes.c_void_p(A), 512, 256, 256, 128]
+    assert lib.mpgemm_w8a16_config(*common, 0, ctypes.c_void_p(A), None, 0, 14, None) == UNSUPPORTED
+    assert lib.mpgemm_wfp8a16_config(ctypes.c_void_p(A), 0, 0, ctypes.c_void_p(A),
+                                     ctypes.c_void_p(A), 512, 256, 256, 128, ctypes.c_void_p(A),
+                                     None, 0, 14, None) == UNSUPPORTED
 
 
 def test_pack_and_unpack_validation():
@@ -226,7 +243,7 @@ def test_binding_fp8_format_names_match_header():
     assert mp.FP8_FORMATS == {"e4m3": 0, "e5m2": 1}
 
 
-@pytest.mark.parametrize("cfg", [5, 10, 11, 14, -1])
+@pytest.mark.parametrize("cfg", [5, 10, 11, 15, -1])
 def test_unknown_configuration_ids_are_rejected(cfg):
     # 10 and 11 named 16x16x32 tiled kernels that the selector never chose; they are gone
     assert _gemm(M=128, K=256, cfg=cfg) == INVALID

@@ -40,7 +40,7 @@ def test_largest_m_at_k16384():
     M = LIMIT // K - 129                     # (M + 128) * K = 2^31 - 16384
     rng = np.random.default_rng(1)
     rows = np.unique(np.concatenate([[0, M - 1, M - 2, M // 2], rng.choice(M, 8, replace=False)]))
-    check(M, K, N, [0, 12, 13], rows, np.arange(N), 11)
+    check(M, K, N, [0, 12, 13, 14], rows, np.arange(N), 11)
 
 
 def test_largest_n_at_k16384():

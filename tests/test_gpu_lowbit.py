@@ -26,7 +26,7 @@ ONE = {"f16": 0x3C00, "bf16": 0x3F80}
 def configs_for(M):
     """Every configuration that runs M rows: the small-M kernel ids, and for M > 64 the two
     32x32x16 tiled ids (on the codes rewritten in the 4-bit layout)."""
-    return [0] + [c for c in (1, 2, 3, 4) if M <= 16 * c] + ([12, 13] if M > 64 else [])
+    return [0] + [c for c in (1, 2, 3, 4) if M <= 16 * c] + ([12, 13, 14] if M > 64 else [])
 
 
 def make(bits, K, N, g, sym, seed, lo=0.005, hi=0.05):

@@ -39,7 +39,8 @@ def tol(dtype):
 DECODE_CONFIGS = (1, 2, 3, 4)
 PREFILL_X32 = 12      # 32x32x16 kernel, 128 x 256 tile
 PREFILL_X32_TALL = 13  # the same with a 256 x 128 workgroup tile
-PREFILL_CONFIGS = (PREFILL_X32, PREFILL_X32_TALL)
+PREFILL_X32_WIDE = 14  # the same with a 256 x 256 workgroup tile
+PREFILL_CONFIGS = (PREFILL_X32, PREFILL_X32_TALL, PREFILL_X32_WIDE)
 
 
 def say(msg):
@@ -291,7 +292,7 @@ def _full_shape(wl, M, K, N, nrows=4, configs=None):
         del y, bad
 
 
-TILED = [0, PREFILL_X32, PREFILL_X32_TALL]
+TILED = [0, PREFILL_X32, PREFILL_X32_TALL, PREFILL_X32_WIDE]
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
@@ -399,7 +400,7 @@ def test_nonfinite_inputs_propagate():
         assert np.isfinite(np.delete(y, 3, axis=0)).all()
 
 
-@pytest.mark.parametrize("config", [PREFILL_X32, PREFILL_X32_TALL])
+@pytest.mark.parametrize("config", PREFILL_CONFIGS)
 @pytest.mark.parametrize("K", [256, 768, 1280])
 def test_ring_stage_waits_regression_tiny_grids_bit_exact(config, K):
     """Regression guard for the LDS-ring race (a stage could pass its barrier before its

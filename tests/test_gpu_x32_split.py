@@ -18,7 +18,8 @@ from test_gpu_parity import REL_TOL, dev_half, dev_u8, host_bits, oracle_sample,
 
 pytestmark = pytest.mark.gpu
 
-X32, X32_TALL = 12, 13
+X32, X32_TALL, X32_WIDE = 12, 13, 14
+TILE = {X32: (128, 256), X32_TALL: (256, 128), X32_WIDE: (256, 256)}
 COUNTER_BYTES = 256 * 1024
 
 
@@ -29,7 +30,7 @@ def cus():
 def parts(M, N, K, config):
     """The split rule: fewer tiles than CUs split P ways when P tiles <= CUs, parts keep
     whole 256-deep stage blocks and at least 1024 of K, and K needs no padding."""
-    bm, bn = (128, 256) if config == X32 else (256, 128)
+    bm, bn = TILE[config]
     Np, Kp = -(-N // 16) * 16, -(-K // 128) * 128
     loop = -(-Kp // 256) * 256
     tiles = -(-M // bm) * -(-Np // bn)
@@ -52,6 +53,8 @@ def run(case, packed, config, env=None, monkeypatch=None):
 
 @pytest.mark.parametrize("M,K,N,config,P", [(130, 2048, 256, X32, 2), (130, 4096, 256, X32, 4),
                                             (130, 4096, 256, X32_TALL, 4),
+                                            (130, 4096, 256, X32_WIDE, 4),
+                                            (300, 8192, 512, X32_WIDE, 8),
                                             (300, 8192, 256, X32_TALL, 8),
                                             (200, 8192, 512, X32, 8)])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -72,7 +75,7 @@ def test_split_tiles_match_oracle(M, K, N, config, P, dtype, monkeypatch):
     assert rel_err(y0, want, dtype) <= REL_TOL
 
 
-@pytest.mark.parametrize("config", [X32, X32_TALL])
+@pytest.mark.parametrize("config", [X32, X32_TALL, X32_WIDE])
 def test_split_exact_sums_bit_exact(config):
     """X in {-1, 0, 1}, s = 2^-8: every partial sum is exact in fp32 whatever the split."""
     M, K, N, g = 130, 4096, 256, 128
@@ -142,3 +145,37 @@ def test_split_leaves_counters_zero_and_runs_whole_tiles_without_workspace(monke
         whole = run(case, packed, config, "0", monkeypatch)
         monkeypatch.delenv("MPGEMM_X32_SPLIT")
         assert np.array_equal(host_bits(y), whole)
+
+
+def test_wide_tile_splits_only_with_room_for_its_partials(monkeypatch):
+    """2048 x 14336 x 4096 on the 256 x 256 tile: 128 tiles, split in two only when the
+    workspace holds 256 partials of 256 KiB; the default workspace (sized for the other
+    tiles, which run whole here) gives the unsplit result bit for bit, and a larger one the
+    split, both against the oracle on sampled outputs."""
+    M, K, N = 2048, 14336, 4096
+    if cus() == 256:
+        assert parts(M, N, K, X32_WIDE) == 2
+    need = COUNTER_BYTES + 128 * 2 * 256 * 256 * 4
+    assert int(mp.lib().mpgemm_workspace_bytes(M, N, K, 128, 0)) < need
+    case = workloads.make_case(workloads.LLAMA3_8B_DECODE, M, K, N)
+    packed = pack_case(case)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 12, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 256, replace=False)]))
+    want = oracle_sample(case, rows, cols)
+    r_t, c_t = torch.as_tensor(rows, device="cuda"), torch.as_tensor(cols, device="cuda")
+    x = dev_half(case["x"])
+    say("wide tile: default workspace, then a larger one, then the split turned off")
+    y_def = mp.w4a16(x, packed, config=X32_WIDE)
+    big = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y_split = mp.w4a16(x, packed, config=X32_WIDE, workspace=big)
+    torch.cuda.synchronize()
+    assert int(big[:COUNTER_BYTES].count_nonzero()) == 0
+    monkeypatch.setenv("MPGEMM_X32_SPLIT", "0")
+    y_whole = mp.w4a16(x, packed, config=X32_WIDE)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y_def), host_bits(y_whole))
+    for y in (y_def, y_split):
+        got = host_bits(y[r_t][:, c_t].contiguous())
+        assert rel_err(got, want, "f16") <= REL_TOL
+    assert not np.array_equal(host_bits(y_split), host_bits(y_whole))   # it did split

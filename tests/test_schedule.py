@@ -1,6 +1,6 @@
-"""Workgroup schedule of the tiled kernels (ids 12 and 13), checked on the host through
+"""Workgroup schedule of the tiled kernels (ids 12, 13 and 14), checked on the host through
 mpgemm_prefill_schedule: every output tile is computed exactly once -- whole by one
-workgroup, or split over P workgroups that take each K part once -- for both tile shapes,
+workgroup, or split over P workgroups that take each K part once -- for every tile shape,
 with and without the K split of small grids.  The schedule is the same function the
 kernels call (x32_work_of), compiled for the host."""
 import random
@@ -10,7 +10,8 @@ import torch
 
 import weight_only_quantized_mpgemm_amd as mp
 
-CONFIGS = (12, 13)
+CONFIGS = (12, 13, 14)
+TILES = {12: (128, 256), 13: (256, 128), 14: (256, 256)}
 
 
 def _padded_n(N):
@@ -19,7 +20,7 @@ def _padded_n(N):
 
 def _check(M, N, K, cfg, cus):
     info, work = mp.prefill_schedule(M, N, K, cfg, cus)
-    bm, bn = (128, 256) if cfg == 12 else (256, 128)
+    bm, bn = TILES[cfg]
     tm, tn = (M + bm - 1) // bm, (_padded_n(N) + bn - 1) // bn
     assert (info["tile_m"], info["tile_n"], info["tiles_m"], info["tiles_n"]) == (bm, bn, tm, tn)
     tiles, full, P, grid = tm * tn, info["full"], info["parts"], info["grid"]
@@ -91,6 +92,10 @@ def test_split_takes_the_largest_part_count_that_fits():
     assert _check(128, 5120, 25600, 13, 256)["parts"] == 5
     # a grid with as many tiles as units runs whole
     assert _check(2048, 4096 * 4, 4096, 12, 256)["parts"] == 1
+    # the 256 x 256 tile: 8 x 16 tiles at M = 2048, N = 4096 split K = 14336 (56 blocks) in
+    # two; 8 x 112 tiles at N = 28672 run whole
+    assert _check(2048, 4096, 14336, 14, 256)["parts"] == 2
+    assert _check(2048, 28672, 4096, 14, 256)["parts"] == 1
 
 
 def test_schedule_rejects_bad_arguments():

@@ -399,7 +399,7 @@ def _gemm(kind: str, x: torch.Tensor, packed: PackedWeights, out, config, worksp
         ws = int(lib().mpgemm_workspace_bytes(M, N, K, packed.group, act))
     if workspace is None:
         workspace = workspace_for(x.device, ws)
-    elif ws:
+    else:                       # all of it: the 256 x 256 tile may split K in more than ws
         _need(workspace, torch.uint8, (workspace.numel(),), "workspace")
         ws = workspace.numel()
     if kind == "fp8":

@@ -28,6 +28,7 @@ enum ConfigId {
     kConfigDecode4 = 4,
     kConfigPrefillX32 = 12,    // 32x32x16 kernel, 128 x 256 workgroup tile
     kConfigPrefillX32Tall = 13,  // same, 256 x 128 workgroup tile
+    kConfigPrefillX32Wide = 14,  // same, 256 x 256 workgroup tile (4-bit codes)
 };
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -85,12 +86,37 @@ int pick_tile(int M, int N, int K) {
     return kConfigPrefillX32;
 }
 
-int select_config(int M, int N, int K) {
+bool tiled_config(int cfg) {
+    return cfg == kConfigPrefillX32 || cfg == kConfigPrefillX32Tall ||
+           cfg == kConfigPrefillX32Wide;
+}
+hipError_t launch_tiled(int cfg, const mpgemm::GemmArgs &a, hipStream_t s) {
+    if (cfg == kConfigPrefillX32Tall) return mpgemm::launch_prefill_x32_tall(a, s);
+    if (cfg == kConfigPrefillX32Wide) return mpgemm::launch_prefill_x32_wide(a, s);
+    return mpgemm::launch_prefill_x32(a, s);
+}
+
+// The 256 x 256 tile (4-bit codes) where its grid covers at least three quarters of the
+// compute units: it then beat both other tiles on every measured shape, by 2-15%
+// (Llama-3-8B QKV at M = 2048: 192 tiles, 91 us against 98 and 104; gate_up 2048: 392
+// against 401; at M = 8192 7-10% on all four Llama-3-8B projections, 8% on Llama-3-70B
+// bf16 gate_up and down at M = 4096, 6-10% on Qwen3-32B gate_up and down).  Smaller grids
+// would need its K split, whose partials are twice the other tiles' (and more than the
+// reported workspace holds): there the other tiles, split, were up to twice as fast.
+bool wide_fills(int M, int N, int K) {
+    int cus = 256;
+    mpgemm::x32_grid(M, N, K, 3, nullptr, &cus);        // the device's units (256 if none)
+    const int64_t tiles = (int64_t)((M + 255) / 256) * ((mpgemm::padded_n(N) + 255) / 256);
+    return 4 * tiles >= 3 * (int64_t)cus;
+}
+
+int select_config(int M, int N, int K, bool wide_ok = true) {
     if (M <= 16) return kConfigDecode1;
     const int64_t nk = (int64_t)N * K;
     if (M <= 32 || (M <= 64 && nk <= 4096 * 4096)) return (M + 15) / 16;
     if (M <= 128) return pick_tile(M, N, K);
     if (M > 256 && M <= 384 && K < 16384) return kConfigPrefillX32;
+    if (wide_ok && wide_fills(M, N, K)) return kConfigPrefillX32Wide;
     if (M >= 2048 && N < 16384 && K < 8192) return kConfigPrefillX32;
     return kConfigPrefillX32Tall;
 }
@@ -126,9 +152,13 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     const int st = check_shape(M, N, K, group);
     if (st != MPGEMM_OK) return st;
     if (config_id != kConfigSelect &&
-        !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) ||
-          config_id == kConfigPrefillX32 || config_id == kConfigPrefillX32Tall))
+        !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) || tiled_config(config_id)))
         return MPGEMM_ERR_INVALID_ARG;
+    // The 256 x 256 tile is built for 4-bit codes (and the 2- and 3-bit ones, which reach the
+    // tiled kernels rewritten in the 4-bit layout).
+    if (config_id == kConfigPrefillX32Wide && code != mpgemm::kU4 && code != mpgemm::kU2 &&
+        code != mpgemm::kU3)
+        return MPGEMM_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return MPGEMM_OK;
     if (Y == nullptr) return MPGEMM_ERR_INVALID_ARG;
     if (!aligned16(Y)) return MPGEMM_ERR_ALIGNMENT;
@@ -142,9 +172,10 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     // 2- and 3-bit codes reach the tiled kernels only through the 4-bit rewrite (M > 64):
     // up to 64 rows they take the strip kernel at every N.
     const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
+    const bool four_bit_layout = code == mpgemm::kU4 || lowbit;
     const int cfg = config_id != kConfigSelect ? config_id
                     : lowbit && M <= 64     ? (M + 15) / 16
-                                            : select_config(M, N, K);
+                                            : select_config(M, N, K, four_bit_layout);
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
     const int Kp = mpgemm::padded_k(K);
@@ -188,8 +219,7 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
             if (getenv("MPGEMM_LOG"))
                 fprintf(stderr, "mpgemm: W%dA16 M=%d N=%d K=%d g=%d -> 4-bit repack, %s\n",
                         code == mpgemm::kU2 ? 2 : 3, M, N, K, group, mpgemm_config_name(xcfg));
-            return hip_status(xcfg == kConfigPrefillX32Tall ? mpgemm::launch_prefill_x32_tall(c, s)
-                                                            : mpgemm::launch_prefill_x32(c, s));
+            return hip_status(launch_tiled(xcfg, c, s));
         }
         if (config_id != kConfigSelect) return MPGEMM_ERR_WORKSPACE;
         const size_t need = mpgemm::decode_workspace_bytes(64, N, K, group, kConfigDecode4);
@@ -215,8 +245,7 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
         fprintf(stderr, "mpgemm: %s M=%d N=%d K=%d g=%d dtype=%d sym=%d -> %s\n", names[code],
                 M, N, K, group, dtype, symmetric, mpgemm_config_name(cfg));
     }
-    if (cfg == kConfigPrefillX32) return hip_status(mpgemm::launch_prefill_x32(a, s));
-    if (cfg == kConfigPrefillX32Tall) return hip_status(mpgemm::launch_prefill_x32_tall(a, s));
+    if (tiled_config(cfg)) return hip_status(launch_tiled(cfg, a, s));
     return hip_status(mpgemm::launch_decode(a, cfg, s));
 }
 
@@ -644,11 +673,10 @@ int mpgemm_prefill_schedule(int M, int N, int K, int config_id, int cus, int *in
                             int capacity) {
     if (info == nullptr || M <= 0 || N <= 0 || K <= 0 || cus < 0 || capacity < 0)
         return MPGEMM_ERR_INVALID_ARG;
-    if (config_id != kConfigPrefillX32 && config_id != kConfigPrefillX32Tall)
-        return MPGEMM_ERR_INVALID_ARG;
+    if (!tiled_config(config_id)) return MPGEMM_ERR_INVALID_ARG;
     if (const int st = check_shape(M, N, K, 128)) return st;
-    return mpgemm::x32_schedule(M, N, K, config_id == kConfigPrefillX32Tall ? 1 : 2, cus, info,
-                                work, capacity);
+    const int sh = config_id == kConfigPrefillX32Tall ? 1 : config_id == kConfigPrefillX32 ? 2 : 3;
+    return mpgemm::x32_schedule(M, N, K, sh, cus, info, work, capacity);
 }
 
 const char *mpgemm_config_name(int config_id) {
@@ -659,6 +687,7 @@ const char *mpgemm_config_name(int config_id) {
         case kConfigDecode4: return "decode_splitk_m64";
         case kConfigPrefillX32: return "prefill_x32_128x256";
         case kConfigPrefillX32Tall: return "prefill_x32_256x128";
+        case kConfigPrefillX32Wide: return "prefill_x32_256x256";
         default: return "";
     }
 }

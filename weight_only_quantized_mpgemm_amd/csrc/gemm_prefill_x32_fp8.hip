@@ -4,11 +4,12 @@
 
 namespace mpgemm {
 
-hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream) {
+hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int sh, hipStream_t stream) {
+    if (sh == 3) return hipErrorInvalidValue;          // the 256 x 256 tile: 4-bit codes only
     if (a.code == kE5M2)
-        nb == 1 ? launch_x32<1, kE5M2>(a, stream) : launch_x32<2, kE5M2>(a, stream);
+        sh == 1 ? launch_x32<1, kE5M2>(a, stream) : launch_x32<2, kE5M2>(a, stream);
     else
-        nb == 1 ? launch_x32<1, kE4M3>(a, stream) : launch_x32<2, kE4M3>(a, stream);
+        sh == 1 ? launch_x32<1, kE4M3>(a, stream) : launch_x32<2, kE4M3>(a, stream);
     return hipGetLastError();
 }
 

@@ -75,28 +75,32 @@ size_t decode_workspace_bytes(int M, int N, int K, int group, int mblocks);
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
 // The 32x32x16 kernel with a 256 (m) x 128 (n) workgroup tile.
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
-// Their instantiations per code format, one translation unit each (nb: column blocks per
-// wave, 2 for the 128 x 256 tile, 1 for 256 x 128).
-hipError_t launch_prefill_x32_u4(const GemmArgs &a, int nb, hipStream_t stream);
-hipError_t launch_prefill_x32_u8(const GemmArgs &a, int nb, hipStream_t stream);
-hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int nb, hipStream_t stream);
+// The 32x32x16 kernel with a 256 (m) x 256 (n) workgroup tile (4-bit codes only;
+// hipErrorInvalidValue for the others).
+hipError_t launch_prefill_x32_wide(const GemmArgs &a, hipStream_t stream);
+// Their instantiations per code format, one translation unit each (sh: tile shape, 1 for
+// 256 x 128, 2 for 128 x 256, 3 for 256 x 256).
+hipError_t launch_prefill_x32_u4(const GemmArgs &a, int sh, hipStream_t stream);
+hipError_t launch_prefill_x32_u8(const GemmArgs &a, int sh, hipStream_t stream);
+hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int sh, hipStream_t stream);
 // Sub-4-bit packed codes (Kp x Np, padded sizes) rewritten in the 4-bit packed layout
 // (Kp*Np/2 bytes at `out`, 16-byte aligned), so that the 4-bit kernels with the same meta
 // plane dequantize every weight to the same value (symmetric codes are shifted by
 // 8 - 2^(bits-1) onto the 4-bit symmetric zero 8).
 hipError_t launch_repack_lowbit_u4(int bits, bool symmetric, const void *packed_codes, int Kp,
                                    int Np, void *out, hipStream_t stream);
-// Workspace bytes with which the 32x32x16 kernels (either tile shape) split the K range of
-// their tiles (grids of fewer tiles than compute units); 0 when they never do for this
-// shape.  N, K: user shape.
+// Workspace bytes with which the 128 x 256 and 256 x 128 kernels split the K range of their
+// tiles (grids of fewer tiles than compute units); 0 when they never do for this shape.
+// The 256 x 256 kernel splits when the workspace it gets also holds its partials, and runs
+// unsplit otherwise.  N, K: user shape.
 size_t x32_workspace_bytes(int M, int N, int K);
-// Workgroups of a 32x32x16 launch with nb column blocks per wave, with the K split it takes
+// Workgroups of a 32x32x16 launch in tile shape sh, with the K split it takes
 // on the current device (256 compute units when none is current); *parts: its part count,
 // *cus: the compute units assumed (either pointer may be NULL).
-int x32_grid(int M, int N, int K, int nb, int *parts, int *cus);
-// Workgroup schedule of a 32x32x16 launch with nb column blocks per wave (host only):
+int x32_grid(int M, int N, int K, int sh, int *parts, int *cus);
+// Workgroup schedule of a 32x32x16 launch in tile shape sh (host only):
 // info[8] and work[4 grid] as mpgemm_prefill_schedule documents; returns the grid size.
-int x32_schedule(int M, int N, int K, int nb, int cus, int *info, int *work, int capacity);
+int x32_schedule(int M, int N, int K, int sh, int cus, int *info, int *work, int capacity);
 
 // Decode attention over an 8-bit KV cache (attention.hip).
 struct AttnArgs {

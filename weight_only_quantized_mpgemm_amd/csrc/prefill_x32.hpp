@@ -62,8 +62,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kXThreads = 256;
 constexpr int kXStages = 4;                  // 64-deep LDS stages in the ring
-constexpr int tile_m(int nb) { return 32 * (8 / nb); }   // workgroup tile rows (m)
-constexpr int tile_n(int nb) { return 128 * nb; }        // workgroup tile columns (n)
+// Workgroup tile shapes SH: 1 = 256 (m) x 128 (n), 2 = 128 x 256, 3 = 256 x 256.  Each of
+// the four waves owns shape_nb(SH) 32-column blocks of shape_mb(SH) 32-row blocks.
+constexpr int shape_nb(int sh) { return sh == 1 ? 1 : 2; }
+constexpr int shape_mb(int sh) { return sh == 2 ? 4 : 8; }
+constexpr int tile_m(int sh) { return 32 * shape_mb(sh); }    // workgroup tile rows (m)
+constexpr int tile_n(int sh) { return 128 * shape_nb(sh); }   // workgroup tile columns (n)
+// Workgroups of the split reduction per tile: four chunks of a lane's 4 NB MB each.
+constexpr int x32_reduce_wgs(int sh) { return shape_nb(sh) * shape_mb(sh); }
 // Weight register sets (loads run NWS - 1 tiles ahead): four for 4-bit codes with
 // g = 128; two for g = 64, whose doubled scale/zero registers would not fit four sets
 // without spilling, and two for 8-bit codes (twice the code registers per set).
@@ -349,7 +355,7 @@ __host__ __device__ inline X32Work x32_work_of(int b, int tm, int tn, int full, 
 // hold rows below M (MA < 8 / NB when M <= 32 MA): the MFMAs and activation operand reads
 // of the others are skipped (their accumulators stay zero and are never stored); loads and
 // DMAs are unchanged (rows past M read as zeros).
-template <int ACT, bool SYM, int G, int NWS, int NB, int CODE, bool RAG, int MA>
+template <int ACT, bool SYM, int G, int NWS, int SH, int CODE, bool RAG, int MA>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
@@ -370,8 +376,10 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // 16 x 128 tile of 4-bit codes, one slot of each of two 16 x 64 tiles of 8-bit codes.
     constexpr int WV = BITS / 4;
     constexpr int GPT = kTileK / G;          // groups per 128-deep tile (1 or 2)
-    constexpr int MB = 8 / NB;               // 32-row blocks per wave
-    constexpr int BM = tile_m(NB), BN = tile_n(NB);
+    constexpr int NB = shape_nb(SH);         // 32-column blocks per wave
+    constexpr int MB = shape_mb(SH);         // 32-row blocks per wave
+    constexpr int NMF = 2 * NB * MB;         // MFMAs per 32-deep step (16, or 32 at SH 3)
+    constexpr int BM = tile_m(SH), BN = tile_n(SH);
     constexpr int kChunks = BM * 8;          // 16-byte chunks per stage (8 per 64-deep row)
     // Loads each wave issues per weight tile: 2 NB WV 16-byte code slots (column blocks x
     // k halves x pieces), plus scales (and zeros) per column block and group.
@@ -406,13 +414,18 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // (Offset arrays have fixed bounds, of which MB / NB entries are used: with bounds
     // that depend on a template parameter, the host pass of this compiler silently emits
     // no launch stub for the kernel.)
+    // The 256 x 256 tile keeps only block 0's offset and adds i times the 8-row stride at
+    // each DMA (eight offsets would not fit its registers): rows past M then take offsets
+    // past the plane, or wrap into it for the largest planes; either way their loads do
+    // not fault, and those rows' results are never stored.
     uint32_t xoff[8];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < (SH == 3 ? 1 : MB); ++i) {
         const int r = 8 * (wave * MB + i) + (lane >> 3);
-        const uint32_t row = (uint32_t)min(m_blk + r, M);
+        const uint32_t row = SH == 3 ? (uint32_t)(m_blk + r) : (uint32_t)min(m_blk + r, M);
         xoff[i] = (row * Kx + (((lane & 7) ^ (lane >> 3)) * 8) + t0 * 128) * 2u;
     }
+    const uint32_t xstep = 16u * (uint32_t)Kx;        // 8 rows of activations, in bytes
     // Ragged K: first k of the lane's chunk within a stage.
     const int k_chunk = ((lane & 7) ^ (lane >> 3)) * 8;
     // Weight slots: column block nb (strips strip0 + 2nb, +1), k half u.  Strips past N
@@ -461,7 +474,14 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     auto dma_part = [&](int st, auto buf, int i) __attribute__((always_inline)) {
         const int sc = min(st, S - 1);
         const uint32_t soff_k = (uint32_t)sc * 128u;
-        uint32_t off = xoff[i];
+        uint32_t off;
+        if constexpr (SH == 3) {
+            uint32_t step = (uint32_t)i * xstep;
+            asm volatile("" : "+s"(step));     // added here, not hoisted as 8 registers
+            off = xoff[0] + step;
+        } else {
+            off = xoff[i];
+        }
         if constexpr (RAG) off = sc * 64 + k_chunk < Kx ? off : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * MB + i) * 64],
@@ -525,8 +545,10 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     };
 
     // Dequantization operations of the next step.  Four words (word q = (u, nb) = (q / 2,
-    // q % 2)): operation o is step o / 4 of word o % 4.  Two words (q = u): word 0's
-    // operations first, then word 1's.
+    // q % 2)): operation o is step o / 4 of word o % 4.  Two words (q = u), and the four
+    // words of the 256 x 256 tile (whose 32-MFMA steps put an MFMA between any two
+    // operations anyway, and whose registers hold only one word's scratch values): word
+    // 0's operations first, then word 1's, and so on.
     auto run_ops = [&](auto LO, auto HI, const WSet &wn, const DqT(&dn)[NB][GPT], int word_n,
                        DqTmp(&tmp)[2 * NB], u32x4_t(&an)[2][NB]) __attribute__((always_inline)) {
         constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
@@ -534,8 +556,9 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
             (([&] {
                  constexpr int o = lo + O;
                  if constexpr (o < hi) {
-                     constexpr int q = NB == 2 ? o % 4 : o / Ops::kCount;
-                     constexpr int op = NB == 2 ? o / 4 : o % Ops::kCount;
+                     constexpr bool rr = NB == 2 && SH != 3;     // round-robin
+                     constexpr int q = rr ? o % 4 : o / Ops::kCount;
+                     constexpr int op = rr ? o / 4 : o % Ops::kCount;
                      constexpr int u = q / NB, nb = q % NB;
                      if constexpr (BITS == 4)
                          Ops::template run<op>(wn.w[nb][u][0][word_n], dn[nb][(word_n * 32) / G],
@@ -585,6 +608,43 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // One 32-deep step of the 256 x 256 tile: 32 MFMAs, MFMA i on column block i % 2, row
+    // block (i % 16) / 2 and k half i / 16, so each activation operand feeds two MFMAs in a
+    // row.  Its activation operands are single-buffered (a second set would not fit beside
+    // 256 accumulators): after MFMA 2r the step reads its own second-half operand of row
+    // block r, whose register the previous step last read 15 MFMAs before, and after MFMA
+    // 16 + 2r the next step's first-half operand of row block r, last read here 15 MFMAs
+    // before.  The dequantization of the next step's four words is spread over the 32
+    // MFMAs as in the other shapes.
+    auto step_wide = [&](const u32x4_t(&a)[2][NB], u32x4_t(&b)[2][MB], u32x4_t(&an)[2][NB],
+                         const WSet &wn, const DqT(&dn)[NB][GPT], int word_n, auto buf, int s,
+                         auto bufn, int s_n, auto hook) __attribute__((always_inline)) {
+        DqTmp tmp[2 * NB];
+        constexpr int total = 2 * NB * Ops::kCount;
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (([&] {
+                 constexpr int u = I / 16, mb = (I % 16) / 2, nb = I % 2;
+                 mfma32<ACT>(acc[nb][mb], a[u][nb], b[u][mb]);
+                 if constexpr (I % 2 == 0) {
+                     if constexpr (u == 0)
+                         b[1][mb] = xs[decltype(buf)::value][mb * 256 + brow + ((4 * s + 2) ^ cb)];
+                     else
+                         b[0][mb] = xs[decltype(bufn)::value][mb * 256 + brow + ((4 * s_n) ^ cb)];
+                 }
+                 run_ops(IC<(total * I) / 32>(), IC<(total * (I + 1)) / 32>(), wn, dn, word_n,
+                         tmp, an);
+                 hook(IC<I>());
+                 __builtin_amdgcn_sched_barrier(0);
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, 32>{});
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) asm volatile("" ::"v"(a[u][nb]));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     // One 64-deep stage st (ring buffer BUF = st % 4, tile t = st / 2, half H = st % 2,
     // weight set TW = t % NWS): step 0 runs word 2H and prepares word 2H+1 from this
     // stage's buffer; step 1 runs word 2H+1 and prepares the next stage's first step (the
@@ -607,7 +667,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         // as before, instead of as one burst per wave at the barrier.
         auto dma_hook = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
-            constexpr int every = 16 / MB;
+            constexpr int every = NMF / MB;
             if constexpr (i % every == 1) dma_part(st + 3, IC<(buf + 3) % kXStages>(), i / every);
         };
         auto w_hook = [&](auto I) __attribute__((always_inline)) {
@@ -622,13 +682,24 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
                 }
             }
         };
-        step(A[0], B[0], A[1], B[1], ws[tw], dq[tw], 2 * h + 1, BUF, 1, dma_hook);
-        if (h == 1) {
-            make_dq(ws[nw], dq[nw]);
-            __builtin_amdgcn_sched_barrier(0);
-            step(A[1], B[1], A[0], B[0], ws[nw], dq[nw], 0, IC<nbuf>(), 0, w_hook);
+        if constexpr (SH == 3) {
+            step_wide(A[0], B[0], A[1], ws[tw], dq[tw], 2 * h + 1, BUF, 0, BUF, 1, dma_hook);
+            if (h == 1) {
+                make_dq(ws[nw], dq[nw]);
+                __builtin_amdgcn_sched_barrier(0);
+                step_wide(A[1], B[0], A[0], ws[nw], dq[nw], 0, BUF, 1, IC<nbuf>(), 0, w_hook);
+            } else {
+                step_wide(A[1], B[0], A[0], ws[tw], dq[tw], 2, BUF, 1, IC<nbuf>(), 0, w_hook);
+            }
         } else {
-            step(A[1], B[1], A[0], B[0], ws[tw], dq[tw], 2, IC<nbuf>(), 0, w_hook);
+            step(A[0], B[0], A[1], B[1], ws[tw], dq[tw], 2 * h + 1, BUF, 1, dma_hook);
+            if (h == 1) {
+                make_dq(ws[nw], dq[nw]);
+                __builtin_amdgcn_sched_barrier(0);
+                step(A[1], B[1], A[0], B[0], ws[nw], dq[nw], 0, IC<nbuf>(), 0, w_hook);
+            } else {
+                step(A[1], B[1], A[0], B[0], ws[tw], dq[tw], 2, IC<nbuf>(), 0, w_hook);
+            }
         }
     };
     // Stages st .. st+3 (tiles 2u, 2u+1 of a 2 * NWS-stage block, u = 0 or 1); LAST: the
@@ -712,7 +783,54 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // tile row r sits at chunk c ^ (r % 16), so the 8-byte writes of 16 rows and the
     // 16-byte reads of a row each spread over all 64 banks.
     __syncthreads();
-    {
+    if constexpr (SH == 3) {
+        // The 256 x 256 tile: its 256 accumulators leave no registers to round them in bulk,
+        // so they go to LDS in fp32 straight from the accumulator registers, one 128-row
+        // half of the tile (128 KiB, the whole ring) at a time, and are rounded as they
+        // come back as whole rows.  16-byte chunk c (of 64) of half-tile row r sits at
+        // chunk c ^ (r % 16), so the writes of 16 rows spread over all 64 banks.
+        constexpr int CPR = BN / 4;              // 16-byte fp32 chunks per tile row
+        constexpr int HR = BM / 2;               // rows per half
+        static_assert(HR * BN * 4 == (int)sizeof(xs), "a half tile fills the ring");
+        f32x4_t *ot = reinterpret_cast<f32x4_t *>(&xs[0][0]);
+        const int n_blk = nt * BN;
+        const bool aligned = (Ny & 7) == 0;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if (hf == 1) __syncthreads();        // every read of the first half is done
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = wave * 16 + 8 * nb + 2 * q + (lane >> 5);
+#pragma unroll
+                    for (int mb = 0; mb < MB / 2; ++mb) {
+                        const int r = mb * 32 + (lane & 31), b = hf * (MB / 2) + mb;
+                        ot[r * CPR + (c ^ (r & 15))] =
+                            f32x4_t{acc[nb][b][4 * q], acc[nb][b][4 * q + 1], acc[nb][b][4 * q + 2],
+                                    acc[nb][b][4 * q + 3]};
+                    }
+                }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < HR * (CPR / 2) / kXThreads; ++i) {
+                const int idx = i * kXThreads + tid;
+                const int r = idx / (CPR / 2), cp = idx % (CPR / 2);   // 8 outputs per thread
+                const int m = m_blk + hf * HR + r, n = n_blk + 8 * cp;
+                if (m >= M || n >= Ny) continue;
+                const u32x2_t lo = round4<ACT>(ot[r * CPR + ((2 * cp) ^ (r & 15))]);
+                const u32x2_t hi = round4<ACT>(ot[r * CPR + ((2 * cp + 1) ^ (r & 15))]);
+                const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
+                uint16_t *p = Y + (size_t)m * Ny + n;
+                if (aligned && n + 8 <= Ny) {
+                    *reinterpret_cast<u32x4_t *>(p) = v;
+                } else {
+                    const int avail = min(8, Ny - n);
+                    for (int e = 0; e < avail; ++e) p[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+    } else {
         constexpr int CPR = BN / 8;              // 16-byte chunks per tile row
         static_assert(BM * BN * 2 <= (int)sizeof(xs), "the result tile fits the ring");
         u32x2_t *ot = reinterpret_cast<u32x2_t *>(&xs[0][0]);
@@ -753,19 +871,21 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 }
 
 // Y of the split tiles: the sum of their P fp32 partials, in split order (so results do not
-// depend on which part ran first), rounded once to the output format.  Eight workgroups per
-// tile, four of its 32 register-order chunks each: thread `tid` reads the four floats that
+// depend on which part ran first), rounded once to the output format.  NB MB workgroups per
+// tile (8, or 16 for the 256 x 256 tile), four of a lane's 4 NB MB register-order chunks
+// each: thread `tid` reads the four floats that
 // thread `tid` of the main kernel wrote for each of its chunks -- all 4 P loads issued
 // before the first add, so one memory round trip covers them -- and knows their (m, n)
 // the same way.
-template <int ACT, int NB>
+template <int ACT, int SH>
 __global__ __launch_bounds__(kXThreads) void x32_split_reduce_kernel(
     const f32x4_t *__restrict__ part, int full, int P, int M, int N, int Ny,
     uint16_t *__restrict__ Y) {
-    constexpr int MB = 8 / NB, BM = tile_m(NB), BN = tile_n(NB);
+    constexpr int NB = shape_nb(SH), MB = shape_mb(SH), BM = tile_m(SH), BN = tile_n(SH);
     constexpr int kChunksPerPart = BM * BN / 4;
     constexpr int kMaxParts = 8, kCpt = 4;     // parts, chunks per thread
-    const int sidx = blockIdx.x >> 3, c0 = (blockIdx.x & 7) * kCpt;
+    constexpr int kWgs = x32_reduce_wgs(SH);
+    const int sidx = blockIdx.x / kWgs, c0 = (blockIdx.x % kWgs) * kCpt;
     int mt, nt;
     tile_of(full + sidx, (M + BM - 1) / BM, (N + BN - 1) / BN, mt, nt);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -834,17 +954,17 @@ inline X32Split x32_split(int tiles, int loop_k, bool rag, int cus) {
         }
     return sp;
 }
-inline size_t x32_split_bytes(const X32Split &sp, int tiles, int nb) {
+inline size_t x32_split_bytes(const X32Split &sp, int tiles, int sh) {
     if (sp.p == 1) return 0;
-    return kSplitCounterBytes + (size_t)(tiles - sp.full) * sp.p * tile_m(nb) * tile_n(nb) * 4;
+    return kSplitCounterBytes + (size_t)(tiles - sp.full) * sp.p * tile_m(sh) * tile_n(sh) * 4;
 }
 
-template <int ACT, bool SYM, int G, int NB, int CODE, bool RAG>
+template <int ACT, bool SYM, int G, int SH, int CODE, bool RAG>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
-    const int tiles = ((a.Np + tile_n(NB) - 1) / tile_n(NB)) * ((a.M + tile_m(NB) - 1) / tile_m(NB));
+    const int tiles = ((a.Np + tile_n(SH) - 1) / tile_n(SH)) * ((a.M + tile_m(SH) - 1) / tile_m(SH));
     const int loop_k = x32_loop_k(a.Kp);
     X32Split sp = x32_split(tiles, loop_k, RAG, device_cus());
-    const size_t need = x32_split_bytes(sp, tiles, NB);
+    const size_t need = x32_split_bytes(sp, tiles, SH);
     if (need > a.workspace_bytes || a.workspace == nullptr ||
         ((uintptr_t)a.workspace & 15u) != 0)
         sp = X32Split{tiles, 1};
@@ -853,53 +973,57 @@ void launch_one(const GemmArgs &a, hipStream_t stream) {
                            : nullptr;
     const dim3 grid((unsigned)(sp.full + (tiles - sp.full) * sp.p));
     // Row blocks that can hold rows below M: one tile row of a 256-row tile needs a quarter
-    // of them up to 64 rows, half up to 128; one of a 128-row tile half up to 64.
-    constexpr int MB = 8 / NB;
+    // of them up to 64 rows, half up to 128; one of a 128-row tile half up to 64.  (The
+    // 256 x 256 tile always runs all eight.)
+    constexpr int MB = shape_mb(SH);
     auto run = [&](auto MA) __attribute__((always_inline)) {
-        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, NB, CODE, RAG, decltype(MA)::value>
+        prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, SH, CODE, RAG, decltype(MA)::value>
             <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
                                                    loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
                                                    part);
     };
-    if constexpr (NB == 1) {
+    if constexpr (SH == 1) {
         if (a.M <= 8 * MB) run(IC<MB / 4>());
         else if (a.M <= 16 * MB) run(IC<MB / 2>());
         else run(IC<MB>());
-    } else {
+    } else if constexpr (SH == 2) {
         if (a.M <= 16 * MB) run(IC<MB / 2>());
         else run(IC<MB>());
+    } else {
+        run(IC<MB>());
     }
     if (sp.p > 1)
-        x32_split_reduce_kernel<ACT, NB><<<dim3((unsigned)(tiles - sp.full) * 8), dim3(kXThreads),
-                                           0, stream>>>(reinterpret_cast<const f32x4_t *>(part),
-                                                        sp.full, sp.p, a.M, a.Np, a.N, a.Y);
+        x32_split_reduce_kernel<ACT, SH>
+            <<<dim3((unsigned)(tiles - sp.full) * x32_reduce_wgs(SH)), dim3(kXThreads), 0,
+               stream>>>(reinterpret_cast<const f32x4_t *>(part), sp.full, sp.p, a.M, a.Np, a.N,
+                         a.Y);
 }
 
-template <int ACT, int NB, int CODE, bool RAG>
+template <int ACT, int SH, int CODE, bool RAG>
 void launch_act(const GemmArgs &a, hipStream_t stream) {
     if constexpr (kCodeFp8<CODE>) {         // FP8 codes carry no zero point
-        a.group == 128 ? launch_one<ACT, true, 128, NB, CODE, RAG>(a, stream)
-                       : launch_one<ACT, true, 64, NB, CODE, RAG>(a, stream);
+        a.group == 128 ? launch_one<ACT, true, 128, SH, CODE, RAG>(a, stream)
+                       : launch_one<ACT, true, 64, SH, CODE, RAG>(a, stream);
     } else {
         const bool sym = a.zeros == nullptr;
         if (a.group == 128) {
-            sym ? launch_one<ACT, true, 128, NB, CODE, RAG>(a, stream)
-                : launch_one<ACT, false, 128, NB, CODE, RAG>(a, stream);
+            sym ? launch_one<ACT, true, 128, SH, CODE, RAG>(a, stream)
+                : launch_one<ACT, false, 128, SH, CODE, RAG>(a, stream);
         } else {
-            sym ? launch_one<ACT, true, 64, NB, CODE, RAG>(a, stream)
-                : launch_one<ACT, false, 64, NB, CODE, RAG>(a, stream);
+            sym ? launch_one<ACT, true, 64, SH, CODE, RAG>(a, stream)
+                : launch_one<ACT, false, 64, SH, CODE, RAG>(a, stream);
         }
     }
 }
 
-// Every variant of code format CODE with NB column blocks per wave.
-template <int NB, int CODE>
+// Every variant of code format CODE in tile shape SH.
+template <int SH, int CODE>
 void launch_x32(const GemmArgs &a, hipStream_t stream) {
     const bool rag = a.K != x32_loop_k(a.Kp);
     if (a.act == kBF16)
-        rag ? launch_act<kBF16, NB, CODE, true>(a, stream) : launch_act<kBF16, NB, CODE, false>(a, stream);
+        rag ? launch_act<kBF16, SH, CODE, true>(a, stream) : launch_act<kBF16, SH, CODE, false>(a, stream);
     else
-        rag ? launch_act<kF16, NB, CODE, true>(a, stream) : launch_act<kF16, NB, CODE, false>(a, stream);
+        rag ? launch_act<kF16, SH, CODE, true>(a, stream) : launch_act<kF16, SH, CODE, false>(a, stream);
 }
 
 }  // namespace
