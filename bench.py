@@ -13,10 +13,13 @@ divided by the step time), plus HBM GB/s of algorithmic bytes, the roofline of t
 kernel, per-config GEMM lines and the CPU oracle timed on bounded samples (cpu_baseline).
 
 Timing.
-  * The timed steps launch every GEMM from Python.  Kernel durations come from hipEvents
-    recorded, inside the timed steps, on the stream the library launches on, around each
-    run of consecutive launches of one kernel (the four GEMMs of one M), divided by the
-    launches in it.  `roofline` uses them for the dominant kernel; it also carries the
+  * The timed steps launch every GEMM from Python (the host enqueues a step in about an
+    eighth of the GPU's time for it).  Kernel durations come from hipEvents recorded,
+    inside the timed steps, on the stream the library launches on, around each run of
+    consecutive launches of one kernel (the four GEMMs of one M, or fewer where the
+    selector changes kernel), divided by the launches in it.  Every event is created
+    before the timed region: creating them inside it let single stalls of 40-70 ms into
+    the 20-step window on some boxes.  `roofline` uses them for the dominant kernel; it also carries the
     average launch duration of the same kernel in the committed rocprofv3 kernel trace
     (profiles/w4a16_llama3_8b_m1_16_2048_kernel_trace.txt, written by --trace-summary from
     a trace of this same command) while the kernel sources still hash to the digest it
@@ -674,36 +677,34 @@ def main():
     calls = [(M, K, N, label) for M in MS for K, N, label in shapes]
     cfg_of = {c: mp.select_config(c[0], c[2], c[1], g, torch.float16) for c in calls}
     # runs of consecutive launches of one kernel at one M within a step: (kernel, [calls])
-    runs, run_starts = [], set()
-    for i, c in enumerate(calls):
+    runs = []
+    for c in calls:
         name = mp.config_name(cfg_of[c])
         if runs and runs[-1][0] == name and runs[-1][1][-1][0] == c[0]:
             runs[-1][1].append(c)
         else:
             runs.append((name, [c]))
-            run_starts.add(i)
-    run_events = []
     shape_idx = {(K, N): j for j, (K, N, _) in enumerate(shapes)}
 
-    def step(s, record):
-        evs = []
-        for i, (M, K, N, label) in enumerate(calls):
-            c = (s * len(MS) + MS.index(M)) % copies
-            if record and i in run_starts:
-                evs.append(torch.cuda.Event(enable_timing=True))
-                evs[-1].record(stream)
-            mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
-        if record:
-            evs.append(torch.cuda.Event(enable_timing=True))
+    def step(s, evs=None):
+        for r, (_, rcalls) in enumerate(runs):
+            if evs is not None:
+                evs[r].record(stream)
+            for M, K, N, label in rcalls:
+                c = (s * len(MS) + MS.index(M)) % copies
+                mp.w4a16(xs[(M, K)], pool[c][shape_idx[(K, N)]], out=ys[(M, N)])
+        if evs is not None:
             evs[-1].record(stream)
-            run_events.append(evs)
 
     for s in range(args.warmup):
-        step(s, record=False)
+        step(s)
+    # every event exists before the timed region (creating one can reach into the driver)
+    run_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(runs) + 1)]
+                  for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(args.warmup + s, record=True)
+        step(args.warmup + s, run_events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 

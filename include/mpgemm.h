@@ -131,7 +131,9 @@ int mpgemm_unpack(const void *packed_codes, const void *packed_meta, int K, int 
  * largest need of the configurations that can run M rows, and of 64-row chunks when
  * M > 64), or when a tiled kernel (M > 32) splits the K range of its tiles because the
  * grid has fewer tiles than the device has compute units (a tiled configuration forced at
- * M <= 32 runs unsplit).  The workspace holds arrival
+ * M <= 32 runs unsplit).  The 256 x 256 tile (id 14) is not counted: its partials are twice
+ * the others', and it splits only when the workspace passed holds them (the selector takes
+ * it only for grids that need no split).  The workspace holds arrival
  * counters in its first 256 KiB and fp32 partial sums after them.
  *   - It must be all zero before its first use; every call leaves the counters zero again,
  *     so one zeroed allocation serves any number of later calls.
@@ -189,26 +191,30 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * MPGEMM_ERR_UNSUPPORTED; an unknown id returns MPGEMM_ERR_INVALID_ARG).  Ids: 1..4
  * small-M kernel with 1..4 row blocks of 16 (M <= 16*id); 12 tiled large-M kernel on
  * 32x32x16 MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a
- * 256 x 128 tile.  Ids 12 and 13 take every shape.  The selector picks 1..2 for M <= 32,
- * and 3..4 for M <= 64 with N K <= 4096 * 4096; else for M <= 128 the tile whose grid (with
- * its K split, on the current device's compute units, 256 when none is current) fills more
- * units (on a tie 13 when both fill every unit or only 13 runs unsplit, else 12; 12 when 13
- * alone needs more than one round); 12 for 256 < M <= 384 with K < 16384 and for
- * M >= 2048 with N < 16384 and K < 8192; else 13.
+ * 256 x 128 tile; 14 the same with a 256 x 256 tile (4-bit codes, and 2- and 3-bit codes
+ * through their 4-bit rewrite; 8-bit and FP8 codes return MPGEMM_ERR_UNSUPPORTED).  Ids
+ * 12, 13 and 14 take every shape.  The selector picks 1..2 for M <= 32, and 3..4 for
+ * M <= 64 with N K <= 4096 * 4096; else for M <= 128 the tile whose grid (with its K split,
+ * on the current device's compute units, 256 when none is current) fills more units (on a
+ * tie 13 when both fill every unit or only 13 runs unsplit, else 12; 12 when 13 alone needs
+ * more than one round); 12 for 256 < M <= 384 with K < 16384; 14 (4-bit layouts) when its
+ * grid of 256 x 256 tiles covers at least three quarters of the compute units; 12 for
+ * M >= 2048 with N < 16384 and K < 8192; else 13.  The returned id is that of 4-bit codes;
+ * 8-bit and FP8 codes take 13 or 12 by the same rules where it says 14.
  * (2- and 3-bit codes take 1..4 for every M <= 64.)
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
 const char *mpgemm_config_name(int config_id);
 
 /*
- * Workgroup schedule of the tiled kernels (ids 12 and 13), computed on the host for
+ * Workgroup schedule of the tiled kernels (ids 12, 13 and 14), computed on the host for
  * inspection; makes no GPU call.  The pages fix no tile order: this is the library's own
  * (tiles spread over the eight XCDs in contiguous ranges, walked four M-tiles at a time;
  * a grid of fewer tiles than compute units splits every tile's K range into P parts,
  * reduced by a second kernel).  It is the schedule mpgemm_w4a16_config runs when its
  * workspace holds mpgemm_workspace_bytes() bytes on a device with `cus` compute units
- * (0: no K split).
- *   M, N, K, config_id  shape (K % 8 == 0) and id 12 or 13
+ * (0: no K split; for id 14, a workspace that holds its partials).
+ *   M, N, K, config_id  shape (K % 8 == 0) and id 12, 13 or 14
  *   cus       compute units (256 on MI355X)
  *   info      out, int[8]: grid size, tile rows, tile columns, M tiles, N tiles (over the
  *             padded N), workgroups that run a whole tile, parts per split tile (1: none),
@@ -269,7 +275,7 @@ int mpgemm_unpack_w8(const void *packed_codes, const void *packed_meta, int K, i
  * Y[M][N] = X[M][K] * dequant(W8)[K][N] with fp32 accumulation; arguments as for
  * mpgemm_w4a16, with planes written by mpgemm_pack_weights_w8.  mpgemm_w8a16_config runs
  * one configuration (ids as for mpgemm_w4a16_config: 1..4 small-M, 12 and 13 tiled
- * 32x32x16).
+ * 32x32x16; 14 returns MPGEMM_ERR_UNSUPPORTED).
  */
 int mpgemm_w8a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
                  int M, int N, int K, int group, int symmetric, void *Y, void *workspace,
@@ -346,10 +352,10 @@ int mpgemm_wfp8a16_config(const void *X, int dtype, int fp8_format, const void *
  * rewritten in the 4-bit layout in the workspace (bits: 2 and 3-bit codes are valid 4-bit
  * codes; symmetric codes shift onto the 4-bit zero 8, so every weight dequantizes to the
  * same value) and a 32x32x16 tiled kernel runs on them with the same meta plane
- * (configurations 0, 12 and 13).  That needs mpgemm_workspace_bytes_lowbit() bytes;
+ * (configurations 0, 12, 13 and 14).  That needs mpgemm_workspace_bytes_lowbit() bytes;
  * configuration 0 with less runs the small-M kernel on 64-row chunks instead (reading the
- * weights once per chunk), configurations 12 and 13 return MPGEMM_ERR_WORKSPACE.  A bits value other than 2 or 3 returns
- * MPGEMM_ERR_INVALID_ARG.
+ * weights once per chunk), configurations 12, 13 and 14 return MPGEMM_ERR_WORKSPACE.  A
+ * bits value other than 2 or 3 returns MPGEMM_ERR_INVALID_ARG.
  */
 
 /* Workspace for mpgemm_wlowbit_a16(_config): that of mpgemm_workspace_bytes, and for
