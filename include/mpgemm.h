@@ -213,7 +213,10 @@ const char *mpgemm_config_name(int config_id);
  * a grid of fewer tiles than compute units splits every tile's K range into P parts,
  * reduced by a second kernel).  It is the schedule mpgemm_w4a16_config runs when its
  * workspace holds mpgemm_workspace_bytes() bytes on a device with `cus` compute units
- * (0: no K split; for id 14, a workspace that holds its partials).
+ * (0: no K split; for id 14, a workspace that holds its partials).  One exception: where
+ * id 14's grid has a last round that would fill at most half of the units, the library
+ * runs its whole rounds over the leading columns and the rest as id 13 tiles, a second
+ * launch; the schedule shown is that of the single id-14 grid.
  *   M, N, K, config_id  shape (K % 8 == 0) and id 12, 13 or 14
  *   cus       compute units (256 on MI355X)
  *   info      out, int[8]: grid size, tile rows, tile columns, M tiles, N tiles (over the

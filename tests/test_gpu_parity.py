@@ -318,6 +318,18 @@ def test_llama3_70b_bf16_small_m(M, K, N, label):
     _full_shape(workloads.LLAMA3_70B, M, K, N)
 
 
+@pytest.mark.parametrize("wl", [workloads.LLAMA3_8B_DECODE, workloads.LLAMA3_70B,
+                                workloads.QWEN3_32B], ids=lambda w: w.name)
+def test_wide_tile_last_round_as_narrower_tiles_ragged(wl):
+    """Config 14 at M = 300, K = 384, N = 33000: 2 x 130 tiles of 256 x 256 on 256 units,
+    so one round of them over the first 32768 columns and the other 232 columns (ragged) as
+    256 x 128 tiles in a second launch, with a K that is not a multiple of the stage loop's
+    256, in each workload's format (fp16 g128 asymmetric, bf16, fp16 g64 symmetric)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split point assumes 256 compute units")
+    _full_shape(wl, 300, 384, 33000, configs=[PREFILL_X32_WIDE])
+
+
 @pytest.mark.parametrize("K,N,label", workloads.LLAMA3_70B.shapes)
 def test_llama3_70b_bf16_m4096(K, N, label):
     _full_shape(workloads.LLAMA3_70B, 4096, K, N, configs=TILED)

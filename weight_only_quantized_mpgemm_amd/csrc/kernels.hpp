@@ -48,13 +48,14 @@ struct GemmArgs {
     const uint32_t *codes;      // packed codes plane (Kp x Np matrix)
     const uint16_t *scales;     // meta plane: scales
     const uint8_t *zeros;       // meta plane: zeros (nullptr when symmetric)
-    uint16_t *Y;                // [M][N] output bits (row stride N)
+    uint16_t *Y;                // [M][N] output bits (row stride ldy, or N when 0)
     int M, N, K, group;         // user shape (K % 8 == 0)
     int Kp, Np;                 // padded shape of the packed planes
     int act;                    // Act
     int code;                   // Code: format of the packed codes
     void *workspace;            // split-K partials and counters (decode and tiled kernels)
     size_t workspace_bytes;     // its size (0 without a workspace)
+    int ldy = 0;                // Y's row stride when it is not N (a column range of Y)
 };
 
 // Both split-K schemes keep their arrival counters in the first kSplitCounterBytes of the

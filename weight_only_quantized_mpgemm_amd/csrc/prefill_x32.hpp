@@ -359,12 +359,14 @@ template <int ACT, bool SYM, int G, int NWS, int SH, int CODE, bool RAG, int MA>
 __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const uint16_t *__restrict__ X, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    int Kw, int Kx, int Ny, uint16_t *__restrict__ Y, int full, int P, float *__restrict__ part) {
+    int Kw, int Kx, int Ny, int ldy, uint16_t *__restrict__ Y, int full, int P,
+    float *__restrict__ part) {
     // N: the padded column count of the packed planes; Kw: their padded K (a multiple of
     // 128); K: the loop length, Kw rounded up to a multiple of 256 (the stage loop runs
     // blocks of four 64-deep stages; a 128-deep tile past Kw re-reads the last weight tile
     // against activations that read as zero, adding exact zeros); Kx: activation row length
-    // (the user K); Ny: output row length (the user N).
+    // (the user K); Ny: output columns (the user N); ldy: Y's row stride (Ny, or the full
+    // row of a launch that covers a column range of Y).
     // full, P, part: workgroups past the first `full` take 1/P of the K range of one tile
     // each (P consecutive workgroups per tile; P = 1: no split) and store fp32 partials in
     // `part` instead of Y.
@@ -794,7 +796,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         static_assert(HR * BN * 4 == (int)sizeof(xs), "a half tile fills the ring");
         f32x4_t *ot = reinterpret_cast<f32x4_t *>(&xs[0][0]);
         const int n_blk = nt * BN;
-        const bool aligned = (Ny & 7) == 0;
+        const bool aligned = (ldy & 7) == 0;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             if (hf == 1) __syncthreads();        // every read of the first half is done
@@ -821,7 +823,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
                 const u32x2_t lo = round4<ACT>(ot[r * CPR + ((2 * cp) ^ (r & 15))]);
                 const u32x2_t hi = round4<ACT>(ot[r * CPR + ((2 * cp + 1) ^ (r & 15))]);
                 const u32x4_t v = {lo[0], lo[1], hi[0], hi[1]};
-                uint16_t *p = Y + (size_t)m * Ny + n;
+                uint16_t *p = Y + (size_t)m * ldy + n;
                 if (aligned && n + 8 <= Ny) {
                     *reinterpret_cast<u32x4_t *>(p) = v;
                 } else {
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         __syncthreads();
         const u32x4_t *oc = &xs[0][0];
         const int n_blk = nt * BN;
-        const bool aligned = (Ny & 7) == 0;
+        const bool aligned = (ldy & 7) == 0;
 #pragma unroll
         for (int i = 0; i < BM * CPR / kXThreads; ++i) {
             const int idx = i * kXThreads + tid;
@@ -859,7 +861,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
             const int m = m_blk + r, n = n_blk + 8 * c;
             if (m >= M || n >= Ny) continue;
             const u32x4_t v = oc[r * CPR + (c ^ (r & 15))];
-            uint16_t *p = Y + (size_t)m * Ny + n;
+            uint16_t *p = Y + (size_t)m * ldy + n;
             if (aligned && n + 8 <= Ny) {
                 *reinterpret_cast<u32x4_t *>(p) = v;
             } else {
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
 // the same way.
 template <int ACT, int SH>
 __global__ __launch_bounds__(kXThreads) void x32_split_reduce_kernel(
-    const f32x4_t *__restrict__ part, int full, int P, int M, int N, int Ny,
+    const f32x4_t *__restrict__ part, int full, int P, int M, int N, int Ny, int ldy,
     uint16_t *__restrict__ Y) {
     constexpr int NB = shape_nb(SH), MB = shape_mb(SH), BM = tile_m(SH), BN = tile_n(SH);
     constexpr int kChunksPerPart = BM * BN / 4;
@@ -905,7 +907,7 @@ __global__ __launch_bounds__(kXThreads) void x32_split_reduce_kernel(
         const int i = c0 + j, nb = i / (4 * MB), mb = (i / 4) % MB, q = i % 4;
         const int n = nt * BN + wave * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
         const int m = mt * BM + mb * 32 + (lane & 31);
-        if (m < M && n < Ny) store4<ACT>(Y + (size_t)m * Ny + n, Ny - n, s);
+        if (m < M && n < Ny) store4<ACT>(Y + (size_t)m * ldy + n, Ny - n, s);
     }
 }
 
@@ -959,8 +961,9 @@ inline size_t x32_split_bytes(const X32Split &sp, int tiles, int sh) {
     return kSplitCounterBytes + (size_t)(tiles - sp.full) * sp.p * tile_m(sh) * tile_n(sh) * 4;
 }
 
+// One launch of tile shape SH over the whole of `a` (with the K split of small grids).
 template <int ACT, bool SYM, int G, int SH, int CODE, bool RAG>
-void launch_one(const GemmArgs &a, hipStream_t stream) {
+void launch_tiles(const GemmArgs &a, hipStream_t stream) {
     const int tiles = ((a.Np + tile_n(SH) - 1) / tile_n(SH)) * ((a.M + tile_m(SH) - 1) / tile_m(SH));
     const int loop_k = x32_loop_k(a.Kp);
     X32Split sp = x32_split(tiles, loop_k, RAG, device_cus());
@@ -979,7 +982,8 @@ void launch_one(const GemmArgs &a, hipStream_t stream) {
     auto run = [&](auto MA) __attribute__((always_inline)) {
         prefill_x32_kernel<ACT, SYM, G, kXWSets<G, CODE>, SH, CODE, RAG, decltype(MA)::value>
             <<<grid, dim3(kXThreads), 0, stream>>>(a.X, a.codes, a.scales, a.zeros, a.M, a.Np,
-                                                   loop_k, a.Kp, a.K, a.N, a.Y, sp.full, sp.p,
+                                                   loop_k, a.Kp, a.K, a.N, a.ldy ? a.ldy : a.N,
+                                                   a.Y, sp.full, sp.p,
                                                    part);
     };
     if constexpr (SH == 1) {
@@ -996,7 +1000,45 @@ void launch_one(const GemmArgs &a, hipStream_t stream) {
         x32_split_reduce_kernel<ACT, SH>
             <<<dim3((unsigned)(tiles - sp.full) * x32_reduce_wgs(SH)), dim3(kXThreads), 0,
                stream>>>(reinterpret_cast<const f32x4_t *>(part), sp.full, sp.p, a.M, a.Np, a.N,
-                         a.Y);
+                         a.ldy ? a.ldy : a.N, a.Y);
+}
+
+// Columns [n0, n1) of `a` (n0 a multiple of 16; n1 a multiple of 16 or a.N) as a GEMM of
+// its own: the packed planes are strip-major (a 16-column strip's codes, scales and zeros
+// are contiguous), so the range is an offset view of them and of Y, with Y's row stride.
+inline GemmArgs column_range(const GemmArgs &a, int n0, int n1, int group, int bits) {
+    GemmArgs r = a;
+    const size_t strips = (size_t)(n0 / 16), groups = (size_t)(a.Kp / group);
+    r.codes = a.codes + strips * (a.Kp / 128) * (64 * bits);     // 256 bits bytes per tile
+    r.scales = a.scales + strips * groups * 16;
+    r.zeros = a.zeros ? a.zeros + strips * groups * (16 * bits / 8) : nullptr;
+    r.Y = a.Y + n0;
+    r.ldy = a.ldy ? a.ldy : a.N;
+    r.N = (n1 < a.N ? n1 : a.N) - n0;
+    r.Np = (n1 < a.N ? n1 : a.Np) - n0;
+    return r;
+}
+
+// The 256 x 256 tile with a last round that would fill at most half of the compute units
+// runs its whole rounds over the leading columns and the remaining columns as one round of
+// 256 x 128 tiles (a second launch, no partials): the half-empty round of 256 x 256 tiles
+// took nearly a full round's time (Llama-3-8B gate_up at M = 2048: 896 tiles, 3.5 rounds).
+template <int ACT, bool SYM, int G, int SH, int CODE, bool RAG>
+void launch_one(const GemmArgs &a, hipStream_t stream) {
+    if constexpr (SH == 3) {
+        const int cus = device_cus();
+        const int tm = (a.M + 255) / 256, tn = (a.Np + 255) / 256;
+        const int rounds = cus > 0 ? tm * tn / cus : 0, rest = tm * tn - rounds * cus;
+        if (rounds > 0 && rest > 0 && 2 * rest <= cus && cus % tm == 0) {
+            const int n1 = rounds * (cus / tm) * 256;
+            launch_tiles<ACT, SYM, G, 3, CODE, RAG>(column_range(a, 0, n1, G, kCodeBits<CODE>),
+                                                    stream);
+            launch_tiles<ACT, SYM, G, 1, CODE, RAG>(column_range(a, n1, a.N, G, kCodeBits<CODE>),
+                                                    stream);
+            return;
+        }
+    }
+    launch_tiles<ACT, SYM, G, SH, CODE, RAG>(a, stream);
 }
 
 template <int ACT, int SH, int CODE, bool RAG>
