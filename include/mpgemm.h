@@ -191,16 +191,14 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * MPGEMM_ERR_UNSUPPORTED; an unknown id returns MPGEMM_ERR_INVALID_ARG).  Ids: 1..4
  * small-M kernel with 1..4 row blocks of 16 (M <= 16*id); 12 tiled large-M kernel on
  * 32x32x16 MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a
- * 256 x 128 tile; 14 the same with a 256 x 256 tile (4-bit codes, and 2- and 3-bit codes
- * through their 4-bit rewrite; 8-bit and FP8 codes return MPGEMM_ERR_UNSUPPORTED).  Ids
- * 12, 13 and 14 take every shape.  The selector picks 1..2 for M <= 32, and 3..4 for
+ * 256 x 128 tile; 14 the same with a 256 x 256 tile.  Ids 12, 13 and 14 take every
+ * shape.  The selector picks 1..2 for M <= 32, and 3..4 for
  * M <= 64 with N K <= 4096 * 4096; else for M <= 128 the tile whose grid (with its K split,
  * on the current device's compute units, 256 when none is current) fills more units (on a
  * tie 13 when both fill every unit or only 13 runs unsplit, else 12; 12 when 13 alone needs
- * more than one round); 12 for 256 < M <= 384 with K < 16384; 14 (4-bit layouts) when its
- * grid of 256 x 256 tiles covers at least three quarters of the compute units; 12 for
- * M >= 2048 with N < 16384 and K < 8192; else 13.  The returned id is that of 4-bit codes;
- * 8-bit and FP8 codes take 13 or 12 by the same rules where it says 14.
+ * more than one round); 12 for 256 < M <= 384 with K < 16384; 14 when its grid of
+ * 256 x 256 tiles covers at least three quarters of the compute units; 12 for M >= 2048
+ * with N < 16384 and K < 8192; else 13.
  * (2- and 3-bit codes take 1..4 for every M <= 64.)
  */
 int mpgemm_select_config(int M, int N, int K, int group, int dtype);
@@ -277,8 +275,8 @@ int mpgemm_unpack_w8(const void *packed_codes, const void *packed_meta, int K, i
 /*
  * Y[M][N] = X[M][K] * dequant(W8)[K][N] with fp32 accumulation; arguments as for
  * mpgemm_w4a16, with planes written by mpgemm_pack_weights_w8.  mpgemm_w8a16_config runs
- * one configuration (ids as for mpgemm_w4a16_config: 1..4 small-M, 12 and 13 tiled
- * 32x32x16; 14 returns MPGEMM_ERR_UNSUPPORTED).
+ * one configuration (ids as for mpgemm_w4a16_config: 1..4 small-M, 12, 13 and 14 tiled
+ * 32x32x16).
  */
 int mpgemm_w8a16(const void *X, int dtype, const void *packed_codes, const void *packed_meta,
                  int M, int N, int K, int group, int symmetric, void *Y, void *workspace,

@@ -146,17 +146,6 @@ def test_gemm_validation(kw, status):
     assert _gemm(**kw) == status
 
 
-def test_wide_tile_rejects_8bit_and_fp8_codes():
-    """The 256 x 256 tile (id 14) is built for 4-bit codes: the 8-bit and FP8 entry points
-    refuse it before touching any pointer."""
-    lib = mp.lib()
-    common = [ctypes.c_void_p(A), 0, ctypes.c_void_p(A), ctypes.c_void_p(A), 512, 256, 256, 128]
-    assert lib.mpgemm_w8a16_config(*common, 0, ctypes.c_void_p(A), None, 0, 14, None) == UNSUPPORTED
-    assert lib.mpgemm_wfp8a16_config(ctypes.c_void_p(A), 0, 0, ctypes.c_void_p(A),
-                                     ctypes.c_void_p(A), 512, 256, 256, 128, ctypes.c_void_p(A),
-                                     None, 0, 14, None) == UNSUPPORTED
-
-
 def test_pack_and_unpack_validation():
     lib = mp.lib()
     vp = ctypes.c_void_p

@@ -10,7 +10,7 @@ Bars as for integer codes (test_gpu_parity):
   * random inputs: max|Y - Y_ref| / max|Y_ref| <= 5e-3, Y_ref from the oracle;
   * NaN and infinite codes: the columns they reach are NaN / infinite on both sides.
 Every configuration that runs FP8 codes is forced on the cases it can run: the small-M
-kernel (ids 1..4) and the 32x32x16 tiled kernel in both tile shapes (12, 13).
+kernel (ids 1..4) and the 32x32x16 tiled kernel in every tile shape (12, 13, 14).
 """
 import numpy as np
 import pytest
@@ -24,7 +24,7 @@ from test_gpu_parity import REL_TOL, dev_half, dev_u8, host_bits, rel_err, say
 pytestmark = pytest.mark.gpu
 
 DECODE = (1, 2, 3, 4)
-TILED = (12, 13)
+TILED = (12, 13, 14)
 FORMATS = ("e4m3", "e5m2")
 ALL = np.arange(256, dtype=np.uint8)
 FINITE = {"e4m3": ALL[(ALL & 0x7F) != 0x7F], "e5m2": ALL[(ALL & 0x7C) != 0x7C]}
@@ -191,7 +191,7 @@ def test_fp8_qwen3_8b_full_shapes(fmt, M, K, N, label):
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 12), replace=False)]))
     cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 192, replace=False)]))
     want = ref(case, rows, cols)
-    cfgs = [0] + ([12, 13] if M > 64 else [])
+    cfgs = [0] + ([12, 13, 14] if M > 64 else [])
     for cfg in cfgs:
         say(f"fp8 qwen3-8b {fmt} M={M} K={K} N={N} config={cfg}")
         assert rel_err(run(case, packed, cfg, rows, cols), want, "bf16") <= REL_TOL, cfg
@@ -235,7 +235,7 @@ def test_fp8_k_a_multiple_of_128_not_256_runs_every_tiled_config(M):
     case = workloads.make_case_fp8(workloads.QWEN3_8B_FP8, M, K, N, "e4m3")
     packed = pack(case)
     want = ref(case)
-    for cfg in (0, 12, 13):
+    for cfg in (0, 12, 13, 14):
         say(f"fp8 K=384 M={M} config={cfg}")
         assert rel_err(run(case, packed, cfg), want, "bf16") <= REL_TOL, cfg
 

@@ -169,7 +169,7 @@ def test_lowbit_large_m_equals_the_4bit_gemm_of_the_same_codes_bit_for_bit(bits,
     shift = 8 - (1 << (bits - 1)) if sym else 0
     p4 = mp.pack_weights(dev_u8(codes + shift), dev_half(scales),
                          None if zeros is None else dev_u8(zeros), g)
-    for cfg in (0, 12, 13):
+    for cfg in (0, 12, 13, 14):
         y = run(x, packed, "f16", cfg)
         y4 = host_bits(mp.w4a16(dev_half(x), p4, config=cfg if cfg else 12 if M < 512 else 13))
         say(f"w{bits} vs w4 sym={sym} config={cfg}")

@@ -27,7 +27,7 @@ SHAPES = [(200, 48), (256, 40), (384, 7), (136, 1), (1000, 33), (4104, 100), (8,
 
 
 def configs(M, K, code):
-    return [c for c in (1, 2, 3, 4) if M <= 16 * c] + [12, 13] + ([14] if code == "w4" else [])
+    return [c for c in (1, 2, 3, 4) if M <= 16 * c] + [12, 13, 14]
 
 
 def make(code, K, N, g, sym, seed):

@@ -6,7 +6,7 @@ Bars as for 4-bit codes (test_gpu_parity):
     activations with power-of-two scales): bit-exact;
   * random inputs: max|Y - Y_ref| / max|Y_ref| <= 5e-3, Y_ref from the oracle.
 Every configuration that runs 8-bit codes is forced on the cases it can run: the small-M
-kernel (ids 1..4) and the 32x32x16 tiled kernel in both tile shapes (12, 13).
+kernel (ids 1..4) and the 32x32x16 tiled kernel in every tile shape (12, 13, 14).
 """
 import numpy as np
 import pytest
@@ -20,7 +20,7 @@ from test_gpu_parity import REL_TOL, dev_half, dev_u8, host_bits, rel_err, say
 pytestmark = pytest.mark.gpu
 
 DECODE = (1, 2, 3, 4)
-TILED = (12, 13)
+TILED = (12, 13, 14)
 
 
 def configs_for(M):
@@ -150,7 +150,7 @@ def test_w8_llama3_8b_full_shapes(M, K, N, label):
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 12), replace=False)]))
     cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 192, replace=False)]))
     ref = ref8(case, rows, cols)
-    cfgs = [0] + ([12, 13] if M > 64 else [])
+    cfgs = [0] + ([12, 13, 14] if M > 64 else [])
     for cfg in cfgs:
         say(f"w8 8B M={M} K={K} N={N} config={cfg}")
         assert rel_err(run8(case, packed, cfg, rows, cols), ref, "f16") <= REL_TOL, cfg
@@ -166,7 +166,7 @@ def test_w8_k_a_multiple_of_128_not_256_runs_every_tiled_config(M):
                 zeros=zeros, group=128, dtype="f16")
     packed = pack8(case)
     want = ref8(case)
-    for cfg in (0, 12, 13):
+    for cfg in (0, 12, 13, 14):
         say(f"w8 K=384 M={M} config={cfg}")
         assert rel_err(run8(case, packed, cfg), want, "f16") <= REL_TOL, cfg
 

@@ -28,7 +28,7 @@ enum ConfigId {
     kConfigDecode4 = 4,
     kConfigPrefillX32 = 12,    // 32x32x16 kernel, 128 x 256 workgroup tile
     kConfigPrefillX32Tall = 13,  // same, 256 x 128 workgroup tile
-    kConfigPrefillX32Wide = 14,  // same, 256 x 256 workgroup tile (4-bit codes)
+    kConfigPrefillX32Wide = 14,  // same, 256 x 256 workgroup tile
 };
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -110,13 +110,13 @@ bool wide_fills(int M, int N, int K) {
     return 4 * tiles >= 3 * (int64_t)cus;
 }
 
-int select_config(int M, int N, int K, bool wide_ok = true) {
+int select_config(int M, int N, int K) {
     if (M <= 16) return kConfigDecode1;
     const int64_t nk = (int64_t)N * K;
     if (M <= 32 || (M <= 64 && nk <= 4096 * 4096)) return (M + 15) / 16;
     if (M <= 128) return pick_tile(M, N, K);
     if (M > 256 && M <= 384 && K < 16384) return kConfigPrefillX32;
-    if (wide_ok && wide_fills(M, N, K)) return kConfigPrefillX32Wide;
+    if (wide_fills(M, N, K)) return kConfigPrefillX32Wide;
     if (M >= 2048 && N < 16384 && K < 8192) return kConfigPrefillX32;
     return kConfigPrefillX32Tall;
 }
@@ -154,11 +154,6 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     if (config_id != kConfigSelect &&
         !((config_id >= kConfigDecode1 && config_id <= kConfigDecode4) || tiled_config(config_id)))
         return MPGEMM_ERR_INVALID_ARG;
-    // The 256 x 256 tile is built for 4-bit codes (and the 2- and 3-bit ones, which reach the
-    // tiled kernels rewritten in the 4-bit layout).
-    if (config_id == kConfigPrefillX32Wide && code != mpgemm::kU4 && code != mpgemm::kU2 &&
-        code != mpgemm::kU3)
-        return MPGEMM_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return MPGEMM_OK;
     if (Y == nullptr) return MPGEMM_ERR_INVALID_ARG;
     if (!aligned16(Y)) return MPGEMM_ERR_ALIGNMENT;
@@ -172,10 +167,9 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     // 2- and 3-bit codes reach the tiled kernels only through the 4-bit rewrite (M > 64):
     // up to 64 rows they take the strip kernel at every N.
     const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
-    const bool four_bit_layout = code == mpgemm::kU4 || lowbit;
     const int cfg = config_id != kConfigSelect ? config_id
                     : lowbit && M <= 64     ? (M + 15) / 16
-                                            : select_config(M, N, K, four_bit_layout);
+                                            : select_config(M, N, K);
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
     const int Kp = mpgemm::padded_k(K);

@@ -4,12 +4,21 @@
 
 namespace mpgemm {
 
-hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int sh, hipStream_t stream) {
-    if (sh == 3) return hipErrorInvalidValue;          // the 256 x 256 tile: 4-bit codes only
-    if (a.code == kE5M2)
-        sh == 1 ? launch_x32<1, kE5M2>(a, stream) : launch_x32<2, kE5M2>(a, stream);
+template <int CODE>
+void by_shape(const GemmArgs &a, int sh, hipStream_t stream) {
+    if (sh == 1)
+        launch_x32<1, CODE>(a, stream);
+    else if (sh == 2)
+        launch_x32<2, CODE>(a, stream);
     else
-        sh == 1 ? launch_x32<1, kE4M3>(a, stream) : launch_x32<2, kE4M3>(a, stream);
+        launch_x32<3, CODE>(a, stream);
+}
+
+hipError_t launch_prefill_x32_fp8(const GemmArgs &a, int sh, hipStream_t stream) {
+    if (a.code == kE5M2)
+        by_shape<kE5M2>(a, sh, stream);
+    else
+        by_shape<kE4M3>(a, sh, stream);
     return hipGetLastError();
 }
 

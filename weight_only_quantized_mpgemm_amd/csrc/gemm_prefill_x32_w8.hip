@@ -5,8 +5,12 @@
 namespace mpgemm {
 
 hipError_t launch_prefill_x32_u8(const GemmArgs &a, int sh, hipStream_t stream) {
-    if (sh == 3) return hipErrorInvalidValue;          // the 256 x 256 tile: 4-bit codes only
-    sh == 1 ? launch_x32<1, kU8>(a, stream) : launch_x32<2, kU8>(a, stream);
+    if (sh == 1)
+        launch_x32<1, kU8>(a, stream);
+    else if (sh == 2)
+        launch_x32<2, kU8>(a, stream);
+    else
+        launch_x32<3, kU8>(a, stream);
     return hipGetLastError();
 }
 

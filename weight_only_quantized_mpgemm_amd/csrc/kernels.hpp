@@ -76,8 +76,7 @@ size_t decode_workspace_bytes(int M, int N, int K, int group, int mblocks);
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream);
 // The 32x32x16 kernel with a 256 (m) x 128 (n) workgroup tile.
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream);
-// The 32x32x16 kernel with a 256 (m) x 256 (n) workgroup tile (4-bit codes only;
-// hipErrorInvalidValue for the others).
+// The 32x32x16 kernel with a 256 (m) x 256 (n) workgroup tile.
 hipError_t launch_prefill_x32_wide(const GemmArgs &a, hipStream_t stream);
 // Their instantiations per code format, one translation unit each (sh: tile shape, 1 for
 // 256 x 128, 2 for 128 x 256, 3 for 256 x 256).
