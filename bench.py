@@ -18,8 +18,9 @@ Timing.
     inside the timed steps, on the stream the library launches on, around each run of
     consecutive launches of one kernel (the four GEMMs of one M, or fewer where the
     selector changes kernel), divided by the launches in it.  Every event is created
-    before the timed region: creating them inside it let single stalls of 40-70 ms into
-    the 20-step window on some boxes.  `roofline` uses them for the dominant kernel; it also carries the
+    before the timed region (creating them inside it let single stalls of 40-70 ms into
+    the 20-step window on some boxes), with hipEventDisableSystemFence: a default event's
+    system-scope release made the kernel after it wait for a cache writeback.  `roofline` uses them for the dominant kernel; it also carries the
     average launch duration of the same kernel in the committed rocprofv3 kernel trace
     (profiles/w4a16_llama3_8b_m1_16_2048_kernel_trace.txt, written by --trace-summary from
     a trace of this same command) while the kernel sources still hash to the digest it
@@ -164,6 +165,16 @@ def log(msg):
 
 # ------------------------------------------------------------------ rocprofv3 summary --
 
+def launches_of_call(mp, M, K, N):
+    """GEMM kernel launches of one mpgemm_w4a16 call the selector makes at this shape on
+    MI355X's 256 compute units (two where the 256 x 256 tile runs its last round's columns
+    as 256 x 128 tiles)."""
+    cfg = mp.select_config(M, N, K, 128, __import__("torch").float16)
+    if cfg < 12:
+        return 1
+    return mp.prefill_launches(M, N, K, cfg, 256)[0]
+
+
 def trace_summary(csv_path, out_path, steps, warmup, cmd):
     """Writes the kernel-trace summary bench.py's roofline reads: the GEMM kernels'
     dispatches of the timed steps (12 per step, after `warmup` steps) of a rocprofv3
@@ -174,16 +185,23 @@ def trace_summary(csv_path, out_path, steps, warmup, cmd):
     gemm = [r for r in rows if "decode_kernel" in r["Kernel_Name"] or
             "prefill_x32_kernel" in r["Kernel_Name"]]
     calls = [(M, K, N) for M in MS for K, N, _ in LLAMA_SHAPES]
-    first = warmup * len(calls)
-    timed = gemm[first:first + steps * len(calls)]
-    assert len(timed) == steps * len(calls), (len(gemm), first, steps)
+    per_step = sum(launches_of_call(mp, M, K, N) for M, K, N in calls)
+    first = warmup * per_step
+    timed = gemm[first:first + steps * per_step]
+    assert len(timed) == steps * per_step, (len(gemm), first, steps)
     per_kernel, per_gemm = {}, {}
-    for i, r in enumerate(timed):
-        M, K, N = calls[i % len(calls)]
-        name = mp.config_name(mp.select_config(M, N, K, 128, __import__("torch").float16))
-        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-        per_kernel.setdefault(name, []).append(d)
-        per_gemm.setdefault((name, M, K, N), []).append(d)
+    i = 0
+    for _ in range(steps):
+        for M, K, N in calls:
+            n = launches_of_call(mp, M, K, N)
+            rs = timed[i:i + n]
+            i += n
+            name = mp.config_name(mp.select_config(M, N, K, 128, __import__("torch").float16))
+            # a call of two launches (the 256 x 256 tile's last round as 256 x 128 tiles):
+            # first start to last end, one call
+            d = (int(rs[-1]["End_Timestamp"]) - int(rs[0]["Start_Timestamp"])) / 1000.0
+            per_kernel.setdefault(name, []).append(d)
+            per_gemm.setdefault((name, M, K, N), []).append(d)
     stats = {}
     for r in rows:
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
@@ -194,7 +212,8 @@ def trace_summary(csv_path, out_path, steps, warmup, cmd):
         fh.write(f"# source_digest: {kernel_source_digest()}\n")
         fh.write(f"# timed steps only ({steps} steps after {warmup} warmup); durations = "
                  "End-Start per dispatch\n\n")
-        fh.write("## per kernel (the figure bench.py's roofline uses: average launch duration)\n")
+        fh.write("## per kernel (the figure bench.py's roofline uses: average launch duration; a "
+                 "call that runs two launches counts once, first start to last end)\n")
         fh.write(f"{'kernel':24s} {'launches':>9s} {'avg_us':>10s}\n")
         for k, v in sorted(per_kernel.items()):
             fh.write(f"{k:24s} {len(v):9d} {sum(v) / len(v):10.3f}\n")
@@ -241,12 +260,16 @@ def traffic_summary(fetch_csv, write_csv, out_path, steps, warmup, cmds):
         cal = next(v for n, v in disp if "copyBuffer" in n or "copy" in n.lower())
         factors.append(true_kib / cal)
         gemm = [v for n, v in disp if "decode_kernel" in n or "prefill_x32_kernel" in n]
-        first = warmup * len(calls)
-        timed = gemm[first:first + steps * len(calls)]
-        assert len(timed) == steps * len(calls), (counter, len(gemm))
-        t = {}
-        for i, v in enumerate(timed):
-            t.setdefault(calls[i % len(calls)], []).append(v)
+        per_step = sum(launches_of_call(mp, M, K, N) for M, K, N in calls)
+        first = warmup * per_step
+        timed = gemm[first:first + steps * per_step]
+        assert len(timed) == steps * per_step, (counter, len(gemm))
+        t, i = {}, 0
+        for _ in range(steps):
+            for c in calls:
+                n = launches_of_call(mp, *c)
+                t.setdefault(c, []).append(sum(timed[i:i + n]))    # the call's launches
+                i += n
         tables.append({k: sum(v) / len(v) for k, v in t.items()})
         tables[-1]["_cal"] = cal
     with open(out_path, "w") as fh:
@@ -359,14 +382,22 @@ def counters_workload(lib_path):
     torch.cuda.synchronize()
     del src, dst
     pools = {}
+    # after every call, a marker (a fill of int16 zeros, a kernel nothing else launches here):
+    # the summary adds up the kernels between two markers as one call (a call can run two
+    # launches, e.g. the 256 x 256 tile's last round as 256 x 128 tiles)
+    mark = torch.empty(1, dtype=torch.int16, device=dev)
     for M, K, N in COUNTER_SHAPES:
         if (K, N) not in pools:
             pools[(K, N)] = make_pool(mp, torch, dev, Spec(M=1, K=K, N=N, label="counters"))
         pool = pools[(K, N)]
         x = torch.randn(M, K, device=dev).half()
         y = torch.empty(M, N, device=dev, dtype=torch.float16)
+        mark.fill_(7)
+        torch.cuda.synchronize()
         for i in range(1 + COUNTER_REPS):
             mp.w4a16(x, pool[i % len(pool)], out=y)
+            torch.cuda.synchronize()
+            mark.fill_(7)
             torch.cuda.synchronize()
         log(f"counters: M={M} K={K} N={N} x {COUNTER_REPS}")
 
@@ -401,16 +432,27 @@ def counters_summary(runs, out_path):
         ids = sorted(table)
         cal = next(d for d in ids if "copy" in table[d][0].lower())
         factor = (1 << 20) / table[cal][3]["FETCH_SIZE"]
-        gemm = [d for d in ids if "decode_kernel" in table[d][0] or "prefill_x32_kernel" in table[d][0]]
+        # calls: the GEMM kernels between two markers (int16 fills), in order
+        calls, cur, started = [], [], False
+        for d in ids[ids.index(cal) + 1:]:
+            name = table[d][0]
+            if "FillFunctor<short>" in name:
+                if started and cur:
+                    calls.append(cur)
+                cur, started = [], True
+            elif started and ("decode_kernel" in name or "prefill_x32_kernel" in name):
+                cur.append(d)
         per = 1 + COUNTER_REPS
-        assert len(gemm) == per * len(COUNTER_SHAPES), (label, len(gemm))
+        assert len(calls) == per * len(COUNTER_SHAPES), (label, len(calls))
         lines += ["", f"## {label}", f"# command: {cmd}", f"# FETCH_SIZE calibration factor {factor:.4f}",
                   "# kernel                  M      K      N   dur_us  clk_GHz  mfma_busy  waves"
                   "   VALU/wave  VALU_M  wait_cyc/wave  fetch_MB  fetch/alg"]
         for i, (M, K, N) in enumerate(COUNTER_SHAPES):
-            ds = gemm[i * per + 1:(i + 1) * per]
-            avg = {c: sum(table[d][3].get(c, 0.0) for d in ds) / len(ds) for c in COUNTERS}
-            dur = sum(table[d][2] - table[d][1] for d in ds) / len(ds)          # ns
+            cs = calls[i * per + 1:(i + 1) * per]
+            ds = [d for c in cs for d in c]
+            avg = {c: sum(table[d][3].get(c, 0.0) for d in ds) / len(cs) for c in COUNTERS}
+            # a call's duration: first start to last end of its kernels
+            dur = sum(table[c[-1]][2] - table[c[0]][1] for c in cs) / len(cs)      # ns
             gui = avg["GRBM_GUI_ACTIVE"] / 8
             clk = gui / dur
             mfma = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024) if gui else 0.0
@@ -460,6 +502,46 @@ def make_pool(mp, torch, dev, spec, min_copies=3):
         sc.uniform_(spec.scale_lo, spec.scale_hi)
         pool.append(mp.PackedWeights(codes, meta, K, N, g, spec.sym, bits, fp8))
     return pool
+
+
+class TimingEvent:
+    """A HIP event made with hipEventDisableSystemFence, for the timed steps' run
+    boundaries: recording it skips the system-scope release (a cache writeback) that a
+    default event performs, which the next kernel would otherwise wait for.  The events
+    only time work that torch.cuda.synchronize() has already waited for."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self.ev = ctypes.c_void_p()
+        st = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                      self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream):
+        st = TimingEvent._hip.hipEventRecord(self.ev, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_ms(self, later):
+        ms = ctypes.c_float()
+        st = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, later.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.ev:
+            TimingEvent._hip.hipEventDestroy(self.ev)
 
 
 def time_cold(torch, stream, launch, n):
@@ -699,7 +781,7 @@ def main():
     for s in range(args.warmup):
         step(s)
     # every event exists before the timed region (creating one can reach into the driver)
-    run_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(runs) + 1)]
+    run_events = [[TimingEvent() for _ in range(len(runs) + 1)]
                   for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -715,7 +797,7 @@ def main():
     # per kernel: total event time over the timed steps, launches, flops and bytes
     per_cfg = {}
     for r, (name, rcalls) in enumerate(runs):
-        t = sum(evs[r].elapsed_time(evs[r + 1]) * 1e-3 for evs in run_events)
+        t = sum(evs[r].elapsed_ms(evs[r + 1]) * 1e-3 for evs in run_events)
         agg = per_cfg.setdefault(name, {"t": 0.0, "flops": 0, "bytes": 0, "n": 0, "calls": [],
                                         "bound": "hbm" if rcalls[0][0] <= 64 else "mfma"})
         agg["t"] += t

@@ -227,6 +227,17 @@ const char *mpgemm_config_name(int config_id);
  */
 int mpgemm_prefill_schedule(int M, int N, int K, int config_id, int cus, int *info, int *work,
                             int capacity);
+
+/*
+ * Kernel launches one call of a tiled configuration (ids 12, 13, 14) makes on a device with
+ * `cus` compute units, computed on the host for inspection (profilers list launches, not
+ * calls); makes no GPU call.  1, or 2 where id 14 runs its last round's columns as id 13
+ * tiles (the exception mpgemm_prefill_schedule describes); a K split's reduction kernel is
+ * not counted.  *split_column (may be NULL): the first column of the second launch, or N.
+ * Returns MPGEMM_ERR_INVALID_ARG for a non-positive size, negative cus or another id,
+ * MPGEMM_ERR_UNSUPPORTED for shapes mpgemm_w4a16 rejects.
+ */
+int mpgemm_prefill_launches(int M, int N, int K, int config_id, int cus, int *split_column);
 int mpgemm_w4a16_config(const void *X, int dtype, const void *packed_codes,
                         const void *packed_meta, int M, int N, int K, int group, int symmetric,
                         void *Y, void *workspace, size_t workspace_bytes, int config_id,

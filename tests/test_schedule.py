@@ -106,3 +106,32 @@ def test_schedule_rejects_bad_arguments():
         assert lib.mpgemm_prefill_schedule(*args, info.data_ptr(), None, 0) == -1
     assert lib.mpgemm_prefill_schedule(64, 64, 64, 12, 256, None, None, 0) == -1
     assert lib.mpgemm_prefill_schedule(64, 64, 68, 12, 256, info.data_ptr(), None, 0) == -2
+
+
+def test_wide_tile_runs_a_half_empty_last_round_as_narrower_tiles():
+    # 8 x 112 = 896 tiles of 256 x 256 on 256 units: three rounds over 24576 columns, the
+    # other 4096 as one round of 256 x 128 tiles
+    assert mp.prefill_launches(2048, 28672, 4096, 14) == (2, 24576)
+    # 16 x 40 = 640 (Llama-3-70B QKV at M = 4096): two rounds over 8192 columns
+    assert mp.prefill_launches(4096, 10240, 8192, 14) == (2, 8192)
+    # whole rounds, a last round more than half full, or no whole round: one launch
+    assert mp.prefill_launches(8192, 28672, 4096, 14) == (1, 28672)     # 14 rounds
+    assert mp.prefill_launches(2048, 6144, 4096, 14) == (1, 6144)       # 192 tiles
+    assert mp.prefill_launches(1024, 28672, 4096, 14) == (1, 28672)     # 448: 1.75 rounds
+    # units that the tile rows do not divide: one launch
+    assert mp.prefill_launches(2048, 28672, 4096, 14, cus=304) == (1, 28672)
+    # the other tiles always launch once
+    for cfg in (12, 13):
+        assert mp.prefill_launches(2048, 28672, 4096, cfg) == (1, 28672)
+    # the split column falls on whole tiles and leaves whole tile rows for one more round
+    rng = random.Random(5)
+    for _ in range(2000):
+        M, N = rng.randint(1, 20000), rng.randint(1, 4000) * 16
+        n, col = mp.prefill_launches(M, N, 4096, 14)
+        tm, tn = -(-M // 256), -(-N // 256)
+        if n == 2:
+            assert col % 256 == 0 and 0 < col < N
+            assert tm * (col // 256) % 256 == 0                       # whole rounds
+            assert 0 < 2 * tm * (-(-(N - col) // 256)) <= 256         # at most half a round
+        else:
+            assert col == N

@@ -45,6 +45,7 @@ SIGNATURES = {
     "mpgemm_w4a16": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "mpgemm_select_config": (_i, [_i, _i, _i, _i, _i]),
     "mpgemm_config_name": (ctypes.c_char_p, [_i]),
+    "mpgemm_prefill_launches": (_i, [_i, _i, _i, _i, _i, _vp]),
     "mpgemm_prefill_schedule": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i]),
     "mpgemm_w4a16_config": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i,
                                  _vp]),
@@ -323,6 +324,15 @@ def prefill_schedule(M: int, N: int, K: int, config_id: int, cus: int = 256):
            "mpgemm_prefill_schedule")
     keys = ("grid", "tile_m", "tile_n", "tiles_m", "tiles_n", "full", "parts", "loop_k")
     return dict(zip(keys, info.tolist())), work
+
+
+def prefill_launches(M: int, N: int, K: int, config_id: int, cus: int = 256):
+    """(kernel launches, first column of the second launch or N) of one call of a tiled
+    configuration, computed on the host."""
+    col = ctypes.c_int(0)
+    n = lib().mpgemm_prefill_launches(M, N, K, config_id, cus, ctypes.addressof(col))
+    _check(min(n, 0), "mpgemm_prefill_launches")
+    return n, col.value
 
 
 class WorkspaceCache:

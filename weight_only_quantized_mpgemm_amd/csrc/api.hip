@@ -673,6 +673,15 @@ int mpgemm_prefill_schedule(int M, int N, int K, int config_id, int cus, int *in
     return mpgemm::x32_schedule(M, N, K, sh, cus, info, work, capacity);
 }
 
+int mpgemm_prefill_launches(int M, int N, int K, int config_id, int cus, int *split_column) {
+    if (M <= 0 || N <= 0 || K <= 0 || cus < 0) return MPGEMM_ERR_INVALID_ARG;
+    if (!tiled_config(config_id)) return MPGEMM_ERR_INVALID_ARG;
+    if (const int st = check_shape(M, N, K, 128)) return st;
+    const int n1 = config_id == kConfigPrefillX32Wide ? mpgemm::x32_wide_split_column(M, N, cus) : 0;
+    if (split_column) *split_column = n1 ? n1 : N;
+    return n1 ? 2 : 1;
+}
+
 const char *mpgemm_config_name(int config_id) {
     switch (config_id) {
         case kConfigDecode1: return "decode_splitk_m16";

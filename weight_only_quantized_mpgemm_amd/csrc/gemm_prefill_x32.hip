@@ -71,6 +71,8 @@ int x32_schedule(int M, int N, int K, int sh, int cus, int *info, int *work, int
     return grid;
 }
 
+int x32_wide_split_column(int M, int N, int cus) { return wide_split_column(M, padded_n(N), cus); }
+
 hipError_t launch_prefill_x32(const GemmArgs &a, hipStream_t stream) { return by_code(a, 2, stream); }
 hipError_t launch_prefill_x32_tall(const GemmArgs &a, hipStream_t stream) {
     return by_code(a, 1, stream);

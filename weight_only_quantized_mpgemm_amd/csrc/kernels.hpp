@@ -101,6 +101,9 @@ int x32_grid(int M, int N, int K, int sh, int *parts, int *cus);
 // Workgroup schedule of a 32x32x16 launch in tile shape sh (host only):
 // info[8] and work[4 grid] as mpgemm_prefill_schedule documents; returns the grid size.
 int x32_schedule(int M, int N, int K, int sh, int cus, int *info, int *work, int capacity);
+// The 256 x 256 kernel on `cus` compute units: the first column it leaves to a second launch
+// of 256 x 128 tiles (its last round's columns), or 0 when it runs in one launch.  N: user N.
+int x32_wide_split_column(int M, int N, int cus);
 
 // Decode attention over an 8-bit KV cache (attention.hip).
 struct AttnArgs {

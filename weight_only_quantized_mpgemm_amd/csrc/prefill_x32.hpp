@@ -1023,14 +1023,20 @@ inline GemmArgs column_range(const GemmArgs &a, int n0, int n1, int group, int b
 // runs its whole rounds over the leading columns and the remaining columns as one round of
 // 256 x 128 tiles (a second launch, no partials): the half-empty round of 256 x 256 tiles
 // took nearly a full round's time (Llama-3-8B gate_up at M = 2048: 896 tiles, 3.5 rounds).
+// The first column of the 256 x 128 launch (0: one launch), for M rows, Np padded columns
+// and `cus` compute units.
+inline int wide_split_column(int M, int Np, int cus) {
+    const int tm = (M + 255) / 256, tn = (Np + 255) / 256;
+    const int rounds = cus > 0 ? tm * tn / cus : 0, rest = tm * tn - rounds * cus;
+    if (rounds > 0 && rest > 0 && 2 * rest <= cus && cus % tm == 0)
+        return rounds * (cus / tm) * 256;
+    return 0;
+}
+
 template <int ACT, bool SYM, int G, int SH, int CODE, bool RAG>
 void launch_one(const GemmArgs &a, hipStream_t stream) {
     if constexpr (SH == 3) {
-        const int cus = device_cus();
-        const int tm = (a.M + 255) / 256, tn = (a.Np + 255) / 256;
-        const int rounds = cus > 0 ? tm * tn / cus : 0, rest = tm * tn - rounds * cus;
-        if (rounds > 0 && rest > 0 && 2 * rest <= cus && cus % tm == 0) {
-            const int n1 = rounds * (cus / tm) * 256;
+        if (const int n1 = wide_split_column(a.M, a.Np, device_cus())) {
             launch_tiles<ACT, SYM, G, 3, CODE, RAG>(column_range(a, 0, n1, G, kCodeBits<CODE>),
                                                     stream);
             launch_tiles<ACT, SYM, G, 1, CODE, RAG>(column_range(a, n1, a.N, G, kCodeBits<CODE>),
