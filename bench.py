@@ -451,8 +451,9 @@ def counters_summary(runs, out_path):
             cs = calls[i * per + 1:(i + 1) * per]
             ds = [d for c in cs for d in c]
             avg = {c: sum(table[d][3].get(c, 0.0) for d in ds) / len(cs) for c in COUNTERS}
-            # a call's duration: first start to last end of its kernels
-            dur = sum(table[c[-1]][2] - table[c[0]][1] for c in cs) / len(cs)      # ns
+            # a call's duration: its kernels' durations added (counter collection serializes
+            # the launches of a call with gaps of its own between them)
+            dur = sum(table[d][2] - table[d][1] for d in ds) / len(cs)             # ns
             gui = avg["GRBM_GUI_ACTIVE"] / 8
             clk = gui / dur
             mfma = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024) if gui else 0.0
