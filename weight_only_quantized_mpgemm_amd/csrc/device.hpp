@@ -14,6 +14,7 @@ namespace mpgemm {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -132,10 +133,11 @@ __device__ __forceinline__ u32x4_t dequant_word_bf16_biased(uint32_t w) {
 __device__ __forceinline__ float ubyte(uint32_t v, int b) {
     return (float)((v >> (8 * b)) & 0xFFu);
 }
+// Two fp32 values rounded to bf16 (nearest even), lo in the low half.  Converted as one
+// vector, so the compiler emits a single two-source v_cvt_pk_bf16_f32; two scalar casts
+// became two conversions, a shift and an OR.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo;
-    const __bf16 b = (__bf16)hi;
-    return (uint32_t)bitcast<uint16_t>(a) | ((uint32_t)bitcast<uint16_t>(b) << 16);
+    return bitcast<uint32_t>(__builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 __device__ __forceinline__ u32x4_t dequant_word_bf16(uint32_t w, float s, float nzs) {
     const uint32_t lo = w & 0x0F0F0F0Fu;

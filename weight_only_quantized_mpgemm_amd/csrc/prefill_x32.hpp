@@ -653,17 +653,22 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // next tile's word 0 when H == 1).  Stage 2t loads tile t + NWS - 1, except in the
     // final four stages (LAST), whose weight loads nothing would read.
     // The wait: vmcnt counts a wave's loads in issue order, and after its DMA of stage
-    // st+1 the wave issued at least the MB loads of its DMA of stage st+2 (DMAs write LDS,
-    // so the compiler neither moves them across the barrier nor drops them); leaving at
-    // most MB loads in flight therefore finds stage st+1 in LDS.  The weight loads are not
-    // counted: the compiler may move them (their memory never changes) or drop them when
-    // dead, as in the final stages, which therefore issue none.
-    auto stage = [&](int st, auto BUF, auto H, auto TW, auto LOADW) __attribute__((always_inline)) {
+    // st+1 (step 0 of stage st-2) the wave issued at least the MB loads of its DMA of stage
+    // st+2 (DMAs write LDS, so the compiler neither moves them across the barrier nor drops
+    // them); leaving at most MB loads in flight therefore finds stage st+1 in LDS.  One of
+    // stages st-2 and st-1 loaded a weight tile in its step 1, after that DMA: WBEHIND
+    // says so, and the wait then also leaves those kWLoads loads in flight, so a weight
+    // tile has until two stages later to land instead of one step.  The prologue's weight
+    // loads are not counted (the compiler has moved them past its barrier), so the first
+    // stage of a block that can follow it does not pass WBEHIND; nor do the final stages,
+    // which issue no weight loads (the compiler would drop them as dead).  The build walks
+    // every launch path of the generated code and fails if a wait could pass early.
+    auto stage = [&](int st, auto BUF, auto H, auto TW, auto LOADW, auto WBEHIND) __attribute__((always_inline)) {
         constexpr int buf = decltype(BUF)::value, h = decltype(H)::value, tw = decltype(TW)::value;
         constexpr int nbuf = (buf + 1) % kXStages, nw = (tw + 1) % NWS;
         constexpr bool loadw = decltype(LOADW)::value != 0;
         const int t = st >> 1;
-        wait_vm_barrier<MB>();
+        wait_vm_barrier<MB + (decltype(WBEHIND)::value ? kWLoads : 0)>();
         // The next stage's DMA (MB blocks) and, in the first half of a tile, the weight
         // loads of tile t + NWS - 1 go out one at a time between MFMAs, in the same order
         // as before, instead of as one burst per wave at the barrier.
@@ -705,15 +710,16 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         }
     };
     // Stages st .. st+3 (tiles 2u, 2u+1 of a 2 * NWS-stage block, u = 0 or 1); LAST: the
-    // kernel's final four stages.
+    // kernel's final four stages.  Stage st follows the prologue or a stage that loaded
+    // weights two stages back: only the second four of a block (u = 1) always does.
     auto four = [&](int st, auto U, auto LAST) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
         constexpr bool last = decltype(LAST)::value != 0;
         constexpr int lw = last ? 0 : 1;
-        stage(st + 0, IC<0>(), IC<0>(), IC<(2 * u) % NWS>(), IC<lw>());
-        stage(st + 1, IC<1>(), IC<1>(), IC<(2 * u) % NWS>(), IC<lw>());
-        stage(st + 2, IC<2>(), IC<0>(), IC<(2 * u + 1) % NWS>(), IC<lw>());
-        stage(st + 3, IC<3>(), IC<1>(), IC<(2 * u + 1) % NWS>(), IC<lw>());
+        stage(st + 0, IC<0>(), IC<0>(), IC<(2 * u) % NWS>(), IC<lw>(), IC<u>());
+        stage(st + 1, IC<1>(), IC<1>(), IC<(2 * u) % NWS>(), IC<lw>(), IC<lw>());
+        stage(st + 2, IC<2>(), IC<0>(), IC<(2 * u + 1) % NWS>(), IC<lw>(), IC<lw>());
+        stage(st + 3, IC<3>(), IC<1>(), IC<(2 * u + 1) % NWS>(), IC<lw>(), IC<lw>());
     };
 
     // Prologue: stages 0..2 in flight, tiles 0 .. NWS-2, then stage 0's first operands.
