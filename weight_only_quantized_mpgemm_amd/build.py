@@ -145,6 +145,23 @@ def stage_wait_violations(seq: list[str], mb: int) -> list[tuple]:
     return bad
 
 
+def ring_shape(name: str) -> tuple[int, int | None]:
+    """(ring stages, DMA loads per wave and stage) of a 32x32x16 tiled kernel, from its
+    template arguments <ACT, SYM, G, NWS, SH, CODE, RAG, MA>: tiles whose live row blocks
+    MA fill less than the tile (one row of tiles; not the 256 x 256 tile), with four weight
+    register sets, keep only those rows in an eight-stage ring, the others all rows in four
+    stages."""
+    args = re.search(r"prefill_x32_kernelI((?:L[ib]\d+E){8})E", name)
+    if args is None:                     # no template arguments: a four-stage ring
+        return 4, None
+    vals = [int(v) for v in re.findall(r"L[ib](\d+)E", args.group(1))]
+    nws, sh, ma = vals[3], vals[4], vals[7]
+    mb = {1: 8, 2: 4, 3: 8}[sh]
+    if sh != 3 and ma < mb and nws == 4:
+        return 8, ma
+    return 4, mb
+
+
 def ring_wait_violations(asm: str) -> list[tuple[str, str, list]]:
     """Checks every 32x32x16 tiled kernel's stage waits along the paths a launch takes:
     prologue, then the stage loop once and twice, then (four-weight-set kernels) the
@@ -156,8 +173,12 @@ def ring_wait_violations(asm: str) -> list[tuple[str, str, list]]:
         lines = _path_lines(asm, name)
         lab = {ln[:-1]: i for i, ln in enumerate(lines) if re.match(r"\.LBB\w+:$", ln)}
         b0 = next(i for i, ln in enumerate(lines) if ln.startswith("s_barrier"))
-        # DMA loads per stage and wave: the prologue issues three stages
-        mb = sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // 3
+        # DMA loads per stage and wave: the prologue issues all stages of the ring but one
+        xs, dmb = ring_shape(name)
+        mb = sum(1 for ln in lines[:b0] if ln.startswith("buffer_load") and " lds" in ln) // (xs - 1)
+        if dmb is not None and mb != dmb:
+            out.append((name, "prologue", [(-1, mb, dmb)]))
+            continue
         br = next(i for i in range(b0, len(lines)) if lines[i].startswith("s_cbranch"))
         skip = lines[br].split()[1]
         top = next(i for i in range(br + 1, len(lines)) if re.match(r"\.LBB\w+:$", lines[i]))

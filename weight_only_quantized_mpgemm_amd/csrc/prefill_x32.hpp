@@ -61,7 +61,7 @@ namespace {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kXThreads = 256;
-constexpr int kXStages = 4;                  // 64-deep LDS stages in the ring
+constexpr int kXStages = 4;                  // 64-deep LDS stages in the ring (eight at small M)
 // Workgroup tile shapes SH: 1 = 256 (m) x 128 (n), 2 = 128 x 256, 3 = 256 x 256.  Each of
 // the four waves owns shape_nb(SH) 32-column blocks of shape_mb(SH) 32-row blocks.
 constexpr int shape_nb(int sh) { return sh == 1 ? 1 : 2; }
@@ -80,6 +80,20 @@ template <int N>
 struct IC {
     static constexpr int value = N;
 };
+
+// Loads a stage's wait may leave in flight: every load the wave issued after the DMA of
+// the stage after it.  That DMA went out in step 0 of stage st + 2 - XS (DMAs run XS - 1
+// stages ahead); after it came the weight loads of that stage's step 1, and all loads of
+// the XS - 3 stages in between: their DMAs (DMB each) and, in the even stages of a pass
+// that loads weights (LW), kWLoads weight loads.  Only stages of the same pass of the
+// stage loop are counted (KB: the stage's place in the pass): the pass may follow the
+// prologue, whose weight loads the compiler moves past its barrier.
+constexpr int stage_wait_loads(int xs, int dmb, int wloads, int kb, bool lw) {
+    int n = (xs - 3) * dmb;
+    for (int j = kb + 2 - xs; j <= kb - 1; ++j)
+        if (lw && j >= 0 && j % 2 == 0) n += wloads;
+    return n;
+}
 
 // Wait until at most NV vector-memory operations of this wave are outstanding, then meet
 // the rest of the workgroup.  The memory clobber keeps LDS accesses on their side of it.
@@ -382,12 +396,22 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     constexpr int MB = shape_mb(SH);         // 32-row blocks per wave
     constexpr int NMF = 2 * NB * MB;         // MFMAs per 32-deep step (16, or 32 at SH 3)
     constexpr int BM = tile_m(SH), BN = tile_n(SH);
-    constexpr int kChunks = BM * 8;          // 16-byte chunks per stage (8 per 64-deep row)
+    // One row of tiles whose live rows (MA row blocks) fill less than the tile, with four
+    // weight sets: the ring holds only those rows, in eight stages instead of four, so its
+    // DMAs run seven stages ahead and a weight tile has about six stages to land.  Few
+    // rows make a short step (MA of MB row blocks), and with four stages the loads were not
+    // covered.  (With two weight sets the compiler merged the eight-stage pass with the
+    // tail and copied weight registers at the loop head, behind a full load wait.)
+    constexpr bool DEEP = SH != 3 && MA < MB && NWS == 4;
+    constexpr int XS = DEEP ? 8 : kXStages;  // ring stages
+    constexpr int SR = DEEP ? 32 * MA : BM;  // rows per stage
+    constexpr int DMB = SR / 32;             // DMA blocks of 8 rows per wave and stage
+    constexpr int kChunks = SR * 8;          // 16-byte chunks per stage (8 per 64-deep row)
     // Loads each wave issues per weight tile: 2 NB WV 16-byte code slots (column blocks x
     // k halves x pieces), plus scales (and zeros) per column block and group.
     constexpr int kWLoads = 2 * NB * WV + NB * GPT * (SYM ? 1 : 2);
     static_assert(kWLoads <= 16, "weight loads are spread over one step's 16 MFMAs");
-    __shared__ u32x4_t xs[kXStages][kChunks];
+    __shared__ u32x4_t xs[XS][kChunks];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -410,10 +434,10 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     const rsrc_t zrs = make_rsrc(zeros, (uint32_t)((size_t)groups * N * BITS / 8));
     const DqConst dc = make_dq_const<CODE>();
 
-    // DMA source offsets: wave w fills blocks b = MB w + i of every stage; block b holds
+    // DMA source offsets: wave w fills blocks b = DMB w + i of every stage; block b holds
     // rows 8b .. 8b+7, lane l writes LDS chunk 64b + l = (row 8b + l/8, physical chunk l%8),
     // which holds logical chunk (l%8) ^ (l/8).  Rows past M read zeros (one past the end).
-    // (Offset arrays have fixed bounds, of which MB / NB entries are used: with bounds
+    // (Offset arrays have fixed bounds, of which DMB / NB entries are used: with bounds
     // that depend on a template parameter, the host pass of this compiler silently emits
     // no launch stub for the kernel.)
     // The 256 x 256 tile keeps only block 0's offset and adds i times the 8-row stride at
@@ -422,8 +446,8 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     // not fault, and those rows' results are never stored.
     uint32_t xoff[8];
 #pragma unroll
-    for (int i = 0; i < (SH == 3 ? 1 : MB); ++i) {
-        const int r = 8 * (wave * MB + i) + (lane >> 3);
+    for (int i = 0; i < (SH == 3 ? 1 : DMB); ++i) {
+        const int r = 8 * (wave * DMB + i) + (lane >> 3);
         const uint32_t row = SH == 3 ? (uint32_t)(m_blk + r) : (uint32_t)min(m_blk + r, M);
         xoff[i] = (row * Kx + (((lane & 7) ^ (lane >> 3)) * 8) + t0 * 128) * 2u;
     }
@@ -467,12 +491,13 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         u32x4_t w[NB][2][WV];                // [nb][u][piece]: the tile's four 32-deep steps
         uint32_t s[NB][GPT], z[NB][GPT];
     };
-    static_assert(NWS == 2 || NWS == 4, "the stage loop unrolls 2 * NWS stages");
+    static_assert(NWS == 2 || NWS == 4, "a pass of the stage loop holds whole weight-set rotations");
+    static_assert(XS == 4 || XS == 8, "ring depth");
     WSet ws[NWS];
     DqT dq[NWS][NB][GPT];
     u32x4_t A[2][2][NB], B[2][2][MB];        // [set][u][nb] / [set][u][mb]
 
-    // Block i (of MB) of this wave's share of stage st's DMA.
+    // Block i (of DMB) of this wave's share of stage st's DMA.
     auto dma_part = [&](int st, auto buf, int i) __attribute__((always_inline)) {
         const int sc = min(st, S - 1);
         const uint32_t soff_k = (uint32_t)sc * 128u;
@@ -486,12 +511,12 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         }
         if constexpr (RAG) off = sc * 64 + k_chunk < Kx ? off : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * MB + i) * 64],
+            xrs, (__attribute__((address_space(3))) void *)&xs[decltype(buf)::value][(wave * DMB + i) * 64],
             16, off, soff_k, 0, 0);
     };
     auto dma = [&](int st, auto buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < MB; ++i) dma_part(st, buf, i);
+        for (int i = 0; i < DMB; ++i) dma_part(st, buf, i);
     };
     // Load j (of kWLoads) of weight tile t: the 2 NB code slots, then scales and zeros.
     auto load_w_part = [&](int t, WSet &w, auto J) __attribute__((always_inline)) {
@@ -647,35 +672,34 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One 64-deep stage st (ring buffer BUF = st % 4, tile t = st / 2, half H = st % 2,
+    // One 64-deep stage st (ring buffer BUF = st % XS, tile t = st / 2, half H = st % 2,
     // weight set TW = t % NWS): step 0 runs word 2H and prepares word 2H+1 from this
-    // stage's buffer; step 1 runs word 2H+1 and prepares the next stage's first step (the
-    // next tile's word 0 when H == 1).  Stage 2t loads tile t + NWS - 1, except in the
+    // stage's buffer, and issues the DMA of stage st + XS - 1 into the buffer stage st - 1
+    // read; step 1 runs word 2H+1 and prepares the next stage's first step (the next
+    // tile's word 0 when H == 1).  Stage 2t loads tile t + NWS - 1 in step 1, except in the
     // final four stages (LAST), whose weight loads nothing would read.
-    // The wait: vmcnt counts a wave's loads in issue order, and after its DMA of stage
-    // st+1 (step 0 of stage st-2) the wave issued at least the MB loads of its DMA of stage
-    // st+2 (DMAs write LDS, so the compiler neither moves them across the barrier nor drops
-    // them); leaving at most MB loads in flight therefore finds stage st+1 in LDS.  One of
-    // stages st-2 and st-1 loaded a weight tile in its step 1, after that DMA: WBEHIND
-    // says so, and the wait then also leaves those kWLoads loads in flight, so a weight
-    // tile has until two stages later to land instead of one step.  The prologue's weight
-    // loads are not counted (the compiler has moved them past its barrier), so the first
-    // stage of a block that can follow it does not pass WBEHIND; nor do the final stages,
-    // which issue no weight loads (the compiler would drop them as dead).  The build walks
-    // every launch path of the generated code and fails if a wait could pass early.
-    auto stage = [&](int st, auto BUF, auto H, auto TW, auto LOADW, auto WBEHIND) __attribute__((always_inline)) {
+    // The wait (WAITN, from stage_wait_loads): vmcnt counts a wave's loads in issue order,
+    // so leaving in flight no more loads than the wave issued after its DMA of stage st+1
+    // finds that stage in LDS.  DMAs write LDS, so the compiler neither moves them across
+    // the barrier nor drops them; the weight loads it may move (their memory never
+    // changes) or drop when dead, as in the final stages, which therefore issue none.  The
+    // count takes weight loads only from the same pass of the stage loop, after the DMA in
+    // program order; the build walks every launch path of the generated code and fails if
+    // a wait could pass early.  Counting them lets a weight tile land up to XS - 2 stages
+    // after it was requested instead of within the next step.
+    auto stage = [&](int st, auto BUF, auto H, auto TW, auto LOADW, auto WAITN) __attribute__((always_inline)) {
         constexpr int buf = decltype(BUF)::value, h = decltype(H)::value, tw = decltype(TW)::value;
-        constexpr int nbuf = (buf + 1) % kXStages, nw = (tw + 1) % NWS;
+        constexpr int nbuf = (buf + 1) % XS, nw = (tw + 1) % NWS;
         constexpr bool loadw = decltype(LOADW)::value != 0;
         const int t = st >> 1;
-        wait_vm_barrier<MB + (decltype(WBEHIND)::value ? kWLoads : 0)>();
-        // The next stage's DMA (MB blocks) and, in the first half of a tile, the weight
-        // loads of tile t + NWS - 1 go out one at a time between MFMAs, in the same order
-        // as before, instead of as one burst per wave at the barrier.
+        wait_vm_barrier<decltype(WAITN)::value>();
+        // The DMA of stage st + XS - 1 (DMB blocks) and, in the first half of a tile, the
+        // weight loads of tile t + NWS - 1 go out one at a time between MFMAs, instead of as
+        // one burst per wave at the barrier.
         auto dma_hook = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
-            constexpr int every = NMF / MB;
-            if constexpr (i % every == 1) dma_part(st + 3, IC<(buf + 3) % kXStages>(), i / every);
+            constexpr int every = NMF / DMB;
+            if constexpr (i % every == 1) dma_part(st + XS - 1, IC<(buf + XS - 1) % XS>(), i / every);
         };
         auto w_hook = [&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
@@ -709,29 +733,34 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
             }
         }
     };
-    // Stages st .. st+3 (tiles 2u, 2u+1 of a 2 * NWS-stage block, u = 0 or 1); LAST: the
-    // kernel's final four stages.  Stage st follows the prologue or a stage that loaded
-    // weights two stages back: only the second four of a block (u = 1) always does.
+    // Stages st .. st+3 (tiles 2u, 2u+1 of a pass of the stage loop, u = 0 or 1); LAST: the
+    // kernel's final four stages, a pass of their own.
     auto four = [&](int st, auto U, auto LAST) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
         constexpr bool last = decltype(LAST)::value != 0;
         constexpr int lw = last ? 0 : 1;
-        stage(st + 0, IC<0>(), IC<0>(), IC<(2 * u) % NWS>(), IC<lw>(), IC<u>());
-        stage(st + 1, IC<1>(), IC<1>(), IC<(2 * u) % NWS>(), IC<lw>(), IC<lw>());
-        stage(st + 2, IC<2>(), IC<0>(), IC<(2 * u + 1) % NWS>(), IC<lw>(), IC<lw>());
-        stage(st + 3, IC<3>(), IC<1>(), IC<(2 * u + 1) % NWS>(), IC<lw>(), IC<lw>());
+        constexpr int b = 4 * u;
+        stage(st + 0, IC<(b + 0) % XS>(), IC<0>(), IC<(2 * u) % NWS>(), IC<lw>(),
+              IC<stage_wait_loads(XS, DMB, kWLoads, b + 0, lw)>());
+        stage(st + 1, IC<(b + 1) % XS>(), IC<1>(), IC<(2 * u) % NWS>(), IC<lw>(),
+              IC<stage_wait_loads(XS, DMB, kWLoads, b + 1, lw)>());
+        stage(st + 2, IC<(b + 2) % XS>(), IC<0>(), IC<(2 * u + 1) % NWS>(), IC<lw>(),
+              IC<stage_wait_loads(XS, DMB, kWLoads, b + 2, lw)>());
+        stage(st + 3, IC<(b + 3) % XS>(), IC<1>(), IC<(2 * u + 1) % NWS>(), IC<lw>(),
+              IC<stage_wait_loads(XS, DMB, kWLoads, b + 3, lw)>());
     };
 
-    // Prologue: stages 0..2 in flight, tiles 0 .. NWS-2, then stage 0's first operands.
-    // The DMAs go first; the prologue's wait leaves at most their last two stages in
-    // flight, so stage 0 has landed whatever the compiler does with the weight loads.
-    dma(0, IC<0>());
-    dma(1, IC<1>());
-    dma(2, IC<2>());
+    // Prologue: stages 0 .. XS-2 in flight, tiles 0 .. NWS-2, then stage 0's first
+    // operands.  The DMAs go first; the prologue's wait leaves at most their last XS - 2
+    // stages in flight, so stage 0 has landed whatever the compiler does with the weight
+    // loads.
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+        (dma(J, IC<J>()), ...);
+    }(std::make_integer_sequence<int, XS - 1>{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NWS - 1; ++t) load_w(t, ws[t]);
-    wait_vm_barrier<2 * MB>();
+    wait_vm_barrier<(XS - 2) * DMB>();
     make_dq(ws[0], dq[0]);
     read_b(IC<0>(), 0, B[0]);
     dequant_a(ws[0], dq[0], 0, A[0]);
@@ -741,18 +770,20 @@ __global__ __launch_bounds__(kXThreads) void prefill_x32_kernel(
     asm volatile("s_nop 4" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-    // S is a multiple of 4: blocks of 2 * NWS stages, then a four-stage tail (a block's
-    // first four stages, so ring buffers and weight sets line up).
+    // S is a multiple of 4: passes of PASS stages (whole rotations of the ring and of the
+    // weight sets), then, for eight-stage passes, a four-stage tail (a pass's first four
+    // stages, so ring buffers and weight sets line up).
     // Each pass ends with mfma_drain, so whatever the compiler places after the loop (it
     // may copy accumulators between registers right at the loop exit) finds the inline-asm
     // MFMAs' results written.
+    constexpr int PASS = (NWS == 4 || XS == 8) ? 8 : 4;
     int st = 0;
-    for (; st + 2 * NWS <= S; st += 2 * NWS) {
+    for (; st + PASS <= S; st += PASS) {
         four(st, IC<0>(), IC<0>());
-        if constexpr (NWS == 4) four(st + 4, IC<1>(), IC<0>());
+        if constexpr (PASS == 8) four(st + 4, IC<1>(), IC<0>());
         mfma_drain();
     }
-    if constexpr (NWS == 4) {
+    if constexpr (PASS == 8) {
         if (st < S) {
             four(st, IC<0>(), IC<1>());
             mfma_drain();
