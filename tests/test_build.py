@@ -95,6 +95,58 @@ def _kernel_asm(tail_wait):
     return "\n" + "\n".join(lines)
 
 
+def _mangled(nws, sh, ma):
+    """A tiled kernel's name with template arguments <ACT, SYM, G, NWS, SH, CODE, RAG, MA>."""
+    return (f"_ZN6mpgemm12_GLOBAL__N_118prefill_x32_kernelILi0ELb0ELi128ELi{nws}ELi{sh}"
+            f"ELi0ELb0ELi{ma}EEEvPKt")
+
+
+def test_ring_shape_follows_the_template_arguments():
+    # one row of tiles with fewer live row blocks than the tile, four weight sets: eight
+    # stages holding the live rows; otherwise four stages of the whole tile
+    assert build.ring_shape(_mangled(4, 1, 2)) == (8, 2)
+    assert build.ring_shape(_mangled(4, 1, 4)) == (8, 4)
+    assert build.ring_shape(_mangled(4, 2, 2)) == (8, 2)
+    assert build.ring_shape(_mangled(4, 1, 8)) == (4, 8)
+    assert build.ring_shape(_mangled(4, 2, 4)) == (4, 4)
+    assert build.ring_shape(_mangled(4, 3, 8)) == (4, 8)
+    assert build.ring_shape(_mangled(2, 1, 2)) == (4, 8)
+    assert build.ring_shape(_mangled(2, 2, 2)) == (4, 4)
+    assert build.ring_shape("_Z18prefill_x32_kernelv") == (4, None)
+
+
+def _deep_kernel_asm(stage_waits):
+    """An eight-stage ring kernel's skeleton (two DMA loads per stage, four weight loads in
+    the even stages): prologue of seven DMA stages, then one pass of eight stages whose
+    waits are given, then the end of the kernel."""
+    dma = "\tbuffer_load_dwordx4 v1, s[0:3], s4 offen lds"
+    w = "\tbuffer_load_dwordx4 v[2:5], v6, s[8:11], s4 offen"
+    lines = ["_ZN6mpgemm12_GLOBAL__N_118prefill_x32_kernelILi0ELb0ELi128ELi4ELi1ELi0ELb0ELi2EEEv:"]
+    lines += [dma] * 14 + [w] * 4 + ["\ts_waitcnt vmcnt(12)", "\ts_barrier",
+                                     "\ts_cbranch_scc1 .LBB0_9", ".LBB0_2:"]
+    for k, wait in enumerate(stage_waits):
+        lines += [f"\ts_waitcnt vmcnt({wait})", "\ts_barrier", dma, dma]
+        if k % 2 == 0:
+            lines += [w] * 4
+    lines += ["\ts_cbranch_scc1 .LBB0_2", "\ts_cbranch_scc1 .LBB0_7", ".LBB0_6:",
+              "\ts_nop 0", ".LBB0_7:", "\ts_endpgm", ".LBB0_9:", "\ts_mov_b32 s5, 0",
+              "\ts_branch .LBB0_7", ".Lfunc_end0:", ""]
+    return "\n" + "\n".join(lines)
+
+
+def test_ring_wait_check_counts_weight_loads_behind_the_dma_of_an_eight_stage_ring():
+    # stage k (of a pass) needs the DMA issued six stages earlier, in stage k - 6; behind it
+    # are the DMAs of five stages (10 loads) and the weight loads of the even stages from
+    # k - 6 on, counted only within the pass (the first pass follows the prologue)
+    good = [10 + 4 * sum(1 for j in range(max(0, k - 6), k) if j % 2 == 0) for k in range(8)]
+    assert good == [10, 14, 14, 18, 18, 22, 22, 22]
+    assert build.ring_wait_violations(_deep_kernel_asm(good)) == []
+    # one more than the 22 loads behind the DMA stage 7 needs lets that wait pass early
+    bad = build.ring_wait_violations(_deep_kernel_asm(good[:7] + [23]))
+    assert {path for _, path, _ in bad} == {"loop once", "loop twice"}
+    assert all(v[0] % 8 == 0 and v[1:] == (22, 23) for _, _, vs in bad for v in vs)
+
+
 def test_ring_wait_check_walks_loop_and_tail_paths():
     assert build.ring_wait_violations(_kernel_asm(2)) == []
     bad = build.ring_wait_violations(_kernel_asm(5))     # tail waits leave too much in flight
