@@ -164,6 +164,7 @@ struct DqF16 {
 };
 struct DqBF16 {
     float s, nzs;
+    float nz_hi, nz_lo;          // -(1024 + z) s and -(64 + z) s, for the magic-number form
 };
 
 __device__ __forceinline__ DqF16 make_dq_f16(uint16_t s_bits, uint32_t z) {
@@ -181,6 +182,9 @@ __device__ __forceinline__ DqBF16 make_dq_bf16(uint16_t s_bits, uint32_t z) {
     DqBF16 d;
     d.s = (float)bitcast<_Float16>(s_bits);
     d.nzs = -(float)z * d.s;     // exact: 4-bit integer times 11-bit significand
+    // exact too: integers of at most 11 bits (8-bit z: 1279) times an 11-bit significand
+    d.nz_hi = -(1024.0f + (float)z) * d.s;
+    d.nz_lo = -(64.0f + (float)z) * d.s;
     return d;
 }
 

@@ -155,12 +155,14 @@ struct DqTmp {
     float f[8];
 };
 
-// Operation OP of the dequantization of word w into out (8 weights, k order), in the
-// same arithmetic as Dq<ACT>::word.  fp16 (13 operations): one shift, four isolate-and-
-// combine (1024 + q / 64 + q), four exact packed adds of -(B + z), four packed multiplies
-// by s (the one rounding).  bf16 (14 operations): spread nibbles to bytes (two), eight
-// convert-and-fma q * s - z * s (exact in fp32), four conversions to bf16 pairs (the one
-// rounding).
+// Operation OP of the dequantization of word w into out (8 weights, k order), with the
+// results of Dq<ACT>::word.  fp16 (13 operations): one shift, four isolate-and-combine
+// (1024 + q / 64 + q as fp16 pairs), four exact packed adds of -(B + z), four packed
+// multiplies by s (the one rounding).  bf16 (17 operations): the same shift and isolate-
+// and-combine, eight mixed-precision fmas (B + q) s - (B + z) s that read each fp16 half
+// directly and are exact in fp32 (11-bit integers times an 11-bit significand; the
+// difference (q - z) s has at most 16 bits), four conversions to bf16 pairs (the one
+// rounding).  Dq<kBF16>::word computes q s - z s instead: the same exact values.
 template <int ACT>
 struct DqOps;
 
@@ -194,22 +196,25 @@ struct DqOps<kF16> {
 
 template <>
 struct DqOps<kBF16> {
-    static constexpr int kCount = 14;
+    static constexpr int kCount = 17;
     template <int OP>
     static __device__ __forceinline__ void run(uint32_t w, const DqBF16 &d, const DqConst &c,
                                                DqTmp &t, u32x4_t &out) {
-        // lo bytes: e0 e4 e1 e5; hi bytes: e2 e6 e3 e7
         if constexpr (OP == 0) {
-            t.h[0] = w & c.m_byte;
-        } else if constexpr (OP == 1) {
-            t.h[1] = (w >> 4) & c.m_byte;
-        } else if constexpr (OP >= 2 && OP <= 9) {
-            constexpr int e = OP - 2;                       // element e0 .. e7
-            constexpr int src = (e >> 1) & 1;               // e0 e1 e4 e5 in lo
-            constexpr int byte = ((e & 1) << 1) | (e >> 2);
-            t.f[e] = __builtin_fmaf(ubyte(t.h[src], byte), d.s, d.nzs);
+            asm("v_lshrrev_b32 %0, 8, %1" : "=v"(t.sh) : "v"(w));
+        } else if constexpr (OP >= 1 && OP <= 4) {
+            constexpr int j = OP - 1;
+            const uint32_t src = (j < 2) ? w : t.sh;
+            if constexpr ((j & 1) == 0)
+                asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t.h[j]) : "v"(src), "s"(c.m_lo), "v"(c.b_hi));
+            else
+                asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t.h[j]) : "v"(src), "s"(c.m_hi), "v"(c.b_lo));
+        } else if constexpr (OP >= 5 && OP <= 12) {
+            constexpr int e = OP - 5, j = e / 2;
+            const uint16_t bits = (uint16_t)((e & 1) ? t.h[j] >> 16 : t.h[j]);
+            t.f[e] = __builtin_fmaf((float)bitcast<_Float16>(bits), d.s, (j & 1) ? d.nz_lo : d.nz_hi);
         } else {
-            constexpr int j = OP - 10;
+            constexpr int j = OP - 13;
             out[j] = pack_bf16x2(t.f[2 * j], t.f[2 * j + 1]);
         }
     }
