@@ -190,7 +190,9 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * config_id 0 means "select"; an id that cannot run the shape returns
  * MPGEMM_ERR_UNSUPPORTED; an unknown id returns MPGEMM_ERR_INVALID_ARG).  Ids: 1..4
  * small-M kernel with 1..4 row blocks of 16 (M <= 16*id); 12 tiled large-M kernel on
- * 32x32x16 MFMAs with a four-stage LDS ring, 128 x 256 workgroup tile; 13 the same with a
+ * 32x32x16 MFMAs with an LDS activation ring (four stages; eight stages of only the rows
+ * below M when one row of tiles leaves part of the tile empty and g = 128 with 4-bit
+ * codes), 128 x 256 workgroup tile; 13 the same with a
  * 256 x 128 tile; 14 the same with a 256 x 256 tile.  Ids 12, 13 and 14 take every
  * shape.  The selector picks 1..2 for M <= 32, and 3..4 for
  * M <= 64 with N K <= 4096 * 4096; else for M <= 128 the tile whose grid (with its K split,
