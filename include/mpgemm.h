@@ -195,10 +195,11 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * codes), 128 x 256 workgroup tile; 13 the same with a
  * 256 x 128 tile; 14 the same with a 256 x 256 tile.  Ids 12, 13 and 14 take every
  * shape.  The selector picks 1..2 for M <= 32, and 3..4 for
- * M <= 64 with N K <= 4096 * 4096; else for M <= 128 the tile whose grid (with its K split,
- * on the current device's compute units, 256 when none is current) fills more units (on a
- * tie 13 when both fill every unit or only 13 runs unsplit, else 12; 12 when 13 alone needs
- * more than one round); 12 for 256 < M <= 384 with K < 16384; 14 when its grid of
+ * M <= 64 (48 for 4-bit codes with group 128) with N K <= 4096 * 4096; else for M <= 128
+ * the tile whose grid (with its K split, on the current device's compute units, 256 when
+ * none is current) fills more units (on a tie 12 when both fill every unit and K >= 16384,
+ * else 13 when both fill every unit or only 13 runs unsplit, else 12; 12 when 13 alone
+ * needs more than one round); 12 for 256 < M <= 384 with K < 16384; 14 when its grid of
  * 256 x 256 tiles covers at least three quarters of the compute units; 12 for M >= 2048
  * with N < 16384 and K < 8192; else 13.
  * (2- and 3-bit codes take 1..4 for every M <= 64.)

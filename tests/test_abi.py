@@ -72,7 +72,9 @@ def test_selector_and_config_names():
     assert sel(33, 4096, 4096, 128, 0) == 3
     assert sel(48, 4096, 4096, 128, 0) == 3
     assert sel(33, 6144, 4096, 128, 0) == 13          # 192 workgroups against 96
-    assert sel(64, 4096, 4096, 128, 1) == 4
+    assert sel(49, 4096, 4096, 128, 1) == 13         # 4-bit, g = 128: the eight-stage ring
+    assert sel(64, 4096, 4096, 128, 1) == 13
+    assert sel(64, 4096, 4096, 64, 1) == 4           # g = 64: four stages
     assert sel(64, 4096, 4224, 128, 0) == 13          # N K past 4096 * 4096; 32 tiles, 16
     assert sel(33, 16384, 4096, 128, 0) == 13         # both fill all 256 units
     assert sel(64, 57344, 8192, 128, 1) == 12         # 448 tiles of 256 x 128: two rounds
@@ -83,6 +85,8 @@ def test_selector_and_config_names():
     assert sel(128, 8192, 8192, 128, 1) == 13         # 256 each: every unit filled
     assert sel(128, 5120, 25600, 64, 0) == 13         # 160 against 80
     assert sel(128, 4096, 14336, 128, 0) == 13        # 256 against 128
+    assert sel(64, 8192, 28672, 128, 1) == 12         # 256 each, K >= 16384
+    assert sel(128, 8192, 28672, 128, 1) == 12
     # larger M: the 256-row tile, except where the 128-row one pads less (257..384 rows)
     assert sel(129, 4096, 4096, 128, 0) == 13
     assert sel(256, 28672, 4096, 128, 0) == 13

@@ -63,12 +63,16 @@ int hip_status(hipError_t e) {
 // activations once per tile through LDS and split the K range of small grids -- were 1.2
 // to 3.3x faster on MI355X (cold weights; Llama-3-70B bf16 QKV at M = 64: 43 us against 98,
 // gate_up 137 against 457; Qwen3-32B down 86 against 193), except on the smallest
-// matrices (Llama-3-8B O, 4096 x 4096: 19 us against 23 at M = 64).  Up to 128 rows both
+// matrices (N K <= 4096 x 4096) up to 64 rows, or 48 with 4-bit codes at g = 128, whose
+// tiled kernels keep the live rows in an eight-stage ring (Llama-3-8B O: three row blocks
+// 14.0 us against 14.5 at M = 40, four 18.6 against 14.7 at M = 64).  Up to 128 rows both
 // tiles run one tile row (their MFMAs skip the row blocks past M), and the one whose grid,
 // with its K split, fills more compute units wins: Llama-3-8B shapes went to the
 // 256 x 128 tile (QKV M = 64: 192 workgroups against 96, 19.4 us against 20.5; gate_up,
 // unsplit against split in two, 31.4 against 36.4), and so did grids that both fill every
-// unit (Llama-3-70B O: 28.0 against 29.3); the Llama-3-70B and Qwen3-32B QKV and gate_up
+// unit (Llama-3-70B O: 24.8 against 25.6 at M = 64) unless K >= 16384 (Llama-3-70B down,
+// 128 x 256 split eight ways against 256 x 128 split four: 49.4 against 53.3 at M = 64,
+// 67.5 against 73.1 at M = 128); the Llama-3-70B and Qwen3-32B QKV and gate_up
 // went to the 128 x 256 one (equal partial fill, or a 256 x 128 grid of more than one round:
 // 70B gate_up 115 against 125 us).  Above 128 rows the 256 x 128 tile, whose
 // dequantized weights each feed 256 rows (0-15% faster from 160 to 8192 rows on all three
@@ -82,6 +86,7 @@ int pick_tile(int M, int N, int K) {
     if (g13 > cus && g12 <= cus) return kConfigPrefillX32;
     const int f12 = g12 < cus ? g12 : cus, f13 = g13 < cus ? g13 : cus;
     if (f13 > f12) return kConfigPrefillX32Tall;
+    if (f13 == f12 && f13 == cus && K >= 16384) return kConfigPrefillX32;
     if (f13 == f12 && (f13 == cus || (p13 == 1 && p12 > 1))) return kConfigPrefillX32Tall;
     return kConfigPrefillX32;
 }
@@ -110,10 +115,13 @@ bool wide_fills(int M, int N, int K) {
     return 4 * tiles >= 3 * (int64_t)cus;
 }
 
-int select_config(int M, int N, int K) {
+int select_config(int M, int N, int K, int group, int code) {
     if (M <= 16) return kConfigDecode1;
     const int64_t nk = (int64_t)N * K;
-    if (M <= 32 || (M <= 64 && nk <= 4096 * 4096)) return (M + 15) / 16;
+    // The tiled kernels' eight-stage ring (4-bit codes, g = 128) beats four row blocks of
+    // the small-M kernel on the smallest matrices too.
+    const int small_m = code == mpgemm::kU4 && group == 128 ? 48 : 64;
+    if (M <= 32 || (M <= small_m && nk <= 4096 * 4096)) return (M + 15) / 16;
     if (M <= 128) return pick_tile(M, N, K);
     if (M > 256 && M <= 384 && K < 16384) return kConfigPrefillX32;
     if (wide_fills(M, N, K)) return kConfigPrefillX32Wide;
@@ -169,7 +177,7 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
     const bool lowbit = code == mpgemm::kU2 || code == mpgemm::kU3;
     const int cfg = config_id != kConfigSelect ? config_id
                     : lowbit && M <= 64     ? (M + 15) / 16
-                                            : select_config(M, N, K);
+                                            : select_config(M, N, K, group, code);
     if (cfg >= kConfigDecode1 && cfg <= kConfigDecode4 && M > 16 * cfg)
         return MPGEMM_ERR_UNSUPPORTED;
     const int Kp = mpgemm::padded_k(K);
@@ -209,7 +217,8 @@ int gemm_impl(int code, const void *X, int dtype, const void *packed_codes,
             c.codes = (const uint32_t *)codes4;
             c.code = mpgemm::kU4;
             c.workspace_bytes = off;
-            const int xcfg = config_id != kConfigSelect ? cfg : select_config(M, N, K);
+            const int xcfg =
+                config_id != kConfigSelect ? cfg : select_config(M, N, K, group, mpgemm::kU4);
             if (getenv("MPGEMM_LOG"))
                 fprintf(stderr, "mpgemm: W%dA16 M=%d N=%d K=%d g=%d -> 4-bit repack, %s\n",
                         code == mpgemm::kU2 ? 2 : 3, M, N, K, group, mpgemm_config_name(xcfg));
@@ -658,9 +667,8 @@ int mpgemm_attention_decode_kvfp8(const void *Q, int dtype, int fp8_format, cons
 }
 
 int mpgemm_select_config(int M, int N, int K, int group, int dtype) {
-    (void)group;
     (void)dtype;
-    return select_config(M < 0 ? 0 : M, N, K);
+    return select_config(M < 0 ? 0 : M, N, K, group, mpgemm::kU4);
 }
 
 int mpgemm_prefill_schedule(int M, int N, int K, int config_id, int cus, int *info, int *work,
