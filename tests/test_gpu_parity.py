@@ -439,3 +439,36 @@ def test_ring_stage_waits_regression_tiny_grids_bit_exact(config, K):
                 print(f"[diag] rep={rep}: {len(bad)} wrong; rows {sorted(set(bad[:, 0].tolist()))[:24]}",
                       flush=True)
             assert np.array_equal(y, w), rep
+
+
+@pytest.mark.parametrize("config", (PREFILL_X32, PREFILL_X32_TALL))
+@pytest.mark.parametrize("M", [40, 64, 100])
+@pytest.mark.parametrize("K", [256, 768, 2048])
+def test_short_grid_ring_bit_exact(config, M, K):
+    """One row of tiles with fewer live rows than the tile: with 4-bit codes at g = 128 the
+    tiled kernels keep only the live rows, in an eight-stage ring whose stage waits count
+    the weight loads behind each DMA (M = 40 and 64 on both tiles, 100 on the 256-row
+    one).  One-hot activation rows make every output a dequantized weight, so a stage read
+    before its DMA landed, or a wrong ring slot, shows as a wrong bit.  K = 256 and 768 run
+    the four-stage tail, 2048 whole passes and a K split over two workgroups; each case
+    runs five times."""
+    N, g = 272, 128
+    codes, scales, zeros = workloads.weights(K, N, g, False, 0.005, 0.02, 7 * K + M + config)
+    rng = np.random.default_rng(K + 3 * M + config)
+    picks = rng.choice(K, M, replace=False)
+    for dtype in ("f16", "bf16"):
+        one = 0x3C00 if dtype == "f16" else 0x3F80
+        x = np.zeros((M, K), dtype=np.uint16)
+        x[np.arange(M), picks] = one
+        case = dict(x=x, codes=codes, scales=scales, zeros=zeros, group=g, dtype=dtype)
+        packed = pack_case(case)
+        w = oracle.dequant(codes, scales, zeros, g, dtype)[picks]
+        xd = dev_half(x, dtype)
+        say(f"short-grid ring config={config} M={M} K={K} {dtype}")
+        for rep in range(5):
+            y = host_bits(mp.w4a16(xd, packed, config=config))
+            if not np.array_equal(y, w):
+                bad = np.argwhere(y != w)
+                print(f"[diag] rep={rep}: {len(bad)} wrong; rows {sorted(set(bad[:, 0].tolist()))[:24]}",
+                      flush=True)
+            assert np.array_equal(y, w), rep
