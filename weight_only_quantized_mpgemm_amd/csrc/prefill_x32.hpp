@@ -35,7 +35,8 @@
 //     HBM latency under full load exceeds the one to two stages a two-set scheme gives;
 //   - activations are the B operand (columns = m), read from a ring of four BM x 64 LDS
 //     stages filled by buffer_load_dwordx4 ... lds three stages ahead (XOR-swizzled 16-byte
-//     chunks, chunk ^ row % 8, so eight consecutive rows hit eight bank groups);
+//     chunks, chunk ^ row % 8, so eight consecutive rows hit eight bank groups); a short
+//     grid keeps only its live rows, in eight stages filled seven ahead;
 //   - each 32-deep step runs 16 MFMAs; after MFMA i come 1/16 of the next step's work: its
 //     LDS operand reads (2 MB per step) and dequantization operations (13 or 14 for each of
 //     the next step's 2 NB weight words).  With four words the operations go round-robin
