@@ -200,7 +200,8 @@ int mpgemm_w4a16_noalloc(const void *X, int dtype, const void *packed_codes,
  * none is current) fills more units (on a tie 12 when both fill every unit and K >= 16384,
  * else 13 when both fill every unit or only 13 runs unsplit, else 12; 12 when 13 alone
  * needs more than one round); 12 for 256 < M <= 384 with K < 16384; 14 when its grid of
- * 256 x 256 tiles covers at least three quarters of the compute units; 12 for M >= 2048
+ * 256 x 256 tiles covers at least three quarters of the compute units, or at least half
+ * of them in one round while both other tiles' grids exceed one round; 12 for M >= 2048
  * with N < 16384 and K < 8192; else 13.
  * (2- and 3-bit codes take 1..4 for every M <= 64.)
  */

@@ -105,6 +105,9 @@ def test_selector_and_config_names():
     assert sel(256, 57344, 8192, 128, 1) == 14        # 224 tiles
     assert sel(300, 57344, 8192, 128, 1) == 12        # 257..384 rows: the 128-row tile
     assert sel(1024, 4096, 14336, 128, 0) == 13       # 64 tiles: the split 256 x 128 one
+    assert sel(1024, 10240, 5120, 64, 0) == 14        # 160 tiles, one round; 320 of the others
+    assert sel(768, 10240, 5120, 64, 0) == 13         # 120 tiles: under half the units
+    assert sel(2048, 4096, 4096, 128, 0) == 12        # 128 tiles, but 256 x 128 fits one round
     for cid in (1, 2, 3, 4, 12, 13, 14):
         assert mp.config_name(cid)
     for cid in (7, 10, 11):

@@ -108,11 +108,18 @@ hipError_t launch_tiled(int cfg, const mpgemm::GemmArgs &a, hipStream_t s) {
 // bf16 gate_up and down at M = 4096, 6-10% on Qwen3-32B gate_up and down).  Smaller grids
 // would need its K split, whose partials are twice the other tiles' (and more than the
 // reported workspace holds): there the other tiles, split, were up to twice as fast.
+// Also where its grid is one round of at least half the units while the 256 x 128 tiles
+// would need a second, partial one (Qwen3-32B QKV at M = 1024: 160 wide tiles, 107 us
+// against 132 for 320 tiles of 256 x 128 and 129 for 320 of 128 x 256).
 bool wide_fills(int M, int N, int K) {
     int cus = 256;
     mpgemm::x32_grid(M, N, K, 3, nullptr, &cus);        // the device's units (256 if none)
-    const int64_t tiles = (int64_t)((M + 255) / 256) * ((mpgemm::padded_n(N) + 255) / 256);
-    return 4 * tiles >= 3 * (int64_t)cus;
+    const int64_t Np = mpgemm::padded_n(N);
+    const int64_t tiles = (int64_t)((M + 255) / 256) * ((Np + 255) / 256);
+    if (4 * tiles >= 3 * (int64_t)cus) return true;
+    const int64_t t13 = (int64_t)((M + 255) / 256) * ((Np + 127) / 128);
+    const int64_t t12 = (int64_t)((M + 127) / 128) * ((Np + 255) / 256);
+    return tiles <= cus && 2 * tiles >= cus && t13 > cus && t12 > cus;
 }
 
 int select_config(int M, int N, int K, int group, int code) {
